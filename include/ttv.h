@@ -1,0 +1,232 @@
+/*
+ * ttv.h -- C ABI of the token-tree verification library (tree-based parallel
+ * decoding step of tree speculative inference) for AMD Instinct MI355X (gfx950).
+ *
+ * Sources cited below (page title, then the section on it):
+ *   [SI]  "SpecInfer: Accelerating Generative Large Language Model Serving with
+ *         Tree-based Speculative Inference and Verification" -- source-linked
+ *         summary of arXiv 2305.09781v4 (paperlayer.ai).
+ *   [SSD] "Accelerating LLM Inference with Staged Speculative Decoding" --
+ *         source-linked summary of arXiv 2308.04623v1 (paperlayer.ai).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument except `stream` is a DEVICE pointer owned by the
+ *    caller.  The library never allocates, frees or retains a pointer.
+ *  - Calls are asynchronous on `stream` (NULL = the default stream); no call
+ *    synchronises the host.  Failures inside a kernel surface at the caller's
+ *    next synchronisation.
+ *  - All arguments are validated on the host BEFORE any HIP call, so every
+ *    error status below except TTV_E_LAUNCH can be produced on a machine
+ *    without a GPU.  On an error status nothing has been enqueued.
+ *  - Per-request problems that only the device can see (a malformed tree, a
+ *    prefix length that breaks the host's promise) are reported in the nullable
+ *    `dev_status[B]` array (TTV_OK or the error code per request); the outputs
+ *    of such a request are defined per entry point.
+ *  - Tensors are dense, row-major, with the shapes written next to them.
+ *  - Node 0 of every tree is its root; a tree is valid iff parents[0] == -1 and
+ *    0 <= parents[i] < i for i >= 1 (any topological numbering; depth-first is
+ *    one valid numbering but is not assumed).
+ *  - The library holds no global state; calls on different streams are
+ *    independent as long as their output buffers do not overlap.
+ */
+#ifndef TTV_H
+#define TTV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ttv_status;
+enum {
+  TTV_OK = 0,
+  TTV_E_NULL = 1,        /* a required pointer is NULL                         */
+  TTV_E_SHAPE = 2,       /* a size is out of range or inconsistent             */
+  TTV_E_DTYPE = 3,       /* unknown dtype / mode enum value                    */
+  TTV_E_UNSUPPORTED = 4, /* N > 128, D not in {64,128}, Hq % Hkv != 0, ...      */
+  TTV_E_WORKSPACE = 5,   /* workspace NULL or smaller than *_workspace_size    */
+  TTV_E_LAUNCH = 6,      /* a kernel launch failed (hipGetLastError)           */
+  TTV_E_TREE = 7         /* device: malformed parents[] of one request         */
+};
+
+typedef int32_t ttv_dtype;
+enum { TTV_F32 = 0, TTV_BF16 = 1 };
+
+typedef int32_t ttv_verify_mode;
+enum { TTV_GREEDY = 0, TTV_STOCHASTIC = 1 };
+
+#define TTV_MAX_NODES 128 /* N <= 128: one or two 64-bit ancestor words per node */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* ttv_status_string(ttv_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t ttv_version(void);
+
+/*
+ * ttv_tree_topology -- the topology-aware causal mask of every request's token
+ * tree [SI] §4 "Tree-Based Parallel Decoding" (topology-aware causal masking)
+ * and "Tree Attention" (a node stands for the token sequence from the root to
+ * it), plus the node depths that position encodings need ([SSD] §3
+ * "Implementation": the tree controls positional embeddings and causal mask).
+ *
+ *   parents   int32 [B,N]      parent node of each node, parents[b,0] == -1
+ *   anc_out   uint64 [B,N,W]   W = ceil(N/64); bit j%64 of word j/64 of
+ *                              anc_out[b,i] is set iff node j lies on the path
+ *                              root -> i (node i itself included).  Nullable.
+ *   depth_out int32 [B,N]      number of edges from the root.  Nullable.
+ *   dev_status int32 [B]       nullable; TTV_E_TREE for a malformed tree, whose
+ *                              anc_out rows are then 0 and depth_out rows -1.
+ * Errors: TTV_E_NULL (parents), TTV_E_SHAPE (B < 1 or N < 1),
+ *         TTV_E_UNSUPPORTED (N > 128), TTV_E_LAUNCH.
+ */
+ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents,
+                             uint64_t* anc_out, int32_t* depth_out,
+                             int32_t* dev_status, void* stream);
+
+/*
+ * ttv_tree_attn -- tree attention for every node of every request in one
+ * launch [SI] §4 "Tree Attention" and "Tree-Based Parallel Decoding": the
+ * output of node i is ordinary causal attention of node i's query over the
+ * sequence node i represents, i.e. the request's prefix KV (positions
+ * 0..L_b-1) followed by the tree-KV rows of the nodes on the path root -> i.
+ * The prefix part and the in-tree part are two parts of one softmax ([SSD] §3
+ * "Implementation" partitions attention the same way).
+ *
+ *   dt          TTV_F32 or TTV_BF16: element type of q, k_*, v_*, out.
+ *   B,N         requests, tree nodes per request (1 <= N <= 128).
+ *   Hq,Hkv,D    query heads, key/value heads (Hq % Hkv == 0; query head hq
+ *               reads kv head hq / (Hq/Hkv)), head dim D in {64,128}.
+ *   scale       softmax scale applied to q.k (usually 1/sqrt(D)).
+ *   q           [B,N,Hq,D]  queries of the tree nodes (positions already
+ *               encoded by the caller at L_b + depth).
+ *   k_cache,v_cache [B,Hkv,Lcap,D]  prefix cache; rows 0..L_b-1 are read.
+ *   cache_len   int32 [B] (device) L_b, the prefix length of request b.
+ *   Lmax        host promise: max_b L_b (sizes the launch); requires
+ *               0 <= Lmax <= Lcap.  A request with L_b < 0 or L_b > Lmax is
+ *               reported as TTV_E_SHAPE in dev_status and gets zero output.
+ *   k_tree,v_tree [B,Hkv,N,D]  keys/values of the tree nodes themselves.
+ *   parents     int32 [B,N]  tree of each request (see conventions).
+ *   out         [B,N,Hq,D]  attention output, type dt (bf16 rounded to
+ *               nearest even from fp32).  A request with a malformed tree gets
+ *               zeros and dev_status TTV_E_TREE.
+ *   lse         float [B,N,Hq], nullable: natural-log sum-exp of the scaled
+ *               scores (0 for a rejected request).
+ *   workspace   device scratch of >= ttv_tree_attn_workspace_size(...) bytes
+ *               (may be NULL when that size is 0).  Its contents need no
+ *               initialisation and are garbage afterwards.
+ *   rows_per_block, chunk_keys  launch tuning: 0 = automatic; otherwise query
+ *               rows per workgroup (16, 32, 64, 128 or 256 on the matrix-core
+ *               path) and prefix keys per workgroup (a positive multiple of
+ *               64).  The same values must be given to the size query.
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE, TTV_E_UNSUPPORTED,
+ *         TTV_E_WORKSPACE, TTV_E_LAUNCH.
+ */
+ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq,
+                         int32_t Hkv, int32_t D, float scale, const void* q,
+                         const void* k_cache, const void* v_cache, int32_t Lcap,
+                         const int32_t* cache_len, int32_t Lmax,
+                         const void* k_tree, const void* v_tree,
+                         const int32_t* parents, void* out, float* lse,
+                         int32_t* dev_status, void* workspace,
+                         size_t workspace_bytes, int32_t rows_per_block,
+                         int32_t chunk_keys, void* stream);
+
+/* Bytes of workspace ttv_tree_attn needs for these sizes (0 if none);
+ * returns (size_t)-1 for arguments ttv_tree_attn would reject. */
+size_t ttv_tree_attn_workspace_size(ttv_dtype dt, int32_t B, int32_t N,
+                                    int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t Lmax, int32_t rows_per_block,
+                                    int32_t chunk_keys);
+
+/*
+ * ttv_tree_verify -- verify every request's token tree against the LLM's
+ * outputs at each node and return the longest accepted root-to-node path
+ * ([SI] §4 "Token Tree Verification", "Token Verification"; §6: greedy
+ * verification reproduces incremental decoding's token sequences).
+ *
+ *   mode     TTV_GREEDY: llm holds logits; node c is accepted iff its parent
+ *            is accepted and tokens[c] == argmax of llm[b,parent(c),:]
+ *            (fp32 compare, lowest index wins ties; logits must be finite).
+ *            The path ends at the deepest accepted node d (lowest index on
+ *            ties) and the bonus token is argmax llm[b,d,:].
+ *            TTV_STOCHASTIC: multi-step speculative sampling.  llm[b,u,:] is
+ *            the LLM's next-token distribution after node u, ssm[b,c,:] is
+ *            the distribution node c's token was drawn from (row 0 unused).
+ *            Starting at the root with residual w = llm[b,u,:] and mass s = 1,
+ *            the children c of u are tested in ascending node index with the
+ *            uniform r = u_accept[b,c]: accept iff (r*q[x])*s < w[x]
+ *            (fp32, two multiplies, strict), x = tokens[c], q = ssm[b,c,:].
+ *            On acceptance move to c (w = llm[b,c,:], s = 1).  On rejection
+ *            w[v] = max(fmaf(-s, q[v], w[v]), +0) for all v and
+ *            s = (float)(sum_v fx(w[v]) * 2^-40), fx(x) = floor(x * 2^40) as
+ *            uint64; s == 0 stops testing and resets w = llm[b,u,:].  When no
+ *            child is accepted the bonus token is drawn from w by inverse CDF
+ *            over the exact integer prefix sums of fx(w): with
+ *            S = sum fx(w), R = floor(u_bonus[b] * 2^24), T = floor(R*S/2^24),
+ *            the bonus is the smallest t with sum_{v<=t} fx(w[v]) > T
+ *            (argmax w if S == 0).  Probabilities must lie in [0,1] and
+ *            uniforms in [0,1).
+ *   B,N,V    requests, nodes per request (<= 128), vocabulary (>= 1).
+ *   parents  int32 [B,N]; tokens int32 [B,N] (tokens[b,0] = root's token,
+ *            unused); llm float [B,N,V]; ssm float [B,N,V] (stochastic only,
+ *            else NULL); u_accept float [B,N] and u_bonus float [B]
+ *            (stochastic only, else NULL): the uniforms the method draws,
+ *            supplied by the caller.
+ *   path     int32 [B,N]: path[b,k] = node at depth k on the accepted path,
+ *            -1 after the end.   path_len int32 [B]: accepted nodes + 1 (>= 1).
+ *   out_tokens int32 [B,N]: tokens of path[1..], then the bonus token, -1
+ *            after (path_len entries in all).
+ *   A malformed tree gives path_len 0 and -1 everywhere, dev_status TTV_E_TREE.
+ *   workspace >= ttv_tree_verify_workspace_size(...) bytes (contents need no
+ *            initialisation).
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE (mode), TTV_E_UNSUPPORTED,
+ *         TTV_E_WORKSPACE, TTV_E_LAUNCH.
+ */
+ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N,
+                           int32_t V, const int32_t* parents,
+                           const int32_t* tokens, const float* llm,
+                           const float* ssm, const float* u_accept,
+                           const float* u_bonus, int32_t* path,
+                           int32_t* path_len, int32_t* out_tokens,
+                           int32_t* dev_status, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B,
+                                      int32_t N, int32_t V);
+
+/*
+ * ttv_kv_commit -- write the accepted path's KV rows into the contiguous cache
+ * ([SI] §4 "Tree-Based Parallel Decoding": verified and speculated tokens share
+ * one key-value cache; only the accepted ones stay).  For request b with
+ * L = cache_len_in[b] and n = path_len[b]:
+ *   k_cache[b,h,L+j,:] = k_tree[b,h,path[b,j],:] (same for v), j < n, all h;
+ *   cache_len_out[b] = L + n;  committed_src[b,j] = path[b,j] (j < n), -1 after.
+ * Copies are bit-exact.  Rows >= L+n and other requests are untouched.
+ *
+ *   dt           element type (only its size matters).
+ *   k_tree,v_tree [B,Hkv,N,D];  k_cache,v_cache [B,Hkv,Lcap,D].
+ *   cache_len_in, cache_len_out int32 [B] (may be the same array).
+ *   Lmax         host promise max_b L_b; requires Lmax + N <= Lcap.
+ *   path, path_len  as written by ttv_tree_verify (device, no host copy).
+ *   committed_src int32 [B,N], nullable.
+ *   dev_status   nullable; TTV_E_SHAPE when L < 0, L > Lmax, n outside
+ *                [0,N] or a path entry outside [0,N): nothing of that request
+ *                is written except cache_len_out[b] = L (and -1 sources).
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE, TTV_E_UNSUPPORTED, TTV_E_LAUNCH.
+ */
+ttv_status ttv_kv_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv,
+                         int32_t D, int32_t Lcap, const void* k_tree,
+                         const void* v_tree, void* k_cache, void* v_cache,
+                         const int32_t* cache_len_in, int32_t* cache_len_out,
+                         int32_t Lmax, const int32_t* path,
+                         const int32_t* path_len, int32_t* committed_src,
+                         int32_t* dev_status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTV_H */

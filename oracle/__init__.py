@@ -1,0 +1,233 @@
+"""CPU oracle of the tree-based parallel decoding step -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg
+may import this package.  The GPU library never imports, links or calls it, and
+this package imports nothing from the GPU library: the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64 attention); this module only
+marshals numpy arrays.  Each function names the passage it follows:
+
+* [SI]  "SpecInfer: Accelerating Generative Large Language Model Serving with
+  Tree-based Speculative Inference and Verification" (paperlayer.ai summary of
+  arXiv 2305.09781v4).
+* [SSD] "Accelerating LLM Inference with Staged Speculative Decoding"
+  (paperlayer.ai summary of arXiv 2308.04623v1).
+
+Pinned by tests/test_oracle_*.py against closed forms, library routines
+(torch SDPA in fp64, numpy matrix inverse and argmax), brute force and
+statistical tests; see each function for its pins.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OK, E_SHAPE, E_TREE = 0, 2, 7
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no fused multiply-adds)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-fopenmp",
+             "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.orc_topology.argtypes = [I, I, P, P, P, P]
+    lib.orc_tree_attn_rows.argtypes = [I, I, I, I, I, ctypes.c_double, P, P, P, I,
+                                       P, P, P, P, I, P, P, P, P]
+    lib.orc_verify_greedy.argtypes = [I, I, I, P, P, P, P, P, P, P]
+    lib.orc_verify_mss.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P]
+    lib.orc_kv_commit.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
+    for f in (lib.orc_topology, lib.orc_tree_attn_rows, lib.orc_verify_greedy,
+              lib.orc_verify_mss, lib.orc_kv_commit):
+        f.restype = None
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+@contextlib.contextmanager
+def use_library(path):
+    """Run the wrappers against another build of oracle.c (the mutation tests
+    compile deliberately broken copies to show that the pins catch them)."""
+    global _lib
+    saved = _load()
+    _lib = _bind(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def topology(parents):
+    """[SI] §4 "Tree Attention": depth and root->node ancestor bitsets.
+
+    parents int32 [B,N] -> (depth int32 [B,N], anc uint64 [B,N,W], status [B]).
+    """
+    par, pp = _c(parents, np.int32)
+    B, N = par.shape
+    W = (N + 63) // 64
+    depth = np.empty((B, N), np.int32)
+    anc = np.empty((B, N, W), np.uint64)
+    status = np.empty(B, np.int32)
+    _load().orc_topology(B, N, pp, depth.ctypes.data_as(ctypes.c_void_p),
+                         anc.ctypes.data_as(ctypes.c_void_p),
+                         status.ctypes.data_as(ctypes.c_void_p))
+    return depth, anc, status
+
+
+def tree_attn_rows(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, scale,
+                   rows):
+    """[SI] §4 "Tree Attention"/"Tree-Based Parallel Decoding", [SSD] §3.
+
+    Attention of the listed rows (b, i, hq) over prefix ++ path(root -> i), in
+    fp64.  q [B,N,Hq,D], k/v_cache [B,Hkv,Lcap,D], k/v_tree [B,Hkv,N,D] (any
+    float type; widened to float32 exactly), rows int [R,3].
+    Returns (out float64 [R,D], lse float64 [R], status int32 [R]).
+    """
+    q, qp = _c(q, np.float32)
+    kc, kcp = _c(k_cache, np.float32)
+    vc, vcp = _c(v_cache, np.float32)
+    kt, ktp = _c(k_tree, np.float32)
+    vt, vtp = _c(v_tree, np.float32)
+    par, pp = _c(parents, np.int32)
+    cl, clp = _c(cache_len, np.int32)
+    rows, rp = _c(np.asarray(rows).reshape(-1, 3), np.int32)
+    B, N, Hq, D = q.shape
+    Hkv, Lcap = kc.shape[1], kc.shape[2]
+    assert kc.shape == (B, Hkv, Lcap, D) and vc.shape == kc.shape
+    assert kt.shape == (B, Hkv, N, D) and vt.shape == kt.shape
+    assert par.shape == (B, N) and cl.shape == (B,) and Hq % Hkv == 0
+    assert rows.size == 0 or (rows[:, 0].min() >= 0 and rows[:, 0].max() < B
+                              and rows[:, 2].min() >= 0 and rows[:, 2].max() < Hq)
+    R = rows.shape[0]
+    out = np.zeros((R, D), np.float64)
+    lse = np.zeros(R, np.float64)
+    status = np.zeros(R, np.int32)
+    _load().orc_tree_attn_rows(B, N, Hq, Hkv, D, float(scale), qp, kcp, vcp, Lcap, clp,
+                               ktp, vtp, pp, R, rp,
+                               out.ctypes.data_as(ctypes.c_void_p),
+                               lse.ctypes.data_as(ctypes.c_void_p),
+                               status.ctypes.data_as(ctypes.c_void_p))
+    return out, lse, status
+
+
+def all_rows(B, N, Hq):
+    """Every (b, i, hq) row in [B,N,Hq] order."""
+    b, i, h = np.meshgrid(np.arange(B), np.arange(N), np.arange(Hq), indexing="ij")
+    return np.stack([b.ravel(), i.ravel(), h.ravel()], axis=1).astype(np.int32)
+
+
+def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, scale):
+    """Full output [B,N,Hq,D] (fp64), lse [B,N,Hq], per-row status."""
+    B, N, Hq, D = np.shape(q)
+    out, lse, st = tree_attn_rows(q, k_cache, v_cache, cache_len, k_tree, v_tree,
+                                  parents, scale, all_rows(B, N, Hq))
+    return out.reshape(B, N, Hq, D), lse.reshape(B, N, Hq), st.reshape(B, N, Hq)
+
+
+def verify_greedy(parents, tokens, llm):
+    """[SI] §4 "Token Tree Verification", §6: greedy acceptance of the tree.
+
+    parents/tokens int32 [B,N], llm float32 [B,N,V] logits.
+    Returns (path [B,N], path_len [B], out_tokens [B,N], status [B]).
+    """
+    par, pp = _c(parents, np.int32)
+    tok, tp = _c(tokens, np.int32)
+    lg, lp = _c(llm, np.float32)
+    B, N = par.shape
+    V = lg.shape[2]
+    assert lg.shape == (B, N, V) and tok.shape == (B, N)
+    path = np.empty((B, N), np.int32)
+    plen = np.empty(B, np.int32)
+    outt = np.empty((B, N), np.int32)
+    st = np.empty(B, np.int32)
+    _load().orc_verify_greedy(B, N, V, pp, tp, lp, path.ctypes.data_as(ctypes.c_void_p),
+                              plen.ctypes.data_as(ctypes.c_void_p),
+                              outt.ctypes.data_as(ctypes.c_void_p),
+                              st.ctypes.data_as(ctypes.c_void_p))
+    return path, plen, outt, st
+
+
+def verify_mss(parents, tokens, llm, ssm, u_accept, u_bonus):
+    """[SI] §4 "Token Verification": multi-step speculative sampling.
+
+    llm/ssm float32 [B,N,V] probabilities, u_accept float32 [B,N], u_bonus
+    float32 [B] uniforms in [0,1).  Returns (path, path_len, out_tokens, status).
+    """
+    par, pp = _c(parents, np.int32)
+    tok, tp = _c(tokens, np.int32)
+    p, ppr = _c(llm, np.float32)
+    q, qpr = _c(ssm, np.float32)
+    ua, uap = _c(u_accept, np.float32)
+    ub, ubp = _c(u_bonus, np.float32)
+    B, N = par.shape
+    V = p.shape[2]
+    assert p.shape == (B, N, V) and q.shape == p.shape
+    assert ua.shape == (B, N) and ub.shape == (B,) and tok.shape == (B, N)
+    assert tok.min(initial=0) >= 0 and tok.max(initial=0) < V
+    path = np.empty((B, N), np.int32)
+    plen = np.empty(B, np.int32)
+    outt = np.empty((B, N), np.int32)
+    st = np.empty(B, np.int32)
+    _load().orc_verify_mss(B, N, V, pp, tp, ppr, qpr, uap, ubp,
+                           path.ctypes.data_as(ctypes.c_void_p),
+                           plen.ctypes.data_as(ctypes.c_void_p),
+                           outt.ctypes.data_as(ctypes.c_void_p),
+                           st.ctypes.data_as(ctypes.c_void_p))
+    return path, plen, outt, st
+
+
+def kv_commit(k_tree, v_tree, k_cache, v_cache, cache_len_in, path, path_len, Lmax):
+    """[SI] §4 "Tree-Based Parallel Decoding": keep the accepted path's KV.
+
+    Works on copies of k_cache/v_cache (any dtype, bytes are copied).  Returns
+    (k_cache', v_cache', cache_len_out, committed_src, status).
+    """
+    kt = np.ascontiguousarray(k_tree)
+    vt = np.ascontiguousarray(v_tree)
+    kc = np.array(k_cache, copy=True, order="C")
+    vc = np.array(v_cache, copy=True, order="C")
+    assert kt.dtype == kc.dtype == vt.dtype == vc.dtype
+    B, Hkv, N, D = kt.shape
+    Lcap = kc.shape[2]
+    cl, clp = _c(cache_len_in, np.int32)
+    pa, pap = _c(path, np.int32)
+    pl, plp = _c(path_len, np.int32)
+    clo = np.empty(B, np.int32)
+    src = np.empty((B, N), np.int32)
+    st = np.empty(B, np.int32)
+    V = ctypes.c_void_p
+    _load().orc_kv_commit(B, N, Hkv, D, kt.dtype.itemsize, Lcap, int(Lmax),
+                          kt.ctypes.data_as(V), vt.ctypes.data_as(V),
+                          kc.ctypes.data_as(V), vc.ctypes.data_as(V), clp,
+                          clo.ctypes.data_as(V), pap, plp, src.ctypes.data_as(V),
+                          st.ctypes.data_as(V))
+    return kc, vc, clo, src, st

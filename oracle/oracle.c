@@ -1,0 +1,348 @@
+/*
+ * oracle.c -- plain, slow CPU reference of the tree-based parallel decoding
+ * step.  TEST INFRASTRUCTURE ONLY: the library under test never links, loads or
+ * calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no code, header or constant with the GPU library.
+ *
+ * Every function follows a plain definition, in the order the definition
+ * states it, with no blocking, fusion or reordering:
+ *   [SI]  "SpecInfer: Accelerating Generative Large Language Model Serving with
+ *         Tree-based Speculative Inference and Verification" (paperlayer.ai
+ *         summary of arXiv 2305.09781v4).
+ *   [SSD] "Accelerating LLM Inference with Staged Speculative Decoding"
+ *         (paperlayer.ai summary of arXiv 2308.04623v1).
+ * Attention is computed in fp64 from the exact input values.  The stochastic
+ * verifier works in fp32 with the operation order its definition fixes,
+ * because its accept/reject decisions and sampled tokens are integers that
+ * must come out the same on every implementation.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -fPIC -shared -lm
+ * (-ffp-contract=off: no multiply-add is fused unless written as fmaf).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_E_SHAPE 2
+#define ORC_E_TREE 7
+
+/* ------------------------------------------------------------------------ */
+/* Tree topology.  [SI] §4 "Tree Attention": node i stands for the token     */
+/* sequence on the path root -> i.  A tree is valid iff parents[0] == -1 and  */
+/* 0 <= parents[i] < i.                                                       */
+/* ------------------------------------------------------------------------ */
+static int tree_is_valid(int N, const int32_t* par) {
+  if (par[0] != -1) return 0;
+  for (int i = 1; i < N; ++i)
+    if (par[i] < 0 || par[i] >= i) return 0;
+  return 1;
+}
+
+/* depth[b,i] = edges from the root; anc[b,i,w] = bitset of the nodes on the
+ * path root -> i (i included), found by walking the parent pointers. */
+void orc_topology(int B, int N, const int32_t* parents, int32_t* depth,
+                  uint64_t* anc, int32_t* status) {
+  const int W = (N + 63) / 64;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* par = parents + (size_t)b * N;
+    int32_t* dep = depth + (size_t)b * N;
+    uint64_t* an = anc + (size_t)b * N * W;
+    memset(an, 0, sizeof(uint64_t) * (size_t)N * W);
+    if (!tree_is_valid(N, par)) {
+      for (int i = 0; i < N; ++i) dep[i] = -1;
+      status[b] = ORC_E_TREE;
+      continue;
+    }
+    for (int i = 0; i < N; ++i) {
+      int d = -1;
+      for (int j = i; j != -1; j = par[j]) {
+        an[(size_t)i * W + j / 64] |= (uint64_t)1 << (j % 64);
+        d += 1;
+      }
+      dep[i] = d;
+    }
+    status[b] = ORC_OK;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tree attention.  [SI] §4 "Tree Attention" / "Tree-Based Parallel          */
+/* Decoding": the output of node i is causal attention of q_i over the        */
+/* sequence node i represents = the request's prefix KV rows 0..L_b-1 then    */
+/* the tree KV rows of the nodes on root -> i, in that order ([SSD] §3        */
+/* "Implementation": cache part + in-batch part).  Query head hq reads kv     */
+/* head hq / (Hq/Hkv).                                                        */
+/*   s_j = scale * sum_d q[d] k_j[d]   (fp64)                                 */
+/*   o   = sum_j exp(s_j - m) v_j / sum_j exp(s_j - m),  m = max_j s_j        */
+/*   lse = m + ln sum_j exp(s_j - m)                                          */
+/* Only the listed rows (b, i, hq) are computed, so a large problem can be     */
+/* checked on a sample.  Inputs are float arrays holding the exact values      */
+/* (bf16 widens to float exactly).  status[r]: 0, ORC_E_TREE, ORC_E_SHAPE;     */
+/* a rejected row gets o = 0 and lse = 0.                                      */
+/* ------------------------------------------------------------------------ */
+void orc_tree_attn_rows(int B, int N, int Hq, int Hkv, int D, double scale,
+                        const float* q, const float* k_cache,
+                        const float* v_cache, int Lcap,
+                        const int32_t* cache_len, const float* k_tree,
+                        const float* v_tree, const int32_t* parents,
+                        int nrows, const int32_t* rows, double* out,
+                        double* lse, int32_t* status) {
+  const int G = Hq / Hkv;
+  (void)B;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < nrows; ++r) {
+    const int b = rows[3 * r + 0], i = rows[3 * r + 1], hq = rows[3 * r + 2];
+    const int h = hq / G;
+    const int32_t* par = parents + (size_t)b * N;
+    const int L = cache_len[b];
+    double* o = out + (size_t)r * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    lse[r] = 0.0;
+    if (!tree_is_valid(N, par)) { status[r] = ORC_E_TREE; continue; }
+    if (L < 0 || L > Lcap || i < 0 || i >= N) { status[r] = ORC_E_SHAPE; continue; }
+
+    /* the key/value rows of the sequence node i represents */
+    int* path = (int*)malloc(sizeof(int) * (size_t)N);
+    int depth = 0;
+    for (int j = i; j != -1; j = par[j]) path[depth++] = j; /* i .. root */
+    const int nkeys = L + depth;
+    const float** krow = (const float**)malloc(sizeof(float*) * (size_t)nkeys);
+    const float** vrow = (const float**)malloc(sizeof(float*) * (size_t)nkeys);
+    double* s = (double*)malloc(sizeof(double) * (size_t)nkeys);
+    for (int t = 0; t < L; ++t) {
+      size_t off = (((size_t)b * Hkv + h) * Lcap + t) * D;
+      krow[t] = k_cache + off;
+      vrow[t] = v_cache + off;
+    }
+    for (int t = 0; t < depth; ++t) {
+      int node = path[depth - 1 - t]; /* root first */
+      size_t off = (((size_t)b * Hkv + h) * N + node) * D;
+      krow[L + t] = k_tree + off;
+      vrow[L + t] = v_tree + off;
+    }
+    const float* qi = q + (((size_t)b * N + i) * Hq + hq) * D;
+
+    /* pass 1: scores and their maximum */
+    double m = -INFINITY;
+    for (int t = 0; t < nkeys; ++t) {
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d) dot += (double)qi[d] * (double)krow[t][d];
+      s[t] = scale * dot;
+      if (s[t] > m) m = s[t];
+    }
+    /* pass 2: normaliser and weighted sum of values */
+    double den = 0.0;
+    for (int t = 0; t < nkeys; ++t) {
+      double e = exp(s[t] - m);
+      den += e;
+      for (int d = 0; d < D; ++d) o[d] += e * (double)vrow[t][d];
+    }
+    for (int d = 0; d < D; ++d) o[d] /= den;
+    lse[r] = m + log(den);
+    status[r] = ORC_OK;
+    free(path);
+    free(krow);
+    free(vrow);
+    free(s);
+  }
+}
+
+/* Writes path[b,k] (node at depth k, -1 after the end) for the path root->end
+ * and returns its length (end's depth + 1). */
+static int write_path(int N, const int32_t* par, int end, int32_t* path) {
+  int len = 0;
+  for (int j = end; j != -1; j = par[j]) ++len;
+  for (int k = 0; k < N; ++k) path[k] = -1;
+  int k = len - 1;
+  for (int j = end; j != -1; j = par[j]) path[k--] = j;
+  return len;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Greedy verification.  [SI] §4 "Token Tree Verification" and §6 (greedy    */
+/* verification emits exactly incremental decoding's tokens):                 */
+/*   amax[u] = argmax_v llm[b,u,v]  (fp32 compare, first index wins ties)     */
+/*   accepted(0); accepted(c) iff accepted(parent c) and tokens[c] ==          */
+/*                amax[parent c]                                               */
+/*   end d = deepest accepted node (lowest index on ties)                     */
+/*   path = root -> d; out_tokens = tokens of path[1..], then amax[d].        */
+/* ------------------------------------------------------------------------ */
+void orc_verify_greedy(int B, int N, int V, const int32_t* parents,
+                       const int32_t* tokens, const float* llm, int32_t* path,
+                       int32_t* path_len, int32_t* out_tokens,
+                       int32_t* status) {
+  int32_t* amax = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+  int32_t* dep = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+  char* acc = (char*)malloc((size_t)N);
+  for (int b = 0; b < B; ++b) {
+    const int32_t* par = parents + (size_t)b * N;
+    const int32_t* tok = tokens + (size_t)b * N;
+    int32_t* pb = path + (size_t)b * N;
+    int32_t* ob = out_tokens + (size_t)b * N;
+    for (int k = 0; k < N; ++k) { pb[k] = -1; ob[k] = -1; }
+    if (!tree_is_valid(N, par)) {
+      path_len[b] = 0;
+      status[b] = ORC_E_TREE;
+      continue;
+    }
+    for (int u = 0; u < N; ++u) {
+      const float* row = llm + ((size_t)b * N + u) * V;
+      int best = 0;
+      for (int v = 1; v < V; ++v)
+        if (row[v] > row[best]) best = v;
+      amax[u] = best;
+    }
+    acc[0] = 1;
+    dep[0] = 0;
+    for (int c = 1; c < N; ++c) {
+      dep[c] = dep[par[c]] + 1;
+      acc[c] = acc[par[c]] && tok[c] == amax[par[c]];
+    }
+    int end = 0;
+    for (int c = 1; c < N; ++c)
+      if (acc[c] && dep[c] > dep[end]) end = c;
+    int len = write_path(N, par, end, pb);
+    for (int k = 0; k + 1 < len; ++k) ob[k] = tok[pb[k + 1]];
+    ob[len - 1] = amax[end];
+    path_len[b] = len;
+    status[b] = ORC_OK;
+  }
+  free(amax);
+  free(dep);
+  free(acc);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stochastic verification: multi-step speculative sampling, [SI] §4 "Token   */
+/* Verification" (verifies across branches and keeps the LLM's distribution). */
+/* The page states the guarantee, not the arithmetic; the arithmetic below is  */
+/* this library's fixed reading of it (residual w with mass s, children in     */
+/* ascending node index, one caller-supplied uniform per tested child and one  */
+/* per request for the final sample, exact integer sums in 2^-40 units).       */
+/* ------------------------------------------------------------------------ */
+static uint64_t fx(float x) { return (uint64_t)((double)x * 1099511627776.0); }
+
+static float mass(const float* w, int V) {
+  uint64_t S = 0;
+  for (int v = 0; v < V; ++v) S += fx(w[v]);
+  return (float)((double)S * (1.0 / 1099511627776.0));
+}
+
+/* Inverse-CDF draw from the unnormalised w with uniform ub in [0,1). */
+static int sample_from(const float* w, int V, float ub) {
+  uint64_t S = 0;
+  for (int v = 0; v < V; ++v) S += fx(w[v]);
+  if (S == 0) {
+    int best = 0;
+    for (int v = 1; v < V; ++v)
+      if (w[v] > w[best]) best = v;
+    return best;
+  }
+  uint64_t R = (uint64_t)(ub * 16777216.0f); /* exact: scaling by 2^24 */
+  uint64_t hi = S >> 24, lo = S & 0xFFFFFFu;
+  uint64_t T = R * hi + ((R * lo) >> 24); /* floor(R*S / 2^24), no overflow */
+  uint64_t c = 0;
+  for (int v = 0; v < V; ++v) {
+    c += fx(w[v]);
+    if (c > T) return v;
+  }
+  return V - 1; /* unreachable: T < S */
+}
+
+void orc_verify_mss(int B, int N, int V, const int32_t* parents,
+                    const int32_t* tokens, const float* llm, const float* ssm,
+                    const float* u_accept, const float* u_bonus, int32_t* path,
+                    int32_t* path_len, int32_t* out_tokens, int32_t* status) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int b = 0; b < B; ++b) {
+    const int32_t* par = parents + (size_t)b * N;
+    const int32_t* tok = tokens + (size_t)b * N;
+    int32_t* pb = path + (size_t)b * N;
+    int32_t* ob = out_tokens + (size_t)b * N;
+    for (int k = 0; k < N; ++k) { pb[k] = -1; ob[k] = -1; }
+    if (!tree_is_valid(N, par)) {
+      path_len[b] = 0;
+      status[b] = ORC_E_TREE;
+      continue;
+    }
+    float* w = (float*)malloc(sizeof(float) * (size_t)V);
+    int u = 0;
+    for (;;) {
+      const float* p_u = llm + ((size_t)b * N + u) * V;
+      memcpy(w, p_u, sizeof(float) * (size_t)V);
+      float s = 1.0f;
+      int next = -1;
+      for (int c = u + 1; c < N; ++c) { /* children of u, ascending index */
+        if (par[c] != u) continue;
+        const float* qc = ssm + ((size_t)b * N + c) * V;
+        const int x = tok[c];
+        const float r = u_accept[(size_t)b * N + c];
+        const float lhs = (r * qc[x]) * s;
+        if (lhs < w[x]) { next = c; break; } /* accepted */
+        /* rejected: w <- max(w - s*q, 0), s <- its mass */
+        for (int v = 0; v < V; ++v) {
+          float d = fmaf(-s, qc[v], w[v]);
+          w[v] = d > 0.0f ? d : 0.0f;
+        }
+        s = mass(w, V);
+        if (s == 0.0f) { /* empty residual: stop, sample from p_u */
+          memcpy(w, p_u, sizeof(float) * (size_t)V);
+          break;
+        }
+      }
+      if (next < 0) break;
+      u = next;
+    }
+    const int bonus = sample_from(w, V, u_bonus[b]);
+    const int len = write_path(N, par, u, pb);
+    for (int k = 0; k + 1 < len; ++k) ob[k] = tok[pb[k + 1]];
+    ob[len - 1] = bonus;
+    path_len[b] = len;
+    status[b] = ORC_OK;
+    free(w);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* KV commit.  [SI] §4 "Tree-Based Parallel Decoding": verified and          */
+/* speculated tokens share one KV cache; the accepted path's rows are kept.   */
+/*   cache[b,h,L+j,:] = tree[b,h,path[b,j],:]  (j < path_len[b], every h)     */
+/*   new_len[b] = L + path_len[b]; committed_src[b,j] = path[b,j] or -1.      */
+/* Byte copies (elt = bytes per element).  A request whose L or path breaks   */
+/* the bounds is left untouched (status ORC_E_SHAPE, new_len = L).            */
+/* ------------------------------------------------------------------------ */
+void orc_kv_commit(int B, int N, int Hkv, int D, int elt, int Lcap, int Lmax,
+                   const void* k_tree, const void* v_tree, void* k_cache,
+                   void* v_cache, const int32_t* cache_len_in,
+                   int32_t* cache_len_out, const int32_t* path,
+                   const int32_t* path_len, int32_t* committed_src,
+                   int32_t* status) {
+  const size_t row = (size_t)D * elt;
+  for (int b = 0; b < B; ++b) {
+    const int L = cache_len_in[b];
+    const int n = path_len[b];
+    const int32_t* pb = path + (size_t)b * N;
+    int ok = L >= 0 && L <= Lmax && L <= Lcap && n >= 0 && n <= N &&
+             L + n <= Lcap;
+    for (int j = 0; ok && j < n; ++j)
+      if (pb[j] < 0 || pb[j] >= N) ok = 0;
+    for (int j = 0; j < N; ++j)
+      committed_src[(size_t)b * N + j] = (ok && j < n) ? pb[j] : -1;
+    if (!ok) {
+      cache_len_out[b] = L;
+      status[b] = ORC_E_SHAPE;
+      continue;
+    }
+    for (int h = 0; h < Hkv; ++h)
+      for (int j = 0; j < n; ++j) {
+        size_t src = (((size_t)b * Hkv + h) * N + pb[j]) * row;
+        size_t dst = (((size_t)b * Hkv + h) * Lcap + (L + j)) * row;
+        memcpy((char*)k_cache + dst, (const char*)k_tree + src, row);
+        memcpy((char*)v_cache + dst, (const char*)v_tree + src, row);
+      }
+    cache_len_out[b] = L + n;
+    status[b] = ORC_OK;
+  }
+}

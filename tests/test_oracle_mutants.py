@@ -1,0 +1,94 @@
+"""The pins catch plausible mistakes: each case below compiles a copy of
+oracle.c with one deliberate mistake (a dropped term, a wrong sign, index or
+comparison) and checks that at least the named pin fails on it.  The mistakes
+live only in temporary copies built on the CPU."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_attn as A
+import test_oracle_commit as C
+import test_oracle_greedy as G
+import test_oracle_mss as M
+import test_oracle_topology as T
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = [
+    # (id, original text, mistaken text, pin that must fail)
+    ("topology_self_bit", "for (int j = i; j != -1; j = par[j]) {\n        an[",
+     "for (int j = par[i]; j != -1; j = par[j]) {\n        an[",
+     lambda: T.test_matches_inverse_of_parent_matrix(8, 2)),
+    ("attn_dropped_scale", "s[t] = scale * dot;", "s[t] = dot;",
+     lambda: A.test_brute_force_sdpa({})),
+    ("attn_head_mapping", "const int h = hq / G;", "const int h = hq % Hkv;",
+     A.test_gqa_head_mapping),
+    ("attn_lse_missing_max", "lse[r] = m + log(den);", "lse[r] = log(den);",
+     A.test_single_key_returns_value_exactly),
+    ("attn_path_without_self", "for (int j = i; j != -1; j = par[j]) path[depth++] = j;",
+     "for (int j = par[i]; j != -1; j = par[j]) path[depth++] = j;",
+     lambda: A.test_brute_force_sdpa({})),
+    ("attn_prefix_row_shift", "* Lcap + t) * D;", "* Lcap + t + 1) * D;",
+     A.test_chain_is_causal_attention),
+    ("greedy_ties_to_highest", "if (row[v] > row[best]) best = v;",
+     "if (row[v] >= row[best]) best = v;", G.test_ties_go_to_lowest_index),
+    ("greedy_parent_not_required", "acc[c] = acc[par[c]] && tok[c] == amax[par[c]];",
+     "acc[c] = tok[c] == amax[par[c]];",
+     lambda: [G.test_random_small_trees(s) for s in range(6)]),
+    ("greedy_deepest_tie_to_highest", "if (acc[c] && dep[c] > dep[end]) end = c;",
+     "if (acc[c] && dep[c] >= dep[end]) end = c;",
+     G.test_deepest_accepted_node_wins_over_lower_index),
+    ("mss_residual_sign", "float d = fmaf(-s, qc[v], w[v]);",
+     "float d = fmaf(s, qc[v], w[v]);",
+     lambda: M.test_sample_after_rejection_is_normalised_residual(0)),
+    ("mss_mass_dropped_from_test", "const float lhs = (r * qc[x]) * s;",
+     "const float lhs = r * qc[x];", M.test_second_child_tested_against_residual),
+    ("mss_mass_not_updated", "s = mass(w, V);", "s = 1.0f;",
+     M.test_second_child_tested_against_residual),
+    ("mss_no_fallback_on_empty_residual",
+     "memcpy(w, p_u, sizeof(float) * (size_t)V);\n          break;", "break;",
+     M.test_half_q_empties_residual_and_falls_back_to_p),
+    ("mss_cdf_not_strict", "if (c > T) return v;", "if (c >= T) return v;",
+     M.test_inverse_cdf_end_points),
+    ("mss_accept_not_strict", "if (lhs < w[x]) { next = c; break; }",
+     "if (lhs <= w[x]) { next = c; break; }", M.test_inverse_cdf_end_points),
+    ("commit_off_by_one", "* Lcap + (L + j)) * row;", "* Lcap + (L + j + 1)) * row;",
+     C.test_full_chain_acceptance_appends_tree),
+    ("commit_length", "cache_len_out[b] = L + n;", "cache_len_out[b] = L + n - 1;",
+     C.test_full_chain_acceptance_appends_tree),
+    ("commit_reversed_path", "* N + pb[j]) * row;", "* N + pb[n - 1 - j]) * row;",
+     C.test_partial_path_and_canaries),
+]
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("mutants")
+
+
+@pytest.mark.parametrize("mid,orig,bad,pin", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pin_catches_mutant(mid, orig, bad, pin, mutant_dir):
+    src = open(SRC).read()
+    assert src.count(orig) == 1, "mutation site must be unique: %r" % orig
+    path = os.path.join(str(mutant_dir), mid + ".c")
+    open(path, "w").write(src.replace(orig, bad))
+    so = os.path.join(str(mutant_dir), "lib" + mid + ".so")
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp",
+                           "-fPIC", "-shared", "-o", so, path, "-lm"])
+    with oracle.use_library(so):
+        with pytest.raises(AssertionError):
+            pin()
+
+
+def test_unmutated_copy_passes_the_same_pins(mutant_dir):
+    so = os.path.join(str(mutant_dir), "libclean.so")
+    shutil.copy(SRC, os.path.join(str(mutant_dir), "clean.c"))
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp",
+                           "-fPIC", "-shared", "-o", so,
+                           os.path.join(str(mutant_dir), "clean.c"), "-lm"])
+    with oracle.use_library(so):
+        for _, _, _, pin in MUTANTS:
+            pin()
