@@ -1,0 +1,292 @@
+"""Benchmark of the tree-verification step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A step is one pass of the whole path over one batch of synthetic input:
+tree_attn (prefix + tree-masked attention of every node) -> tree_verify ->
+kv_commit, enqueued back to back on one stream with no host synchronisation.
+The default workload is c2, the LLaMA-7B-shaped layer (1 request, 64-node
+expansion tree, 32 heads of 128, prefix 512, vocabulary 32000, greedy).
+Inputs are resident in HBM before timing starts; each step reads a different
+copy of them (enough copies to exceed twice the 256 MB last-level cache), so
+the prefix KV and logits come from HBM, not from cache.
+
+Prints one JSON line: value = verified tree-node queries per second (B*N per
+step); roofline = tree_attn's algorithmic KV bytes per launch over its average
+launch time (HIP events on the launch stream); cpu_baseline = the CPU oracle
+timed on a bounded sample of the same workload (the oracle is test
+infrastructure; it is imported only here, for that leg).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import token_tree_verification_attn_amd as ttv  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MALL_BYTES = 256 << 20
+METRIC = "tree_attn KV HBM GB/s (% of peak) + verified tree-node queries/sec, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Inputs:
+    """One device copy of a workload's inputs plus preallocated outputs."""
+
+    def __init__(self, d, dev):
+        dt = torch.bfloat16 if d["dtype"] == "bf16" else torch.float32
+        f = lambda k: torch.from_numpy(np.ascontiguousarray(d[k])).to(dev)
+        self.q = f("q").to(dt)
+        self.k_cache = f("k_cache").to(dt)
+        self.v_cache = f("v_cache").to(dt)
+        self.k_tree = f("k_tree").to(dt)
+        self.v_tree = f("v_tree").to(dt)
+        self.parents, self.tokens, self.cache_len = f("parents"), f("tokens"), f("cache_len")
+        self.llm = f("llm")
+        self.ssm = f("ssm") if "ssm" in d else None
+        self.u_accept = f("u_accept") if "u_accept" in d else None
+        self.u_bonus = f("u_bonus") if "u_bonus" in d else None
+        B, N, Hq, D = self.q.shape
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+        self.st = torch.empty(B, dtype=torch.int32, device=dev)
+        self.path = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.plen = torch.empty(B, dtype=torch.int32, device=dev)
+        self.outt = torch.empty((B, N), dtype=torch.int32, device=dev)
+        self.len_out = torch.empty(B, dtype=torch.int32, device=dev)
+        self.src = torch.empty((B, N), dtype=torch.int32, device=dev)
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in
+                   (self.q, self.k_cache, self.v_cache, self.k_tree, self.v_tree, self.llm)
+                   + ((self.ssm,) if self.ssm is not None else ()))
+
+
+class Step:
+    def __init__(self, d, copies, dev):
+        self.d = d
+        self.copies = copies
+        self.mode = ttv.GREEDY if d["mode"] == "greedy" else ttv.STOCHASTIC
+        c = copies[0]
+        B, N, Hq, D = c.q.shape
+        dt = c.q.dtype
+        self.ws_attn = torch.empty(max(1, ttv.tree_attn_workspace_size(
+            dt, B, N, Hq, d["Hkv"], D, d["Lmax"])), dtype=torch.uint8, device=dev)
+        self.ws_ver = torch.empty(max(1, ttv.tree_verify_workspace_size(
+            self.mode, B, N, d["V"])), dtype=torch.uint8, device=dev)
+
+    def attn(self, c):
+        ttv.tree_attn(c.q, c.k_cache, c.v_cache, c.cache_len, c.k_tree, c.v_tree, c.parents,
+                      self.d["Lmax"], scale=self.d["scale"], out=c.out, lse=c.lse,
+                      dev_status=c.st, workspace=self.ws_attn)
+
+    def verify(self, c):
+        ttv.tree_verify(self.mode, c.parents, c.tokens, c.llm, c.ssm, c.u_accept, c.u_bonus,
+                        path=c.path, path_len=c.plen, out_tokens=c.outt, dev_status=c.st,
+                        workspace=self.ws_ver)
+
+    def commit(self, c):
+        # lengths go to a separate array, so repeated steps rewrite the same rows
+        ttv.kv_commit(c.k_tree, c.v_tree, c.k_cache, c.v_cache, c.cache_len, c.path, c.plen,
+                      self.d["Lmax"], cache_len_out=c.len_out, committed_src=c.src,
+                      dev_status=c.st)
+
+    def __call__(self, i):
+        c = self.copies[i % len(self.copies)]
+        self.attn(c)
+        self.verify(c)
+        self.commit(c)
+
+
+def timed(fn, n, stream):
+    """Average ms per call of fn(i), i = 0..n-1, from HIP events recorded on
+    the launch stream around the whole loop."""
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def tree_depths(par):
+    depth = np.zeros_like(par)
+    for i in range(1, par.shape[1]):
+        depth[:, i] = depth[np.arange(par.shape[0]), par[:, i]] + 1
+    return depth
+
+
+def attn_work(d):
+    """Algorithmic work of one tree_attn launch: bytes = every prefix and tree
+    K/V element read once, sum_b (L_b + N) * Hkv * D * 2 * elt; flops = 4 * D
+    per (query row, key it attends to), sum over rows of L_b + depth + 1."""
+    elt = 2 if d["dtype"] == "bf16" else 4
+    L = d["cache_len"].astype(np.int64)
+    N, Hkv, Hq, D = d["N"], d["Hkv"], d["Hq"], d["D"]
+    kv_bytes = int(((L + N) * Hkv * D * 2 * elt).sum())
+    keys = (L[:, None] + tree_depths(d["parents"]) + 1).astype(np.int64)  # [B, N]
+    flops = int(4 * D * Hq * keys.sum())
+    return kv_bytes, flops
+
+
+def source_hash():
+    """Hash of the attention kernel sources a stored counter profile belongs to."""
+    h = hashlib.sha256()
+    for f in ("attn.hip", "ttv_common.h", "api.cpp"):
+        h.update(open(os.path.join(ROOT, "token_tree_verification_attn_amd", "csrc", f),
+                      "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """HBM bytes per tree_attn launch from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel changed since."""
+    f = os.path.join(ROOT, "profiles", "tree_attn_%s_traffic.json" % workload)
+    if not os.path.exists(f):
+        return None
+    rec = json.load(open(f))
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(d, budget_s):
+    """The CPU oracle on a bounded sample of the same workload: full verify
+    and commit, and attention over a sample of query rows, extrapolated to
+    the whole step; reported in tree-node queries/s."""
+    import oracle
+    B, N, Hq = d["B"], d["N"], d["Hq"]
+    rows_all = oracle.all_rows(B, N, Hq)
+    rng = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    if d["mode"] == "greedy":
+        path, plen, _, _ = oracle.verify_greedy(d["parents"], d["tokens"], d["llm"])
+    else:
+        path, plen, _, _ = oracle.verify_mss(d["parents"], d["tokens"], d["llm"], d["ssm"],
+                                             d["u_accept"], d["u_bonus"])
+    t_verify = time.perf_counter() - t0
+    kc = d["k_cache"][:1]  # commit on request-0-sized copies keeps memory bounded
+    t0 = time.perf_counter()
+    oracle.kv_commit(d["k_tree"][:1], d["v_tree"][:1], kc, d["v_cache"][:1],
+                     d["cache_len"][:1], path[:1], plen[:1], d["Lmax"])
+    t_commit = (time.perf_counter() - t0) * B
+    # attention: grow the row sample until the time budget is spent
+    n, done, t_rows = 64, 0, 0.0
+    while True:
+        sel = rows_all[rng.choice(len(rows_all), size=min(n, len(rows_all)), replace=False)]
+        t0 = time.perf_counter()
+        oracle.tree_attn_rows(d["q"], d["k_cache"], d["v_cache"], d["cache_len"], d["k_tree"],
+                              d["v_tree"], d["parents"], d["scale"], sel)
+        t_rows += time.perf_counter() - t0
+        done += len(sel)
+        if t_rows + t_verify + t_commit >= budget_s or done >= len(rows_all):
+            break
+        n = min(len(rows_all), n * 2)
+    t_attn = t_rows / done * len(rows_all)
+    step_s = t_attn + t_verify + t_commit
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": B * N / step_s, "unit": "tree-node queries/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "verify on the whole batch, commit on request 0 (x B), attention on "
+                      "%d of %d query rows (sampled uniformly, time extrapolated); "
+                      "%.1f s of CPU work" % (done, len(rows_all), t_rows + t_verify + t_commit),
+            "step_ms": step_s * 1e3}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of CPU oracle work for the baseline (0 = skip)")
+    ap.add_argument("--warm", action="store_true",
+                    help="reuse one input copy (cache-resident) instead of rotating copies")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = synth.make(args.workload)
+    first = Inputs(d, dev)
+    per_copy = first.nbytes()
+    ncopies = 1 if args.warm else max(1, min(64, -(-2 * MALL_BYTES // per_copy)))
+    copies = [first] + [Inputs(d, dev) for _ in range(ncopies - 1)]
+    log("workload %s: %d input copies of %.1f MB" % (args.workload, ncopies, per_copy / 1e6))
+    step = Step(d, copies, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps, stream)
+    # per-entry-point times over the same rotation
+    ms_attn = timed(lambda i: step.attn(copies[i % ncopies]), args.steps, stream)
+    ms_verify = timed(lambda i: step.verify(copies[i % ncopies]), args.steps, stream)
+    ms_commit = timed(lambda i: step.commit(copies[i % ncopies]), args.steps, stream)
+    st = torch.stack([c.st for c in copies]).cpu()
+    assert int(st.abs().sum()) == 0, "a request was rejected: %s" % st
+
+    B, N = d["B"], d["N"]
+    kv_bytes, flops = attn_work(d)
+    kv_gbs = kv_bytes / (ms_attn * 1e-3) / 1e9
+    mfma_bound = args.workload == "c4"
+    if mfma_bound:
+        ach = flops / (ms_attn * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": kv_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kv_gbs / HBM_PEAK_GBS}
+    tr = stored_traffic(args.workload)
+    roof["traffic"] = tr
+    roof["kernel"] = "ttv_tree_attn (all kernels of one call)"
+    roof["per_launch_algorithmic"] = flops if mfma_bound else kv_bytes
+    roof["avg_launch_us"] = ms_attn * 1e3
+
+    res = {
+        "metric": METRIC,
+        "value": B * N / (ms_step * 1e-3),
+        "unit": "tree-node queries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": d["dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "N": N, "Hq": d["Hq"], "Hkv": d["Hkv"],
+                   "D": d["D"], "prefix": synth.WORKLOADS[args.workload].L, "V": d["V"],
+                   "verify": d["mode"], "input_copies": ncopies,
+                   "inputs": "rotated, HBM-resident" if ncopies > 1 else "one copy (warm)"},
+        "tree_attn_kv_gbs": kv_gbs,
+        "tree_attn_kv_frac_of_hbm_peak": kv_gbs / HBM_PEAK_GBS,
+        "stage_us": {"tree_attn": ms_attn * 1e3, "tree_verify": ms_verify * 1e3,
+                     "kv_commit": ms_commit * 1e3},
+        "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

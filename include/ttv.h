@@ -24,6 +24,8 @@
  *    `dev_status[B]` array (TTV_OK or the error code per request); the outputs
  *    of such a request are defined per entry point.
  *  - Tensors are dense, row-major, with the shapes written next to them.
+ *    Pointers to q, k_*, v_*, out (and llm, ssm) must be 16-byte aligned
+ *    (TTV_E_ALIGN otherwise); allocator-returned device memory always is.
  *  - Node 0 of every tree is its root; a tree is valid iff parents[0] == -1 and
  *    0 <= parents[i] < i for i >= 1 (any topological numbering; depth-first is
  *    one valid numbering but is not assumed).
@@ -49,7 +51,8 @@ enum {
   TTV_E_UNSUPPORTED = 4, /* N > 128, D not in {64,128}, Hq % Hkv != 0, ...      */
   TTV_E_WORKSPACE = 5,   /* workspace NULL or smaller than *_workspace_size    */
   TTV_E_LAUNCH = 6,      /* a kernel launch failed (hipGetLastError)           */
-  TTV_E_TREE = 7         /* device: malformed parents[] of one request         */
+  TTV_E_TREE = 7,        /* device: malformed parents[] of one request         */
+  TTV_E_ALIGN = 8        /* a tensor pointer is not 16-byte aligned            */
 };
 
 typedef int32_t ttv_dtype;
@@ -119,11 +122,13 @@ ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents,
  *               (may be NULL when that size is 0).  Its contents need no
  *               initialisation and are garbage afterwards.
  *   rows_per_block, chunk_keys  launch tuning: 0 = automatic; otherwise query
- *               rows per workgroup (16, 32, 64, 128 or 256 on the matrix-core
- *               path) and prefix keys per workgroup (a positive multiple of
- *               64).  The same values must be given to the size query.
+ *               rows per workgroup (64, 128 or 256 on the matrix-core path,
+ *               which serves bf16 with N*Hq/Hkv >= 16; 16 on the FMA path)
+ *               and prefix keys per workgroup (a positive multiple of 64);
+ *               other values give TTV_E_UNSUPPORTED.  The same values must be
+ *               given to the size query.
  * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE, TTV_E_UNSUPPORTED,
- *         TTV_E_WORKSPACE, TTV_E_LAUNCH.
+ *         TTV_E_ALIGN, TTV_E_WORKSPACE, TTV_E_LAUNCH.
  */
 ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq,
                          int32_t Hkv, int32_t D, float scale, const void* q,
@@ -180,11 +185,14 @@ size_t ttv_tree_attn_workspace_size(ttv_dtype dt, int32_t B, int32_t N,
  *            -1 after the end.   path_len int32 [B]: accepted nodes + 1 (>= 1).
  *   out_tokens int32 [B,N]: tokens of path[1..], then the bonus token, -1
  *            after (path_len entries in all).
- *   A malformed tree gives path_len 0 and -1 everywhere, dev_status TTV_E_TREE.
+ *   A malformed tree gives path_len 0 and -1 everywhere, dev_status TTV_E_TREE;
+ *   in stochastic mode a non-root token outside [0,V) does the same with
+ *   TTV_E_SHAPE.  Stochastic mode needs V <= 36864 (the residual lives in
+ *   on-chip memory), else TTV_E_UNSUPPORTED.
  *   workspace >= ttv_tree_verify_workspace_size(...) bytes (contents need no
  *            initialisation).
  * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE (mode), TTV_E_UNSUPPORTED,
- *         TTV_E_WORKSPACE, TTV_E_LAUNCH.
+ *         TTV_E_ALIGN, TTV_E_WORKSPACE, TTV_E_LAUNCH.
  */
 ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N,
                            int32_t V, const int32_t* parents,
@@ -216,7 +224,8 @@ size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B,
  *   dev_status   nullable; TTV_E_SHAPE when L < 0, L > Lmax, n outside
  *                [0,N] or a path entry outside [0,N): nothing of that request
  *                is written except cache_len_out[b] = L (and -1 sources).
- * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE, TTV_E_UNSUPPORTED, TTV_E_LAUNCH.
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE, TTV_E_UNSUPPORTED,
+ *         TTV_E_ALIGN, TTV_E_LAUNCH.
  */
 ttv_status ttv_kv_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv,
                          int32_t D, int32_t Lcap, const void* k_tree,

@@ -192,7 +192,6 @@ def verify_mss(parents, tokens, llm, ssm, u_accept, u_bonus):
     V = p.shape[2]
     assert p.shape == (B, N, V) and q.shape == p.shape
     assert ua.shape == (B, N) and ub.shape == (B,) and tok.shape == (B, N)
-    assert tok.min(initial=0) >= 0 and tok.max(initial=0) < V
     path = np.empty((B, N), np.int32)
     plen = np.empty(B, np.int32)
     outt = np.empty((B, N), np.int32)

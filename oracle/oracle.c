@@ -267,6 +267,14 @@ void orc_verify_mss(int B, int N, int V, const int32_t* parents,
       status[b] = ORC_E_TREE;
       continue;
     }
+    int tokens_ok = 1; /* every drafted token must index the vocabulary */
+    for (int c = 1; c < N; ++c)
+      if (tok[c] < 0 || tok[c] >= V) tokens_ok = 0;
+    if (!tokens_ok) {
+      path_len[b] = 0;
+      status[b] = ORC_E_SHAPE;
+      continue;
+    }
     float* w = (float*)malloc(sizeof(float) * (size_t)V);
     int u = 0;
     for (;;) {

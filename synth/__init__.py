@@ -262,7 +262,8 @@ def make(s: Union[str, Spec], parents: Optional[np.ndarray] = None,
     for b in range(B):
         if parents is not None:
             par[b] = parents[b]
-            tok[b] = sibling_distinct_tokens(rk, par[b], V) if V > 1 else 0
+            if s.mode != "stochastic":
+                tok[b] = sibling_distinct_tokens(rk, par[b], V)
             continue
         if s.tree == "random":
             par[b] = random_tree(rt, N, s.dmax, s.max_children)
@@ -277,6 +278,8 @@ def make(s: Union[str, Spec], parents: Optional[np.ndarray] = None,
             continue
         else:
             raise ValueError(s.tree)
+        if s.mode == "stochastic":
+            continue  # drawn from the ssm rows below
         tok[b] = topk_tokens(rk, par[b], V) if s.tree == "expansion" else \
             sibling_distinct_tokens(rk, par[b], V)
     out.update(parents=par, tokens=tok)

@@ -1,0 +1,157 @@
+"""The C-ABI library loads without a GPU, exports every function include/ttv.h
+declares, and rejects bad arguments on the host before any HIP call (so each
+error status below is produced here, on a machine with no GPU).  Fake device
+pointers are used only in calls that must fail validation."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import token_tree_verification_attn_amd as ttv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttv.h")
+A = 0x10000          # a 16-byte aligned fake pointer (never dereferenced)
+MIS = 0x10008        # a misaligned fake pointer
+SZ_ERR = ctypes.c_size_t(-1).value
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(ttv_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_attn_workspace_size",
+              "ttv_tree_verify", "ttv_tree_verify_workspace_size", "ttv_kv_commit",
+              "ttv_status_string", "ttv_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ttv.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ttv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ttv_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+    # the C ABI is the only exported interface of the library
+    assert all(n.startswith("ttv_") for n in exported)
+
+
+def test_library_links_no_torch():
+    out = subprocess.run(["ldd", ttv.LIB_PATH], capture_output=True, text=True).stdout
+    assert "torch" not in out and "python" not in out
+
+
+def test_status_strings():
+    for s in range(9):
+        assert ttv.status_string(s) != "unknown status"
+    assert ttv.status_string(99) == "unknown status"
+
+
+def attn(**kw):
+    args = dict(dt=1, B=1, N=8, Hq=4, Hkv=2, D=64, scale=0.125, q=A, kc=A, vc=A, Lcap=128,
+                cl=A, Lmax=100, kt=A, vt=A, par=A, out=A, lse=None, st=None, ws=A,
+                wsb=1 << 30, rpb=0, ck=0)
+    args.update(kw)
+    return ttv.lib().ttv_tree_attn(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), ttv.E_DTYPE),
+    (dict(q=None), ttv.E_NULL), (dict(kc=None), ttv.E_NULL), (dict(par=None), ttv.E_NULL),
+    (dict(out=None), ttv.E_NULL), (dict(cl=None), ttv.E_NULL),
+    (dict(B=0), ttv.E_SHAPE), (dict(N=0), ttv.E_SHAPE), (dict(Lmax=129), ttv.E_SHAPE),
+    (dict(Lmax=-1), ttv.E_SHAPE), (dict(scale=float("nan")), ttv.E_SHAPE),
+    (dict(N=129), ttv.E_UNSUPPORTED), (dict(D=96), ttv.E_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), ttv.E_UNSUPPORTED), (dict(rpb=96), ttv.E_UNSUPPORTED),
+    (dict(ck=100), ttv.E_UNSUPPORTED), (dict(dt=0, rpb=64), ttv.E_UNSUPPORTED),
+    (dict(q=MIS), ttv.E_ALIGN), (dict(vt=MIS), ttv.E_ALIGN), (dict(out=MIS), ttv.E_ALIGN),
+    (dict(ws=None, ck=64), ttv.E_WORKSPACE), (dict(wsb=16, ck=64), ttv.E_WORKSPACE),
+])
+def test_tree_attn_host_validation(kw, status):
+    assert attn(**kw) == status
+
+
+def test_tree_attn_workspace_size_matches_plan():
+    f = ttv.lib().ttv_tree_attn_workspace_size
+    assert f(1, 1, 8, 4, 2, 64, 100, 0, 64) == 1 * 2 * 2 * 16 * 66 * 4   # 2 chunks of 64
+    assert f(1, 1, 8, 4, 2, 64, 64, 0, 64) == 0                          # one chunk
+    assert f(1, 1, 129, 4, 2, 64, 64, 0, 0) == SZ_ERR
+    assert f(9, 1, 8, 4, 2, 64, 64, 0, 0) == SZ_ERR
+    # the binding allocates exactly that much
+    assert ttv.tree_attn_workspace_size(torch.bfloat16, 1, 8, 4, 2, 64, 100, 0, 64) == 16896
+
+
+def verify(**kw):
+    args = dict(mode=0, B=2, N=8, V=100, par=A, tok=A, llm=A, ssm=None, ua=None, ub=None,
+                path=A, plen=A, outt=A, st=None, ws=A, wsb=1 << 30)
+    args.update(kw)
+    return ttv.lib().ttv_tree_verify(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mode=2), ttv.E_DTYPE),
+    (dict(par=None), ttv.E_NULL), (dict(llm=None), ttv.E_NULL), (dict(path=None), ttv.E_NULL),
+    (dict(mode=1), ttv.E_NULL), (dict(mode=1, ssm=A, ua=A), ttv.E_NULL),
+    (dict(B=0), ttv.E_SHAPE), (dict(V=0), ttv.E_SHAPE),
+    (dict(N=200), ttv.E_UNSUPPORTED),
+    (dict(mode=1, ssm=A, ua=A, ub=A, V=40000), ttv.E_UNSUPPORTED),
+    (dict(llm=MIS), ttv.E_ALIGN), (dict(mode=1, ssm=MIS, ua=A, ub=A), ttv.E_ALIGN),
+    (dict(ws=None), ttv.E_WORKSPACE), (dict(wsb=8), ttv.E_WORKSPACE),
+])
+def test_tree_verify_host_validation(kw, status):
+    assert verify(**kw) == status
+
+
+def test_tree_verify_workspace_size():
+    f = ttv.lib().ttv_tree_verify_workspace_size
+    assert f(1, 4, 64, 32000) == 0           # stochastic needs none
+    assert f(1, 4, 64, 40000) == SZ_ERR      # vocabulary too large for on-chip residual
+    assert f(0, 1, 64, 32000) > 0
+    assert f(0, 1, 200, 32000) == SZ_ERR
+    assert f(5, 1, 8, 32) == SZ_ERR
+
+
+def commit(**kw):
+    args = dict(dt=1, B=2, N=8, Hkv=2, D=64, Lcap=100, kt=A, vt=A, kc=A, vc=A, cli=A, clo=A,
+                Lmax=50, path=A, plen=A, src=None, st=None)
+    args.update(kw)
+    return ttv.lib().ttv_kv_commit(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), ttv.E_DTYPE),
+    (dict(kt=None), ttv.E_NULL), (dict(clo=None), ttv.E_NULL), (dict(plen=None), ttv.E_NULL),
+    (dict(B=0), ttv.E_SHAPE), (dict(Lmax=93), ttv.E_SHAPE), (dict(Lcap=-1), ttv.E_SHAPE),
+    (dict(N=129, Lcap=1000), ttv.E_UNSUPPORTED), (dict(D=32), ttv.E_UNSUPPORTED),
+    (dict(kc=MIS), ttv.E_ALIGN),
+])
+def test_kv_commit_host_validation(kw, status):
+    assert commit(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(par=None), ttv.E_NULL), (dict(B=0), ttv.E_SHAPE), (dict(N=129), ttv.E_UNSUPPORTED),
+])
+def test_tree_topology_host_validation(kw, status):
+    args = dict(B=1, N=8, par=A, anc=None, depth=None, st=None)
+    args.update(kw)
+    assert ttv.lib().ttv_tree_topology(*args.values(), None) == status
+
+
+def test_binding_checks_tensors_before_calling():
+    q = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(ValueError):
+        ttv.tree_attn(q, torch.zeros(1, 1, 8, 64), torch.zeros(1, 1, 8, 64),
+                      torch.zeros(1, dtype=torch.int32), torch.zeros(1, 1, 4, 64),
+                      torch.zeros(1, 1, 5, 64), torch.zeros(1, 4, dtype=torch.int32), Lmax=4)
+    with pytest.raises(TypeError):
+        ttv.tree_verify(ttv.GREEDY, torch.zeros(1, 4, dtype=torch.int64),
+                        torch.zeros(1, 4, dtype=torch.int32), torch.zeros(1, 4, 10))

@@ -1,0 +1,128 @@
+"""GPU tree verification vs the oracle, bit for bit (paths, lengths, tokens,
+statuses): greedy on the greedy workloads and edge cases (two-word trees,
+ties, repeated sibling tokens, vocabularies that are not a multiple of 4),
+multi-step speculative sampling on the stochastic workload and edge cases
+(p == q, an emptied residual, many rejections, out-of-range tokens)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import token_tree_verification_attn_amd as ttv
+from gpu_case import announce, check_verify, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_greedy_workloads(name):
+    announce("verify greedy %s" % name)
+    check_verify(synth.make(name, with_kv=False))
+
+
+def greedy_spec(**kw):
+    base = dict(name="g", B=6, N=40, Hq=1, Hkv=1, D=64, L=0, dtype="f32", V=1000,
+                mode="greedy", tree="random", seed=99, dmax=12, max_children=4,
+                logit_sigma=1.0, plant=0.9)
+    base.update(kw)
+    return synth.Spec(**base)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(), dict(N=128, dmax=127, max_children=2, seed=5), dict(N=128, tree="chain", plant=1.0),
+    dict(N=65, tree="star"), dict(N=1), dict(V=30, seed=7), dict(V=4099, seed=8),
+    dict(N=64, B=33, plant=0.0, V=5), dict(V=130000, B=2, N=8, seed=9),
+])
+def test_greedy_edge_cases(kw):
+    announce("verify greedy edge %s" % kw)
+    check_verify(synth.make(greedy_spec(**kw), with_kv=False))
+
+
+def test_greedy_ties_and_repeated_siblings():
+    announce("verify greedy ties")
+    B, N, V = 3, 6, 16
+    par = np.tile(np.array([-1, 0, 0, 1, 2, 2], np.int32), (B, 1))
+    tok = np.tile(np.array([0, 5, 5, 7, 7, 9], np.int32), (B, 1))
+    llm = np.zeros((B, N, V), np.float32)
+    llm[:, 0, 5] = 1.0                 # both children (token 5) accepted
+    llm[0, 1, 7] = 1.0                 # request 0: node 3 accepted (depth 2)
+    llm[1, 2, [7, 9]] = 1.0            # request 1: tie 7 vs 9 -> 7: node 4 accepted
+    d = dict(mode="greedy", parents=par, tokens=tok, llm=llm, B=B)
+    check_verify(d)
+
+
+def test_greedy_malformed():
+    announce("verify greedy malformed")
+    d = synth.make(greedy_spec(B=4), with_kv=False)
+    d["parents"] = d["parents"].copy()
+    d["parents"][2, 0] = 3
+    check_verify(d)
+
+
+def test_stochastic_workload():
+    announce("verify stochastic c5")
+    d = synth.make("c5", with_kv=False)
+    _, plen, _, _ = check_verify(d)
+    assert plen.max().item() >= 2
+
+
+def mss_spec(**kw):
+    base = dict(name="s", B=16, N=24, Hq=1, Hkv=1, D=64, L=0, dtype="f32", V=50,
+                mode="stochastic", tree="random", seed=123, dmax=6, max_children=4,
+                temperature=0.8, prob_sigma=1.0)
+    base.update(kw)
+    return synth.Spec(**base)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(), dict(V=7, seed=1), dict(N=128, dmax=127, max_children=3, seed=2),
+    dict(N=1), dict(V=32000, B=4, N=16, seed=3), dict(V=36864, B=2, N=8, seed=4),
+    dict(V=33, prob_sigma=4.0, seed=5), dict(N=65, tree="star", V=20, seed=6),
+])
+def test_stochastic_edge_cases(kw):
+    announce("verify stochastic edge %s" % kw)
+    check_verify(synth.make(mss_spec(**kw), with_kv=False))
+
+
+def test_stochastic_p_equals_q_chain128():
+    announce("verify stochastic p == q chain 128")
+    d = synth.make(mss_spec(B=3, N=128, tree="chain", V=40), with_kv=False)
+    d["ssm"] = d["ssm"].copy()
+    d["ssm"][:, 1:] = d["llm"][:, :-1]
+    _, plen, _, _ = check_verify(d)
+    assert torch.all(plen == 128)
+
+
+def test_stochastic_empty_residual():
+    announce("verify stochastic emptied residual")
+    # root's p = half of its first child's q: that child is accepted iff
+    # r < 1/2, and its rejection leaves an empty residual (max(q/2 - q, 0))
+    d = synth.make(mss_spec(B=32, N=6, V=20, tree="star", seed=11), with_kv=False)
+    d["llm"] = d["llm"].copy()
+    d["llm"][:, 0] = 0.5 * d["ssm"][:, 1]
+    _, plen, _, _ = check_verify(d)
+    assert 0 < int((plen == 1).sum()) < 32
+
+
+def test_stochastic_bad_tokens_and_tree():
+    announce("verify stochastic bad inputs")
+    d = synth.make(mss_spec(B=4), with_kv=False)
+    d["tokens"] = d["tokens"].copy()
+    d["parents"] = d["parents"].copy()
+    d["tokens"][1, 3] = d["V"]
+    d["tokens"][2, 5] = -1
+    d["parents"][3, 2] = 2
+    _, _, _, st = check_verify(d)
+    assert list(st.cpu().numpy()) == [0, 2, 2, 7]
+
+
+def test_verify_is_deterministic():
+    announce("verify determinism")
+    d = synth.make("c5", with_kv=False)
+    t = to_dev(d)
+    a = ttv.tree_verify(ttv.STOCHASTIC, t["parents"], t["tokens"], t["llm"], t["ssm"],
+                        t["u_accept"], t["u_bonus"])
+    b = ttv.tree_verify(ttv.STOCHASTIC, t["parents"], t["tokens"], t["llm"], t["ssm"],
+                        t["u_accept"], t["u_bonus"])
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -270,3 +270,6 @@ def test_malformed_tree_and_determinism():
     path, plen, outt, st = a
     assert st[2] == oracle.E_TREE and plen[2] == 0 and np.all(path[2] == -1)
     assert np.all(st[[0, 1, 3]] == 0)
+    tok[3, 5] = V          # a drafted token outside the vocabulary
+    path, plen, outt, st = oracle.verify_mss(par, tok, llm, ssm, ua, ub)
+    assert st[3] == oracle.E_SHAPE and plen[3] == 0 and np.all(outt[3] == -1)

@@ -1,0 +1,253 @@
+"""token_tree_verification_attn_amd -- Python binding of libttv.
+
+libttv is the C-ABI library (include/ttv.h) that runs the tree-based parallel
+decoding step of tree speculative inference on AMD MI355X (gfx950):
+
+* ``tree_topology``  ancestor bitsets / depths of each request's token tree
+* ``tree_attn``      attention of every tree node over prefix KV + its root path
+* ``tree_verify``    greedy or multi-step-speculative-sampling acceptance
+* ``kv_commit``      accepted path's KV rows appended to the contiguous cache
+
+This module only marshals arguments: it checks tensor dtypes, shapes, devices
+and contiguity, allocates outputs with torch, and passes raw device pointers
+plus torch's current HIP stream to the library.  Every step of the path runs in
+the library's kernels; there is no fallback.  Importing works anywhere; the
+first call raises ``LibraryNotBuilt`` if libttv.so is missing and ``TTVError``
+for a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["tree_topology", "tree_attn", "tree_verify", "kv_commit",
+           "tree_attn_workspace_size", "tree_verify_workspace_size", "status_string",
+           "TTVError", "LibraryNotBuilt", "lib", "LIB_PATH", "GREEDY", "STOCHASTIC"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttv.so")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH, E_TREE, E_ALIGN = range(9)
+F32, BF16 = 0, 1
+GREEDY, STOCHASTIC = 0, 1
+MAX_NODES = 128
+
+
+class LibraryNotBuilt(ImportError):
+    pass
+
+
+class TTVError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, status_string(status), status))
+
+
+_lib = None
+_P, _I, _F, _SZ, _U64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t,
+                         ctypes.c_uint64)
+
+
+def lib():
+    """The loaded libttv.so (loaded on first use)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryNotBuilt(
+                "libttv.so is not built; run `python -m token_tree_verification_attn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ttv_status_string.argtypes = [_I]
+        L.ttv_status_string.restype = ctypes.c_char_p
+        L.ttv_version.restype = _I
+        L.ttv_tree_topology.argtypes = [_I, _I, _P, _P, _P, _P, _P]
+        L.ttv_tree_attn.argtypes = [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P, _I, _P, _P,
+                                    _P, _P, _P, _P, _P, _SZ, _I, _I, _P]
+        L.ttv_tree_attn_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I]
+        L.ttv_tree_attn_workspace_size.restype = _SZ
+        L.ttv_tree_verify.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _SZ, _P]
+        L.ttv_tree_verify_workspace_size.argtypes = [_I, _I, _I, _I]
+        L.ttv_tree_verify_workspace_size.restype = _SZ
+        L.ttv_kv_commit.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                                    _P, _P, _P]
+        for f in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_verify", "ttv_kv_commit"):
+            getattr(L, f).restype = _I
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().ttv_status_string(int(s)).decode()
+
+
+def _check(fn, st):
+    if st != OK:
+        raise TTVError(fn, st)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _dt(dtype):
+    if dtype == torch.float32:
+        return F32
+    if dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % dtype)
+
+
+def tree_topology(parents: torch.Tensor, dev_status: Optional[torch.Tensor] = None):
+    """Ancestor bitsets and depths; returns (anc int64 [B,N,W] holding the uint64
+    words, depth int32 [B,N], dev_status int32 [B])."""
+    B, N = parents.shape
+    dev = parents.device
+    _need(parents, "parents", torch.int32, (B, N), dev)
+    W = (N + 63) // 64
+    anc = torch.empty((B, N, W), dtype=torch.int64, device=dev)
+    depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if dev_status is None:
+        dev_status = torch.empty(B, dtype=torch.int32, device=dev)
+    _check("ttv_tree_topology", lib().ttv_tree_topology(B, N, _ptr(parents), _ptr(anc),
+                                                        _ptr(depth), _ptr(dev_status),
+                                                        _stream(dev)))
+    return anc, depth, dev_status
+
+
+def tree_attn_workspace_size(dtype, B, N, Hq, Hkv, D, Lmax, rows_per_block=0, chunk_keys=0):
+    n = lib().ttv_tree_attn_workspace_size(_dt(dtype), B, N, Hq, Hkv, D, Lmax, rows_per_block,
+                                           chunk_keys)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("unsupported tree_attn sizes")
+    return n
+
+
+def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int,
+              scale: Optional[float] = None, out=None, lse=None, want_lse: bool = True,
+              dev_status=None, workspace=None, rows_per_block: int = 0, chunk_keys: int = 0):
+    """Tree attention for every node; returns (out [B,N,Hq,D], lse [B,N,Hq] or None,
+    dev_status [B])."""
+    B, N, Hq, D = q.shape
+    Hkv, Lcap = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    dt = q.dtype
+    _need(q, "q", dt, (B, N, Hq, D), dev)
+    _need(k_cache, "k_cache", dt, (B, Hkv, Lcap, D), dev)
+    _need(v_cache, "v_cache", dt, (B, Hkv, Lcap, D), dev)
+    _need(k_tree, "k_tree", dt, (B, Hkv, N, D), dev)
+    _need(v_tree, "v_tree", dt, (B, Hkv, N, D), dev)
+    _need(cache_len, "cache_len", torch.int32, (B,), dev)
+    _need(parents, "parents", torch.int32, (B, N), dev)
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, N, Hq, D), dtype=dt, device=dev)
+    _need(out, "out", dt, (B, N, Hq, D), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, N, Hq), dev)
+    if dev_status is None:
+        dev_status = torch.empty(B, dtype=torch.int32, device=dev)
+    nbytes = tree_attn_workspace_size(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ttv_tree_attn(_dt(dt), B, N, Hq, Hkv, D, float(scale), _ptr(q), _ptr(k_cache),
+                             _ptr(v_cache), Lcap, _ptr(cache_len), int(Lmax), _ptr(k_tree),
+                             _ptr(v_tree), _ptr(parents), _ptr(out), _ptr(lse),
+                             _ptr(dev_status), _ptr(workspace), wsb, rows_per_block,
+                             chunk_keys, _stream(dev))
+    _check("ttv_tree_attn", st)
+    return out, lse, dev_status
+
+
+def tree_verify_workspace_size(mode, B, N, V):
+    n = lib().ttv_tree_verify_workspace_size(mode, B, N, V)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("unsupported tree_verify sizes")
+    return n
+
+
+def tree_verify(mode: int, parents, tokens, llm, ssm=None, u_accept=None, u_bonus=None,
+                path=None, path_len=None, out_tokens=None, dev_status=None, workspace=None):
+    """Greedy (mode GREEDY, llm = logits) or multi-step speculative sampling
+    (mode STOCHASTIC, llm/ssm = probabilities, caller's uniforms).  Returns
+    (path [B,N], path_len [B], out_tokens [B,N], dev_status [B])."""
+    B, N = parents.shape
+    V = llm.shape[2]
+    dev = parents.device
+    _need(parents, "parents", torch.int32, (B, N), dev)
+    _need(tokens, "tokens", torch.int32, (B, N), dev)
+    _need(llm, "llm", torch.float32, (B, N, V), dev)
+    if mode == STOCHASTIC:
+        _need(ssm, "ssm", torch.float32, (B, N, V), dev)
+        _need(u_accept, "u_accept", torch.float32, (B, N), dev)
+        _need(u_bonus, "u_bonus", torch.float32, (B,), dev)
+    if path is None:
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if dev_status is None:
+        dev_status = torch.empty(B, dtype=torch.int32, device=dev)
+    nbytes = tree_verify_workspace_size(mode, B, N, V)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ttv_tree_verify(mode, B, N, V, _ptr(parents), _ptr(tokens), _ptr(llm), _ptr(ssm),
+                               _ptr(u_accept), _ptr(u_bonus), _ptr(path), _ptr(path_len),
+                               _ptr(out_tokens), _ptr(dev_status), _ptr(workspace), wsb,
+                               _stream(dev))
+    _check("ttv_tree_verify", st)
+    return path, path_len, out_tokens, dev_status
+
+
+def kv_commit(k_tree, v_tree, k_cache, v_cache, cache_len_in, path, path_len, Lmax: int,
+              cache_len_out=None, committed_src=None, want_src: bool = True, dev_status=None):
+    """Append the accepted path's KV rows to the cache in place.  Returns
+    (cache_len_out [B], committed_src [B,N] or None, dev_status [B])."""
+    B, Hkv, N, D = k_tree.shape
+    Lcap = k_cache.shape[2]
+    dev = k_tree.device
+    dt = k_tree.dtype
+    _need(k_tree, "k_tree", dt, (B, Hkv, N, D), dev)
+    _need(v_tree, "v_tree", dt, (B, Hkv, N, D), dev)
+    _need(k_cache, "k_cache", dt, (B, Hkv, Lcap, D), dev)
+    _need(v_cache, "v_cache", dt, (B, Hkv, Lcap, D), dev)
+    _need(cache_len_in, "cache_len_in", torch.int32, (B,), dev)
+    _need(path, "path", torch.int32, (B, N), dev)
+    _need(path_len, "path_len", torch.int32, (B,), dev)
+    if cache_len_out is None:
+        cache_len_out = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(cache_len_out, "cache_len_out", torch.int32, (B,), dev)
+    if committed_src is None and want_src:
+        committed_src = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if dev_status is None:
+        dev_status = torch.empty(B, dtype=torch.int32, device=dev)
+    st = lib().ttv_kv_commit(_dt(dt), B, N, Hkv, D, Lcap, _ptr(k_tree), _ptr(v_tree),
+                             _ptr(k_cache), _ptr(v_cache), _ptr(cache_len_in),
+                             _ptr(cache_len_out), int(Lmax), _ptr(path), _ptr(path_len),
+                             _ptr(committed_src), _ptr(dev_status), _stream(dev))
+    _check("ttv_kv_commit", st)
+    return cache_len_out, committed_src, dev_status

@@ -1,0 +1,226 @@
+// api.cpp -- the C ABI of libttv (declared in include/ttv.h): argument
+// validation (before any HIP call), launch plans, launches.  No allocation,
+// no global state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "launch.h"
+#include "ttv.h"
+
+using namespace ttv;
+
+namespace {
+
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+// Launch plan of ttv_tree_attn; returns TTV_OK or the status the call gives.
+ttv_status attn_plan(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, int Lmax,
+                     int rpb_hint, int chunk_hint, AttnPlan* p) {
+  if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
+  if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || D < 1 || Lmax < 0) return TTV_E_SHAPE;
+  if (N > TTV_MAX_NODES || (D != 64 && D != 128) || Hq % Hkv != 0) return TTV_E_UNSUPPORTED;
+  if (rpb_hint < 0 || chunk_hint < 0 || chunk_hint % 64 != 0) return TTV_E_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  const long R = (long)N * G;
+  if (R > (1L << 24)) return TTV_E_UNSUPPORTED;
+  p->rows = (int)R;
+  p->mfma = dt == TTV_BF16 && R >= 16;
+  const long pairs = (long)B * Hkv;
+  if (pairs > kMaxGridYZ) return TTV_E_UNSUPPORTED;
+  if (p->mfma) {
+    if (rpb_hint) {
+      if (rpb_hint != 64 && rpb_hint != 128 && rpb_hint != 256) return TTV_E_UNSUPPORTED;
+      p->rows_per_block = rpb_hint;
+    } else {
+      // widest row block that R fills, narrowed until the launch has ~2
+      // workgroups per compute unit before any KV split is considered
+      int rb = R >= 128 ? 128 : 64;
+      while (rb > 64 && pairs * ceil_div(R, rb) < 512) rb /= 2;
+      p->rows_per_block = rb;
+    }
+  } else {
+    if (rpb_hint && rpb_hint != 16) return TTV_E_UNSUPPORTED;
+    p->rows_per_block = 16;
+  }
+  p->row_blocks = ceil_div(R, p->rows_per_block);
+  if (p->row_blocks > kMaxGridYZ) return TTV_E_UNSUPPORTED;
+  const long units = pairs * p->row_blocks;
+  int chunk;
+  if (chunk_hint) {
+    chunk = chunk_hint;
+  } else {
+    const long want = (512 + units - 1) / units;  // chunks per unit for ~512 workgroups
+    long c = want > 1 ? (Lmax + want - 1) / want : Lmax;
+    c = (c + 63) / 64 * 64;
+    if (c < 256) c = 256;
+    chunk = (int)c;
+  }
+  p->chunk_keys = chunk;
+  p->chunks = Lmax > 0 ? ceil_div(Lmax, chunk) : 1;
+  if (p->chunks < 1) p->chunks = 1;
+  p->ws_bytes = p->chunks > 1 ? (size_t)pairs * p->chunks * R * (size_t)(D + 2) * sizeof(float) : 0;
+  return TTV_OK;
+}
+
+ttv_status launch_status(hipError_t e) { return e == hipSuccess ? TTV_OK : TTV_E_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ttv_status_string(ttv_status s) {
+  switch (s) {
+    case TTV_OK: return "ok";
+    case TTV_E_NULL: return "null pointer";
+    case TTV_E_SHAPE: return "bad shape or size";
+    case TTV_E_DTYPE: return "bad dtype or mode";
+    case TTV_E_UNSUPPORTED: return "unsupported size or option";
+    case TTV_E_WORKSPACE: return "workspace missing or too small";
+    case TTV_E_LAUNCH: return "kernel launch failed";
+    case TTV_E_TREE: return "malformed token tree";
+    case TTV_E_ALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int32_t ttv_version(void) { return 100; }
+
+ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents, uint64_t* anc_out,
+                             int32_t* depth_out, int32_t* dev_status, void* stream) {
+  if (!parents) return TTV_E_NULL;
+  if (B < 1 || N < 1) return TTV_E_SHAPE;
+  if (N > TTV_MAX_NODES) return TTV_E_UNSUPPORTED;
+  return launch_status(launch_topology(B, N, parents, anc_out, depth_out, dev_status,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t ttv_tree_attn_workspace_size(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq,
+                                    int32_t Hkv, int32_t D, int32_t Lmax,
+                                    int32_t rows_per_block, int32_t chunk_keys) {
+  AttnPlan p;
+  if (attn_plan(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys, &p) != TTV_OK)
+    return (size_t)-1;
+  return p.ws_bytes;
+}
+
+ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                         int32_t D, float scale, const void* q, const void* k_cache,
+                         const void* v_cache, int32_t Lcap, const int32_t* cache_len,
+                         int32_t Lmax, const void* k_tree, const void* v_tree,
+                         const int32_t* parents, void* out, float* lse, int32_t* dev_status,
+                         void* workspace, size_t workspace_bytes, int32_t rows_per_block,
+                         int32_t chunk_keys, void* stream) {
+  if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
+  if (!q || !k_cache || !v_cache || !cache_len || !k_tree || !v_tree || !parents || !out)
+    return TTV_E_NULL;
+  if (Lcap < 0 || Lmax > Lcap || !std::isfinite(scale)) return TTV_E_SHAPE;
+  AttnPlan p;
+  const ttv_status st = attn_plan(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys, &p);
+  if (st != TTV_OK) return st;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_tree) ||
+      !aligned16(v_tree) || !aligned16(out))
+    return TTV_E_ALIGN;
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return TTV_E_WORKSPACE;
+  if (p.ws_bytes > 0 && !aligned16(workspace)) return TTV_E_ALIGN;
+
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_tree = k_tree;
+  a.v_tree = v_tree;
+  a.cache_len = cache_len;
+  a.parents = parents;
+  a.out = out;
+  a.lse = lse;
+  a.dev_status = dev_status;
+  a.B = B;
+  a.N = N;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.D = D;
+  a.Lcap = Lcap;
+  a.Lmax = Lmax;
+  a.R = p.rows;
+  a.rows_per_block = p.rows_per_block;
+  a.chunk_keys = p.chunk_keys;
+  a.chunks = p.chunks;
+  a.scale_log2 = scale * 1.44269504088896340736f;
+  if (p.chunks > 1) {
+    a.ws_acc = static_cast<float*>(workspace);
+    a.ws_ml = a.ws_acc + (size_t)B * Hkv * p.chunks * p.rows * D;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = p.mfma ? launch_attn_mfma(a, s) : launch_attn_fma(a, dt == TTV_BF16, s);
+  if (e != hipSuccess) return TTV_E_LAUNCH;
+  if (p.chunks > 1) return launch_status(launch_attn_combine(a, dt == TTV_BF16, s));
+  return TTV_OK;
+}
+
+size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V) {
+  if (mode != TTV_GREEDY && mode != TTV_STOCHASTIC) return (size_t)-1;
+  if (B < 1 || N < 1 || V < 1 || N > TTV_MAX_NODES) return (size_t)-1;
+  if (mode == TTV_STOCHASTIC) return V > kMssMaxVocab ? (size_t)-1 : 0;
+  if ((long)B * N > 0x7fffffffL) return (size_t)-1;
+  return greedy_plan(B, N, V).ws_bytes;
+}
+
+ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V,
+                           const int32_t* parents, const int32_t* tokens, const float* llm,
+                           const float* ssm, const float* u_accept, const float* u_bonus,
+                           int32_t* path, int32_t* path_len, int32_t* out_tokens,
+                           int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (mode != TTV_GREEDY && mode != TTV_STOCHASTIC) return TTV_E_DTYPE;
+  if (!parents || !tokens || !llm || !path || !path_len || !out_tokens) return TTV_E_NULL;
+  if (mode == TTV_STOCHASTIC && (!ssm || !u_accept || !u_bonus)) return TTV_E_NULL;
+  if (B < 1 || N < 1 || V < 1) return TTV_E_SHAPE;
+  if (N > TTV_MAX_NODES) return TTV_E_UNSUPPORTED;
+  if ((long)B * N > 0x7fffffffL) return TTV_E_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == TTV_STOCHASTIC) {
+    if (V > kMssMaxVocab) return TTV_E_UNSUPPORTED;
+    if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
+    return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm, u_accept, u_bonus,
+                                           path, path_len, out_tokens, dev_status, s));
+  }
+  const GreedyPlan p = greedy_plan(B, N, V);
+  if (p.splits > kMaxGridYZ) return TTV_E_UNSUPPORTED;
+  if (!aligned16(llm)) return TTV_E_ALIGN;
+  if (!workspace || workspace_bytes < p.ws_bytes) return TTV_E_WORKSPACE;
+  if (!aligned16(workspace)) return TTV_E_ALIGN;
+  return launch_status(launch_verify_greedy(B, N, V, parents, tokens, llm, path, path_len,
+                                            out_tokens, dev_status, workspace, p, s));
+}
+
+ttv_status ttv_kv_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv, int32_t D,
+                         int32_t Lcap, const void* k_tree, const void* v_tree, void* k_cache,
+                         void* v_cache, const int32_t* cache_len_in, int32_t* cache_len_out,
+                         int32_t Lmax, const int32_t* path, const int32_t* path_len,
+                         int32_t* committed_src, int32_t* dev_status, void* stream) {
+  if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
+  if (!k_tree || !v_tree || !k_cache || !v_cache || !cache_len_in || !cache_len_out || !path ||
+      !path_len)
+    return TTV_E_NULL;
+  if (B < 1 || N < 1 || Hkv < 1 || D < 1 || Lmax < 0 || Lcap < 0) return TTV_E_SHAPE;
+  if (N > TTV_MAX_NODES || (D != 64 && D != 128)) return TTV_E_UNSUPPORTED;
+  if ((long)Lmax + N > Lcap) return TTV_E_SHAPE;
+  if (!aligned16(k_tree) || !aligned16(v_tree) || !aligned16(k_cache) || !aligned16(v_cache))
+    return TTV_E_ALIGN;
+  const int elt = dt == TTV_BF16 ? 2 : 4;
+  return launch_status(launch_kv_commit(elt, B, N, Hkv, D, Lcap, k_tree, v_tree, k_cache, v_cache,
+                                        cache_len_in, cache_len_out, Lmax, path, path_len,
+                                        committed_src, dev_status,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// commit.hip -- ttv_kv_commit: append the accepted path's KV rows to the
+// contiguous cache ([SI] §4 "Tree-Based Parallel Decoding": verified and
+// speculated tokens share one key-value cache; what stays is the accepted
+// path).  One workgroup per request copies its Hkv * path_len rows of K and V
+// in 16-byte vectors; it reads the path straight from the verifier's device
+// output, so no host round trip sits between the two calls.
+#include "launch.h"
+#include "ttv_common.h"
+
+namespace ttv {
+
+__global__ __launch_bounds__(256) void kv_commit_kernel(
+    int row_bytes, int N, int Hkv, int Lcap, int Lmax, const u32x4* __restrict__ k_tree,
+    const u32x4* __restrict__ v_tree, u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
+    const int32_t* __restrict__ cache_len_in, int32_t* cache_len_out,
+    const int32_t* __restrict__ path, const int32_t* __restrict__ path_len,
+    int32_t* __restrict__ committed_src, int32_t* __restrict__ dev_status) {
+  __shared__ int32_t s_path[kMaxNodes];
+  __shared__ int s_bad_node;
+  const int b = blockIdx.x;
+  // cache_len_out may alias cache_len_in: only this workgroup touches entry b,
+  // and every thread reads it before the barrier that precedes the write.
+  const int L = cache_len_in[b];
+  const int n = path_len[b];
+  const bool shape_ok = L >= 0 && L <= Lmax && n >= 0 && n <= N && L + n <= Lcap;
+  if (threadIdx.x == 0) s_bad_node = 0;
+  __syncthreads();
+  if (shape_ok) {
+    for (int j = threadIdx.x; j < n; j += blockDim.x) {
+      const int p = path[(size_t)b * N + j];
+      s_path[j] = p;
+      if (p < 0 || p >= N) s_bad_node = 1;  // every writer stores the same value
+    }
+  }
+  __syncthreads();
+  const bool ok = shape_ok && s_bad_node == 0;
+  if (ok) {
+    const int vec = row_bytes / 16;  // 16-byte vectors per row
+    const int per_head = n * vec;
+    const int total = Hkv * per_head;
+    for (int t = threadIdx.x; t < total; t += blockDim.x) {
+      const int h = t / per_head;
+      const int r = t - h * per_head;
+      const int j = r / vec;
+      const int e = r - j * vec;
+      const size_t src = (((size_t)b * Hkv + h) * N + s_path[j]) * vec + e;
+      const size_t dst = (((size_t)b * Hkv + h) * Lcap + (L + j)) * vec + e;
+      k_cache[dst] = k_tree[src];
+      v_cache[dst] = v_tree[src];
+    }
+  }
+  if (committed_src) {
+    for (int j = threadIdx.x; j < N; j += blockDim.x)
+      committed_src[(size_t)b * N + j] = (ok && j < n) ? s_path[j] : -1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    cache_len_out[b] = ok ? L + n : L;
+    if (dev_status) dev_status[b] = ok ? TTV_OK : TTV_E_SHAPE;
+  }
+}
+
+hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,
+                            const void* k_tree, const void* v_tree, void* k_cache,
+                            void* v_cache, const int32_t* cache_len_in,
+                            int32_t* cache_len_out, int Lmax, const int32_t* path,
+                            const int32_t* path_len, int32_t* committed_src,
+                            int32_t* dev_status, hipStream_t s) {
+  hipLaunchKernelGGL(kv_commit_kernel, dim3(B), dim3(256), 0, s, D * elt, N, Hkv, Lcap, Lmax,
+                     static_cast<const u32x4*>(k_tree), static_cast<const u32x4*>(v_tree),
+                     static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), cache_len_in,
+                     cache_len_out, path, path_len, committed_src, dev_status);
+  return hipGetLastError();
+}
+
+}  // namespace ttv

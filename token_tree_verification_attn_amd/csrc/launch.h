@@ -1,0 +1,79 @@
+// launch.h -- host-side launch plans and launcher declarations (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ttv {
+
+// ------------------------------------------------------------- attention --
+// Launch plan of ttv_tree_attn, a pure function of the call's sizes (the
+// size query and the call compute the same plan).
+struct AttnPlan {
+  bool mfma;           // matrix-core path (bf16 and >= 16 query rows per kv head)
+  int rows;            // R = N * G query rows per (request, kv head)
+  int rows_per_block;  // query rows handled by one workgroup
+  int row_blocks;      // ceil(R / rows_per_block)
+  int chunk_keys;      // prefix keys per workgroup (multiple of 64)
+  int chunks;          // ceil(Lmax / chunk_keys), at least 1
+  size_t ws_bytes;     // split-KV partials (0 when chunks == 1)
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const void* k_tree;
+  const void* v_tree;
+  const int32_t* cache_len;
+  const int32_t* parents;
+  void* out;
+  float* lse;
+  int32_t* dev_status;
+  float* ws_acc;   // [B*Hkv][chunks][R][D]  unnormalised fp32 partial outputs
+  float* ws_ml;    // [B*Hkv][chunks][R][2]  running max (log2 units) and sum
+  int B, N, Hq, Hkv, G, D, Lcap, Lmax, R;
+  int rows_per_block, chunk_keys, chunks;
+  float scale_log2;  // softmax scale * log2(e): scores are kept in log2 units
+};
+
+hipError_t launch_attn_fma(const AttnArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_combine(const AttnArgs& a, bool bf16, hipStream_t s);
+
+// -------------------------------------------------------------- topology --
+hipError_t launch_topology(int B, int N, const int32_t* parents, uint64_t* anc_out,
+                           int32_t* depth_out, int32_t* dev_status, hipStream_t s);
+
+// ---------------------------------------------------------- verification --
+struct GreedyPlan {
+  int splits;       // workgroups per logits row
+  int slice;        // vocabulary entries per split (multiple of 4)
+  size_t ws_bytes;  // (value, index) partial argmax per (row, split)
+};
+GreedyPlan greedy_plan(int B, int N, int V);
+
+hipError_t launch_verify_greedy(int B, int N, int V, const int32_t* parents,
+                                const int32_t* tokens, const float* llm,
+                                int32_t* path, int32_t* path_len, int32_t* out_tokens,
+                                int32_t* dev_status, void* ws, const GreedyPlan& p,
+                                hipStream_t s);
+
+// Largest vocabulary the stochastic verifier holds in LDS.
+constexpr int kMssMaxVocab = 36864;
+hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
+                             const int32_t* tokens, const float* llm, const float* ssm,
+                             const float* u_accept, const float* u_bonus, int32_t* path,
+                             int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
+                             hipStream_t s);
+
+// ----------------------------------------------------------------- commit --
+hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,
+                            const void* k_tree, const void* v_tree, void* k_cache,
+                            void* v_cache, const int32_t* cache_len_in,
+                            int32_t* cache_len_out, int Lmax, const int32_t* path,
+                            const int32_t* path_len, int32_t* committed_src,
+                            int32_t* dev_status, hipStream_t s);
+
+}  // namespace ttv

@@ -1,0 +1,160 @@
+// ttv_common.h -- device-side helpers shared by the kernels of libttv.
+//
+// Sources cited (page title, then section):
+//   [SI]  "SpecInfer: Accelerating Generative Large Language Model Serving with
+//         Tree-based Speculative Inference and Verification" (paperlayer.ai
+//         summary of arXiv 2305.09781v4).
+//   [SSD] "Accelerating LLM Inference with Staged Speculative Decoding"
+//         (paperlayer.ai summary of arXiv 2308.04623v1).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ttv.h"
+
+namespace ttv {
+
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kMaxNodes = TTV_MAX_NODES;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// ------------------------------------------------------ wave primitives ----
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = __shfl(static_cast<uint32_t>(v), src);
+  uint32_t hi = __shfl(static_cast<uint32_t>(v >> 32), src);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
+  uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_u64(v, m);
+  return v;
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m));
+  return v;
+}
+
+// --------------------------------------------------------- tree topology --
+// Ancestor bitsets of one request's token tree, built by ONE wavefront.
+// [SI] §4 "Tree Attention": node i stands for the sequence root -> i, so the
+// mask row of node i is the set of nodes on that path ("topology-aware causal
+// mask", §4 "Tree-Based Parallel Decoding").
+//
+// Lane l holds nodes l and l+64.  Pointer doubling: a node keeps the set A of
+// path nodes it has gathered and a jump pointer J to the nearest path node not
+// yet in A (initially A = {i}, J = parent(i)).  Each round every node with
+// J >= 0 reads (A_J, J_J) of node J through a wave shuffle (ds_bpermute) and
+// sets A |= A_J, J = J_J, so the covered path length doubles; a ballot ends
+// the loop once every J is -1 (ceil(log2(depth+1)) rounds, at most 7).
+// Validity (parents[0] == -1, 0 <= parents[i] < i) is checked with a ballot
+// first; an invalid tree writes nothing and returns false.
+//
+// On return (valid tree) s_anc[2*i + w] holds word w of node i's bitset and
+// s_depth[i] its depth, for i < N.  All 64 lanes must call it; the caller
+// synchronises before other waves read the LDS arrays.
+__device__ inline bool wave_build_tree(const int32_t* __restrict__ par, int N,
+                                       uint64_t* s_anc, int32_t* s_depth) {
+  const int lane = lane_id();
+  const int i0 = lane, i1 = lane + 64;
+  const int p0 = i0 < N ? par[i0] : -1;
+  const int p1 = i1 < N ? par[i1] : -1;
+  const bool bad0 = i0 < N && (i0 == 0 ? p0 != -1 : (p0 < 0 || p0 >= i0));
+  const bool bad1 = i1 < N && (p1 < 0 || p1 >= i1);
+  if (__ballot(bad0 || bad1) != 0ull) return false;
+
+  // A for node i0 (words lo/hi) and node i1; node i0 < 64 lives in word 0.
+  uint64_t a0lo = i0 < N ? (1ull << i0) : 0ull, a0hi = 0ull;
+  uint64_t a1lo = 0ull, a1hi = i1 < N ? (1ull << (i1 - 64)) : 0ull;
+  int j0 = p0, j1 = p1;
+  const bool two = N > 64;
+  while (__ballot(j0 >= 0 || j1 >= 0) != 0ull) {
+    // gather (A_J, J_J) for J = j0 and J = j1 from lane J & 63, slot J >> 6.
+    // j0 < i0 < 64 always lies in slot 0, whose high word is 0.
+    const int s0 = j0 & 63, s1 = j1 & 63;
+    const uint64_t r0a = shfl_u64(a0lo, s0);
+    const int r0j = __shfl(j0, s0);
+    if (two) {
+      // node j1 lies in slot 0 (j1 < 64) or slot 1 of lane s1
+      const uint64_t r1a = shfl_u64(a0lo, s1);
+      const int r1j = __shfl(j0, s1);
+      const uint64_t q1a = shfl_u64(a1lo, s1);
+      const uint64_t q1b = shfl_u64(a1hi, s1);
+      const int q1j = __shfl(j1, s1);
+      if (j1 >= 0) {
+        if (j1 < 64) {
+          a1lo |= r1a;
+          j1 = r1j;
+        } else {
+          a1lo |= q1a;
+          a1hi |= q1b;
+          j1 = q1j;
+        }
+      }
+    }
+    if (j0 >= 0) {
+      a0lo |= r0a;
+      j0 = r0j;
+    }
+  }
+  if (i0 < N) {
+    s_anc[2 * i0] = a0lo;
+    s_anc[2 * i0 + 1] = a0hi;
+    s_depth[i0] = __popcll(a0lo) + __popcll(a0hi) - 1;
+  }
+  if (i1 < N) {
+    s_anc[2 * i1] = a1lo;
+    s_anc[2 * i1 + 1] = a1hi;
+    s_depth[i1] = __popcll(a1lo) + __popcll(a1hi) - 1;
+  }
+  return true;
+}
+
+// Tree validity only (one wave): parents[0] == -1 and 0 <= parents[i] < i.
+__device__ inline bool wave_tree_valid(const int32_t* __restrict__ par, int N) {
+  bool bad = false;
+  for (int i = lane_id(); i < N; i += kWave) {
+    const int p = par[i];
+    bad |= (i == 0) ? (p != -1) : (p < 0 || p >= i);
+  }
+  return __ballot(bad) == 0ull;
+}
+
+}  // namespace ttv

@@ -1,0 +1,413 @@
+// verify.hip -- ttv_tree_verify kernels.
+//
+// [SI] §4 "Token Tree Verification": every candidate sequence of the tree is
+// verified in parallel against the LLM's output at each node; §4 "Token
+// Verification": greedy matching, or multi-step speculative sampling that
+// tests the children of the current node in turn against a residual
+// distribution and keeps the LLM's output distribution.
+#include <limits.h>
+
+#include "launch.h"
+#include "ttv_common.h"
+
+namespace ttv {
+
+// ====================================================================== //
+// Greedy                                                                   //
+// ====================================================================== //
+// (value, index) max with the lowest index winning ties -- the same result
+// as a left-to-right scan that replaces only on a strictly greater value.
+__device__ __forceinline__ void amax_merge(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+// Kernel A: per (node row, vocabulary slice) argmax, streaming the logits
+// once with 16-byte loads.  grid = (B*N, splits).
+template <bool VEC>
+__global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __restrict__ llm, int V,
+                                                             int slice, int splits,
+                                                             float* __restrict__ ws_val,
+                                                             int* __restrict__ ws_idx) {
+  __shared__ float s_v[4];
+  __shared__ int s_i[4];
+  const int row = blockIdx.x, sp = blockIdx.y;
+  const int v0 = sp * slice, v1 = min(V, v0 + slice);
+  const float* x = llm + (size_t)row * V;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  if (VEC) {
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
+    for (int f = v0 / 4 + threadIdx.x; f < v1 / 4; f += 256) {
+      const f32x4 q = __builtin_nontemporal_load(x4 + f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax_merge(bv, bi, q[e], 4 * f + e);
+    }
+  } else {
+    for (int v = v0 + threadIdx.x; v < v1; v += 256) amax_merge(bv, bi, x[v], v);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) amax_merge(bv, bi, __shfl_xor(bv, m), __shfl_xor(bi, m));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_v[wave] = bv;
+    s_i[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) amax_merge(bv, bi, s_v[w], s_i[w]);
+    ws_val[(size_t)row * splits + sp] = bv;
+    ws_idx[(size_t)row * splits + sp] = bi;
+  }
+}
+
+// Kernel B: one wavefront per request.  amax[i] from the partials, then the
+// acceptance scan over parent indices: e_i = (token of i == amax of its
+// parent), E = ballot(e_i or i == 0), and node i is accepted iff its whole
+// root path lies in E, i.e. (anc[i] & ~E) == 0.  The path ends at the deepest
+// accepted node (lowest index on ties), found with a wave max.
+__global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
+                                                         const int32_t* __restrict__ parents,
+                                                         const int32_t* __restrict__ tokens,
+                                                         const float* __restrict__ ws_val,
+                                                         const int* __restrict__ ws_idx,
+                                                         int32_t* __restrict__ path,
+                                                         int32_t* __restrict__ path_len,
+                                                         int32_t* __restrict__ out_tokens,
+                                                         int32_t* __restrict__ dev_status) {
+  __shared__ uint64_t s_anc[2 * kMaxNodes];
+  __shared__ int32_t s_depth[kMaxNodes];
+  __shared__ int32_t s_amax[kMaxNodes];
+  __shared__ int32_t s_path[kMaxNodes];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int32_t* par = parents + (size_t)b * N;
+  const int32_t* tok = tokens + (size_t)b * N;
+  const bool ok = wave_build_tree(par, N, s_anc, s_depth);
+  if (!ok) {
+    for (int k = lane; k < N; k += kWave) {
+      path[(size_t)b * N + k] = -1;
+      out_tokens[(size_t)b * N + k] = -1;
+    }
+    if (lane == 0) {
+      path_len[b] = 0;
+      if (dev_status) dev_status[b] = TTV_E_TREE;
+    }
+    return;
+  }
+  for (int i = lane; i < N; i += kWave) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int sp = 0; sp < splits; ++sp)
+      amax_merge(bv, bi, ws_val[((size_t)b * N + i) * splits + sp], ws_idx[((size_t)b * N + i) * splits + sp]);
+    s_amax[i] = bi;
+  }
+  __syncthreads();
+  const int i0 = lane, i1 = lane + 64;
+  const bool e0 = i0 < N && (i0 == 0 || tok[i0] == s_amax[par[i0]]);
+  const bool e1 = i1 < N && tok[i1] == s_amax[par[i1]];
+  const uint64_t E0 = __ballot(e0), E1 = __ballot(e1);
+  int key = -1;  // (depth, -index) of the deepest accepted node
+  if (i0 < N && (s_anc[2 * i0] & ~E0) == 0ull && (s_anc[2 * i0 + 1] & ~E1) == 0ull)
+    key = max(key, (s_depth[i0] << 8) | (255 - i0));
+  if (i1 < N && (s_anc[2 * i1] & ~E0) == 0ull && (s_anc[2 * i1 + 1] & ~E1) == 0ull)
+    key = max(key, (s_depth[i1] << 8) | (255 - i1));
+  key = wave_max_i32(key);  // the root is always accepted: key >= 0
+  const int end = 255 - (key & 255), dend = key >> 8;
+  const uint64_t pe0 = s_anc[2 * end], pe1 = s_anc[2 * end + 1];
+  if (i0 < N && ((pe0 >> i0) & 1ull)) s_path[s_depth[i0]] = i0;
+  if (i1 < N && ((pe1 >> (i1 - 64)) & 1ull)) s_path[s_depth[i1]] = i1;
+  __syncthreads();
+  for (int k = lane; k < N; k += kWave) {
+    path[(size_t)b * N + k] = k <= dend ? s_path[k] : -1;
+    out_tokens[(size_t)b * N + k] = k < dend ? tok[s_path[k + 1]] : (k == dend ? s_amax[end] : -1);
+  }
+  if (lane == 0) {
+    path_len[b] = dend + 1;
+    if (dev_status) dev_status[b] = TTV_OK;
+  }
+}
+
+GreedyPlan greedy_plan(int B, int N, int V) {
+  GreedyPlan p;
+  const long rows = (long)B * N;
+  long s = (2048 + rows - 1) / rows;
+  const long cap = V / 1024 > 1 ? V / 1024 : 1;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  int slice = (int)((V + s - 1) / s);
+  slice = (slice + 3) / 4 * 4;
+  p.slice = slice;
+  p.splits = (V + slice - 1) / slice;
+  p.ws_bytes = (size_t)rows * p.splits * 8;
+  return p;
+}
+
+hipError_t launch_verify_greedy(int B, int N, int V, const int32_t* parents,
+                                const int32_t* tokens, const float* llm,
+                                int32_t* path, int32_t* path_len, int32_t* out_tokens,
+                                int32_t* dev_status, void* ws, const GreedyPlan& p,
+                                hipStream_t s) {
+  float* ws_val = static_cast<float*>(ws);
+  int* ws_idx = reinterpret_cast<int*>(ws_val + (size_t)B * N * p.splits);
+  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(llm) & 15) == 0);
+  const dim3 grid(B * N, p.splits);
+  if (vec) hipLaunchKernelGGL(argmax_partial_kernel<true>, grid, dim3(256), 0, s, llm, V, p.slice, p.splits, ws_val, ws_idx);
+  else hipLaunchKernelGGL(argmax_partial_kernel<false>, grid, dim3(256), 0, s, llm, V, p.slice, p.splits, ws_val, ws_idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(greedy_scan_kernel, dim3(B), dim3(kWave), 0, s, N, p.splits, parents, tokens,
+                     ws_val, ws_idx, path, path_len, out_tokens, dev_status);
+  return hipGetLastError();
+}
+
+// ====================================================================== //
+// Stochastic: multi-step speculative sampling, one workgroup per request    //
+// ====================================================================== //
+constexpr int kMssThreads = 1024;
+
+// floor(x * 2^40) for finite x in [0, 2^24), from the float's fields: a
+// normal x is m * 2^(e-150) with a 24-bit m, so x * 2^40 = m * 2^(e-110).
+__device__ __forceinline__ uint64_t fx40(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const int e = (u >> 23) & 0xff;
+  if (e == 0) return 0ull;  // zero or subnormal: below 2^-126
+  const uint64_t m = (u & 0x7fffffu) | 0x800000u;
+  const int sh = e - 110;
+  if (sh >= 0) return m << sh;
+  if (sh <= -24) return 0ull;
+  return m >> (-sh);
+}
+// LDS index of vocabulary entry v: one pad word every 32 keeps both the
+// strided (v = k*1024 + t) and the contiguous per-thread walks conflict-free.
+__device__ __forceinline__ int widx(int v) { return v + (v >> 5); }
+
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* s_red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  v = wave_sum_u64(v);
+  __syncthreads();  // s_red free from its previous use
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  uint64_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kMssThreads / 64; ++w) t += s_red[w];
+  return t;
+}
+
+// Exclusive prefix sum over the threads of the block (thread order).
+__device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* s_red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint64_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t o = shfl_u64(incl, lane >= d ? lane - d : lane);
+    if (lane >= d) incl += o;
+  }
+  __syncthreads();
+  if (lane == 63) s_red[wave] = incl;
+  __syncthreads();
+  uint64_t before = 0;
+  for (int w = 0; w < wave; ++w) before += s_red[w];
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kMssThreads) void mss_kernel(
+    int N, int V, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
+    const float* __restrict__ llm, const float* __restrict__ ssm,
+    const float* __restrict__ u_accept, const float* __restrict__ u_bonus,
+    int32_t* __restrict__ path, int32_t* __restrict__ path_len,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status) {
+  extern __shared__ float s_w[];  // residual w, widx() layout
+  __shared__ int32_t s_par[kMaxNodes];
+  __shared__ int32_t s_tok[kMaxNodes];
+  __shared__ int32_t s_path[kMaxNodes];
+  __shared__ unsigned long long s_kids[kMaxNodes][2];
+  __shared__ uint64_t s_first_ok[2];
+  __shared__ uint64_t s_red[kMssThreads / 64];
+  __shared__ int s_status, s_pick;
+
+  const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
+  const size_t rowN = (size_t)b * N;
+  // ---- tree, tokens and the children of every node
+  if (t < N) {
+    s_par[t] = parents[rowN + t];
+    s_tok[t] = tokens[rowN + t];
+    s_kids[t][0] = 0ull;
+    s_kids[t][1] = 0ull;
+  }
+  if (t == 0) s_status = 0;
+  __syncthreads();
+  if (wave < 2) {  // nodes 0..127: tree validity and token range
+    bool bad_tree = false, bad_tok = false;
+    if (t < N) {
+      const int p = s_par[t];
+      bad_tree = (t == 0) ? (p != -1) : (p < 0 || p >= t);
+      bad_tok = t > 0 && (s_tok[t] < 0 || s_tok[t] >= V);
+    }
+    const uint64_t bt = __ballot(bad_tree), bk = __ballot(bad_tok);
+    if ((t & 63) == 0) {
+      if (bt) atomicOr(&s_status, 1);
+      if (bk) atomicOr(&s_status, 2);
+    }
+  }
+  __syncthreads();
+  const int st = s_status;
+  if (st != 0) {
+    for (int k = t; k < N; k += kMssThreads) {
+      path[rowN + k] = -1;
+      out_tokens[rowN + k] = -1;
+    }
+    if (t == 0) {
+      path_len[b] = 0;
+      if (dev_status) dev_status[b] = (st & 1) ? TTV_E_TREE : TTV_E_SHAPE;
+    }
+    return;
+  }
+  // children bitsets; first-attempt test of every non-root node with w = p of
+  // its parent and mass 1 (only first children use it) -- gathers only
+  bool first_ok = false;
+  if (t >= 1 && t < N) {
+    const int p = s_par[t], x = s_tok[t];
+    atomicOr(&s_kids[p][t >> 6], 1ull << (t & 63));
+    const float r = u_accept[rowN + t];
+    const float qx = ssm[(rowN + t) * V + x];
+    const float px = llm[(rowN + p) * V + x];
+    first_ok = (r * qx) * 1.0f < px;
+  }
+  if (wave < 2) {
+    const uint64_t bal = __ballot(first_ok);
+    if ((t & 63) == 0) s_first_ok[wave] = bal;
+  }
+  __syncthreads();
+
+  auto load_p_row = [&](int u) {
+    const float* p = llm + (rowN + u) * V;
+    for (int v = t; v < V; v += kMssThreads) s_w[widx(v)] = p[v];
+    __syncthreads();
+  };
+
+  // ---- the walk: control flow is uniform, decisions are recomputed by every
+  // thread from the same LDS / global values
+  int u = 0;
+  for (;;) {
+    uint64_t k0 = s_kids[u][0], k1 = s_kids[u][1];
+    if ((k0 | k1) == 0ull) {  // leaf: the bonus comes from p_u
+      load_p_row(u);
+      break;
+    }
+    const int c0 = k0 ? __ffsll((unsigned long long)k0) - 1 : 64 + __ffsll((unsigned long long)k1) - 1;
+    const bool ok0 = (c0 < 64 ? (s_first_ok[0] >> c0) : (s_first_ok[1] >> (c0 - 64))) & 1ull;
+    if (ok0) {
+      u = c0;
+      continue;
+    }
+    // first child rejected: sequential residual tests at u
+    load_p_row(u);
+    float s = 1.0f;
+    int next = -1;
+    bool first = true;
+    while (k0 | k1) {
+      int c;
+      if (k0) {
+        c = __ffsll((unsigned long long)k0) - 1;
+        k0 &= k0 - 1;
+      } else {
+        c = 64 + __ffsll((unsigned long long)k1) - 1;
+        k1 &= k1 - 1;
+      }
+      const float* q = ssm + (rowN + c) * V;
+      if (!first) {  // the first child's test (w = p_u, s = 1) is already known
+        const int x = s_tok[c];
+        const float lhs = (u_accept[rowN + c] * q[x]) * s;
+        if (lhs < s_w[widx(x)]) {
+          next = c;
+          break;
+        }
+      }
+      first = false;
+      // rejected: w = max(w - s*q, +0), s = its mass in 2^-40 units
+      uint64_t part = 0;
+      for (int v = t; v < V; v += kMssThreads) {
+        const float d = fmaf(-s, q[v], s_w[widx(v)]);
+        const float w = d > 0.0f ? d : 0.0f;
+        s_w[widx(v)] = w;
+        part += fx40(w);
+      }
+      const uint64_t S = block_sum_u64(part, s_red);  // its barriers publish s_w
+      s = (float)((double)S * 0x1p-40);
+      if (s == 0.0f) {  // empty residual: stop testing, sample from p_u
+        load_p_row(u);
+        break;
+      }
+    }
+    if (next < 0) break;  // bonus from the residual in s_w
+    u = next;
+  }
+
+  // ---- bonus: inverse CDF over the exact integer prefix sums of fx40(w)
+  const int per = (V + kMssThreads - 1) / kMssThreads;
+  const int v_lo = min(V, t * per), v_hi = min(V, v_lo + per);
+  uint64_t mine = 0;
+  for (int v = v_lo; v < v_hi; ++v) mine += fx40(s_w[widx(v)]);
+  const uint64_t excl = block_excl_scan_u64(mine, s_red);
+  const uint64_t S = block_sum_u64(mine, s_red);
+  if (t == 0) s_pick = -1;
+  __syncthreads();
+  if (S > 0) {
+    const uint64_t R = (uint64_t)(u_bonus[b] * 16777216.0f);
+    const uint64_t T = R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24);  // floor(R*S/2^24)
+    if (excl <= T && T < excl + mine) {
+      uint64_t cum = excl;
+      for (int v = v_lo; v < v_hi; ++v) {
+        cum += fx40(s_w[widx(v)]);
+        if (cum > T) {
+          s_pick = v;
+          break;
+        }
+      }
+    }
+  } else if (t == 0) {  // nothing representable left: the largest entry
+    int bi = 0;
+    for (int v = 1; v < V; ++v)
+      if (s_w[widx(v)] > s_w[widx(bi)]) bi = v;
+    s_pick = bi;
+  }
+  __syncthreads();
+  const int bonus = s_pick;
+
+  // ---- path root -> u and the emitted tokens
+  if (t == 0) {
+    int d = 0;
+    for (int j = u; j != -1; j = s_par[j]) ++d;
+    int k = d - 1;
+    for (int j = u; j != -1; j = s_par[j]) s_path[k--] = j;
+    s_pick = d;
+  }
+  __syncthreads();
+  const int len = s_pick;
+  for (int k = t; k < N; k += kMssThreads) {
+    path[rowN + k] = k < len ? s_path[k] : -1;
+    out_tokens[rowN + k] = k + 1 < len ? s_tok[s_path[k + 1]] : (k + 1 == len ? bonus : -1);
+  }
+  if (t == 0) {
+    path_len[b] = len;
+    if (dev_status) dev_status[b] = TTV_OK;
+  }
+}
+
+hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
+                             const int32_t* tokens, const float* llm, const float* ssm,
+                             const float* u_accept, const float* u_bonus, int32_t* path,
+                             int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
+                             hipStream_t s) {
+  const size_t lds = (size_t)(V + (V >> 5) + 1) * sizeof(float);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mss_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mss_kernel, dim3(B), dim3(kMssThreads), lds, s, N, V, parents, tokens, llm,
+                     ssm, u_accept, u_bonus, path, path_len, out_tokens, dev_status);
+  return hipGetLastError();
+}
+
+}  // namespace ttv
