@@ -119,8 +119,9 @@ ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents,
  *   lse         float [B,N,Hq], nullable: natural-log sum-exp of the scaled
  *               scores (0 for a rejected request).
  *   workspace   device scratch of >= ttv_tree_attn_workspace_size(...) bytes
- *               (may be NULL when that size is 0).  Its contents need no
- *               initialisation and are garbage afterwards.
+ *               (may be NULL when that size is 0): fp32 partials of the
+ *               split-KV launch.  Its contents need no initialisation and are
+ *               garbage afterwards; calls sharing one must not overlap.
  *   rows_per_block, chunk_keys  launch tuning: 0 = automatic; otherwise query
  *               rows per workgroup (64, 128 or 256 on the matrix-core path,
  *               which serves bf16 with N*Hq/Hkv >= 16; 16 on the FMA path)

@@ -81,7 +81,9 @@ def test_tree_attn_host_validation(kw, status):
 
 def test_tree_attn_workspace_size_matches_plan():
     f = ttv.lib().ttv_tree_attn_workspace_size
-    assert f(1, 1, 8, 4, 2, 64, 100, 0, 64) == 1 * 2 * 2 * 16 * 66 * 4   # 2 chunks of 64
+    # 2 chunks of 64 keys -> fp32 partials, D + 2 floats per (pair, chunk, row)
+    assert f(1, 1, 8, 4, 2, 64, 100, 0, 64) == 1 * 2 * 2 * 16 * 66 * 4
+    assert f(0, 1, 8, 4, 2, 64, 100, 0, 64) == 1 * 2 * 2 * 16 * 66 * 4
     assert f(1, 1, 8, 4, 2, 64, 64, 0, 64) == 0                          # one chunk
     assert f(1, 1, 129, 4, 2, 64, 64, 0, 0) == SZ_ERR
     assert f(9, 1, 8, 4, 2, 64, 64, 0, 0) == SZ_ERR

@@ -170,7 +170,7 @@ def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int
         dev_status = torch.empty(B, dtype=torch.int32, device=dev)
     nbytes = tree_attn_workspace_size(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys)
     if workspace is None and nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)  # counters start at 0
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().ttv_tree_attn(_dt(dt), B, N, Hq, Hkv, D, float(scale), _ptr(q), _ptr(k_cache),
                              _ptr(v_cache), Lcap, _ptr(cache_len), int(Lmax), _ptr(k_tree),

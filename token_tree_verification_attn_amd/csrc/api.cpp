@@ -160,7 +160,7 @@ ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t
     a.ws_ml = a.ws_acc + (size_t)B * Hkv * p.chunks * p.rows * D;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = p.mfma ? launch_attn_mfma(a, s) : launch_attn_fma(a, dt == TTV_BF16, s);
+  const hipError_t e = p.mfma ? launch_attn_mfma(a, s) : launch_attn_fma(a, dt == TTV_BF16, s);
   if (e != hipSuccess) return TTV_E_LAUNCH;
   if (p.chunks > 1) return launch_status(launch_attn_combine(a, dt == TTV_BF16, s));
   return TTV_OK;

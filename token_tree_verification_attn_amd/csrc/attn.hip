@@ -7,7 +7,9 @@
 // part (rows 0..L_b-1 of k/v_cache, unmasked) and an in-tree part (k/v_tree,
 // masked by the ancestor bitset); both feed one online softmax.
 //
-// Work decomposition (one workgroup = 4 wavefronts):
+// This file holds the FMA path (fp32, or bf16 with fewer than 16 query rows
+// per kv head) and the split-KV combine; the matrix-core path is in
+// attn_mfma.hip.  Work decomposition (one workgroup = 4 wavefronts):
 //   blockIdx.z = b * Hkv + h          request and kv head
 //   blockIdx.y = row block            query rows r = i * G + g (node i, head
 //                                     g of the GQA group) packed together, so
@@ -207,279 +209,6 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
 }
 
 // =========================================================================
-// Matrix-core path (bf16): per 64-key tile every wavefront computes
-//   S^T[key][query] = K Q^T      (v_mfma_f32_16x16x32_bf16, A = K from LDS,
-//                                 B = this wave's queries, held in registers)
-// then the online softmax on S^T (a query's 64 scores sit in 4 lanes x 16
-// registers, so its max needs two xor-shuffles), then
-//   O^T[d][query] += V^T P^T     (A = V^T from the transposed LDS tile,
-//                                 B = P^T straight from the S^T registers)
-// The K tile and the transposed V tile are staged once in LDS and shared by
-// the 4 wavefronts (4 * QW packed query rows); the next tile's global loads
-// are issued before the current tile's math.
-// =========================================================================
-template <int D, int QW>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int KT = kKeysPerTile;
-  constexpr int QT = QW / 16;          // 16-query MFMA tiles per wave
-  constexpr int KS = D / 32;           // 32-wide d steps of Q K^T
-  constexpr int DT = D / 16;           // 16-wide d tiles of the output
-  constexpr int KPAD = D + 8;          // s_k row stride in bf16 (16-byte pad)
-  constexpr int VPAD = KT + 8;         // s_vt row stride in bf16 (16-byte pad)
-  constexpr int CPK = D / 8;           // 16-byte chunks per key row
-  constexpr int LPT = KT * CPK / 256;  // chunks per thread per tile, for K and for V
-  constexpr int RB = 4 * QW;           // query rows per block
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[KT * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VPAD];
-  __shared__ uint64_t s_anc[2 * kMaxNodes];
-  __shared__ int32_t s_depth[kMaxNodes];
-  __shared__ int s_status;
-
-  const int c = blockIdx.x, rb = blockIdx.y, bh = blockIdx.z;
-  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g16 = lane >> 4, c16 = lane & 15;
-  const int N = a.N, G = a.G, R = a.R;
-  const int L = a.cache_len[b];
-  if (wave == 0) {
-    const bool tree_ok = wave_build_tree(a.parents + (size_t)b * N, N, s_anc, s_depth);
-    if (lane == 0) {
-      s_status = request_status(tree_ok, L, a.Lmax);
-      if (a.dev_status && c == 0 && rb == 0 && h == 0) a.dev_status[b] = s_status;
-    }
-  }
-  __syncthreads();
-  const int status = s_status;
-  const int row_base = rb * RB + wave * QW;
-
-  if (status != TTV_OK) {
-    if (a.chunks == 1) {
-      for (int t = threadIdx.x; t < RB * D; t += blockDim.x) {
-        const int r = rb * RB + t / D, d = t % D;
-        if (r >= R) continue;
-        const int i = r / G, hq = h * G + (r - i * G);
-        static_cast<uint16_t*>(a.out)[(((size_t)b * N + i) * a.Hq + hq) * D + d] = 0;
-        if (d == 0 && a.lse) a.lse[((size_t)b * N + i) * a.Hq + hq] = 0.f;
-      }
-    }
-    return;
-  }
-  const int k_begin = c * a.chunk_keys;
-  const int k_end = min(L, k_begin + a.chunk_keys);
-  const int nP = (k_begin < k_end) ? (k_end - k_begin + KT - 1) / KT : 0;
-  const int nT = (c == 0) ? (N + KT - 1) / KT : 0;
-  const int ntiles = nP + nT;
-  if (ntiles == 0) return;
-
-  // ---- this wave's queries as MFMA B operands: lane (c16, g16) of tile qt
-  // holds query row row_base + qt*16 + c16, d = ks*32 + g16*8 .. +7
-  const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  bf16x8 qB[QT][KS];
-  uint64_t anc_lo[QT], anc_hi[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int r = row_base + qt * 16 + c16;
-    const bool rv = r < R;
-    const int i = rv ? r / G : 0;
-    const int hq = h * G + (rv ? r - i * G : 0);
-    const uint16_t* qr = q + (((size_t)b * N + i) * a.Hq + hq) * D + g16 * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = rv ? *reinterpret_cast<const u32x4*>(qr + ks * 32) : u32x4{0u, 0u, 0u, 0u};
-      qB[qt][ks] = __builtin_bit_cast(bf16x8, v);
-    }
-    anc_lo[qt] = rv ? s_anc[2 * i] : 0ull;
-    anc_hi[qt] = rv ? s_anc[2 * i + 1] : 0ull;
-  }
-
-  f32x4 oacc[QT][DT];
-  float m_run[QT], l_run[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + ((size_t)bh * a.Lcap) * D;
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + ((size_t)bh * a.Lcap) * D;
-  const uint16_t* ktr = static_cast<const uint16_t*>(a.k_tree) + ((size_t)bh * N) * D;
-  const uint16_t* vtr = static_cast<const uint16_t*>(a.v_tree) + ((size_t)bh * N) * D;
-
-  u32x4 kreg[LPT], vreg[LPT];
-  auto tile_info = [&](int tile, const uint16_t*& ks, const uint16_t*& vs, int& key0, int& nvalid) {
-    if (tile < nP) {
-      key0 = k_begin + tile * KT;
-      nvalid = min(KT, k_end - key0);
-      ks = kc;
-      vs = vc;
-    } else {
-      key0 = (tile - nP) * KT;
-      nvalid = min(KT, N - key0);
-      ks = ktr;
-      vs = vtr;
-    }
-  };
-  auto load_tile = [&](int tile) {
-    const uint16_t *ks, *vs;
-    int key0, nvalid;
-    tile_info(tile, ks, vs, key0, nvalid);
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int ch = threadIdx.x + 256 * j;
-      const int key = ch / CPK, dc = (ch % CPK) * 8;
-      if (key < nvalid) {
-        const size_t off = (size_t)(key0 + key) * D + dc;
-        kreg[j] = *reinterpret_cast<const u32x4*>(ks + off);
-        vreg[j] = *reinterpret_cast<const u32x4*>(vs + off);
-      } else {
-        kreg[j] = u32x4{0u, 0u, 0u, 0u};
-        vreg[j] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-
-  load_tile(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const uint16_t *ks_unused, *vs_unused;
-    int key0, nvalid;
-    tile_info(tile, ks_unused, vs_unused, key0, nvalid);
-    const bool is_tree = tile >= nP;
-
-    __syncthreads();  // every wave is done with the previous tile's LDS
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int ch = threadIdx.x + 256 * j;
-      const int key = ch / CPK, dc = (ch % CPK) * 8;
-      *reinterpret_cast<u32x4*>(&s_k[key * KPAD + dc]) = kreg[j];
-      const u32x4 v = vreg[j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s_vt[(dc + 2 * e) * VPAD + key] = static_cast<uint16_t>(v[e] & 0xffffu);
-        s_vt[(dc + 2 * e + 1) * VPAD + key] = static_cast<uint16_t>(v[e] >> 16);
-      }
-    }
-    __syncthreads();
-    if (tile + 1 < ntiles) load_tile(tile + 1);  // in flight during the math below
-
-    // ---- S^T = K Q^T for 64 keys x QW queries
-    f32x4 s[4][QT];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(&s_k[(kt * 16 + c16) * KPAD + ks * 32 + g16 * 8]);
-        const bf16x8 A = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          s[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qB[qt][ks], s[kt][qt], 0, 0, 0);
-      }
-    }
-
-    // ---- online softmax on S^T: lane holds keys kt*16 + g16*4 + e of query c16
-    bf16x8 pB[QT][2];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kk = kt * 16 + g16 * 4 + e;
-          bool ok = kk < nvalid;
-          if (is_tree) {
-            const int j = key0 + kk;
-            const uint64_t w = j < 64 ? anc_lo[qt] : anc_hi[qt];
-            ok = ok && ((w >> (j & 63)) & 1ull);
-          }
-          const float t = ok ? s[kt][qt][e] * a.scale_log2 : -INFINITY;
-          s[kt][qt][e] = t;
-          mx = fmaxf(mx, t);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qt], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_use);
-      m_run[qt] = m_new;
-      float psum = 0.f;
-      float p[4][4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[kt][e] = __builtin_amdgcn_exp2f(s[kt][qt][e] - m_use);
-          psum += p[kt][e];
-        }
-      l_run[qt] = l_run[qt] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= alpha;
-      // P^T as B operands of two K=32 steps: slots 0-3 = keys 32*k2 + g16*4 + e,
-      // slots 4-7 = keys 32*k2 + 16 + g16*4 + e
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        u32x4 pk;
-        pk[0] = pack_bf16x2(p[2 * k2][0], p[2 * k2][1]);
-        pk[1] = pack_bf16x2(p[2 * k2][2], p[2 * k2][3]);
-        pk[2] = pack_bf16x2(p[2 * k2 + 1][0], p[2 * k2 + 1][1]);
-        pk[3] = pack_bf16x2(p[2 * k2 + 1][2], p[2 * k2 + 1][3]);
-        pB[qt][k2] = __builtin_bit_cast(bf16x8, pk);
-      }
-    }
-
-    // ---- O^T += V^T P^T ; A lane (c16, g16) = V^T[d][same key slots as P^T]
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const uint16_t* vrow = &s_vt[(dt * 16 + c16) * VPAD + k2 * 32 + g16 * 4];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-        const u32x4 av = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        const bf16x8 A = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pB[qt][k2], oacc[qt][dt], 0, 0, 0);
-      }
-    }
-  }
-
-  // ---- finish: the 4 lanes of a query hold disjoint key subsets of l
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    float lt = l_run[qt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    const int r = row_base + qt * 16 + c16;
-    if (r >= R) continue;
-    const int i = r / G, hq = h * G + (r - i * G);
-    if (a.chunks == 1) {
-      const float inv = 1.f / lt;
-      uint16_t* o = static_cast<uint16_t*>(a.out) + (((size_t)b * N + i) * a.Hq + hq) * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 v = oacc[qt][dt] * inv;
-        *reinterpret_cast<u32x2*>(o + dt * 16 + g16 * 4) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
-      if (g16 == 0 && a.lse) a.lse[((size_t)b * N + i) * a.Hq + hq] = (m_run[qt] + __log2f(lt)) * kLn2;
-    } else {
-      const size_t pr = ((size_t)bh * a.chunks + c) * R + r;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<f32x4*>(a.ws_acc + pr * D + dt * 16 + g16 * 4) = oacc[qt][dt];
-      if (g16 == 0) {
-        a.ws_ml[pr * 2] = m_run[qt];
-        a.ws_ml[pr * 2 + 1] = lt;
-      }
-    }
-  }
-}
-
-// =========================================================================
 // Split-KV combine: o = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),
 // M = max_c m_c, over the chunks that hold keys of request b (chunk 0 always
 // does: it owns the tree keys, and every node sees at least itself).
@@ -540,22 +269,6 @@ hipError_t launch_attn_fma(const AttnArgs& a, bool bf16, hipStream_t s) {
     if (a.D == 64) hipLaunchKernelGGL((attn_fma_kernel<float, 64>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((attn_fma_kernel<float, 128>), grid, dim3(256), 0, s, a);
   }
-  return hipGetLastError();
-}
-
-template <int D>
-static void launch_mfma_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
-  switch (a.rows_per_block) {
-    case 64: hipLaunchKernelGGL((attn_mfma_kernel<D, 16>), grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((attn_mfma_kernel<D, 32>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_mfma_kernel<D, 64>), grid, dim3(256), 0, s, a); break;
-  }
-}
-
-hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid = attn_grid(a);
-  if (a.D == 64) launch_mfma_d<64>(a, grid, s);
-  else launch_mfma_d<128>(a, grid, s);
   return hipGetLastError();
 }
 

@@ -1,0 +1,452 @@
+// attn_mfma.hip -- matrix-core tree attention for bf16 ([SI] §4 "Tree
+// Attention", "Tree-Based Parallel Decoding"; [SSD] §3 "Implementation": a
+// cache part and an in-tree part, both feeding one softmax).
+//
+// One workgroup = 4 wavefronts handles one (request b, kv head h, block of
+// 4*QW packed query rows r = node*G + g, chunk of prefix keys).  Per tile of
+// KT keys:
+//   S^T[key][query] = K Q^T     v_mfma_f32_16x16x32_bf16, A = K (LDS,
+//                               ds_read_b128), B = the wave's queries (VGPRs)
+//   online softmax on S^T       a query's KT scores sit in 4 lanes x KT/16
+//                               registers; its max needs two xor-shuffles
+//   O^T[d][query] += V^T P^T    A = V^T read from the row-major V tile with
+//                               ds_read_b64_tr_b16, B = P^T straight from the
+//                               S^T registers (bf16 by v_cvt_pk_bf16_f32)
+// KV tiles are copied HBM -> LDS by the hardware (global_load_lds_dwordx4,
+// 16 bytes per lane, no register staging) into a ring of NST stages, so the
+// loads of the next tiles are in flight while the current one is computed.
+// Each 16-byte chunk of a tile row is stored at an XOR-swizzled position (the
+// lanes choose their source addresses accordingly), which keeps both LDS read
+// patterns free of bank conflicts.
+//
+// Workgroups are numbered XCD-first: the dispatcher deals consecutive
+// workgroups round-robin to the 8 XCDs, and the remap below gives each XCD a
+// contiguous range of work items, so the row blocks that stream the same KV
+// chunk run on the same XCD and share its L2.
+#include <type_traits>
+
+#include "launch.h"
+#include "ttv_common.h"
+
+#define TTV_LDS __attribute__((address_space(3)))
+#define TTV_GLOBAL __attribute__((address_space(1)))
+
+namespace ttv {
+
+namespace {
+
+constexpr float kLn2f = 0.693147180559945309f;
+constexpr int kXcds = 8;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // RNE
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | [15:14],
+// expcnt[6:4] = 7 and lgkmcnt[11:8] = 15 mean "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+}  // namespace
+
+template <int D, int QW, int KT, int NST>
+struct MfmaCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int QT = QW / 16;           // 16-query MFMA tiles per wave
+  static constexpr int KS = D / 32;            // 32-wide d steps of K Q^T
+  static constexpr int DT = D / 16;            // 16-wide d tiles of O^T
+  static constexpr int KB = KT / 16;           // 16-key tiles per KV tile
+  static constexpr int PK = KT / 32;           // 32-key steps of V^T P^T
+  static constexpr int CPR = D / 8;            // 16-byte chunks per key row
+  static constexpr int TILE_BYTES = KT * D * 2;        // one K (or V) tile
+  static constexpr int LOADS = TILE_BYTES / 16 / kThreads;  // per thread per tile
+  static constexpr int RB = kWaves * QW;       // query rows per workgroup
+  static constexpr int LDS_BYTES = NST * 2 * TILE_BYTES;
+  static_assert(LOADS >= 1 && TILE_BYTES % (16 * kThreads) == 0, "tile / loads");
+  static_assert(NST == 2, "the pipeline waits assume two stages");
+};
+
+// Chunk swizzles: the physical 16-byte slot of logical chunk c of key row k.
+template <int CPR>
+__device__ __forceinline__ int swz_k(int key, int c) { return c ^ (key & (CPR - 1)); }
+template <int CPR>
+__device__ __forceinline__ int swz_v(int key, int c) { return c ^ ((key << 1) & (CPR - 1)); }
+
+// Tile schedule of one workgroup: chunk 0 first takes the nT in-tree tiles
+// (keys 0..N-1 of k/v_tree, which depend on nothing but N), then every chunk
+// takes its prefix tiles (keys [c*chunk, min(L, (c+1)*chunk)) of k/v_cache).
+struct Sched {
+  int nT, nP, k_begin, k_end;
+  __device__ bool tree(int t) const { return t < nT; }
+  __device__ int key0(int t) const { return t < nT ? t * 64 : k_begin + (t - nT) * 64; }
+};
+
+// 64-query waves need the accumulation registers (AGPRs) of a whole SIMD:
+// one workgroup per CU; narrower waves run two workgroups per CU.
+template <int D, int QW, int KT, int NST>
+__global__ __launch_bounds__(256, (QW >= 64 ? 1 : 2)) void attn_mfma2_kernel(AttnArgs a, int work_items) {
+  using C = MfmaCfg<D, QW, KT, NST>;
+  static_assert(KT == 64, "Sched assumes 64-key tiles");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char s_dyn[];
+  __shared__ uint64_t s_anc[2 * kMaxNodes];
+  __shared__ int32_t s_depth[kMaxNodes];
+  __shared__ int s_status;
+
+  // ---- XCD-first work item: rb fastest, then chunk, then (b, h)
+  const int nb = gridDim.x;
+  const int xcd = blockIdx.x % kXcds;
+  const int per_xcd = (nb + kXcds - 1) / kXcds;
+  const int item = xcd * per_xcd + blockIdx.x / kXcds;
+  if (item >= work_items) return;
+  const int nrb = (a.R + C::RB - 1) / C::RB;
+  const int rb = item % nrb;
+  const int c = (item / nrb) % a.chunks;
+  const int bh = item / (nrb * a.chunks);
+  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g16 = lane >> 4, c16 = lane & 15;
+  const int N = a.N, G = a.G, R = a.R;
+  const int row_base = rb * C::RB + wave * QW;
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+
+  const char* kc = static_cast<const char*>(a.k_cache) + (size_t)bh * a.Lcap * D * 2;
+  const char* vc = static_cast<const char*>(a.v_cache) + (size_t)bh * a.Lcap * D * 2;
+  const char* ktr = static_cast<const char*>(a.k_tree) + (size_t)bh * N * D * 2;
+  const char* vtr = static_cast<const char*>(a.v_tree) + (size_t)bh * N * D * 2;
+
+  // ---- per-lane constants of the HBM -> LDS copies.  Wave w, copy j fills
+  // LDS slots (j*4 + w)*64 + lane of a tile (16 bytes each, placed by the
+  // hardware at base + 16*lane); slot p holds key p / CPR, logical chunk
+  // swz(key, p % CPR), i.e. this lane reads byte offset key*2D + 16*swz(...)
+  // of the tile's first row.
+  uint32_t koff[C::LOADS], voff[C::LOADS];
+  int lkey[C::LOADS];
+#pragma unroll
+  for (int j = 0; j < C::LOADS; ++j) {
+    const int slot = (j * C::kWaves + wave) * 64 + lane;
+    const int key = slot / C::CPR, phys = slot % C::CPR;
+    lkey[j] = key;
+    koff[j] = key * (D * 2) + swz_k<C::CPR>(key, phys) * 16;
+    voff[j] = key * (D * 2) + swz_v<C::CPR>(key, phys) * 16;
+  }
+  Sched sc;
+  sc.nT = (c == 0) ? (N + KT - 1) / KT : 0;
+  sc.nP = 0;
+  sc.k_begin = c * a.chunk_keys;
+  sc.k_end = sc.k_begin;
+  // Copies of tile t into ring stage S.  Keys past the tile's valid ones
+  // re-read the last valid row (finite values; their scores are masked), so
+  // no copy leaves the tensors or reads rows at or beyond the prefix length.
+  auto issue = [&](int tile, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    const bool tree = sc.tree(tile);
+    const int key0 = sc.key0(tile);
+    const int nvalid = tree ? min(KT, N - key0) : min(KT, sc.k_end - key0);
+    const char* ks = (tree ? ktr : kc) + (size_t)key0 * (D * 2);
+    const char* vs = (tree ? vtr : vc) + (size_t)key0 * (D * 2);
+    TTV_LDS unsigned char* kst = (TTV_LDS unsigned char*)(s_dyn + S * 2 * C::TILE_BYTES);
+    TTV_LDS unsigned char* vst = kst + C::TILE_BYTES;
+    const bool full = nvalid == KT;
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      uint32_t ko = koff[j], vo = voff[j];
+      if (!full) {
+        const int shift = (min(lkey[j], nvalid - 1) - lkey[j]) * (D * 2);
+        ko += shift;
+        vo += shift;
+      }
+      const int wbase = (j * C::kWaves + wave) * 1024;
+      __builtin_amdgcn_global_load_lds((TTV_GLOBAL void*)(ks + ko), (TTV_LDS void*)(kst + wbase), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((TTV_GLOBAL void*)(vs + vo), (TTV_LDS void*)(vst + wbase), 16, 0, 0);
+    }
+  };
+
+  // ---- prologue, latency-first: the in-tree tiles (chunk 0) and the queries
+  // are requested before the prefix length and the tree topology arrive
+  int issued = 0;
+  if (sc.nT > 0) {
+    issue(0, std::integral_constant<int, 0>{});
+    issued = 1;
+    if (sc.nT > 1) {
+      issue(1, std::integral_constant<int, 1>{});
+      issued = 2;
+    }
+  }
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  bf16x8 qB[C::QT][C::KS];
+  int qnode[C::QT];
+#pragma unroll
+  for (int qt = 0; qt < C::QT; ++qt) {
+    const int r = row_base + qt * 16 + c16;
+    const bool rv = r < R;
+    const int i = rv ? r / G : 0;
+    qnode[qt] = rv ? i : -1;
+    const int hq = h * G + (rv ? r - i * G : 0);
+    const uint16_t* qr = q + (((size_t)b * N + i) * a.Hq + hq) * D + g16 * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const u32x4 v = rv ? *reinterpret_cast<const u32x4*>(qr + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+      qB[qt][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  const int L = a.cache_len[b];
+  if (wave == 0) {
+    const bool tree_ok = wave_build_tree(a.parents + (size_t)b * N, N, s_anc, s_depth);
+    if (lane == 0) {
+      int st = TTV_OK;
+      if (!tree_ok) st = TTV_E_TREE;
+      else if (L < 0 || L > a.Lmax) st = TTV_E_SHAPE;
+      s_status = st;
+      if (a.dev_status && c == 0 && rb == 0 && h == 0) a.dev_status[b] = st;
+    }
+  }
+  __syncthreads();
+  const int status = s_status;
+  if (status == TTV_OK) {
+    sc.k_end = min(L, sc.k_begin + a.chunk_keys);
+    sc.nP = (sc.k_begin < sc.k_end) ? (sc.k_end - sc.k_begin + KT - 1) / KT : 0;
+  }
+  const int ntiles = status == TTV_OK ? sc.nT + sc.nP : 0;
+  if (issued == 0 && ntiles > 0) {
+    issue(0, std::integral_constant<int, 0>{});
+    issued = 1;
+  }
+  if (issued == 1 && ntiles > 1) {
+    issue(1, std::integral_constant<int, 1>{});
+    issued = 2;
+  }
+
+  uint64_t anc_lo[C::QT], anc_hi[C::QT];
+#pragma unroll
+  for (int qt = 0; qt < C::QT; ++qt) {
+    anc_lo[qt] = qnode[qt] >= 0 ? s_anc[2 * qnode[qt]] : 0ull;
+    anc_hi[qt] = qnode[qt] >= 0 ? s_anc[2 * qnode[qt] + 1] : 0ull;
+  }
+  f32x4 oacc[C::QT][C::DT];
+  float m_run[C::QT], l_run[C::QT];
+#pragma unroll
+  for (int qt = 0; qt < C::QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- per-lane LDS read offsets (stage, key block and 32-key step are
+  // immediates).  K: lane (c16, g16) of key block kb reads row kb*16 + c16,
+  // logical chunk ks*4 + g16; its swizzle depends on c16 only.  V: see the
+  // transposed read below; its swizzle depends on g16*4 + c16/4 only.
+  uint32_t krd[C::KS], vrd[C::DT];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+    krd[ks] = c16 * (D * 2) + swz_k<C::CPR>(c16, ks * 4 + g16) * 16;
+  {
+    const int vkey = g16 * 4 + (c16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int dcol = dt * 16 + 4 * (c16 & 3);
+      vrd[dt] = vkey * (D * 2) + swz_v<C::CPR>(vkey, dcol >> 3) * 16 + ((dcol >> 2) & 1) * 8;
+    }
+  }
+
+  // ---- one tile of math from ring stage S.  Masking is branch free: bit k
+  // of tmask[qt] says whether key key0 + k is visible to this lane's query
+  // (all ones for a full prefix tile; the valid-key prefix for a tail tile;
+  // the ancestor bits for an in-tree tile).
+  auto compute = [&](int tile, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    const TTV_LDS unsigned char* kst = (const TTV_LDS unsigned char*)(s_dyn + S * 2 * C::TILE_BYTES);
+    const TTV_LDS unsigned char* vst = kst + C::TILE_BYTES;
+    const bool tree = sc.tree(tile);
+    const int key0 = sc.key0(tile);
+    const int nvalid = tree ? min(KT, N - key0) : min(KT, sc.k_end - key0);
+    const uint64_t vmask = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+    uint64_t tmask[C::QT];
+#pragma unroll
+    for (int qt = 0; qt < C::QT; ++qt) {
+      const uint64_t w = key0 < 64 ? anc_lo[qt] : anc_hi[qt];
+      tmask[qt] = ((tree ? w : ~0ull) & vmask) >> (g16 * 4);  // lane keys: kb*16 + g16*4 + e
+    }
+    // S^T = K Q^T
+    f32x4 s[C::KB][C::QT];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+      for (int qt = 0; qt < C::QT; ++qt) s[kb][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const u32x4 av = *(const TTV_LDS u32x4*)(kst + krd[ks] + kb * 16 * (D * 2));
+        const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+        for (int qt = 0; qt < C::QT; ++qt)
+          s[kb][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qB[qt][ks], s[kb][qt], 0, 0, 0);
+      }
+    }
+    // online softmax; lane holds keys kb*16 + g16*4 + e of query c16
+    bf16x8 pB[C::QT][C::PK];
+#pragma unroll
+    for (int qt = 0; qt < C::QT; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = (tmask[qt] >> (kb * 16 + e)) & 1ull;
+          const float t = ok ? s[kb][qt][e] * a.scale_log2 : -INFINITY;
+          s[kb][qt][e] = t;
+          mx = fmaxf(mx, t);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[qt], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_use);
+      m_run[qt] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[kb][qt][e] - m_use);
+          s[kb][qt][e] = p;
+          psum += p;
+        }
+      l_run[qt] = l_run[qt] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) oacc[qt][dt] *= alpha;
+      // P^T operands: slots 0-3 = keys 32*k2 + g16*4 + e, 4-7 = +16
+#pragma unroll
+      for (int k2 = 0; k2 < C::PK; ++k2) {
+        const u32x4 pk = {pack2(s[2 * k2][qt][0], s[2 * k2][qt][1]),
+                          pack2(s[2 * k2][qt][2], s[2 * k2][qt][3]),
+                          pack2(s[2 * k2 + 1][qt][0], s[2 * k2 + 1][qt][1]),
+                          pack2(s[2 * k2 + 1][qt][2], s[2 * k2 + 1][qt][3])};
+        pB[qt][k2] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+    // O^T += V^T P^T.  ds_read_b64_tr_b16 gives lane i (of its 16-lane group)
+    // element i%4 of the 8-byte rows fetched by lanes 4j + i/4 of the group;
+    // lane r of group g fetches V[32*k2 + 4g + r/4 (+16)][dt*16 + 4*(r%4) ..+3],
+    // so lane i receives V[32*k2 + 4g + j (+16)][dt*16 + i], j = 0..3: the A
+    // operand row of output column d = dt*16 + i for the P^T key slots.
+#pragma unroll
+    for (int k2 = 0; k2 < C::PK; ++k2) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const TTV_LDS unsigned char* pa = vst + vrd[dt] + k2 * 32 * (D * 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)pa);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)(pa + 16 * (D * 2)));
+        const bf16x8 A = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+        for (int qt = 0; qt < C::QT; ++qt)
+          oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pB[qt][k2], oacc[qt][dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- the pipeline: two tiles in flight.  Each wave waits for its own
+  // copies of the current tile (vmcnt counts the copies issued after them),
+  // then a barrier publishes every wave's copies; after the math a second
+  // barrier frees the stage for the copies of the tile two ahead.  The loop
+  // is unrolled by two so that every LDS offset is an immediate.
+  auto step = [&](int tile, auto stage_tag) {
+    if (tile + 1 < ntiles) wait_vmcnt<2 * C::LOADS>();  // tile+1's copies may stay in flight
+    else wait_vmcnt<0>();
+    __syncthreads();
+    compute(tile, stage_tag);
+    __syncthreads();
+    if (tile + NST < ntiles) issue(tile + NST, stage_tag);
+  };
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    step(tile, std::integral_constant<int, 0>{});
+    if (tile + 1 < ntiles) step(tile + 1, std::integral_constant<int, 1>{});
+  }
+  wait_vmcnt<0>();  // copies issued for a rejected request must land before exit
+
+  // ---- finish: the 4 lanes of a query hold disjoint key subsets of l
+  const bool has_work = ntiles > 0;
+  if (a.chunks == 1) {
+#pragma unroll
+    for (int qt = 0; qt < C::QT; ++qt) {
+      float lt = l_run[qt];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+      const int r = row_base + qt * 16 + c16;
+      if (r >= R) continue;
+      const int i = r / G, hq = h * G + (r - i * G);
+      uint16_t* o = out + (((size_t)b * N + i) * a.Hq + hq) * D;
+      const float inv = has_work ? 1.f / lt : 0.f;  // a rejected request gets zeros
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const f32x4 v = oacc[qt][dt] * inv;
+        *reinterpret_cast<u32x2*>(o + dt * 16 + g16 * 4) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+      }
+      if (g16 == 0 && a.lse)
+        a.lse[((size_t)b * N + i) * a.Hq + hq] = has_work ? (m_run[qt] + __log2f(lt)) * kLn2f : 0.f;
+    }
+    return;
+  }
+
+  // ---- split KV: write the fp32 partial; attn_combine_kernel merges them.
+  // (Merging in the last-arriving workgroup would need a device-scope release
+  // per workgroup, which on this chip writes back the XCD's whole L2 and was
+  // measured slower than a second launch.)
+  if (!has_work) return;
+#pragma unroll
+  for (int qt = 0; qt < C::QT; ++qt) {
+    float lt = l_run[qt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int r = row_base + qt * 16 + c16;
+    if (r >= R) continue;
+    const size_t pr = ((size_t)bh * a.chunks + c) * R + r;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+      *reinterpret_cast<f32x4*>(a.ws_acc + pr * D + dt * 16 + g16 * 4) = oacc[qt][dt];
+    if (g16 == 0) {
+      a.ws_ml[pr * 2] = m_run[qt];
+      a.ws_ml[pr * 2 + 1] = lt;
+    }
+  }
+}
+
+template <int D, int QW, int KT, int NST>
+static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
+  using C = MfmaCfg<D, QW, KT, NST>;
+  const int nrb = (a.R + C::RB - 1) / C::RB;
+  const long items = (long)a.B * a.Hkv * nrb * a.chunks;
+  const long blocks = (items + kXcds - 1) / kXcds * kXcds;
+  auto kern = attn_mfma2_kernel<D, QW, KT, NST>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::kThreads), C::LDS_BYTES, s, a, (int)items);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
+  if (a.D == 64) {
+    switch (a.rows_per_block) {
+      case 64: return launch_cfg<64, 16, 64, 2>(a, s);
+      case 128: return launch_cfg<64, 32, 64, 2>(a, s);
+      default: return launch_cfg<64, 64, 64, 2>(a, s);
+    }
+  }
+  switch (a.rows_per_block) {
+    case 64: return launch_cfg<128, 16, 64, 2>(a, s);
+    case 128: return launch_cfg<128, 32, 64, 2>(a, s);
+    default: return launch_cfg<128, 64, 64, 2>(a, s);
+  }
+}
+
+}  // namespace ttv

@@ -20,17 +20,16 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(
   const int b = blockIdx.x;
   // cache_len_out may alias cache_len_in: only this workgroup touches entry b,
   // and every thread reads it before the barrier that precedes the write.
+  // lengths and the whole path row are requested together (one round trip)
   const int L = cache_len_in[b];
   const int n = path_len[b];
+  const int pj = threadIdx.x < N ? path[(size_t)b * N + threadIdx.x] : -1;
   const bool shape_ok = L >= 0 && L <= Lmax && n >= 0 && n <= N && L + n <= Lcap;
   if (threadIdx.x == 0) s_bad_node = 0;
   __syncthreads();
-  if (shape_ok) {
-    for (int j = threadIdx.x; j < n; j += blockDim.x) {
-      const int p = path[(size_t)b * N + j];
-      s_path[j] = p;
-      if (p < 0 || p >= N) s_bad_node = 1;  // every writer stores the same value
-    }
+  if (threadIdx.x < N) {
+    s_path[threadIdx.x] = pj;
+    if (shape_ok && threadIdx.x < n && (pj < 0 || pj >= N)) s_bad_node = 1;  // same value from every writer
   }
   __syncthreads();
   const bool ok = shape_ok && s_bad_node == 0;

@@ -129,11 +129,14 @@ __global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
   }
 }
 
+// Vocabulary splits per logits row: enough workgroups to cover the chip
+// (~512), at most 4 so the scan merges few partials, none below 4096 entries.
 GreedyPlan greedy_plan(int B, int N, int V) {
   GreedyPlan p;
   const long rows = (long)B * N;
-  long s = (2048 + rows - 1) / rows;
-  const long cap = V / 1024 > 1 ? V / 1024 : 1;
+  long s = (512 + rows - 1) / rows;
+  const long cap = V / 4096 > 1 ? V / 4096 : 1;
+  if (s > 4) s = 4;
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   int slice = (int)((V + s - 1) / s);
@@ -281,9 +284,23 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   }
   __syncthreads();
 
+  // Row passes touch v = t + 1024*k; the loads of 8 consecutive k are issued
+  // together so their latencies overlap.
   auto load_p_row = [&](int u) {
     const float* p = llm + (rowN + u) * V;
-    for (int v = t; v < V; v += kMssThreads) s_w[widx(v)] = p[v];
+    for (int v0 = t; v0 < V; v0 += 8 * kMssThreads) {
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int v = v0 + k * kMssThreads;
+        x[k] = v < V ? p[v] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int v = v0 + k * kMssThreads;
+        if (v < V) s_w[widx(v)] = x[k];
+      }
+    }
     __syncthreads();
   };
 
@@ -328,11 +345,23 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       first = false;
       // rejected: w = max(w - s*q, +0), s = its mass in 2^-40 units
       uint64_t part = 0;
-      for (int v = t; v < V; v += kMssThreads) {
-        const float d = fmaf(-s, q[v], s_w[widx(v)]);
-        const float w = d > 0.0f ? d : 0.0f;
-        s_w[widx(v)] = w;
-        part += fx40(w);
+      for (int v0 = t; v0 < V; v0 += 8 * kMssThreads) {
+        float qv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int v = v0 + k * kMssThreads;
+          qv[k] = v < V ? q[v] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int v = v0 + k * kMssThreads;
+          if (v < V) {
+            const float d = fmaf(-s, qv[k], s_w[widx(v)]);
+            const float w = d > 0.0f ? d : 0.0f;
+            s_w[widx(v)] = w;
+            part += fx40(w);
+          }
+        }
       }
       const uint64_t S = block_sum_u64(part, s_red);  // its barriers publish s_w
       s = (float)((double)S * 0x1p-40);
