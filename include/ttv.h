@@ -103,7 +103,8 @@ ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents,
  *   B,N         requests, tree nodes per request (1 <= N <= 128).
  *   Hq,Hkv,D    query heads, key/value heads (Hq % Hkv == 0; query head hq
  *               reads kv head hq / (Hq/Hkv)), head dim D in {64,128}.
- *   scale       softmax scale applied to q.k (usually 1/sqrt(D)).
+ *   scale       softmax scale applied to q.k, finite and > 0 (usually
+ *               1/sqrt(D)); TTV_E_SHAPE otherwise.
  *   q           [B,N,Hq,D]  queries of the tree nodes (positions already
  *               encoded by the caller at L_b + depth).
  *   k_cache,v_cache [B,Hkv,Lcap,D]  prefix cache; rows 0..L_b-1 are read.

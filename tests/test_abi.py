@@ -69,6 +69,7 @@ def attn(**kw):
     (dict(out=None), ttv.E_NULL), (dict(cl=None), ttv.E_NULL),
     (dict(B=0), ttv.E_SHAPE), (dict(N=0), ttv.E_SHAPE), (dict(Lmax=129), ttv.E_SHAPE),
     (dict(Lmax=-1), ttv.E_SHAPE), (dict(scale=float("nan")), ttv.E_SHAPE),
+    (dict(scale=0.0), ttv.E_SHAPE), (dict(scale=-0.125), ttv.E_SHAPE),
     (dict(N=129), ttv.E_UNSUPPORTED), (dict(D=96), ttv.E_UNSUPPORTED),
     (dict(Hq=6, Hkv=4), ttv.E_UNSUPPORTED), (dict(rpb=96), ttv.E_UNSUPPORTED),
     (dict(ck=100), ttv.E_UNSUPPORTED), (dict(dt=0, rpb=64), ttv.E_UNSUPPORTED),

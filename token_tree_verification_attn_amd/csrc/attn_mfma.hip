@@ -56,9 +56,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 }  // namespace
 
-template <int D, int QW, int KT, int NST>
+template <int D, int QW, int NW, int NST>
 struct MfmaCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int KT = 64;                // keys per tile
+  static constexpr int kWaves = NW;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int QT = QW / 16;           // 16-query MFMA tiles per wave
   static constexpr int KS = D / 32;            // 32-wide d steps of K Q^T
@@ -70,8 +71,11 @@ struct MfmaCfg {
   static constexpr int LOADS = TILE_BYTES / 16 / kThreads;  // per thread per tile
   static constexpr int RB = kWaves * QW;       // query rows per workgroup
   static constexpr int LDS_BYTES = NST * 2 * TILE_BYTES;
+  // workgroups per CU the launch bounds promise: one whole-SIMD wave (QW 64),
+  // two waves per SIMD otherwise
+  static constexpr int MIN_BLOCKS = (QW >= 64 || NW >= 8) ? 1 : 2;
   static_assert(LOADS >= 1 && TILE_BYTES % (16 * kThreads) == 0, "tile / loads");
-  static_assert(NST == 2, "the pipeline waits assume two stages");
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
 };
 
 // Chunk swizzles: the physical 16-byte slot of logical chunk c of key row k.
@@ -89,12 +93,11 @@ struct Sched {
   __device__ int key0(int t) const { return t < nT ? t * 64 : k_begin + (t - nT) * 64; }
 };
 
-// 64-query waves need the accumulation registers (AGPRs) of a whole SIMD:
-// one workgroup per CU; narrower waves run two workgroups per CU.
-template <int D, int QW, int KT, int NST>
-__global__ __launch_bounds__(256, (QW >= 64 ? 1 : 2)) void attn_mfma2_kernel(AttnArgs a, int work_items) {
-  using C = MfmaCfg<D, QW, KT, NST>;
-  static_assert(KT == 64, "Sched assumes 64-key tiles");
+template <int D, int QW, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) void attn_mfma2_kernel(
+    AttnArgs a, int work_items) {
+  using C = MfmaCfg<D, QW, NW, NST>;
+  constexpr int KT = C::KT;
   extern __shared__ __attribute__((aligned(1024))) unsigned char s_dyn[];
   __shared__ uint64_t s_anc[2 * kMaxNodes];
   __shared__ int32_t s_depth[kMaxNodes];
@@ -170,17 +173,21 @@ __global__ __launch_bounds__(256, (QW >= 64 ? 1 : 2)) void attn_mfma2_kernel(Att
     }
   };
 
-  // ---- prologue, latency-first: the in-tree tiles (chunk 0) and the queries
-  // are requested before the prefix length and the tree topology arrive
-  int issued = 0;
-  if (sc.nT > 0) {
-    issue(0, std::integral_constant<int, 0>{});
-    issued = 1;
-    if (sc.nT > 1) {
-      issue(1, std::integral_constant<int, 1>{});
-      issued = 2;
+  // tile -> its ring stage as a compile-time constant (LDS offsets are immediates)
+  auto issue_any = [&](int tile) {
+    switch (tile % NST) {
+      case 0: issue(tile, std::integral_constant<int, 0>{}); break;
+      case 1: issue(tile, std::integral_constant<int, 1 % NST>{}); break;
+      case 2: issue(tile, std::integral_constant<int, 2 % NST>{}); break;
+      default: issue(tile, std::integral_constant<int, 3 % NST>{}); break;
     }
-  }
+  };
+
+  // ---- prologue, latency-first: the in-tree tiles (chunk 0) and the queries
+  // are requested before the prefix length and the tree topology arrive.
+  // Tiles 0 .. NST-2 are in flight when the loop starts.
+  int issued = 0;
+  while (issued < sc.nT && issued < NST - 1) issue_any(issued++);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   bf16x8 qB[C::QT][C::KS];
   int qnode[C::QT];
@@ -216,14 +223,7 @@ __global__ __launch_bounds__(256, (QW >= 64 ? 1 : 2)) void attn_mfma2_kernel(Att
     sc.nP = (sc.k_begin < sc.k_end) ? (sc.k_end - sc.k_begin + KT - 1) / KT : 0;
   }
   const int ntiles = status == TTV_OK ? sc.nT + sc.nP : 0;
-  if (issued == 0 && ntiles > 0) {
-    issue(0, std::integral_constant<int, 0>{});
-    issued = 1;
-  }
-  if (issued == 1 && ntiles > 1) {
-    issue(1, std::integral_constant<int, 1>{});
-    issued = 2;
-  }
+  while (issued < ntiles && issued < NST - 1) issue_any(issued++);
 
   uint64_t anc_lo[C::QT], anc_hi[C::QT];
 #pragma unroll
@@ -258,10 +258,18 @@ __global__ __launch_bounds__(256, (QW >= 64 ? 1 : 2)) void attn_mfma2_kernel(Att
     }
   }
 
-  // ---- one tile of math from ring stage S.  Masking is branch free: bit k
-  // of tmask[qt] says whether key key0 + k is visible to this lane's query
-  // (all ones for a full prefix tile; the valid-key prefix for a tail tile;
-  // the ancestor bits for an in-tree tile).
+  // ---- one tile of math from ring stage S.
+  // Masking: bit k of tmask[qt] says whether key key0 + k is visible to this
+  // lane's query (the valid-key prefix for a tail tile, the ancestor bits for
+  // an in-tree tile); full prefix tiles skip it.
+  // Softmax: scores stay raw until the exponent, exp2(s*c - m) with
+  // c = scale*log2(e) > 0, so masked scores are -inf and the max is taken on
+  // raw scores.  The running max m only moves when a tile's max exceeds it by
+  // more than kLazy (log2 units); the probabilities are then at most 2^kLazy,
+  // which is exact after the final normalisation and far from fp32 overflow,
+  // and the rescale of O is skipped when no query of the wave needs it.
+  constexpr float kLazy = 8.0f;
+  const float cs = a.scale_log2;
   auto compute = [&](int tile, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
     const TTV_LDS unsigned char* kst = (const TTV_LDS unsigned char*)(s_dyn + S * 2 * C::TILE_BYTES);
@@ -269,60 +277,92 @@ __global__ __launch_bounds__(256, (QW >= 64 ? 1 : 2)) void attn_mfma2_kernel(Att
     const bool tree = sc.tree(tile);
     const int key0 = sc.key0(tile);
     const int nvalid = tree ? min(KT, N - key0) : min(KT, sc.k_end - key0);
-    const uint64_t vmask = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
-    uint64_t tmask[C::QT];
+    const bool masked = tree || nvalid < KT;
+    // K fragments of the whole tile first: one LDS latency for all of them
+    u32x4 kf[C::KB][C::KS];
 #pragma unroll
-    for (int qt = 0; qt < C::QT; ++qt) {
-      const uint64_t w = key0 < 64 ? anc_lo[qt] : anc_hi[qt];
-      tmask[qt] = ((tree ? w : ~0ull) & vmask) >> (g16 * 4);  // lane keys: kb*16 + g16*4 + e
-    }
-    // S^T = K Q^T
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        kf[kb][ks] = *(const TTV_LDS u32x4*)(kst + krd[ks] + kb * 16 * (D * 2));
+    // S^T = K Q^T, d-step outermost so that KB*QT independent accumulations
+    // sit between two MFMAs of one chain
     f32x4 s[C::KB][C::QT];
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int qt = 0; qt < C::QT; ++qt) s[kb][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const u32x4 av = *(const TTV_LDS u32x4*)(kst + krd[ks] + kb * 16 * (D * 2));
-        const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const bf16x8 A = __builtin_bit_cast(bf16x8, kf[kb][ks]);
 #pragma unroll
         for (int qt = 0; qt < C::QT; ++qt)
           s[kb][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qB[qt][ks], s[kb][qt], 0, 0, 0);
       }
+    // V^T fragments are requested now; their latency hides behind the softmax.
+    // ds_read_b64_tr_b16 gives lane i (of its 16-lane group) element i%4 of
+    // the 8-byte rows fetched by lanes 4j + i/4 of the group; lane r of group
+    // g fetches V[32*k2 + 4g + r/4 (+16)][dt*16 + 4*(r%4) ..+3], so lane i
+    // receives V[32*k2 + 4g + j (+16)][dt*16 + i], j = 0..3: the A operand
+    // row of output column dt*16 + i for the P^T key slots.
+    // (With two or more query tiles per wave the registers run short; those
+    // shapes fetch each 32-key step's fragments right before its MFMAs.)
+    constexpr bool kEarlyV = C::QT == 1;
+    i16x4 vlo[C::PK][C::DT], vhi[C::PK][C::DT];
+    auto fetch_v = [&](int k2) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const TTV_LDS unsigned char* pa = vst + vrd[dt] + k2 * 32 * (D * 2);
+        vlo[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)pa);
+        vhi[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)(pa + 16 * (D * 2)));
+      }
+    };
+    if (kEarlyV) {
+#pragma unroll
+      for (int k2 = 0; k2 < C::PK; ++k2) fetch_v(k2);
     }
     // online softmax; lane holds keys kb*16 + g16*4 + e of query c16
     bf16x8 pB[C::QT][C::PK];
+    float alpha[C::QT];
+    bool any_rescale = false;
 #pragma unroll
     for (int qt = 0; qt < C::QT; ++qt) {
+      if (masked) {
+        const uint64_t w = key0 < 64 ? anc_lo[qt] : anc_hi[qt];
+        const uint64_t vmask = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
+        const uint64_t tm = ((tree ? w : ~0ull) & vmask) >> (g16 * 4);  // lane keys: kb*16 + g16*4 + e
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!((tm >> (kb * 16 + e)) & 1ull)) s[kb][qt][e] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = (tmask[qt] >> (kb * 16 + e)) & 1ull;
-          const float t = ok ? s[kb][qt][e] * a.scale_log2 : -INFINITY;
-          s[kb][qt][e] = t;
-          mx = fmaxf(mx, t);
-        }
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[kb][qt][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qt], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_use);
+      const float mt = mx * cs;  // this tile's max in log2 units (-inf if all masked)
+      const bool move = mt > m_run[qt] + kLazy;  // false while both are -inf
+      const float m_new = move ? mt : m_run[qt];
+      alpha[qt] = move ? __builtin_amdgcn_exp2f(m_run[qt] - m_new) : 1.f;
+      any_rescale |= move;
       m_run[qt] = m_new;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[kb][qt][e] - m_use);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qt][e], cs, -m_use));
           s[kb][qt][e] = p;
           psum += p;
         }
-      l_run[qt] = l_run[qt] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) oacc[qt][dt] *= alpha;
+      l_run[qt] = l_run[qt] * alpha[qt] + psum;
       // P^T operands: slots 0-3 = keys 32*k2 + g16*4 + e, 4-7 = +16
 #pragma unroll
       for (int k2 = 0; k2 < C::PK; ++k2) {
@@ -333,18 +373,19 @@ __global__ __launch_bounds__(256, (QW >= 64 ? 1 : 2)) void attn_mfma2_kernel(Att
         pB[qt][k2] = __builtin_bit_cast(bf16x8, pk);
       }
     }
-    // O^T += V^T P^T.  ds_read_b64_tr_b16 gives lane i (of its 16-lane group)
-    // element i%4 of the 8-byte rows fetched by lanes 4j + i/4 of the group;
-    // lane r of group g fetches V[32*k2 + 4g + r/4 (+16)][dt*16 + 4*(r%4) ..+3],
-    // so lane i receives V[32*k2 + 4g + j (+16)][dt*16 + i], j = 0..3: the A
-    // operand row of output column d = dt*16 + i for the P^T key slots.
+    if (__builtin_amdgcn_ballot_w64(any_rescale)) {
+#pragma unroll
+      for (int qt = 0; qt < C::QT; ++qt)
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) oacc[qt][dt] *= alpha[qt];
+    }
+    // O^T += V^T P^T
 #pragma unroll
     for (int k2 = 0; k2 < C::PK; ++k2) {
+      if (!kEarlyV) fetch_v(k2);
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const TTV_LDS unsigned char* pa = vst + vrd[dt] + k2 * 32 * (D * 2);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)pa);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)(pa + 16 * (D * 2)));
+        const i16x4 lo = vlo[k2][dt], hi = vhi[k2][dt];
         const bf16x8 A = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
             lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
@@ -354,22 +395,27 @@ __global__ __launch_bounds__(256, (QW >= 64 ? 1 : 2)) void attn_mfma2_kernel(Att
     }
   };
 
-  // ---- the pipeline: two tiles in flight.  Each wave waits for its own
-  // copies of the current tile (vmcnt counts the copies issued after them),
-  // then a barrier publishes every wave's copies; after the math a second
-  // barrier frees the stage for the copies of the tile two ahead.  The loop
-  // is unrolled by two so that every LDS offset is an immediate.
+  // ---- the pipeline: NST-1 tiles in flight during each tile's math.  Each
+  // wave waits for its own copies of the current tile (vmcnt counts the
+  // copies issued after them), then one barrier both publishes every wave's
+  // copies and proves that every wave has finished the previous tile, whose
+  // stage then receives the copies of the tile NST-1 ahead.  The loop is
+  // unrolled by NST so that every LDS offset is an immediate.
   auto step = [&](int tile, auto stage_tag) {
-    if (tile + 1 < ntiles) wait_vmcnt<2 * C::LOADS>();  // tile+1's copies may stay in flight
+    constexpr int S = decltype(stage_tag)::value;
+    const int ahead = min(NST - 2, ntiles - 1 - tile);  // tiles issued after this one
+    if (ahead >= 2) wait_vmcnt<4 * C::LOADS>();
+    else if (ahead == 1) wait_vmcnt<2 * C::LOADS>();
     else wait_vmcnt<0>();
     __syncthreads();
+    if (tile + NST - 1 < ntiles) issue(tile + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
     compute(tile, stage_tag);
-    __syncthreads();
-    if (tile + NST < ntiles) issue(tile + NST, stage_tag);
   };
-  for (int tile = 0; tile < ntiles; tile += 2) {
+  for (int tile = 0; tile < ntiles; tile += NST) {
     step(tile, std::integral_constant<int, 0>{});
-    if (tile + 1 < ntiles) step(tile + 1, std::integral_constant<int, 1>{});
+    if (tile + 1 < ntiles) step(tile + 1, std::integral_constant<int, 1 % NST>{});
+    if (NST > 2 && tile + 2 < ntiles) step(tile + 2, std::integral_constant<int, 2 % NST>{});
+    if (NST > 3 && tile + 3 < ntiles) step(tile + 3, std::integral_constant<int, 3 % NST>{});
   }
   wait_vmcnt<0>();  // copies issued for a rejected request must land before exit
 
@@ -420,13 +466,13 @@ __global__ __launch_bounds__(256, (QW >= 64 ? 1 : 2)) void attn_mfma2_kernel(Att
   }
 }
 
-template <int D, int QW, int KT, int NST>
+template <int D, int QW, int NW, int NST>
 static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
-  using C = MfmaCfg<D, QW, KT, NST>;
+  using C = MfmaCfg<D, QW, NW, NST>;
   const int nrb = (a.R + C::RB - 1) / C::RB;
   const long items = (long)a.B * a.Hkv * nrb * a.chunks;
   const long blocks = (items + kXcds - 1) / kXcds * kXcds;
-  auto kern = attn_mfma2_kernel<D, QW, KT, NST>;
+  auto kern = attn_mfma2_kernel<D, QW, NW, NST>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (e != hipSuccess) return e;
@@ -434,18 +480,21 @@ static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// rows per workgroup -> shape: 64 rows = 4 waves x 16 queries, two 64 KB
+// workgroups per CU; 128 = 8 x 16 and 256 = 8 x 32, one workgroup per CU
+// with a 4-deep 128 KB ring.
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.D == 64) {
     switch (a.rows_per_block) {
-      case 64: return launch_cfg<64, 16, 64, 2>(a, s);
-      case 128: return launch_cfg<64, 32, 64, 2>(a, s);
-      default: return launch_cfg<64, 64, 64, 2>(a, s);
+      case 64: return launch_cfg<64, 16, 4, 2>(a, s);
+      case 128: return launch_cfg<64, 16, 8, 4>(a, s);
+      default: return launch_cfg<64, 32, 8, 4>(a, s);
     }
   }
   switch (a.rows_per_block) {
-    case 64: return launch_cfg<128, 16, 64, 2>(a, s);
-    case 128: return launch_cfg<128, 32, 64, 2>(a, s);
-    default: return launch_cfg<128, 64, 64, 2>(a, s);
+    case 64: return launch_cfg<128, 16, 4, 2>(a, s);
+    case 128: return launch_cfg<128, 16, 8, 4>(a, s);
+    default: return launch_cfg<128, 32, 8, 4>(a, s);
   }
 }
 

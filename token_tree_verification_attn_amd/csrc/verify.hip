@@ -39,11 +39,24 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __rest
   float bv = -INFINITY;
   int bi = INT_MAX;
   if (VEC) {
+    // 8 independent 16-byte loads in flight per thread, merged in index order
     const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
-    for (int f = v0 / 4 + threadIdx.x; f < v1 / 4; f += 256) {
-      const f32x4 q = __builtin_nontemporal_load(x4 + f);
+    const int f1 = v1 / 4;
+    for (int f0 = v0 / 4 + threadIdx.x; f0 < f1; f0 += 8 * 256) {
+      f32x4 q[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) amax_merge(bv, bi, q[e], 4 * f + e);
+      for (int k = 0; k < 8; ++k) {
+        const int f = f0 + k * 256;
+        q[k] = f < f1 ? __builtin_nontemporal_load(x4 + f) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int f = f0 + k * 256;
+        if (f < f1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) amax_merge(bv, bi, q[k][e], 4 * f + e);
+        }
+      }
     }
   } else {
     for (int v = v0 + threadIdx.x; v < v1; v += 256) amax_merge(bv, bi, x[v], v);
