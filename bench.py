@@ -169,7 +169,7 @@ def attn_work(d):
 def source_hash():
     """Hash of the attention kernel sources a stored counter profile belongs to."""
     h = hashlib.sha256()
-    for f in ("attn.hip", "ttv_common.h", "api.cpp"):
+    for f in ("attn.hip", "attn_mfma.hip", "ttv_common.h", "launch.h", "api.cpp"):
         h.update(open(os.path.join(ROOT, "token_tree_verification_attn_amd", "csrc", f),
                       "rb").read())
     return h.hexdigest()[:16]

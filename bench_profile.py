@@ -55,7 +55,8 @@ def rocprof(outdir, args, prog, timeout):
         sys.stderr.write(res.stdout[-3000:] + res.stderr[-3000:])
         raise SystemExit("rocprofv3 produced no results (rc %d)" % res.returncode)
     print("  %.1f s: %s" % (time.time() - t0, " ".join(cmd)), flush=True)
-    return {os.path.basename(f): f for f in files}, " ".join(cmd)
+    # the checkout's own path differs from machine to machine
+    return {os.path.basename(f): f for f in files}, " ".join(cmd).replace(ROOT, "<repo>")
 
 
 def counter_kib(files, counter, match):
