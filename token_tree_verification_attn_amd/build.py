@@ -5,7 +5,9 @@
 All HIP sources and the C-ABI host code go into one shared library next to this
 file.  Packed-fp32 instruction selection is turned off for every device
 compile (-packed-fp32-ops); the host pass warns that it does not know that
-feature, which is harmless.
+feature, which is harmless.  Matrix-core results are kept in ordinary VGPRs
+(-amdgpu-mfma-vgpr-form): the attention scores feed vector ALU work right
+after their MFMAs, and accumulator registers would cost a copy each way.
 """
 from __future__ import annotations
 
@@ -25,6 +27,7 @@ FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
 

@@ -34,22 +34,25 @@ ttv_status attn_plan(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, int Lma
   p->mfma = dt == TTV_BF16 && R >= 16;
   const long pairs = (long)B * Hkv;
   if (pairs > kMaxGridYZ) return TTV_E_UNSUPPORTED;
-  // Workgroups that fit on the chip at once: two 4-wave (64-row) workgroups
-  // or one 8-wave (128/256-row) workgroup per CU, 256 CUs.
+  // Workgroups that fit on the chip at once: one matrix-core workgroup per CU
+  // (its copy ring takes 128 KB of LDS), two FMA workgroups; 256 CUs.
   long slots = 512;
   if (p->mfma) {
     if (rpb_hint) {
       if (rpb_hint != 64 && rpb_hint != 128 && rpb_hint != 256) return TTV_E_UNSUPPORTED;
       p->rows_per_block = rpb_hint;
     } else {
-      // the widest row block R fills: every extra row block of a kv head
-      // re-reads that head's KV (from L2, but through the CU's copy engine),
-      // so idle CUs are filled by splitting the prefix instead (measured on
-      // MI355X: e.g. 64 q rows per kv head x 32768 keys runs 27% faster as
-      // 256-row blocks with a 2-way split than as 128-row blocks unsplit)
-      p->rows_per_block = R <= 64 ? 64 : (R <= 128 ? 128 : 256);
+      // 128-row blocks (8 waves x 16 queries) up to 512 rows per kv head:
+      // their softmax work per wave is the lightest, and a second row block
+      // re-reads the head's KV from L2 rather than HBM.  Above that, every
+      // extra row block costs one more pass of the KV through the CU copy
+      // engines, and 256-row blocks win.  (Measured on MI355X: 256 rows x
+      // 2048 keys per head, 128-row blocks unsplit run 13% faster than
+      // 256-row blocks with a 2-way split; 1024 rows x 32768 keys, 256-row
+      // blocks run 17% faster than 128-row ones.)
+      p->rows_per_block = R <= 64 ? 64 : (R <= 512 ? 128 : 256);
     }
-    if (p->rows_per_block > 64) slots = 256;
+    slots = 256;
   } else {
     if (rpb_hint && rpb_hint != 16) return TTV_E_UNSUPPORTED;
     p->rows_per_block = 16;

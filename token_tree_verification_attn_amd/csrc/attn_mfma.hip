@@ -8,7 +8,7 @@
 //   S^T[key][query] = K Q^T     v_mfma_f32_16x16x32_bf16, A = K (LDS,
 //                               ds_read_b128), B = the wave's queries (VGPRs)
 //   online softmax on S^T       a query's KT scores sit in 4 lanes x KT/16
-//                               registers; its max needs two xor-shuffles
+//                               registers; its max needs two lane swaps
 //   O^T[d][query] += V^T P^T    A = V^T read from the row-major V tile with
 //                               ds_read_b64_tr_b16, B = P^T straight from the
 //                               S^T registers (bf16 by v_cvt_pk_bf16_f32)
@@ -54,6 +54,56 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// One HBM -> LDS copy of 16 bytes per lane: lane l's 16 bytes at gptr land
+// at LDS address lds_base + 16*l (lds_base is wave-uniform, passed in M0).
+// It is written as inline assembly on purpose.  The compiler's memory-counter
+// bookkeeping treats an LDS-DMA copy as a pending write to all of LDS, and
+// before every later LDS read it cannot tell apart from the copy's target --
+// the transposed V reads -- it drains every copy in flight (vmcnt(0)), which
+// defeats the ring.  Issued this way the copies are ordered by the ring's own
+// waits instead (wait_vmcnt for this wave's copies, then ring_barrier).
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(base), "v"(gptr) : "memory", "m0");
+}
+
+// Workgroup barrier for the copy ring.  __syncthreads() carries
+// workgroup-scope fences, and the compiler may satisfy them by draining every
+// outstanding vector-memory operation (vmcnt(0)), which would also wait for
+// the tiles still in flight.  Here the caller has already waited for the
+// copies that must have landed (wait_vmcnt), LDS reads are drained
+// explicitly, and the compiler-only fences keep LDS accesses on their side
+// of the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Reductions over the lanes l, l^16, l^32, l^48 (the four lanes that hold one
+// query's scores): v_permlane16_swap / v_permlane32_swap exchange the halves
+// of each 32-lane (64-lane) group in the VALU, with no LDS round trip.
+// Called with the same register twice, each returns both halves' values in
+// every lane (one in each result), so combining the two results reduces over
+// the pair.
+__device__ __forceinline__ float red16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float red32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float red16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float red32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace
 
 template <int D, int QW, int NW, int NST>
@@ -71,9 +121,8 @@ struct MfmaCfg {
   static constexpr int LOADS = TILE_BYTES / 16 / kThreads;  // per thread per tile
   static constexpr int RB = kWaves * QW;       // query rows per workgroup
   static constexpr int LDS_BYTES = NST * 2 * TILE_BYTES;
-  // workgroups per CU the launch bounds promise: one whole-SIMD wave (QW 64),
-  // two waves per SIMD otherwise
-  static constexpr int MIN_BLOCKS = (QW >= 64 || NW >= 8) ? 1 : 2;
+  // one workgroup per CU: the 4-deep ring takes 128 KB of LDS
+  static constexpr int MIN_BLOCKS = 1;
   static_assert(LOADS >= 1 && TILE_BYTES % (16 * kThreads) == 0, "tile / loads");
   static_assert(NST >= 2 && NST <= 4, "ring depth");
 };
@@ -168,8 +217,8 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
         vo += shift;
       }
       const int wbase = (j * C::kWaves + wave) * 1024;
-      __builtin_amdgcn_global_load_lds((TTV_GLOBAL void*)(ks + ko), (TTV_LDS void*)(kst + wbase), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((TTV_GLOBAL void*)(vs + vo), (TTV_LDS void*)(vst + wbase), 16, 0, 0);
+      lds_dma16(ks + ko, (uint32_t)(uintptr_t)(kst + wbase));
+      lds_dma16(vs + vo, (uint32_t)(uintptr_t)(vst + wbase));
     }
   };
 
@@ -205,7 +254,17 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
       qB[qt][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // The prefix tiles need only L: they are requested as soon as it arrives,
+  // before the tree topology is built.  L is clamped to [0, Lmax] for the
+  // copies, so they stay inside the cache even when L is invalid; such a
+  // request is rejected below and its copies are drained unused.
   const int L = a.cache_len[b];
+  {
+    const int Lc = min(max(L, 0), a.Lmax);
+    sc.k_end = min(Lc, sc.k_begin + a.chunk_keys);
+    sc.nP = (sc.k_begin < sc.k_end) ? (sc.k_end - sc.k_begin + KT - 1) / KT : 0;
+  }
+  while (issued < sc.nT + sc.nP && issued < NST - 1) issue_any(issued++);
   if (wave == 0) {
     const bool tree_ok = wave_build_tree(a.parents + (size_t)b * N, N, s_anc, s_depth);
     if (lane == 0) {
@@ -218,12 +277,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   }
   __syncthreads();
   const int status = s_status;
-  if (status == TTV_OK) {
-    sc.k_end = min(L, sc.k_begin + a.chunk_keys);
-    sc.nP = (sc.k_begin < sc.k_end) ? (sc.k_end - sc.k_begin + KT - 1) / KT : 0;
-  }
   const int ntiles = status == TTV_OK ? sc.nT + sc.nP : 0;
-  while (issued < ntiles && issued < NST - 1) issue_any(issued++);
 
   uint64_t anc_lo[C::QT], anc_hi[C::QT];
 #pragma unroll
@@ -344,8 +398,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[kb][qt][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = red32_max(red16_max(mx));
       const float mt = mx * cs;  // this tile's max in log2 units (-inf if all masked)
       const bool move = mt > m_run[qt] + kLazy;  // false while both are -inf
       const float m_new = move ? mt : m_run[qt];
@@ -407,7 +460,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     if (ahead >= 2) wait_vmcnt<4 * C::LOADS>();
     else if (ahead == 1) wait_vmcnt<2 * C::LOADS>();
     else wait_vmcnt<0>();
-    __syncthreads();
+    ring_barrier();
     if (tile + NST - 1 < ntiles) issue(tile + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
     compute(tile, stage_tag);
   };
@@ -424,9 +477,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   if (a.chunks == 1) {
 #pragma unroll
     for (int qt = 0; qt < C::QT; ++qt) {
-      float lt = l_run[qt];
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
+      const float lt = red32_sum(red16_sum(l_run[qt]));
       const int r = row_base + qt * 16 + c16;
       if (r >= R) continue;
       const int i = r / G, hq = h * G + (r - i * G);
@@ -450,9 +501,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   if (!has_work) return;
 #pragma unroll
   for (int qt = 0; qt < C::QT; ++qt) {
-    float lt = l_run[qt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = red32_sum(red16_sum(l_run[qt]));
     const int r = row_base + qt * 16 + c16;
     if (r >= R) continue;
     const size_t pr = ((size_t)bh * a.chunks + c) * R + r;
@@ -480,19 +529,18 @@ static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// rows per workgroup -> shape: 64 rows = 4 waves x 16 queries, two 64 KB
-// workgroups per CU; 128 = 8 x 16 and 256 = 8 x 32, one workgroup per CU
-// with a 4-deep 128 KB ring.
+// rows per workgroup -> shape: 64 rows = 4 waves x 16 queries, 128 = 8 x 16
+// and 256 = 8 x 32; each one workgroup per CU with a 4-deep 128 KB ring.
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.D == 64) {
     switch (a.rows_per_block) {
-      case 64: return launch_cfg<64, 16, 4, 2>(a, s);
+      case 64: return launch_cfg<64, 16, 4, 4>(a, s);
       case 128: return launch_cfg<64, 16, 8, 4>(a, s);
       default: return launch_cfg<64, 32, 8, 4>(a, s);
     }
   }
   switch (a.rows_per_block) {
-    case 64: return launch_cfg<128, 16, 4, 2>(a, s);
+    case 64: return launch_cfg<128, 16, 4, 4>(a, s);
     case 128: return launch_cfg<128, 16, 8, 4>(a, s);
     default: return launch_cfg<128, 32, 8, 4>(a, s);
   }

@@ -1,15 +1,21 @@
 // commit.hip -- ttv_kv_commit: append the accepted path's KV rows to the
 // contiguous cache ([SI] §4 "Tree-Based Parallel Decoding": verified and
 // speculated tokens share one key-value cache; what stays is the accepted
-// path).  One workgroup per request copies its Hkv * path_len rows of K and V
-// in 16-byte vectors; it reads the path straight from the verifier's device
-// output, so no host round trip sits between the two calls.
+// path).  One workgroup of 1024 threads per request copies its
+// Hkv * path_len rows of K and V in 16-byte vectors, kCommitIlp vectors of
+// each per thread in flight at once; it reads the path straight from the
+// verifier's device output, so no host round trip sits between the two calls.
+// (One workgroup per request keeps cache_len_out[b] = L + n ordered after
+// every read of cache_len_in[b], which the two arrays may share.)
 #include "launch.h"
 #include "ttv_common.h"
 
 namespace ttv {
 
-__global__ __launch_bounds__(256) void kv_commit_kernel(
+constexpr int kCommitThreads = 1024;
+constexpr int kCommitIlp = 4;
+
+__global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
     int row_bytes, int N, int Hkv, int Lcap, int Lmax, const u32x4* __restrict__ k_tree,
     const u32x4* __restrict__ v_tree, u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
     const int32_t* __restrict__ cache_len_in, int32_t* cache_len_out,
@@ -37,15 +43,31 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(
     const int vec = row_bytes / 16;  // 16-byte vectors per row
     const int per_head = n * vec;
     const int total = Hkv * per_head;
-    for (int t = threadIdx.x; t < total; t += blockDim.x) {
-      const int h = t / per_head;
-      const int r = t - h * per_head;
-      const int j = r / vec;
-      const int e = r - j * vec;
-      const size_t src = (((size_t)b * Hkv + h) * N + s_path[j]) * vec + e;
-      const size_t dst = (((size_t)b * Hkv + h) * Lcap + (L + j)) * vec + e;
-      k_cache[dst] = k_tree[src];
-      v_cache[dst] = v_tree[src];
+    for (int t0 = threadIdx.x; t0 < total; t0 += kCommitIlp * kCommitThreads) {
+      // all loads of this round first, then the stores
+      size_t dst[kCommitIlp];
+      u32x4 kv[kCommitIlp], vv[kCommitIlp];
+#pragma unroll
+      for (int u = 0; u < kCommitIlp; ++u) {
+        const int t = t0 + u * kCommitThreads;
+        if (t < total) {
+          const int h = t / per_head;
+          const int r = t - h * per_head;
+          const int j = r / vec;
+          const int e = r - j * vec;
+          const size_t src = (((size_t)b * Hkv + h) * N + s_path[j]) * vec + e;
+          dst[u] = (((size_t)b * Hkv + h) * Lcap + (L + j)) * vec + e;
+          kv[u] = k_tree[src];
+          vv[u] = v_tree[src];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCommitIlp; ++u) {
+        if (t0 + u * kCommitThreads < total) {
+          k_cache[dst[u]] = kv[u];
+          v_cache[dst[u]] = vv[u];
+        }
+      }
     }
   }
   if (committed_src) {
@@ -65,7 +87,7 @@ hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,
                             int32_t* cache_len_out, int Lmax, const int32_t* path,
                             const int32_t* path_len, int32_t* committed_src,
                             int32_t* dev_status, hipStream_t s) {
-  hipLaunchKernelGGL(kv_commit_kernel, dim3(B), dim3(256), 0, s, D * elt, N, Hkv, Lcap, Lmax,
+  hipLaunchKernelGGL(kv_commit_kernel, dim3(B), dim3(kCommitThreads), 0, s, D * elt, N, Hkv, Lcap, Lmax,
                      static_cast<const u32x4*>(k_tree), static_cast<const u32x4*>(v_tree),
                      static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), cache_len_in,
                      cache_len_out, path, path_len, committed_src, dev_status);
