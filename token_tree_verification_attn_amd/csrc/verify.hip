@@ -195,9 +195,33 @@ __device__ __forceinline__ uint64_t fx40(float x) {
   if (sh <= -24) return 0ull;
   return m >> (-sh);
 }
-// LDS index of vocabulary entry v: one pad word every 32 keeps both the
-// strided (v = k*1024 + t) and the contiguous per-thread walks conflict-free.
-__device__ __forceinline__ int widx(int v) { return v + (v >> 5); }
+// LDS index of vocabulary entry v: four pad words after every 128 keep the
+// 16-byte accesses of the row passes aligned and both the 16-byte
+// (v = 4*(t + 1024*j)) and the 4-byte (v = t + 1024*k) walks conflict-free.
+__device__ __forceinline__ int widx(int v) { return v + 4 * (v >> 7); }
+
+// floor(x * 2^40) as a double: exact, and so is any sum of such terms below
+// 2^53 in any order -- the same integers fx40() gives, summed in the fp64 ALU.
+__device__ __forceinline__ double fx40d(float x) { return floor(ldexp((double)x, 40)); }
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Sum over the block of integer-valued doubles (exact below 2^53).
+__device__ __forceinline__ double block_sum_f64(double v, double* s_redd) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  v = wave_sum_f64(v);
+  __syncthreads();  // s_redd free from its previous use
+  if (lane == 0) s_redd[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < kMssThreads / 64; ++w) t += s_redd[w];
+  return t;
+}
 
 __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* s_red) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -228,19 +252,111 @@ __device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* s_
   return before + incl - v;
 }
 
+// Row passes.  With 16-byte-aligned rows (VEC) a row moves whole: thread t
+// requests entries v = 4*(t + kMssThreads*j) .. +3, j < kMssRowChunks, all
+// at once (one memory round trip per pass), and their LDS slots are the 16
+// bytes at widx(v) = 4t + 4*(t/32) + 4224*j.  Otherwise entries
+// v = t + kMssThreads*k are streamed, 8 loads in flight per thread.
+constexpr int kMssRowChunks = (kMssMaxVocab + 4 * kMssThreads - 1) / (4 * kMssThreads);
+constexpr int kMssChunkStride = 4 * kMssThreads + 4 * ((4 * kMssThreads) >> 7);  // widx step of j
+
+// s_w[widx(v)] = row[v]
+template <bool VEC>
+__device__ __forceinline__ void mss_row_to_lds(const float* __restrict__ row, int V, float* s_w) {
+  const int t = threadIdx.x;
+  if (VEC) {
+    f32x4 r[kMssRowChunks];
+#pragma unroll
+    for (int j = 0; j < kMssRowChunks; ++j) {
+      const int v = 4 * (t + kMssThreads * j);
+      r[j] = v < V ? *reinterpret_cast<const f32x4*>(row + v) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    f32x4* wp = reinterpret_cast<f32x4*>(s_w + 4 * t + 4 * (t >> 5));
+#pragma unroll
+    for (int j = 0; j < kMssRowChunks; ++j)
+      if (4 * (t + kMssThreads * j) < V) wp[(kMssChunkStride / 4) * j] = r[j];
+  } else {
+    for (int v0 = t; v0 < V; v0 += 8 * kMssThreads) {
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int v = v0 + k * kMssThreads;
+        x[k] = v < V ? row[v] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int v = v0 + k * kMssThreads;
+        if (v < V) s_w[widx(v)] = x[k];
+      }
+    }
+  }
+}
+
+// w = max(w - s*q, +0) in place; returns this thread's sum of fx40(w) (as
+// an integer-valued double)
+template <bool VEC>
+__device__ __forceinline__ double mss_residual(const float* __restrict__ q, int V, float s, float* s_w) {
+  const int t = threadIdx.x;
+  double part = 0.0;
+  if (VEC) {
+    f32x4 r[kMssRowChunks];
+#pragma unroll
+    for (int j = 0; j < kMssRowChunks; ++j) {
+      const int v = 4 * (t + kMssThreads * j);
+      r[j] = v < V ? *reinterpret_cast<const f32x4*>(q + v) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    f32x4* wp = reinterpret_cast<f32x4*>(s_w + 4 * t + 4 * (t >> 5));
+#pragma unroll
+    for (int j = 0; j < kMssRowChunks; ++j)
+      if (4 * (t + kMssThreads * j) < V) {
+        f32x4 w = wp[(kMssChunkStride / 4) * j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float d = fmaf(-s, r[j][e], w[e]);
+          w[e] = d > 0.0f ? d : 0.0f;
+          part += fx40d(w[e]);
+        }
+        wp[(kMssChunkStride / 4) * j] = w;
+      }
+  } else {
+    for (int v0 = t; v0 < V; v0 += 8 * kMssThreads) {
+      float qv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int v = v0 + k * kMssThreads;
+        qv[k] = v < V ? q[v] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int v = v0 + k * kMssThreads;
+        if (v < V) {
+          const float d = fmaf(-s, qv[k], s_w[widx(v)]);
+          const float w = d > 0.0f ? d : 0.0f;
+          s_w[widx(v)] = w;
+          part += fx40d(w);
+        }
+      }
+    }
+  }
+  return part;
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     int N, int V, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
     const float* __restrict__ llm, const float* __restrict__ ssm,
     const float* __restrict__ u_accept, const float* __restrict__ u_bonus,
     int32_t* __restrict__ path, int32_t* __restrict__ path_len,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status) {
-  extern __shared__ float s_w[];  // residual w, widx() layout
+  extern __shared__ __attribute__((aligned(16))) float s_w[];  // residual w, widx() layout
   __shared__ int32_t s_par[kMaxNodes];
   __shared__ int32_t s_tok[kMaxNodes];
   __shared__ int32_t s_path[kMaxNodes];
+  __shared__ float s_rq[kMaxNodes];  // u_accept[c] * q_c[token c]: the left side of c's test at s = 1
   __shared__ unsigned long long s_kids[kMaxNodes][2];
   __shared__ uint64_t s_first_ok[2];
   __shared__ uint64_t s_red[kMssThreads / 64];
+  __shared__ double s_redd[kMssThreads / 64];
   __shared__ int s_status, s_pick;
 
   const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
@@ -280,16 +396,15 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     }
     return;
   }
-  // children bitsets; first-attempt test of every non-root node with w = p of
-  // its parent and mass 1 (only first children use it) -- gathers only
+  // children bitsets, r*q[x] of every non-root node, and its first-attempt
+  // test with w = p of its parent and mass 1 (only first children use it)
   bool first_ok = false;
   if (t >= 1 && t < N) {
     const int p = s_par[t], x = s_tok[t];
     atomicOr(&s_kids[p][t >> 6], 1ull << (t & 63));
-    const float r = u_accept[rowN + t];
-    const float qx = ssm[(rowN + t) * V + x];
-    const float px = llm[(rowN + p) * V + x];
-    first_ok = (r * qx) * 1.0f < px;
+    const float rq = u_accept[rowN + t] * ssm[(rowN + t) * V + x];
+    s_rq[t] = rq;
+    first_ok = rq * 1.0f < llm[(rowN + p) * V + x];
   }
   if (wave < 2) {
     const uint64_t bal = __ballot(first_ok);
@@ -297,28 +412,28 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   }
   __syncthreads();
 
-  // Row passes touch v = t + 1024*k; the loads of 8 consecutive k are issued
-  // together so their latencies overlap.
+  // s_w = p_u.  The first barrier lets every thread finish reading the old
+  // residual (the test that led here reads it), the second publishes p_u.
   auto load_p_row = [&](int u) {
-    const float* p = llm + (rowN + u) * V;
-    for (int v0 = t; v0 < V; v0 += 8 * kMssThreads) {
-      float x[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int v = v0 + k * kMssThreads;
-        x[k] = v < V ? p[v] : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int v = v0 + k * kMssThreads;
-        if (v < V) s_w[widx(v)] = x[k];
-      }
-    }
     __syncthreads();
+    mss_row_to_lds<VEC>(llm + (rowN + u) * V, V, s_w);
+    __syncthreads();
+  };
+  auto pop_child = [](uint64_t& k0, uint64_t& k1) {
+    int c;
+    if (k0) {
+      c = __ffsll((unsigned long long)k0) - 1;
+      k0 &= k0 - 1;
+    } else {
+      c = 64 + __ffsll((unsigned long long)k1) - 1;
+      k1 &= k1 - 1;
+    }
+    return c;
   };
 
   // ---- the walk: control flow is uniform, decisions are recomputed by every
-  // thread from the same LDS / global values
+  // thread from the same LDS values.  Every row is requested whole: one
+  // memory round trip per pass.
   int u = 0;
   for (;;) {
     uint64_t k0 = s_kids[u][0], k1 = s_kids[u][1];
@@ -338,46 +453,20 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     int next = -1;
     bool first = true;
     while (k0 | k1) {
-      int c;
-      if (k0) {
-        c = __ffsll((unsigned long long)k0) - 1;
-        k0 &= k0 - 1;
-      } else {
-        c = 64 + __ffsll((unsigned long long)k1) - 1;
-        k1 &= k1 - 1;
-      }
-      const float* q = ssm + (rowN + c) * V;
-      if (!first) {  // the first child's test (w = p_u, s = 1) is already known
-        const int x = s_tok[c];
-        const float lhs = (u_accept[rowN + c] * q[x]) * s;
-        if (lhs < s_w[widx(x)]) {
+      const int c = pop_child(k0, k1);
+      if (!first) {  // c's test against w, mass s
+        const bool accept = s_rq[c] * s < s_w[widx(s_tok[c])];
+        __syncthreads();  // every thread has read w[x] before it is updated below
+        if (accept) {
           next = c;
           break;
         }
       }
       first = false;
-      // rejected: w = max(w - s*q, +0), s = its mass in 2^-40 units
-      uint64_t part = 0;
-      for (int v0 = t; v0 < V; v0 += 8 * kMssThreads) {
-        float qv[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int v = v0 + k * kMssThreads;
-          qv[k] = v < V ? q[v] : 0.f;
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int v = v0 + k * kMssThreads;
-          if (v < V) {
-            const float d = fmaf(-s, qv[k], s_w[widx(v)]);
-            const float w = d > 0.0f ? d : 0.0f;
-            s_w[widx(v)] = w;
-            part += fx40(w);
-          }
-        }
-      }
-      const uint64_t S = block_sum_u64(part, s_red);  // its barriers publish s_w
-      s = (float)((double)S * 0x1p-40);
+      // rejected: w = max(w - s*q_c, +0), s = its mass in 2^-40 units
+      const double part = mss_residual<VEC>(ssm + (rowN + c) * V, V, s, s_w);
+      const double S = block_sum_f64(part, s_redd);  // its barriers publish s_w
+      s = (float)(S * 0x1p-40);
       if (s == 0.0f) {  // empty residual: stop testing, sample from p_u
         load_p_row(u);
         break;
@@ -443,12 +532,15 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                              const float* u_accept, const float* u_bonus, int32_t* path,
                              int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
                              hipStream_t s) {
-  const size_t lds = (size_t)(V + (V >> 5) + 1) * sizeof(float);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mss_kernel),
+  const size_t lds = (size_t)(V + 4 * (V >> 7) + 4) * sizeof(float);  // widx(V - 1) + 1, 16-byte padded
+  const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(llm) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(ssm) & 15) == 0;
+  auto kern = vec ? mss_kernel<true> : mss_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mss_kernel, dim3(B), dim3(kMssThreads), lds, s, N, V, parents, tokens, llm,
-                     ssm, u_accept, u_bonus, path, path_len, out_tokens, dev_status);
+  hipLaunchKernelGGL(kern, dim3(B), dim3(kMssThreads), lds, s, N, V, parents, tokens, llm, ssm,
+                     u_accept, u_bonus, path, path_len, out_tokens, dev_status);
   return hipGetLastError();
 }
 
