@@ -121,14 +121,19 @@ ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents,
  *               scores (0 for a rejected request).
  *   workspace   device scratch of >= ttv_tree_attn_workspace_size(...) bytes
  *               (may be NULL when that size is 0): fp32 partials of the
- *               split-KV launch.  Its contents need no initialisation and are
- *               garbage afterwards; calls sharing one must not overlap.
+ *               split-KV launch (and, when the split is planned on the
+ *               device, the chunk count of each request).  Its contents need
+ *               no initialisation and are garbage afterwards; calls sharing
+ *               one must not overlap.
  *   rows_per_block, chunk_keys  launch tuning: 0 = automatic; otherwise query
  *               rows per workgroup (64, 128 or 256 on the matrix-core path,
  *               which serves bf16 with N*Hq/Hkv >= 16; 16 on the FMA path)
  *               and prefix keys per workgroup (a positive multiple of 64);
  *               other values give TTV_E_UNSUPPORTED.  The same values must be
- *               given to the size query.
+ *               given to the size query.  With chunk_keys = 0, 2..64
+ *               requests and fewer (request, kv head, row block) units than
+ *               CUs, the split follows the actual prefix lengths read on the
+ *               device (longer requests get more workgroups).
  * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE, TTV_E_UNSUPPORTED,
  *         TTV_E_ALIGN, TTV_E_WORKSPACE, TTV_E_LAUNCH.
  */

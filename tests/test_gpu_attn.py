@@ -5,7 +5,10 @@ configuration the benchmark uses), plus edge cases: N = 1, empty prefix,
 chains and stars, N = 64/65/128 (bitset word boundary), GQA group sizes 1..16,
 ragged prefix lengths, the FMA path in bf16 (fewer than 16 rows per kv head)
 and fp32, head dim 64, every row-block size and forced KV splits, and
-rejected requests (malformed tree, prefix longer than the promise)."""
+rejected requests (malformed tree, prefix longer than the promise).  Batches
+of 2..64 requests take the split planned on the device from the actual
+lengths; explicit length mixes (empty, one key, tile boundaries, the maximum)
+check that every key is covered exactly once."""
 import numpy as np
 import pytest
 import torch
@@ -87,3 +90,24 @@ def test_rejected_requests(ck):
                                       d["k_tree"], d["v_tree"], d["parents"], d["scale"], rows)
     got = out.float().cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
     np.testing.assert_allclose(got, ref, atol=2e-2, rtol=1e-2)
+
+
+BALANCED = {
+    # name: (spec, explicit prefix lengths or None)
+    "mixed_lengths": (dict(B=8, N=32, Hq=16, Hkv=4, L=4096), [0, 1, 63, 64, 65, 3000, 17, 4096]),
+    "one_long_many_short": (dict(B=12, N=24, Hq=8, Hkv=2, L=6000), [6000] + [40] * 11),
+    "tree_tiles_split_n128": (dict(B=3, N=128, Hq=8, Hkv=4, L=(10, 600)), None),
+    "b64_lane_limit": (dict(B=64, N=16, Hq=8, Hkv=2, L=(0, 700)), None),
+    "b65_host_split": (dict(B=65, N=16, Hq=8, Hkv=2, L=(0, 700)), None),
+    "many_row_blocks": (dict(B=2, N=64, Hq=64, Hkv=8, L=(300, 1200)), None),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BALANCED))
+def test_balanced_split(case):
+    announce("attn balanced split %s" % case)
+    kw, lengths = BALANCED[case]
+    d = synth.make(spec(**kw))
+    if lengths is not None:
+        d["cache_len"] = np.array(lengths, np.int32)
+    check_attn(d)

@@ -75,7 +75,26 @@ ttv_status attn_plan(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, int Lma
   p->chunk_keys = chunk;
   p->chunks = Lmax > 0 ? ceil_div(Lmax, chunk) : 1;
   if (p->chunks < 1) p->chunks = 1;
+  p->items = 0;
+  // Several requests and fewer work units than CUs: the prefix lengths may
+  // differ, so the matrix-core path plans the split on the device from the
+  // actual lengths (attn_plan.h) over `slots` workgroups, a unit taking at
+  // most twice the even share of chunks (which bounds the workspace).  The
+  // plan costs one more memory round trip before the first copy, so it is
+  // only used where the split can change (measured on MI355X: 8 requests of
+  // 1169..3643 keys run 4% faster; 256 units, each its own workgroup either
+  // way, 12% slower).
+  p->balanced = p->mfma && !chunk_hint && B > 1 && B <= kBalancedMaxB && units < slots;
+  if (p->balanced) {
+    const long tiles_max = (N + 63) / 64 + ((long)Lmax + 63) / 64;
+    long cmax = (2 * slots + units - 1) / units;
+    if (cmax > tiles_max) cmax = tiles_max;
+    p->chunks = cmax > 1 ? (int)cmax : 1;
+    p->chunk_keys = 0;
+    p->items = (int)slots;
+  }
   p->ws_bytes = p->chunks > 1 ? (size_t)pairs * p->chunks * R * (size_t)(D + 2) * sizeof(float) : 0;
+  if (p->balanced && p->chunks > 1) p->ws_bytes += (size_t)B * sizeof(int32_t);  // chunks per request
   return TTV_OK;
 }
 
@@ -164,10 +183,14 @@ ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t
   a.rows_per_block = p.rows_per_block;
   a.chunk_keys = p.chunk_keys;
   a.chunks = p.chunks;
+  a.balanced = p.balanced ? 1 : 0;
+  a.row_blocks = p.row_blocks;
+  a.items = p.items;
   a.scale_log2 = scale * 1.44269504088896340736f;
   if (p.chunks > 1) {
     a.ws_acc = static_cast<float*>(workspace);
     a.ws_ml = a.ws_acc + (size_t)B * Hkv * p.chunks * p.rows * D;
+    if (p.balanced) a.ws_nchunks = reinterpret_cast<int32_t*>(a.ws_ml + (size_t)B * Hkv * p.chunks * p.rows * 2);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = p.mfma ? launch_attn_mfma(a, s) : launch_attn_fma(a, dt == TTV_BF16, s);

@@ -211,7 +211,8 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
 // =========================================================================
 // Split-KV combine: o = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),
 // M = max_c m_c, over the chunks that hold keys of request b (chunk 0 always
-// does: it owns the tree keys, and every node sees at least itself).
+// does: it owns the tree keys, and every node sees at least itself; with the
+// balanced split every chunk of the request holds keys).
 // One wavefront per query row; lanes cover D.
 // =========================================================================
 template <typename T, int D>
@@ -235,7 +236,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     return;
   }
   int used = 1;
-  while (used < a.chunks && used * a.chunk_keys < L) ++used;
+  if (a.balanced) {
+    used = a.ws_nchunks[b];  // written by the request's first work item
+    if (used == 1) return;   // that item wrote the output itself
+  } else {
+    while (used < a.chunks && used * a.chunk_keys < L) ++used;
+  }
   const size_t base = (size_t)bh * a.chunks * R + r;
   float M = -INFINITY;
   for (int c = 0; c < used; ++c) M = fmaxf(M, a.ws_ml[(base + (size_t)c * R) * 2]);

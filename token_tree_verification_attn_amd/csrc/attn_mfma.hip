@@ -25,6 +25,7 @@
 // chunk run on the same XCD and share its L2.
 #include <type_traits>
 
+#include "attn_plan.h"
 #include "launch.h"
 #include "ttv_common.h"
 
@@ -133,13 +134,16 @@ __device__ __forceinline__ int swz_k(int key, int c) { return c ^ (key & (CPR - 
 template <int CPR>
 __device__ __forceinline__ int swz_v(int key, int c) { return c ^ ((key << 1) & (CPR - 1)); }
 
-// Tile schedule of one workgroup: chunk 0 first takes the nT in-tree tiles
-// (keys 0..N-1 of k/v_tree, which depend on nothing but N), then every chunk
-// takes its prefix tiles (keys [c*chunk, min(L, (c+1)*chunk)) of k/v_cache).
+// Tile schedule of one workgroup: first nT in-tree tiles (keys from
+// tree0*64 on, of k/v_tree), then nP prefix tiles (keys [k_begin, k_end) of
+// k/v_cache).  With the split fixed on the host, chunk 0 takes all in-tree
+// tiles (they depend on nothing but N) and chunk c the prefix keys
+// [c*chunk, min(L, (c+1)*chunk)); with the balanced split a chunk is a range
+// of the unit's tile list (attn_plan.h).
 struct Sched {
-  int nT, nP, k_begin, k_end;
+  int nT, tree0, nP, k_begin, k_end;
   __device__ bool tree(int t) const { return t < nT; }
-  __device__ int key0(int t) const { return t < nT ? t * 64 : k_begin + (t - nT) * 64; }
+  __device__ int key0(int t) const { return t < nT ? (tree0 + t) * 64 : k_begin + (t - nT) * 64; }
 };
 
 template <int D, int QW, int NW, int NST>
@@ -159,10 +163,24 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   const int item = xcd * per_xcd + blockIdx.x / kXcds;
   if (item >= work_items) return;
   const int nrb = (a.R + C::RB - 1) / C::RB;
-  const int rb = item % nrb;
-  const int c = (item / nrb) % a.chunks;
-  const int bh = item / (nrb * a.chunks);
-  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+  int b, h, rb, c, n_chunks;
+  PlanItem pl;
+  if (a.balanced) {
+    if (!attn_plan_item(a, item, pl)) return;
+    b = pl.b;
+    h = pl.h;
+    rb = pl.rb;
+    c = pl.c;
+    n_chunks = pl.C;
+  } else {
+    rb = item % nrb;
+    c = (item / nrb) % a.chunks;
+    const int bh0 = item / (nrb * a.chunks);
+    b = bh0 / a.Hkv;
+    h = bh0 - b * a.Hkv;
+    n_chunks = a.chunks;
+  }
+  const int bh = b * a.Hkv + h;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g16 = lane >> 4, c16 = lane & 15;
@@ -191,10 +209,20 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     voff[j] = key * (D * 2) + swz_v<C::CPR>(key, phys) * 16;
   }
   Sched sc;
-  sc.nT = (c == 0) ? (N + KT - 1) / KT : 0;
-  sc.nP = 0;
-  sc.k_begin = c * a.chunk_keys;
-  sc.k_end = sc.k_begin;
+  if (a.balanced) {  // everything is known from the plan, L included
+    const int te = min(pl.t1, pl.nT), tp = max(pl.t0, pl.nT);
+    sc.nT = max(0, te - pl.t0);
+    sc.tree0 = pl.t0;
+    sc.nP = max(0, pl.t1 - tp);
+    sc.k_begin = (tp - pl.nT) * KT;
+    sc.k_end = min(pl.L, sc.k_begin + sc.nP * KT);
+  } else {
+    sc.nT = (c == 0) ? (N + KT - 1) / KT : 0;
+    sc.tree0 = 0;
+    sc.nP = 0;
+    sc.k_begin = c * a.chunk_keys;
+    sc.k_end = sc.k_begin;
+  }
   // Copies of tile t into ring stage S.  Keys past the tile's valid ones
   // re-read the last valid row (finite values; their scores are masked), so
   // no copy leaves the tensors or reads rows at or beyond the prefix length.
@@ -259,7 +287,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   // copies, so they stay inside the cache even when L is invalid; such a
   // request is rejected below and its copies are drained unused.
   const int L = a.cache_len[b];
-  {
+  if (!a.balanced) {
     const int Lc = min(max(L, 0), a.Lmax);
     sc.k_end = min(Lc, sc.k_begin + a.chunk_keys);
     sc.nP = (sc.k_begin < sc.k_end) ? (sc.k_end - sc.k_begin + KT - 1) / KT : 0;
@@ -272,7 +300,10 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
       if (!tree_ok) st = TTV_E_TREE;
       else if (L < 0 || L > a.Lmax) st = TTV_E_SHAPE;
       s_status = st;
-      if (a.dev_status && c == 0 && rb == 0 && h == 0) a.dev_status[b] = st;
+      if (c == 0 && rb == 0 && h == 0) {
+        if (a.dev_status) a.dev_status[b] = st;
+        if (a.ws_nchunks) a.ws_nchunks[b] = n_chunks;
+      }
     }
   }
   __syncthreads();
@@ -474,7 +505,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
 
   // ---- finish: the 4 lanes of a query hold disjoint key subsets of l
   const bool has_work = ntiles > 0;
-  if (a.chunks == 1) {
+  if (n_chunks == 1) {
 #pragma unroll
     for (int qt = 0; qt < C::QT; ++qt) {
       const float lt = red32_sum(red16_sum(l_run[qt]));
@@ -519,7 +550,7 @@ template <int D, int QW, int NW, int NST>
 static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
   using C = MfmaCfg<D, QW, NW, NST>;
   const int nrb = (a.R + C::RB - 1) / C::RB;
-  const long items = (long)a.B * a.Hkv * nrb * a.chunks;
+  const long items = a.balanced ? (long)a.items : (long)a.B * a.Hkv * nrb * a.chunks;
   const long blocks = (items + kXcds - 1) / kXcds * kXcds;
   auto kern = attn_mfma2_kernel<D, QW, NW, NST>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -12,11 +12,14 @@ namespace ttv {
 // size query and the call compute the same plan).
 struct AttnPlan {
   bool mfma;           // matrix-core path (bf16 and >= 16 query rows per kv head)
+  bool balanced;       // split planned on the device from the actual prefix lengths
   int rows;            // R = N * G query rows per (request, kv head)
   int rows_per_block;  // query rows handled by one workgroup
   int row_blocks;      // ceil(R / rows_per_block)
-  int chunk_keys;      // prefix keys per workgroup (multiple of 64)
-  int chunks;          // ceil(Lmax / chunk_keys), at least 1
+  int chunk_keys;      // fixed split: prefix keys per workgroup (multiple of 64)
+  int chunks;          // fixed split: ceil(Lmax / chunk_keys); balanced: the most
+                       // chunks one (request, kv head, row block) may get
+  int items;           // balanced: workgroups launched
   size_t ws_bytes;     // split-KV partials (0 when chunks == 1)
 };
 
@@ -33,10 +36,17 @@ struct AttnArgs {
   int32_t* dev_status;
   float* ws_acc;   // [B*Hkv][chunks][R][D]  unnormalised fp32 partial outputs
   float* ws_ml;    // [B*Hkv][chunks][R][2]  running max (log2 units) and sum
+  int32_t* ws_nchunks;  // [B] balanced split: chunks request b got
   int B, N, Hq, Hkv, G, D, Lcap, Lmax, R;
   int rows_per_block, chunk_keys, chunks;
+  int balanced, row_blocks, items;
   float scale_log2;  // softmax scale * log2(e): scores are kept in log2 units
 };
+
+// Balanced split: at most this many requests (one per lane of a wavefront),
+// and at least this many 64-key tiles per chunk.
+constexpr int kBalancedMaxB = 64;
+constexpr int kBalancedMinTiles = 2;
 
 hipError_t launch_attn_fma(const AttnArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
