@@ -55,17 +55,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// One HBM -> LDS copy of 16 bytes per lane: lane l's 16 bytes at gptr land
-// at LDS address lds_base + 16*l (lds_base is wave-uniform, passed in M0).
+// One HBM -> LDS copy of 16 bytes per lane: lane l's 16 bytes at
+// gbase + voff (gbase wave-uniform, in SGPRs; voff the lane's 32-bit offset)
+// land at LDS address lds_base + 16*l (lds_base wave-uniform, passed in M0).
 // It is written as inline assembly on purpose.  The compiler's memory-counter
 // bookkeeping treats an LDS-DMA copy as a pending write to all of LDS, and
 // before every later LDS read it cannot tell apart from the copy's target --
 // the transposed V reads -- it drains every copy in flight (vmcnt(0)), which
 // defeats the ring.  Issued this way the copies are ordered by the ring's own
 // waits instead (wait_vmcnt for this wave's copies, then ring_barrier).
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(base), "v"(gptr) : "memory", "m0");
+__device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  const uint64_t g = reinterpret_cast<uintptr_t>(gbase);
+  // readfirstlane returns int: each half goes through uint32_t, or the low
+  // word would be sign-extended into the high one
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)g);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
+  const uint64_t gs = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(m0), "v"(voff), "s"(gs) : "memory", "m0");
 }
 
 // Workgroup barrier for the copy ring.  __syncthreads() carries
@@ -245,8 +252,8 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
         vo += shift;
       }
       const int wbase = (j * C::kWaves + wave) * 1024;
-      lds_dma16(ks + ko, (uint32_t)(uintptr_t)(kst + wbase));
-      lds_dma16(vs + vo, (uint32_t)(uintptr_t)(vst + wbase));
+      lds_dma16(ks, ko, (uint32_t)(uintptr_t)(kst + wbase));
+      lds_dma16(vs, vo, (uint32_t)(uintptr_t)(vst + wbase));
     }
   };
 
@@ -415,6 +422,9 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
 #pragma unroll
     for (int qt = 0; qt < C::QT; ++qt) {
       if (masked) {
+        // the empty asm keeps this a branch taken only by tree and tail tiles
+        // (if-converted, its selects would run on every tile)
+        asm volatile("");
         const uint64_t w = key0 < 64 ? anc_lo[qt] : anc_hi[qt];
         const uint64_t vmask = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
         const uint64_t tm = ((tree ? w : ~0ull) & vmask) >> (g16 * 4);  // lane keys: kb*16 + g16*4 + e
@@ -446,6 +456,8 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
           s[kb][qt][e] = p;
           psum += p;
         }
+      // fp32 row sum of the unrounded probabilities (an MFMA sum of the
+      // bf16-rounded P would save these adds but costs the lse ~2^-9)
       l_run[qt] = l_run[qt] * alpha[qt] + psum;
       // P^T operands: slots 0-3 = keys 32*k2 + g16*4 + e, 4-7 = +16
 #pragma unroll

@@ -77,12 +77,14 @@ __device__ inline bool attn_plan_item(const AttnArgs& a, int item, PlanItem& it)
   }
   const uint64_t past = __ballot(lane < a.B && incl > item);
   if (past == 0ull) return false;
-  const int b = __ffsll((unsigned long long)past) - 1;
+  // every result is wave-uniform; readfirstlane tells the compiler so, which
+  // keeps the tile bookkeeping that depends on it in scalar registers
+  const int b = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)past) - 1);
   it.b = b;
-  it.C = __shfl(C, b);
-  it.L = __shfl(L, b);
-  const int nb = __shfl(n, b);
-  const int j = item - (__shfl(incl, b) - U * it.C);
+  it.C = __builtin_amdgcn_readfirstlane(__shfl(C, b));
+  it.L = __builtin_amdgcn_readfirstlane(__shfl(L, b));
+  const int nb = __builtin_amdgcn_readfirstlane(__shfl(n, b));
+  const int j = item - __builtin_amdgcn_readfirstlane(__shfl(incl, b) - U * it.C);
   it.rb = j % a.row_blocks;
   it.c = (j / a.row_blocks) % it.C;
   it.h = j / (a.row_blocks * it.C);
