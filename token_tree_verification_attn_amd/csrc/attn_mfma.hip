@@ -141,16 +141,17 @@ __device__ __forceinline__ int swz_k(int key, int c) { return c ^ (key & (CPR - 
 template <int CPR>
 __device__ __forceinline__ int swz_v(int key, int c) { return c ^ ((key << 1) & (CPR - 1)); }
 
-// Tile schedule of one workgroup: first nT in-tree tiles (keys from
-// tree0*64 on, of k/v_tree), then nP prefix tiles (keys [k_begin, k_end) of
-// k/v_cache).  With the split fixed on the host, chunk 0 takes all in-tree
-// tiles (they depend on nothing but N) and chunk c the prefix keys
-// [c*chunk, min(L, (c+1)*chunk)); with the balanced split a chunk is a range
-// of the unit's tile list (attn_plan.h).
+// Tile schedule of one workgroup: first nP prefix tiles (keys
+// [k_begin, k_end) of k/v_cache), then nT in-tree tiles (keys from tree0*64
+// on, of k/v_tree).  In-tree tiles come last so that the tree topology,
+// which only they need, is built while the prefix streams.  With the split
+// fixed on the host, chunk c takes the prefix keys [c*chunk, min(L,
+// (c+1)*chunk)) and chunk 0 also all in-tree tiles; with the balanced split a
+// chunk is a range of the unit's tile list (attn_plan.h).
 struct Sched {
-  int nT, tree0, nP, k_begin, k_end;
-  __device__ bool tree(int t) const { return t < nT; }
-  __device__ int key0(int t) const { return t < nT ? (tree0 + t) * 64 : k_begin + (t - nT) * 64; }
+  int nP, k_begin, k_end, nT, tree0;
+  __device__ bool tree(int t) const { return t >= nP; }
+  __device__ int key0(int t) const { return t < nP ? k_begin + t * 64 : (tree0 + t - nP) * 64; }
 };
 
 template <int D, int QW, int NW, int NST>
@@ -159,9 +160,6 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   using C = MfmaCfg<D, QW, NW, NST>;
   constexpr int KT = C::KT;
   extern __shared__ __attribute__((aligned(1024))) unsigned char s_dyn[];
-  __shared__ uint64_t s_anc[2 * kMaxNodes];
-  __shared__ int32_t s_depth[kMaxNodes];
-  __shared__ int s_status;
 
   // ---- XCD-first work item: rb fastest, then chunk, then (b, h)
   const int nb = gridDim.x;
@@ -215,21 +213,33 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     koff[j] = key * (D * 2) + swz_k<C::CPR>(key, phys) * 16;
     voff[j] = key * (D * 2) + swz_v<C::CPR>(key, phys) * 16;
   }
+  // The request's prefix length (raw, for its status) and tree are requested
+  // first; the prefix tiles of the fixed split wait for L, the topology is
+  // only needed at the first in-tree tile.
+  const int L = a.cache_len[b];
+  const int32_t* par = a.parents + (size_t)b * N;
+  const int p0 = lane < N ? par[lane] : -1;
+  const int p1 = lane + 64 < N ? par[lane + 64] : -1;
   Sched sc;
-  if (a.balanced) {  // everything is known from the plan, L included
-    const int te = min(pl.t1, pl.nT), tp = max(pl.t0, pl.nT);
-    sc.nT = max(0, te - pl.t0);
-    sc.tree0 = pl.t0;
-    sc.nP = max(0, pl.t1 - tp);
-    sc.k_begin = (tp - pl.nT) * KT;
+  if (a.balanced) {  // everything is known from the plan, L (clamped) included
+    const int nPtot = (pl.L + KT - 1) / KT;  // the unit's tiles: nPtot prefix, then pl.nT in-tree
+    const int pe = min(pl.t1, nPtot), tt = max(pl.t0, nPtot);
+    sc.nP = max(0, pe - pl.t0);
+    sc.k_begin = pl.t0 * KT;
     sc.k_end = min(pl.L, sc.k_begin + sc.nP * KT);
+    sc.nT = max(0, pl.t1 - tt);
+    sc.tree0 = tt - nPtot;
   } else {
+    // L is clamped to [0, Lmax] for the copies, so they stay inside the
+    // cache even when L is invalid; such a request is rejected at the end
+    const int Lc = min(max(L, 0), a.Lmax);
+    sc.k_begin = c * a.chunk_keys;
+    sc.k_end = min(Lc, sc.k_begin + a.chunk_keys);
+    sc.nP = (sc.k_begin < sc.k_end) ? (sc.k_end - sc.k_begin + KT - 1) / KT : 0;
     sc.nT = (c == 0) ? (N + KT - 1) / KT : 0;
     sc.tree0 = 0;
-    sc.nP = 0;
-    sc.k_begin = c * a.chunk_keys;
-    sc.k_end = sc.k_begin;
   }
+  const int ntiles = sc.nP + sc.nT;
   // Copies of tile t into ring stage S.  Keys past the tile's valid ones
   // re-read the last valid row (finite values; their scores are masked), so
   // no copy leaves the tensors or reads rows at or beyond the prefix length.
@@ -257,21 +267,14 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     }
   };
 
-  // tile -> its ring stage as a compile-time constant (LDS offsets are immediates)
-  auto issue_any = [&](int tile) {
-    switch (tile % NST) {
-      case 0: issue(tile, std::integral_constant<int, 0>{}); break;
-      case 1: issue(tile, std::integral_constant<int, 1 % NST>{}); break;
-      case 2: issue(tile, std::integral_constant<int, 2 % NST>{}); break;
-      default: issue(tile, std::integral_constant<int, 3 % NST>{}); break;
-    }
-  };
 
-  // ---- prologue, latency-first: the in-tree tiles (chunk 0) and the queries
-  // are requested before the prefix length and the tree topology arrive.
-  // Tiles 0 .. NST-2 are in flight when the loop starts.
-  int issued = 0;
-  while (issued < sc.nT && issued < NST - 1) issue_any(issued++);
+  // ---- prologue: tiles 0 .. NST-2 and the queries are in flight when the
+  // loop starts.  No workgroup barrier: the ring's first one is the first.
+  // (explicit stages: a loop over tile % NST here keeps the source pointers
+  // in private memory, and every access to those waits on the copies)
+  if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
+  if (NST > 2 && ntiles > 1) issue(1, std::integral_constant<int, 1 % NST>{});
+  if (NST > 3 && ntiles > 2) issue(2, std::integral_constant<int, 2 % NST>{});
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   bf16x8 qB[C::QT][C::KS];
   int qnode[C::QT];
@@ -289,39 +292,31 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
       qB[qt][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // The prefix tiles need only L: they are requested as soon as it arrives,
-  // before the tree topology is built.  L is clamped to [0, Lmax] for the
-  // copies, so they stay inside the cache even when L is invalid; such a
-  // request is rejected below and its copies are drained unused.
-  const int L = a.cache_len[b];
-  if (!a.balanced) {
-    const int Lc = min(max(L, 0), a.Lmax);
-    sc.k_end = min(Lc, sc.k_begin + a.chunk_keys);
-    sc.nP = (sc.k_begin < sc.k_end) ? (sc.k_end - sc.k_begin + KT - 1) / KT : 0;
-  }
-  while (issued < sc.nT + sc.nP && issued < NST - 1) issue_any(issued++);
-  if (wave == 0) {
-    const bool tree_ok = wave_build_tree(a.parents + (size_t)b * N, N, s_anc, s_depth);
-    if (lane == 0) {
-      int st = TTV_OK;
-      if (!tree_ok) st = TTV_E_TREE;
-      else if (L < 0 || L > a.Lmax) st = TTV_E_SHAPE;
-      s_status = st;
-      if (c == 0 && rb == 0 && h == 0) {
-        if (a.dev_status) a.dev_status[b] = st;
-        if (a.ws_nchunks) a.ws_nchunks[b] = n_chunks;
-      }
-    }
-  }
-  __syncthreads();
-  const int status = s_status;
-  const int ntiles = status == TTV_OK ? sc.nT + sc.nP : 0;
 
+  // Ancestor bitsets of this lane's query nodes, built by every wave in its
+  // own registers (no LDS, no barrier) when it first needs them: at the first
+  // in-tree tile, or at the end for a workgroup that reports the request's
+  // status without holding in-tree tiles.
   uint64_t anc_lo[C::QT], anc_hi[C::QT];
+  bool tree_ok = true, tree_built = false;
+  auto build_tree = [&]() {
+    uint64_t a0lo, a1lo, a1hi;
+    tree_ok = wave_tree_bits(p0, p1, N, a0lo, a1lo, a1hi);
+#pragma unroll
+    for (int qt = 0; qt < C::QT; ++qt) {
+      const int i = qnode[qt] >= 0 ? qnode[qt] : 0;
+      const uint64_t lo0 = shfl_u64(a0lo, i & 63);
+      const uint64_t lo1 = shfl_u64(a1lo, i & 63);
+      const uint64_t hi1 = shfl_u64(a1hi, i & 63);
+      anc_lo[qt] = qnode[qt] < 0 ? 0ull : (i < 64 ? lo0 : lo1);
+      anc_hi[qt] = qnode[qt] < 0 || i < 64 ? 0ull : hi1;
+    }
+    tree_built = true;
+  };
 #pragma unroll
   for (int qt = 0; qt < C::QT; ++qt) {
-    anc_lo[qt] = qnode[qt] >= 0 ? s_anc[2 * qnode[qt]] : 0ull;
-    anc_hi[qt] = qnode[qt] >= 0 ? s_anc[2 * qnode[qt] + 1] : 0ull;
+    anc_lo[qt] = 0ull;
+    anc_hi[qt] = 0ull;
   }
   f32x4 oacc[C::QT][C::DT];
   float m_run[C::QT], l_run[C::QT];
@@ -505,6 +500,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     else wait_vmcnt<0>();
     ring_barrier();
     if (tile + NST - 1 < ntiles) issue(tile + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
+    if (tile == sc.nP) build_tree();  // the first in-tree tile
     compute(tile, stage_tag);
   };
   for (int tile = 0; tile < ntiles; tile += NST) {
@@ -513,10 +509,22 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     if (NST > 2 && tile + 2 < ntiles) step(tile + 2, std::integral_constant<int, 2 % NST>{});
     if (NST > 3 && tile + 3 < ntiles) step(tile + 3, std::integral_constant<int, 3 % NST>{});
   }
-  wait_vmcnt<0>();  // copies issued for a rejected request must land before exit
+  wait_vmcnt<0>();  // every copy has landed before the workgroup ends
 
-  // ---- finish: the 4 lanes of a query hold disjoint key subsets of l
-  const bool has_work = ntiles > 0;
+  // ---- the request's status: its tree (known once built) and its length.
+  // The first work item of the request reports it (and, for the combine
+  // kernel, its chunk count).
+  const bool writer = c == 0 && rb == 0 && h == 0;
+  if (!tree_built && (n_chunks == 1 || writer)) build_tree();
+  const int status = !tree_ok ? TTV_E_TREE : (L < 0 || L > a.Lmax ? TTV_E_SHAPE : TTV_OK);
+  if (writer && wave == 0 && lane == 0) {
+    if (a.dev_status) a.dev_status[b] = status;
+    if (a.ws_nchunks) a.ws_nchunks[b] = n_chunks;
+  }
+
+  // ---- finish: the 4 lanes of a query hold disjoint key subsets of l; a
+  // rejected request gets zeros (its work was done on clamped inputs)
+  const bool has_work = status == TTV_OK && ntiles > 0;
   if (n_chunks == 1) {
 #pragma unroll
     for (int qt = 0; qt < C::QT; ++qt) {

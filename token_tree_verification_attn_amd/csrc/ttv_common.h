@@ -87,22 +87,27 @@ __device__ __forceinline__ int wave_max_i32(int v) {
 // Validity (parents[0] == -1, 0 <= parents[i] < i) is checked with a ballot
 // first; an invalid tree writes nothing and returns false.
 //
-// On return (valid tree) s_anc[2*i + w] holds word w of node i's bitset and
-// s_depth[i] its depth, for i < N.  All 64 lanes must call it; the caller
-// synchronises before other waves read the LDS arrays.
-__device__ inline bool wave_build_tree(const int32_t* __restrict__ par, int N,
-                                       uint64_t* s_anc, int32_t* s_depth) {
+// wave_tree_bits works in registers only: from the parents p0 = parents[l],
+// p1 = parents[l + 64] (-1 past N) it returns in lane l the bitsets of nodes
+// l (a0lo; its high word is 0) and l + 64 (a1lo, a1hi), or false for an
+// invalid tree.  wave_build_tree loads the parents itself and stores the
+// result in LDS: on return (valid tree) s_anc[2*i + w] holds word w of node
+// i's bitset and s_depth[i] its depth, for i < N.  All 64 lanes must call
+// either; the caller synchronises before other waves read the LDS arrays.
+__device__ inline bool wave_tree_bits(int p0, int p1, int N, uint64_t& a0lo, uint64_t& a1lo,
+                                      uint64_t& a1hi) {
   const int lane = lane_id();
   const int i0 = lane, i1 = lane + 64;
-  const int p0 = i0 < N ? par[i0] : -1;
-  const int p1 = i1 < N ? par[i1] : -1;
   const bool bad0 = i0 < N && (i0 == 0 ? p0 != -1 : (p0 < 0 || p0 >= i0));
   const bool bad1 = i1 < N && (p1 < 0 || p1 >= i1);
+  a0lo = 0ull;
+  a1lo = 0ull;
+  a1hi = 0ull;
   if (__ballot(bad0 || bad1) != 0ull) return false;
 
   // A for node i0 (words lo/hi) and node i1; node i0 < 64 lives in word 0.
-  uint64_t a0lo = i0 < N ? (1ull << i0) : 0ull, a0hi = 0ull;
-  uint64_t a1lo = 0ull, a1hi = i1 < N ? (1ull << (i1 - 64)) : 0ull;
+  a0lo = i0 < N ? (1ull << i0) : 0ull;
+  a1hi = i1 < N ? (1ull << (i1 - 64)) : 0ull;
   int j0 = p0, j1 = p1;
   const bool two = N > 64;
   while (__ballot(j0 >= 0 || j1 >= 0) != 0ull) {
@@ -134,6 +139,18 @@ __device__ inline bool wave_build_tree(const int32_t* __restrict__ par, int N,
       j0 = r0j;
     }
   }
+  return true;
+}
+
+__device__ inline bool wave_build_tree(const int32_t* __restrict__ par, int N,
+                                       uint64_t* s_anc, int32_t* s_depth) {
+  const int lane = lane_id();
+  const int i0 = lane, i1 = lane + 64;
+  const int p0 = i0 < N ? par[i0] : -1;
+  const int p1 = i1 < N ? par[i1] : -1;
+  uint64_t a0lo, a1lo, a1hi;
+  if (!wave_tree_bits(p0, p1, N, a0lo, a1lo, a1hi)) return false;
+  const uint64_t a0hi = 0ull;
   if (i0 < N) {
     s_anc[2 * i0] = a0lo;
     s_anc[2 * i0 + 1] = a0hi;
