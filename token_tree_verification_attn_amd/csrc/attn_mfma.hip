@@ -75,6 +75,41 @@ __device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(m0), "v"(voff), "s"(gs) : "memory", "m0");
 }
 
+// Loads of the queries and parent indices, issued before the tile copies and
+// also as inline assembly: the compiler would wait for a load it knows of
+// with vmcnt(0) at the value's first use, which (the copies being invisible
+// to it) drains every tile in flight.  wait_pin then waits for exactly these
+// loads (vmcnt = the copies issued after them) in the same statement that
+// hands their registers back to the compiler, so nothing reads or moves the
+// registers before the data has landed (its comment names the registers, to
+// check that in the assembly).  Only the address is read at issue.
+__device__ __forceinline__ u32x4 gload16_async(const void* p) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ int gload4_async(const void* p) {
+  int v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+template <int N, int NQ>
+__device__ __forceinline__ void wait_pin(u32x4 (&q)[NQ], int& p0, int& p1) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  if constexpr (NQ == 2) {
+    asm volatile("s_waitcnt vmcnt(%4) ; %0 %1 %2 %3" : "+v"(q[0]), "+v"(q[1]), "+v"(p0), "+v"(p1) : "n"(N) : "memory");
+  } else if constexpr (NQ == 4) {
+    asm volatile("s_waitcnt vmcnt(%6) ; %0 %1 %2 %3 %4 %5"
+                 : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(p0), "+v"(p1) : "n"(N) : "memory");
+  } else {
+    static_assert(NQ == 8, "query fragments per lane");
+    asm volatile("s_waitcnt vmcnt(%10) ; %0 %1 %2 %3 %4 %5 %6 %7 %8 %9"
+                 : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]), "+v"(q[6]),
+                   "+v"(q[7]), "+v"(p0), "+v"(p1)
+                 : "n"(N) : "memory");
+  }
+}
+
 // Workgroup barrier for the copy ring.  __syncthreads() carries
 // workgroup-scope fences, and the compiler may satisfy them by draining every
 // outstanding vector-memory operation (vmcnt(0)), which would also wait for
@@ -114,11 +149,13 @@ __device__ __forceinline__ float red32_sum(float v) {
 
 }  // namespace
 
-template <int D, int QW, int NW, int NST>
+template <int D, int QW, int NW, int NST, bool PP>
 struct MfmaCfg {
   static constexpr int KT = 64;                // keys per tile
   static constexpr int kWaves = NW;
   static constexpr int kThreads = 64 * kWaves;
+  // with the two-group schedule only the first group issues copies
+  static constexpr int kCopyWaves = PP ? NW / 2 : NW;
   static constexpr int QT = QW / 16;           // 16-query MFMA tiles per wave
   static constexpr int KS = D / 32;            // 32-wide d steps of K Q^T
   static constexpr int DT = D / 16;            // 16-wide d tiles of O^T
@@ -126,13 +163,15 @@ struct MfmaCfg {
   static constexpr int PK = KT / 32;           // 32-key steps of V^T P^T
   static constexpr int CPR = D / 8;            // 16-byte chunks per key row
   static constexpr int TILE_BYTES = KT * D * 2;        // one K (or V) tile
-  static constexpr int LOADS = TILE_BYTES / 16 / kThreads;  // per thread per tile
+  static constexpr int LOADS = TILE_BYTES / 16 / (64 * kCopyWaves);  // per copying thread per tile
   static constexpr int RB = kWaves * QW;       // query rows per workgroup
   static constexpr int LDS_BYTES = NST * 2 * TILE_BYTES;
-  // one workgroup per CU: the 4-deep ring takes 128 KB of LDS
+  // one workgroup per CU: the ring takes up to the 160 KB of a CU's LDS
   static constexpr int MIN_BLOCKS = 1;
-  static_assert(LOADS >= 1 && TILE_BYTES % (16 * kThreads) == 0, "tile / loads");
-  static_assert(NST >= 2 && NST <= 4, "ring depth");
+  static_assert(LOADS >= 1 && TILE_BYTES % (16 * 64 * kCopyWaves) == 0, "tile / loads");
+  static_assert(NST >= 2 && NST <= 5 && (!PP || NST >= 3), "ring depth");
+  static_assert(!PP || NW == 8, "two groups of one wave per SIMD");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
 };
 
 // Chunk swizzles: the physical 16-byte slot of logical chunk c of key row k.
@@ -154,10 +193,10 @@ struct Sched {
   __device__ int key0(int t) const { return t < nP ? k_begin + t * 64 : (tree0 + t - nP) * 64; }
 };
 
-template <int D, int QW, int NW, int NST>
-__global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) void attn_mfma2_kernel(
+template <int D, int QW, int NW, int NST, bool PP>
+__global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST, PP>::MIN_BLOCKS)) void attn_mfma2_kernel(
     AttnArgs a, int work_items) {
-  using C = MfmaCfg<D, QW, NW, NST>;
+  using C = MfmaCfg<D, QW, NW, NST, PP>;
   constexpr int KT = C::KT;
   extern __shared__ __attribute__((aligned(1024))) unsigned char s_dyn[];
 
@@ -198,8 +237,8 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   const char* ktr = static_cast<const char*>(a.k_tree) + (size_t)bh * N * D * 2;
   const char* vtr = static_cast<const char*>(a.v_tree) + (size_t)bh * N * D * 2;
 
-  // ---- per-lane constants of the HBM -> LDS copies.  Wave w, copy j fills
-  // LDS slots (j*4 + w)*64 + lane of a tile (16 bytes each, placed by the
+  // ---- per-lane constants of the HBM -> LDS copies.  Copying wave w, copy j
+  // fills LDS slots (j*W + w)*64 + lane of a tile (W copying waves) (16 bytes each, placed by the
   // hardware at base + 16*lane); slot p holds key p / CPR, logical chunk
   // swz(key, p % CPR), i.e. this lane reads byte offset key*2D + 16*swz(...)
   // of the tile's first row.
@@ -207,19 +246,35 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   int lkey[C::LOADS];
 #pragma unroll
   for (int j = 0; j < C::LOADS; ++j) {
-    const int slot = (j * C::kWaves + wave) * 64 + lane;
+    const int slot = (j * C::kCopyWaves + wave) * 64 + lane;
     const int key = slot / C::CPR, phys = slot % C::CPR;
     lkey[j] = key;
     koff[j] = key * (D * 2) + swz_k<C::CPR>(key, phys) * 16;
     voff[j] = key * (D * 2) + swz_v<C::CPR>(key, phys) * 16;
   }
-  // The request's prefix length (raw, for its status) and tree are requested
-  // first; the prefix tiles of the fixed split wait for L, the topology is
-  // only needed at the first in-tree tile.
+  // The request's prefix length (raw, for its status), its tree and this
+  // wave's queries are requested first; the prefix tiles of the fixed split
+  // wait for L, the topology is only needed at the first in-tree tile.  The
+  // parent and query loads go out before the copies (see gload16_async);
+  // lanes and rows past the end read index 0 / row 0 and are masked below.
   const int L = a.cache_len[b];
   const int32_t* par = a.parents + (size_t)b * N;
-  const int p0 = lane < N ? par[lane] : -1;
-  const int p1 = lane + 64 < N ? par[lane + 64] : -1;
+  int p0 = gload4_async(par + min(lane, N - 1));
+  int p1 = gload4_async(par + min(lane + 64, N - 1));
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  u32x4 qraw[C::QT * C::KS];
+  int qnode[C::QT];
+#pragma unroll
+  for (int qt = 0; qt < C::QT; ++qt) {
+    const int r = row_base + qt * 16 + c16;
+    const bool rv = r < R;
+    const int i = rv ? r / G : 0;
+    qnode[qt] = rv ? i : -1;
+    const int hq = h * G + (rv ? r - i * G : 0);
+    const uint16_t* qr = q + (((size_t)b * N + i) * a.Hq + hq) * D + g16 * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qraw[qt * C::KS + ks] = gload16_async(qr + ks * 32);
+  }
   Sched sc;
   if (a.balanced) {  // everything is known from the plan, L (clamped) included
     const int nPtot = (pl.L + KT - 1) / KT;  // the unit's tiles: nPtot prefix, then pl.nT in-tree
@@ -261,37 +316,43 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
         ko += shift;
         vo += shift;
       }
-      const int wbase = (j * C::kWaves + wave) * 1024;
+      const int wbase = (j * C::kCopyWaves + wave) * 1024;
       lds_dma16(ks, ko, (uint32_t)(uintptr_t)(kst + wbase));
       lds_dma16(vs, vo, (uint32_t)(uintptr_t)(vst + wbase));
     }
   };
 
 
-  // ---- prologue: tiles 0 .. NST-2 and the queries are in flight when the
-  // loop starts.  No workgroup barrier: the ring's first one is the first.
+  // ---- prologue: the first tiles and the queries are in flight when the
+  // loop starts: NST-1 tiles, or NST with the two-group schedule (whose
+  // stages stay busy one phase longer).  No workgroup barrier: the ring's
+  // first one is the first.
   // (explicit stages: a loop over tile % NST here keeps the source pointers
   // in private memory, and every access to those waits on the copies)
-  if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
-  if (NST > 2 && ntiles > 1) issue(1, std::integral_constant<int, 1 % NST>{});
-  if (NST > 3 && ntiles > 2) issue(2, std::integral_constant<int, 2 % NST>{});
-  const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  bf16x8 qB[C::QT][C::KS];
-  int qnode[C::QT];
-#pragma unroll
-  for (int qt = 0; qt < C::QT; ++qt) {
-    const int r = row_base + qt * 16 + c16;
-    const bool rv = r < R;
-    const int i = rv ? r / G : 0;
-    qnode[qt] = rv ? i : -1;
-    const int hq = h * G + (rv ? r - i * G : 0);
-    const uint16_t* qr = q + (((size_t)b * N + i) * a.Hq + hq) * D + g16 * 8;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const u32x4 v = rv ? *reinterpret_cast<const u32x4*>(qr + ks * 32) : u32x4{0u, 0u, 0u, 0u};
-      qB[qt][ks] = __builtin_bit_cast(bf16x8, v);
-    }
+  constexpr int kPre = PP ? NST : NST - 1;
+  const bool copier = !PP || wave < C::kCopyWaves;
+  if (copier) {
+    if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
+    if (kPre > 1 && ntiles > 1) issue(1, std::integral_constant<int, 1 % NST>{});
+    if (kPre > 2 && ntiles > 2) issue(2, std::integral_constant<int, 2 % NST>{});
+    if (kPre > 3 && ntiles > 3) issue(3, std::integral_constant<int, 3 % NST>{});
+    if (kPre > 4 && ntiles > 4) issue(4, std::integral_constant<int, 4 % NST>{});
   }
+  // Queries and parents have landed once no more than this wave's prologue
+  // copies are outstanding.  One wait_pin with a fixed count (a wave with a
+  // short or no prologue drains first): one per case would give the compiler
+  // one definition per case to merge, and it merges by copying the registers
+  // before the wait.
+  if (!copier || ntiles < kPre) wait_vmcnt<0>();
+  wait_pin<kPre * 2 * C::LOADS>(qraw, p0, p1);
+  p0 = lane < N ? p0 : -1;
+  p1 = lane + 64 < N ? p1 : -1;
+  bf16x8 qB[C::QT][C::KS];
+#pragma unroll
+  for (int qt = 0; qt < C::QT; ++qt)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      qB[qt][ks] = __builtin_bit_cast(bf16x8, qnode[qt] >= 0 ? qraw[qt * C::KS + ks] : u32x4{0u, 0u, 0u, 0u});
 
   // Ancestor bitsets of this lane's query nodes, built by every wave in its
   // own registers (no LDS, no barrier) when it first needs them: at the first
@@ -345,7 +406,8 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     }
   }
 
-  // ---- one tile of math from ring stage S.
+  // ---- the math of one tile, in pieces that the two schedules below order
+  // differently.
   // Masking: bit k of tmask[qt] says whether key key0 + k is visible to this
   // lane's query (the valid-key prefix for a tail tile, the ancestor bits for
   // an in-tree tile); full prefix tiles skip it.
@@ -357,24 +419,24 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   // and the rescale of O is skipped when no query of the wave needs it.
   constexpr float kLazy = 8.0f;
   const float cs = a.scale_log2;
-  auto compute = [&](int tile, auto stage_tag) {
+  using KFrag = u32x4[C::KB][C::KS];
+  using SAcc = f32x4[C::KB][C::QT];
+  using VFrag = i16x4[C::PK][C::DT];
+  using PFrag = bf16x8[C::QT][C::PK];
+  // K fragments of the tile in stage S, all requested at once (one LDS
+  // latency for all of them)
+  auto read_k = [&](auto stage_tag, KFrag& kf) {
     constexpr int S = decltype(stage_tag)::value;
     const TTV_LDS unsigned char* kst = (const TTV_LDS unsigned char*)(s_dyn + S * 2 * C::TILE_BYTES);
-    const TTV_LDS unsigned char* vst = kst + C::TILE_BYTES;
-    const bool tree = sc.tree(tile);
-    const int key0 = sc.key0(tile);
-    const int nvalid = tree ? min(KT, N - key0) : min(KT, sc.k_end - key0);
-    const bool masked = tree || nvalid < KT;
-    // K fragments of the whole tile first: one LDS latency for all of them
-    u32x4 kf[C::KB][C::KS];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
         kf[kb][ks] = *(const TTV_LDS u32x4*)(kst + krd[ks] + kb * 16 * (D * 2));
-    // S^T = K Q^T, d-step outermost so that KB*QT independent accumulations
-    // sit between two MFMAs of one chain
-    f32x4 s[C::KB][C::QT];
+  };
+  // S^T = K Q^T, d-step outermost so that KB*QT independent accumulations
+  // sit between two MFMAs of one chain
+  auto qk = [&](const KFrag& kf, SAcc& s) {
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -388,31 +450,36 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
         for (int qt = 0; qt < C::QT; ++qt)
           s[kb][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qB[qt][ks], s[kb][qt], 0, 0, 0);
       }
-    // V^T fragments are requested now; their latency hides behind the softmax.
-    // ds_read_b64_tr_b16 gives lane i (of its 16-lane group) element i%4 of
-    // the 8-byte rows fetched by lanes 4j + i/4 of the group; lane r of group
-    // g fetches V[32*k2 + 4g + r/4 (+16)][dt*16 + 4*(r%4) ..+3], so lane i
-    // receives V[32*k2 + 4g + j (+16)][dt*16 + i], j = 0..3: the A operand
-    // row of output column dt*16 + i for the P^T key slots.
-    // (With two or more query tiles per wave the registers run short; those
-    // shapes fetch each 32-key step's fragments right before its MFMAs.)
-    constexpr bool kEarlyV = C::QT == 1;
-    i16x4 vlo[C::PK][C::DT], vhi[C::PK][C::DT];
-    auto fetch_v = [&](int k2) {
+  };
+  // V^T fragments of 32-key step k2 of the tile in stage S.
+  // ds_read_b64_tr_b16 gives lane i (of its 16-lane group) element i%4 of
+  // the 8-byte rows fetched by lanes 4j + i/4 of the group; lane r of group
+  // g fetches V[32*k2 + 4g + r/4 (+16)][dt*16 + 4*(r%4) ..+3], so lane i
+  // receives V[32*k2 + 4g + j (+16)][dt*16 + i], j = 0..3: the A operand
+  // row of output column dt*16 + i for the P^T key slots.
+  // With one query tile per wave all of a tile's V^T fragments are fetched
+  // ahead of the MFMAs that use them; with two or more the registers run
+  // short, and each 32-key step's fragments are fetched right before its
+  // MFMAs.
+  constexpr bool kEarlyV = C::QT == 1;
+  auto read_v = [&](auto stage_tag, int k2, VFrag& vlo, VFrag& vhi) {
+    constexpr int S = decltype(stage_tag)::value;
+    const TTV_LDS unsigned char* vst = (const TTV_LDS unsigned char*)(s_dyn + S * 2 * C::TILE_BYTES) + C::TILE_BYTES;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const TTV_LDS unsigned char* pa = vst + vrd[dt] + k2 * 32 * (D * 2);
-        vlo[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)pa);
-        vhi[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)(pa + 16 * (D * 2)));
-      }
-    };
-    if (kEarlyV) {
-#pragma unroll
-      for (int k2 = 0; k2 < C::PK; ++k2) fetch_v(k2);
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const TTV_LDS unsigned char* pa = vst + vrd[dt] + k2 * 32 * (D * 2);
+      vlo[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)pa);
+      vhi[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)(pa + 16 * (D * 2)));
     }
-    // online softmax; lane holds keys kb*16 + g16*4 + e of query c16
-    bf16x8 pB[C::QT][C::PK];
-    float alpha[C::QT];
+  };
+  // online softmax of tile `tile` in place of its scores; lane holds keys
+  // kb*16 + g16*4 + e of query c16.  Returns whether any query of the lane
+  // moved its running max (O must then be rescaled by alpha).
+  auto softmax = [&](int tile, SAcc& s, PFrag& pB, float (&alpha)[C::QT]) -> bool {
+    const bool tree = sc.tree(tile);
+    const int key0 = sc.key0(tile);
+    const int nvalid = tree ? min(KT, N - key0) : min(KT, sc.k_end - key0);
+    const bool masked = tree || nvalid < KT;
     bool any_rescale = false;
 #pragma unroll
     for (int qt = 0; qt < C::QT; ++qt) {
@@ -464,16 +531,22 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
         pB[qt][k2] = __builtin_bit_cast(bf16x8, pk);
       }
     }
-    if (__builtin_amdgcn_ballot_w64(any_rescale)) {
+    return any_rescale;
+  };
+  auto rescale = [&](const float (&alpha)[C::QT], bool any) {
+    if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
       for (int qt = 0; qt < C::QT; ++qt)
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) oacc[qt][dt] *= alpha[qt];
     }
-    // O^T += V^T P^T
+  };
+  // O^T += V^T P^T for the tile in stage S (V^T fragments already in vlo/vhi
+  // with one query tile per wave)
+  auto pv = [&](auto stage_tag, VFrag& vlo, VFrag& vhi, const PFrag& pB) {
 #pragma unroll
     for (int k2 = 0; k2 < C::PK; ++k2) {
-      if (!kEarlyV) fetch_v(k2);
+      if (!kEarlyV) read_v(stage_tag, k2, vlo, vhi);
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
         const i16x4 lo = vlo[k2][dt], hi = vhi[k2][dt];
@@ -486,28 +559,132 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     }
   };
 
-  // ---- the pipeline: NST-1 tiles in flight during each tile's math.  Each
-  // wave waits for its own copies of the current tile (vmcnt counts the
-  // copies issued after them), then one barrier both publishes every wave's
-  // copies and proves that every wave has finished the previous tile, whose
-  // stage then receives the copies of the tile NST-1 ahead.  The loop is
-  // unrolled by NST so that every LDS offset is an immediate.
-  auto step = [&](int tile, auto stage_tag) {
-    constexpr int S = decltype(stage_tag)::value;
-    const int ahead = min(NST - 2, ntiles - 1 - tile);  // tiles issued after this one
-    if (ahead >= 2) wait_vmcnt<4 * C::LOADS>();
-    else if (ahead == 1) wait_vmcnt<2 * C::LOADS>();
-    else wait_vmcnt<0>();
-    ring_barrier();
-    if (tile + NST - 1 < ntiles) issue(tile + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
-    if (tile == sc.nP) build_tree();  // the first in-tree tile
-    compute(tile, stage_tag);
+  // the same with each 32-key step's V^T fragments fetched one step ahead
+  auto pv_ahead = [&](auto stage_tag, VFrag& vlo, VFrag& vhi, const PFrag& pB) {
+    read_v(stage_tag, 0, vlo, vhi);
+#pragma unroll
+    for (int k2 = 0; k2 < C::PK; ++k2) {
+      if (k2 + 1 < C::PK) read_v(stage_tag, k2 + 1, vlo, vhi);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const i16x4 lo = vlo[k2][dt], hi = vhi[k2][dt];
+        const bf16x8 A = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+        for (int qt = 0; qt < C::QT; ++qt)
+          oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pB[qt][k2], oacc[qt][dt], 0, 0, 0);
+      }
+    }
   };
-  for (int tile = 0; tile < ntiles; tile += NST) {
-    step(tile, std::integral_constant<int, 0>{});
-    if (tile + 1 < ntiles) step(tile + 1, std::integral_constant<int, 1 % NST>{});
-    if (NST > 2 && tile + 2 < ntiles) step(tile + 2, std::integral_constant<int, 2 % NST>{});
-    if (NST > 3 && tile + 3 < ntiles) step(tile + 3, std::integral_constant<int, 3 % NST>{});
+
+  if constexpr (!PP) {
+    // ---- one wave schedule: NST-1 tiles in flight during each tile's math.
+    // Each wave waits for its own copies of the current tile (vmcnt counts
+    // the copies issued after them), then one barrier both publishes every
+    // wave's copies and proves that every wave has finished the previous
+    // tile, whose stage then receives the copies of the tile NST-1 ahead.
+    // The loop is unrolled by NST so that every LDS offset is an immediate.
+    auto step = [&](int tile, auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;
+      const int ahead = min(NST - 2, ntiles - 1 - tile);  // tiles issued after this one
+      if (ahead >= 3) wait_vmcnt<6 * C::LOADS>();
+      else if (ahead == 2) wait_vmcnt<4 * C::LOADS>();
+      else if (ahead == 1) wait_vmcnt<2 * C::LOADS>();
+      else wait_vmcnt<0>();
+      ring_barrier();
+      if (tile + NST - 1 < ntiles) issue(tile + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
+      if (tile == sc.nP) build_tree();  // the first in-tree tile
+      KFrag kf;
+      SAcc s;
+      VFrag vlo, vhi;
+      PFrag pB;
+      float alpha[C::QT];
+      read_k(stage_tag, kf);
+      qk(kf, s);
+      if (kEarlyV) {
+#pragma unroll
+        for (int k2 = 0; k2 < C::PK; ++k2) read_v(stage_tag, k2, vlo, vhi);
+      }
+      const bool any = softmax(tile, s, pB, alpha);
+      rescale(alpha, any);
+      pv(stage_tag, vlo, vhi, pB);
+    };
+    for (int tile = 0; tile < ntiles; tile += NST) {
+      step(tile, std::integral_constant<int, 0>{});
+      if (tile + 1 < ntiles) step(tile + 1, std::integral_constant<int, 1 % NST>{});
+      if (NST > 2 && tile + 2 < ntiles) step(tile + 2, std::integral_constant<int, 2 % NST>{});
+      if (NST > 3 && tile + 3 < ntiles) step(tile + 3, std::integral_constant<int, 3 % NST>{});
+      if (NST > 4 && tile + 4 < ntiles) step(tile + 4, std::integral_constant<int, 4 % NST>{});
+    }
+  } else {
+    // ---- two-group schedule.  Waves 0..NW/2-1 (group A) and NW/2..NW-1
+    // (group B) hold one wave per SIMD each.  Every wave alternates a matrix
+    // phase M(t) = [O += P(t-1) V(t-1), then S(t) = K(t) Q^T: P(t-1) is dead
+    // before S(t) is born; with one query tile per wave K(t) is requested
+    // first and V^T one 32-key step ahead, with two (registers) each right
+    // before its use] and a vector phase
+    // X(t) = softmax of S(t), each opened by a workgroup barrier.  Group B
+    // takes one extra barrier before its first phase and group A one after
+    // its last, so B runs one phase behind A: while the waves of one group
+    // issue MFMAs the waves of the other run the softmax on the same SIMDs.
+    // Barrier 2t opens M(t) of A and X(t-1) of B; 2t+1 opens X(t) of A and
+    // M(t) of B.
+    // Copies (group A only): tile t is read from barrier 2t on (A's M(t))
+    // and for the last time in B's M(t+1), which ends before barrier 2t+4.
+    // So A waits for its copies of tile t before barrier 2t, and right after
+    // barrier 2t refills the stage of tile t-2 with tile t+NST-2: NST-2
+    // tiles in flight ahead of the one A starts on.
+    const bool grp_b = wave >= NW / 2;
+    SAcc s_cur;                 // scores of tile t between M(t) and X(t)
+    PFrag p_prev;               // P of tile t between X(t) and M(t+1)
+    float a_prev[C::QT];
+    bool r_prev = false;
+#pragma unroll
+    for (int qt = 0; qt < C::QT; ++qt) a_prev[qt] = 1.f;
+    auto pp_step = [&](int t, auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;
+      constexpr int SV = (S + NST - 1) % NST;  // stage of tile t-1
+      if (!grp_b && t < ntiles) {
+        // copies issued after tile t's: the prologue's up to tile NST-1,
+        // then tile u+NST-2 at each M(u), u = 2 .. t-1
+        const int ahead = min(max(NST - 1, t + NST - 3), ntiles - 1) - t;
+        if (ahead >= 4) wait_vmcnt<8 * C::LOADS>();
+        else if (ahead == 3) wait_vmcnt<6 * C::LOADS>();
+        else if (ahead == 2) wait_vmcnt<4 * C::LOADS>();
+        else if (ahead == 1) wait_vmcnt<2 * C::LOADS>();
+        else wait_vmcnt<0>();
+      }
+      ring_barrier();
+      if (!grp_b && t >= 2 && t + NST - 2 < ntiles)
+        issue(t + NST - 2, std::integral_constant<int, (S + NST - 2) % NST>{});
+      // M(t)
+      const bool do_qk = t < ntiles, do_pv = t >= 1;
+      KFrag kf;
+      VFrag vlo, vhi;
+      if (kEarlyV && do_qk) read_k(stage_tag, kf);
+      if (do_pv) {
+        rescale(a_prev, r_prev);
+        if constexpr (kEarlyV) pv_ahead(std::integral_constant<int, SV>{}, vlo, vhi, p_prev);
+        else pv(std::integral_constant<int, SV>{}, vlo, vhi, p_prev);
+      }
+      if (!kEarlyV && do_qk) read_k(stage_tag, kf);
+      if (do_qk) qk(kf, s_cur);
+      // X(t)
+      if (do_qk) {
+        ring_barrier();
+        if (t == sc.nP) build_tree();  // the first in-tree tile
+        r_prev = softmax(t, s_cur, p_prev, a_prev);
+      }
+    };
+    if (grp_b) ring_barrier();
+    for (int t = 0; t <= ntiles; t += NST) {
+      pp_step(t, std::integral_constant<int, 0>{});
+      if (t + 1 <= ntiles) pp_step(t + 1, std::integral_constant<int, 1 % NST>{});
+      if (NST > 2 && t + 2 <= ntiles) pp_step(t + 2, std::integral_constant<int, 2 % NST>{});
+      if (NST > 3 && t + 3 <= ntiles) pp_step(t + 3, std::integral_constant<int, 3 % NST>{});
+      if (NST > 4 && t + 4 <= ntiles) pp_step(t + 4, std::integral_constant<int, 4 % NST>{});
+    }
+    if (!grp_b) ring_barrier();
   }
   wait_vmcnt<0>();  // every copy has landed before the workgroup ends
 
@@ -566,13 +743,13 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   }
 }
 
-template <int D, int QW, int NW, int NST>
+template <int D, int QW, int NW, int NST, bool PP>
 static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
-  using C = MfmaCfg<D, QW, NW, NST>;
+  using C = MfmaCfg<D, QW, NW, NST, PP>;
   const int nrb = (a.R + C::RB - 1) / C::RB;
   const long items = a.balanced ? (long)a.items : (long)a.B * a.Hkv * nrb * a.chunks;
   const long blocks = (items + kXcds - 1) / kXcds * kXcds;
-  auto kern = attn_mfma2_kernel<D, QW, NW, NST>;
+  auto kern = attn_mfma2_kernel<D, QW, NW, NST, PP>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (e != hipSuccess) return e;
@@ -580,20 +757,21 @@ static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// rows per workgroup -> shape: 64 rows = 4 waves x 16 queries, 128 = 8 x 16
-// and 256 = 8 x 32; each one workgroup per CU with a 4-deep 128 KB ring.
+// rows per workgroup -> shape: 64 rows = 4 waves x 16 queries (one wave per
+// SIMD, 4-deep ring); 128 = 8 x 16 and 256 = 8 x 32 (two waves per SIMD, the
+// two-group schedule, 5-deep ring: 160 KB at D = 128).  One workgroup per CU.
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.D == 64) {
     switch (a.rows_per_block) {
-      case 64: return launch_cfg<64, 16, 4, 4>(a, s);
-      case 128: return launch_cfg<64, 16, 8, 4>(a, s);
-      default: return launch_cfg<64, 32, 8, 4>(a, s);
+      case 64: return launch_cfg<64, 16, 4, 4, false>(a, s);
+      case 128: return launch_cfg<64, 16, 8, 5, true>(a, s);
+      default: return launch_cfg<64, 32, 8, 5, true>(a, s);
     }
   }
   switch (a.rows_per_block) {
-    case 64: return launch_cfg<128, 16, 4, 4>(a, s);
-    case 128: return launch_cfg<128, 16, 8, 4>(a, s);
-    default: return launch_cfg<128, 32, 8, 4>(a, s);
+    case 64: return launch_cfg<128, 16, 4, 4, false>(a, s);
+    case 128: return launch_cfg<128, 16, 8, 5, true>(a, s);
+    default: return launch_cfg<128, 32, 8, 5, true>(a, s);
   }
 }
 
