@@ -149,13 +149,11 @@ __device__ __forceinline__ float red32_sum(float v) {
 
 }  // namespace
 
-template <int D, int QW, int NW, int NST, bool PP>
+template <int D, int QW, int NW, int NST>
 struct MfmaCfg {
   static constexpr int KT = 64;                // keys per tile
   static constexpr int kWaves = NW;
   static constexpr int kThreads = 64 * kWaves;
-  // with the two-group schedule only the first group issues copies
-  static constexpr int kCopyWaves = PP ? NW / 2 : NW;
   static constexpr int QT = QW / 16;           // 16-query MFMA tiles per wave
   static constexpr int KS = D / 32;            // 32-wide d steps of K Q^T
   static constexpr int DT = D / 16;            // 16-wide d tiles of O^T
@@ -163,14 +161,13 @@ struct MfmaCfg {
   static constexpr int PK = KT / 32;           // 32-key steps of V^T P^T
   static constexpr int CPR = D / 8;            // 16-byte chunks per key row
   static constexpr int TILE_BYTES = KT * D * 2;        // one K (or V) tile
-  static constexpr int LOADS = TILE_BYTES / 16 / (64 * kCopyWaves);  // per copying thread per tile
+  static constexpr int LOADS = TILE_BYTES / 16 / kThreads;  // per thread per tile
   static constexpr int RB = kWaves * QW;       // query rows per workgroup
   static constexpr int LDS_BYTES = NST * 2 * TILE_BYTES;
-  // one workgroup per CU: the ring takes up to the 160 KB of a CU's LDS
+  // one workgroup per CU: the 4-deep ring takes 128 KB of LDS
   static constexpr int MIN_BLOCKS = 1;
-  static_assert(LOADS >= 1 && TILE_BYTES % (16 * 64 * kCopyWaves) == 0, "tile / loads");
-  static_assert(NST >= 2 && NST <= 5 && (!PP || NST >= 3), "ring depth");
-  static_assert(!PP || NW == 8, "two groups of one wave per SIMD");
+  static_assert(LOADS >= 1 && TILE_BYTES % (16 * kThreads) == 0, "tile / loads");
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
 };
 
@@ -193,10 +190,10 @@ struct Sched {
   __device__ int key0(int t) const { return t < nP ? k_begin + t * 64 : (tree0 + t - nP) * 64; }
 };
 
-template <int D, int QW, int NW, int NST, bool PP>
-__global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST, PP>::MIN_BLOCKS)) void attn_mfma2_kernel(
+template <int D, int QW, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) void attn_mfma2_kernel(
     AttnArgs a, int work_items) {
-  using C = MfmaCfg<D, QW, NW, NST, PP>;
+  using C = MfmaCfg<D, QW, NW, NST>;
   constexpr int KT = C::KT;
   extern __shared__ __attribute__((aligned(1024))) unsigned char s_dyn[];
 
@@ -237,8 +234,8 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST, PP>::MIN_BLOCKS))
   const char* ktr = static_cast<const char*>(a.k_tree) + (size_t)bh * N * D * 2;
   const char* vtr = static_cast<const char*>(a.v_tree) + (size_t)bh * N * D * 2;
 
-  // ---- per-lane constants of the HBM -> LDS copies.  Copying wave w, copy j
-  // fills LDS slots (j*W + w)*64 + lane of a tile (W copying waves) (16 bytes each, placed by the
+  // ---- per-lane constants of the HBM -> LDS copies.  Wave w, copy j fills
+  // LDS slots (j*NW + w)*64 + lane of a tile (16 bytes each, placed by the
   // hardware at base + 16*lane); slot p holds key p / CPR, logical chunk
   // swz(key, p % CPR), i.e. this lane reads byte offset key*2D + 16*swz(...)
   // of the tile's first row.
@@ -246,7 +243,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST, PP>::MIN_BLOCKS))
   int lkey[C::LOADS];
 #pragma unroll
   for (int j = 0; j < C::LOADS; ++j) {
-    const int slot = (j * C::kCopyWaves + wave) * 64 + lane;
+    const int slot = (j * C::kWaves + wave) * 64 + lane;
     const int key = slot / C::CPR, phys = slot % C::CPR;
     lkey[j] = key;
     koff[j] = key * (D * 2) + swz_k<C::CPR>(key, phys) * 16;
@@ -316,34 +313,26 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST, PP>::MIN_BLOCKS))
         ko += shift;
         vo += shift;
       }
-      const int wbase = (j * C::kCopyWaves + wave) * 1024;
+      const int wbase = (j * C::kWaves + wave) * 1024;
       lds_dma16(ks, ko, (uint32_t)(uintptr_t)(kst + wbase));
       lds_dma16(vs, vo, (uint32_t)(uintptr_t)(vst + wbase));
     }
   };
 
 
-  // ---- prologue: the first tiles and the queries are in flight when the
-  // loop starts: NST-1 tiles, or NST with the two-group schedule (whose
-  // stages stay busy one phase longer).  No workgroup barrier: the ring's
-  // first one is the first.
+  // ---- prologue: tiles 0 .. NST-2 and the queries are in flight when the
+  // loop starts.  No workgroup barrier: the ring's first one is the first.
   // (explicit stages: a loop over tile % NST here keeps the source pointers
   // in private memory, and every access to those waits on the copies)
-  constexpr int kPre = PP ? NST : NST - 1;
-  const bool copier = !PP || wave < C::kCopyWaves;
-  if (copier) {
-    if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
-    if (kPre > 1 && ntiles > 1) issue(1, std::integral_constant<int, 1 % NST>{});
-    if (kPre > 2 && ntiles > 2) issue(2, std::integral_constant<int, 2 % NST>{});
-    if (kPre > 3 && ntiles > 3) issue(3, std::integral_constant<int, 3 % NST>{});
-    if (kPre > 4 && ntiles > 4) issue(4, std::integral_constant<int, 4 % NST>{});
-  }
-  // Queries and parents have landed once no more than this wave's prologue
-  // copies are outstanding.  One wait_pin with a fixed count (a wave with a
-  // short or no prologue drains first): one per case would give the compiler
-  // one definition per case to merge, and it merges by copying the registers
-  // before the wait.
-  if (!copier || ntiles < kPre) wait_vmcnt<0>();
+  constexpr int kPre = NST - 1;
+  if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
+  if (kPre > 1 && ntiles > 1) issue(1, std::integral_constant<int, 1 % NST>{});
+  if (kPre > 2 && ntiles > 2) issue(2, std::integral_constant<int, 2 % NST>{});
+  // Queries and parents have landed once no more than the prologue's copies
+  // are outstanding.  One wait_pin with a fixed count (a short prologue
+  // drains first): one per case would give the compiler one definition per
+  // case to merge, and it merges by copying the registers before the wait.
+  if (ntiles < kPre) wait_vmcnt<0>();
   wait_pin<kPre * 2 * C::LOADS>(qraw, p0, p1);
   p0 = lane < N ? p0 : -1;
   p1 = lane + 64 < N ? p1 : -1;
@@ -406,8 +395,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST, PP>::MIN_BLOCKS))
     }
   }
 
-  // ---- the math of one tile, in pieces that the two schedules below order
-  // differently.
+  // ---- the math of one tile, in pieces.
   // Masking: bit k of tmask[qt] says whether key key0 + k is visible to this
   // lane's query (the valid-key prefix for a tail tile, the ancestor bits for
   // an in-tree tile); full prefix tiles skip it.
@@ -559,132 +547,41 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST, PP>::MIN_BLOCKS))
     }
   };
 
-  // the same with each 32-key step's V^T fragments fetched one step ahead
-  auto pv_ahead = [&](auto stage_tag, VFrag& vlo, VFrag& vhi, const PFrag& pB) {
-    read_v(stage_tag, 0, vlo, vhi);
+  // ---- the pipeline: NST-1 tiles in flight during each tile's math.
+  // Each wave waits for its own copies of the current tile (vmcnt counts
+  // the copies issued after them), then one barrier both publishes every
+  // wave's copies and proves that every wave has finished the previous
+  // tile, whose stage then receives the copies of the tile NST-1 ahead.
+  // The loop is unrolled by NST so that every LDS offset is an immediate.
+  auto step = [&](int tile, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    const int ahead = min(NST - 2, ntiles - 1 - tile);  // tiles issued after this one
+    if (ahead >= 2) wait_vmcnt<4 * C::LOADS>();
+    else if (ahead == 1) wait_vmcnt<2 * C::LOADS>();
+    else wait_vmcnt<0>();
+    ring_barrier();
+    if (tile + NST - 1 < ntiles) issue(tile + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
+    if (tile == sc.nP) build_tree();  // the first in-tree tile
+    KFrag kf;
+    SAcc s;
+    VFrag vlo, vhi;
+    PFrag pB;
+    float alpha[C::QT];
+    read_k(stage_tag, kf);
+    qk(kf, s);
+    if (kEarlyV) {
 #pragma unroll
-    for (int k2 = 0; k2 < C::PK; ++k2) {
-      if (k2 + 1 < C::PK) read_v(stage_tag, k2 + 1, vlo, vhi);
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const i16x4 lo = vlo[k2][dt], hi = vhi[k2][dt];
-        const bf16x8 A = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
-            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-        for (int qt = 0; qt < C::QT; ++qt)
-          oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pB[qt][k2], oacc[qt][dt], 0, 0, 0);
-      }
+      for (int k2 = 0; k2 < C::PK; ++k2) read_v(stage_tag, k2, vlo, vhi);
     }
+    const bool any = softmax(tile, s, pB, alpha);
+    rescale(alpha, any);
+    pv(stage_tag, vlo, vhi, pB);
   };
-
-  if constexpr (!PP) {
-    // ---- one wave schedule: NST-1 tiles in flight during each tile's math.
-    // Each wave waits for its own copies of the current tile (vmcnt counts
-    // the copies issued after them), then one barrier both publishes every
-    // wave's copies and proves that every wave has finished the previous
-    // tile, whose stage then receives the copies of the tile NST-1 ahead.
-    // The loop is unrolled by NST so that every LDS offset is an immediate.
-    auto step = [&](int tile, auto stage_tag) {
-      constexpr int S = decltype(stage_tag)::value;
-      const int ahead = min(NST - 2, ntiles - 1 - tile);  // tiles issued after this one
-      if (ahead >= 3) wait_vmcnt<6 * C::LOADS>();
-      else if (ahead == 2) wait_vmcnt<4 * C::LOADS>();
-      else if (ahead == 1) wait_vmcnt<2 * C::LOADS>();
-      else wait_vmcnt<0>();
-      ring_barrier();
-      if (tile + NST - 1 < ntiles) issue(tile + NST - 1, std::integral_constant<int, (S + NST - 1) % NST>{});
-      if (tile == sc.nP) build_tree();  // the first in-tree tile
-      KFrag kf;
-      SAcc s;
-      VFrag vlo, vhi;
-      PFrag pB;
-      float alpha[C::QT];
-      read_k(stage_tag, kf);
-      qk(kf, s);
-      if (kEarlyV) {
-#pragma unroll
-        for (int k2 = 0; k2 < C::PK; ++k2) read_v(stage_tag, k2, vlo, vhi);
-      }
-      const bool any = softmax(tile, s, pB, alpha);
-      rescale(alpha, any);
-      pv(stage_tag, vlo, vhi, pB);
-    };
-    for (int tile = 0; tile < ntiles; tile += NST) {
-      step(tile, std::integral_constant<int, 0>{});
-      if (tile + 1 < ntiles) step(tile + 1, std::integral_constant<int, 1 % NST>{});
-      if (NST > 2 && tile + 2 < ntiles) step(tile + 2, std::integral_constant<int, 2 % NST>{});
-      if (NST > 3 && tile + 3 < ntiles) step(tile + 3, std::integral_constant<int, 3 % NST>{});
-      if (NST > 4 && tile + 4 < ntiles) step(tile + 4, std::integral_constant<int, 4 % NST>{});
-    }
-  } else {
-    // ---- two-group schedule.  Waves 0..NW/2-1 (group A) and NW/2..NW-1
-    // (group B) hold one wave per SIMD each.  Every wave alternates a matrix
-    // phase M(t) = [O += P(t-1) V(t-1), then S(t) = K(t) Q^T: P(t-1) is dead
-    // before S(t) is born; with one query tile per wave K(t) is requested
-    // first and V^T one 32-key step ahead, with two (registers) each right
-    // before its use] and a vector phase
-    // X(t) = softmax of S(t), each opened by a workgroup barrier.  Group B
-    // takes one extra barrier before its first phase and group A one after
-    // its last, so B runs one phase behind A: while the waves of one group
-    // issue MFMAs the waves of the other run the softmax on the same SIMDs.
-    // Barrier 2t opens M(t) of A and X(t-1) of B; 2t+1 opens X(t) of A and
-    // M(t) of B.
-    // Copies (group A only): tile t is read from barrier 2t on (A's M(t))
-    // and for the last time in B's M(t+1), which ends before barrier 2t+4.
-    // So A waits for its copies of tile t before barrier 2t, and right after
-    // barrier 2t refills the stage of tile t-2 with tile t+NST-2: NST-2
-    // tiles in flight ahead of the one A starts on.
-    const bool grp_b = wave >= NW / 2;
-    SAcc s_cur;                 // scores of tile t between M(t) and X(t)
-    PFrag p_prev;               // P of tile t between X(t) and M(t+1)
-    float a_prev[C::QT];
-    bool r_prev = false;
-#pragma unroll
-    for (int qt = 0; qt < C::QT; ++qt) a_prev[qt] = 1.f;
-    auto pp_step = [&](int t, auto stage_tag) {
-      constexpr int S = decltype(stage_tag)::value;
-      constexpr int SV = (S + NST - 1) % NST;  // stage of tile t-1
-      if (!grp_b && t < ntiles) {
-        // copies issued after tile t's: the prologue's up to tile NST-1,
-        // then tile u+NST-2 at each M(u), u = 2 .. t-1
-        const int ahead = min(max(NST - 1, t + NST - 3), ntiles - 1) - t;
-        if (ahead >= 4) wait_vmcnt<8 * C::LOADS>();
-        else if (ahead == 3) wait_vmcnt<6 * C::LOADS>();
-        else if (ahead == 2) wait_vmcnt<4 * C::LOADS>();
-        else if (ahead == 1) wait_vmcnt<2 * C::LOADS>();
-        else wait_vmcnt<0>();
-      }
-      ring_barrier();
-      if (!grp_b && t >= 2 && t + NST - 2 < ntiles)
-        issue(t + NST - 2, std::integral_constant<int, (S + NST - 2) % NST>{});
-      // M(t)
-      const bool do_qk = t < ntiles, do_pv = t >= 1;
-      KFrag kf;
-      VFrag vlo, vhi;
-      if (kEarlyV && do_qk) read_k(stage_tag, kf);
-      if (do_pv) {
-        rescale(a_prev, r_prev);
-        if constexpr (kEarlyV) pv_ahead(std::integral_constant<int, SV>{}, vlo, vhi, p_prev);
-        else pv(std::integral_constant<int, SV>{}, vlo, vhi, p_prev);
-      }
-      if (!kEarlyV && do_qk) read_k(stage_tag, kf);
-      if (do_qk) qk(kf, s_cur);
-      // X(t)
-      if (do_qk) {
-        ring_barrier();
-        if (t == sc.nP) build_tree();  // the first in-tree tile
-        r_prev = softmax(t, s_cur, p_prev, a_prev);
-      }
-    };
-    if (grp_b) ring_barrier();
-    for (int t = 0; t <= ntiles; t += NST) {
-      pp_step(t, std::integral_constant<int, 0>{});
-      if (t + 1 <= ntiles) pp_step(t + 1, std::integral_constant<int, 1 % NST>{});
-      if (NST > 2 && t + 2 <= ntiles) pp_step(t + 2, std::integral_constant<int, 2 % NST>{});
-      if (NST > 3 && t + 3 <= ntiles) pp_step(t + 3, std::integral_constant<int, 3 % NST>{});
-      if (NST > 4 && t + 4 <= ntiles) pp_step(t + 4, std::integral_constant<int, 4 % NST>{});
-    }
-    if (!grp_b) ring_barrier();
+  for (int tile = 0; tile < ntiles; tile += NST) {
+    step(tile, std::integral_constant<int, 0>{});
+    if (tile + 1 < ntiles) step(tile + 1, std::integral_constant<int, 1 % NST>{});
+    if (NST > 2 && tile + 2 < ntiles) step(tile + 2, std::integral_constant<int, 2 % NST>{});
+    if (NST > 3 && tile + 3 < ntiles) step(tile + 3, std::integral_constant<int, 3 % NST>{});
   }
   wait_vmcnt<0>();  // every copy has landed before the workgroup ends
 
@@ -743,13 +640,13 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST, PP>::MIN_BLOCKS))
   }
 }
 
-template <int D, int QW, int NW, int NST, bool PP>
+template <int D, int QW, int NW, int NST>
 static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
-  using C = MfmaCfg<D, QW, NW, NST, PP>;
+  using C = MfmaCfg<D, QW, NW, NST>;
   const int nrb = (a.R + C::RB - 1) / C::RB;
   const long items = a.balanced ? (long)a.items : (long)a.B * a.Hkv * nrb * a.chunks;
   const long blocks = (items + kXcds - 1) / kXcds * kXcds;
-  auto kern = attn_mfma2_kernel<D, QW, NW, NST, PP>;
+  auto kern = attn_mfma2_kernel<D, QW, NW, NST>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (e != hipSuccess) return e;
@@ -757,21 +654,20 @@ static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// rows per workgroup -> shape: 64 rows = 4 waves x 16 queries (one wave per
-// SIMD, 4-deep ring); 128 = 8 x 16 and 256 = 8 x 32 (two waves per SIMD, the
-// two-group schedule, 5-deep ring: 160 KB at D = 128).  One workgroup per CU.
+// rows per workgroup -> shape: 64 rows = 4 waves x 16 queries, 128 = 8 x 16
+// and 256 = 8 x 32; each one workgroup per CU with a 4-deep 128 KB ring.
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.D == 64) {
     switch (a.rows_per_block) {
-      case 64: return launch_cfg<64, 16, 4, 4, false>(a, s);
-      case 128: return launch_cfg<64, 16, 8, 5, true>(a, s);
-      default: return launch_cfg<64, 32, 8, 5, true>(a, s);
+      case 64: return launch_cfg<64, 16, 4, 4>(a, s);
+      case 128: return launch_cfg<64, 16, 8, 4>(a, s);
+      default: return launch_cfg<64, 32, 8, 4>(a, s);
     }
   }
   switch (a.rows_per_block) {
-    case 64: return launch_cfg<128, 16, 4, 4, false>(a, s);
-    case 128: return launch_cfg<128, 16, 8, 5, true>(a, s);
-    default: return launch_cfg<128, 32, 8, 5, true>(a, s);
+    case 64: return launch_cfg<128, 16, 4, 4>(a, s);
+    case 128: return launch_cfg<128, 16, 8, 4>(a, s);
+    default: return launch_cfg<128, 32, 8, 4>(a, s);
   }
 }
 
