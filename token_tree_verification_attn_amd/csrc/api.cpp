@@ -65,9 +65,12 @@ ttv_status attn_plan(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, int Lma
     chunk = chunk_hint;
   } else {
     // split the prefix only as far as needed to occupy the free slots, in
-    // chunks of at least 256 keys (fp32 partials cost ~2*rows/chunk of the KV)
+    // chunks of at least 256 keys (fp32 partials cost ~2*rows/chunk of the KV),
+    // and not at all up to 512 keys: there a split saves at most a few tiles
+    // per workgroup, about what the combine launch costs (measured on MI355X:
+    // 32 heads x 64 rows x 512 keys, unsplit 4% faster than two chunks)
     const long want = (slots + units - 1) / units;
-    long c = want > 1 ? (Lmax + want - 1) / want : Lmax;
+    long c = want > 1 && Lmax > 512 ? (Lmax + want - 1) / want : Lmax;
     c = (c + 63) / 64 * 64;
     if (c < 256) c = 256;
     chunk = (int)c;
