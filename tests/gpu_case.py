@@ -105,11 +105,14 @@ def check_verify(d, t=None):
     return path, plen, outt, st
 
 
-def check_commit(d, t, path, plen):
-    """kv_commit on device copies of the cache vs the oracle's byte copy."""
+def check_commit(d, t, path, plen, in_place=False):
+    """kv_commit on device copies of the cache vs the oracle's byte copy; with
+    in_place the new lengths overwrite the input lengths (one workgroup per
+    request), else they go to their own array (one per request and kv head)."""
     kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
-    clo, src, st = ttv.kv_commit(t["k_tree"], t["v_tree"], kc, vc, t["cache_len"], path, plen,
-                                 d["Lmax"])
+    lens = t["cache_len"].clone()
+    clo, src, st = ttv.kv_commit(t["k_tree"], t["v_tree"], kc, vc, lens, path, plen, d["Lmax"],
+                                 cache_len_out=lens if in_place else None)
     torch.cuda.synchronize()
     view = torch.int16 if kc.dtype == torch.bfloat16 else torch.int32
     np_dt = np.int16 if kc.dtype == torch.bfloat16 else np.int32

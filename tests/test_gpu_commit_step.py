@@ -19,10 +19,11 @@ def commit_case(**kw):
     return synth.make(synth.Spec(**base), with_verify=False)
 
 
+@pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("kw", [dict(), dict(dtype="f32", D=64), dict(N=128, tree="chain"),
-                                dict(B=9, N=1)])
-def test_commit_paths(kw):
-    announce("commit %s" % kw)
+                                dict(B=9, N=1), dict(Hkv=8, Hq=8, N=40, B=3), dict(Hkv=1, Hq=4)])
+def test_commit_paths(kw, in_place):
+    announce("commit %s in_place=%s" % (kw, in_place))
     d = commit_case(**kw)
     t = to_dev(d)
     rng = np.random.default_rng(5)
@@ -40,18 +41,19 @@ def test_commit_paths(kw):
             p.append(u)
         path[b, :len(p)] = p
         plen[b] = len(p)
-    check_commit(d, t, torch.from_numpy(path).cuda(), torch.from_numpy(plen).cuda())
+    check_commit(d, t, torch.from_numpy(path).cuda(), torch.from_numpy(plen).cuda(), in_place)
 
 
-def test_commit_rejects_bad_requests():
-    announce("commit bad requests")
+@pytest.mark.parametrize("in_place", [False, True])
+def test_commit_rejects_bad_requests(in_place):
+    announce("commit bad requests in_place=%s" % in_place)
     d = commit_case(B=4)
     t = to_dev(d)
     path = torch.zeros((4, 16), dtype=torch.int32, device="cuda") - 1
     path[:, 0] = 0
     path[2, 1] = 16                                    # node id out of range
     plen = torch.tensor([1, 17, 2, 0], dtype=torch.int32, device="cuda")  # 17 > N
-    check_commit(d, t, path, plen)
+    check_commit(d, t, path, plen, in_place)
 
 
 def test_commit_in_place_lengths():
