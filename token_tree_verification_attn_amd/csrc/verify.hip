@@ -76,11 +76,16 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __rest
   }
 }
 
-// Kernel B: one wavefront per request.  amax[i] from the partials, then the
-// acceptance scan over parent indices: e_i = (token of i == amax of its
-// parent), E = ballot(e_i or i == 0), and node i is accepted iff its whole
-// root path lies in E, i.e. (anc[i] & ~E) == 0.  The path ends at the deepest
-// accepted node (lowest index on ties), found with a wave max.
+// Kernel B: one wavefront per request; lane l holds nodes l and l + 64.
+// Everything it reads (parents, tokens, the nodes' argmax partials) is
+// requested at once; the rest works on registers: ancestor bitsets by
+// shuffle pointer doubling, amax of a node's parent by a shuffle from the
+// lane that holds it.  e_i = (token of i == amax of its parent),
+// E = ballot(e_i or i == 0), and node i is accepted iff its whole root path
+// lies in E, i.e. (anc[i] & ~E) == 0.  The path ends at the deepest accepted
+// node (lowest index on ties), found with a wave max; LDS only orders the
+// path's nodes by depth.
+constexpr int kMaxSplits = 4;  // greedy_plan never makes more
 __global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
                                                          const int32_t* __restrict__ parents,
                                                          const int32_t* __restrict__ tokens,
@@ -90,15 +95,34 @@ __global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
                                                          int32_t* __restrict__ path_len,
                                                          int32_t* __restrict__ out_tokens,
                                                          int32_t* __restrict__ dev_status) {
-  __shared__ uint64_t s_anc[2 * kMaxNodes];
-  __shared__ int32_t s_depth[kMaxNodes];
-  __shared__ int32_t s_amax[kMaxNodes];
   __shared__ int32_t s_path[kMaxNodes];
   const int b = blockIdx.x, lane = threadIdx.x;
+  const int i0 = lane, i1 = lane + 64;
+  const bool v0 = i0 < N, v1 = i1 < N;
   const int32_t* par = parents + (size_t)b * N;
   const int32_t* tok = tokens + (size_t)b * N;
-  const bool ok = wave_build_tree(par, N, s_anc, s_depth);
-  if (!ok) {
+  const int p0 = v0 ? par[i0] : -1, p1 = v1 ? par[i1] : -1;
+  const int t0 = v0 ? tok[i0] : -1, t1 = v1 ? tok[i1] : -1;
+  float bv0[kMaxSplits], bv1[kMaxSplits];
+  int bi0[kMaxSplits], bi1[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    const size_t r0 = ((size_t)b * N + i0) * splits + sp, r1 = ((size_t)b * N + i1) * splits + sp;
+    const bool u0 = v0 && sp < splits, u1 = v1 && sp < splits;
+    bv0[sp] = u0 ? ws_val[r0] : -INFINITY;
+    bi0[sp] = u0 ? ws_idx[r0] : INT_MAX;
+    bv1[sp] = u1 ? ws_val[r1] : -INFINITY;
+    bi1[sp] = u1 ? ws_idx[r1] : INT_MAX;
+  }
+  float m0 = -INFINITY, m1 = -INFINITY;
+  int am0 = INT_MAX, am1 = INT_MAX;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    amax_merge(m0, am0, bv0[sp], bi0[sp]);
+    amax_merge(m1, am1, bv1[sp], bi1[sp]);
+  }
+  uint64_t a0lo, a1lo, a1hi;
+  if (!wave_tree_bits(p0, p1, N, a0lo, a1lo, a1hi)) {
     for (int k = lane; k < N; k += kWave) {
       path[(size_t)b * N + k] = -1;
       out_tokens[(size_t)b * N + k] = -1;
@@ -109,32 +133,39 @@ __global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
     }
     return;
   }
-  for (int i = lane; i < N; i += kWave) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    for (int sp = 0; sp < splits; ++sp)
-      amax_merge(bv, bi, ws_val[((size_t)b * N + i) * splits + sp], ws_idx[((size_t)b * N + i) * splits + sp]);
-    s_amax[i] = bi;
-  }
-  __syncthreads();
-  const int i0 = lane, i1 = lane + 64;
-  const bool e0 = i0 < N && (i0 == 0 || tok[i0] == s_amax[par[i0]]);
-  const bool e1 = i1 < N && tok[i1] == s_amax[par[i1]];
+  // node x lives in lane x & 63, slot x >> 6: both slots are shuffled by
+  // every lane, then each picks its own
+  auto node_int = [&](int x0, int x1, int x) {
+    const int a = __shfl(x0, x & 63), c = __shfl(x1, x & 63);
+    return x < 64 ? a : c;
+  };
+  const int q0 = max(p0, 0), q1 = max(p1, 0);
+  const int amp0 = node_int(am0, am1, q0), amp1 = node_int(am0, am1, q1);
+  const bool e0 = v0 && (i0 == 0 || t0 == amp0);
+  const bool e1 = v1 && t1 == amp1;
   const uint64_t E0 = __ballot(e0), E1 = __ballot(e1);
+  const int d0 = __popcll(a0lo) - 1, d1 = __popcll(a1lo) + __popcll(a1hi) - 1;
   int key = -1;  // (depth, -index) of the deepest accepted node
-  if (i0 < N && (s_anc[2 * i0] & ~E0) == 0ull && (s_anc[2 * i0 + 1] & ~E1) == 0ull)
-    key = max(key, (s_depth[i0] << 8) | (255 - i0));
-  if (i1 < N && (s_anc[2 * i1] & ~E0) == 0ull && (s_anc[2 * i1 + 1] & ~E1) == 0ull)
-    key = max(key, (s_depth[i1] << 8) | (255 - i1));
+  if (v0 && (a0lo & ~E0) == 0ull) key = max(key, (d0 << 8) | (255 - i0));
+  if (v1 && (a1lo & ~E0) == 0ull && (a1hi & ~E1) == 0ull) key = max(key, (d1 << 8) | (255 - i1));
   key = wave_max_i32(key);  // the root is always accepted: key >= 0
   const int end = 255 - (key & 255), dend = key >> 8;
-  const uint64_t pe0 = s_anc[2 * end], pe1 = s_anc[2 * end + 1];
-  if (i0 < N && ((pe0 >> i0) & 1ull)) s_path[s_depth[i0]] = i0;
-  if (i1 < N && ((pe1 >> (i1 - 64)) & 1ull)) s_path[s_depth[i1]] = i1;
+  const uint64_t x_lo0 = shfl_u64(a0lo, end & 63), x_lo1 = shfl_u64(a1lo, end & 63);
+  const uint64_t x_hi1 = shfl_u64(a1hi, end & 63);
+  const uint64_t pe0 = end < 64 ? x_lo0 : x_lo1, pe1 = end < 64 ? 0ull : x_hi1;
+  if (v0 && ((pe0 >> i0) & 1ull)) s_path[d0] = i0;
+  if (v1 && ((pe1 >> (i1 - 64)) & 1ull)) s_path[d1] = i1;
   __syncthreads();
-  for (int k = lane; k < N; k += kWave) {
-    path[(size_t)b * N + k] = k <= dend ? s_path[k] : -1;
-    out_tokens[(size_t)b * N + k] = k < dend ? tok[s_path[k + 1]] : (k == dend ? s_amax[end] : -1);
+  const int am_end = node_int(am0, am1, end);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int k = lane + r * kWave;
+    const int nxt = (k < N && k < dend) ? s_path[k + 1] : 0;
+    const int tk = node_int(t0, t1, nxt);
+    if (k < N) {
+      path[(size_t)b * N + k] = k <= dend ? s_path[k] : -1;
+      out_tokens[(size_t)b * N + k] = k < dend ? tk : (k == dend ? am_end : -1);
+    }
   }
   if (lane == 0) {
     path_len[b] = dend + 1;
@@ -149,7 +180,7 @@ GreedyPlan greedy_plan(int B, int N, int V) {
   const long rows = (long)B * N;
   long s = (512 + rows - 1) / rows;
   const long cap = V / 4096 > 1 ? V / 4096 : 1;
-  if (s > 4) s = 4;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   int slice = (int)((V + s - 1) / s);
