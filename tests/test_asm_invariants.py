@@ -1,5 +1,5 @@
-"""Properties of the compiled tree-attention kernels that their correctness
-rests on but that no numeric test can pin down reliably (CPU only: hipcc
+"""Properties of the compiled kernels that their correctness or speed rests on
+but that no numeric test can pin down reliably (CPU only: hipcc
 cross-compiles gfx950 assembly without a GPU).
 
 The query and parent loads of attn_mfma.hip are issued as inline assembly
@@ -7,11 +7,12 @@ ahead of the tile copies and waited for by one `s_waitcnt vmcnt(N)` statement
 that names their registers in a trailing comment.  The compiler does not know
 those registers are still being written: if it read or copied one before that
 wait, the kernel would use stale data.  So, for every attention kernel:
-  * no private (scratch) memory -- scratch accesses would also wait on the
-    tile copies;
   * exactly one such wait, guarding exactly the async loads' destinations;
   * on every control-flow path from the loads to the wait, no instruction
     touches a register whose load is still in flight.
+And no kernel of the library uses private (scratch) memory: scratch accesses
+are vector memory operations, so each one waits on every load in flight (the
+tile copies, the row passes).
 """
 import os
 import re
@@ -73,10 +74,21 @@ def test_every_shape_compiled(asm):
     assert len(names) == 6, sorted(names)
 
 
-def test_no_private_memory(asm):
-    for name, (ins, _) in kernels(asm).items():
-        assert not [t for t in ins if t.startswith("scratch_")], name
-    assert not [l for l in asm if re.search(r"\.private_segment_fixed_size:\s*[1-9]", l)]
+@pytest.mark.parametrize("src", ["attn_mfma.hip", "attn.hip", "verify.hip", "commit.hip",
+                                 "topology.hip"])
+def test_no_private_memory(src, tmp_path):
+    # every kernel of the library: private (scratch) accesses are vector
+    # memory operations, so each one also waits on the loads in flight
+    if not os.path.exists(ttv_build.HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    out = str(tmp_path / "k.s")
+    flags = [f for f in ttv_build.FLAGS if f not in ("-shared", "-fPIC")]
+    res = subprocess.run([ttv_build.HIPCC] + flags + ["--cuda-device-only", "-S", "-o", out,
+                          os.path.join(ttv_build.CSRC, src)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    lines = open(out).read().split("\n")
+    assert not [l for l in lines if l.strip().startswith("scratch_")], src
+    assert not [l for l in lines if re.search(r"\.private_segment_fixed_size:\s*[1-9]", l)], src
 
 
 def guard_violations(ins, labels):

@@ -231,9 +231,12 @@ __device__ __forceinline__ uint64_t fx40(float x) {
 // (v = 4*(t + 1024*j)) and the 4-byte (v = t + 1024*k) walks conflict-free.
 __device__ __forceinline__ int widx(int v) { return v + 4 * (v >> 7); }
 
-// floor(x * 2^40) as a double: exact, and so is any sum of such terms below
-// 2^53 in any order -- the same integers fx40() gives, summed in the fp64 ALU.
-__device__ __forceinline__ double fx40d(float x) { return floor(ldexp((double)x, 40)); }
+// floor(x * 2^40) as a double, for x in [0, 1]: the scaling by 2^40 and the
+// floor are exact in fp32 (a power-of-two scale of a float, no overflow; a
+// result of 2^23 or more is already an integer), the widening is exact, and
+// so is any sum of such terms below 2^53 in any order -- the same integers
+// fx40() gives.
+__device__ __forceinline__ double fx40d(float x) { return (double)floorf(x * 0x1p40f); }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -254,32 +257,27 @@ __device__ __forceinline__ double block_sum_f64(double v, double* s_redd) {
   return t;
 }
 
-__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* s_red) {
+// Exclusive prefix sum over the threads of the block (thread order) of
+// integer-valued doubles (exact below 2^53); `total` gets the block's sum.
+__device__ __forceinline__ double block_excl_scan_f64(double v, double* s_redd, double& total) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  v = wave_sum_u64(v);
-  __syncthreads();  // s_red free from its previous use
-  if (lane == 0) s_red[wave] = v;
-  __syncthreads();
-  uint64_t t = 0;
-#pragma unroll
-  for (int w = 0; w < kMssThreads / 64; ++w) t += s_red[w];
-  return t;
-}
-
-// Exclusive prefix sum over the threads of the block (thread order).
-__device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* s_red) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint64_t incl = v;
+  double incl = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const uint64_t o = shfl_u64(incl, lane >= d ? lane - d : lane);
+    const double o = __shfl_up(incl, d);
     if (lane >= d) incl += o;
   }
+  __syncthreads();  // s_redd free from its previous use
+  if (lane == 63) s_redd[wave] = incl;
   __syncthreads();
-  if (lane == 63) s_red[wave] = incl;
-  __syncthreads();
-  uint64_t before = 0;
-  for (int w = 0; w < wave; ++w) before += s_red[w];
+  double before = 0.0, tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kMssThreads / 64; ++w) {
+    const double x = s_redd[w];
+    tot += x;
+    before += w < wave ? x : 0.0;
+  }
+  total = tot;
   return before + incl - v;
 }
 
@@ -386,12 +384,12 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   __shared__ float s_rq[kMaxNodes];  // u_accept[c] * q_c[token c]: the left side of c's test at s = 1
   __shared__ unsigned long long s_kids[kMaxNodes][2];
   __shared__ uint64_t s_first_ok[2];
-  __shared__ uint64_t s_red[kMssThreads / 64];
   __shared__ double s_redd[kMssThreads / 64];
   __shared__ int s_status, s_pick;
 
   const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
   const size_t rowN = (size_t)b * N;
+  const float ub = u_bonus[b];  // requested now, used by the final draw
   // ---- tree, tokens and the children of every node
   if (t < N) {
     s_par[t] = parents[rowN + t];
@@ -450,17 +448,6 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     mss_row_to_lds<VEC>(llm + (rowN + u) * V, V, s_w);
     __syncthreads();
   };
-  auto pop_child = [](uint64_t& k0, uint64_t& k1) {
-    int c;
-    if (k0) {
-      c = __ffsll((unsigned long long)k0) - 1;
-      k0 &= k0 - 1;
-    } else {
-      c = 64 + __ffsll((unsigned long long)k1) - 1;
-      k1 &= k1 - 1;
-    }
-    return c;
-  };
 
   // ---- the walk: control flow is uniform, decisions are recomputed by every
   // thread from the same LDS values.  Every row is requested whole: one
@@ -484,7 +471,16 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     int next = -1;
     bool first = true;
     while (k0 | k1) {
-      const int c = pop_child(k0, k1);
+      // lowest remaining child (written out: a helper taking both words by
+      // reference made the compiler keep them in private memory)
+      int c;
+      if (k0) {
+        c = __ffsll((unsigned long long)k0) - 1;
+        k0 &= k0 - 1;
+      } else {
+        c = 64 + __ffsll((unsigned long long)k1) - 1;
+        k1 &= k1 - 1;
+      }
       if (!first) {  // c's test against w, mass s
         const bool accept = s_rq[c] * s < s_w[widx(s_tok[c])];
         __syncthreads();  // every thread has read w[x] before it is updated below
@@ -507,27 +503,65 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     u = next;
   }
 
-  // ---- bonus: inverse CDF over the exact integer prefix sums of fx40(w)
-  const int per = (V + kMssThreads - 1) / kMssThreads;
+  // ---- bonus: inverse CDF over the exact integer prefix sums of fx40(w).
+  // Thread t owns the entries [per*t, per*t + per), per a multiple of 4, so
+  // each 4-entry group is 16 aligned bytes of s_w (a 128-entry block never
+  // splits one); masses are exact integers carried in doubles.
+  const int per = 4 * ((V + 4 * kMssThreads - 1) / (4 * kMssThreads));
+  constexpr int kGroups = (kMssMaxVocab + 4 * kMssThreads - 1) / (4 * kMssThreads);
   const int v_lo = min(V, t * per), v_hi = min(V, v_lo + per);
-  uint64_t mine = 0;
-  for (int v = v_lo; v < v_hi; ++v) mine += fx40(s_w[widx(v)]);
-  const uint64_t excl = block_excl_scan_u64(mine, s_red);
-  const uint64_t S = block_sum_u64(mine, s_red);
+  double mine = 0.0, gsum[kGroups];  // gsum[i]: mass of the group at v_lo + 4i
+#pragma unroll
+  for (int i = 0; i < kGroups; ++i) {
+    const int v = v_lo + 4 * i;
+    double g = 0.0;
+    if (v < v_hi) {
+      const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g += v + e < v_hi ? fx40d(w4[e]) : 0.0;
+    }
+    gsum[i] = g;
+    mine += g;
+  }
+  double Sd;
+  const double excl = block_excl_scan_f64(mine, s_redd, Sd);
   if (t == 0) s_pick = -1;
   __syncthreads();
-  if (S > 0) {
-    const uint64_t R = (uint64_t)(u_bonus[b] * 16777216.0f);
+  if (Sd > 0.0) {
+    const uint64_t S = (uint64_t)Sd, lo = (uint64_t)excl, hi = (uint64_t)(excl + mine);
+    const uint64_t R = (uint64_t)(ub * 16777216.0f);
     const uint64_t T = R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24);  // floor(R*S/2^24)
-    if (excl <= T && T < excl + mine) {
-      uint64_t cum = excl;
-      for (int v = v_lo; v < v_hi; ++v) {
-        cum += fx40(s_w[widx(v)]);
-        if (cum > T) {
-          s_pick = v;
-          break;
+    if (lo <= T && T < hi) {
+      // the group that crosses T from the register sums, then its entries
+      // (unrolled with constant indices: gsum stays in registers; a group
+      // with no entries has mass 0 and never crosses)
+      uint64_t cum = lo;
+      int gi = kGroups - 1;
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < kGroups; ++i) {
+        const uint64_t g = (uint64_t)gsum[i];
+        if (!found && cum + g > T) {
+          gi = i;
+          found = true;
+        } else if (!found) {
+          cum += g;
         }
       }
+      const int v = v_lo + 4 * gi;
+      const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
+      int pick = v_hi - 1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (v + e < v_hi) {
+          cum += fx40(w4[e]);
+          if (cum > T) {
+            pick = v + e;
+            break;
+          }
+        }
+      }
+      s_pick = pick;
     }
   } else if (t == 0) {  // nothing representable left: the largest entry
     int bi = 0;
