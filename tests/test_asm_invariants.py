@@ -91,6 +91,17 @@ def test_no_private_memory(src, tmp_path):
     assert not [l for l in lines if re.search(r"\.private_segment_fixed_size:\s*[1-9]", l)], src
 
 
+def test_copies_padded_after_their_base(asm):
+    # each tile copy reads its base address from SGPRs that v_readfirstlane
+    # (VALU) wrote just before; a vector-memory read of an SGPR needs 5 wait
+    # states after a VALU write of it, and the compiler cannot add them inside
+    # inline assembly (without them a copy took a stale base and faulted)
+    for name, (ins, _) in kernels(asm).items():
+        copies = [i for i, t in enumerate(ins) if t.startswith("global_load_lds")]
+        assert copies, name
+        assert all(ins[i - 1].startswith("s_nop 4") for i in copies), name
+
+
 def guard_violations(ins, labels):
     """Instructions that touch a register of an async load before its wait,
     on any control-flow path from the first load to the wait."""

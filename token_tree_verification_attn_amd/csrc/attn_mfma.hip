@@ -72,7 +72,13 @@ __device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)g);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
   const uint64_t gs = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(m0), "v"(voff), "s"(gs) : "memory", "m0");
+  // M0 (the LDS base) is an operand bound to that register: the compiler
+  // loads it and knows it changed.  The SGPR pair is written by VALU
+  // (v_readfirstlane) just before; a vector-memory read of an SGPR needs 5
+  // wait states after a VALU write of it, which the compiler inserts for
+  // instructions it sees but not inside inline assembly -- hence the s_nop
+  // (without it the copy can take a stale base and fault).
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %1, %2" : : "{m0}"(m0), "v"(voff), "s"(gs) : "memory");
 }
 
 // Loads of the queries and parent indices, issued before the tile copies and
