@@ -57,7 +57,7 @@ def kernels(lines):
     for i, name in starts:
         ins, labels = [], {}
         j = i + 1
-        while "s_endpgm" not in lines[j]:
+        while not lines[j].startswith(".Lfunc_end"):  # (a kernel may end early too)
             m = re.match(r"^(\.LBB\w+):", lines[j])
             t = lines[j].strip()
             if m:
@@ -130,6 +130,8 @@ def guard_violations(ins, labels):
                 continue
             if vregs(rest) & pend:
                 bad.append(t)
+            if op == "s_endpgm":
+                break
             if op == "s_branch":
                 pc = labels[rest.strip()]
                 continue
