@@ -9,12 +9,15 @@ Runs, each as its own child process under rocprofv3 (the program follows
   2. --pmc FETCH_SIZE, then --pmc WRITE_SIZE of the same bench in eager mode,
      one counter group per run -> KiB per dispatch of every tree_attn kernel;
   3. the same two counters on a plain device copy of known size (`--copy-ref`
-     mode of this script), whose ratio to the true bytes calibrates them.
-Writes tree_attn_W_kernels.md (durations, with the command) and
+     mode of this script), whose ratio to the true bytes calibrates them;
+  4. one --pmc run of SQ counters plus GRBM_GUI_ACTIVE on the eager bench ->
+     matrix-core busy fraction and instruction mix of the attention kernels.
+Writes tree_attn_W_kernels.md (durations, with the command),
 tree_attn_W_traffic.json + .md (HBM bytes per tree_attn launch = calibrated
 FETCH + WRITE, tagged with the kernel sources' hash; bench.py reports it only
-while that hash matches) to gpurun_out/profile_W/summary/ -- the summaries
-that are kept are copied from there into profiles/.
+while that hash matches) and tree_attn_W_counters.md to
+gpurun_out/profile_W/summary/ -- the summaries that are kept are copied from
+there into profiles/.
 """
 from __future__ import annotations
 
@@ -30,6 +33,10 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 256 << 20
+CUS, SIMDS_PER_CU, XCDS = 256, 4, 8
+# one pass: at most 8 SQ counters and 2 GRBM counters per run
+SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_MFMA",
+               "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT"]
 
 
 def copy_ref():
@@ -149,6 +156,30 @@ def main():
         fh.write("\nCommands (run from /tmp with TMPDIR=/tmp):\n\n")
         for c in rec["commands"]:
             fh.write("    %s\n" % c)
+    # 4. matrix-core busy fraction and instruction mix
+    ctrs = SQ_COUNTERS + ["GRBM_GUI_ACTIVE"]
+    f, c_sq = rocprof(os.path.join(out, "sq"), ["--pmc"] + ctrs, eager, 120)
+    per = {k: counter_kib(f, k, ["attn_mfma2", "attn_fma"]) for k in ctrs}
+    with open(os.path.join(dest, "tree_attn_%s_counters.md" % w), "w") as fh:
+        fh.write("# SQ counters of the attention kernel, workload %s\n\n" % w)
+        fh.write("One rocprofv3 --pmc run (averages per dispatch):\n\n    %s\n\n" % c_sq)
+        fh.write("SQ_VALU_MFMA_BUSY_CYCLES sums the SIMDs' matrix-core busy cycles (16 per "
+                 "v_mfma_f32_16x16x32_bf16) and GRBM_GUI_ACTIVE the %d XCDs' active cycles, so "
+                 "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d x %d CUs x %d "
+                 "SIMDs); VALU issue = 4 cycles per SQ_INSTS_VALU (wave64 on a 16-lane SIMD) over "
+                 "the same SIMD-cycles.\n\n" % (XCDS, XCDS, CUS, SIMDS_PER_CU))
+        fh.write("| kernel | MFMA busy | VALU issue | MFMA instr | VALU instr | LDS instr "
+                 "| LDS wait / wave cycles | LDS bank conflicts | active cycles per XCD |\n"
+                 "|---|---|---|---|---|---|---|---|---|\n")
+        for name in per["SQ_INSTS_MFMA"]:
+            g = {k: per[k].get(name, float("nan")) for k in ctrs}
+            simd_cycles = g["GRBM_GUI_ACTIVE"] / XCDS * CUS * SIMDS_PER_CU
+            fh.write("| `%s` | %.1f%% | %.1f%% | %.3g | %.3g | %.3g | %.1f%% | %.3g | %.3g |\n" % (
+                name.split("(")[0], 100 * g["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles,
+                100 * 4 * g["SQ_INSTS_VALU"] / simd_cycles, g["SQ_INSTS_MFMA"],
+                g["SQ_INSTS_VALU"], g["SQ_INSTS_LDS"],
+                100 * g["SQ_WAIT_INST_LDS"] / max(g["SQ_WAVE_CYCLES"], 1),
+                g["SQ_LDS_BANK_CONFLICT"], g["GRBM_GUI_ACTIVE"] / XCDS))
     print(json.dumps({k: rec[k] for k in ("workload", "hbm_bytes_per_launch",
                                           "algorithmic_kv_bytes", "fetch_factor")}))
 
