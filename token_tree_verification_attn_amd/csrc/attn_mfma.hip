@@ -2,9 +2,10 @@
 // Attention", "Tree-Based Parallel Decoding"; [SSD] §3 "Implementation": a
 // cache part and an in-tree part, both feeding one softmax).
 //
-// One workgroup = 4 wavefronts handles one (request b, kv head h, block of
-// 4*QW packed query rows r = node*G + g, chunk of prefix keys).  Per tile of
-// KT keys:
+// One workgroup = NW wavefronts (4 or 8, one workgroup per CU) handles one
+// (request b, kv head h, block of NW*QW packed query rows r = node*G + g,
+// chunk of its key tiles: prefix tiles first, then in-tree tiles).  Per tile
+// of KT keys:
 //   S^T[key][query] = K Q^T     v_mfma_f32_16x16x32_bf16, A = K (LDS,
 //                               ds_read_b128), B = the wave's queries (VGPRs)
 //   online softmax on S^T       a query's KT scores sit in 4 lanes x KT/16
@@ -30,7 +31,6 @@
 #include "ttv_common.h"
 
 #define TTV_LDS __attribute__((address_space(3)))
-#define TTV_GLOBAL __attribute__((address_space(1)))
 
 namespace ttv {
 
