@@ -111,3 +111,19 @@ def test_balanced_split(case):
     if lengths is not None:
         d["cache_len"] = np.array(lengths, np.int32)
     check_attn(d)
+
+
+@pytest.mark.parametrize("L,ck", [(0, 0), (191, 0), (192, 0), (193, 0), (1000, 0), (4096, 0),
+                                  (191, 256), (450, 256), (4095, 256)])
+def test_prefix_shorter_than_promise(L, ck):
+    """One request (fixed split), promised 4096 keys, holding L: the first
+    tiles of a chunk are copied before L is read, so every cache row at or
+    past L is NaN here -- a copy of such a row reaching the math would turn
+    the outputs into NaN."""
+    announce("attn prefix %d of promised 4096, chunk_keys=%d" % (L, ck))
+    d = synth.make(spec(B=1, N=48, Hq=16, Hkv=4, L=4096))
+    d["cache_len"] = np.array([L], np.int32)
+    for k in ("k_cache", "v_cache"):
+        d[k] = d[k].copy()
+        d[k][:, :, L:, :] = np.nan
+    check_attn(d, chunk_keys=ck)

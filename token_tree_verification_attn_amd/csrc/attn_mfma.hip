@@ -169,12 +169,18 @@ struct MfmaCfg {
   static constexpr int TILE_BYTES = KT * D * 2;        // one K (or V) tile
   static constexpr int LOADS = TILE_BYTES / 16 / kThreads;  // per thread per tile
   static constexpr int RB = kWaves * QW;       // query rows per workgroup
+  // LDS: the K tiles of all stages, then the V tiles of all stages, so that
+  // every stage, key-block and 32-key-step offset of the fragment reads is
+  // below 64 KB of a per-lane base and fits the DS instructions' 16-bit
+  // immediate (no address arithmetic in the tile loop)
   static constexpr int LDS_BYTES = NST * 2 * TILE_BYTES;
+  static constexpr int V_REGION = NST * TILE_BYTES;
   // one workgroup per CU: the 4-deep ring takes 128 KB of LDS
   static constexpr int MIN_BLOCKS = 1;
   static_assert(LOADS >= 1 && TILE_BYTES % (16 * kThreads) == 0, "tile / loads");
   static_assert(NST >= 2 && NST <= 4, "ring depth");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
+  static_assert(V_REGION <= 65536, "fragment read offsets must fit the 16-bit DS offset");
 };
 
 // Chunk swizzles: the physical 16-byte slot of logical chunk c of key row k.
@@ -229,16 +235,27 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   }
   const int bh = b * a.Hkv + h;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is wave-uniform; readfirstlane tells the compiler so, which
+  // keeps the copies' LDS destinations (M0) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g16 = lane >> 4, c16 = lane & 15;
   const int N = a.N, G = a.G, R = a.R;
   const int row_base = rb * C::RB + wave * QW;
   uint16_t* out = static_cast<uint16_t*>(a.out);
 
-  const char* kc = static_cast<const char*>(a.k_cache) + (size_t)bh * a.Lcap * D * 2;
-  const char* vc = static_cast<const char*>(a.v_cache) + (size_t)bh * a.Lcap * D * 2;
-  const char* ktr = static_cast<const char*>(a.k_tree) + (size_t)bh * N * D * 2;
-  const char* vtr = static_cast<const char*>(a.v_tree) + (size_t)bh * N * D * 2;
+  // The (request, kv head) bases come out of 64-bit products that the
+  // compiler forms on the VALU; they are wave-uniform, and readfirstlane
+  // puts them in scalar registers once, so that no copy needs its own.
+  auto uniform = [](const char* p) {
+    const uint64_t v = reinterpret_cast<uintptr_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+  };
+  const char* kc = uniform(static_cast<const char*>(a.k_cache) + (size_t)bh * a.Lcap * D * 2);
+  const char* vc = uniform(static_cast<const char*>(a.v_cache) + (size_t)bh * a.Lcap * D * 2);
+  const char* ktr = uniform(static_cast<const char*>(a.k_tree) + (size_t)bh * N * D * 2);
+  const char* vtr = uniform(static_cast<const char*>(a.v_tree) + (size_t)bh * N * D * 2);
 
   // ---- per-lane constants of the HBM -> LDS copies.  Wave w, copy j fills
   // LDS slots (j*NW + w)*64 + lane of a tile (16 bytes each, placed by the
@@ -256,11 +273,13 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     voff[j] = key * (D * 2) + swz_v<C::CPR>(key, phys) * 16;
   }
   // The request's prefix length (raw, for its status), its tree and this
-  // wave's queries are requested first; the prefix tiles of the fixed split
-  // wait for L, the topology is only needed at the first in-tree tile.  The
+  // wave's queries are requested first; the topology is only needed at the
+  // first in-tree tile.  L is read through the scalar cache: its wait then
+  // counts scalar loads only, not the tile copies issued meanwhile.  The
   // parent and query loads go out before the copies (see gload16_async);
   // lanes and rows past the end read index 0 / row 0 and are masked below.
-  const int L = a.cache_len[b];
+  const int L = *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(a.cache_len + b));
   const int32_t* par = a.parents + (size_t)b * N;
   int p0 = gload4_async(par + min(lane, N - 1));
   int p1 = gload4_async(par + min(lane + 64, N - 1));
@@ -278,6 +297,33 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qraw[qt * C::KS + ks] = gload16_async(qr + ks * 32);
   }
+  // ---- speculative prologue (fixed split): the first ring tiles of chunk c
+  // start at key c*chunk_keys whatever L is, so they are copied before L
+  // arrives -- but only if they lie below Lmax (inside the cache) and inside
+  // the chunk.  Once L is known, a chunk whose first tiles are not all full
+  // prefix tiles drains these copies and issues its real prologue (a copy of
+  // rows at or past L must not be used: those rows may hold non-finite
+  // values, and a zero probability times a NaN is still a NaN).
+  constexpr int kPre = NST - 1;
+  const int spec_begin = a.balanced ? 0 : c * a.chunk_keys;
+  const bool spec = !a.balanced && a.chunk_keys >= kPre * KT && spec_begin + kPre * KT <= a.Lmax;
+  auto issue_full = [&](int key0, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    TTV_LDS unsigned char* kst = (TTV_LDS unsigned char*)(s_dyn + S * C::TILE_BYTES);
+    TTV_LDS unsigned char* vst = (TTV_LDS unsigned char*)(s_dyn + C::V_REGION + S * C::TILE_BYTES);
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int wbase = (j * C::kWaves + wave) * 1024;
+      lds_dma16(kc + (size_t)key0 * (D * 2), koff[j], (uint32_t)(uintptr_t)(kst + wbase));
+      lds_dma16(vc + (size_t)key0 * (D * 2), voff[j], (uint32_t)(uintptr_t)(vst + wbase));
+    }
+  };
+  if (spec) {
+    issue_full(spec_begin, std::integral_constant<int, 0>{});
+    if (kPre > 1) issue_full(spec_begin + KT, std::integral_constant<int, 1 % NST>{});
+    if (kPre > 2) issue_full(spec_begin + 2 * KT, std::integral_constant<int, 2 % NST>{});
+  }
+
   Sched sc;
   if (a.balanced) {  // everything is known from the plan, L (clamped) included
     const int nPtot = (pl.L + KT - 1) / KT;  // the unit's tiles: nPtot prefix, then pl.nT in-tree
@@ -290,7 +336,9 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   } else {
     // L is clamped to [0, Lmax] for the copies, so they stay inside the
     // cache even when L is invalid; such a request is rejected at the end
-    const int Lc = min(max(L, 0), a.Lmax);
+    // (readfirstlane: L is uniform, and the copy bases derived from it stay
+    // in scalar registers)
+    const int Lc = min(max(__builtin_amdgcn_readfirstlane(L), 0), a.Lmax);
     sc.k_begin = c * a.chunk_keys;
     sc.k_end = min(Lc, sc.k_begin + a.chunk_keys);
     sc.nP = (sc.k_begin < sc.k_end) ? (sc.k_end - sc.k_begin + KT - 1) / KT : 0;
@@ -308,8 +356,8 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     const int nvalid = tree ? min(KT, N - key0) : min(KT, sc.k_end - key0);
     const char* ks = (tree ? ktr : kc) + (size_t)key0 * (D * 2);
     const char* vs = (tree ? vtr : vc) + (size_t)key0 * (D * 2);
-    TTV_LDS unsigned char* kst = (TTV_LDS unsigned char*)(s_dyn + S * 2 * C::TILE_BYTES);
-    TTV_LDS unsigned char* vst = kst + C::TILE_BYTES;
+    TTV_LDS unsigned char* kst = (TTV_LDS unsigned char*)(s_dyn + S * C::TILE_BYTES);
+    TTV_LDS unsigned char* vst = (TTV_LDS unsigned char*)(s_dyn + C::V_REGION + S * C::TILE_BYTES);
     const bool full = nvalid == KT;
 #pragma unroll
     for (int j = 0; j < C::LOADS; ++j) {
@@ -330,10 +378,16 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   // loop starts.  No workgroup barrier: the ring's first one is the first.
   // (explicit stages: a loop over tile % NST here keeps the source pointers
   // in private memory, and every access to those waits on the copies)
-  constexpr int kPre = NST - 1;
-  if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
-  if (kPre > 1 && ntiles > 1) issue(1, std::integral_constant<int, 1 % NST>{});
-  if (kPre > 2 && ntiles > 2) issue(2, std::integral_constant<int, 2 % NST>{});
+  // The speculative copies stand if the chunk's first kPre tiles are full
+  // prefix tiles from spec_begin; otherwise each wave drains them (it
+  // rewrites only its own LDS slots) and issues the real ones.
+  const bool spec_ok = spec && sc.k_begin == spec_begin && sc.k_end - sc.k_begin >= kPre * KT;
+  if (spec && !spec_ok) wait_vmcnt<0>();
+  if (!spec_ok) {
+    if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
+    if (kPre > 1 && ntiles > 1) issue(1, std::integral_constant<int, 1 % NST>{});
+    if (kPre > 2 && ntiles > 2) issue(2, std::integral_constant<int, 2 % NST>{});
+  }
   // Queries and parents have landed once no more than the prologue's copies
   // are outstanding.  One wait_pin with a fixed count (a short prologue
   // drains first): one per case would give the compiler one definition per
@@ -388,16 +442,23 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   // immediates).  K: lane (c16, g16) of key block kb reads row kb*16 + c16,
   // logical chunk ks*4 + g16; its swizzle depends on c16 only.  V: see the
   // transposed read below; its swizzle depends on g16*4 + c16/4 only.
+  // Each is kept as a full LDS address of stage 0 in a VGPR that the
+  // compiler cannot split (the empty asm): the stage and block offsets are
+  // then immediates of the reads.
   uint32_t krd[C::KS], vrd[C::DT];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)s_dyn;
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks)
-    krd[ks] = c16 * (D * 2) + swz_k<C::CPR>(c16, ks * 4 + g16) * 16;
+  for (int ks = 0; ks < C::KS; ++ks) {
+    krd[ks] = lds0 + c16 * (D * 2) + swz_k<C::CPR>(c16, ks * 4 + g16) * 16;
+    asm volatile("" : "+v"(krd[ks]));
+  }
   {
     const int vkey = g16 * 4 + (c16 >> 2);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       const int dcol = dt * 16 + 4 * (c16 & 3);
-      vrd[dt] = vkey * (D * 2) + swz_v<C::CPR>(vkey, dcol >> 3) * 16 + ((dcol >> 2) & 1) * 8;
+      vrd[dt] = lds0 + C::V_REGION + vkey * (D * 2) + swz_v<C::CPR>(vkey, dcol >> 3) * 16 + ((dcol >> 2) & 1) * 8;
+      asm volatile("" : "+v"(vrd[dt]));
     }
   }
 
@@ -421,12 +482,11 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   // latency for all of them)
   auto read_k = [&](auto stage_tag, KFrag& kf) {
     constexpr int S = decltype(stage_tag)::value;
-    const TTV_LDS unsigned char* kst = (const TTV_LDS unsigned char*)(s_dyn + S * 2 * C::TILE_BYTES);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-        kf[kb][ks] = *(const TTV_LDS u32x4*)(kst + krd[ks] + kb * 16 * (D * 2));
+        kf[kb][ks] = *(const TTV_LDS u32x4*)(uintptr_t)(krd[ks] + S * C::TILE_BYTES + kb * 16 * (D * 2));
   };
   // S^T = K Q^T, d-step outermost so that KB*QT independent accumulations
   // sit between two MFMAs of one chain
@@ -458,12 +518,11 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   constexpr bool kEarlyV = C::QT == 1;
   auto read_v = [&](auto stage_tag, int k2, VFrag& vlo, VFrag& vhi) {
     constexpr int S = decltype(stage_tag)::value;
-    const TTV_LDS unsigned char* vst = (const TTV_LDS unsigned char*)(s_dyn + S * 2 * C::TILE_BYTES) + C::TILE_BYTES;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      const TTV_LDS unsigned char* pa = vst + vrd[dt] + k2 * 32 * (D * 2);
-      vlo[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)pa);
-      vhi[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)(pa + 16 * (D * 2)));
+      const uint32_t pa = vrd[dt] + S * C::TILE_BYTES + k2 * 32 * (D * 2);
+      vlo[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)(uintptr_t)pa);
+      vhi[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)(uintptr_t)(pa + 16 * (D * 2)));
     }
   };
   // online softmax of tile `tile` in place of its scores; lane holds keys
