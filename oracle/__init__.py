@@ -54,8 +54,9 @@ def _bind(lib):
     lib.orc_verify_greedy.argtypes = [I, I, I, P, P, P, P, P, P, P]
     lib.orc_verify_mss.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P]
     lib.orc_kv_commit.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
+    lib.orc_tree_expand.argtypes = [I, I, I, I, P, P, P, I, P, P, P, P, P]
     for f in (lib.orc_topology, lib.orc_tree_attn_rows, lib.orc_verify_greedy,
-              lib.orc_verify_mss, lib.orc_kv_commit):
+              lib.orc_verify_mss, lib.orc_kv_commit, lib.orc_tree_expand):
         f.restype = None
     return lib
 
@@ -230,3 +231,31 @@ def kv_commit(k_tree, v_tree, k_cache, v_cache, cache_len_in, path, path_len, Lm
                           clo.ctypes.data_as(V), pap, plp, src.ctypes.data_as(V),
                           st.ctypes.data_as(V))
     return kc, vc, clo, src, st
+
+
+def tree_expand(probs, frontier, n_in, k, parents, tokens, src_row=None):
+    """[SI] §3 "Expansion-based token tree construction", one level: every
+    frontier node (in order) gets its row's k most probable tokens (ties: the
+    lower token id) as children, appended after the n_in[b] existing nodes.
+
+    probs float32 [B,F,V], frontier int32 [B,F] (-1 = none), n_in int32 [B],
+    parents/tokens int32 [B,Ncap] (the existing tree; copies are returned),
+    src_row int32 [B,Ncap] or None ->
+    (parents, tokens, src_row, n_out int32 [B], status int32 [B]).
+    """
+    pr, pp = _c(probs, np.float32)
+    B, F, V = pr.shape
+    fr, fp = _c(frontier, np.int32)
+    ni, nip = _c(n_in, np.int32)
+    par = np.array(parents, np.int32, copy=True, order="C")
+    tok = np.array(tokens, np.int32, copy=True, order="C")
+    Ncap = par.shape[1]
+    src = (np.full((B, Ncap), -1, np.int32) if src_row is None
+           else np.array(src_row, np.int32, copy=True, order="C"))
+    n_out = np.empty(B, np.int32)
+    status = np.empty(B, np.int32)
+    P = ctypes.c_void_p
+    _load().orc_tree_expand(B, F, V, int(k), pp, fp, nip, Ncap, par.ctypes.data_as(P),
+                            tok.ctypes.data_as(P), src.ctypes.data_as(P),
+                            n_out.ctypes.data_as(P), status.ctypes.data_as(P))
+    return par, tok, src, n_out, status

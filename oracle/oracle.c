@@ -354,3 +354,61 @@ void orc_kv_commit(int B, int N, int Hkv, int D, int elt, int Lcap, int Lmax,
     status[b] = ORC_OK;
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Expansion-based token-tree construction, one level.  [SI] §3 "Expansion- */
+/* based token tree construction": a speculative model's top-k tokens at a   */
+/* node become that node's children (the LLM's token is often among them).   */
+/* For request b, the existing tree has n_in[b] nodes; every frontier node   */
+/* fr = frontier[b,f] >= 0, taken in order of f, gets k children: the k      */
+/* tokens of highest probability in its row probs[b,f,:], most probable      */
+/* first, an equal probability going to the lower token id.  They are        */
+/* appended as nodes n_in[b] + r*k + j (r = the rank of f among the frontier */
+/* entries >= 0), with src_row = f, so parents < children holds.             */
+/* A frontier entry outside [-1, n_in[b]) gives ORC_E_TREE, more than Ncap   */
+/* nodes (or n_in[b] < 1) ORC_E_SHAPE; such a request keeps n_out = n_in and */
+/* gets nothing written.  Selection by repeated scans for the best untaken   */
+/* token (k passes over the row).                                            */
+/* ------------------------------------------------------------------------ */
+void orc_tree_expand(int B, int F, int V, int k, const float* probs, const int32_t* frontier,
+                     const int32_t* n_in, int Ncap, int32_t* parents, int32_t* tokens,
+                     int32_t* src_row, int32_t* n_out, int32_t* status) {
+  unsigned char* taken = (unsigned char*)malloc((size_t)V);
+  for (int b = 0; b < B; ++b) {
+    const int32_t* fb = frontier + (size_t)b * F;
+    const int nin = n_in[b];
+    int count = 0, bad = 0;
+    for (int f = 0; f < F; ++f) {
+      if (fb[f] < -1 || fb[f] >= nin) bad = 1;
+      if (fb[f] >= 0) ++count;
+    }
+    n_out[b] = nin;
+    if (bad) {
+      status[b] = ORC_E_TREE;
+      continue;
+    }
+    if (nin < 1 || (long)nin + (long)count * k > Ncap) {
+      status[b] = ORC_E_SHAPE;
+      continue;
+    }
+    int pos = nin;
+    for (int f = 0; f < F; ++f) {
+      if (fb[f] < 0) continue;
+      const float* row = probs + ((size_t)b * F + f) * V;
+      memset(taken, 0, (size_t)V);
+      for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int v = 0; v < V; ++v)
+          if (!taken[v] && (best < 0 || row[v] > row[best])) best = v;  /* strict: lower id wins ties */
+        taken[best] = 1;
+        parents[(size_t)b * Ncap + pos] = fb[f];
+        tokens[(size_t)b * Ncap + pos] = best;
+        src_row[(size_t)b * Ncap + pos] = f;
+        ++pos;
+      }
+    }
+    n_out[b] = pos;
+    status[b] = ORC_OK;
+  }
+  free(taken);
+}

@@ -11,6 +11,7 @@ import pytest
 import oracle
 import test_oracle_attn as A
 import test_oracle_commit as C
+import test_oracle_expand as E
 import test_oracle_greedy as G
 import test_oracle_mss as M
 import test_oracle_topology as T
@@ -55,6 +56,12 @@ MUTANTS = [
      M.test_inverse_cdf_end_points),
     ("mss_accept_not_strict", "if (lhs < w[x]) { next = c; break; }",
      "if (lhs <= w[x]) { next = c; break; }", M.test_inverse_cdf_end_points),
+    ("expand_ties_to_highest", "(best < 0 || row[v] > row[best])", "(best < 0 || row[v] >= row[best])",
+     lambda: [E.test_topk_matches_stable_argsort_with_ties(s) for s in range(5)]),
+    ("expand_token_reused", "taken[best] = 1;", "taken[best] = 0;",
+     E.test_invariants_and_skipped_frontier_entries),
+    ("expand_rank_counts_holes", "if (fb[f] < 0) continue;", "if (fb[f] < 0) { pos += k; continue; }",
+     E.test_invariants_and_skipped_frontier_entries),
     ("commit_off_by_one", "* Lcap + (L + j)) * row;", "* Lcap + (L + j + 1)) * row;",
      C.test_full_chain_acceptance_appends_tree),
     ("commit_length", "cache_len_out[b] = L + n;", "cache_len_out[b] = L + n - 1;",
