@@ -242,6 +242,44 @@ ttv_status ttv_kv_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv,
                          const int32_t* path_len, int32_t* committed_src,
                          int32_t* dev_status, void* stream);
 
+/*
+ * ttv_tree_expand -- one level of expansion-based token-tree construction
+ * ([SI] §3 "Expansion-based token tree construction": a speculative model's
+ * top-k tokens at a node become that node's children).  For request b, whose
+ * tree has n_in[b] nodes in parents[b,:n_in[b]] / tokens[b,:n_in[b]], every
+ * frontier entry fr = frontier[b,f] >= 0, in order of f, gets k children: the
+ * k tokens of highest probability in probs[b,f,:], most probable first, an
+ * equal probability going to the lower token id.  With r = the rank of f
+ * among the request's entries >= 0, child j is node n = n_in[b] + r*k + j:
+ *   parents[b,n] = fr;  tokens[b,n] = token;  src_row[b,n] = f;
+ *   n_out[b] = n_in[b] + (number of entries >= 0) * k.
+ * Nodes are so numbered parents-first (expanding one depth per call in index
+ * order gives breadth-first numbering), and src_row tells which row each new
+ * token came from (the draft distribution a stochastic verifier needs).
+ * Entries < n_in[b] of parents/tokens/src_row and entries past n_out[b] are
+ * untouched.
+ *
+ *   probs        float32 [B,F,V] device, no NaN (other values compared as
+ *                they are).
+ *   frontier     int32 [B,F] device: node ids in [0, n_in[b]), -1 = none.
+ *   n_in         int32 [B] device, nodes already in the tree (>= 1: the root).
+ *   Ncap         row length of parents/tokens/src_row, 1..128.
+ *   parents, tokens  int32 [B,Ncap] device, appended to in place.
+ *   src_row      int32 [B,Ncap] device, nullable.
+ *   n_out        int32 [B] device (may not alias n_in).
+ *   dev_status   int32 [B] device, nullable: TTV_E_TREE for a frontier entry
+ *                outside [-1, n_in[b]), TTV_E_SHAPE for n_in[b] < 1 or more
+ *                than Ncap nodes; such a request gets n_out[b] = n_in[b] and
+ *                nothing else written.
+ *   1 <= k <= min(16, V); F <= 128.
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_UNSUPPORTED, TTV_E_LAUNCH.
+ */
+ttv_status ttv_tree_expand(int32_t B, int32_t F, int32_t V, int32_t k,
+                           const float* probs, const int32_t* frontier,
+                           const int32_t* n_in, int32_t Ncap, int32_t* parents,
+                           int32_t* tokens, int32_t* src_row, int32_t* n_out,
+                           int32_t* dev_status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

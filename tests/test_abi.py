@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_attn_workspace_size",
               "ttv_tree_verify", "ttv_tree_verify_workspace_size", "ttv_kv_commit",
-              "ttv_status_string", "ttv_version"):
+              "ttv_tree_expand", "ttv_status_string", "ttv_version"):
         assert n in names
 
 
@@ -158,3 +158,17 @@ def test_binding_checks_tensors_before_calling():
     with pytest.raises(TypeError):
         ttv.tree_verify(ttv.GREEDY, torch.zeros(1, 4, dtype=torch.int64),
                         torch.zeros(1, 4, dtype=torch.int32), torch.zeros(1, 4, 10))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(probs=None), ttv.E_NULL), (dict(fr=None), ttv.E_NULL), (dict(nout=None), ttv.E_NULL),
+    (dict(B=0), ttv.E_SHAPE), (dict(F=0), ttv.E_SHAPE), (dict(k=0), ttv.E_SHAPE),
+    (dict(V=4, k=5), ttv.E_SHAPE), (dict(Ncap=0), ttv.E_SHAPE),
+    (dict(k=17), ttv.E_UNSUPPORTED), (dict(F=129), ttv.E_UNSUPPORTED),
+    (dict(Ncap=129), ttv.E_UNSUPPORTED),
+])
+def test_tree_expand_host_validation(kw, status):
+    args = dict(B=2, F=4, V=100, k=3, probs=A, fr=A, nin=A, Ncap=64, par=A, tok=A, src=None,
+                nout=A, st=None)
+    args.update(kw)
+    assert ttv.lib().ttv_tree_expand(*args.values(), None) == status

@@ -23,7 +23,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["tree_topology", "tree_attn", "tree_verify", "kv_commit",
+__all__ = ["tree_topology", "tree_attn", "tree_verify", "kv_commit", "tree_expand",
            "tree_attn_workspace_size", "tree_verify_workspace_size", "status_string",
            "TTVError", "LibraryNotBuilt", "lib", "LIB_PATH", "GREEDY", "STOCHASTIC"]
 
@@ -72,7 +72,9 @@ def lib():
         L.ttv_tree_verify_workspace_size.restype = _SZ
         L.ttv_kv_commit.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                     _P, _P, _P]
-        for f in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_verify", "ttv_kv_commit"):
+        L.ttv_tree_expand.argtypes = [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
+        for f in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_verify", "ttv_kv_commit",
+                  "ttv_tree_expand"):
             getattr(L, f).restype = _I
         _lib = L
     return _lib
@@ -251,3 +253,31 @@ def kv_commit(k_tree, v_tree, k_cache, v_cache, cache_len_in, path, path_len, Lm
                              _ptr(committed_src), _ptr(dev_status), _stream(dev))
     _check("ttv_kv_commit", st)
     return cache_len_out, committed_src, dev_status
+
+
+def tree_expand(probs, frontier, n_in, k: int, parents, tokens, src_row=None, n_out=None,
+                dev_status=None):
+    """One level of expansion-based tree construction, appended in place to
+    parents/tokens [B,Ncap] (and src_row [B,Ncap] if given): every frontier
+    node's k most probable tokens become its children.  Returns (n_out [B],
+    dev_status [B])."""
+    B, F, V = probs.shape
+    Ncap = parents.shape[1]
+    dev = probs.device
+    _need(probs, "probs", torch.float32, (B, F, V), dev)
+    _need(frontier, "frontier", torch.int32, (B, F), dev)
+    _need(n_in, "n_in", torch.int32, (B,), dev)
+    _need(parents, "parents", torch.int32, (B, Ncap), dev)
+    _need(tokens, "tokens", torch.int32, (B, Ncap), dev)
+    if src_row is not None:
+        _need(src_row, "src_row", torch.int32, (B, Ncap), dev)
+    if n_out is None:
+        n_out = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(n_out, "n_out", torch.int32, (B,), dev)
+    if dev_status is None:
+        dev_status = torch.empty(B, dtype=torch.int32, device=dev)
+    st = lib().ttv_tree_expand(B, F, V, int(k), _ptr(probs), _ptr(frontier), _ptr(n_in), Ncap,
+                               _ptr(parents), _ptr(tokens), _ptr(src_row), _ptr(n_out),
+                               _ptr(dev_status), _stream(dev))
+    _check("ttv_tree_expand", st)
+    return n_out, dev_status

@@ -259,4 +259,19 @@ ttv_status ttv_kv_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv, int32_
                                         static_cast<hipStream_t>(stream)));
 }
 
+ttv_status ttv_tree_expand(int32_t B, int32_t F, int32_t V, int32_t k, const float* probs,
+                           const int32_t* frontier, const int32_t* n_in, int32_t Ncap,
+                           int32_t* parents, int32_t* tokens, int32_t* src_row, int32_t* n_out,
+                           int32_t* dev_status, void* stream) {
+  if (!probs || !frontier || !n_in || !parents || !tokens || !n_out) return TTV_E_NULL;
+  if (B < 1 || F < 1 || V < 1 || Ncap < 1 || k < 1 || k > V) return TTV_E_SHAPE;
+  if (k > kExpandMaxK || F > TTV_MAX_NODES || Ncap > TTV_MAX_NODES || B > kMaxGridYZ)
+    return TTV_E_UNSUPPORTED;
+  // 16-byte loads when every row starts on a 16-byte boundary
+  const bool vec = V % 4 == 0 && aligned16(probs);
+  return launch_status(launch_tree_expand(B, F, V, k, probs, frontier, n_in, Ncap, parents, tokens,
+                                          src_row, n_out, dev_status, vec,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

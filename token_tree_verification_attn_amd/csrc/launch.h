@@ -86,4 +86,12 @@ hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,
                             const int32_t* path_len, int32_t* committed_src,
                             int32_t* dev_status, hipStream_t s);
 
+// ------------------------------------------------------ tree expansion --
+// Largest top-k one expansion call takes (a thread's list lives in registers).
+constexpr int kExpandMaxK = 16;
+hipError_t launch_tree_expand(int B, int F, int V, int k, const float* probs,
+                              const int32_t* frontier, const int32_t* n_in, int Ncap,
+                              int32_t* parents, int32_t* tokens, int32_t* src_row,
+                              int32_t* n_out, int32_t* dev_status, bool vec, hipStream_t s);
+
 }  // namespace ttv
