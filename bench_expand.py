@@ -1,0 +1,132 @@
+"""Throughput of one level of expansion-based token-tree construction
+(ttv_tree_expand) on one GPU.
+
+    python bench_expand.py [--steps K] [--warmup W] [--B 16] [--F 16] [--V 32000] [--k 4]
+
+Workload: B requests, each expanding F frontier nodes by the k most probable
+tokens of their speculator rows of V fp32 probabilities (softmax of N(0,2)
+logits at temperature 0.8, the stochastic workload's recipe).  Inputs are
+resident in HBM and rotated over enough copies to exceed twice the 256 MB
+MALL; the calls are replayed from a HIP graph and timed with HIP events on
+the launch stream.  One JSON line: value = frontier rows expanded per second;
+roofline = the rows' bytes (B*F*V*4, each read once) per call over the call's
+average duration, against the 8 TB/s HBM peak; cpu_baseline = the oracle on a
+bounded sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402  (timing and graph helpers)
+import token_tree_verification_attn_amd as ttv  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+
+
+def make_probs(B, F, V, seed=1005):
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 11]))
+    z = rng.normal(0.0, 2.0, (B, F, V)) / 0.8
+    e = np.exp(z - z.max(-1, keepdims=True))
+    return (e / e.sum(-1, keepdims=True)).astype(np.float32)
+
+
+def cpu_baseline(probs, k, budget_s):
+    """The oracle on whole requests until the budget is spent; rows/s."""
+    import oracle
+    B, F, V = probs.shape
+    frontier = np.arange(F, dtype=np.int32)[None, :]
+    par = np.full((1, 128), -1, np.int32)
+    tok = np.zeros((1, 128), np.int32)
+    n_in = np.array([F], np.int32)
+    rows, t0 = 0, time.perf_counter()
+    b = 0
+    while True:
+        oracle.tree_expand(probs[b:b + 1], frontier, n_in, k, par, tok)
+        rows += F
+        b = (b + 1) % B
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": rows / el, "unit": "frontier rows/s", "cores": 1, "kind": "oracle",
+            "sample": "%d rows (%d requests of %d rows, V=%d, k=%d) in %.1f s of CPU work"
+                      % (rows, rows // F, F, V, k, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--B", type=int, default=16)
+    ap.add_argument("--F", type=int, default=16)
+    ap.add_argument("--V", type=int, default=32000)
+    ap.add_argument("--k", type=int, default=4)
+    ap.add_argument("--cpu-budget", type=float, default=3.0)
+    args = ap.parse_args()
+    B, F, V, k = args.B, args.F, args.V, args.k
+    assert F + F * k <= 128, "the expanded tree must fit 128 nodes"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    probs = make_probs(B, F, V)
+    per_copy = probs.nbytes
+    ncopies = max(1, min(64, -(-2 * bench.MALL_BYTES // per_copy)))
+    pt = torch.from_numpy(probs).to(dev)
+    copies = [pt] + [pt.clone() for _ in range(ncopies - 1)]
+    frontier = torch.arange(F, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
+    n_in = torch.full((B,), F, dtype=torch.int32, device=dev)
+    parents = torch.full((B, 128), -1, dtype=torch.int32, device=dev)
+    tokens = torch.zeros((B, 128), dtype=torch.int32, device=dev)
+    src = torch.full((B, 128), -1, dtype=torch.int32, device=dev)
+    n_out = torch.empty(B, dtype=torch.int32, device=dev)
+    st = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def call(i):
+        ttv.tree_expand(copies[i % ncopies], frontier, n_in, k, parents, tokens, src_row=src,
+                        n_out=n_out, dev_status=st)
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    g = bench.capture(lambda: [call(i) for i in range(ncopies)], dev)
+    if g is not None:
+        reps = max(1, -(-args.steps // ncopies))
+        steps = reps * ncopies
+        ms = bench.timed(lambda i: g.replay(), reps, stream) / ncopies
+        launch = "hip graph replay"
+    else:
+        steps = args.steps
+        ms = bench.timed(call, steps, stream)
+        launch = "eager"
+    assert int(st.abs().sum()) == 0 and int((n_out != F + F * k).sum()) == 0
+    rows = B * F
+    gbs = rows * V * 4 / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "tree_expand frontier rows/s (one expansion level)", "value": rows / (ms * 1e-3),
+        "unit": "frontier rows/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "expand", "B": B, "F": F, "V": V, "k": k,
+                   "input_copies": ncopies, "launch": launch, "inputs": "rotated, HBM-resident"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tree_expand_kernel", "per_launch_algorithmic": rows * V * 4,
+                     "avg_launch_us": ms * 1e3},
+    }
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(probs, k, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

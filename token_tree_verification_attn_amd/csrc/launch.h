@@ -87,7 +87,7 @@ hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,
                             int32_t* dev_status, hipStream_t s);
 
 // ------------------------------------------------------ tree expansion --
-// Largest top-k one expansion call takes (a thread's list lives in registers).
+// Largest top-k one expansion call takes.
 constexpr int kExpandMaxK = 16;
 hipError_t launch_tree_expand(int B, int F, int V, int k, const float* probs,
                               const int32_t* frontier, const int32_t* n_in, int Ncap,
