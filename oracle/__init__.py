@@ -55,8 +55,9 @@ def _bind(lib):
     lib.orc_verify_mss.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P]
     lib.orc_kv_commit.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
     lib.orc_tree_expand.argtypes = [I, I, I, I, P, P, P, I, P, P, P, P, P]
+    lib.orc_tree_merge.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P]
     for f in (lib.orc_topology, lib.orc_tree_attn_rows, lib.orc_verify_greedy,
-              lib.orc_verify_mss, lib.orc_kv_commit, lib.orc_tree_expand):
+              lib.orc_verify_mss, lib.orc_kv_commit, lib.orc_tree_expand, lib.orc_tree_merge):
         f.restype = None
     return lib
 
@@ -258,4 +259,28 @@ def tree_expand(probs, frontier, n_in, k, parents, tokens, src_row=None):
     _load().orc_tree_expand(B, F, V, int(k), pp, fp, nip, Ncap, par.ctypes.data_as(P),
                             tok.ctypes.data_as(P), src.ctypes.data_as(P),
                             n_out.ctypes.data_as(P), status.ctypes.data_as(P))
+    return par, tok, src, n_out, status
+
+
+def tree_merge(seqs, seq_len, root_tok, Ncap):
+    """[SI] §3 "Merge-based token tree construction": the union of S
+    speculated sequences below the root, each distinct prefix one node,
+    numbered depth by depth in order of the lowest sequence index reaching it.
+
+    seqs int32 [B,S,Ls], seq_len int32 [B,S], root_tok int32 [B] ->
+    (parents, tokens, src int32 [B,Ncap] (-1 past n_out), n_out [B], status [B]).
+    """
+    sq, sp = _c(seqs, np.int32)
+    B, S, Ls = sq.shape
+    ln, lp = _c(seq_len, np.int32)
+    rt, rp = _c(root_tok, np.int32)
+    par = np.full((B, Ncap), -1, np.int32)
+    tok = np.full((B, Ncap), -1, np.int32)
+    src = np.full((B, Ncap), -1, np.int32)
+    n_out = np.empty(B, np.int32)
+    status = np.empty(B, np.int32)
+    P = ctypes.c_void_p
+    _load().orc_tree_merge(B, S, Ls, sp, lp, rp, int(Ncap), par.ctypes.data_as(P),
+                           tok.ctypes.data_as(P), src.ctypes.data_as(P),
+                           n_out.ctypes.data_as(P), status.ctypes.data_as(P))
     return par, tok, src, n_out, status

@@ -412,3 +412,82 @@ void orc_tree_expand(int B, int F, int V, int k, const float* probs, const int32
   }
   free(taken);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Merge-based token-tree construction.  [SI] §3 "Merge-based token tree     */
+/* construction": the outputs of several speculative models are combined    */
+/* into one tree that contains each of their token sequences.  For request b */
+/* the S sequences seqs[b,s,0..len[b,s]-1] hang below the root (node 0,      */
+/* token root_tok[b]); every distinct non-empty prefix becomes one node, a    */
+/* shared prefix once.  Nodes are numbered depth by depth, and within a depth */
+/* in order of the lowest sequence index whose prefix it is (its "leader");   */
+/* src[b,node] = s*Ls + d for leader s and position d (-1 for the root).     */
+/* A length outside [0, Ls] or more than Ncap nodes gives ORC_E_SHAPE (n_out */
+/* = 0, nothing written).  Prefixes are compared token by token.             */
+/* ------------------------------------------------------------------------ */
+static int same_prefix(const int32_t* a, const int32_t* c, int d) {
+  for (int t = 0; t < d; ++t)
+    if (a[t] != c[t]) return 0;
+  return 1;
+}
+
+void orc_tree_merge(int B, int S, int Ls, const int32_t* seqs, const int32_t* seq_len,
+                    const int32_t* root_tok, int Ncap, int32_t* parents, int32_t* tokens,
+                    int32_t* src, int32_t* n_out, int32_t* status) {
+  int32_t* node_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)S * (Ls + 1));
+  for (int b = 0; b < B; ++b) {
+    const int32_t* sq = seqs + (size_t)b * S * Ls;
+    const int32_t* ln = seq_len + (size_t)b * S;
+    int bad = 0, maxlen = 0;
+    for (int s = 0; s < S; ++s) {
+      if (ln[s] < 0 || ln[s] > Ls) bad = 1;
+      else if (ln[s] > maxlen) maxlen = ln[s];
+    }
+    /* count the nodes first: a request that does not fit gets nothing */
+    int n = 1;
+    if (!bad) {
+      for (int d = 1; d <= maxlen; ++d)
+        for (int s = 0; s < S; ++s) {
+          if (ln[s] < d) continue;
+          int leader = 1;
+          for (int t = 0; t < s && leader; ++t)
+            if (ln[t] >= d && same_prefix(sq + (size_t)t * Ls, sq + (size_t)s * Ls, d)) leader = 0;
+          n += leader;
+        }
+    }
+    if (bad || n > Ncap) {
+      n_out[b] = 0;
+      status[b] = ORC_E_SHAPE;
+      continue;
+    }
+    int32_t* pb = parents + (size_t)b * Ncap;
+    int32_t* tb = tokens + (size_t)b * Ncap;
+    int32_t* rb = src + (size_t)b * Ncap;
+    pb[0] = -1;
+    tb[0] = root_tok[b];
+    rb[0] = -1;
+    for (int s = 0; s < S; ++s) node_of[(size_t)s * (Ls + 1)] = 0;
+    int next = 1;
+    for (int d = 1; d <= maxlen; ++d)
+      for (int s = 0; s < S; ++s) {
+        if (ln[s] < d) continue;
+        int lead = s;
+        for (int t = 0; t < s; ++t)
+          if (ln[t] >= d && same_prefix(sq + (size_t)t * Ls, sq + (size_t)s * Ls, d)) {
+            lead = t;
+            break;
+          }
+        if (lead == s) {
+          pb[next] = node_of[(size_t)s * (Ls + 1) + d - 1];
+          tb[next] = sq[(size_t)s * Ls + d - 1];
+          rb[next] = s * Ls + d - 1;
+          node_of[(size_t)s * (Ls + 1) + d] = next++;
+        } else {
+          node_of[(size_t)s * (Ls + 1) + d] = node_of[(size_t)lead * (Ls + 1) + d];
+        }
+      }
+    n_out[b] = next;
+    status[b] = ORC_OK;
+  }
+  free(node_of);
+}

@@ -12,6 +12,7 @@ import oracle
 import test_oracle_attn as A
 import test_oracle_commit as C
 import test_oracle_expand as E
+import test_oracle_merge as MG
 import test_oracle_greedy as G
 import test_oracle_mss as M
 import test_oracle_topology as T
@@ -62,6 +63,15 @@ MUTANTS = [
      E.test_invariants_and_skipped_frontier_entries),
     ("expand_rank_counts_holes", "if (fb[f] < 0) continue;", "if (fb[f] < 0) { pos += k; continue; }",
      E.test_invariants_and_skipped_frontier_entries),
+    ("merge_leader_ignores_length",
+     "if (ln[t] >= d && same_prefix(sq + (size_t)t * Ls, sq + (size_t)s * Ls, d)) {",
+     "if (same_prefix(sq + (size_t)t * Ls, sq + (size_t)s * Ls, d)) {",
+     lambda: [MG.test_brute_force_prefix_sets(s) for s in range(8)]),
+    ("merge_prefix_short_by_one", "for (int t = 0; t < d; ++t)\n    if (a[t] != c[t]) return 0;",
+     "for (int t = 0; t + 1 < d; ++t)\n    if (a[t] != c[t]) return 0;",
+     lambda: [MG.test_brute_force_prefix_sets(s) for s in range(8)]),
+    ("merge_parent_same_depth", "pb[next] = node_of[(size_t)s * (Ls + 1) + d - 1];",
+     "pb[next] = node_of[(size_t)s * (Ls + 1) + (d > 1 ? d - 2 : 0)];", MG.test_hand_example),
     ("commit_off_by_one", "* Lcap + (L + j)) * row;", "* Lcap + (L + j + 1)) * row;",
      C.test_full_chain_acceptance_appends_tree),
     ("commit_length", "cache_len_out[b] = L + n;", "cache_len_out[b] = L + n - 1;",
