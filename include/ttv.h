@@ -280,6 +280,41 @@ ttv_status ttv_tree_expand(int32_t B, int32_t F, int32_t V, int32_t k,
                            int32_t* tokens, int32_t* src_row, int32_t* n_out,
                            int32_t* dev_status, void* stream);
 
+/*
+ * ttv_tree_merge -- merge-based token-tree construction ([SI] §3
+ * "Merge-based token tree construction": the outputs of several speculative
+ * models are combined into one tree that contains each of their token
+ * sequences).  For request b, the S sequences seqs[b,s,0..seq_len[b,s]-1]
+ * hang below the root (node 0, token root_tok[b]); every distinct non-empty
+ * prefix becomes one node, so a prefix the sequences share appears once.
+ * Nodes are numbered depth by depth, and within a depth in order of the
+ * lowest sequence index whose prefix the node is (its leader s), which puts
+ * parents first:
+ *   parents[b,0] = -1, tokens[b,0] = root_tok[b], src[b,0] = -1;
+ *   node n at depth d+1: parents[b,n] = its prefix's node at depth d,
+ *   tokens[b,n] = seqs[b,s,d], src[b,n] = s*Ls + d (the speculator row the
+ *   token came from, for a stochastic verifier);  n_out[b] = node count.
+ * Entries past n_out[b] are untouched.
+ *
+ *   seqs         int32 [B,S,Ls] device (token ids, compared for equality).
+ *   seq_len      int32 [B,S] device, each in [0, Ls].
+ *   root_tok     int32 [B] device.
+ *   Ncap         row length of parents/tokens/src, 1..128.
+ *   parents, tokens  int32 [B,Ncap] device (output).
+ *   src          int32 [B,Ncap] device, nullable.
+ *   n_out        int32 [B] device.
+ *   dev_status   int32 [B] device, nullable: TTV_E_SHAPE for a length
+ *                outside [0, Ls] or more than Ncap nodes; such a request
+ *                gets n_out[b] = 0 and nothing else written.
+ *   S <= 64, Ls <= 128.
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_UNSUPPORTED, TTV_E_LAUNCH.
+ */
+ttv_status ttv_tree_merge(int32_t B, int32_t S, int32_t Ls, const int32_t* seqs,
+                          const int32_t* seq_len, const int32_t* root_tok,
+                          int32_t Ncap, int32_t* parents, int32_t* tokens,
+                          int32_t* src, int32_t* n_out, int32_t* dev_status,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_attn_workspace_size",
               "ttv_tree_verify", "ttv_tree_verify_workspace_size", "ttv_kv_commit",
-              "ttv_tree_expand", "ttv_status_string", "ttv_version"):
+              "ttv_tree_expand", "ttv_tree_merge", "ttv_status_string", "ttv_version"):
         assert n in names
 
 
@@ -172,3 +172,17 @@ def test_tree_expand_host_validation(kw, status):
                 nout=A, st=None)
     args.update(kw)
     assert ttv.lib().ttv_tree_expand(*args.values(), None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seqs=None), ttv.E_NULL), (dict(ln=None), ttv.E_NULL), (dict(root=None), ttv.E_NULL),
+    (dict(par=None), ttv.E_NULL), (dict(B=0), ttv.E_SHAPE), (dict(S=0), ttv.E_SHAPE),
+    (dict(Ls=0), ttv.E_SHAPE), (dict(Ncap=0), ttv.E_SHAPE),
+    (dict(S=65), ttv.E_UNSUPPORTED), (dict(Ls=129), ttv.E_UNSUPPORTED),
+    (dict(Ncap=129), ttv.E_UNSUPPORTED),
+])
+def test_tree_merge_host_validation(kw, status):
+    args = dict(B=2, S=4, Ls=16, seqs=A, ln=A, root=A, Ncap=64, par=A, tok=A, src=None, nout=A,
+                st=None)
+    args.update(kw)
+    assert ttv.lib().ttv_tree_merge(*args.values(), None) == status

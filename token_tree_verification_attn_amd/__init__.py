@@ -23,7 +23,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["tree_topology", "tree_attn", "tree_verify", "kv_commit", "tree_expand",
+__all__ = ["tree_topology", "tree_attn", "tree_verify", "kv_commit", "tree_expand", "tree_merge",
            "tree_attn_workspace_size", "tree_verify_workspace_size", "status_string",
            "TTVError", "LibraryNotBuilt", "lib", "LIB_PATH", "GREEDY", "STOCHASTIC"]
 
@@ -73,8 +73,9 @@ def lib():
         L.ttv_kv_commit.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                                     _P, _P, _P]
         L.ttv_tree_expand.argtypes = [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
+        L.ttv_tree_merge.argtypes = [_I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
         for f in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_verify", "ttv_kv_commit",
-                  "ttv_tree_expand"):
+                  "ttv_tree_expand", "ttv_tree_merge"):
             getattr(L, f).restype = _I
         _lib = L
     return _lib
@@ -281,3 +282,32 @@ def tree_expand(probs, frontier, n_in, k: int, parents, tokens, src_row=None, n_
                                _ptr(dev_status), _stream(dev))
     _check("ttv_tree_expand", st)
     return n_out, dev_status
+
+
+def tree_merge(seqs, seq_len, root_tok, Ncap: int = 128, parents=None, tokens=None, src=None,
+               n_out=None, dev_status=None):
+    """The union of S speculated sequences below each request's root as one
+    token tree.  Returns (parents [B,Ncap], tokens [B,Ncap], src [B,Ncap],
+    n_out [B], dev_status [B]); entries past n_out are as passed in (-1 when
+    allocated here)."""
+    B, S, Ls = seqs.shape
+    dev = seqs.device
+    _need(seqs, "seqs", torch.int32, (B, S, Ls), dev)
+    _need(seq_len, "seq_len", torch.int32, (B, S), dev)
+    _need(root_tok, "root_tok", torch.int32, (B,), dev)
+    out = []
+    for t, name in ((parents, "parents"), (tokens, "tokens"), (src, "src")):
+        if t is None:
+            t = torch.full((B, Ncap), -1, dtype=torch.int32, device=dev)
+        _need(t, name, torch.int32, (B, Ncap), dev)
+        out.append(t)
+    if n_out is None:
+        n_out = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(n_out, "n_out", torch.int32, (B,), dev)
+    if dev_status is None:
+        dev_status = torch.empty(B, dtype=torch.int32, device=dev)
+    st = lib().ttv_tree_merge(B, S, Ls, _ptr(seqs), _ptr(seq_len), _ptr(root_tok), Ncap,
+                              _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(n_out),
+                              _ptr(dev_status), _stream(dev))
+    _check("ttv_tree_merge", st)
+    return out[0], out[1], out[2], n_out, dev_status

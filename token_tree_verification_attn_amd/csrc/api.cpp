@@ -274,4 +274,17 @@ ttv_status ttv_tree_expand(int32_t B, int32_t F, int32_t V, int32_t k, const flo
                                           static_cast<hipStream_t>(stream)));
 }
 
+ttv_status ttv_tree_merge(int32_t B, int32_t S, int32_t Ls, const int32_t* seqs,
+                          const int32_t* seq_len, const int32_t* root_tok, int32_t Ncap,
+                          int32_t* parents, int32_t* tokens, int32_t* src, int32_t* n_out,
+                          int32_t* dev_status, void* stream) {
+  if (!seqs || !seq_len || !root_tok || !parents || !tokens || !n_out) return TTV_E_NULL;
+  if (B < 1 || S < 1 || Ls < 1 || Ncap < 1) return TTV_E_SHAPE;
+  if (S > kMergeMaxSeqs || Ls > kMergeMaxLen || Ncap > TTV_MAX_NODES || B > 2147483647 / 64)
+    return TTV_E_UNSUPPORTED;
+  return launch_status(launch_tree_merge(B, S, Ls, seqs, seq_len, root_tok, Ncap, parents, tokens,
+                                         src, n_out, dev_status,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -94,4 +94,11 @@ hipError_t launch_tree_expand(int B, int F, int V, int k, const float* probs,
                               int32_t* parents, int32_t* tokens, int32_t* src_row,
                               int32_t* n_out, int32_t* dev_status, bool vec, hipStream_t s);
 
+// ------------------------------------------------------------ tree merge --
+constexpr int kMergeMaxSeqs = 64;   // sequences per request: one per lane of a wavefront
+constexpr int kMergeMaxLen = 128;   // tokens per sequence (the tree has at most 128 nodes)
+hipError_t launch_tree_merge(int B, int S, int Ls, const int32_t* seqs, const int32_t* seq_len,
+                             const int32_t* root_tok, int Ncap, int32_t* parents, int32_t* tokens,
+                             int32_t* src, int32_t* n_out, int32_t* dev_status, hipStream_t s);
+
 }  // namespace ttv
