@@ -1,7 +1,9 @@
-"""Throughput of one level of expansion-based token-tree construction
-(ttv_tree_expand) on one GPU.
+"""Throughput of token-tree construction on one GPU: one level of
+expansion-based construction (ttv_tree_expand, the default), or merge-based
+construction (ttv_tree_merge, --op merge).
 
     python bench_expand.py [--steps K] [--warmup W] [--B 16] [--F 16] [--V 32000] [--k 4]
+    python bench_expand.py --op merge [--B 4] [--S 4] [--Ls 16]
 
 Workload: B requests, each expanding F frontier nodes by the k most probable
 tokens of their speculator rows of V fp32 probabilities (softmax of N(0,2)
@@ -63,8 +65,51 @@ def cpu_baseline(probs, k, budget_s):
                       % (rows, rows // F, F, V, k, el)}
 
 
+def bench_merge(args):
+    """Merge of S speculated sequences of Ls tokens per request (each repeats
+    the first 0..3 tokens of the one before, vocabulary 32000): latency per
+    call (the tree is built by one wavefront per request)."""
+    B, S, Ls = args.B, args.S, args.Ls
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rng = np.random.default_rng(np.random.SeedSequence([1004, 12]))
+    seqs = rng.integers(0, 32000, (B, S, Ls)).astype(np.int32)
+    for b in range(B):
+        for s in range(1, S):
+            d = int(rng.integers(0, 4))
+            seqs[b, s, :d] = seqs[b, s - 1, :d]
+    t_seqs = torch.from_numpy(seqs).to(dev)
+    t_len = torch.full((B, S), Ls, dtype=torch.int32, device=dev)
+    t_root = torch.zeros(B, dtype=torch.int32, device=dev)
+    outs = [torch.full((B, 128), -1, dtype=torch.int32, device=dev) for _ in range(3)]
+    n_out = torch.empty(B, dtype=torch.int32, device=dev)
+    st = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def call(i):
+        ttv.tree_merge(t_seqs, t_len, t_root, 128, *outs, n_out=n_out, dev_status=st)
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    g = bench.capture(lambda: [call(i) for i in range(16)], dev)
+    reps = max(1, -(-args.steps // 16))
+    ms = bench.timed(lambda i: g.replay(), reps, stream) / 16
+    assert int(st.abs().sum()) == 0
+    print(json.dumps({
+        "metric": "tree_merge trees/s", "value": B / (ms * 1e-3), "unit": "trees/s", "n_gpus": 1,
+        "steps": reps * 16, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "merge", "B": B, "S": S, "Ls": Ls,
+                   "nodes": n_out.cpu().tolist(), "launch": "hip graph replay"},
+        "roofline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--op", choices=["expand", "merge"], default="expand")
+    ap.add_argument("--S", type=int, default=4)
+    ap.add_argument("--Ls", type=int, default=16)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--B", type=int, default=16)
@@ -73,6 +118,8 @@ def main():
     ap.add_argument("--k", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=3.0)
     args = ap.parse_args()
+    if args.op == "merge":
+        return bench_merge(args)
     B, F, V, k = args.B, args.F, args.V, args.k
     assert F + F * k <= 128, "the expanded tree must fit 128 nodes"
     dev = torch.device("cuda:0")
