@@ -56,8 +56,10 @@ def _bind(lib):
     lib.orc_kv_commit.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
     lib.orc_tree_expand.argtypes = [I, I, I, I, P, P, P, I, P, P, P, P, P]
     lib.orc_tree_merge.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P]
+    lib.orc_probs_from_logits.argtypes = [I, I, ctypes.c_double, I, P, P]
     for f in (lib.orc_topology, lib.orc_tree_attn_rows, lib.orc_verify_greedy,
-              lib.orc_verify_mss, lib.orc_kv_commit, lib.orc_tree_expand, lib.orc_tree_merge):
+              lib.orc_verify_mss, lib.orc_kv_commit, lib.orc_tree_expand, lib.orc_tree_merge,
+              lib.orc_probs_from_logits):
         f.restype = None
     return lib
 
@@ -284,3 +286,16 @@ def tree_merge(seqs, seq_len, root_tok, Ncap):
                            tok.ctypes.data_as(P), src.ctypes.data_as(P),
                            n_out.ctypes.data_as(P), status.ctypes.data_as(P))
     return par, tok, src, n_out, status
+
+
+def probs_from_logits(logits, T=1.0, topk=0):
+    """Next-token probabilities from logits [..., V] at temperature T,
+    restricted to the topk highest logits when topk > 0 (equal logits: the
+    lower token id first); fp64 arithmetic, fp32 result."""
+    z, zp = _c(logits, np.float32)
+    V = z.shape[-1]
+    R = z.size // V
+    out = np.empty_like(z)
+    _load().orc_probs_from_logits(R, V, float(T), int(topk), zp,
+                                  out.ctypes.data_as(ctypes.c_void_p))
+    return out

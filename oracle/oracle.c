@@ -491,3 +491,39 @@ void orc_tree_merge(int B, int S, int Ls, const int32_t* seqs, const int32_t* se
   }
   free(node_of);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Probabilities from logits.  [SI] §4 "Token Verification" takes the LLM's  */
+/* and the speculators' next-token distributions for stochastic decoding;    */
+/* [SSD] §4 samples with top-k (k = 50) at temperature T = 1.  Row r:        */
+/* kept = all tokens, or with topk > 0 the topk highest logits (equal logits: */
+/* the lower token id first); probs[r,v] = exp((z_v - m)/T) / sum over kept   */
+/* of exp((z_u - m)/T) for kept v, 0 otherwise, m = the largest kept logit;   */
+/* in fp64, stored as fp32.                                                   */
+/* ------------------------------------------------------------------------ */
+void orc_probs_from_logits(int R, int V, double T, int topk, const float* logits, float* probs) {
+  unsigned char* kept = (unsigned char*)malloc((size_t)V);
+  for (int r = 0; r < R; ++r) {
+    const float* z = logits + (size_t)r * V;
+    float* p = probs + (size_t)r * V;
+    if (topk > 0 && topk < V) {
+      memset(kept, 0, (size_t)V);
+      for (int j = 0; j < topk; ++j) {
+        int best = -1;
+        for (int v = 0; v < V; ++v)
+          if (!kept[v] && (best < 0 || z[v] > z[best])) best = v;
+        kept[best] = 1;
+      }
+    } else {
+      memset(kept, 1, (size_t)V);
+    }
+    double m = -INFINITY;
+    for (int v = 0; v < V; ++v)
+      if (kept[v] && (double)z[v] > m) m = (double)z[v];
+    double s = 0.0;
+    for (int v = 0; v < V; ++v)
+      if (kept[v]) s += exp(((double)z[v] - m) / T);
+    for (int v = 0; v < V; ++v) p[v] = kept[v] ? (float)(exp(((double)z[v] - m) / T) / s) : 0.0f;
+  }
+  free(kept);
+}

@@ -13,6 +13,7 @@ import test_oracle_attn as A
 import test_oracle_commit as C
 import test_oracle_expand as E
 import test_oracle_merge as MG
+import test_oracle_probs as PR
 import test_oracle_greedy as G
 import test_oracle_mss as M
 import test_oracle_topology as T
@@ -72,6 +73,11 @@ MUTANTS = [
      lambda: [MG.test_brute_force_prefix_sets(s) for s in range(8)]),
     ("merge_parent_same_depth", "pb[next] = node_of[(size_t)s * (Ls + 1) + d - 1];",
      "pb[next] = node_of[(size_t)s * (Ls + 1) + (d > 1 ? d - 2 : 0)];", MG.test_hand_example),
+    ("probs_temperature_dropped", "if (kept[v]) s += exp(((double)z[v] - m) / T);",
+     "if (kept[v]) s += exp(((double)z[v] - m));", lambda: PR.test_matches_scipy_softmax(0.8)),
+    ("probs_topk_ties_to_highest", "if (!kept[v] && (best < 0 || z[v] > z[best])) best = v;",
+     "if (!kept[v] && (best < 0 || z[v] >= z[best])) best = v;",
+     lambda: PR.test_topk_keeps_the_stable_argsort_prefix(5)),
     ("commit_off_by_one", "* Lcap + (L + j)) * row;", "* Lcap + (L + j + 1)) * row;",
      C.test_full_chain_acceptance_appends_tree),
     ("commit_length", "cache_len_out[b] = L + n;", "cache_len_out[b] = L + n - 1;",
