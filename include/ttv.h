@@ -315,6 +315,31 @@ ttv_status ttv_tree_merge(int32_t B, int32_t S, int32_t Ls, const int32_t* seqs,
                           int32_t* src, int32_t* n_out, int32_t* dev_status,
                           void* stream);
 
+/*
+ * ttv_probs_from_logits -- next-token probabilities from logits at a
+ * temperature, optionally over the top-k logits only ([SI] §4 "Token
+ * Verification": the stochastic verifier takes the LLM's and the
+ * speculators' next-token distributions; [SSD] §4 samples with top-k, k = 50,
+ * at T = 1).  For each of the R rows of V logits z:
+ *   kept = every token, or with 0 < topk < V the topk highest logits (equal
+ *          logits: the lower token id first);
+ *   probs[r,v] = exp((z_v - m)/T) / sum over kept u of exp((z_u - m)/T) for
+ *          kept v, 0 otherwise; m = the row maximum.
+ * fp32 arithmetic (exp as 2^(x log2 e)); each row is read once from HBM and
+ * written once.
+ *
+ *   R            rows (e.g. B*N for [B,N,V] logits).
+ *   logits       float32 [R,V] device, finite.
+ *   probs        float32 [R,V] device (may not alias logits).
+ *   temperature  finite, > 0 (TTV_E_SHAPE otherwise).
+ *   topk         0 (or >= V): every token; 1..512: the topk highest;
+ *                larger values below V give TTV_E_UNSUPPORTED.
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_UNSUPPORTED, TTV_E_LAUNCH.
+ */
+ttv_status ttv_probs_from_logits(int32_t R, int32_t V, float temperature,
+                                 int32_t topk, const float* logits, float* probs,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

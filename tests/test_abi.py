@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_attn_workspace_size",
               "ttv_tree_verify", "ttv_tree_verify_workspace_size", "ttv_kv_commit",
-              "ttv_tree_expand", "ttv_tree_merge", "ttv_status_string", "ttv_version"):
+              "ttv_tree_expand", "ttv_tree_merge", "ttv_probs_from_logits", "ttv_status_string", "ttv_version"):
         assert n in names
 
 
@@ -186,3 +186,15 @@ def test_tree_merge_host_validation(kw, status):
                 st=None)
     args.update(kw)
     assert ttv.lib().ttv_tree_merge(*args.values(), None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(z=None), ttv.E_NULL), (dict(p=None), ttv.E_NULL), (dict(R=0), ttv.E_SHAPE),
+    (dict(V=0), ttv.E_SHAPE), (dict(T=0.0), ttv.E_SHAPE), (dict(T=float("inf")), ttv.E_SHAPE),
+    (dict(T=float("nan")), ttv.E_SHAPE), (dict(k=-1), ttv.E_SHAPE),
+    (dict(k=513), ttv.E_UNSUPPORTED),
+])
+def test_probs_from_logits_host_validation(kw, status):
+    args = dict(R=4, V=1000, T=0.8, k=50, z=A, p=A)
+    args.update(kw)
+    assert ttv.lib().ttv_probs_from_logits(*args.values(), None) == status

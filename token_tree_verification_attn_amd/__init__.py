@@ -23,7 +23,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["tree_topology", "tree_attn", "tree_verify", "kv_commit", "tree_expand", "tree_merge",
+__all__ = ["tree_topology", "tree_attn", "tree_verify", "kv_commit", "tree_expand", "tree_merge", "probs_from_logits",
            "tree_attn_workspace_size", "tree_verify_workspace_size", "status_string",
            "TTVError", "LibraryNotBuilt", "lib", "LIB_PATH", "GREEDY", "STOCHASTIC"]
 
@@ -74,8 +74,9 @@ def lib():
                                     _P, _P, _P]
         L.ttv_tree_expand.argtypes = [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
         L.ttv_tree_merge.argtypes = [_I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
+        L.ttv_probs_from_logits.argtypes = [_I, _I, _F, _I, _P, _P, _P]
         for f in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_verify", "ttv_kv_commit",
-                  "ttv_tree_expand", "ttv_tree_merge"):
+                  "ttv_tree_expand", "ttv_tree_merge", "ttv_probs_from_logits"):
             getattr(L, f).restype = _I
         _lib = L
     return _lib
@@ -311,3 +312,19 @@ def tree_merge(seqs, seq_len, root_tok, Ncap: int = 128, parents=None, tokens=No
                               _ptr(dev_status), _stream(dev))
     _check("ttv_tree_merge", st)
     return out[0], out[1], out[2], n_out, dev_status
+
+
+def probs_from_logits(logits, temperature: float = 1.0, topk: int = 0, out=None):
+    """Probabilities over the last axis of fp32 logits [..., V] at a
+    temperature, restricted to the topk highest logits when topk > 0."""
+    V = logits.shape[-1]
+    R = logits.numel() // V
+    dev = logits.device
+    _need(logits, "logits", torch.float32, tuple(logits.shape), dev)
+    if out is None:
+        out = torch.empty_like(logits)
+    _need(out, "out", torch.float32, tuple(logits.shape), dev)
+    st = lib().ttv_probs_from_logits(R, V, float(temperature), int(topk), _ptr(logits),
+                                     _ptr(out), _stream(dev))
+    _check("ttv_probs_from_logits", st)
+    return out

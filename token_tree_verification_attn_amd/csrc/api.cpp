@@ -287,4 +287,15 @@ ttv_status ttv_tree_merge(int32_t B, int32_t S, int32_t Ls, const int32_t* seqs,
                                          static_cast<hipStream_t>(stream)));
 }
 
+ttv_status ttv_probs_from_logits(int32_t R, int32_t V, float temperature, int32_t topk,
+                                 const float* logits, float* probs, void* stream) {
+  if (!logits || !probs) return TTV_E_NULL;
+  if (R < 1 || V < 1 || topk < 0 || !std::isfinite(temperature) || !(temperature > 0.f))
+    return TTV_E_SHAPE;
+  if (topk > kProbsMaxTopk && topk < V) return TTV_E_UNSUPPORTED;
+  const bool vec = V % 4 == 0 && aligned16(logits) && aligned16(probs);
+  return launch_status(launch_probs(R, V, temperature, topk, logits, probs, vec,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

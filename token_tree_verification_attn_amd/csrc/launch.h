@@ -101,4 +101,9 @@ hipError_t launch_tree_merge(int B, int S, int Ls, const int32_t* seqs, const in
                              const int32_t* root_tok, int Ncap, int32_t* parents, int32_t* tokens,
                              int32_t* src, int32_t* n_out, int32_t* dev_status, hipStream_t s);
 
+// --------------------------------------------------------- probabilities --
+constexpr int kProbsMaxTopk = 512;  // the top-k bound comes from 512 per-thread maxima
+hipError_t launch_probs(int R, int V, float T, int topk, const float* logits, float* probs,
+                        bool vec, hipStream_t s);
+
 }  // namespace ttv
