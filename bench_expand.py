@@ -4,6 +4,7 @@ construction (ttv_tree_merge, --op merge).
 
     python bench_expand.py [--steps K] [--warmup W] [--B 16] [--F 16] [--V 32000] [--k 4]
     python bench_expand.py --op merge [--B 4] [--S 4] [--Ls 16]
+    python bench_expand.py --op probs [--B 16] [--F 64] [--V 32000] [--k 0] [--T 0.8]
 
 Workload: B requests, each expanding F frontier nodes by the k most probable
 tokens of their speculator rows of V fp32 probabilities (softmax of N(0,2)
@@ -105,9 +106,49 @@ def bench_merge(args):
         "roofline": None}), flush=True)
 
 
+def bench_probs(args):
+    """Probabilities from logits for B*F rows of V logits (N(0,2), the
+    stochastic workload's recipe) at temperature T, top-k k (0: all tokens);
+    each row read once and written once: 8V bytes per row."""
+    B, F, V = args.B, args.F, args.V
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rng = np.random.default_rng(np.random.SeedSequence([1005, 13]))
+    z = torch.from_numpy(rng.normal(0.0, 2.0, (B * F, V)).astype(np.float32)).to(dev)
+    per_copy = 2 * z.numel() * 4
+    ncopies = max(1, min(64, -(-2 * bench.MALL_BYTES // per_copy)))
+    ins = [z] + [z.clone() for _ in range(ncopies - 1)]
+    outs = [torch.empty_like(z) for _ in range(ncopies)]
+
+    def call(i):
+        ttv.probs_from_logits(ins[i % ncopies], args.T, args.k, out=outs[i % ncopies])
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    g = bench.capture(lambda: [call(i) for i in range(ncopies)], dev)
+    reps = max(1, -(-args.steps // ncopies))
+    ms = bench.timed(lambda i: g.replay(), reps, stream) / ncopies
+    nbytes = B * F * V * 8
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "probs_from_logits rows/s", "value": B * F / (ms * 1e-3), "unit": "rows/s",
+        "n_gpus": 1, "steps": reps * ncopies, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "probs", "rows": B * F, "V": V, "T": args.T, "topk": args.k,
+                   "input_copies": ncopies, "launch": "hip graph replay",
+                   "inputs": "rotated, HBM-resident"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "probs_kernel",
+                     "per_launch_algorithmic": nbytes, "avg_launch_us": ms * 1e3}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--op", choices=["expand", "merge"], default="expand")
+    ap.add_argument("--op", choices=["expand", "merge", "probs"], default="expand")
+    ap.add_argument("--T", type=float, default=0.8)
     ap.add_argument("--S", type=int, default=4)
     ap.add_argument("--Ls", type=int, default=16)
     ap.add_argument("--steps", type=int, default=400)
@@ -120,6 +161,8 @@ def main():
     args = ap.parse_args()
     if args.op == "merge":
         return bench_merge(args)
+    if args.op == "probs":
+        return bench_probs(args)
     B, F, V, k = args.B, args.F, args.V, args.k
     assert F + F * k <= 128, "the expanded tree must fit 128 nodes"
     dev = torch.device("cuda:0")

@@ -6,11 +6,14 @@
 // One 512-thread workgroup per row.  A row of up to 32768 logits is requested
 // whole (16 16-byte loads per thread) and kept in registers; a longer one is
 // streamed, once per pass.  With top-k, the k-th entry of the row in the
-// order (higher logit, then lower token id) is found as in tree expansion: the
-// k-th largest of the 512 per-thread maxima bounds it from below, the entries
-// at or above that bound are gathered in LDS, and k rounds of a wave arg-max,
-// each over the entries ranking after the previous winner, give it; an entry
-// is kept iff it ranks at or before it.  Then m = the row maximum (always
+// order (higher logit, then lower token id) is found much as in tree
+// expansion: the smallest over the 8 waves of each wave's ceil(k/8)-th
+// largest per-thread maximum bounds it from below, the entries at or above
+// that bound are gathered in LDS, and the one that exactly k-1
+// gathered entries rank before is it (each thread counts for its own
+// candidates; a row whose ties overflow the buffer takes k rounds of a
+// block arg-max over the whole row instead); an entry is kept iff it ranks at
+// or before it.  Then m = the row maximum (always
 // kept), s = the sum over kept entries of 2^((z - m) * log2(e) / T), and
 // probs = 2^((z - m) * log2(e) / T) / s for kept entries, 0 for the others.
 // The row is read once from HBM and written once.
@@ -51,7 +54,6 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
                                                              const float* __restrict__ logits,
                                                              float* __restrict__ probs) {
   __shared__ float s_red[kProbWaves];
-  __shared__ float s_max[kProbThreads];
   __shared__ float s_cv[kProbCandidates];
   __shared__ int s_ci[kProbCandidates];
   __shared__ float s_wv[kProbWaves];
@@ -126,37 +128,30 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
   float kv = -INFINITY;
   int ki = INT_MAX;
   if (topk > 0 && topk < V) {
-    s_max[tid] = tmax;
+    // a lower bound of the k-th entry: every wave takes the ceil(k/8)-th
+    // largest of its 64 per-thread maxima, and the smallest of those has at
+    // least 8*ceil(k/8) >= k entries of the row at or above it
     if (tid == 0) s_cnt = 0;
-    __syncthreads();
-    if (wave == 0) {
-      constexpr int PER = kProbThreads / 64;
-      float a[PER];
-#pragma unroll
-      for (int j = 0; j < PER; ++j) a[j] = s_max[j * 64 + lane];
-      float thr = -INFINITY;
-      for (int r = 0; r < topk; ++r) {  // the topk-th largest per-thread maximum
-        float lm = a[0];
-#pragma unroll
-        for (int j = 1; j < PER; ++j) lm = fmaxf(lm, a[j]);
-        float wm = lm;
+    {
+      const int kw = (topk + kProbWaves - 1) / kProbWaves;
+      float a = tmax, wm = -INFINITY;
+      for (int r = 0; r < kw; ++r) {  // remove one copy of the wave's largest per round
+        wm = a;
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1) wm = fmaxf(wm, __shfl_xor(wm, s));
-        const uint64_t has = __ballot(lm == wm);
-        if (lane == __ffsll((unsigned long long)has) - 1) {
-          bool done = false;
-#pragma unroll
-          for (int j = 0; j < PER; ++j)
-            if (!done && a[j] == wm) {
-              a[j] = -INFINITY;
-              done = true;
-            }
-        }
-        thr = wm;
+        const uint64_t has = __ballot(a == wm);
+        if (lane == __ffsll((unsigned long long)has) - 1) a = -INFINITY;
       }
-      if (lane == 0) s_thr = thr;
+      if (lane == 0) s_red[wave] = wm;
+      __syncthreads();
+      if (tid == 0) {
+        float t = s_red[0];
+#pragma unroll
+        for (int w = 1; w < kProbWaves; ++w) t = fminf(t, s_red[w]);
+        s_thr = t;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     const float thr = s_thr;
     visit_row([&](float z, int i) {
       if (z >= thr) {
@@ -169,48 +164,57 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
     });
     __syncthreads();
     const int cnt = s_cnt;
-    float pv = INFINITY;
-    int pi = -1;
-    for (int j = 0; j < topk; ++j) {  // k rounds, each the best after the previous winner
-      float bv = -INFINITY;
-      int bi = INT_MAX;
-      if (cnt <= kProbCandidates) {
-        for (int q = tid; q < cnt; q += kProbThreads) {
-          const float z = s_cv[q];
-          const int i = s_ci[q];
-          if (p_ranks_before(pv, pi, z, i) && p_ranks_before(z, i, bv, bi)) {
-            bv = z;
-            bi = i;
-          }
+    if (cnt <= kProbCandidates) {
+      // the gathered pairs are distinct (distinct ids), so their ranks are
+      // 0..cnt-1 and exactly one candidate has rank topk-1 (cnt >= topk)
+      for (int q = tid; q < cnt; q += kProbThreads) {
+        const float z = s_cv[q];
+        const int i = s_ci[q];
+        int rank = 0;
+        for (int u = 0; u < cnt; ++u) rank += p_ranks_before(s_cv[u], s_ci[u], z, i) ? 1 : 0;
+        if (rank == topk - 1) {
+          s_wv[0] = z;
+          s_wi[0] = i;
         }
-      } else {  // too many ties for the buffer: the whole row
+      }
+      __syncthreads();
+      kv = s_wv[0];
+      ki = s_wi[0];
+    } else {
+      // too many ties for the buffer: topk rounds over the whole row, each
+      // the best entry ranking after the previous winner
+      float pv = INFINITY;
+      int pi = -1;
+      for (int j = 0; j < topk; ++j) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
         visit_row([&](float z, int i) {
           if (p_ranks_before(pv, pi, z, i) && p_ranks_before(z, i, bv, bi)) {
             bv = z;
             bi = i;
           }
         });
-      }
-      p_wave_argmax(bv, bi);
-      if (lane == 0) {
-        s_wv[wave] = bv;
-        s_wi[wave] = bi;
-      }
-      __syncthreads();
-      bv = s_wv[0];
-      bi = s_wi[0];
-#pragma unroll
-      for (int w = 1; w < kProbWaves; ++w)
-        if (p_ranks_before(s_wv[w], s_wi[w], bv, bi)) {
-          bv = s_wv[w];
-          bi = s_wi[w];
+        p_wave_argmax(bv, bi);
+        if (lane == 0) {
+          s_wv[wave] = bv;
+          s_wi[wave] = bi;
         }
-      __syncthreads();
-      pv = bv;
-      pi = bi;
+        __syncthreads();
+        bv = s_wv[0];
+        bi = s_wi[0];
+#pragma unroll
+        for (int w = 1; w < kProbWaves; ++w)
+          if (p_ranks_before(s_wv[w], s_wi[w], bv, bi)) {
+            bv = s_wv[w];
+            bi = s_wi[w];
+          }
+        __syncthreads();
+        pv = bv;
+        pi = bi;
+      }
+      kv = pv;
+      ki = pi;
     }
-    kv = pv;
-    ki = pi;
   }
   auto kept = [&](float z, int i) { return z > kv || (z == kv && i <= ki); };
 
