@@ -57,7 +57,8 @@ def _bind(lib):
     lib.orc_tree_expand.argtypes = [I, I, I, I, P, P, P, I, P, P, P, P, P]
     lib.orc_tree_merge.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P]
     lib.orc_probs_from_logits.argtypes = [I, I, ctypes.c_double, I, P, P]
-    for f in (lib.orc_topology, lib.orc_tree_attn_rows, lib.orc_verify_greedy,
+    lib.orc_kv_commit_inplace.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]
+    for f in (lib.orc_kv_commit_inplace, lib.orc_topology, lib.orc_tree_attn_rows, lib.orc_verify_greedy,
               lib.orc_verify_mss, lib.orc_kv_commit, lib.orc_tree_expand, lib.orc_tree_merge,
               lib.orc_probs_from_logits):
         f.restype = None
@@ -299,3 +300,28 @@ def probs_from_logits(logits, T=1.0, topk=0):
     _load().orc_probs_from_logits(R, V, float(T), int(topk), zp,
                                   out.ctypes.data_as(ctypes.c_void_p))
     return out
+
+
+def kv_commit_inplace(k_cache, v_cache, cache_len_in, path, path_len, Lmax, N):
+    """[SI] §4 "Tree-Based Parallel Decoding" with the tree inside the cache:
+    node i at row L + i; row L + j takes the old row L + path[j] (j < n).
+
+    Works on copies of k_cache/v_cache [B,Hkv,Lcap,D] (bytes are copied).
+    Returns (k_cache', v_cache', cache_len_out, committed_src, status).
+    """
+    kc = np.array(k_cache, copy=True, order="C")
+    vc = np.array(v_cache, copy=True, order="C")
+    assert kc.dtype == vc.dtype
+    B, Hkv, Lcap, D = kc.shape
+    cl, clp = _c(cache_len_in, np.int32)
+    pa, pap = _c(path, np.int32)
+    pl, plp = _c(path_len, np.int32)
+    clo = np.empty(B, np.int32)
+    src = np.empty((B, N), np.int32)
+    st = np.empty(B, np.int32)
+    V = ctypes.c_void_p
+    _load().orc_kv_commit_inplace(B, N, Hkv, D, kc.dtype.itemsize, Lcap, int(Lmax),
+                                  kc.ctypes.data_as(V), vc.ctypes.data_as(V), clp,
+                                  clo.ctypes.data_as(V), pap, plp, src.ctypes.data_as(V),
+                                  st.ctypes.data_as(V))
+    return kc, vc, clo, src, st

@@ -527,3 +527,52 @@ void orc_probs_from_logits(int R, int V, double T, int topk, const float* logits
   }
   free(kept);
 }
+
+/* ------------------------------------------------------------------------ */
+/* KV commit with the tree inside the cache.  [SI] §4 "Tree-Based Parallel  */
+/* Decoding": verified and speculated tokens are stored together in one      */
+/* key-value cache.  Here tree node i's K/V sit at cache row L + i (L =      */
+/* cache_len_in[b]); committing keeps the accepted path: row L + j takes the */
+/* old row L + path[b,j] for j < n = path_len[b] (the n source rows are all  */
+/* taken before any is written), cache_len_out[b] = L + n, committed_src as  */
+/* in orc_kv_commit.  A bad length or path entry (as there, with the tree    */
+/* rows L .. L+N-1 inside the cache) gives ORC_E_SHAPE and nothing written.  */
+/* ------------------------------------------------------------------------ */
+void orc_kv_commit_inplace(int B, int N, int Hkv, int D, int elt, int Lcap, int Lmax,
+                           void* k_cache, void* v_cache, const int32_t* cache_len_in,
+                           int32_t* cache_len_out, const int32_t* path,
+                           const int32_t* path_len, int32_t* committed_src, int32_t* status) {
+  const size_t row = (size_t)D * elt;
+  char* tk = (char*)malloc(row * (size_t)(N > 0 ? N : 1));
+  char* tv = (char*)malloc(row * (size_t)(N > 0 ? N : 1));
+  for (int b = 0; b < B; ++b) {
+    const int L = cache_len_in[b];
+    const int n = path_len[b];
+    const int32_t* pb = path + (size_t)b * N;
+    int ok = L >= 0 && L <= Lmax && n >= 0 && n <= N && (long)L + N <= Lcap;
+    for (int j = 0; ok && j < n; ++j)
+      if (pb[j] < 0 || pb[j] >= N) ok = 0;
+    for (int j = 0; j < N; ++j)
+      committed_src[(size_t)b * N + j] = (ok && j < n) ? pb[j] : -1;
+    if (!ok) {
+      cache_len_out[b] = L;
+      status[b] = ORC_E_SHAPE;
+      continue;
+    }
+    for (int h = 0; h < Hkv; ++h) {
+      const size_t base = ((size_t)b * Hkv + h) * Lcap;
+      for (int j = 0; j < n; ++j) {  /* take the sources ... */
+        memcpy(tk + (size_t)j * row, (const char*)k_cache + (base + L + pb[j]) * row, row);
+        memcpy(tv + (size_t)j * row, (const char*)v_cache + (base + L + pb[j]) * row, row);
+      }
+      for (int j = 0; j < n; ++j) {  /* ... then write them */
+        memcpy((char*)k_cache + (base + L + j) * row, tk + (size_t)j * row, row);
+        memcpy((char*)v_cache + (base + L + j) * row, tv + (size_t)j * row, row);
+      }
+    }
+    cache_len_out[b] = n + L;
+    status[b] = ORC_OK;
+  }
+  free(tk);
+  free(tv);
+}

@@ -11,6 +11,7 @@ import pytest
 import oracle
 import test_oracle_attn as A
 import test_oracle_commit as C
+import test_oracle_commit_inplace as CI
 import test_oracle_expand as E
 import test_oracle_merge as MG
 import test_oracle_probs as PR
@@ -78,6 +79,10 @@ MUTANTS = [
     ("probs_topk_ties_to_highest", "if (!kept[v] && (best < 0 || z[v] > z[best])) best = v;",
      "if (!kept[v] && (best < 0 || z[v] >= z[best])) best = v;",
      lambda: PR.test_topk_keeps_the_stable_argsort_prefix(5)),
+    ("commit_inplace_source_without_length",
+     "memcpy(tk + (size_t)j * row, (const char*)k_cache + (base + L + pb[j]) * row, row);",
+     "memcpy(tk + (size_t)j * row, (const char*)k_cache + (base + pb[j]) * row, row);",
+     lambda: [CI.test_equals_separate_tree_commit(s) for s in range(6)]),
     ("commit_off_by_one", "* Lcap + (L + j)) * row;", "* Lcap + (L + j + 1)) * row;",
      C.test_full_chain_acceptance_appends_tree),
     ("commit_length", "cache_len_out[b] = L + n;", "cache_len_out[b] = L + n - 1;",
