@@ -112,7 +112,12 @@ ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents,
  *   Lmax        host promise: max_b L_b (sizes the launch); requires
  *               0 <= Lmax <= Lcap.  A request with L_b < 0 or L_b > Lmax is
  *               reported as TTV_E_SHAPE in dev_status and gets zero output.
- *   k_tree,v_tree [B,Hkv,N,D]  keys/values of the tree nodes themselves.
+ *   k_tree,v_tree [B,Hkv,N,D]  keys/values of the tree nodes themselves;
+ *               or both NULL: the tree's K/V are stored in the cache after
+ *               the prefix ([SI] §4: verified and speculated tokens share one
+ *               cache), node i at row L_b + i (row min(max(L_b,0),Lmax) + i
+ *               for a rejected length), which requires Lmax + N <= Lcap
+ *               (TTV_E_SHAPE otherwise).  One NULL alone is TTV_E_NULL.
  *   parents     int32 [B,N]  tree of each request (see conventions).
  *   out         [B,N,Hq,D]  attention output, type dt (bf16 rounded to
  *               nearest even from fp32).  A request with a malformed tree gets
@@ -338,6 +343,38 @@ ttv_status ttv_tree_merge(int32_t B, int32_t S, int32_t Ls, const int32_t* seqs,
  */
 ttv_status ttv_probs_from_logits(int32_t R, int32_t V, float temperature,
                                  int32_t topk, const float* logits, float* probs,
+                                 void* stream);
+
+/*
+ * ttv_kv_commit_inplace -- ttv_kv_commit for a tree stored inside the cache
+ * ([SI] §4 "Tree-Based Parallel Decoding": verified and speculated tokens
+ * share one key-value cache; only the accepted ones stay).  Tree node i's K/V
+ * are at row L + i (L = cache_len_in[b], the layout ttv_tree_attn reads with
+ * NULL tree pointers); for n = path_len[b]:
+ *   k_cache[b,h,L+j,:] = old k_cache[b,h,L+path[b,j],:] (same for v), j < n,
+ *   all h (every source row is read before any destination is written);
+ *   cache_len_out[b] = L + n;  committed_src[b,j] = path[b,j] (j < n), -1 after.
+ * Copies are bit-exact.  Rows L+n .. L+N-1 keep stale tree rows; rows outside
+ * [L, L+N) and other requests are untouched.
+ *
+ *   dt           element type (only its size matters).
+ *   k_cache,v_cache [B,Hkv,Lcap,D] device, updated in place.
+ *   cache_len_in, cache_len_out int32 [B] (may be the same array).
+ *   Lmax         host promise max_b L_b; requires Lmax + N <= Lcap.
+ *   path, path_len  as written by ttv_tree_verify (device, no host copy).
+ *   committed_src int32 [B,N], nullable.
+ *   dev_status   nullable; TTV_E_SHAPE when L < 0, L > Lmax, n outside
+ *                [0,N] or a path entry outside [0,N): nothing of that request
+ *                is written except cache_len_out[b] = L (and -1 sources).
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE, TTV_E_UNSUPPORTED,
+ *         TTV_E_ALIGN, TTV_E_LAUNCH.
+ */
+ttv_status ttv_kv_commit_inplace(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv,
+                                 int32_t D, int32_t Lcap, void* k_cache,
+                                 void* v_cache, const int32_t* cache_len_in,
+                                 int32_t* cache_len_out, int32_t Lmax,
+                                 const int32_t* path, const int32_t* path_len,
+                                 int32_t* committed_src, int32_t* dev_status,
                                  void* stream);
 
 #ifdef __cplusplus

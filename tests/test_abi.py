@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_attn_workspace_size",
               "ttv_tree_verify", "ttv_tree_verify_workspace_size", "ttv_kv_commit",
-              "ttv_tree_expand", "ttv_tree_merge", "ttv_probs_from_logits", "ttv_status_string", "ttv_version"):
+              "ttv_tree_expand", "ttv_tree_merge", "ttv_probs_from_logits", "ttv_kv_commit_inplace", "ttv_status_string",
+              "ttv_version"):
         assert n in names
 
 
@@ -75,6 +76,8 @@ def attn(**kw):
     (dict(ck=100), ttv.E_UNSUPPORTED), (dict(dt=0, rpb=64), ttv.E_UNSUPPORTED),
     (dict(q=MIS), ttv.E_ALIGN), (dict(vt=MIS), ttv.E_ALIGN), (dict(out=MIS), ttv.E_ALIGN),
     (dict(ws=None, ck=64), ttv.E_WORKSPACE), (dict(wsb=16, ck=64), ttv.E_WORKSPACE),
+    (dict(kt=None), ttv.E_NULL), (dict(vt=None), ttv.E_NULL),
+    (dict(kt=None, vt=None, Lmax=125), ttv.E_SHAPE),   # tree in the cache: Lmax + N > Lcap
 ])
 def test_tree_attn_host_validation(kw, status):
     assert attn(**kw) == status
@@ -198,3 +201,16 @@ def test_probs_from_logits_host_validation(kw, status):
     args = dict(R=4, V=1000, T=0.8, k=50, z=A, p=A)
     args.update(kw)
     assert ttv.lib().ttv_probs_from_logits(*args.values(), None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), ttv.E_DTYPE), (dict(kc=None), ttv.E_NULL), (dict(clo=None), ttv.E_NULL),
+    (dict(path=None), ttv.E_NULL), (dict(B=0), ttv.E_SHAPE), (dict(Lmax=93), ttv.E_SHAPE),
+    (dict(Lcap=-1), ttv.E_SHAPE), (dict(N=129, Lcap=1000), ttv.E_UNSUPPORTED),
+    (dict(D=32), ttv.E_UNSUPPORTED), (dict(kc=MIS), ttv.E_ALIGN),
+])
+def test_kv_commit_inplace_host_validation(kw, status):
+    args = dict(dt=1, B=2, N=8, Hkv=2, D=64, Lcap=100, kc=A, vc=A, cli=A, clo=A, Lmax=50,
+                path=A, plen=A, src=None, st=None)
+    args.update(kw)
+    assert ttv.lib().ttv_kv_commit_inplace(*args.values(), None) == status

@@ -23,7 +23,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["tree_topology", "tree_attn", "tree_verify", "kv_commit", "tree_expand", "tree_merge", "probs_from_logits",
+__all__ = ["tree_topology", "tree_attn", "tree_verify", "kv_commit", "tree_expand", "tree_merge", "probs_from_logits", "kv_commit_inplace",
            "tree_attn_workspace_size", "tree_verify_workspace_size", "status_string",
            "TTVError", "LibraryNotBuilt", "lib", "LIB_PATH", "GREEDY", "STOCHASTIC"]
 
@@ -75,7 +75,9 @@ def lib():
         L.ttv_tree_expand.argtypes = [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
         L.ttv_tree_merge.argtypes = [_I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
         L.ttv_probs_from_logits.argtypes = [_I, _I, _F, _I, _P, _P, _P]
-        for f in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_verify", "ttv_kv_commit",
+        L.ttv_kv_commit_inplace.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P,
+                                            _P, _P, _P]
+        for f in ("ttv_kv_commit_inplace", "ttv_tree_topology", "ttv_tree_attn", "ttv_tree_verify", "ttv_kv_commit",
                   "ttv_tree_expand", "ttv_tree_merge", "ttv_probs_from_logits"):
             getattr(L, f).restype = _I
         _lib = L
@@ -149,7 +151,8 @@ def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int
               scale: Optional[float] = None, out=None, lse=None, want_lse: bool = True,
               dev_status=None, workspace=None, rows_per_block: int = 0, chunk_keys: int = 0):
     """Tree attention for every node; returns (out [B,N,Hq,D], lse [B,N,Hq] or None,
-    dev_status [B])."""
+    dev_status [B]).  k_tree = v_tree = None reads node i's K/V from cache row
+    L_b + i."""
     B, N, Hq, D = q.shape
     Hkv, Lcap = k_cache.shape[1], k_cache.shape[2]
     dev = q.device
@@ -157,8 +160,9 @@ def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int
     _need(q, "q", dt, (B, N, Hq, D), dev)
     _need(k_cache, "k_cache", dt, (B, Hkv, Lcap, D), dev)
     _need(v_cache, "v_cache", dt, (B, Hkv, Lcap, D), dev)
-    _need(k_tree, "k_tree", dt, (B, Hkv, N, D), dev)
-    _need(v_tree, "v_tree", dt, (B, Hkv, N, D), dev)
+    if k_tree is not None or v_tree is not None:  # both None: tree K/V at cache rows L_b + i
+        _need(k_tree, "k_tree", dt, (B, Hkv, N, D), dev)
+        _need(v_tree, "v_tree", dt, (B, Hkv, N, D), dev)
     _need(cache_len, "cache_len", torch.int32, (B,), dev)
     _need(parents, "parents", torch.int32, (B, N), dev)
     if scale is None:
@@ -328,3 +332,32 @@ def probs_from_logits(logits, temperature: float = 1.0, topk: int = 0, out=None)
                                      _ptr(out), _stream(dev))
     _check("ttv_probs_from_logits", st)
     return out
+
+
+def kv_commit_inplace(k_cache, v_cache, cache_len_in, path, path_len, Lmax: int, N: int,
+                      cache_len_out=None, committed_src=None, want_src: bool = True,
+                      dev_status=None):
+    """Keep the accepted path of a tree stored in the cache (node i at row
+    L + i), compacting its rows to L, L+1, .. in place.  Returns
+    (cache_len_out [B], committed_src [B,N] or None, dev_status [B])."""
+    B, Hkv, Lcap, D = k_cache.shape
+    dev = k_cache.device
+    dt = k_cache.dtype
+    _need(k_cache, "k_cache", dt, (B, Hkv, Lcap, D), dev)
+    _need(v_cache, "v_cache", dt, (B, Hkv, Lcap, D), dev)
+    _need(cache_len_in, "cache_len_in", torch.int32, (B,), dev)
+    _need(path, "path", torch.int32, (B, N), dev)
+    _need(path_len, "path_len", torch.int32, (B,), dev)
+    if cache_len_out is None:
+        cache_len_out = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(cache_len_out, "cache_len_out", torch.int32, (B,), dev)
+    if committed_src is None and want_src:
+        committed_src = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if dev_status is None:
+        dev_status = torch.empty(B, dtype=torch.int32, device=dev)
+    st = lib().ttv_kv_commit_inplace(_dt(dt), B, N, Hkv, D, Lcap, _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(cache_len_in), _ptr(cache_len_out), int(Lmax),
+                                     _ptr(path), _ptr(path_len), _ptr(committed_src),
+                                     _ptr(dev_status), _stream(dev))
+    _check("ttv_kv_commit_inplace", st)
+    return cache_len_out, committed_src, dev_status

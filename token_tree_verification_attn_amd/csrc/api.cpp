@@ -150,14 +150,16 @@ ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t
                          void* workspace, size_t workspace_bytes, int32_t rows_per_block,
                          int32_t chunk_keys, void* stream) {
   if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
-  if (!q || !k_cache || !v_cache || !cache_len || !k_tree || !v_tree || !parents || !out)
+  if (!q || !k_cache || !v_cache || !cache_len || !parents || !out || (!k_tree != !v_tree))
     return TTV_E_NULL;
+  const bool tree_in_cache = !k_tree;  // both NULL: node i at cache row L_b + i
   if (Lcap < 0 || Lmax > Lcap || !std::isfinite(scale) || !(scale > 0.f)) return TTV_E_SHAPE;
+  if (tree_in_cache && (long)Lmax + N > Lcap) return TTV_E_SHAPE;
   AttnPlan p;
   const ttv_status st = attn_plan(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys, &p);
   if (st != TTV_OK) return st;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_tree) ||
-      !aligned16(v_tree) || !aligned16(out))
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (!tree_in_cache && (!aligned16(k_tree) || !aligned16(v_tree))) || !aligned16(out))
     return TTV_E_ALIGN;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return TTV_E_WORKSPACE;
   if (p.ws_bytes > 0 && !aligned16(workspace)) return TTV_E_ALIGN;
@@ -169,6 +171,7 @@ ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t
   a.v_cache = v_cache;
   a.k_tree = k_tree;
   a.v_tree = v_tree;
+  a.tree_in_cache = tree_in_cache ? 1 : 0;
   a.cache_len = cache_len;
   a.parents = parents;
   a.out = out;
@@ -296,6 +299,25 @@ ttv_status ttv_probs_from_logits(int32_t R, int32_t V, float temperature, int32_
   const bool vec = V % 4 == 0 && aligned16(logits) && aligned16(probs);
   return launch_status(launch_probs(R, V, temperature, topk, logits, probs, vec,
                                     static_cast<hipStream_t>(stream)));
+}
+
+ttv_status ttv_kv_commit_inplace(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv, int32_t D,
+                                 int32_t Lcap, void* k_cache, void* v_cache,
+                                 const int32_t* cache_len_in, int32_t* cache_len_out,
+                                 int32_t Lmax, const int32_t* path, const int32_t* path_len,
+                                 int32_t* committed_src, int32_t* dev_status, void* stream) {
+  if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
+  if (!k_cache || !v_cache || !cache_len_in || !cache_len_out || !path || !path_len)
+    return TTV_E_NULL;
+  if (B < 1 || N < 1 || Hkv < 1 || D < 1 || Lmax < 0 || Lcap < 0) return TTV_E_SHAPE;
+  if (N > TTV_MAX_NODES || (D != 64 && D != 128)) return TTV_E_UNSUPPORTED;
+  if ((long)Lmax + N > Lcap) return TTV_E_SHAPE;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return TTV_E_ALIGN;
+  const int elt = dt == TTV_BF16 ? 2 : 4;
+  return launch_status(launch_kv_commit_inplace(elt, B, N, Hkv, D, Lcap, k_cache, v_cache,
+                                                cache_len_in, cache_len_out, Lmax, path,
+                                                path_len, committed_src, dev_status,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -134,8 +134,11 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
 
   const T* kc = static_cast<const T*>(a.k_cache) + ((size_t)bh * a.Lcap) * D;
   const T* vc = static_cast<const T*>(a.v_cache) + ((size_t)bh * a.Lcap) * D;
-  const T* kt = static_cast<const T*>(a.k_tree) + ((size_t)bh * N) * D;
-  const T* vt = static_cast<const T*>(a.v_tree) + ((size_t)bh * N) * D;
+  // the tree's K/V: their own tensors, or the cache rows after the prefix
+  // (node i at row Lc + i, Lc = L clamped to [0, Lmax]; rows < Lmax + N <= Lcap)
+  const int Lc = min(max(L, 0), a.Lmax);
+  const T* kt = a.tree_in_cache ? kc + (size_t)Lc * D : static_cast<const T*>(a.k_tree) + ((size_t)bh * N) * D;
+  const T* vt = a.tree_in_cache ? vc + (size_t)Lc * D : static_cast<const T*>(a.v_tree) + ((size_t)bh * N) * D;
 
   for (int tile = 0; tile < nP + nT; ++tile) {
     const bool is_tree = tile >= nP;

@@ -254,8 +254,10 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   };
   const char* kc = uniform(static_cast<const char*>(a.k_cache) + (size_t)bh * a.Lcap * D * 2);
   const char* vc = uniform(static_cast<const char*>(a.v_cache) + (size_t)bh * a.Lcap * D * 2);
-  const char* ktr = uniform(static_cast<const char*>(a.k_tree) + (size_t)bh * N * D * 2);
-  const char* vtr = uniform(static_cast<const char*>(a.v_tree) + (size_t)bh * N * D * 2);
+  // the tree's K/V: their own tensors, or the cache rows after the prefix
+  // (set below once the prefix length is known)
+  const char* ktr = a.tree_in_cache ? kc : uniform(static_cast<const char*>(a.k_tree) + (size_t)bh * N * D * 2);
+  const char* vtr = a.tree_in_cache ? vc : uniform(static_cast<const char*>(a.v_tree) + (size_t)bh * N * D * 2);
 
   // ---- per-lane constants of the HBM -> LDS copies.  Wave w, copy j fills
   // LDS slots (j*NW + w)*64 + lane of a tile (16 bytes each, placed by the
@@ -346,6 +348,11 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     sc.tree0 = 0;
   }
   const int ntiles = sc.nP + sc.nT;
+  if (a.tree_in_cache) {  // node i at row Lc + i, Lc = L clamped to [0, Lmax] (rows < Lmax + N <= Lcap)
+    const int Lc = a.balanced ? pl.L : min(max(__builtin_amdgcn_readfirstlane(L), 0), a.Lmax);
+    ktr = kc + (size_t)Lc * (D * 2);
+    vtr = vc + (size_t)Lc * (D * 2);
+  }
   // Copies of tile t into ring stage S.  Keys past the tile's valid ones
   // re-read the last valid row (finite values; their scores are masked), so
   // no copy leaves the tensors or reads rows at or beyond the prefix length.

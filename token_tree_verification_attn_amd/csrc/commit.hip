@@ -107,4 +107,85 @@ hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,
   return hipGetLastError();
 }
 
+// ttv_kv_commit_inplace: the tree's K/V live in the cache after the prefix
+// (node i at row L + i); row L + j takes the old row L + path[j].  Sources
+// and destinations overlap, so each (request, kv head) first reads its n
+// source rows of K and V into LDS, then -- after a barrier -- writes them
+// (path entries grow along the path, so only this staging order matters
+// when the rows move in parallel).  As above: one workgroup per (request,
+// kv head), or one per request over all heads when cache_len_out is
+// cache_len_in.
+__global__ __launch_bounds__(kCommitHeadThreads) void kv_commit_inplace_kernel(
+    int row_bytes, int N, int Hkv, int Lcap, int Lmax, u32x4* __restrict__ k_cache,
+    u32x4* __restrict__ v_cache, const int32_t* __restrict__ cache_len_in, int32_t* cache_len_out,
+    const int32_t* __restrict__ path, const int32_t* __restrict__ path_len,
+    int32_t* __restrict__ committed_src, int32_t* __restrict__ dev_status) {
+  extern __shared__ u32x4 s_rows[];  // [K | V][N rows][vec]
+  __shared__ int32_t s_path[kMaxNodes];
+  __shared__ int s_bad_node;
+  const int b = blockIdx.x;
+  const bool per_head = gridDim.y > 1;
+  const int h0 = per_head ? (int)blockIdx.y : 0, nh = per_head ? 1 : Hkv;
+  const bool first = blockIdx.y == 0;
+  const int L = cache_len_in[b];
+  const int n = path_len[b];
+  const bool shape_ok = L >= 0 && L <= Lmax && n >= 0 && n <= N && (long)L + N <= Lcap;
+  if (threadIdx.x == 0) s_bad_node = 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < N; j += blockDim.x) {
+    const int pj = path[(size_t)b * N + j];
+    s_path[j] = pj;
+    if (shape_ok && j < n && (pj < 0 || pj >= N)) s_bad_node = 1;  // same value from every writer
+  }
+  __syncthreads();
+  const bool ok = shape_ok && s_bad_node == 0;
+  if (ok) {
+    const int vec = row_bytes / 16;
+    const int total = n * vec;
+    for (int h = h0; h < h0 + nh; ++h) {
+      const size_t base = ((size_t)b * Hkv + h) * Lcap + L;  // row L of this head
+      for (int t = threadIdx.x; t < total; t += blockDim.x) {
+        const int j = t / vec, e = t - (t / vec) * vec;
+        const size_t src = (base + s_path[j]) * vec + e;
+        s_rows[t] = k_cache[src];
+        s_rows[N * vec + t] = v_cache[src];
+      }
+      __syncthreads();  // every source row is read before any is written
+      for (int t = threadIdx.x; t < total; t += blockDim.x) {
+        const int j = t / vec, e = t - (t / vec) * vec;
+        const size_t dst = (base + j) * vec + e;
+        k_cache[dst] = s_rows[t];
+        v_cache[dst] = s_rows[N * vec + t];
+      }
+      __syncthreads();  // before the next head's rows overwrite the staging area
+    }
+  }
+  if (committed_src && first) {
+    for (int j = threadIdx.x; j < N; j += blockDim.x)
+      committed_src[(size_t)b * N + j] = (ok && j < n) ? s_path[j] : -1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && first) {
+    cache_len_out[b] = ok ? L + n : L;
+    if (dev_status) dev_status[b] = ok ? TTV_OK : TTV_E_SHAPE;
+  }
+}
+
+hipError_t launch_kv_commit_inplace(int elt, int B, int N, int Hkv, int D, int Lcap, void* k_cache,
+                                    void* v_cache, const int32_t* cache_len_in,
+                                    int32_t* cache_len_out, int Lmax, const int32_t* path,
+                                    const int32_t* path_len, int32_t* committed_src,
+                                    int32_t* dev_status, hipStream_t s) {
+  const bool per_head = cache_len_out != cache_len_in && Hkv > 1 && Hkv <= 65535;
+  const size_t lds = (size_t)2 * N * D * elt;  // K and V rows of one head: at most 128 KB
+  const dim3 grid(B, per_head ? Hkv : 1);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kv_commit_inplace_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kv_commit_inplace_kernel, grid, dim3(kCommitHeadThreads), lds, s, D * elt, N,
+                     Hkv, Lcap, Lmax, static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache),
+                     cache_len_in, cache_len_out, path, path_len, committed_src, dev_status);
+  return hipGetLastError();
+}
+
 }  // namespace ttv

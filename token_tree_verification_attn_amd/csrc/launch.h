@@ -40,6 +40,7 @@ struct AttnArgs {
   int B, N, Hq, Hkv, G, D, Lcap, Lmax, R;
   int rows_per_block, chunk_keys, chunks;
   int balanced, row_blocks, items;
+  int tree_in_cache;  // k_tree/v_tree NULL: node i's K/V at cache row L_b + i
   float scale_log2;  // softmax scale * log2(e): scores are kept in log2 units
 };
 
@@ -105,5 +106,11 @@ hipError_t launch_tree_merge(int B, int S, int Ls, const int32_t* seqs, const in
 constexpr int kProbsMaxTopk = 512;  // the top-k bound comes from 512 per-thread maxima
 hipError_t launch_probs(int R, int V, float T, int topk, const float* logits, float* probs,
                         bool vec, hipStream_t s);
+
+hipError_t launch_kv_commit_inplace(int elt, int B, int N, int Hkv, int D, int Lcap, void* k_cache,
+                                    void* v_cache, const int32_t* cache_len_in,
+                                    int32_t* cache_len_out, int Lmax, const int32_t* path,
+                                    const int32_t* path_len, int32_t* committed_src,
+                                    int32_t* dev_status, hipStream_t s);
 
 }  // namespace ttv
