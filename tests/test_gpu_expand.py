@@ -137,3 +137,13 @@ def test_expansion_schedule_builds_the_workload_tree():
     ref_tree = synth.expansion_tree(int(n_in[0]), widths)
     for b in range(B):
         assert par[b, :n_in[b]].tolist() == ref_tree.tolist()
+
+
+def test_benchmark_configuration():
+    """The configuration bench_expand.py times: 16 requests x 16 frontier rows
+    of 32000 probabilities (its own input recipe), k = 4."""
+    announce("expand benchmark configuration 16 x 16 x 32000, k=4")
+    import bench_expand
+    probs = bench_expand.make_probs(16, 16, 32000)
+    frontier = np.tile(np.arange(16, dtype=np.int32), (16, 1))
+    check(probs, frontier, np.full(16, 16, np.int32), 4, 128)

@@ -50,3 +50,13 @@ def test_stochastic_workload_rows():
     rng = np.random.default_rng(1005)
     z = rng.normal(0.0, 2.0, (2, 64, 32000)).astype(np.float32)
     check(z, 0.8, 0)
+
+
+@pytest.mark.parametrize("k", [0, 50])
+def test_benchmark_configuration(k):
+    """The configuration bench_expand.py --op probs times: 1024 rows of 32000
+    N(0,2) logits at T = 0.8 (its own input recipe), all tokens and top-50."""
+    announce("probs benchmark configuration 1024 x 32000, T=0.8, topk=%d" % k)
+    rng = np.random.default_rng(np.random.SeedSequence([1005, 13]))
+    z = rng.normal(0.0, 2.0, (1024, 32000)).astype(np.float32)
+    check(z, 0.8, k)
