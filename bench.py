@@ -5,6 +5,9 @@
 A step is one pass of the whole path over one batch of synthetic input:
 tree_attn (prefix + tree-masked attention of every node) -> tree_verify ->
 kv_commit, enqueued back to back on one stream with no host synchronisation.
+Greedy workloads take verification and commit in one pass
+(tree_verify_commit: argmax partials, then one launch that scans the tree and
+copies the accepted rows); --unfused times the two separate calls instead.
 The default workload is c2, the LLaMA-7B-shaped layer (1 request, 64-node
 expansion tree, 32 heads of 128, prefix 512, vocabulary 32000, greedy).
 Inputs are resident in HBM before timing starts; each step reads a different
@@ -78,7 +81,7 @@ class Inputs:
 
 
 class Step:
-    def __init__(self, d, copies, dev):
+    def __init__(self, d, copies, dev, fuse=True):
         self.d = d
         self.copies = copies
         self.mode = ttv.GREEDY if d["mode"] == "greedy" else ttv.STOCHASTIC
@@ -89,6 +92,7 @@ class Step:
             dt, B, N, Hq, d["Hkv"], D, d["Lmax"])), dtype=torch.uint8, device=dev)
         self.ws_ver = torch.empty(max(1, ttv.tree_verify_workspace_size(
             self.mode, B, N, d["V"])), dtype=torch.uint8, device=dev)
+        self.fused = fuse and self.mode == ttv.GREEDY  # one pass: verification + commit
 
     def attn(self, c):
         ttv.tree_attn(c.q, c.k_cache, c.v_cache, c.cache_len, c.k_tree, c.v_tree, c.parents,
@@ -106,11 +110,20 @@ class Step:
                       self.d["Lmax"], cache_len_out=c.len_out, committed_src=c.src,
                       dev_status=c.st)
 
+    def verify_commit(self, c):
+        ttv.tree_verify_commit(c.parents, c.tokens, c.llm, c.k_tree, c.v_tree, c.k_cache,
+                               c.v_cache, c.cache_len, self.d["Lmax"], cache_len_out=c.len_out,
+                               path=c.path, path_len=c.plen, out_tokens=c.outt,
+                               committed_src=c.src, dev_status=c.st, workspace=self.ws_ver)
+
     def __call__(self, i):
         c = self.copies[i % len(self.copies)]
         self.attn(c)
-        self.verify(c)
-        self.commit(c)
+        if self.fused:
+            self.verify_commit(c)
+        else:
+            self.verify(c)
+            self.commit(c)
 
 
 def timed(fn, n, stream):
@@ -249,6 +262,8 @@ def main():
                     help="time eager launches instead of HIP-graph replays")
     ap.add_argument("--warm", action="store_true",
                     help="reuse one input copy (cache-resident) instead of rotating copies")
+    ap.add_argument("--unfused", action="store_true",
+                    help="greedy verification and commit as two calls instead of one pass")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -262,7 +277,7 @@ def main():
     ncopies = 1 if args.warm else max(1, min(64, -(-2 * MALL_BYTES // per_copy)))
     copies = [first] + [Inputs(d, dev) for _ in range(ncopies - 1)]
     log("workload %s: %d input copies of %.1f MB" % (args.workload, ncopies, per_copy / 1e6))
-    step = Step(d, copies, dev)
+    step = Step(d, copies, dev, fuse=not args.unfused)
     stream = torch.cuda.current_stream(dev)
 
     for i in range(args.warmup):
@@ -289,6 +304,7 @@ def main():
     ms_attn = stage_ms(step.attn)
     ms_verify = stage_ms(step.verify)
     ms_commit = stage_ms(step.commit)
+    ms_fused = stage_ms(step.verify_commit) if step.fused else None
     st = torch.stack([c.st for c in copies]).cpu()
     assert int(st.abs().sum()) == 0, "a request was rejected: %s" % st
 
@@ -319,13 +335,16 @@ def main():
         "dtype": d["dtype"], "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "N": N, "Hq": d["Hq"], "Hkv": d["Hkv"],
                    "D": d["D"], "prefix": synth.WORKLOADS[args.workload].L, "V": d["V"],
-                   "verify": d["mode"], "input_copies": ncopies,
+                   "verify": d["mode"],
+                   "verify_commit": "one pass" if step.fused else "two calls",
+                   "input_copies": ncopies,
                    "launch": "hip graph replay" if graph is not None else "eager",
                    "inputs": "rotated, HBM-resident" if ncopies > 1 else "one copy (warm)"},
         "tree_attn_kv_gbs": kv_gbs,
         "tree_attn_kv_frac_of_hbm_peak": kv_gbs / HBM_PEAK_GBS,
         "stage_us": {"tree_attn": ms_attn * 1e3, "tree_verify": ms_verify * 1e3,
-                     "kv_commit": ms_commit * 1e3},
+                     "kv_commit": ms_commit * 1e3,
+                     "tree_verify_commit": ms_fused * 1e3 if ms_fused is not None else None},
         "roofline": roof,
     }
     if args.cpu_budget > 0:

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_attn_workspace_size",
               "ttv_tree_verify", "ttv_tree_verify_workspace_size", "ttv_kv_commit",
-              "ttv_tree_expand", "ttv_tree_merge", "ttv_probs_from_logits", "ttv_kv_commit_inplace", "ttv_status_string",
+              "ttv_tree_expand", "ttv_tree_merge", "ttv_probs_from_logits", "ttv_kv_commit_inplace", "ttv_tree_verify_commit", "ttv_status_string",
               "ttv_version"):
         assert n in names
 
@@ -214,3 +214,29 @@ def test_kv_commit_inplace_host_validation(kw, status):
                 path=A, plen=A, src=None, st=None)
     args.update(kw)
     assert ttv.lib().ttv_kv_commit_inplace(*args.values(), None) == status
+
+
+def verify_commit(**kw):
+    args = dict(dt=1, B=2, N=8, V=64, Hkv=2, D=64, Lcap=100, par=A, tok=A, llm=A, kt=A, vt=A,
+                kc=A, vc=A, cli=A, clo=A + 0x100, Lmax=50, path=A, plen=A, outt=A, src=None,
+                st=None, ws=A, wsb=1 << 20)
+    args.update(kw)
+    return ttv.lib().ttv_tree_verify_commit(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), ttv.E_DTYPE), (dict(par=None), ttv.E_NULL), (dict(llm=None), ttv.E_NULL),
+    (dict(kc=None), ttv.E_NULL), (dict(clo=None), ttv.E_NULL), (dict(outt=None), ttv.E_NULL),
+    (dict(B=0), ttv.E_SHAPE), (dict(V=0), ttv.E_SHAPE), (dict(Lmax=93), ttv.E_SHAPE),
+    (dict(N=129, Lcap=1000), ttv.E_UNSUPPORTED), (dict(D=32), ttv.E_UNSUPPORTED),
+    (dict(llm=MIS), ttv.E_ALIGN), (dict(kt=MIS), ttv.E_ALIGN), (dict(ws=None), ttv.E_WORKSPACE),
+    (dict(wsb=64), ttv.E_WORKSPACE), (dict(ws=MIS), ttv.E_ALIGN),
+])
+def test_tree_verify_commit_host_validation(kw, status):
+    assert verify_commit(**kw) == status
+
+
+def test_tree_verify_commit_takes_every_commit_shape():
+    """Shared length arrays and the largest rows reach the workspace check."""
+    assert verify_commit(clo=A, ws=None) == ttv.E_WORKSPACE
+    assert verify_commit(dt=0, D=128, N=128, Lcap=1000, ws=None) == ttv.E_WORKSPACE

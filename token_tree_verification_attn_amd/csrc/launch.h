@@ -71,6 +71,18 @@ hipError_t launch_verify_greedy(int B, int N, int V, const int32_t* parents,
                                 int32_t* dev_status, void* ws, const GreedyPlan& p,
                                 hipStream_t s);
 
+// Greedy verification and the KV commit in one pass: argmax partials, then
+// one launch that scans each tree and copies the path's rows.
+hipError_t launch_verify_greedy_commit(int B, int N, int V, const int32_t* parents,
+                                       const int32_t* tokens, const float* llm, int32_t* path,
+                                       int32_t* path_len, int32_t* out_tokens,
+                                       int32_t* dev_status, void* ws, const GreedyPlan& p,
+                                       int elt, int Hkv, int D, int Lcap, int Lmax,
+                                       const void* k_tree, const void* v_tree, void* k_cache,
+                                       void* v_cache, const int32_t* cache_len_in,
+                                       int32_t* cache_len_out, int32_t* committed_src,
+                                       hipStream_t s);
+
 // Largest vocabulary the stochastic verifier holds in LDS.
 constexpr int kMssMaxVocab = 36864;
 hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,

@@ -86,17 +86,20 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __rest
 // node (lowest index on ties), found with a wave max; LDS only orders the
 // path's nodes by depth.
 constexpr int kMaxSplits = 4;  // greedy_plan never makes more
-__global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
-                                                         const int32_t* __restrict__ parents,
-                                                         const int32_t* __restrict__ tokens,
-                                                         const float* __restrict__ ws_val,
-                                                         const int* __restrict__ ws_idx,
-                                                         int32_t* __restrict__ path,
-                                                         int32_t* __restrict__ path_len,
-                                                         int32_t* __restrict__ out_tokens,
-                                                         int32_t* __restrict__ dev_status) {
-  __shared__ int32_t s_path[kMaxNodes];
-  const int b = blockIdx.x, lane = threadIdx.x;
+constexpr int kVerifyCommitThreads = 1024;
+
+// The scan of request b by one wavefront (lanes 0..63 of the caller).  Fills
+// s_path[0..n-1] with the path's nodes by depth; writes path / out_tokens /
+// path_len / dev_status when `write`.  Returns n (0 for a
+// malformed tree).  LDS is only written and read by this wavefront, whose LDS
+// operations complete in order.
+__device__ int greedy_scan_wave(int b, int N, int splits, const int32_t* __restrict__ parents,
+                                const int32_t* __restrict__ tokens,
+                                const float* __restrict__ ws_val, const int* __restrict__ ws_idx,
+                                int32_t* __restrict__ path, int32_t* __restrict__ path_len,
+                                int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status,
+                                bool write, int32_t* s_path) {
+  const int lane = threadIdx.x & 63;
   const int i0 = lane, i1 = lane + 64;
   const bool v0 = i0 < N, v1 = i1 < N;
   const int32_t* par = parents + (size_t)b * N;
@@ -123,15 +126,17 @@ __global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
   }
   uint64_t a0lo, a1lo, a1hi;
   if (!wave_tree_bits(p0, p1, N, a0lo, a1lo, a1hi)) {
-    for (int k = lane; k < N; k += kWave) {
-      path[(size_t)b * N + k] = -1;
-      out_tokens[(size_t)b * N + k] = -1;
+    if (write) {
+      for (int k = lane; k < N; k += kWave) {
+        path[(size_t)b * N + k] = -1;
+        out_tokens[(size_t)b * N + k] = -1;
+      }
+      if (lane == 0) {
+        path_len[b] = 0;
+        if (dev_status) dev_status[b] = TTV_E_TREE;
+      }
     }
-    if (lane == 0) {
-      path_len[b] = 0;
-      if (dev_status) dev_status[b] = TTV_E_TREE;
-    }
-    return;
+    return 0;
   }
   // node x lives in lane x & 63, slot x >> 6: both slots are shuffled by
   // every lane, then each picks its own
@@ -155,22 +160,137 @@ __global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
   const uint64_t pe0 = end < 64 ? x_lo0 : x_lo1, pe1 = end < 64 ? 0ull : x_hi1;
   if (v0 && ((pe0 >> i0) & 1ull)) s_path[d0] = i0;
   if (v1 && ((pe1 >> (i1 - 64)) & 1ull)) s_path[d1] = i1;
-  __syncthreads();
-  const int am_end = node_int(am0, am1, end);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  if (write) {
+    const int am_end = node_int(am0, am1, end);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int k = lane + r * kWave;
-    const int nxt = (k < N && k < dend) ? s_path[k + 1] : 0;
-    const int tk = node_int(t0, t1, nxt);
-    if (k < N) {
-      path[(size_t)b * N + k] = k <= dend ? s_path[k] : -1;
-      out_tokens[(size_t)b * N + k] = k < dend ? tk : (k == dend ? am_end : -1);
+    for (int r = 0; r < 2; ++r) {
+      const int k = lane + r * kWave;
+      const int nxt = (k < N && k < dend) ? s_path[k + 1] : 0;
+      const int tk = node_int(t0, t1, nxt);
+      if (k < N) {
+        path[(size_t)b * N + k] = k <= dend ? s_path[k] : -1;
+        out_tokens[(size_t)b * N + k] = k < dend ? tk : (k == dend ? am_end : -1);
+      }
+    }
+    if (lane == 0) {
+      path_len[b] = dend + 1;
+      if (dev_status) dev_status[b] = TTV_OK;
     }
   }
-  if (lane == 0) {
-    path_len[b] = dend + 1;
-    if (dev_status) dev_status[b] = TTV_OK;
+  return dend + 1;
+}
+
+// Kernel B: one wavefront per request; lane l holds nodes l and l + 64.
+// Everything it reads (parents, tokens, the nodes' argmax partials) is
+// requested at once; the rest works on registers: ancestor bitsets by
+// shuffle pointer doubling, amax of a node's parent by a shuffle from the
+// lane that holds it.  e_i = (token of i == amax of its parent),
+// E = ballot(e_i or i == 0), and node i is accepted iff its whole root path
+// lies in E, i.e. (anc[i] & ~E) == 0.  The path ends at the deepest accepted
+// node (lowest index on ties), found with a wave max; LDS only orders the
+// path's nodes by depth.
+__global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
+                                                         const int32_t* __restrict__ parents,
+                                                         const int32_t* __restrict__ tokens,
+                                                         const float* __restrict__ ws_val,
+                                                         const int* __restrict__ ws_idx,
+                                                         int32_t* __restrict__ path,
+                                                         int32_t* __restrict__ path_len,
+                                                         int32_t* __restrict__ out_tokens,
+                                                         int32_t* __restrict__ dev_status) {
+  __shared__ int32_t s_path[kMaxNodes];
+  greedy_scan_wave(blockIdx.x, N, splits, parents, tokens, ws_val, ws_idx, path, path_len,
+                   out_tokens, dev_status, true, s_path);
+}
+
+// Kernel B and the KV commit in one launch.  Wave 0 scans request b's tree
+// into LDS (the request's first workgroup also writes the verifier's
+// outputs); after one barrier the workgroup copies the path's rows of its kv
+// heads, node s_path[j] to cache row L + j, in 16-byte vectors.  The commit
+// so needs neither a launch of its own nor a read of the path back from
+// memory.  Reading every tree row while the scan runs, to keep only the
+// path's, measured slower: the path is short and its rows are few.
+// Distinct length arrays: one 256-thread workgroup per (request, kv head).
+// Shared ones: one 1024-thread workgroup per request copies every head, and
+// all its threads read cache_len_in[b] before the barrier that precedes the
+// write of cache_len_out[b] (no other workgroup touches entry b).
+// Statuses: the verifier's if it rejects the tree, else the commit's.
+__global__ __launch_bounds__(kVerifyCommitThreads) void greedy_scan_commit_kernel(
+    int N, int splits, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
+    const float* __restrict__ ws_val, const int* __restrict__ ws_idx, int32_t* __restrict__ path,
+    int32_t* __restrict__ path_len, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ dev_status, int row_vecs, int Hkv, int Lcap, int Lmax,
+    const u32x4* __restrict__ k_tree, const u32x4* __restrict__ v_tree,
+    u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, const int32_t* cache_len_in,
+    int32_t* cache_len_out, int32_t* __restrict__ committed_src) {
+  __shared__ int32_t s_path[kMaxNodes];
+  __shared__ int s_n;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const bool per_head = gridDim.y > 1;
+  const int h0 = per_head ? (int)blockIdx.y : 0, nh = per_head ? 1 : Hkv;
+  const bool first = blockIdx.y == 0;  // writes the request's verifier outputs and lengths
+  const int L = cache_len_in[b];
+  if (tid < kWave) {
+    const int n = greedy_scan_wave(b, N, splits, parents, tokens, ws_val, ws_idx, path, path_len,
+                                   out_tokens, nullptr, first, s_path);
+    if (tid == 0) s_n = n;
   }
+  __syncthreads();
+  const int n = s_n;  // 0: malformed tree
+  const bool shape_ok = L >= 0 && L <= Lmax && (long)L + n <= Lcap;
+  const bool ok = n > 0 && shape_ok;
+  if (ok) {
+    const int per = n * row_vecs, total = nh * per;
+    for (int t = tid; t < total; t += blockDim.x) {
+      const int hh = t / per;
+      const int r = t - hh * per;
+      const int j = r / row_vecs, e = r - (r / row_vecs) * row_vecs;
+      const size_t bh = (size_t)b * Hkv + h0 + hh;
+      const size_t src = (bh * N + s_path[j]) * row_vecs + e;
+      const size_t dst = (bh * Lcap + (size_t)(L + j)) * row_vecs + e;
+      const u32x4 kx = k_tree[src], vx = v_tree[src];
+      k_cache[dst] = kx;
+      v_cache[dst] = vx;
+    }
+  }
+  if (first) {
+    if (committed_src)
+      for (int j = tid; j < N; j += blockDim.x)
+        committed_src[(size_t)b * N + j] = (ok && j < n) ? s_path[j] : -1;
+    if (tid == 0) {
+      cache_len_out[b] = ok ? L + n : L;
+      if (dev_status) dev_status[b] = n == 0 ? TTV_E_TREE : (shape_ok ? TTV_OK : TTV_E_SHAPE);
+    }
+  }
+}
+
+hipError_t launch_verify_greedy_commit(int B, int N, int V, const int32_t* parents,
+                                       const int32_t* tokens, const float* llm, int32_t* path,
+                                       int32_t* path_len, int32_t* out_tokens,
+                                       int32_t* dev_status, void* ws, const GreedyPlan& p,
+                                       int elt, int Hkv, int D, int Lcap, int Lmax,
+                                       const void* k_tree, const void* v_tree, void* k_cache,
+                                       void* v_cache, const int32_t* cache_len_in,
+                                       int32_t* cache_len_out, int32_t* committed_src,
+                                       hipStream_t s) {
+  float* ws_val = static_cast<float*>(ws);
+  int* ws_idx = reinterpret_cast<int*>(ws_val + (size_t)B * N * p.splits);
+  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(llm) & 15) == 0);
+  const dim3 grid(B * N, p.splits);
+  if (vec) hipLaunchKernelGGL(argmax_partial_kernel<true>, grid, dim3(256), 0, s, llm, V, p.slice, p.splits, ws_val, ws_idx);
+  else hipLaunchKernelGGL(argmax_partial_kernel<false>, grid, dim3(256), 0, s, llm, V, p.slice, p.splits, ws_val, ws_idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool per_head = cache_len_out != cache_len_in && Hkv > 1 && Hkv <= 65535;
+  const dim3 grid2(B, per_head ? Hkv : 1), block2(per_head ? 256 : kVerifyCommitThreads);
+  hipLaunchKernelGGL(greedy_scan_commit_kernel, grid2, block2, 0, s, N, p.splits, parents, tokens,
+                     ws_val, ws_idx, path, path_len, out_tokens, dev_status, D * elt / 16, Hkv,
+                     Lcap, Lmax, static_cast<const u32x4*>(k_tree),
+                     static_cast<const u32x4*>(v_tree), static_cast<u32x4*>(k_cache),
+                     static_cast<u32x4*>(v_cache), cache_len_in, cache_len_out, committed_src);
+  return hipGetLastError();
 }
 
 // Vocabulary splits per logits row: enough workgroups to cover the chip
