@@ -78,6 +78,13 @@ def mss_spec(**kw):
     dict(), dict(V=7, seed=1), dict(N=128, dmax=127, max_children=3, seed=2),
     dict(N=1), dict(V=32000, B=4, N=16, seed=3), dict(V=36864, B=2, N=8, seed=4),
     dict(V=33, prob_sigma=4.0, seed=5), dict(N=65, tree="star", V=20, seed=6),
+    # rows of 16-byte vectors up to 32768 entries take the double-buffered
+    # walk: its largest vocabulary, a chunk boundary, the first size past it,
+    # and stars whose root tests up to 127 children in a row (both words of
+    # the children bitset, the two row buffers alternating)
+    dict(V=32768, B=3, N=12, seed=7), dict(V=4100, B=8, N=30, seed=8, prob_sigma=0.3),
+    dict(V=32772, B=2, N=8, seed=9), dict(N=65, tree="star", V=64, seed=10),
+    dict(N=128, tree="star", V=128, seed=12, prob_sigma=0.2), dict(V=4, B=8, N=5, seed=13),
 ])
 def test_stochastic_edge_cases(kw):
     announce("verify stochastic edge %s" % kw)

@@ -492,7 +492,57 @@ __device__ __forceinline__ double mss_residual(const float* __restrict__ q, int 
   return part;
 }
 
-template <bool VEC>
+// Double-buffered row passes (16-byte rows, V <= 4 * kMssThreads * kMssPfChunks):
+// a row is requested into registers by mss_issue_row and consumed later, so
+// the next child's row can be in flight while the current one is used.
+constexpr int kMssPfChunks = 8;
+constexpr int kMssPfMaxVocab = 4 * kMssThreads * kMssPfChunks;
+
+// Every lane requests every chunk (entries past the row read its first 16
+// bytes and are never used): loads under a branch make the compiler wait for
+// all outstanding loads at their first use, which would drain the prefetch.
+__device__ __forceinline__ void mss_issue_row(const float* __restrict__ row, int V,
+                                              f32x4 (&r)[kMssPfChunks]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kMssPfChunks; ++j) {
+    const int v = 4 * (t + kMssThreads * j);
+    r[j] = *reinterpret_cast<const f32x4*>(row + (v < V ? v : 0));
+  }
+}
+
+// s_w[widx(v)] = r
+__device__ __forceinline__ void mss_regs_to_lds(const f32x4 (&r)[kMssPfChunks], int V, float* s_w) {
+  const int t = threadIdx.x;
+  f32x4* wp = reinterpret_cast<f32x4*>(s_w + 4 * t + 4 * (t >> 5));
+#pragma unroll
+  for (int j = 0; j < kMssPfChunks; ++j)
+    if (4 * (t + kMssThreads * j) < V) wp[(kMssChunkStride / 4) * j] = r[j];
+}
+
+// w = max(w - s*q, +0) in place with q in registers; returns this thread's
+// sum of fx40(w) (as an integer-valued double)
+__device__ __forceinline__ double mss_residual_regs(const f32x4 (&r)[kMssPfChunks], int V, float s,
+                                                    float* s_w) {
+  const int t = threadIdx.x;
+  double part = 0.0;
+  f32x4* wp = reinterpret_cast<f32x4*>(s_w + 4 * t + 4 * (t >> 5));
+#pragma unroll
+  for (int j = 0; j < kMssPfChunks; ++j)
+    if (4 * (t + kMssThreads * j) < V) {
+      f32x4 w = wp[(kMssChunkStride / 4) * j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = fmaf(-s, r[j][e], w[e]);
+        w[e] = d > 0.0f ? d : 0.0f;
+        part += fx40d(w[e]);
+      }
+      wp[(kMssChunkStride / 4) * j] = w;
+    }
+  return part;
+}
+
+template <bool VEC, bool PF>
 __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     int N, int V, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
     const float* __restrict__ llm, const float* __restrict__ ssm,
@@ -578,7 +628,15 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   for (;;) {
     uint64_t k0 = s_kids[u][0], k1 = s_kids[u][1];
     if ((k0 | k1) == 0ull) {  // leaf: the bonus comes from p_u
-      load_p_row(u);
+      if constexpr (PF) {
+        f32x4 ra[kMssPfChunks];
+        mss_issue_row(llm + (rowN + u) * V, V, ra);
+        __syncthreads();
+        mss_regs_to_lds(ra, V, s_w);
+        __syncthreads();
+      } else {
+        load_p_row(u);
+      }
       break;
     }
     const int c0 = k0 ? __ffsll((unsigned long long)k0) - 1 : 64 + __ffsll((unsigned long long)k1) - 1;
@@ -588,6 +646,63 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       continue;
     }
     // first child rejected: sequential residual tests at u
+    if constexpr (PF) {
+      // p_u and q of the first child are requested together; while child c's
+      // residual pass runs, the next child's row is already in flight (the
+      // buffers alternate by unrolling: copying a register row would wait
+      // for its loads)
+      f32x4 ra[kMssPfChunks], rb[kMssPfChunks];
+      mss_issue_row(llm + (rowN + u) * V, V, ra);
+      mss_issue_row(ssm + (rowN + c0) * V, V, rb);
+      if (k0) k0 &= k0 - 1;
+      else k1 &= k1 - 1;
+      __syncthreads();  // every thread has read the old residual
+      mss_regs_to_lds(ra, V, s_w);
+      __syncthreads();
+      float s = 1.0f;
+      int next = -1, ccur = c0;
+      // one rejected child ccur whose row is in cur: prefetch the next child
+      // into nxt (after the last child, ccur's row again, from cache, so the
+      // request is never under a branch), w = max(w - s*q, +0), then test
+      // the next child; true = done
+      auto pass = [&](f32x4 (&cur)[kMssPfChunks], f32x4 (&nxt)[kMssPfChunks]) -> bool {
+        int cn = -1;
+        if (k0) {
+          cn = __ffsll((unsigned long long)k0) - 1;
+          k0 &= k0 - 1;
+        } else if (k1) {
+          cn = 64 + __ffsll((unsigned long long)k1) - 1;
+          k1 &= k1 - 1;
+        }
+        mss_issue_row(ssm + (rowN + (cn >= 0 ? cn : ccur)) * V, V, nxt);
+        ccur = cn;
+        const double part = mss_residual_regs(cur, V, s, s_w);
+        const double S = block_sum_f64(part, s_redd);  // its barriers publish s_w
+        s = (float)(S * 0x1p-40);
+        if (s == 0.0f) {  // empty residual: stop testing, sample from p_u
+          mss_issue_row(llm + (rowN + u) * V, V, cur);  // cur is consumed
+          __syncthreads();
+          mss_regs_to_lds(cur, V, s_w);
+          __syncthreads();
+          return true;
+        }
+        if (cn < 0) return true;  // every child rejected: bonus from the residual
+        const bool accept = s_rq[cn] * s < s_w[widx(s_tok[cn])];
+        __syncthreads();  // every thread has read w[x] before it is updated
+        if (accept) {
+          next = cn;
+          return true;
+        }
+        return false;
+      };
+      for (;;) {
+        if (pass(rb, ra)) break;
+        if (pass(ra, rb)) break;
+      }
+      if (next < 0) break;  // bonus from the residual in s_w (or p_u)
+      u = next;
+      continue;
+    }
     load_p_row(u);
     float s = 1.0f;
     int next = -1;
@@ -722,7 +837,8 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
   const size_t lds = (size_t)(V + 4 * (V >> 7) + 4) * sizeof(float);  // widx(V - 1) + 1, 16-byte padded
   const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(llm) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(ssm) & 15) == 0;
-  auto kern = vec ? mss_kernel<true> : mss_kernel<false>;
+  auto kern = !vec ? mss_kernel<false, false>
+                   : (V <= kMssPfMaxVocab ? mss_kernel<true, true> : mss_kernel<true, false>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
