@@ -5,9 +5,10 @@
 A step is one pass of the whole path over one batch of synthetic input:
 tree_attn (prefix + tree-masked attention of every node) -> tree_verify ->
 kv_commit, enqueued back to back on one stream with no host synchronisation.
-Greedy workloads take verification and commit in one pass
-(tree_verify_commit: argmax partials, then one launch that scans the tree and
-copies the accepted rows); --unfused times the two separate calls instead.
+Verification and commit run as one pass (tree_verify_commit: greedy = argmax
+partials, then one launch that scans each tree and copies its accepted rows;
+stochastic = the walk's workgroup copies them); --unfused times the two
+separate calls instead.
 The default workload is c2, the LLaMA-7B-shaped layer (1 request, 64-node
 expansion tree, 32 heads of 128, prefix 512, vocabulary 32000, greedy).
 Inputs are resident in HBM before timing starts; each step reads a different
@@ -92,7 +93,7 @@ class Step:
             dt, B, N, Hq, d["Hkv"], D, d["Lmax"])), dtype=torch.uint8, device=dev)
         self.ws_ver = torch.empty(max(1, ttv.tree_verify_workspace_size(
             self.mode, B, N, d["V"])), dtype=torch.uint8, device=dev)
-        self.fused = fuse and self.mode == ttv.GREEDY  # one pass: verification + commit
+        self.fused = fuse  # one pass: verification + commit
 
     def attn(self, c):
         ttv.tree_attn(c.q, c.k_cache, c.v_cache, c.cache_len, c.k_tree, c.v_tree, c.parents,
@@ -111,8 +112,9 @@ class Step:
                       dev_status=c.st)
 
     def verify_commit(self, c):
-        ttv.tree_verify_commit(c.parents, c.tokens, c.llm, c.k_tree, c.v_tree, c.k_cache,
-                               c.v_cache, c.cache_len, self.d["Lmax"], cache_len_out=c.len_out,
+        ttv.tree_verify_commit(self.mode, c.parents, c.tokens, c.llm, c.k_tree, c.v_tree,
+                               c.k_cache, c.v_cache, c.cache_len, self.d["Lmax"], ssm=c.ssm,
+                               u_accept=c.u_accept, u_bonus=c.u_bonus, cache_len_out=c.len_out,
                                path=c.path, path_len=c.plen, out_tokens=c.outt,
                                committed_src=c.src, dev_status=c.st, workspace=self.ws_ver)
 
@@ -263,7 +265,7 @@ def main():
     ap.add_argument("--warm", action="store_true",
                     help="reuse one input copy (cache-resident) instead of rotating copies")
     ap.add_argument("--unfused", action="store_true",
-                    help="greedy verification and commit as two calls instead of one pass")
+                    help="verification and commit as two calls instead of one pass")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "

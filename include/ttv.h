@@ -248,31 +248,35 @@ ttv_status ttv_kv_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv,
                          int32_t* dev_status, void* stream);
 
 /*
- * ttv_tree_verify_commit -- greedy ttv_tree_verify followed by ttv_kv_commit
- * in one pass ([SI] §4 "Token Tree Verification" and "Tree-Based Parallel
- * Decoding": verify the tree, keep the accepted path's KV).  Every output
- * (path, path_len, out_tokens, k_cache/v_cache rows, cache_len_out,
- * committed_src) equals what TTV_GREEDY ttv_tree_verify and then ttv_kv_commit
- * on its path give; the arguments mean what they mean there.  The path goes
- * from the scan to the row copy through on-chip memory, and no launch sits
- * between verification and commit.
+ * ttv_tree_verify_commit -- ttv_tree_verify followed by ttv_kv_commit of its
+ * path in one pass ([SI] §4 "Token Tree Verification", "Token Verification"
+ * and "Tree-Based Parallel Decoding": verify the tree, keep the accepted
+ * path's KV).  Every output (path, path_len, out_tokens, the k_cache/v_cache
+ * rows, cache_len_out, committed_src) equals what ttv_tree_verify(mode, ...)
+ * and then ttv_kv_commit on its path give; the arguments mean what they mean
+ * there.  The path goes from the verifier to the row copy through on-chip
+ * memory: greedy mode runs the argmax partials and then one launch that scans
+ * and copies; stochastic mode copies from the walk's own workgroup.
  *
- *   dev_status  nullable: TTV_E_TREE for a malformed tree (path_len 0,
- *               nothing committed, cache_len_out[b] = L), else TTV_E_SHAPE
+ *   dev_status  nullable: the verifier's status if it rejects the request
+ *               (TTV_E_TREE, or TTV_E_SHAPE for a bad stochastic token: path_len
+ *               0, nothing committed, cache_len_out[b] = L), else TTV_E_SHAPE
  *               when L < 0, L > Lmax or L + path_len > Lcap (nothing
  *               committed, cache_len_out[b] = L), else TTV_OK.
- *   workspace   >= ttv_tree_verify_workspace_size(TTV_GREEDY, B, N, V) bytes.
+ *   workspace   >= ttv_tree_verify_workspace_size(mode, B, N, V) bytes.
  *   cache_len_in and cache_len_out may be the same array, as in ttv_kv_commit.
- * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE, TTV_E_UNSUPPORTED,
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE (mode or dt), TTV_E_UNSUPPORTED,
  *         TTV_E_ALIGN, TTV_E_WORKSPACE, TTV_E_LAUNCH.
  */
-ttv_status ttv_tree_verify_commit(ttv_dtype dt, int32_t B, int32_t N,
-                                  int32_t V, int32_t Hkv, int32_t D,
-                                  int32_t Lcap, const int32_t* parents,
+ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt,
+                                  int32_t B, int32_t N, int32_t V,
+                                  int32_t Hkv, int32_t D, int32_t Lcap,
+                                  const int32_t* parents,
                                   const int32_t* tokens, const float* llm,
-                                  const void* k_tree, const void* v_tree,
-                                  void* k_cache, void* v_cache,
-                                  const int32_t* cache_len_in,
+                                  const float* ssm, const float* u_accept,
+                                  const float* u_bonus, const void* k_tree,
+                                  const void* v_tree, void* k_cache,
+                                  void* v_cache, const int32_t* cache_len_in,
                                   int32_t* cache_len_out, int32_t Lmax,
                                   int32_t* path, int32_t* path_len,
                                   int32_t* out_tokens, int32_t* committed_src,

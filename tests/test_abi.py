@@ -217,9 +217,9 @@ def test_kv_commit_inplace_host_validation(kw, status):
 
 
 def verify_commit(**kw):
-    args = dict(dt=1, B=2, N=8, V=64, Hkv=2, D=64, Lcap=100, par=A, tok=A, llm=A, kt=A, vt=A,
-                kc=A, vc=A, cli=A, clo=A + 0x100, Lmax=50, path=A, plen=A, outt=A, src=None,
-                st=None, ws=A, wsb=1 << 20)
+    args = dict(mode=0, dt=1, B=2, N=8, V=64, Hkv=2, D=64, Lcap=100, par=A, tok=A, llm=A,
+                ssm=None, ua=None, ub=None, kt=A, vt=A, kc=A, vc=A, cli=A, clo=A + 0x100, Lmax=50,
+                path=A, plen=A, outt=A, src=None, st=None, ws=A, wsb=1 << 20)
     args.update(kw)
     return ttv.lib().ttv_tree_verify_commit(*args.values(), None)
 
@@ -230,7 +230,11 @@ def verify_commit(**kw):
     (dict(B=0), ttv.E_SHAPE), (dict(V=0), ttv.E_SHAPE), (dict(Lmax=93), ttv.E_SHAPE),
     (dict(N=129, Lcap=1000), ttv.E_UNSUPPORTED), (dict(D=32), ttv.E_UNSUPPORTED),
     (dict(llm=MIS), ttv.E_ALIGN), (dict(kt=MIS), ttv.E_ALIGN), (dict(ws=None), ttv.E_WORKSPACE),
-    (dict(wsb=64), ttv.E_WORKSPACE), (dict(ws=MIS), ttv.E_ALIGN),
+    (dict(wsb=64), ttv.E_WORKSPACE), (dict(ws=MIS), ttv.E_ALIGN), (dict(mode=2), ttv.E_DTYPE),
+    (dict(mode=1), ttv.E_NULL),                                  # stochastic without ssm
+    (dict(mode=1, ssm=A, ua=A, ub=None), ttv.E_NULL),
+    (dict(mode=1, ssm=A, ua=A, ub=A, V=40000), ttv.E_UNSUPPORTED),  # residual past on-chip memory
+    (dict(mode=1, ssm=MIS, ua=A, ub=A), ttv.E_ALIGN),
 ])
 def test_tree_verify_commit_host_validation(kw, status):
     assert verify_commit(**kw) == status

@@ -77,8 +77,9 @@ def lib():
         L.ttv_probs_from_logits.argtypes = [_I, _I, _F, _I, _P, _P, _P]
         L.ttv_kv_commit_inplace.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P,
                                             _P, _P, _P]
-        L.ttv_tree_verify_commit.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
-                                             _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.ttv_tree_verify_commit.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
+                                             _P, _SZ, _P]
         for f in ("ttv_tree_verify_commit", "ttv_kv_commit_inplace", "ttv_tree_topology", "ttv_tree_attn", "ttv_tree_verify", "ttv_kv_commit",
                   "ttv_tree_expand", "ttv_tree_merge", "ttv_probs_from_logits"):
             getattr(L, f).restype = _I
@@ -263,14 +264,15 @@ def kv_commit(k_tree, v_tree, k_cache, v_cache, cache_len_in, path, path_len, Lm
     return cache_len_out, committed_src, dev_status
 
 
-def tree_verify_commit(parents, tokens, llm, k_tree, v_tree, k_cache, v_cache, cache_len_in,
-                       Lmax: int, cache_len_out=None, path=None, path_len=None, out_tokens=None,
+def tree_verify_commit(mode: int, parents, tokens, llm, k_tree, v_tree, k_cache, v_cache,
+                       cache_len_in, Lmax: int, ssm=None, u_accept=None, u_bonus=None,
+                       cache_len_out=None, path=None, path_len=None, out_tokens=None,
                        committed_src=None, want_src: bool = True, dev_status=None,
                        workspace=None):
-    """Greedy verification and the KV commit of its path in one pass (the
-    same results as tree_verify(GREEDY, ...) then kv_commit(...));
-    cache_len_out may be cache_len_in.  Returns (path, path_len,
-    out_tokens, cache_len_out, committed_src or None, dev_status)."""
+    """Verification (mode GREEDY or STOCHASTIC, as in tree_verify) and the KV
+    commit of its path in one pass: the same results as tree_verify(...) then
+    kv_commit(...); cache_len_out may be cache_len_in.  Returns (path,
+    path_len, out_tokens, cache_len_out, committed_src or None, dev_status)."""
     B, N = parents.shape
     V = llm.shape[2]
     _, Hkv, _, D = k_tree.shape
@@ -280,6 +282,10 @@ def tree_verify_commit(parents, tokens, llm, k_tree, v_tree, k_cache, v_cache, c
     _need(parents, "parents", torch.int32, (B, N), dev)
     _need(tokens, "tokens", torch.int32, (B, N), dev)
     _need(llm, "llm", torch.float32, (B, N, V), dev)
+    if mode == STOCHASTIC:
+        _need(ssm, "ssm", torch.float32, (B, N, V), dev)
+        _need(u_accept, "u_accept", torch.float32, (B, N), dev)
+        _need(u_bonus, "u_bonus", torch.float32, (B,), dev)
     _need(k_tree, "k_tree", dt, (B, Hkv, N, D), dev)
     _need(v_tree, "v_tree", dt, (B, Hkv, N, D), dev)
     _need(k_cache, "k_cache", dt, (B, Hkv, Lcap, D), dev)
@@ -298,15 +304,16 @@ def tree_verify_commit(parents, tokens, llm, k_tree, v_tree, k_cache, v_cache, c
         committed_src = torch.empty((B, N), dtype=torch.int32, device=dev)
     if dev_status is None:
         dev_status = torch.empty(B, dtype=torch.int32, device=dev)
-    nbytes = tree_verify_workspace_size(GREEDY, B, N, V)
+    nbytes = tree_verify_workspace_size(mode, B, N, V)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().ttv_tree_verify_commit(
-        _dt(dt), B, N, V, Hkv, D, Lcap, _ptr(parents), _ptr(tokens), _ptr(llm), _ptr(k_tree),
-        _ptr(v_tree), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len_in), _ptr(cache_len_out),
-        int(Lmax), _ptr(path), _ptr(path_len), _ptr(out_tokens), _ptr(committed_src),
-        _ptr(dev_status), _ptr(workspace), wsb, _stream(dev))
+        mode, _dt(dt), B, N, V, Hkv, D, Lcap, _ptr(parents), _ptr(tokens), _ptr(llm), _ptr(ssm),
+        _ptr(u_accept), _ptr(u_bonus), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache),
+        _ptr(cache_len_in), _ptr(cache_len_out), int(Lmax), _ptr(path), _ptr(path_len),
+        _ptr(out_tokens), _ptr(committed_src), _ptr(dev_status), _ptr(workspace), wsb,
+        _stream(dev))
     _check("ttv_tree_verify_commit", st)
     return path, path_len, out_tokens, cache_len_out, committed_src, dev_status
 

@@ -230,7 +230,7 @@ ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V
     if (V > kMssMaxVocab) return TTV_E_UNSUPPORTED;
     if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
     return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm, u_accept, u_bonus,
-                                           path, path_len, out_tokens, dev_status, s));
+                                           path, path_len, out_tokens, dev_status, CommitArgs{}, s));
   }
   const GreedyPlan p = greedy_plan(B, N, V);
   if (p.splits > kMaxGridYZ) return TTV_E_UNSUPPORTED;
@@ -262,35 +262,47 @@ ttv_status ttv_kv_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv, int32_
                                         static_cast<hipStream_t>(stream)));
 }
 
-ttv_status ttv_tree_verify_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t V, int32_t Hkv,
-                                  int32_t D, int32_t Lcap, const int32_t* parents,
-                                  const int32_t* tokens, const float* llm, const void* k_tree,
-                                  const void* v_tree, void* k_cache, void* v_cache,
-                                  const int32_t* cache_len_in, int32_t* cache_len_out,
-                                  int32_t Lmax, int32_t* path, int32_t* path_len,
-                                  int32_t* out_tokens, int32_t* committed_src,
+ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt, int32_t B, int32_t N,
+                                  int32_t V, int32_t Hkv, int32_t D, int32_t Lcap,
+                                  const int32_t* parents, const int32_t* tokens, const float* llm,
+                                  const float* ssm, const float* u_accept, const float* u_bonus,
+                                  const void* k_tree, const void* v_tree, void* k_cache,
+                                  void* v_cache, const int32_t* cache_len_in,
+                                  int32_t* cache_len_out, int32_t Lmax, int32_t* path,
+                                  int32_t* path_len, int32_t* out_tokens, int32_t* committed_src,
                                   int32_t* dev_status, void* workspace, size_t workspace_bytes,
                                   void* stream) {
+  if (mode != TTV_GREEDY && mode != TTV_STOCHASTIC) return TTV_E_DTYPE;
   if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
   if (!parents || !tokens || !llm || !k_tree || !v_tree || !k_cache || !v_cache ||
       !cache_len_in || !cache_len_out || !path || !path_len || !out_tokens)
     return TTV_E_NULL;
+  if (mode == TTV_STOCHASTIC && (!ssm || !u_accept || !u_bonus)) return TTV_E_NULL;
   if (B < 1 || N < 1 || V < 1 || Hkv < 1 || D < 1 || Lmax < 0 || Lcap < 0) return TTV_E_SHAPE;
   if (N > TTV_MAX_NODES || (D != 64 && D != 128)) return TTV_E_UNSUPPORTED;
   if ((long)B * N > 0x7fffffffL) return TTV_E_UNSUPPORTED;
   if ((long)Lmax + N > Lcap) return TTV_E_SHAPE;
-  const int elt = dt == TTV_BF16 ? 2 : 4;
-  const GreedyPlan p = greedy_plan(B, N, V);
-  if (p.splits > kMaxGridYZ) return TTV_E_UNSUPPORTED;
   if (!aligned16(llm) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(k_cache) ||
       !aligned16(v_cache))
     return TTV_E_ALIGN;
+  const int elt = dt == TTV_BF16 ? 2 : 4;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == TTV_STOCHASTIC) {
+    if (V > kMssMaxVocab) return TTV_E_UNSUPPORTED;
+    if (!aligned16(ssm)) return TTV_E_ALIGN;
+    CommitArgs cm{D * elt / 16, Hkv, Lcap, Lmax, k_tree, v_tree, k_cache, v_cache,
+                  cache_len_in, cache_len_out, committed_src};
+    return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm, u_accept, u_bonus,
+                                           path, path_len, out_tokens, dev_status, cm, s));
+  }
+  const GreedyPlan p = greedy_plan(B, N, V);
+  if (p.splits > kMaxGridYZ) return TTV_E_UNSUPPORTED;
   if (!workspace || workspace_bytes < p.ws_bytes) return TTV_E_WORKSPACE;
   if (!aligned16(workspace)) return TTV_E_ALIGN;
   return launch_status(launch_verify_greedy_commit(
       B, N, V, parents, tokens, llm, path, path_len, out_tokens, dev_status, workspace, p, elt, Hkv,
       D, Lcap, Lmax, k_tree, v_tree, k_cache, v_cache, cache_len_in, cache_len_out, committed_src,
-      static_cast<hipStream_t>(stream)));
+      s));
 }
 
 ttv_status ttv_tree_expand(int32_t B, int32_t F, int32_t V, int32_t k, const float* probs,

@@ -83,13 +83,26 @@ hipError_t launch_verify_greedy_commit(int B, int N, int V, const int32_t* paren
                                        int32_t* cache_len_out, int32_t* committed_src,
                                        hipStream_t s);
 
+// The KV commit of the accepted path, done by the verifier's own workgroup
+// (k_tree == nullptr: no commit).  row_vecs = 16-byte vectors per K/V row.
+struct CommitArgs {
+  int row_vecs, Hkv, Lcap, Lmax;
+  const void* k_tree;
+  const void* v_tree;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* cache_len_in;
+  int32_t* cache_len_out;
+  int32_t* committed_src;
+};
+
 // Largest vocabulary the stochastic verifier holds in LDS.
 constexpr int kMssMaxVocab = 36864;
 hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                              const int32_t* tokens, const float* llm, const float* ssm,
                              const float* u_accept, const float* u_bonus, int32_t* path,
                              int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
-                             hipStream_t s);
+                             const CommitArgs& cm, hipStream_t s);
 
 // ----------------------------------------------------------------- commit --
 hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,

@@ -360,6 +360,12 @@ __device__ __forceinline__ int widx(int v) { return v + 4 * (v >> 7); }
 // fx40() gives.
 __device__ __forceinline__ double fx40d(float x) { return (double)floorf(x * 0x1p40f); }
 
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
@@ -498,16 +504,25 @@ __device__ __forceinline__ double mss_residual(const float* __restrict__ q, int 
 constexpr int kMssPfChunks = 8;
 constexpr int kMssPfMaxVocab = 4 * kMssThreads * kMssPfChunks;
 
-// Every lane requests every chunk (entries past the row read its first 16
-// bytes and are never used): loads under a branch make the compiler wait for
-// all outstanding loads at their first use, which would drain the prefetch.
+// Buffer loads with one resource per chunk (base = the chunk's first entry,
+// range = the bytes of the row from there): entries past the row read as
+// zero without a branch or a clamped address, so one offset register serves
+// every chunk (loads under a branch would also make the compiler wait for
+// all outstanding loads at their first use, draining the prefetch).  The
+// row pointer must be uniform: a resource lives in scalar registers.
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access (gfx9 family)
+
 __device__ __forceinline__ void mss_issue_row(const float* __restrict__ row, int V,
                                               f32x4 (&r)[kMssPfChunks]) {
-  const int t = threadIdx.x;
+  const int off = 16 * (int)threadIdx.x;
 #pragma unroll
   for (int j = 0; j < kMssPfChunks; ++j) {
-    const int v = 4 * (t + kMssThreads * j);
-    r[j] = *reinterpret_cast<const f32x4*>(row + (v < V ? v : 0));
+    const int first = 4 * kMssThreads * j;
+    const int bytes = V > first ? 4 * (V - first) : 0;
+    const float* base = V > first ? row + first : row;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, kBufferWord3);
+    r[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
   }
 }
 
@@ -548,7 +563,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     const float* __restrict__ llm, const float* __restrict__ ssm,
     const float* __restrict__ u_accept, const float* __restrict__ u_bonus,
     int32_t* __restrict__ path, int32_t* __restrict__ path_len,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status) {
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status, CommitArgs cm) {
   extern __shared__ __attribute__((aligned(16))) float s_w[];  // residual w, widx() layout
   __shared__ int32_t s_par[kMaxNodes];
   __shared__ int32_t s_tok[kMaxNodes];
@@ -562,6 +577,11 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
   const size_t rowN = (size_t)b * N;
   const float ub = u_bonus[b];  // requested now, used by the final draw
+  // with the commit: every thread reads the prefix length here, long before
+  // the barrier that precedes the write of the new one (the arrays may alias;
+  // only this workgroup touches entry b)
+  const bool commit = cm.k_tree != nullptr;
+  const int L = commit ? cm.cache_len_in[b] : 0;
   // ---- tree, tokens and the children of every node
   if (t < N) {
     s_par[t] = parents[rowN + t];
@@ -591,9 +611,13 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       path[rowN + k] = -1;
       out_tokens[rowN + k] = -1;
     }
+    if (commit && cm.committed_src)
+      for (int k = t; k < N; k += kMssThreads) cm.committed_src[rowN + k] = -1;
+    __syncthreads();  // every thread has read cache_len_in[b]
     if (t == 0) {
       path_len[b] = 0;
       if (dev_status) dev_status[b] = (st & 1) ? TTV_E_TREE : TTV_E_SHAPE;
+      if (commit) cm.cache_len_out[b] = L;
     }
     return;
   }
@@ -626,7 +650,9 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   // memory round trip per pass.
   int u = 0;
   for (;;) {
-    uint64_t k0 = s_kids[u][0], k1 = s_kids[u][1];
+    // the same in every lane: scalar registers (children, nodes and row
+    // addresses derived from them stay scalar)
+    uint64_t k0 = uniform_u64(s_kids[u][0]), k1 = uniform_u64(s_kids[u][1]);
     if ((k0 | k1) == 0ull) {  // leaf: the bonus comes from p_u
       if constexpr (PF) {
         f32x4 ra[kMssPfChunks];
@@ -823,9 +849,33 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     path[rowN + k] = k < len ? s_path[k] : -1;
     out_tokens[rowN + k] = k + 1 < len ? s_tok[s_path[k + 1]] : (k + 1 == len ? bonus : -1);
   }
+  // ---- the commit: row L + j of every kv head takes tree node s_path[j]
+  bool ok = true;
+  if (commit) {
+    ok = L >= 0 && L <= cm.Lmax && (long)L + len <= cm.Lcap;
+    const int rv = cm.row_vecs, per = len * rv;
+    if (ok) {
+      const u32x4* kt = static_cast<const u32x4*>(cm.k_tree);
+      const u32x4* vt = static_cast<const u32x4*>(cm.v_tree);
+      u32x4* kc = static_cast<u32x4*>(cm.k_cache);
+      u32x4* vc = static_cast<u32x4*>(cm.v_cache);
+      for (int x = t; x < cm.Hkv * per; x += kMssThreads) {
+        const int h = x / per, r = x - (x / per) * per;
+        const int j = r / rv, e = r - (r / rv) * rv;
+        const size_t bh = (size_t)b * cm.Hkv + h;
+        const u32x4 kx = kt[(bh * N + s_path[j]) * rv + e];
+        const u32x4 vx = vt[(bh * N + s_path[j]) * rv + e];
+        kc[(bh * cm.Lcap + (size_t)(L + j)) * rv + e] = kx;
+        vc[(bh * cm.Lcap + (size_t)(L + j)) * rv + e] = vx;
+      }
+    }
+    if (cm.committed_src)
+      for (int k = t; k < N; k += kMssThreads) cm.committed_src[rowN + k] = (ok && k < len) ? s_path[k] : -1;
+    if (t == 0) cm.cache_len_out[b] = ok ? L + len : L;
+  }
   if (t == 0) {
     path_len[b] = len;
-    if (dev_status) dev_status[b] = TTV_OK;
+    if (dev_status) dev_status[b] = ok ? TTV_OK : TTV_E_SHAPE;
   }
 }
 
@@ -833,7 +883,7 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                              const int32_t* tokens, const float* llm, const float* ssm,
                              const float* u_accept, const float* u_bonus, int32_t* path,
                              int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
-                             hipStream_t s) {
+                             const CommitArgs& cm, hipStream_t s) {
   const size_t lds = (size_t)(V + 4 * (V >> 7) + 4) * sizeof(float);  // widx(V - 1) + 1, 16-byte padded
   const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(llm) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(ssm) & 15) == 0;
@@ -843,7 +893,7 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(B), dim3(kMssThreads), lds, s, N, V, parents, tokens, llm, ssm,
-                     u_accept, u_bonus, path, path_len, out_tokens, dev_status);
+                     u_accept, u_bonus, path, path_len, out_tokens, dev_status, cm);
   return hipGetLastError();
 }
 
