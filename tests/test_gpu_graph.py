@@ -1,5 +1,7 @@
 """The whole step captured in a HIP graph: every replay, with eager work and
-synchronisations between replays, reproduces the eager result bit for bit."""
+synchronisations between replays, reproduces the eager result bit for bit --
+with verification and commit as two calls, and as one pass
+(tree_verify_commit), in both verification modes."""
 import numpy as np
 import pytest
 import torch
@@ -11,9 +13,10 @@ from gpu_case import announce, to_dev
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("one_pass", [False, True])
 @pytest.mark.parametrize("name", ["c2", "c5"])
-def test_graph_replays_match_eager(name):
-    announce("graph replay %s" % name)
+def test_graph_replays_match_eager(name, one_pass):
+    announce("graph replay %s one_pass=%s" % (name, one_pass))
     d = synth.make(name)
     t = to_dev(d)
     mode = ttv.GREEDY if d["mode"] == "greedy" else ttv.STOCHASTIC
@@ -34,6 +37,13 @@ def test_graph_replays_match_eager(name):
     def step():
         ttv.tree_attn(t["q"], kc, vc, t["cache_len"], t["k_tree"], t["v_tree"], t["parents"],
                       d["Lmax"], scale=d["scale"], out=out, lse=lse, workspace=ws)
+        if one_pass:
+            ttv.tree_verify_commit(mode, t["parents"], t["tokens"], t["llm"], t["k_tree"],
+                                   t["v_tree"], kc, vc, t["cache_len"], d["Lmax"],
+                                   ssm=t.get("ssm"), u_accept=t.get("u_accept"),
+                                   u_bonus=t.get("u_bonus"), cache_len_out=clo, path=path,
+                                   path_len=plen, out_tokens=outt, workspace=wsv)
+            return
         ttv.tree_verify(mode, t["parents"], t["tokens"], t["llm"], t.get("ssm"),
                         t.get("u_accept"), t.get("u_bonus"), path=path, path_len=plen,
                         out_tokens=outt, workspace=wsv)
