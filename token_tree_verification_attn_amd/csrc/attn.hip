@@ -201,8 +201,17 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
       if (lane == 0 && a.lse) a.lse[((size_t)b * N + i) * a.Hq + hq] = (m[k] + __log2f(l[k])) * kLn2;
     } else {
       const size_t pr = ((size_t)bh * a.chunks + c) * R + r;
+      if constexpr (sizeof(T) == 2) {
+        // bf16 output: the chunk's normalised output in bf16 (a row that
+        // sees no key of the chunk has l = 0 and weight 0: stored as 0)
+        uint16_t* wsb = reinterpret_cast<uint16_t*>(a.ws_acc);
+        const float inv = l[k] > 0.f ? 1.f / l[k] : 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) a.ws_acc[pr * D + lane + 64 * e] = acc[k][e];
+        for (int e = 0; e < E; ++e) wsb[pr * D + lane + 64 * e] = f32_to_bf16(acc[k][e] * inv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) a.ws_acc[pr * D + lane + 64 * e] = acc[k][e];
+      }
       if (lane == 0) {
         a.ws_ml[pr * 2] = m[k];
         a.ws_ml[pr * 2 + 1] = l[k];
@@ -254,9 +263,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   for (int c = 0; c < used; ++c) {
     const size_t pr = base + (size_t)c * R;
     const float w = __builtin_amdgcn_exp2f(a.ws_ml[pr * 2] - M);
-    lsum = fmaf(a.ws_ml[pr * 2 + 1], w, lsum);
+    if constexpr (sizeof(T) == 2) {
+      // bf16 partials hold the chunk's normalised output: weight l * w
+      const uint16_t* wsb = reinterpret_cast<const uint16_t*>(a.ws_acc);
+      const float lw = a.ws_ml[pr * 2 + 1] * w;
+      lsum += lw;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = fmaf(a.ws_acc[pr * D + lane + 64 * e], w, acc[e]);
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(bf16_to_f32(wsb[pr * D + lane + 64 * e]), lw, acc[e]);
+    } else {
+      lsum = fmaf(a.ws_ml[pr * 2 + 1], w, lsum);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(a.ws_acc[pr * D + lane + 64 * e], w, acc[e]);
+    }
   }
   const float inv = 1.f / lsum;
 #pragma unroll

@@ -691,20 +691,28 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     return;
   }
 
-  // ---- split KV: write the fp32 partial; attn_combine_kernel merges them.
+  // ---- split KV: write the partial -- the chunk's normalised output in
+  // bf16 (half the bytes of fp32 sums; the combine kernel, bound by these
+  // bytes, weights it by l * 2^(m - M)) and its m and l in fp32.  A row that
+  // sees no key of the chunk has l = 0 and weight 0: stored as 0.
   // (Merging in the last-arriving workgroup would need a device-scope release
   // per workgroup, which on this chip writes back the XCD's whole L2 and was
   // measured slower than a second launch.)
   if (!has_work) return;
+  uint16_t* wsb = reinterpret_cast<uint16_t*>(a.ws_acc);
 #pragma unroll
   for (int qt = 0; qt < C::QT; ++qt) {
     const float lt = red32_sum(red16_sum(l_run[qt]));
     const int r = row_base + qt * 16 + c16;
     if (r >= R) continue;
     const size_t pr = ((size_t)bh * a.chunks + c) * R + r;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-      *reinterpret_cast<f32x4*>(a.ws_acc + pr * D + dt * 16 + g16 * 4) = oacc[qt][dt];
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const f32x4 v = oacc[qt][dt] * inv;
+      *reinterpret_cast<u32x2*>(wsb + pr * D + dt * 16 + g16 * 4) =
+          u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+    }
     if (g16 == 0) {
       a.ws_ml[pr * 2] = m_run[qt];
       a.ws_ml[pr * 2 + 1] = lt;

@@ -34,7 +34,8 @@ struct AttnArgs {
   void* out;
   float* lse;
   int32_t* dev_status;
-  float* ws_acc;   // [B*Hkv][chunks][R][D]  unnormalised fp32 partial outputs
+  float* ws_acc;   // [B*Hkv][chunks][R][D] partial outputs: fp32 sums (fp32 output), or
+                   // the normalised output as bf16 at the same index (bf16 output)
   float* ws_ml;    // [B*Hkv][chunks][R][2]  running max (log2 units) and sum
   int32_t* ws_nchunks;  // [B] balanced split: chunks request b got
   int B, N, Hq, Hkv, G, D, Lcap, Lmax, R;
