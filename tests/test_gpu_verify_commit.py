@@ -95,6 +95,9 @@ SHAPES = {
     "mss_f32_d64_v50": dict(mode="stochastic", dtype="f32", D=64, V=50),
     "mss_32000_8heads": dict(mode="stochastic", B=3, N=40, Hkv=8, Hq=16, V=32000, L=(5, 300)),
     "mss_chain128": dict(mode="stochastic", N=128, tree="chain", V=40, L=(0, 40)),
+    # empty prefixes (L = Lmax = 0): the path lands at cache rows 0..
+    "empty_prefix": dict(L=0, N=20, Hkv=4, Hq=8),
+    "mss_empty_prefix": dict(mode="stochastic", L=0, N=20, Hkv=4, Hq=8, V=64),
 }
 
 
