@@ -42,3 +42,26 @@ def test_default_bench_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert cb["unit"] == d["unit"] and isinstance(cb["sample"], str)
+
+
+@pytest.mark.parametrize("op", ["expand", "merge", "probs"])
+def test_construction_bench_lines(op):
+    """bench_expand.py's three operations each print one JSON line; the
+    HBM-bound ones carry a roofline against the 8 TB/s peak."""
+    announce("bench_expand.py --op %s --steps 8 --warmup 2" % op)
+    res = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench_expand.py"), "--op", op,
+                          "--steps", "8", "--warmup", "2", "--cpu-budget", "0.3"],
+                         capture_output=True, text=True, timeout=110, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = [ln for ln in res.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["value"] > 0 and d["n_gpus"] == 1 and d["ms_per_step"] > 0
+    assert d["config"]["workload"] == op
+    if op == "merge":
+        assert d["roofline"] is None
+    else:
+        r = d["roofline"]
+        assert r["bound"] == "hbm" and r["peak"] == 8000.0 and 0 < r["frac"] < 1
+    if op == "expand":
+        assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["value"] > 0
