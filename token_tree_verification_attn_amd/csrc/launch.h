@@ -129,7 +129,7 @@ hipError_t launch_tree_merge(int B, int S, int Ls, const int32_t* seqs, const in
                              int32_t* src, int32_t* n_out, int32_t* dev_status, hipStream_t s);
 
 // --------------------------------------------------------- probabilities --
-constexpr int kProbsMaxTopk = 512;  // the top-k bound comes from 512 per-thread maxima
+constexpr int kProbsMaxTopk = 512;  // the top-k bound takes ceil(k/16) <= 64 maxima per wave
 hipError_t launch_probs(int R, int V, float T, int topk, const float* logits, float* probs,
                         bool vec, hipStream_t s);
 
