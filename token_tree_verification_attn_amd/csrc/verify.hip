@@ -213,9 +213,11 @@ __global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
 // memory.  Reading every tree row while the scan runs, to keep only the
 // path's, measured slower: the path is short and its rows are few.
 // Distinct length arrays: one 256-thread workgroup per (request, kv head).
-// Shared ones: one 1024-thread workgroup per request copies every head, and
-// all its threads read cache_len_in[b] before the barrier that precedes the
-// write of cache_len_out[b] (no other workgroup touches entry b).
+// Shared ones: one 1024-thread workgroup per request copies every head; only
+// thread 0 reads cache_len_in[b] (the others take it from LDS after the
+// barrier), and its write of cache_len_out[b] depends on that read, so the
+// read precedes the write without any ordering between waves (no other
+// workgroup touches entry b).
 // Statuses: the verifier's if it rejects the tree, else the commit's.
 __global__ __launch_bounds__(kVerifyCommitThreads) void greedy_scan_commit_kernel(
     int N, int splits, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
@@ -226,19 +228,23 @@ __global__ __launch_bounds__(kVerifyCommitThreads) void greedy_scan_commit_kerne
     u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, const int32_t* cache_len_in,
     int32_t* cache_len_out, int32_t* __restrict__ committed_src) {
   __shared__ int32_t s_path[kMaxNodes];
-  __shared__ int s_n;
+  __shared__ int s_n, s_len;
   const int b = blockIdx.x, tid = threadIdx.x;
   const bool per_head = gridDim.y > 1;
   const int h0 = per_head ? (int)blockIdx.y : 0, nh = per_head ? 1 : Hkv;
   const bool first = blockIdx.y == 0;  // writes the request's verifier outputs and lengths
-  const int L = cache_len_in[b];
   if (tid < kWave) {
+    const int Lr = tid == 0 ? cache_len_in[b] : 0;  // requested with the scan's loads
     const int n = greedy_scan_wave(b, N, splits, parents, tokens, ws_val, ws_idx, path, path_len,
                                    out_tokens, nullptr, first, s_path);
-    if (tid == 0) s_n = n;
+    if (tid == 0) {
+      s_n = n;
+      s_len = Lr;
+    }
   }
   __syncthreads();
   const int n = s_n;  // 0: malformed tree
+  const int L = s_len;
   const bool shape_ok = L >= 0 && L <= Lmax && (long)L + n <= Lcap;
   const bool ok = n > 0 && shape_ok;
   if (ok) {
