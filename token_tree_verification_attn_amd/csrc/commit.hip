@@ -9,8 +9,9 @@
 // apart, and spread over CUs their copies and address translations proceed
 // in parallel (32 heads x 12 rows: 2.5 us against 3.6 us for one workgroup).
 // When cache_len_out is cache_len_in, one workgroup of 1024 threads per
-// request copies every head, which keeps cache_len_out[b] = L + n ordered
-// after every read of cache_len_in[b].
+// request copies every head, so entry b is touched by one workgroup only;
+// in it thread 0 alone reads cache_len_in[b] and writes cache_len_out[b] =
+// L + n, which depends on that read.
 #include "launch.h"
 #include "ttv_common.h"
 
@@ -23,26 +24,29 @@ constexpr int kCommitIlp = 4;
 __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
     int row_bytes, int N, int Hkv, int Lcap, int Lmax, const u32x4* __restrict__ k_tree,
     const u32x4* __restrict__ v_tree, u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
-    const int32_t* __restrict__ cache_len_in, int32_t* cache_len_out,
+    const int32_t* cache_len_in, int32_t* cache_len_out,
     const int32_t* __restrict__ path, const int32_t* __restrict__ path_len,
     int32_t* __restrict__ committed_src, int32_t* __restrict__ dev_status) {
   __shared__ int32_t s_path[kMaxNodes];
-  __shared__ int s_bad_node;
+  __shared__ int s_bad_node, s_len;
   const int b = blockIdx.x;
   // gridDim.y = Hkv: this workgroup copies head blockIdx.y only; else all.
   // cache_len_out may alias cache_len_in only in the second case: then only
-  // this workgroup touches entry b, and every thread reads it before the
-  // barrier that precedes the write.
+  // this workgroup touches entry b; thread 0 alone reads it (the others take
+  // it from LDS) and its write of the new length depends on that read.
   const bool per_head = gridDim.y > 1;
   const int h0 = per_head ? (int)blockIdx.y : 0, nh = per_head ? 1 : Hkv;
   const bool first = blockIdx.y == 0;  // writes the request's lengths and sources
   // lengths and the whole path row are requested together (one round trip)
-  const int L = cache_len_in[b];
   const int n = path_len[b];
   const int pj = threadIdx.x < N ? path[(size_t)b * N + threadIdx.x] : -1;
-  const bool shape_ok = L >= 0 && L <= Lmax && n >= 0 && n <= N && L + n <= Lcap;
-  if (threadIdx.x == 0) s_bad_node = 0;
+  if (threadIdx.x == 0) {
+    s_bad_node = 0;
+    s_len = cache_len_in[b];
+  }
   __syncthreads();
+  const int L = s_len;
+  const bool shape_ok = L >= 0 && L <= Lmax && n >= 0 && n <= N && L + n <= Lcap;
   if (threadIdx.x < N) {
     s_path[threadIdx.x] = pj;
     if (shape_ok && threadIdx.x < n && (pj < 0 || pj >= N)) s_bad_node = 1;  // same value from every writer
@@ -117,21 +121,26 @@ hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,
 // cache_len_in.
 __global__ __launch_bounds__(kCommitHeadThreads) void kv_commit_inplace_kernel(
     int row_bytes, int N, int Hkv, int Lcap, int Lmax, u32x4* __restrict__ k_cache,
-    u32x4* __restrict__ v_cache, const int32_t* __restrict__ cache_len_in, int32_t* cache_len_out,
+    u32x4* __restrict__ v_cache, const int32_t* cache_len_in, int32_t* cache_len_out,
     const int32_t* __restrict__ path, const int32_t* __restrict__ path_len,
     int32_t* __restrict__ committed_src, int32_t* __restrict__ dev_status) {
   extern __shared__ u32x4 s_rows[];  // [K | V][N rows][vec]
   __shared__ int32_t s_path[kMaxNodes];
-  __shared__ int s_bad_node;
+  __shared__ int s_bad_node, s_len;
   const int b = blockIdx.x;
   const bool per_head = gridDim.y > 1;
   const int h0 = per_head ? (int)blockIdx.y : 0, nh = per_head ? 1 : Hkv;
   const bool first = blockIdx.y == 0;
-  const int L = cache_len_in[b];
+  // thread 0 alone reads the prefix length (its write of the new one, which
+  // may alias it, depends on that read); the others take it from LDS
   const int n = path_len[b];
-  const bool shape_ok = L >= 0 && L <= Lmax && n >= 0 && n <= N && (long)L + N <= Lcap;
-  if (threadIdx.x == 0) s_bad_node = 0;
+  if (threadIdx.x == 0) {
+    s_bad_node = 0;
+    s_len = cache_len_in[b];
+  }
   __syncthreads();
+  const int L = s_len;
+  const bool shape_ok = L >= 0 && L <= Lmax && n >= 0 && n <= N && (long)L + N <= Lcap;
   for (int j = threadIdx.x; j < N; j += blockDim.x) {
     const int pj = path[(size_t)b * N + j];
     s_path[j] = pj;
