@@ -578,16 +578,15 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   __shared__ unsigned long long s_kids[kMaxNodes][2];
   __shared__ uint64_t s_first_ok[2];
   __shared__ double s_redd[kMssThreads / 64];
-  __shared__ int s_status, s_pick;
+  __shared__ int s_status, s_pick, s_len;
 
   const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
   const size_t rowN = (size_t)b * N;
   const float ub = u_bonus[b];  // requested now, used by the final draw
-  // with the commit: every thread reads the prefix length here, long before
-  // the barrier that precedes the write of the new one (the arrays may alias;
-  // only this workgroup touches entry b)
+  // with the commit: thread 0 alone reads the prefix length (the others take
+  // it from LDS); its write of the new one, which may alias it, depends on
+  // that read, and only this workgroup touches entry b
   const bool commit = cm.k_tree != nullptr;
-  const int L = commit ? cm.cache_len_in[b] : 0;
   // ---- tree, tokens and the children of every node
   if (t < N) {
     s_par[t] = parents[rowN + t];
@@ -595,8 +594,12 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     s_kids[t][0] = 0ull;
     s_kids[t][1] = 0ull;
   }
-  if (t == 0) s_status = 0;
+  if (t == 0) {
+    s_status = 0;
+    s_len = commit ? cm.cache_len_in[b] : 0;
+  }
   __syncthreads();
+  const int L = s_len;
   if (wave < 2) {  // nodes 0..127: tree validity and token range
     bool bad_tree = false, bad_tok = false;
     if (t < N) {
