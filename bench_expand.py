@@ -154,11 +154,14 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--B", type=int, default=16)
-    ap.add_argument("--F", type=int, default=16)
+    ap.add_argument("--F", type=int, default=None,
+                    help="frontier rows per request (expand: 16) or rows per request (probs: 64)")
     ap.add_argument("--V", type=int, default=32000)
     ap.add_argument("--k", type=int, default=4)
     ap.add_argument("--cpu-budget", type=float, default=3.0)
     args = ap.parse_args()
+    if args.F is None:
+        args.F = 64 if args.op == "probs" else 16
     if args.op == "merge":
         return bench_merge(args)
     if args.op == "probs":
