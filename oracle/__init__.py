@@ -58,9 +58,15 @@ def _bind(lib):
     lib.orc_tree_merge.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P]
     lib.orc_probs_from_logits.argtypes = [I, I, ctypes.c_double, I, P, P]
     lib.orc_kv_commit_inplace.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]
+    U64 = ctypes.c_uint64
+    lib.orc_philox4x64_10.argtypes = [P, P, P]
+    lib.orc_verify_mss_seeded.argtypes = [I, I, I, P, P, P, P, U64, U64, P, P, P, P]
+    lib.orc_set_threads.argtypes = [I]
+    lib.orc_max_threads.restype = I
     for f in (lib.orc_kv_commit_inplace, lib.orc_topology, lib.orc_tree_attn_rows, lib.orc_verify_greedy,
               lib.orc_verify_mss, lib.orc_kv_commit, lib.orc_tree_expand, lib.orc_tree_merge,
-              lib.orc_probs_from_logits):
+              lib.orc_probs_from_logits, lib.orc_philox4x64_10, lib.orc_verify_mss_seeded,
+              lib.orc_set_threads):
         f.restype = None
     return lib
 
@@ -207,6 +213,54 @@ def verify_mss(parents, tokens, llm, ssm, u_accept, u_bonus):
                            outt.ctypes.data_as(ctypes.c_void_p),
                            st.ctypes.data_as(ctypes.c_void_p))
     return path, plen, outt, st
+
+
+def philox4x64_10(counter, key):
+    """Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11, "Parallel random
+    numbers: as easy as 1, 2, 3"): the four 64-bit output words for a counter
+    of four 64-bit words (word 0 least significant) and a key of two."""
+    c = np.ascontiguousarray(np.asarray(counter, dtype=np.uint64).reshape(4))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint64).reshape(2))
+    out = np.empty(4, np.uint64)
+    P = ctypes.c_void_p
+    _load().orc_philox4x64_10(c.ctypes.data_as(P), k.ctypes.data_as(P), out.ctypes.data_as(P))
+    return out
+
+
+def verify_mss_seeded(parents, tokens, llm, ssm, seed, step):
+    """[SI] §4 "Token Verification": multi-step speculative sampling with the
+    uniforms drawn from Philox4x64-10, key (seed, 0): the ratio test of the
+    j-th child (ascending node index) of node u in request b takes counter
+    (j, u, b, step), the final draw at u counter (2^63, u, b, step), each
+    using the 24 high bits of output word 0.  Returns (path, path_len,
+    out_tokens, status) as verify_mss."""
+    par, pp = _c(parents, np.int32)
+    tok, tp = _c(tokens, np.int32)
+    p, ppr = _c(llm, np.float32)
+    q, qpr = _c(ssm, np.float32)
+    B, N = par.shape
+    V = p.shape[2]
+    assert p.shape == (B, N, V) and q.shape == p.shape and tok.shape == (B, N)
+    path = np.empty((B, N), np.int32)
+    plen = np.empty(B, np.int32)
+    outt = np.empty((B, N), np.int32)
+    st = np.empty(B, np.int32)
+    P = ctypes.c_void_p
+    _load().orc_verify_mss_seeded(B, N, V, pp, tp, ppr, qpr, int(seed) & (2**64 - 1),
+                                  int(step) & (2**64 - 1), path.ctypes.data_as(P),
+                                  plen.ctypes.data_as(P), outt.ctypes.data_as(P),
+                                  st.ctypes.data_as(P))
+    return path, plen, outt, st
+
+
+def set_threads(n):
+    """Threads the oracle's parallel loops use from now on."""
+    _load().orc_set_threads(int(n))
+
+
+def max_threads():
+    """Threads the oracle's parallel loops use."""
+    return int(_load().orc_max_threads())
 
 
 def kv_commit(k_tree, v_tree, k_cache, v_cache, cache_len_in, path, path_len, Lmax):

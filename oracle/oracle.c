@@ -20,6 +20,7 @@
  * (-ffp-contract=off: no multiply-add is fused unless written as fmaf).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -215,12 +216,61 @@ void orc_verify_greedy(int B, int N, int V, const int32_t* parents,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Counter-based random numbers: Philox4x64-10 as published by Salmon,        */
+/* Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3"       */
+/* (SC'11).  A 256-bit counter c (four 64-bit words, word 0 least            */
+/* significant) and a 128-bit key k give four 64-bit outputs after ten       */
+/* rounds.  One round multiplies c0 and c2 by the paper's two 64-bit         */
+/* multipliers, keeps the high and low halves of each 128-bit product, and    */
+/* permutes:  c' = (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1,       */
+/* lo(M0*c0)).  Between rounds the key is bumped by the paper's two Weyl      */
+/* constants (the golden ratio and sqrt(3) - 1 in 64-bit fixed point).        */
+/* ------------------------------------------------------------------------ */
+static void mul64_hilo(uint64_t a, uint64_t b, uint64_t* hi, uint64_t* lo) {
+  const unsigned __int128 p = (unsigned __int128)a * b;
+  *hi = (uint64_t)(p >> 64);
+  *lo = (uint64_t)p;
+}
+
+void orc_philox4x64_10(const uint64_t* ctr, const uint64_t* key, uint64_t* out) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint64_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) { k0 += W0; k1 += W1; }
+    uint64_t hi0, lo0, hi1, lo1;
+    mul64_hilo(M0, c0, &hi0, &lo0);
+    mul64_hilo(M1, c2, &hi1, &lo1);
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The 24 high bits of output word 0 for key (seed, 0) and counter
+ * (j, u, b, step): the ratio test of the j-th child (ascending node index,
+ * j = 0, 1, ..) of node u, or the final draw at u when j = 2^63. */
+static uint64_t philox_bits24(uint64_t seed, uint64_t step, uint64_t j, int u, int b) {
+  const uint64_t ctr[4] = {j, (uint64_t)u, (uint64_t)b, step};
+  const uint64_t key[2] = {seed, 0};
+  uint64_t out[4];
+  orc_philox4x64_10(ctr, key, out);
+  return out[0] >> 40;
+}
+#define ORC_BONUS_ORDINAL 0x8000000000000000ull
+
+/* ------------------------------------------------------------------------ */
 /* Stochastic verification: multi-step speculative sampling, [SI] §4 "Token   */
 /* Verification" (verifies across branches and keeps the LLM's distribution). */
 /* The page states the guarantee, not the arithmetic; the arithmetic below is  */
 /* this library's fixed reading of it (residual w with mass s, children in     */
-/* ascending node index, one caller-supplied uniform per tested child and one  */
-/* per request for the final sample, exact integer sums in 2^-40 units).       */
+/* ascending node index, one uniform per tested child and one per request     */
+/* for the final sample, exact integer sums in 2^-40 units).  The uniforms    */
+/* are either given (u_accept[b,c] for the test of child c, u_bonus[b]) or    */
+/* drawn from Philox4x64-10 with key (seed, 0): the test of the j-th child of */
+/* u uses counter (j, u, b, step), the final draw at u counter (2^63, u, b,   */
+/* step); r = (out0 >> 40) * 2^-24 and R = out0 >> 40.                       */
 /* ------------------------------------------------------------------------ */
 static uint64_t fx(float x) { return (uint64_t)((double)x * 1099511627776.0); }
 
@@ -230,8 +280,8 @@ static float mass(const float* w, int V) {
   return (float)((double)S * (1.0 / 1099511627776.0));
 }
 
-/* Inverse-CDF draw from the unnormalised w with uniform ub in [0,1). */
-static int sample_from(const float* w, int V, float ub) {
+/* Inverse-CDF draw from the unnormalised w with the 24-bit integer R. */
+static int sample_from(const float* w, int V, uint64_t R) {
   uint64_t S = 0;
   for (int v = 0; v < V; ++v) S += fx(w[v]);
   if (S == 0) {
@@ -240,7 +290,6 @@ static int sample_from(const float* w, int V, float ub) {
       if (w[v] > w[best]) best = v;
     return best;
   }
-  uint64_t R = (uint64_t)(ub * 16777216.0f); /* exact: scaling by 2^24 */
   uint64_t hi = S >> 24, lo = S & 0xFFFFFFu;
   uint64_t T = R * hi + ((R * lo) >> 24); /* floor(R*S / 2^24), no overflow */
   uint64_t c = 0;
@@ -251,66 +300,88 @@ static int sample_from(const float* w, int V, float ub) {
   return V - 1; /* unreachable: T < S */
 }
 
+/* One request's walk; the uniforms come from u_accept/u_bonus when they are
+ * given (seeded == 0), else from Philox (seed, step). */
+static void mss_request(int b, int N, int V, const int32_t* par, const int32_t* tok,
+                        const float* llm, const float* ssm, const float* u_accept,
+                        const float* u_bonus, int seeded, uint64_t seed, uint64_t step,
+                        int32_t* pb, int32_t* ob, int32_t* path_len, int32_t* status) {
+  for (int k = 0; k < N; ++k) { pb[k] = -1; ob[k] = -1; }
+  if (!tree_is_valid(N, par)) {
+    path_len[b] = 0;
+    status[b] = ORC_E_TREE;
+    return;
+  }
+  int tokens_ok = 1; /* every drafted token must index the vocabulary */
+  for (int c = 1; c < N; ++c)
+    if (tok[c] < 0 || tok[c] >= V) tokens_ok = 0;
+  if (!tokens_ok) {
+    path_len[b] = 0;
+    status[b] = ORC_E_SHAPE;
+    return;
+  }
+  float* w = (float*)malloc(sizeof(float) * (size_t)V);
+  int u = 0;
+  for (;;) {
+    const float* p_u = llm + ((size_t)b * N + u) * V;
+    memcpy(w, p_u, sizeof(float) * (size_t)V);
+    float s = 1.0f;
+    int next = -1;
+    uint64_t j = 0; /* attempt ordinal at u */
+    for (int c = u + 1; c < N; ++c) { /* children of u, ascending index */
+      if (par[c] != u) continue;
+      const float* qc = ssm + ((size_t)b * N + c) * V;
+      const int x = tok[c];
+      const float r = seeded ? (float)philox_bits24(seed, step, j, u, b) * 0x1p-24f
+                             : u_accept[(size_t)b * N + c];
+      ++j;
+      const float lhs = (r * qc[x]) * s;
+      if (lhs < w[x]) { next = c; break; } /* accepted */
+      /* rejected: w <- max(w - s*q, 0), s <- its mass */
+      for (int v = 0; v < V; ++v) {
+        float d = fmaf(-s, qc[v], w[v]);
+        w[v] = d > 0.0f ? d : 0.0f;
+      }
+      s = mass(w, V);
+      if (s == 0.0f) { /* empty residual: stop, sample from p_u */
+        memcpy(w, p_u, sizeof(float) * (size_t)V);
+        break;
+      }
+    }
+    if (next < 0) break;
+    u = next;
+  }
+  const uint64_t R = seeded ? philox_bits24(seed, step, ORC_BONUS_ORDINAL, u, b)
+                            : (uint64_t)(u_bonus[b] * 16777216.0f); /* exact: scaling by 2^24 */
+  const int bonus = sample_from(w, V, R);
+  const int len = write_path(N, par, u, pb);
+  for (int k = 0; k + 1 < len; ++k) ob[k] = tok[pb[k + 1]];
+  ob[len - 1] = bonus;
+  path_len[b] = len;
+  status[b] = ORC_OK;
+  free(w);
+}
+
 void orc_verify_mss(int B, int N, int V, const int32_t* parents,
                     const int32_t* tokens, const float* llm, const float* ssm,
                     const float* u_accept, const float* u_bonus, int32_t* path,
                     int32_t* path_len, int32_t* out_tokens, int32_t* status) {
 #pragma omp parallel for schedule(dynamic, 1)
-  for (int b = 0; b < B; ++b) {
-    const int32_t* par = parents + (size_t)b * N;
-    const int32_t* tok = tokens + (size_t)b * N;
-    int32_t* pb = path + (size_t)b * N;
-    int32_t* ob = out_tokens + (size_t)b * N;
-    for (int k = 0; k < N; ++k) { pb[k] = -1; ob[k] = -1; }
-    if (!tree_is_valid(N, par)) {
-      path_len[b] = 0;
-      status[b] = ORC_E_TREE;
-      continue;
-    }
-    int tokens_ok = 1; /* every drafted token must index the vocabulary */
-    for (int c = 1; c < N; ++c)
-      if (tok[c] < 0 || tok[c] >= V) tokens_ok = 0;
-    if (!tokens_ok) {
-      path_len[b] = 0;
-      status[b] = ORC_E_SHAPE;
-      continue;
-    }
-    float* w = (float*)malloc(sizeof(float) * (size_t)V);
-    int u = 0;
-    for (;;) {
-      const float* p_u = llm + ((size_t)b * N + u) * V;
-      memcpy(w, p_u, sizeof(float) * (size_t)V);
-      float s = 1.0f;
-      int next = -1;
-      for (int c = u + 1; c < N; ++c) { /* children of u, ascending index */
-        if (par[c] != u) continue;
-        const float* qc = ssm + ((size_t)b * N + c) * V;
-        const int x = tok[c];
-        const float r = u_accept[(size_t)b * N + c];
-        const float lhs = (r * qc[x]) * s;
-        if (lhs < w[x]) { next = c; break; } /* accepted */
-        /* rejected: w <- max(w - s*q, 0), s <- its mass */
-        for (int v = 0; v < V; ++v) {
-          float d = fmaf(-s, qc[v], w[v]);
-          w[v] = d > 0.0f ? d : 0.0f;
-        }
-        s = mass(w, V);
-        if (s == 0.0f) { /* empty residual: stop, sample from p_u */
-          memcpy(w, p_u, sizeof(float) * (size_t)V);
-          break;
-        }
-      }
-      if (next < 0) break;
-      u = next;
-    }
-    const int bonus = sample_from(w, V, u_bonus[b]);
-    const int len = write_path(N, par, u, pb);
-    for (int k = 0; k + 1 < len; ++k) ob[k] = tok[pb[k + 1]];
-    ob[len - 1] = bonus;
-    path_len[b] = len;
-    status[b] = ORC_OK;
-    free(w);
-  }
+  for (int b = 0; b < B; ++b)
+    mss_request(b, N, V, parents + (size_t)b * N, tokens + (size_t)b * N, llm, ssm, u_accept,
+                u_bonus, 0, 0, 0, path + (size_t)b * N, out_tokens + (size_t)b * N, path_len,
+                status);
+}
+
+void orc_verify_mss_seeded(int B, int N, int V, const int32_t* parents,
+                           const int32_t* tokens, const float* llm, const float* ssm,
+                           uint64_t seed, uint64_t step, int32_t* path, int32_t* path_len,
+                           int32_t* out_tokens, int32_t* status) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int b = 0; b < B; ++b)
+    mss_request(b, N, V, parents + (size_t)b * N, tokens + (size_t)b * N, llm, ssm, NULL, NULL,
+                1, seed, step, path + (size_t)b * N, out_tokens + (size_t)b * N, path_len,
+                status);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -576,3 +647,8 @@ void orc_kv_commit_inplace(int B, int N, int Hkv, int D, int elt, int Lcap, int 
   free(tk);
   free(tv);
 }
+
+/* Threads of the parallel loops above (the CPU baseline runs the oracle on all
+ * host cores and on one). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }

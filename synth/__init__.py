@@ -23,8 +23,10 @@ token tree construction"):
         D 128, bf16, prefix 32768, vocab 32000, greedy as c2.
     c5  16 requests, 64-node random trees, 32/8 heads, D 128, bf16, prefix
         2048, vocab 32000, stochastic: llm and ssm rows are softmax(z / 0.8),
-        z ~ N(0, 2) per row, each node's token drawn from its ssm row; one
-        Philox uniform per node and one per request.
+        z ~ N(0, 2) per row, each node's token drawn from its ssm row; the
+        verifier's uniforms come from Philox4x64-10 with seed 1005, step 0
+        (explicit uniforms -- one per node and one per request, drawn from
+        numpy's Philox stream -- for the explicit-uniform call).
 
 Every array has its own seeded stream: ``SeedSequence([seed, stream_id])``
 (seed = 1000 + k for workload ck).  Q/K/V are N(0, 1), rounded to bf16 (round
@@ -327,4 +329,7 @@ def make(s: Union[str, Spec], parents: Optional[np.ndarray] = None,
             out["llm"], out["ssm"] = llm, ssm
             out["u_accept"] = uni.random((B, N), dtype=np.float32)
             out["u_bonus"] = uni.random(B, dtype=np.float32)
+            # the seeded verifier draws its own uniforms (Philox4x64-10, key
+            # (seed, 0)); the explicit ones above serve the explicit-uniform call
+            out["seed"], out["step"] = s.seed, 0
     return out

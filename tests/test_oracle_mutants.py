@@ -17,6 +17,7 @@ import test_oracle_merge as MG
 import test_oracle_probs as PR
 import test_oracle_greedy as G
 import test_oracle_mss as M
+import test_oracle_philox as PH
 import test_oracle_topology as T
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
@@ -53,12 +54,27 @@ MUTANTS = [
     ("mss_mass_not_updated", "s = mass(w, V);", "s = 1.0f;",
      M.test_second_child_tested_against_residual),
     ("mss_no_fallback_on_empty_residual",
-     "memcpy(w, p_u, sizeof(float) * (size_t)V);\n          break;", "break;",
+     "memcpy(w, p_u, sizeof(float) * (size_t)V);\n        break;", "break;",
      M.test_half_q_empties_residual_and_falls_back_to_p),
     ("mss_cdf_not_strict", "if (c > T) return v;", "if (c >= T) return v;",
      M.test_inverse_cdf_end_points),
     ("mss_accept_not_strict", "if (lhs < w[x]) { next = c; break; }",
      "if (lhs <= w[x]) { next = c; break; }", M.test_inverse_cdf_end_points),
+    ("philox_one_key_word_bumped", "if (round > 0) { k0 += W0; k1 += W1; }",
+     "if (round > 0) { k0 += W0; }", PH.test_matches_numpy_philox),
+    ("philox_words_swapped", "n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;",
+     "n0 = hi1 ^ c3 ^ k0, n1 = lo1, n2 = hi0 ^ c1 ^ k1, n3 = lo0;", PH.test_matches_numpy_philox),
+    ("philox_nine_rounds", "for (int round = 0; round < 10; ++round) {",
+     "for (int round = 0; round < 9; ++round) {", PH.test_matches_numpy_philox),
+    ("mss_counter_words_swapped", "const uint64_t ctr[4] = {j, (uint64_t)u, (uint64_t)b, step};",
+     "const uint64_t ctr[4] = {(uint64_t)u, j, (uint64_t)b, step};",
+     lambda: PH.test_seeded_walk_uses_documented_counters(1005, 0, {})),
+    ("mss_attempt_ordinal_not_advanced", "      ++j;\n", "\n",
+     lambda: PH.test_seeded_walk_uses_documented_counters(3, 2, dict(
+         B=64, N=9, tree="star", V=8, prob_sigma=3.0))),
+    ("mss_bonus_counter", "#define ORC_BONUS_ORDINAL 0x8000000000000000ull",
+     "#define ORC_BONUS_ORDINAL 0x4000000000000000ull",
+     lambda: PH.test_seeded_walk_uses_documented_counters(1005, 0, {})),
     ("expand_ties_to_highest", "(best < 0 || row[v] > row[best])", "(best < 0 || row[v] >= row[best])",
      lambda: [E.test_topk_matches_stable_argsort_with_ties(s) for s in range(5)]),
     ("expand_token_reused", "taken[best] = 1;", "taken[best] = 0;",
