@@ -1,6 +1,6 @@
 """Benchmark of the tree-verification step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4]
 
 A step is one pass of the whole path over one batch of synthetic input:
 tree_attn (prefix + tree-masked attention of every node) -> tree_verify ->
@@ -9,17 +9,28 @@ Verification and commit run as one pass (tree_verify_commit: greedy = argmax
 partials, then one launch that scans each tree and copies its accepted rows;
 stochastic = the walk's workgroup copies them); --unfused times the two
 separate calls instead.
-The default workload is c2, the LLaMA-7B-shaped layer (1 request, 64-node
-expansion tree, 32 heads of 128, prefix 512, vocabulary 32000, greedy).
+The default workload is c4, the largest one that fits one GPU: the
+long-context 70B-shaped layer (4 requests, 128-node merged trees, 64 query /
+8 kv heads of 128, prefix 32768, vocabulary 32000, greedy).  Its attention
+is bound by the matrix cores (about 1020 flop per KV byte against a bf16
+ridge of about 312), so its roofline is reported against the MFMA peak, with
+the KV GB/s beside it.
 Inputs are resident in HBM before timing starts; each step reads a different
 copy of them (enough copies to exceed twice the 256 MB last-level cache), so
 the prefix KV and logits come from HBM, not from cache.
 
+Exactly --steps steps are timed, each between two HIP events on the launch
+stream (each step one HIP-graph replay; a short spin kernel ahead of them
+lets the host enqueue every step before the first one runs, so the steps run
+back to back).  ms_per_step is the median step time, ms_per_step_mean the
+mean over the same steps.
+
 Prints one JSON line: value = verified tree-node queries per second (B*N per
-step); roofline = tree_attn's algorithmic KV bytes per launch over its average
-launch time (HIP events on the launch stream); cpu_baseline = the CPU oracle
-timed on a bounded sample of the same workload (the oracle is test
-infrastructure; it is imported only here, for that leg).
+step at the median step time); roofline = tree_attn's algorithmic work per
+launch (flops for c4, KV bytes otherwise) over its average launch time (HIP
+events on the launch stream); cpu_baseline = the CPU oracle timed on a
+bounded sample of the same workload on all host cores and on one (the
+oracle is test infrastructure; it is imported only here, for that leg).
 """
 from __future__ import annotations
 
@@ -27,6 +38,8 @@ import argparse
 import hashlib
 import json
 import os
+import platform
+import subprocess
 import sys
 import time
 
@@ -63,8 +76,6 @@ class Inputs:
         self.parents, self.tokens, self.cache_len = f("parents"), f("tokens"), f("cache_len")
         self.llm = f("llm")
         self.ssm = f("ssm") if "ssm" in d else None
-        self.u_accept = f("u_accept") if "u_accept" in d else None
-        self.u_bonus = f("u_bonus") if "u_bonus" in d else None
         B, N, Hq, D = self.q.shape
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
@@ -94,6 +105,9 @@ class Step:
         self.ws_ver = torch.empty(max(1, ttv.tree_verify_workspace_size(
             self.mode, B, N, d["V"])), dtype=torch.uint8, device=dev)
         self.fused = fuse  # one pass: verification + commit
+        # stochastic draws: the workload's seed, step 0 (every timed step
+        # verifies the same batch, so it draws the same uniforms)
+        self.seed, self.step = d.get("seed", 0), d.get("step", 0)
 
     def attn(self, c):
         ttv.tree_attn(c.q, c.k_cache, c.v_cache, c.cache_len, c.k_tree, c.v_tree, c.parents,
@@ -101,9 +115,9 @@ class Step:
                       dev_status=c.st, workspace=self.ws_attn)
 
     def verify(self, c):
-        ttv.tree_verify(self.mode, c.parents, c.tokens, c.llm, c.ssm, c.u_accept, c.u_bonus,
-                        path=c.path, path_len=c.plen, out_tokens=c.outt, dev_status=c.st,
-                        workspace=self.ws_ver)
+        ttv.tree_verify(self.mode, c.parents, c.tokens, c.llm, c.ssm, seed=self.seed,
+                        step=self.step, path=c.path, path_len=c.plen, out_tokens=c.outt,
+                        dev_status=c.st, workspace=self.ws_ver)
 
     def commit(self, c):
         # lengths go to a separate array, so repeated steps rewrite the same rows
@@ -114,32 +128,33 @@ class Step:
     def verify_commit(self, c):
         ttv.tree_verify_commit(self.mode, c.parents, c.tokens, c.llm, c.k_tree, c.v_tree,
                                c.k_cache, c.v_cache, c.cache_len, self.d["Lmax"], ssm=c.ssm,
-                               u_accept=c.u_accept, u_bonus=c.u_bonus, cache_len_out=c.len_out,
+                               seed=self.seed, step=self.step, cache_len_out=c.len_out,
                                path=c.path, path_len=c.plen, out_tokens=c.outt,
                                committed_src=c.src, dev_status=c.st, workspace=self.ws_ver)
 
-    def __call__(self, i):
-        c = self.copies[i % len(self.copies)]
-        self.attn(c)
-        if self.fused:
-            self.verify_commit(c)
-        else:
-            self.verify(c)
-            self.commit(c)
 
-
-def timed(fn, n, stream):
-    """Average ms per call of fn(i), i = 0..n-1, from HIP events recorded on
-    the launch stream around the whole loop."""
+def timed_steps(fns, n, stream):
+    """Run fns[i % len(fns)]() for i = 0..n-1 on `stream`, each between two
+    HIP events recorded on that stream; returns the n durations in ms.  A
+    spin kernel enqueued first keeps the GPU busy while the host enqueues
+    every step, so the steps run back to back as they would in a serving
+    loop, not paced by the host."""
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(2e7))  # ~10 ms of clock cycles: the queue fills meanwhile
+    ev[0].record(stream)
     for i in range(n):
-        fn(i)
-    e1.record(stream)
+        fns[i % len(fns)]()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def summary(ms):
+    a = np.asarray(ms, np.float64)
+    return {"median": float(np.median(a)), "mean": float(a.mean()),
+            "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90))}
 
 
 def capture(fn, dev):
@@ -182,9 +197,11 @@ def attn_work(d):
 
 
 def source_hash():
-    """Hash of the attention kernel sources a stored counter profile belongs to."""
+    """Hash of the attention kernels' own sources, which a stored counter
+    profile belongs to (the host-side entry points may change without
+    changing what the kernels read and write)."""
     h = hashlib.sha256()
-    for f in ("attn.hip", "attn_mfma.hip", "ttv_common.h", "launch.h", "api.cpp"):
+    for f in ("attn.hip", "attn_mfma.hip", "attn_plan.h", "ttv_common.h"):
         h.update(open(os.path.join(ROOT, "token_tree_verification_attn_amd", "csrc", f),
                       "rb").read())
     return h.hexdigest()[:16]
@@ -202,23 +219,37 @@ def stored_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(d, budget_s):
-    """The CPU oracle on a bounded sample of the same workload: verification
-    of the whole batch, the commit of request 0 (scaled by B), and attention
-    on a uniform sample of query rows sized to the time budget (all rows when
-    they fit), the whole repeated until about a quarter of the budget has
-    passed; reported as tree-node queries/s of one full step."""
-    import oracle
+def host_cpu():
+    """The host's logical CPU count and model name."""
+    model = platform.processor() or "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.lower().startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return os.cpu_count() or 1, model
+
+
+def cpu_step(d, budget_s, oracle):
+    """Seconds of one full step of the oracle on the current thread count:
+    verification of the whole batch, the commit of request 0 (time x B), and
+    attention on a uniform sample of query rows sized to the time budget (all
+    rows when they fit, time scaled to all rows), the whole repeated until
+    about a quarter of the budget has passed.  Returns (step seconds,
+    description of the sample)."""
     B, N, Hq = d["B"], d["N"], d["Hq"]
     rows_all = oracle.all_rows(B, N, Hq)
     rng = np.random.default_rng(0)
     attn = lambda rows: oracle.tree_attn_rows(d["q"], d["k_cache"], d["v_cache"], d["cache_len"],
                                               d["k_tree"], d["v_tree"], d["parents"], d["scale"],
                                               rows)
+    probe = min(4 * oracle.max_threads(), len(rows_all))
     t0 = time.perf_counter()
-    attn(rows_all[rng.choice(len(rows_all), size=min(16, len(rows_all)), replace=False)])
-    per_row = (time.perf_counter() - t0) / min(16, len(rows_all))
-    n = int(min(len(rows_all), max(16, 0.6 * budget_s / per_row)))
+    attn(rows_all[rng.choice(len(rows_all), size=probe, replace=False)])
+    per_row = (time.perf_counter() - t0) / probe
+    n = int(min(len(rows_all), max(probe, 0.6 * budget_s / per_row)))
     sample = rows_all if n >= len(rows_all) else \
         rows_all[rng.choice(len(rows_all), size=n, replace=False)]
     t_attn = t_verify = t_commit = 0.0
@@ -231,8 +262,8 @@ def cpu_baseline(d, budget_s):
         if d["mode"] == "greedy":
             path, plen, _, _ = oracle.verify_greedy(d["parents"], d["tokens"], d["llm"])
         else:
-            path, plen, _, _ = oracle.verify_mss(d["parents"], d["tokens"], d["llm"], d["ssm"],
-                                                 d["u_accept"], d["u_bonus"])
+            path, plen, _, _ = oracle.verify_mss_seeded(d["parents"], d["tokens"], d["llm"],
+                                                        d["ssm"], d["seed"], d["step"])
         t2 = time.perf_counter()
         oracle.kv_commit(d["k_tree"][:1], d["v_tree"][:1], d["k_cache"][:1], d["v_cache"][:1],
                          d["cache_len"][:1], path[:1], plen[:1], d["Lmax"])
@@ -241,24 +272,39 @@ def cpu_baseline(d, budget_s):
         t_verify += t2 - t1
         t_commit += (t3 - t2) * B
         reps += 1
-    step_s = (t_attn + t_verify + t_commit) / reps
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": B * N / step_s, "unit": "tree-node queries/s", "cores": threads,
+    desc = ("%d step(s): attention on %d of %d query rows (uniform sample, time scaled to all "
+            "rows), verify of the whole batch, commit of request 0 (time x B); %.1f s"
+            % (reps, len(sample), len(rows_all), time.perf_counter() - start))
+    return (t_attn + t_verify + t_commit) / reps, desc
+
+
+def cpu_baseline(d, budget_s):
+    """The CPU oracle on a bounded sample of the same workload, on every host
+    core (OpenMP over rows and requests) and on one, as tree-node queries/s of
+    one full step."""
+    import oracle
+    ncpu, model = host_cpu()
+    B, N = d["B"], d["N"]
+    oracle.set_threads(ncpu)
+    threads = oracle.max_threads()
+    step_all, desc_all = cpu_step(d, 0.7 * budget_s, oracle)
+    oracle.set_threads(1)
+    step_one, desc_one = cpu_step(d, 0.3 * budget_s, oracle)
+    oracle.set_threads(ncpu)
+    return {"value": B * N / step_all, "unit": "tree-node queries/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d step(s): attention on %d of %d query rows (uniform sample, time "
-                      "scaled to all rows), verify of the whole batch, commit of request 0 "
-                      "(time x B); %.1f s of CPU work" % (reps, len(sample), len(rows_all),
-                                                          time.perf_counter() - start),
-            "step_ms": step_s * 1e3}
+            "sample": "all %d threads: %s; one thread: %s" % (threads, desc_all, desc_one),
+            "step_ms": step_all * 1e3, "value_1thread": B * N / step_one,
+            "step_ms_1thread": step_one * 1e3, "nproc": ncpu, "cpu_model": model}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c4", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=16.0,
                     help="seconds of CPU oracle work for the baseline (0 = skip)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of HIP-graph replays")
@@ -271,6 +317,9 @@ def main():
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d = synth.make(args.workload)
@@ -282,36 +331,41 @@ def main():
     step = Step(d, copies, dev, fuse=not args.unfused)
     stream = torch.cuda.current_stream(dev)
 
+    def launches(fn):
+        """One callable per input copy: a graph replay of fn on that copy
+        (eager launches with --eager or when capture fails)."""
+        out = []
+        for c in copies:
+            g = None if args.eager else capture(lambda c=c: fn(c), dev)
+            out.append(g.replay if g is not None else (lambda c=c: fn(c)))
+        return out
+
+    def one_step(c):
+        step.attn(c)
+        if step.fused:
+            step.verify_commit(c)
+        else:
+            step.verify(c)
+            step.commit(c)
+
     for i in range(args.warmup):
-        step(i)
+        one_step(copies[i % ncopies])
     torch.cuda.synchronize()
-    graph = None
-    if not args.eager:
-        # one HIP graph holding one step per input copy, replayed as a unit
-        graph = capture(lambda: [step(i) for i in range(ncopies)], dev)
-    if graph is not None:
-        reps = max(1, -(-args.steps // ncopies))
-        steps_timed = reps * ncopies
-        ms_step = timed(lambda i: graph.replay(), reps, stream) / ncopies
-    else:
-        steps_timed = args.steps
-        ms_step = timed(step, args.steps, stream)
-    # per-entry-point times over the same rotation (graph-replayed like the step)
-    def stage_ms(fn):
-        g = capture(lambda: [fn(c) for c in copies], dev) if graph is not None else None
-        if g is None:
-            return timed(lambda i: fn(copies[i % ncopies]), args.steps, stream)
-        reps = max(1, -(-args.steps // ncopies))
-        return timed(lambda i: g.replay(), reps, stream) / ncopies
-    ms_attn = stage_ms(step.attn)
-    ms_verify = stage_ms(step.verify)
-    ms_commit = stage_ms(step.commit)
-    ms_fused = stage_ms(step.verify_commit) if step.fused else None
+    step_fns = launches(one_step)
+    graphed = not args.eager and all(getattr(f, "__self__", None) is not None for f in step_fns)
+    t_step = summary(timed_steps(step_fns, args.steps, stream))
+    # per-entry-point times over the same rotation, launched the same way
+    stage = lambda fn: summary(timed_steps(launches(fn), args.steps, stream))
+    t_attn = stage(step.attn)
+    t_verify = stage(step.verify)
+    t_commit = stage(step.commit)
+    t_fused = stage(step.verify_commit) if step.fused else None
     st = torch.stack([c.st for c in copies]).cpu()
     assert int(st.abs().sum()) == 0, "a request was rejected: %s" % st
 
     B, N = d["B"], d["N"]
     kv_bytes, flops = attn_work(d)
+    ms_attn = t_attn["mean"]  # the roofline takes the average launch
     kv_gbs = kv_bytes / (ms_attn * 1e-3) / 1e9
     mfma_bound = args.workload == "c4"
     if mfma_bound:
@@ -321,18 +375,25 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": kv_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": kv_gbs / HBM_PEAK_GBS}
-    tr = stored_traffic(args.workload)
-    roof["traffic"] = tr
+    roof["traffic"] = stored_traffic(args.workload)
+    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
     roof["kernel"] = "ttv_tree_attn (all kernels of one call)"
     roof["per_launch_algorithmic"] = flops if mfma_bound else kv_bytes
+    roof["per_launch_algorithmic_unit"] = "flop" if mfma_bound else "byte"
     roof["avg_launch_us"] = ms_attn * 1e3
+    roof["median_launch_us"] = t_attn["median"] * 1e3
+    roof["kv_gbs"] = kv_gbs
+    roof["kv_frac_of_hbm_peak"] = kv_gbs / HBM_PEAK_GBS
 
+    ms_step = t_step["median"]
+    us = lambda t: None if t is None else {k: v * 1e3 for k, v in t.items()}
     res = {
         "metric": METRIC,
         "value": B * N / (ms_step * 1e-3),
         "unit": "tree-node queries/s",
-        "n_gpus": 1, "steps": steps_timed, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_mean": t_step["mean"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": d["dtype"], "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "N": N, "Hq": d["Hq"], "Hkv": d["Hkv"],
@@ -340,13 +401,15 @@ def main():
                    "verify": d["mode"],
                    "verify_commit": "one pass" if step.fused else "two calls",
                    "input_copies": ncopies,
-                   "launch": "hip graph replay" if graph is not None else "eager",
-                   "inputs": "rotated, HBM-resident" if ncopies > 1 else "one copy (warm)"},
+                   "launch": "hip graph replay per step" if graphed else "eager",
+                   "inputs": "rotated, HBM-resident" if ncopies > 1 else
+                             ("one copy (warm)" if args.warm else
+                              "one copy larger than twice the last-level cache, HBM-resident")},
         "tree_attn_kv_gbs": kv_gbs,
         "tree_attn_kv_frac_of_hbm_peak": kv_gbs / HBM_PEAK_GBS,
-        "stage_us": {"tree_attn": ms_attn * 1e3, "tree_verify": ms_verify * 1e3,
-                     "kv_commit": ms_commit * 1e3,
-                     "tree_verify_commit": ms_fused * 1e3 if ms_fused is not None else None},
+        "stage_us": {"tree_attn": us(t_attn), "tree_verify": us(t_verify),
+                     "kv_commit": us(t_commit), "tree_verify_commit": us(t_fused)},
+        "step_us": us(t_step),
         "roofline": roof,
     }
     if args.cpu_budget > 0:

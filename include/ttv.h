@@ -124,21 +124,19 @@ ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents,
  *               zeros and dev_status TTV_E_TREE.
  *   lse         float [B,N,Hq], nullable: natural-log sum-exp of the scaled
  *               scores (0 for a rejected request).
+ *   anc_out     uint64 [B,N,W], nullable: the tree mask, as ttv_tree_topology
+ *               writes it (ancestor bitset of every node, self included).
+ *   depth_out   int32 [B,N], nullable: node depths, as ttv_tree_topology
+ *               writes them (the positions are L_b + depth).  When either is
+ *               given, the call adds one small launch that writes them.
  *   workspace   device scratch of >= ttv_tree_attn_workspace_size(...) bytes
  *               (may be NULL when that size is 0): fp32 partials of the
  *               split-KV launch (and, when the split is planned on the
  *               device, the chunk count of each request).  Its contents need
  *               no initialisation and are garbage afterwards; calls sharing
  *               one must not overlap.
- *   rows_per_block, chunk_keys  launch tuning: 0 = automatic; otherwise query
- *               rows per workgroup (64, 128 or 256 on the matrix-core path,
- *               which serves bf16 with N*Hq/Hkv >= 16; 16 on the FMA path)
- *               and prefix keys per workgroup (a positive multiple of 64);
- *               other values give TTV_E_UNSUPPORTED.  The same values must be
- *               given to the size query.  With chunk_keys = 0, 2..64
- *               requests and fewer (request, kv head, row block) units than
- *               CUs, the split follows the actual prefix lengths read on the
- *               device (longer requests get more workgroups).
+ * The launch shape (query rows per workgroup, split of the prefix over
+ * workgroups) is chosen from the sizes; ttv_tree_attn_tuned fixes it.
  * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE, TTV_E_UNSUPPORTED,
  *         TTV_E_ALIGN, TTV_E_WORKSPACE, TTV_E_LAUNCH.
  */
@@ -148,16 +146,45 @@ ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq,
                          const int32_t* cache_len, int32_t Lmax,
                          const void* k_tree, const void* v_tree,
                          const int32_t* parents, void* out, float* lse,
+                         uint64_t* anc_out, int32_t* depth_out,
                          int32_t* dev_status, void* workspace,
-                         size_t workspace_bytes, int32_t rows_per_block,
-                         int32_t chunk_keys, void* stream);
+                         size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace ttv_tree_attn needs for these sizes (0 if none);
  * returns (size_t)-1 for arguments ttv_tree_attn would reject. */
 size_t ttv_tree_attn_workspace_size(ttv_dtype dt, int32_t B, int32_t N,
                                     int32_t Hq, int32_t Hkv, int32_t D,
-                                    int32_t Lmax, int32_t rows_per_block,
-                                    int32_t chunk_keys);
+                                    int32_t Lmax);
+
+/*
+ * ttv_tree_attn_tuned -- ttv_tree_attn with a fixed launch shape (the same
+ * results up to rounding order).
+ *   rows_per_block, chunk_keys  0 = automatic; otherwise query rows per
+ *               workgroup (64, 128 or 256 on the matrix-core path, which
+ *               serves bf16 with N*Hq/Hkv >= 16; 16 on the FMA path) and
+ *               prefix keys per workgroup (a positive multiple of 64); other
+ *               values give TTV_E_UNSUPPORTED.  The same values must be given
+ *               to ttv_tree_attn_tuned_workspace_size.  With chunk_keys = 0,
+ *               2..64 requests and fewer (request, kv head, row block) units
+ *               than CUs, the split follows the actual prefix lengths read on
+ *               the device (longer requests get more workgroups).
+ */
+ttv_status ttv_tree_attn_tuned(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq,
+                               int32_t Hkv, int32_t D, float scale,
+                               const void* q, const void* k_cache,
+                               const void* v_cache, int32_t Lcap,
+                               const int32_t* cache_len, int32_t Lmax,
+                               const void* k_tree, const void* v_tree,
+                               const int32_t* parents, void* out, float* lse,
+                               uint64_t* anc_out, int32_t* depth_out,
+                               int32_t* dev_status, void* workspace,
+                               size_t workspace_bytes, int32_t rows_per_block,
+                               int32_t chunk_keys, void* stream);
+
+size_t ttv_tree_attn_tuned_workspace_size(ttv_dtype dt, int32_t B, int32_t N,
+                                          int32_t Hq, int32_t Hkv, int32_t D,
+                                          int32_t Lmax, int32_t rows_per_block,
+                                          int32_t chunk_keys);
 
 /*
  * ttv_tree_verify -- verify every request's token tree against the LLM's
@@ -174,25 +201,29 @@ size_t ttv_tree_attn_workspace_size(ttv_dtype dt, int32_t B, int32_t N,
  *            the LLM's next-token distribution after node u, ssm[b,c,:] is
  *            the distribution node c's token was drawn from (row 0 unused).
  *            Starting at the root with residual w = llm[b,u,:] and mass s = 1,
- *            the children c of u are tested in ascending node index with the
- *            uniform r = u_accept[b,c]: accept iff (r*q[x])*s < w[x]
- *            (fp32, two multiplies, strict), x = tokens[c], q = ssm[b,c,:].
- *            On acceptance move to c (w = llm[b,c,:], s = 1).  On rejection
- *            w[v] = max(fmaf(-s, q[v], w[v]), +0) for all v and
- *            s = (float)(sum_v fx(w[v]) * 2^-40), fx(x) = floor(x * 2^40) as
- *            uint64; s == 0 stops testing and resets w = llm[b,u,:].  When no
- *            child is accepted the bonus token is drawn from w by inverse CDF
- *            over the exact integer prefix sums of fx(w): with
- *            S = sum fx(w), R = floor(u_bonus[b] * 2^24), T = floor(R*S/2^24),
- *            the bonus is the smallest t with sum_{v<=t} fx(w[v]) > T
- *            (argmax w if S == 0).  Probabilities must lie in [0,1] and
- *            uniforms in [0,1).
+ *            the children c of u are tested in ascending node index, the
+ *            j-th of them (j = 0, 1, ..) with the uniform r(j, u): accept iff
+ *            (r*q[x])*s < w[x] (fp32, two multiplies, strict), x = tokens[c],
+ *            q = ssm[b,c,:].  On acceptance move to c (w = llm[b,c,:],
+ *            s = 1).  On rejection w[v] = max(fmaf(-s, q[v], w[v]), +0) for
+ *            all v and s = (float)(sum_v fx(w[v]) * 2^-40), fx(x) =
+ *            floor(x * 2^40) as uint64; s == 0 stops testing and resets
+ *            w = llm[b,u,:].  When no child is accepted the bonus token is
+ *            drawn from w by inverse CDF over the exact integer prefix sums
+ *            of fx(w): with S = sum fx(w), R = R(u), T = floor(R*S/2^24), the
+ *            bonus is the smallest t with sum_{v<=t} fx(w[v]) > T (argmax w
+ *            if S == 0).  Probabilities must lie in [0,1].
+ *            The uniforms are drawn from Philox4x64-10 (Salmon, Moraes, Dror,
+ *            Shaw, SC'11) with key (seed, 0): with o = output word 0 for the
+ *            counter (j, u, b, step) (four 64-bit words, word 0 least
+ *            significant), r(j, u) = (o >> 40) * 2^-24; R(u) = o >> 40 for
+ *            the counter (2^63, u, b, step).  The same (seed, step) gives the
+ *            same results; a new step gives fresh draws.
  *   B,N,V    requests, nodes per request (<= 128), vocabulary (>= 1).
  *   parents  int32 [B,N]; tokens int32 [B,N] (tokens[b,0] = root's token,
  *            unused); llm float [B,N,V]; ssm float [B,N,V] (stochastic only,
- *            else NULL); u_accept float [B,N] and u_bonus float [B]
- *            (stochastic only, else NULL): the uniforms the method draws,
- *            supplied by the caller.
+ *            else NULL); seed, step: the draws' key and counter word 3
+ *            (stochastic only, else ignored).
  *   path     int32 [B,N]: path[b,k] = node at depth k on the accepted path,
  *            -1 after the end.   path_len int32 [B]: accepted nodes + 1 (>= 1).
  *   out_tokens int32 [B,N]: tokens of path[1..], then the bonus token, -1
@@ -209,14 +240,31 @@ size_t ttv_tree_attn_workspace_size(ttv_dtype dt, int32_t B, int32_t N,
 ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N,
                            int32_t V, const int32_t* parents,
                            const int32_t* tokens, const float* llm,
-                           const float* ssm, const float* u_accept,
-                           const float* u_bonus, int32_t* path,
-                           int32_t* path_len, int32_t* out_tokens,
-                           int32_t* dev_status, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           const float* ssm, uint64_t seed, uint64_t step,
+                           int32_t* path, int32_t* path_len,
+                           int32_t* out_tokens, int32_t* dev_status,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B,
                                       int32_t N, int32_t V);
+
+/*
+ * ttv_tree_verify_uniforms -- stochastic ttv_tree_verify with the uniforms
+ * given by the caller instead of drawn from (seed, step): the test of child c
+ * uses r = u_accept[b,c] (each child is tested at most once) and the final
+ * draw R = floor(u_bonus[b] * 2^24).  u_accept float [B,N], u_bonus float [B],
+ * values in [0,1).  Needs no workspace; everything else as ttv_tree_verify.
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_UNSUPPORTED, TTV_E_ALIGN,
+ *         TTV_E_LAUNCH.
+ */
+ttv_status ttv_tree_verify_uniforms(int32_t B, int32_t N, int32_t V,
+                                    const int32_t* parents,
+                                    const int32_t* tokens, const float* llm,
+                                    const float* ssm, const float* u_accept,
+                                    const float* u_bonus, int32_t* path,
+                                    int32_t* path_len, int32_t* out_tokens,
+                                    int32_t* dev_status, void* stream);
 
 /*
  * ttv_kv_commit -- write the accepted path's KV rows into the contiguous cache
@@ -273,8 +321,8 @@ ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt,
                                   int32_t Hkv, int32_t D, int32_t Lcap,
                                   const int32_t* parents,
                                   const int32_t* tokens, const float* llm,
-                                  const float* ssm, const float* u_accept,
-                                  const float* u_bonus, const void* k_tree,
+                                  const float* ssm, uint64_t seed,
+                                  uint64_t step, const void* k_tree,
                                   const void* v_tree, void* k_cache,
                                   void* v_cache, const int32_t* cache_len_in,
                                   int32_t* cache_len_out, int32_t Lmax,

@@ -49,6 +49,25 @@ def sample_rows(d, n, seed=0):
     return np.unique(np.array(rows, np.int32), axis=0)
 
 
+def block_rows(d, per_block, rows_per_block, seed=0):
+    """per_block random query rows from every (request, kv head, block of
+    rows_per_block packed rows r = node*G + g) -- the unit one attention
+    workgroup (or, with a split prefix, each of its chunks' workgroups)
+    computes -- so that every workgroup of the launch has outputs compared."""
+    rng = np.random.default_rng(seed)
+    B, N, Hq, Hkv = d["B"], d["N"], d["Hq"], d["Hkv"]
+    G = Hq // Hkv
+    R = N * G
+    rows = []
+    for b in range(B):
+        for h in range(Hkv):
+            for r0 in range(0, R, rows_per_block):
+                n = min(rows_per_block, R - r0)
+                for r in r0 + rng.choice(n, size=min(per_block, n), replace=False):
+                    rows.append((b, int(r) // G, h * G + int(r) % G))
+    return np.unique(np.array(rows, np.int32), axis=0)
+
+
 def run_attn(d, t, **hints):
     out, lse, st = ttv.tree_attn(t["q"], t["k_cache"], t["v_cache"], t["cache_len"],
                                  t["k_tree"], t["v_tree"], t["parents"], d["Lmax"],
@@ -86,17 +105,27 @@ def check_attn(d, t=None, rows=None, repeat=True, **hints):
     return out, lse, st
 
 
-def check_verify(d, t=None):
+def check_verify(d, t=None, uniforms=False):
+    """GPU tree_verify vs the oracle, bit for bit.  Stochastic inputs are
+    verified with the uniforms drawn from (seed, step) on both sides, or with
+    uniforms=True with the explicit uniforms of the inputs
+    (tree_verify_uniforms)."""
     t = t if t is not None else to_dev(d)
     greedy = d["mode"] == "greedy"
     if greedy:
         path, plen, outt, st = ttv.tree_verify(ttv.GREEDY, t["parents"], t["tokens"], t["llm"])
         ref = oracle.verify_greedy(d["parents"], d["tokens"], d["llm"])
-    else:
-        path, plen, outt, st = ttv.tree_verify(ttv.STOCHASTIC, t["parents"], t["tokens"],
-                                               t["llm"], t["ssm"], t["u_accept"], t["u_bonus"])
+    elif uniforms:
+        path, plen, outt, st = ttv.tree_verify_uniforms(t["parents"], t["tokens"], t["llm"],
+                                                        t["ssm"], t["u_accept"], t["u_bonus"])
         ref = oracle.verify_mss(d["parents"], d["tokens"], d["llm"], d["ssm"], d["u_accept"],
                                 d["u_bonus"])
+    else:
+        path, plen, outt, st = ttv.tree_verify(ttv.STOCHASTIC, t["parents"], t["tokens"],
+                                               t["llm"], t["ssm"], seed=d["seed"],
+                                               step=d["step"])
+        ref = oracle.verify_mss_seeded(d["parents"], d["tokens"], d["llm"], d["ssm"],
+                                       d["seed"], d["step"])
     torch.cuda.synchronize()
     for name, g, r in zip(("path", "path_len", "out_tokens", "status"),
                           (path, plen, outt, st), ref):

@@ -27,7 +27,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ttv_tree_topology", "ttv_tree_attn", "ttv_tree_attn_workspace_size",
-              "ttv_tree_verify", "ttv_tree_verify_workspace_size", "ttv_kv_commit",
+              "ttv_tree_attn_tuned", "ttv_tree_attn_tuned_workspace_size",
+              "ttv_tree_verify", "ttv_tree_verify_workspace_size", "ttv_tree_verify_uniforms",
+              "ttv_kv_commit",
               "ttv_tree_expand", "ttv_tree_merge", "ttv_probs_from_logits", "ttv_kv_commit_inplace", "ttv_tree_verify_commit", "ttv_status_string",
               "ttv_version"):
         assert n in names
@@ -57,11 +59,17 @@ def test_status_strings():
 
 
 def attn(**kw):
+    """ttv_tree_attn_tuned with these arguments; with the launch shape left
+    automatic the same call through ttv_tree_attn must give the same status."""
     args = dict(dt=1, B=1, N=8, Hq=4, Hkv=2, D=64, scale=0.125, q=A, kc=A, vc=A, Lcap=128,
-                cl=A, Lmax=100, kt=A, vt=A, par=A, out=A, lse=None, st=None, ws=A,
-                wsb=1 << 30, rpb=0, ck=0)
+                cl=A, Lmax=100, kt=A, vt=A, par=A, out=A, lse=None, anc=None, depth=None,
+                st=None, ws=A, wsb=1 << 30, rpb=0, ck=0)
     args.update(kw)
-    return ttv.lib().ttv_tree_attn(*args.values(), None)
+    v = list(args.values())
+    st = ttv.lib().ttv_tree_attn_tuned(*v, None)
+    if args["rpb"] == 0 and args["ck"] == 0:
+        assert ttv.lib().ttv_tree_attn(*v[:-2], None) == st
+    return st
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -84,7 +92,7 @@ def test_tree_attn_host_validation(kw, status):
 
 
 def test_tree_attn_workspace_size_matches_plan():
-    f = ttv.lib().ttv_tree_attn_workspace_size
+    f = ttv.lib().ttv_tree_attn_tuned_workspace_size
     # 2 chunks of 64 keys -> fp32 partials, D + 2 floats per (pair, chunk, row)
     assert f(1, 1, 8, 4, 2, 64, 100, 0, 64) == 1 * 2 * 2 * 16 * 66 * 4
     assert f(0, 1, 8, 4, 2, 64, 100, 0, 64) == 1 * 2 * 2 * 16 * 66 * 4
@@ -93,10 +101,15 @@ def test_tree_attn_workspace_size_matches_plan():
     assert f(9, 1, 8, 4, 2, 64, 64, 0, 0) == SZ_ERR
     # the binding allocates exactly that much
     assert ttv.tree_attn_workspace_size(torch.bfloat16, 1, 8, 4, 2, 64, 100, 0, 64) == 16896
+    # the automatic shape: no split up to 512 keys, one shape for both entry points
+    g = ttv.lib().ttv_tree_attn_workspace_size
+    assert g(1, 1, 8, 4, 2, 64, 100) == 0 == f(1, 1, 8, 4, 2, 64, 100, 0, 0)
+    assert g(1, 4, 128, 64, 8, 128, 32768) == f(1, 4, 128, 64, 8, 128, 32768, 0, 0) > 0
+    assert g(1, 1, 129, 4, 2, 64, 64) == SZ_ERR
 
 
 def verify(**kw):
-    args = dict(mode=0, B=2, N=8, V=100, par=A, tok=A, llm=A, ssm=None, ua=None, ub=None,
+    args = dict(mode=0, B=2, N=8, V=100, par=A, tok=A, llm=A, ssm=None, seed=1, step=2**63,
                 path=A, plen=A, outt=A, st=None, ws=A, wsb=1 << 30)
     args.update(kw)
     return ttv.lib().ttv_tree_verify(*args.values(), None)
@@ -105,15 +118,29 @@ def verify(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(mode=2), ttv.E_DTYPE),
     (dict(par=None), ttv.E_NULL), (dict(llm=None), ttv.E_NULL), (dict(path=None), ttv.E_NULL),
-    (dict(mode=1), ttv.E_NULL), (dict(mode=1, ssm=A, ua=A), ttv.E_NULL),
+    (dict(mode=1), ttv.E_NULL),
     (dict(B=0), ttv.E_SHAPE), (dict(V=0), ttv.E_SHAPE),
     (dict(N=200), ttv.E_UNSUPPORTED),
-    (dict(mode=1, ssm=A, ua=A, ub=A, V=40000), ttv.E_UNSUPPORTED),
-    (dict(llm=MIS), ttv.E_ALIGN), (dict(mode=1, ssm=MIS, ua=A, ub=A), ttv.E_ALIGN),
+    (dict(mode=1, ssm=A, V=40000), ttv.E_UNSUPPORTED),
+    (dict(llm=MIS), ttv.E_ALIGN), (dict(mode=1, ssm=MIS), ttv.E_ALIGN),
     (dict(ws=None), ttv.E_WORKSPACE), (dict(wsb=8), ttv.E_WORKSPACE),
 ])
 def test_tree_verify_host_validation(kw, status):
     assert verify(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(par=None), ttv.E_NULL), (dict(ssm=None), ttv.E_NULL), (dict(ua=None), ttv.E_NULL),
+    (dict(ub=None), ttv.E_NULL), (dict(outt=None), ttv.E_NULL),
+    (dict(B=0), ttv.E_SHAPE), (dict(N=0), ttv.E_SHAPE), (dict(V=0), ttv.E_SHAPE),
+    (dict(N=129), ttv.E_UNSUPPORTED), (dict(V=40000), ttv.E_UNSUPPORTED),
+    (dict(llm=MIS), ttv.E_ALIGN), (dict(ssm=MIS), ttv.E_ALIGN),
+])
+def test_tree_verify_uniforms_host_validation(kw, status):
+    args = dict(B=2, N=8, V=100, par=A, tok=A, llm=A, ssm=A, ua=A, ub=A, path=A, plen=A,
+                outt=A, st=None)
+    args.update(kw)
+    assert ttv.lib().ttv_tree_verify_uniforms(*args.values(), None) == status
 
 
 def test_tree_verify_workspace_size():
@@ -218,7 +245,7 @@ def test_kv_commit_inplace_host_validation(kw, status):
 
 def verify_commit(**kw):
     args = dict(mode=0, dt=1, B=2, N=8, V=64, Hkv=2, D=64, Lcap=100, par=A, tok=A, llm=A,
-                ssm=None, ua=None, ub=None, kt=A, vt=A, kc=A, vc=A, cli=A, clo=A + 0x100, Lmax=50,
+                ssm=None, seed=7, step=0, kt=A, vt=A, kc=A, vc=A, cli=A, clo=A + 0x100, Lmax=50,
                 path=A, plen=A, outt=A, src=None, st=None, ws=A, wsb=1 << 20)
     args.update(kw)
     return ttv.lib().ttv_tree_verify_commit(*args.values(), None)
@@ -232,9 +259,8 @@ def verify_commit(**kw):
     (dict(llm=MIS), ttv.E_ALIGN), (dict(kt=MIS), ttv.E_ALIGN), (dict(ws=None), ttv.E_WORKSPACE),
     (dict(wsb=64), ttv.E_WORKSPACE), (dict(ws=MIS), ttv.E_ALIGN), (dict(mode=2), ttv.E_DTYPE),
     (dict(mode=1), ttv.E_NULL),                                  # stochastic without ssm
-    (dict(mode=1, ssm=A, ua=A, ub=None), ttv.E_NULL),
-    (dict(mode=1, ssm=A, ua=A, ub=A, V=40000), ttv.E_UNSUPPORTED),  # residual past on-chip memory
-    (dict(mode=1, ssm=MIS, ua=A, ub=A), ttv.E_ALIGN),
+    (dict(mode=1, ssm=A, V=40000), ttv.E_UNSUPPORTED),  # residual past on-chip memory
+    (dict(mode=1, ssm=MIS), ttv.E_ALIGN),
 ])
 def test_tree_verify_commit_host_validation(kw, status):
     assert verify_commit(**kw) == status

@@ -1,7 +1,8 @@
 """GPU tree attention vs the fp64 oracle on the same seeded inputs.
 
-The five workloads at full size (the long ones on sampled rows, in the launch
-configuration the benchmark uses), plus edge cases: N = 1, empty prefix,
+The five workloads at full size in the launch configuration the benchmark
+uses (every row; the long-context one on rows from every workgroup's unit),
+plus edge cases: N = 1, empty prefix,
 chains and stars, N = 64/65/128 (bitset word boundary), GQA group sizes 1..16,
 ragged prefix lengths, the FMA path in bf16 (fewer than 16 rows per kv head)
 and fp32, head dim 64, every row-block size and forced KV splits, and
@@ -15,22 +16,28 @@ import torch
 
 import synth
 import oracle
-from gpu_case import announce, check_attn, make, run_attn, sample_rows, to_dev
+from gpu_case import announce, block_rows, check_attn, make, run_attn, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
 def test_workload_full(name):
     announce("attn workload %s (all rows)" % name)
     check_attn(make(name))
 
 
-@pytest.mark.parametrize("name,n", [("c4", 384), ("c5", 1024)])
-def test_workload_sampled(name, n):
-    announce("attn workload %s (%d sampled rows)" % (name, n))
-    d = make(name)
-    check_attn(d, rows=sample_rows(d, n))
+def test_long_context_every_workgroup():
+    """The long-context workload at full size, in the launch the benchmark
+    times (256-row blocks, the prefix split planned on the device): 16 rows
+    from every (request, kv head, row block) unit -- each of its chunk
+    workgroups contributes to all of them -- plus the roots and deepest
+    nodes."""
+    announce("attn workload c4 (16 rows of every row block)")
+    d = make("c4")
+    rows = np.unique(np.concatenate([block_rows(d, 16, 256), sample_rows(d, 0)]), axis=0)
+    assert len({(b, h // 8, ((i * 8 + h % 8) // 256)) for b, i, h in rows}) == 4 * 8 * 4
+    check_attn(d, rows=rows)
 
 
 def spec(**kw):

@@ -82,7 +82,8 @@ def test_full_step(name):
                                    scale=d["scale"])
     mode = ttv.GREEDY if d["mode"] == "greedy" else ttv.STOCHASTIC
     path, plen, outt, st_v = ttv.tree_verify(mode, t["parents"], t["tokens"], t["llm"],
-                                             t.get("ssm"), t.get("u_accept"), t.get("u_bonus"))
+                                             t.get("ssm"), seed=d.get("seed", 0),
+                                             step=d.get("step", 0))
     kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
     clo, src, st_c = ttv.kv_commit(t["k_tree"], t["v_tree"], kc, vc, t["cache_len"], path,
                                    plen, d["Lmax"])

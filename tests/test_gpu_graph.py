@@ -40,12 +40,12 @@ def test_graph_replays_match_eager(name, one_pass):
         if one_pass:
             ttv.tree_verify_commit(mode, t["parents"], t["tokens"], t["llm"], t["k_tree"],
                                    t["v_tree"], kc, vc, t["cache_len"], d["Lmax"],
-                                   ssm=t.get("ssm"), u_accept=t.get("u_accept"),
-                                   u_bonus=t.get("u_bonus"), cache_len_out=clo, path=path,
+                                   ssm=t.get("ssm"), seed=d.get("seed", 0),
+                                   step=d.get("step", 0), cache_len_out=clo, path=path,
                                    path_len=plen, out_tokens=outt, workspace=wsv)
             return
         ttv.tree_verify(mode, t["parents"], t["tokens"], t["llm"], t.get("ssm"),
-                        t.get("u_accept"), t.get("u_bonus"), path=path, path_len=plen,
+                        seed=d.get("seed", 0), step=d.get("step", 0), path=path, path_len=plen,
                         out_tokens=outt, workspace=wsv)
         ttv.kv_commit(t["k_tree"], t["v_tree"], kc, vc, t["cache_len"], path, plen, d["Lmax"],
                       cache_len_out=clo)

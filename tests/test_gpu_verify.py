@@ -88,7 +88,35 @@ def mss_spec(**kw):
 ])
 def test_stochastic_edge_cases(kw):
     announce("verify stochastic edge %s" % kw)
-    check_verify(synth.make(mss_spec(**kw), with_kv=False))
+    d = synth.make(mss_spec(**kw), with_kv=False)
+    check_verify(d)
+    check_verify(d, uniforms=True)
+
+
+@pytest.mark.parametrize("seed,step", [(0, 0), (2**64 - 1, 2**64 - 1), (1005, 2**63 + 1),
+                                       (123456789, 7)])
+def test_stochastic_seed_and_step_words(seed, step):
+    """Counter and key words at their extremes: the device Philox and the
+    oracle's agree bit for bit on every path and token."""
+    announce("verify stochastic seed=%d step=%d" % (seed, step))
+    d = synth.make(mss_spec(B=32, N=40, V=60, seed=17, prob_sigma=3.0), with_kv=False)
+    d["seed"], d["step"] = seed, step
+    check_verify(d)
+
+
+def test_stochastic_steps_draw_afresh():
+    """Successive steps on the same inputs draw different uniforms: the bonus
+    tokens of one-node trees over uniform rows vary from step to step, each
+    step matching the oracle."""
+    announce("verify stochastic step sweep")
+    d = synth.make(mss_spec(B=8, N=1, V=16), with_kv=False)
+    d["llm"] = np.full_like(d["llm"], 1.0 / 16)
+    seen = set()
+    for step in range(10):
+        d["step"] = step
+        _, _, outt, _ = check_verify(d)
+        seen.update(outt[:, 0].cpu().numpy().tolist())
+    assert len(seen) >= 10
 
 
 def test_stochastic_p_equals_q_chain128():
@@ -98,6 +126,7 @@ def test_stochastic_p_equals_q_chain128():
     d["ssm"][:, 1:] = d["llm"][:, :-1]
     _, plen, _, _ = check_verify(d)
     assert torch.all(plen == 128)
+    check_verify(d, uniforms=True)
 
 
 def test_stochastic_empty_residual():
@@ -108,6 +137,8 @@ def test_stochastic_empty_residual():
     d["llm"] = d["llm"].copy()
     d["llm"][:, 0] = 0.5 * d["ssm"][:, 1]
     _, plen, _, _ = check_verify(d)
+    assert 0 < int((plen == 1).sum()) < 32
+    _, plen, _, _ = check_verify(d, uniforms=True)
     assert 0 < int((plen == 1).sum()) < 32
 
 
@@ -121,6 +152,8 @@ def test_stochastic_bad_tokens_and_tree():
     d["parents"][3, 2] = 2
     _, _, _, st = check_verify(d)
     assert list(st.cpu().numpy()) == [0, 2, 2, 7]
+    _, _, _, st = check_verify(d, uniforms=True)
+    assert list(st.cpu().numpy()) == [0, 2, 2, 7]
 
 
 def test_verify_is_deterministic():
@@ -128,9 +161,9 @@ def test_verify_is_deterministic():
     d = synth.make("c5", with_kv=False)
     t = to_dev(d)
     a = ttv.tree_verify(ttv.STOCHASTIC, t["parents"], t["tokens"], t["llm"], t["ssm"],
-                        t["u_accept"], t["u_bonus"])
+                        seed=d["seed"], step=d["step"])
     b = ttv.tree_verify(ttv.STOCHASTIC, t["parents"], t["tokens"], t["llm"], t["ssm"],
-                        t["u_accept"], t["u_bonus"])
+                        seed=d["seed"], step=d["step"])
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
@@ -142,5 +175,5 @@ def test_stochastic_repeated_launches():
     for kw in (dict(V=7, seed=1), dict(seed=21), dict(V=32000, B=4, N=16, seed=3)):
         announce("verify stochastic repeated %s" % kw)
         d = synth.make(mss_spec(**kw), with_kv=False)
-        for _ in range(12):
-            check_verify(d)
+        for i in range(12):
+            check_verify(d, uniforms=bool(i % 2))

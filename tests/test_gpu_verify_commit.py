@@ -33,7 +33,7 @@ def run_and_check(d, want_src=True, shared_len=False):
     lens = t["cache_len"]
     greedy = d["mode"] == "greedy"
     mode = ttv.GREEDY if greedy else ttv.STOCHASTIC
-    extra = {} if greedy else dict(ssm=t["ssm"], u_accept=t["u_accept"], u_bonus=t["u_bonus"])
+    extra = {} if greedy else dict(ssm=t["ssm"], seed=d["seed"], step=d["step"])
     # the fused pass
     kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
     lens1 = lens.clone()
@@ -44,8 +44,7 @@ def run_and_check(d, want_src=True, shared_len=False):
     kc2, vc2 = t["k_cache"].clone(), t["v_cache"].clone()
     lens2 = lens.clone()
     path2, plen2, outt2, st_v = ttv.tree_verify(mode, t["parents"], t["tokens"], t["llm"],
-                                                extra.get("ssm"), extra.get("u_accept"),
-                                                extra.get("u_bonus"))
+                                                **extra)
     clo2, src2, st_c = ttv.kv_commit(t["k_tree"], t["v_tree"], kc2, vc2, lens2, path2, plen2,
                                      d["Lmax"], cache_len_out=lens2 if shared_len else None,
                                      want_src=want_src)
@@ -64,8 +63,8 @@ def run_and_check(d, want_src=True, shared_len=False):
     if greedy:
         r_path, r_plen, r_outt, r_st = oracle.verify_greedy(d["parents"], d["tokens"], d["llm"])
     else:
-        r_path, r_plen, r_outt, r_st = oracle.verify_mss(d["parents"], d["tokens"], d["llm"],
-                                                         d["ssm"], d["u_accept"], d["u_bonus"])
+        r_path, r_plen, r_outt, r_st = oracle.verify_mss_seeded(
+            d["parents"], d["tokens"], d["llm"], d["ssm"], d["seed"], d["step"])
     assert np.array_equal(path.cpu().numpy(), r_path)
     assert np.array_equal(plen.cpu().numpy(), r_plen)
     assert np.array_equal(outt.cpu().numpy(), r_outt)

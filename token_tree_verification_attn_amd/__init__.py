@@ -23,8 +23,10 @@ from typing import Optional
 
 import torch
 
-__all__ = ["tree_topology", "tree_attn", "tree_verify", "kv_commit", "tree_expand", "tree_merge", "probs_from_logits", "kv_commit_inplace",
-           "tree_attn_workspace_size", "tree_verify_workspace_size", "status_string",
+__all__ = ["tree_topology", "tree_attn", "tree_verify", "tree_verify_uniforms", "kv_commit",
+           "tree_verify_commit", "tree_expand", "tree_merge", "probs_from_logits",
+           "kv_commit_inplace", "tree_attn_workspace_size", "tree_verify_workspace_size",
+           "status_string",
            "TTVError", "LibraryNotBuilt", "lib", "LIB_PATH", "GREEDY", "STOCHASTIC"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttv.so")
@@ -63,11 +65,17 @@ def lib():
         L.ttv_version.restype = _I
         L.ttv_tree_topology.argtypes = [_I, _I, _P, _P, _P, _P, _P]
         L.ttv_tree_attn.argtypes = [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P, _I, _P, _P,
-                                    _P, _P, _P, _P, _P, _SZ, _I, _I, _P]
-        L.ttv_tree_attn_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I]
+                                    _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.ttv_tree_attn_tuned.argtypes = [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P, _I, _P,
+                                          _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _P]
+        L.ttv_tree_attn_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I]
         L.ttv_tree_attn_workspace_size.restype = _SZ
-        L.ttv_tree_verify.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+        L.ttv_tree_attn_tuned_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I]
+        L.ttv_tree_attn_tuned_workspace_size.restype = _SZ
+        L.ttv_tree_verify.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _U64, _U64, _P, _P, _P, _P,
                                       _P, _SZ, _P]
+        L.ttv_tree_verify_uniforms.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                               _P, _P]
         L.ttv_tree_verify_workspace_size.argtypes = [_I, _I, _I, _I]
         L.ttv_tree_verify_workspace_size.restype = _SZ
         L.ttv_kv_commit.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P,
@@ -77,11 +85,13 @@ def lib():
         L.ttv_probs_from_logits.argtypes = [_I, _I, _F, _I, _P, _P, _P]
         L.ttv_kv_commit_inplace.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P,
                                             _P, _P, _P]
-        L.ttv_tree_verify_commit.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
-                                             _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
+        L.ttv_tree_verify_commit.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _U64,
+                                             _U64, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
                                              _P, _SZ, _P]
-        for f in ("ttv_tree_verify_commit", "ttv_kv_commit_inplace", "ttv_tree_topology", "ttv_tree_attn", "ttv_tree_verify", "ttv_kv_commit",
-                  "ttv_tree_expand", "ttv_tree_merge", "ttv_probs_from_logits"):
+        for f in ("ttv_tree_verify_commit", "ttv_kv_commit_inplace", "ttv_tree_topology",
+                  "ttv_tree_attn", "ttv_tree_attn_tuned", "ttv_tree_verify",
+                  "ttv_tree_verify_uniforms", "ttv_kv_commit", "ttv_tree_expand",
+                  "ttv_tree_merge", "ttv_probs_from_logits"):
             getattr(L, f).restype = _I
         _lib = L
     return _lib
@@ -143,8 +153,11 @@ def tree_topology(parents: torch.Tensor, dev_status: Optional[torch.Tensor] = No
 
 
 def tree_attn_workspace_size(dtype, B, N, Hq, Hkv, D, Lmax, rows_per_block=0, chunk_keys=0):
-    n = lib().ttv_tree_attn_workspace_size(_dt(dtype), B, N, Hq, Hkv, D, Lmax, rows_per_block,
-                                           chunk_keys)
+    if rows_per_block or chunk_keys:
+        n = lib().ttv_tree_attn_tuned_workspace_size(_dt(dtype), B, N, Hq, Hkv, D, Lmax,
+                                                     rows_per_block, chunk_keys)
+    else:
+        n = lib().ttv_tree_attn_workspace_size(_dt(dtype), B, N, Hq, Hkv, D, Lmax)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("unsupported tree_attn sizes")
     return n
@@ -152,10 +165,14 @@ def tree_attn_workspace_size(dtype, B, N, Hq, Hkv, D, Lmax, rows_per_block=0, ch
 
 def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int,
               scale: Optional[float] = None, out=None, lse=None, want_lse: bool = True,
-              dev_status=None, workspace=None, rows_per_block: int = 0, chunk_keys: int = 0):
+              dev_status=None, workspace=None, anc_out=None, depth_out=None,
+              rows_per_block: int = 0, chunk_keys: int = 0):
     """Tree attention for every node; returns (out [B,N,Hq,D], lse [B,N,Hq] or None,
     dev_status [B]).  k_tree = v_tree = None reads node i's K/V from cache row
-    L_b + i."""
+    L_b + i.  anc_out (int64 [B,N,W] holding the uint64 words) and depth_out
+    (int32 [B,N]), when given, receive the tree mask and the node depths.
+    rows_per_block / chunk_keys other than 0 fix the launch shape
+    (ttv_tree_attn_tuned)."""
     B, N, Hq, D = q.shape
     Hkv, Lcap = k_cache.shape[1], k_cache.shape[2]
     dev = q.device
@@ -177,18 +194,24 @@ def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int
         lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, N, Hq), dev)
+    if anc_out is not None:
+        _need(anc_out, "anc_out", torch.int64, (B, N, (N + 63) // 64), dev)
+    if depth_out is not None:
+        _need(depth_out, "depth_out", torch.int32, (B, N), dev)
     if dev_status is None:
         dev_status = torch.empty(B, dtype=torch.int32, device=dev)
     nbytes = tree_attn_workspace_size(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys)
     if workspace is None and nbytes:
-        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)  # counters start at 0
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)  # needs no initialisation
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().ttv_tree_attn(_dt(dt), B, N, Hq, Hkv, D, float(scale), _ptr(q), _ptr(k_cache),
-                             _ptr(v_cache), Lcap, _ptr(cache_len), int(Lmax), _ptr(k_tree),
-                             _ptr(v_tree), _ptr(parents), _ptr(out), _ptr(lse),
-                             _ptr(dev_status), _ptr(workspace), wsb, rows_per_block,
-                             chunk_keys, _stream(dev))
-    _check("ttv_tree_attn", st)
+    args = (_dt(dt), B, N, Hq, Hkv, D, float(scale), _ptr(q), _ptr(k_cache), _ptr(v_cache), Lcap,
+            _ptr(cache_len), int(Lmax), _ptr(k_tree), _ptr(v_tree), _ptr(parents), _ptr(out),
+            _ptr(lse), _ptr(anc_out), _ptr(depth_out), _ptr(dev_status), _ptr(workspace), wsb)
+    if rows_per_block or chunk_keys:
+        _check("ttv_tree_attn_tuned", lib().ttv_tree_attn_tuned(*args, rows_per_block,
+                                                                chunk_keys, _stream(dev)))
+    else:
+        _check("ttv_tree_attn", lib().ttv_tree_attn(*args, _stream(dev)))
     return out, lse, dev_status
 
 
@@ -199,11 +222,12 @@ def tree_verify_workspace_size(mode, B, N, V):
     return n
 
 
-def tree_verify(mode: int, parents, tokens, llm, ssm=None, u_accept=None, u_bonus=None,
+def tree_verify(mode: int, parents, tokens, llm, ssm=None, seed: int = 0, step: int = 0,
                 path=None, path_len=None, out_tokens=None, dev_status=None, workspace=None):
     """Greedy (mode GREEDY, llm = logits) or multi-step speculative sampling
-    (mode STOCHASTIC, llm/ssm = probabilities, caller's uniforms).  Returns
-    (path [B,N], path_len [B], out_tokens [B,N], dev_status [B])."""
+    (mode STOCHASTIC, llm/ssm = probabilities, uniforms drawn on the device
+    from Philox4x64-10 with key (seed, 0) and counter word 3 = step).
+    Returns (path [B,N], path_len [B], out_tokens [B,N], dev_status [B])."""
     B, N = parents.shape
     V = llm.shape[2]
     dev = parents.device
@@ -212,8 +236,52 @@ def tree_verify(mode: int, parents, tokens, llm, ssm=None, u_accept=None, u_bonu
     _need(llm, "llm", torch.float32, (B, N, V), dev)
     if mode == STOCHASTIC:
         _need(ssm, "ssm", torch.float32, (B, N, V), dev)
-        _need(u_accept, "u_accept", torch.float32, (B, N), dev)
-        _need(u_bonus, "u_bonus", torch.float32, (B,), dev)
+    path, path_len, out_tokens, dev_status = _verify_outputs(B, N, dev, path, path_len,
+                                                             out_tokens, dev_status)
+    nbytes = tree_verify_workspace_size(mode, B, N, V)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ttv_tree_verify(mode, B, N, V, _ptr(parents), _ptr(tokens), _ptr(llm), _ptr(ssm),
+                               _u64(seed), _u64(step), _ptr(path), _ptr(path_len),
+                               _ptr(out_tokens), _ptr(dev_status), _ptr(workspace), wsb,
+                               _stream(dev))
+    _check("ttv_tree_verify", st)
+    return path, path_len, out_tokens, dev_status
+
+
+def tree_verify_uniforms(parents, tokens, llm, ssm, u_accept, u_bonus, path=None, path_len=None,
+                         out_tokens=None, dev_status=None):
+    """Multi-step speculative sampling with the caller's uniforms: u_accept
+    [B,N] (the test of child c uses u_accept[b,c]) and u_bonus [B] (the final
+    draw).  Returns (path, path_len, out_tokens, dev_status)."""
+    B, N = parents.shape
+    V = llm.shape[2]
+    dev = parents.device
+    _need(parents, "parents", torch.int32, (B, N), dev)
+    _need(tokens, "tokens", torch.int32, (B, N), dev)
+    _need(llm, "llm", torch.float32, (B, N, V), dev)
+    _need(ssm, "ssm", torch.float32, (B, N, V), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, N), dev)
+    _need(u_bonus, "u_bonus", torch.float32, (B,), dev)
+    path, path_len, out_tokens, dev_status = _verify_outputs(B, N, dev, path, path_len,
+                                                             out_tokens, dev_status)
+    st = lib().ttv_tree_verify_uniforms(B, N, V, _ptr(parents), _ptr(tokens), _ptr(llm),
+                                        _ptr(ssm), _ptr(u_accept), _ptr(u_bonus), _ptr(path),
+                                        _ptr(path_len), _ptr(out_tokens), _ptr(dev_status),
+                                        _stream(dev))
+    _check("ttv_tree_verify_uniforms", st)
+    return path, path_len, out_tokens, dev_status
+
+
+def _u64(x):
+    x = int(x)
+    if not 0 <= x < 2 ** 64:
+        raise ValueError("seed and step are unsigned 64-bit integers")
+    return x
+
+
+def _verify_outputs(B, N, dev, path, path_len, out_tokens, dev_status):
     if path is None:
         path = torch.empty((B, N), dtype=torch.int32, device=dev)
     if path_len is None:
@@ -222,15 +290,10 @@ def tree_verify(mode: int, parents, tokens, llm, ssm=None, u_accept=None, u_bonu
         out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
     if dev_status is None:
         dev_status = torch.empty(B, dtype=torch.int32, device=dev)
-    nbytes = tree_verify_workspace_size(mode, B, N, V)
-    if workspace is None and nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().ttv_tree_verify(mode, B, N, V, _ptr(parents), _ptr(tokens), _ptr(llm), _ptr(ssm),
-                               _ptr(u_accept), _ptr(u_bonus), _ptr(path), _ptr(path_len),
-                               _ptr(out_tokens), _ptr(dev_status), _ptr(workspace), wsb,
-                               _stream(dev))
-    _check("ttv_tree_verify", st)
+    _need(path, "path", torch.int32, (B, N), dev)
+    _need(path_len, "path_len", torch.int32, (B,), dev)
+    _need(out_tokens, "out_tokens", torch.int32, (B, N), dev)
+    _need(dev_status, "dev_status", torch.int32, (B,), dev)
     return path, path_len, out_tokens, dev_status
 
 
@@ -265,11 +328,12 @@ def kv_commit(k_tree, v_tree, k_cache, v_cache, cache_len_in, path, path_len, Lm
 
 
 def tree_verify_commit(mode: int, parents, tokens, llm, k_tree, v_tree, k_cache, v_cache,
-                       cache_len_in, Lmax: int, ssm=None, u_accept=None, u_bonus=None,
+                       cache_len_in, Lmax: int, ssm=None, seed: int = 0, step: int = 0,
                        cache_len_out=None, path=None, path_len=None, out_tokens=None,
                        committed_src=None, want_src: bool = True, dev_status=None,
                        workspace=None):
-    """Verification (mode GREEDY or STOCHASTIC, as in tree_verify) and the KV
+    """Verification (mode GREEDY or STOCHASTIC with (seed, step), as in
+    tree_verify) and the KV
     commit of its path in one pass: the same results as tree_verify(...) then
     kv_commit(...); cache_len_out may be cache_len_in.  Returns (path,
     path_len, out_tokens, cache_len_out, committed_src or None, dev_status)."""
@@ -284,8 +348,6 @@ def tree_verify_commit(mode: int, parents, tokens, llm, k_tree, v_tree, k_cache,
     _need(llm, "llm", torch.float32, (B, N, V), dev)
     if mode == STOCHASTIC:
         _need(ssm, "ssm", torch.float32, (B, N, V), dev)
-        _need(u_accept, "u_accept", torch.float32, (B, N), dev)
-        _need(u_bonus, "u_bonus", torch.float32, (B,), dev)
     _need(k_tree, "k_tree", dt, (B, Hkv, N, D), dev)
     _need(v_tree, "v_tree", dt, (B, Hkv, N, D), dev)
     _need(k_cache, "k_cache", dt, (B, Hkv, Lcap, D), dev)
@@ -310,7 +372,7 @@ def tree_verify_commit(mode: int, parents, tokens, llm, k_tree, v_tree, k_cache,
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().ttv_tree_verify_commit(
         mode, _dt(dt), B, N, V, Hkv, D, Lcap, _ptr(parents), _ptr(tokens), _ptr(llm), _ptr(ssm),
-        _ptr(u_accept), _ptr(u_bonus), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache),
+        _u64(seed), _u64(step), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache),
         _ptr(cache_len_in), _ptr(cache_len_out), int(Lmax), _ptr(path), _ptr(path_len),
         _ptr(out_tokens), _ptr(committed_src), _ptr(dev_status), _ptr(workspace), wsb,
         _stream(dev))

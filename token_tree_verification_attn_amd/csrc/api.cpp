@@ -103,67 +103,20 @@ ttv_status attn_plan(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, int Lma
 
 ttv_status launch_status(hipError_t e) { return e == hipSuccess ? TTV_OK : TTV_E_LAUNCH; }
 
-}  // namespace
-
-extern "C" {
-
-const char* ttv_status_string(ttv_status s) {
-  switch (s) {
-    case TTV_OK: return "ok";
-    case TTV_E_NULL: return "null pointer";
-    case TTV_E_SHAPE: return "bad shape or size";
-    case TTV_E_DTYPE: return "bad dtype or mode";
-    case TTV_E_UNSUPPORTED: return "unsupported size or option";
-    case TTV_E_WORKSPACE: return "workspace missing or too small";
-    case TTV_E_LAUNCH: return "kernel launch failed";
-    case TTV_E_TREE: return "malformed token tree";
-    case TTV_E_ALIGN: return "pointer not 16-byte aligned";
-    default: return "unknown status";
+// The launches of one validated ttv_tree_attn call: the topology (only when
+// its outputs are asked for; the attention kernels rebuild it in registers
+// and report the request's status), the attention kernel, the combine of
+// split partials.  ws = the partials (p.ws_bytes bytes).
+ttv_status launch_attn(const AttnPlan& p, ttv_dtype dt, int B, int N, int Hq, int Hkv, int D,
+                       float scale, const void* q, const void* k_cache, const void* v_cache,
+                       int Lcap, const int32_t* cache_len, int Lmax, const void* k_tree,
+                       const void* v_tree, const int32_t* parents, void* out, float* lse,
+                       uint64_t* anc_out, int32_t* depth_out, int32_t* dev_status, void* ws,
+                       hipStream_t s) {
+  if (anc_out || depth_out) {
+    if (launch_topology(B, N, parents, anc_out, depth_out, nullptr, s) != hipSuccess)
+      return TTV_E_LAUNCH;
   }
-}
-
-int32_t ttv_version(void) { return 100; }
-
-ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents, uint64_t* anc_out,
-                             int32_t* depth_out, int32_t* dev_status, void* stream) {
-  if (!parents) return TTV_E_NULL;
-  if (B < 1 || N < 1) return TTV_E_SHAPE;
-  if (N > TTV_MAX_NODES) return TTV_E_UNSUPPORTED;
-  return launch_status(launch_topology(B, N, parents, anc_out, depth_out, dev_status,
-                                       static_cast<hipStream_t>(stream)));
-}
-
-size_t ttv_tree_attn_workspace_size(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq,
-                                    int32_t Hkv, int32_t D, int32_t Lmax,
-                                    int32_t rows_per_block, int32_t chunk_keys) {
-  AttnPlan p;
-  if (attn_plan(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys, &p) != TTV_OK)
-    return (size_t)-1;
-  return p.ws_bytes;
-}
-
-ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
-                         int32_t D, float scale, const void* q, const void* k_cache,
-                         const void* v_cache, int32_t Lcap, const int32_t* cache_len,
-                         int32_t Lmax, const void* k_tree, const void* v_tree,
-                         const int32_t* parents, void* out, float* lse, int32_t* dev_status,
-                         void* workspace, size_t workspace_bytes, int32_t rows_per_block,
-                         int32_t chunk_keys, void* stream) {
-  if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
-  if (!q || !k_cache || !v_cache || !cache_len || !parents || !out || (!k_tree != !v_tree))
-    return TTV_E_NULL;
-  const bool tree_in_cache = !k_tree;  // both NULL: node i at cache row L_b + i
-  if (Lcap < 0 || Lmax > Lcap || !std::isfinite(scale) || !(scale > 0.f)) return TTV_E_SHAPE;
-  if (tree_in_cache && (long)Lmax + N > Lcap) return TTV_E_SHAPE;
-  AttnPlan p;
-  const ttv_status st = attn_plan(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys, &p);
-  if (st != TTV_OK) return st;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      (!tree_in_cache && (!aligned16(k_tree) || !aligned16(v_tree))) || !aligned16(out))
-    return TTV_E_ALIGN;
-  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return TTV_E_WORKSPACE;
-  if (p.ws_bytes > 0 && !aligned16(workspace)) return TTV_E_ALIGN;
-
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -171,7 +124,7 @@ ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t
   a.v_cache = v_cache;
   a.k_tree = k_tree;
   a.v_tree = v_tree;
-  a.tree_in_cache = tree_in_cache ? 1 : 0;
+  a.tree_in_cache = k_tree ? 0 : 1;
   a.cache_len = cache_len;
   a.parents = parents;
   a.out = out;
@@ -194,15 +147,98 @@ ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t
   a.items = p.items;
   a.scale_log2 = scale * 1.44269504088896340736f;
   if (p.chunks > 1) {
-    a.ws_acc = static_cast<float*>(workspace);
+    a.ws_acc = static_cast<float*>(ws);
     a.ws_ml = a.ws_acc + (size_t)B * Hkv * p.chunks * p.rows * D;
-    if (p.balanced) a.ws_nchunks = reinterpret_cast<int32_t*>(a.ws_ml + (size_t)B * Hkv * p.chunks * p.rows * 2);
+    if (p.balanced)
+      a.ws_nchunks = reinterpret_cast<int32_t*>(a.ws_ml + (size_t)B * Hkv * p.chunks * p.rows * 2);
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = p.mfma ? launch_attn_mfma(a, s) : launch_attn_fma(a, dt == TTV_BF16, s);
   if (e != hipSuccess) return TTV_E_LAUNCH;
   if (p.chunks > 1) return launch_status(launch_attn_combine(a, dt == TTV_BF16, s));
   return TTV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ttv_status_string(ttv_status s) {
+  switch (s) {
+    case TTV_OK: return "ok";
+    case TTV_E_NULL: return "null pointer";
+    case TTV_E_SHAPE: return "bad shape or size";
+    case TTV_E_DTYPE: return "bad dtype or mode";
+    case TTV_E_UNSUPPORTED: return "unsupported size or option";
+    case TTV_E_WORKSPACE: return "workspace missing or too small";
+    case TTV_E_LAUNCH: return "kernel launch failed";
+    case TTV_E_TREE: return "malformed token tree";
+    case TTV_E_ALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int32_t ttv_version(void) { return 200; }
+
+ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents, uint64_t* anc_out,
+                             int32_t* depth_out, int32_t* dev_status, void* stream) {
+  if (!parents) return TTV_E_NULL;
+  if (B < 1 || N < 1) return TTV_E_SHAPE;
+  if (N > TTV_MAX_NODES) return TTV_E_UNSUPPORTED;
+  return launch_status(launch_topology(B, N, parents, anc_out, depth_out, dev_status,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t ttv_tree_attn_tuned_workspace_size(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq,
+                                          int32_t Hkv, int32_t D, int32_t Lmax,
+                                          int32_t rows_per_block, int32_t chunk_keys) {
+  AttnPlan p;
+  if (attn_plan(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys, &p) != TTV_OK)
+    return (size_t)-1;
+  return p.ws_bytes;
+}
+
+size_t ttv_tree_attn_workspace_size(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq,
+                                    int32_t Hkv, int32_t D, int32_t Lmax) {
+  return ttv_tree_attn_tuned_workspace_size(dt, B, N, Hq, Hkv, D, Lmax, 0, 0);
+}
+
+ttv_status ttv_tree_attn_tuned(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                               int32_t D, float scale, const void* q, const void* k_cache,
+                               const void* v_cache, int32_t Lcap, const int32_t* cache_len,
+                               int32_t Lmax, const void* k_tree, const void* v_tree,
+                               const int32_t* parents, void* out, float* lse,
+                               uint64_t* anc_out, int32_t* depth_out, int32_t* dev_status,
+                               void* workspace, size_t workspace_bytes, int32_t rows_per_block,
+                               int32_t chunk_keys, void* stream) {
+  if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
+  if (!q || !k_cache || !v_cache || !cache_len || !parents || !out || (!k_tree != !v_tree))
+    return TTV_E_NULL;
+  const bool tree_in_cache = !k_tree;  // both NULL: node i at cache row L_b + i
+  if (Lcap < 0 || Lmax > Lcap || !std::isfinite(scale) || !(scale > 0.f)) return TTV_E_SHAPE;
+  if (tree_in_cache && (long)Lmax + N > Lcap) return TTV_E_SHAPE;
+  AttnPlan p;
+  const ttv_status st = attn_plan(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys, &p);
+  if (st != TTV_OK) return st;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (!tree_in_cache && (!aligned16(k_tree) || !aligned16(v_tree))) || !aligned16(out))
+    return TTV_E_ALIGN;
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return TTV_E_WORKSPACE;
+  if (p.ws_bytes > 0 && !aligned16(workspace)) return TTV_E_ALIGN;
+  return launch_attn(p, dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap, cache_len, Lmax,
+                     k_tree, v_tree, parents, out, lse, anc_out, depth_out, dev_status,
+                     workspace, static_cast<hipStream_t>(stream));
+}
+
+ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                         int32_t D, float scale, const void* q, const void* k_cache,
+                         const void* v_cache, int32_t Lcap, const int32_t* cache_len,
+                         int32_t Lmax, const void* k_tree, const void* v_tree,
+                         const int32_t* parents, void* out, float* lse, uint64_t* anc_out,
+                         int32_t* depth_out, int32_t* dev_status, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return ttv_tree_attn_tuned(dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap, cache_len,
+                             Lmax, k_tree, v_tree, parents, out, lse, anc_out, depth_out,
+                             dev_status, workspace, workspace_bytes, 0, 0, stream);
 }
 
 size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V) {
@@ -215,13 +251,12 @@ size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B, int32_t N
 
 ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V,
                            const int32_t* parents, const int32_t* tokens, const float* llm,
-                           const float* ssm, const float* u_accept, const float* u_bonus,
-                           int32_t* path, int32_t* path_len, int32_t* out_tokens,
-                           int32_t* dev_status, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           const float* ssm, uint64_t seed, uint64_t step, int32_t* path,
+                           int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   if (mode != TTV_GREEDY && mode != TTV_STOCHASTIC) return TTV_E_DTYPE;
   if (!parents || !tokens || !llm || !path || !path_len || !out_tokens) return TTV_E_NULL;
-  if (mode == TTV_STOCHASTIC && (!ssm || !u_accept || !u_bonus)) return TTV_E_NULL;
+  if (mode == TTV_STOCHASTIC && !ssm) return TTV_E_NULL;
   if (B < 1 || N < 1 || V < 1) return TTV_E_SHAPE;
   if (N > TTV_MAX_NODES) return TTV_E_UNSUPPORTED;
   if ((long)B * N > 0x7fffffffL) return TTV_E_UNSUPPORTED;
@@ -229,8 +264,9 @@ ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V
   if (mode == TTV_STOCHASTIC) {
     if (V > kMssMaxVocab) return TTV_E_UNSUPPORTED;
     if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
-    return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm, u_accept, u_bonus,
-                                           path, path_len, out_tokens, dev_status, CommitArgs{}, s));
+    return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm,
+                                           MssDraws{nullptr, nullptr, seed, step}, path,
+                                           path_len, out_tokens, dev_status, CommitArgs{}, s));
   }
   const GreedyPlan p = greedy_plan(B, N, V);
   if (p.splits > kMaxGridYZ) return TTV_E_UNSUPPORTED;
@@ -239,6 +275,24 @@ ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V
   if (!aligned16(workspace)) return TTV_E_ALIGN;
   return launch_status(launch_verify_greedy(B, N, V, parents, tokens, llm, path, path_len,
                                             out_tokens, dev_status, workspace, p, s));
+}
+
+ttv_status ttv_tree_verify_uniforms(int32_t B, int32_t N, int32_t V, const int32_t* parents,
+                                    const int32_t* tokens, const float* llm, const float* ssm,
+                                    const float* u_accept, const float* u_bonus, int32_t* path,
+                                    int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
+                                    void* stream) {
+  if (!parents || !tokens || !llm || !ssm || !u_accept || !u_bonus || !path || !path_len ||
+      !out_tokens)
+    return TTV_E_NULL;
+  if (B < 1 || N < 1 || V < 1) return TTV_E_SHAPE;
+  if (N > TTV_MAX_NODES || V > kMssMaxVocab) return TTV_E_UNSUPPORTED;
+  if ((long)B * N > 0x7fffffffL) return TTV_E_UNSUPPORTED;
+  if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
+  return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm,
+                                         MssDraws{u_accept, u_bonus, 0, 0}, path, path_len,
+                                         out_tokens, dev_status, CommitArgs{},
+                                         static_cast<hipStream_t>(stream)));
 }
 
 ttv_status ttv_kv_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv, int32_t D,
@@ -265,7 +319,7 @@ ttv_status ttv_kv_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv, int32_
 ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt, int32_t B, int32_t N,
                                   int32_t V, int32_t Hkv, int32_t D, int32_t Lcap,
                                   const int32_t* parents, const int32_t* tokens, const float* llm,
-                                  const float* ssm, const float* u_accept, const float* u_bonus,
+                                  const float* ssm, uint64_t seed, uint64_t step,
                                   const void* k_tree, const void* v_tree, void* k_cache,
                                   void* v_cache, const int32_t* cache_len_in,
                                   int32_t* cache_len_out, int32_t Lmax, int32_t* path,
@@ -277,7 +331,7 @@ ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt, int32_t B,
   if (!parents || !tokens || !llm || !k_tree || !v_tree || !k_cache || !v_cache ||
       !cache_len_in || !cache_len_out || !path || !path_len || !out_tokens)
     return TTV_E_NULL;
-  if (mode == TTV_STOCHASTIC && (!ssm || !u_accept || !u_bonus)) return TTV_E_NULL;
+  if (mode == TTV_STOCHASTIC && !ssm) return TTV_E_NULL;
   if (B < 1 || N < 1 || V < 1 || Hkv < 1 || D < 1 || Lmax < 0 || Lcap < 0) return TTV_E_SHAPE;
   if (N > TTV_MAX_NODES || (D != 64 && D != 128)) return TTV_E_UNSUPPORTED;
   if ((long)B * N > 0x7fffffffL) return TTV_E_UNSUPPORTED;
@@ -292,8 +346,9 @@ ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt, int32_t B,
     if (!aligned16(ssm)) return TTV_E_ALIGN;
     CommitArgs cm{D * elt / 16, Hkv, Lcap, Lmax, k_tree, v_tree, k_cache, v_cache,
                   cache_len_in, cache_len_out, committed_src};
-    return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm, u_accept, u_bonus,
-                                           path, path_len, out_tokens, dev_status, cm, s));
+    return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm,
+                                           MssDraws{nullptr, nullptr, seed, step}, path,
+                                           path_len, out_tokens, dev_status, cm, s));
   }
   const GreedyPlan p = greedy_plan(B, N, V);
   if (p.splits > kMaxGridYZ) return TTV_E_UNSUPPORTED;

@@ -97,13 +97,21 @@ struct CommitArgs {
   int32_t* committed_src;
 };
 
+// Uniforms of the stochastic verifier: u_accept == nullptr draws them from
+// Philox4x64-10 (seed, step); otherwise u_accept[B,N] and u_bonus[B] hold them.
+struct MssDraws {
+  const float* u_accept;
+  const float* u_bonus;
+  uint64_t seed, step;
+};
+
 // Largest vocabulary the stochastic verifier holds in LDS.
 constexpr int kMssMaxVocab = 36864;
 hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                              const int32_t* tokens, const float* llm, const float* ssm,
-                             const float* u_accept, const float* u_bonus, int32_t* path,
-                             int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
-                             const CommitArgs& cm, hipStream_t s);
+                             const MssDraws& dr, int32_t* path, int32_t* path_len,
+                             int32_t* out_tokens, int32_t* dev_status, const CommitArgs& cm,
+                             hipStream_t s);
 
 // ----------------------------------------------------------------- commit --
 hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,

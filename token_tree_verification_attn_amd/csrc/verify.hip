@@ -8,6 +8,7 @@
 #include <limits.h>
 
 #include "launch.h"
+#include "philox.h"
 #include "ttv_common.h"
 
 namespace ttv {
@@ -566,15 +567,15 @@ __device__ __forceinline__ double mss_residual_regs(const f32x4 (&r)[kMssPfChunk
 template <bool VEC, bool PF>
 __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     int N, int V, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
-    const float* __restrict__ llm, const float* __restrict__ ssm,
-    const float* __restrict__ u_accept, const float* __restrict__ u_bonus,
+    const float* __restrict__ llm, const float* __restrict__ ssm, MssDraws dr,
     int32_t* __restrict__ path, int32_t* __restrict__ path_len,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status, CommitArgs cm) {
   extern __shared__ __attribute__((aligned(16))) float s_w[];  // residual w, widx() layout
   __shared__ int32_t s_par[kMaxNodes];
   __shared__ int32_t s_tok[kMaxNodes];
   __shared__ int32_t s_path[kMaxNodes];
-  __shared__ float s_rq[kMaxNodes];  // u_accept[c] * q_c[token c]: the left side of c's test at s = 1
+  __shared__ float s_rq[kMaxNodes];  // r_c * q_c[token c]: the left side of c's test at s = 1
+  __shared__ uint32_t s_bonus[kMaxNodes];  // the final draw's 24-bit integer if the walk ends at u
   __shared__ unsigned long long s_kids[kMaxNodes][2];
   __shared__ uint64_t s_first_ok[2];
   __shared__ double s_redd[kMssThreads / 64];
@@ -582,7 +583,8 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
 
   const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
   const size_t rowN = (size_t)b * N;
-  const float ub = u_bonus[b];  // requested now, used by the final draw
+  // uniforms: drawn here from Philox (seed, step), or given by the caller
+  const bool seeded = dr.u_accept == nullptr;
   // with the commit: thread 0 alone reads the prefix length (the others take
   // it from LDS); its write of the new one, which may alias it, depends on
   // that read, and only this workgroup touches entry b
@@ -631,14 +633,36 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     return;
   }
   // children bitsets, r*q[x] of every non-root node, and its first-attempt
-  // test with w = p of its parent and mass 1 (only first children use it)
-  bool first_ok = false;
+  // test with w = p of its parent and mass 1 (only first children use it).
+  // The gathers go out first; the final-draw integer of every node (the walk
+  // may end anywhere) is computed by waves 2-3 meanwhile.
+  float qx = 0.f, px = 0.f, ua = 0.f;
   if (t >= 1 && t < N) {
     const int p = s_par[t], x = s_tok[t];
     atomicOr(&s_kids[p][t >> 6], 1ull << (t & 63));
-    const float rq = u_accept[rowN + t] * ssm[(rowN + t) * V + x];
+    qx = ssm[(rowN + t) * V + x];
+    px = llm[(rowN + p) * V + x];
+    if (!seeded) ua = dr.u_accept[rowN + t];
+  }
+  static_assert(kMssThreads >= 128 + kMaxNodes, "waves 2-3 compute the final draws");
+  if (t >= 128 && t - 128 < N) {
+    s_bonus[t - 128] = seeded ? mss_draw24(dr.seed, dr.step, kBonusOrdinal, t - 128, b)
+                              : (uint32_t)(dr.u_bonus[b] * 16777216.0f);  // exact: scaling by 2^24
+  }
+  __syncthreads();  // the children bitsets are complete
+  bool first_ok = false;
+  if (t >= 1 && t < N) {
+    const int p = s_par[t];
+    float r = ua;
+    if (seeded) {  // t is the j-th child of p, j = its lower siblings
+      const uint64_t lo = s_kids[p][0], hi = s_kids[p][1];
+      const int j = t < 64 ? __popcll(lo & ((1ull << t) - 1ull))
+                           : __popcll(lo) + __popcll(hi & ((1ull << (t - 64)) - 1ull));
+      r = (float)mss_draw24(dr.seed, dr.step, (uint64_t)j, p, b) * 0x1p-24f;
+    }
+    const float rq = r * qx;
     s_rq[t] = rq;
-    first_ok = rq * 1.0f < llm[(rowN + p) * V + x];
+    first_ok = rq * 1.0f < px;
   }
   if (wave < 2) {
     const uint64_t bal = __ballot(first_ok);
@@ -801,7 +825,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   __syncthreads();
   if (Sd > 0.0) {
     const uint64_t S = (uint64_t)Sd, lo = (uint64_t)excl, hi = (uint64_t)(excl + mine);
-    const uint64_t R = (uint64_t)(ub * 16777216.0f);
+    const uint64_t R = s_bonus[u];
     const uint64_t T = R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24);  // floor(R*S/2^24)
     if (lo <= T && T < hi) {
       // the group that crosses T from the register sums, then its entries
@@ -890,9 +914,9 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
 
 hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                              const int32_t* tokens, const float* llm, const float* ssm,
-                             const float* u_accept, const float* u_bonus, int32_t* path,
-                             int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
-                             const CommitArgs& cm, hipStream_t s) {
+                             const MssDraws& dr, int32_t* path, int32_t* path_len,
+                             int32_t* out_tokens, int32_t* dev_status, const CommitArgs& cm,
+                             hipStream_t s) {
   const size_t lds = (size_t)(V + 4 * (V >> 7) + 4) * sizeof(float);  // widx(V - 1) + 1, 16-byte padded
   const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(llm) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(ssm) & 15) == 0;
@@ -902,7 +926,7 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(B), dim3(kMssThreads), lds, s, N, V, parents, tokens, llm, ssm,
-                     u_accept, u_bonus, path, path_len, out_tokens, dev_status, cm);
+                     dr, path, path_len, out_tokens, dev_status, cm);
   return hipGetLastError();
 }
 
