@@ -10,11 +10,12 @@ Workload: B requests, each expanding F frontier nodes by the k most probable
 tokens of their speculator rows of V fp32 probabilities (softmax of N(0,2)
 logits at temperature 0.8, the stochastic workload's recipe).  Inputs are
 resident in HBM and rotated over enough copies to exceed twice the 256 MB
-MALL; the calls are replayed from a HIP graph and timed with HIP events on
-the launch stream.  One JSON line: value = frontier rows expanded per second;
-roofline = the rows' bytes (B*F*V*4, each read once) per call over the call's
-average duration, against the 8 TB/s HBM peak; cpu_baseline = the oracle on a
-bounded sample of the same rows.
+MALL; exactly --steps calls are timed, each a HIP-graph replay between two
+HIP events on the launch stream.  One JSON line: value = frontier rows
+expanded per second at the median call time; roofline = the rows' bytes
+(B*F*V*4, each read once) per call over the call's average duration, against
+the 8 TB/s HBM peak; cpu_baseline = the oracle on a bounded sample of the
+same rows.
 """
 from __future__ import annotations
 
@@ -66,6 +67,20 @@ def cpu_baseline(probs, k, budget_s):
                       % (rows, rows // F, F, V, k, el)}
 
 
+def time_calls(call, ncopies, steps, dev, stream, eager=False):
+    """Exactly `steps` calls call(i), i = 0..steps-1 (input copy i % ncopies),
+    each a HIP-graph replay of its copy's call (eager with eager=True or when
+    capture fails), timed one by one with HIP events on the launch stream
+    (bench.timed_steps).  Returns (median ms, mean ms, launch kind)."""
+    fns = []
+    for i in range(ncopies):
+        g = None if eager else bench.capture(lambda i=i: call(i), dev)
+        fns.append(g.replay if g is not None else (lambda i=i: call(i)))
+    graphed = all(getattr(f, "__self__", None) is not None for f in fns)
+    t = bench.summary(bench.timed_steps(fns, steps, stream))
+    return t["median"], t["mean"], "hip graph replay per call" if graphed else "eager"
+
+
 def bench_merge(args):
     """Merge of S speculated sequences of Ls tokens per request (each repeats
     the first 0..3 tokens of the one before, vocabulary 32000): latency per
@@ -93,13 +108,12 @@ def bench_merge(args):
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
-    g = bench.capture(lambda: [call(i) for i in range(16)], dev)
-    reps = max(1, -(-args.steps // 16))
-    ms = bench.timed(lambda i: g.replay(), reps, stream) / 16
+    ms, ms_mean, launch = time_calls(call, 1, args.steps, dev, stream)
     assert int(st.abs().sum()) == 0
     print(json.dumps({
         "metric": "tree_merge trees/s", "value": B / (ms * 1e-3), "unit": "trees/s", "n_gpus": 1,
-        "steps": reps * 16, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_mean": ms_mean, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": "merge", "B": B, "S": S, "Ls": Ls,
                    "nodes": n_out.cpu().tolist(), "launch": "hip graph replay"},
@@ -127,22 +141,22 @@ def bench_probs(args):
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
-    g = bench.capture(lambda: [call(i) for i in range(ncopies)], dev)
-    reps = max(1, -(-args.steps // ncopies))
-    ms = bench.timed(lambda i: g.replay(), reps, stream) / ncopies
+    ms, ms_mean, launch = time_calls(call, ncopies, args.steps, dev, stream)
     nbytes = B * F * V * 8
-    gbs = nbytes / (ms * 1e-3) / 1e9
+    gbs = nbytes / (ms_mean * 1e-3) / 1e9
     print(json.dumps({
         "metric": "probs_from_logits rows/s", "value": B * F / (ms * 1e-3), "unit": "rows/s",
-        "n_gpus": 1, "steps": reps * ncopies, "warmup": args.warmup, "ms_per_step": ms,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_mean": ms_mean,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "probs", "rows": B * F, "V": V, "T": args.T, "topk": args.k,
-                   "input_copies": ncopies, "launch": "hip graph replay",
+                   "input_copies": ncopies, "launch": launch,
                    "inputs": "rotated, HBM-resident"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "probs_kernel",
-                     "per_launch_algorithmic": nbytes, "avg_launch_us": ms * 1e3}}), flush=True)
+                     "per_launch_algorithmic": nbytes, "avg_launch_us": ms_mean * 1e3}}),
+          flush=True)
 
 
 def main():
@@ -191,30 +205,22 @@ def main():
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
-    g = bench.capture(lambda: [call(i) for i in range(ncopies)], dev)
-    if g is not None:
-        reps = max(1, -(-args.steps // ncopies))
-        steps = reps * ncopies
-        ms = bench.timed(lambda i: g.replay(), reps, stream) / ncopies
-        launch = "hip graph replay"
-    else:
-        steps = args.steps
-        ms = bench.timed(call, steps, stream)
-        launch = "eager"
+    steps = args.steps
+    ms, ms_mean, launch = time_calls(call, ncopies, steps, dev, stream)
     assert int(st.abs().sum()) == 0 and int((n_out != F + F * k).sum()) == 0
     rows = B * F
-    gbs = rows * V * 4 / (ms * 1e-3) / 1e9
+    gbs = rows * V * 4 / (ms_mean * 1e-3) / 1e9
     res = {
         "metric": "tree_expand frontier rows/s (one expansion level)", "value": rows / (ms * 1e-3),
         "unit": "frontier rows/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "ms_per_step": ms, "ms_per_step_mean": ms_mean, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "expand", "B": B, "F": F, "V": V, "k": k,
                    "input_copies": ncopies, "launch": launch, "inputs": "rotated, HBM-resident"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "tree_expand_kernel", "per_launch_algorithmic": rows * V * 4,
-                     "avg_launch_us": ms * 1e3},
+                     "avg_launch_us": ms_mean * 1e3},
     }
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(probs, k, args.cpu_budget)

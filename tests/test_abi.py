@@ -93,14 +93,15 @@ def test_tree_attn_host_validation(kw, status):
 
 def test_tree_attn_workspace_size_matches_plan():
     f = ttv.lib().ttv_tree_attn_tuned_workspace_size
-    # 2 chunks of 64 keys -> fp32 partials, D + 2 floats per (pair, chunk, row)
-    assert f(1, 1, 8, 4, 2, 64, 100, 0, 64) == 1 * 2 * 2 * 16 * 66 * 4
-    assert f(0, 1, 8, 4, 2, 64, 100, 0, 64) == 1 * 2 * 2 * 16 * 66 * 4
+    # 2 chunks of 64 keys -> per (pair, chunk, row): the partial output (D bf16
+    # values for bf16, D fp32 sums for fp32) and its (max, sum) in fp32
+    assert f(1, 1, 8, 4, 2, 64, 100, 0, 64) == 1 * 2 * 2 * 16 * (64 * 2 + 8)
+    assert f(0, 1, 8, 4, 2, 64, 100, 0, 64) == 1 * 2 * 2 * 16 * (64 * 4 + 8)
     assert f(1, 1, 8, 4, 2, 64, 64, 0, 64) == 0                          # one chunk
     assert f(1, 1, 129, 4, 2, 64, 64, 0, 0) == SZ_ERR
     assert f(9, 1, 8, 4, 2, 64, 64, 0, 0) == SZ_ERR
     # the binding allocates exactly that much
-    assert ttv.tree_attn_workspace_size(torch.bfloat16, 1, 8, 4, 2, 64, 100, 0, 64) == 16896
+    assert ttv.tree_attn_workspace_size(torch.bfloat16, 1, 8, 4, 2, 64, 100, 0, 64) == 8704
     # the automatic shape: no split up to 512 keys, one shape for both entry points
     g = ttv.lib().ttv_tree_attn_workspace_size
     assert g(1, 1, 8, 4, 2, 64, 100) == 0 == f(1, 1, 8, 4, 2, 64, 100, 0, 0)
@@ -270,3 +271,4 @@ def test_tree_verify_commit_takes_every_commit_shape():
     """Shared length arrays and the largest rows reach the workspace check."""
     assert verify_commit(clo=A, ws=None) == ttv.E_WORKSPACE
     assert verify_commit(dt=0, D=128, N=128, Lcap=1000, ws=None) == ttv.E_WORKSPACE
+

@@ -96,12 +96,38 @@ ttv_status attn_plan(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, int Lma
     p->chunk_keys = 0;
     p->items = (int)slots;
   }
-  p->ws_bytes = p->chunks > 1 ? (size_t)pairs * p->chunks * R * (size_t)(D + 2) * sizeof(float) : 0;
+  // partials: the output part (bf16 for bf16 outputs, fp32 sums otherwise)
+  // and the (max, sum) pair of every (pair, chunk, row)
+  const size_t part_elt = dt == TTV_BF16 ? 2 : 4;
+  p->ws_bytes = p->chunks > 1 ? (size_t)pairs * p->chunks * R * ((size_t)D * part_elt + 8) : 0;
   if (p->balanced && p->chunks > 1) p->ws_bytes += (size_t)B * sizeof(int32_t);  // chunks per request
   return TTV_OK;
 }
 
 ttv_status launch_status(hipError_t e) { return e == hipSuccess ? TTV_OK : TTV_E_LAUNCH; }
+
+}  // namespace
+
+namespace ttv {
+
+ttv_status attn_prepare(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, float scale,
+                        const void* q, const void* k_cache, const void* v_cache, int Lcap,
+                        const int32_t* cache_len, int Lmax, const void* k_tree,
+                        const void* v_tree, const int32_t* parents, const void* out,
+                        int rows_per_block, int chunk_keys, AttnPlan* p) {
+  if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
+  if (!q || !k_cache || !v_cache || !cache_len || !parents || !out || (!k_tree != !v_tree))
+    return TTV_E_NULL;
+  const bool tree_in_cache = !k_tree;  // both NULL: node i at cache row L_b + i
+  if (Lcap < 0 || Lmax > Lcap || !std::isfinite(scale) || !(scale > 0.f)) return TTV_E_SHAPE;
+  if (tree_in_cache && (long)Lmax + N > Lcap) return TTV_E_SHAPE;
+  const ttv_status st = attn_plan(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys, p);
+  if (st != TTV_OK) return st;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (!tree_in_cache && (!aligned16(k_tree) || !aligned16(v_tree))) || !aligned16(out))
+    return TTV_E_ALIGN;
+  return TTV_OK;
+}
 
 // The launches of one validated ttv_tree_attn call: the topology (only when
 // its outputs are asked for; the attention kernels rebuild it in registers
@@ -147,10 +173,11 @@ ttv_status launch_attn(const AttnPlan& p, ttv_dtype dt, int B, int N, int Hq, in
   a.items = p.items;
   a.scale_log2 = scale * 1.44269504088896340736f;
   if (p.chunks > 1) {
-    a.ws_acc = static_cast<float*>(ws);
-    a.ws_ml = a.ws_acc + (size_t)B * Hkv * p.chunks * p.rows * D;
-    if (p.balanced)
-      a.ws_nchunks = reinterpret_cast<int32_t*>(a.ws_ml + (size_t)B * Hkv * p.chunks * p.rows * 2);
+    const size_t parts = (size_t)B * Hkv * p.chunks * p.rows;
+    char* w = static_cast<char*>(ws);
+    a.ws_acc = reinterpret_cast<float*>(w);
+    a.ws_ml = reinterpret_cast<float*>(w + parts * D * (dt == TTV_BF16 ? 2 : 4));
+    if (p.balanced) a.ws_nchunks = reinterpret_cast<int32_t*>(a.ws_ml + parts * 2);
   }
   const hipError_t e = p.mfma ? launch_attn_mfma(a, s) : launch_attn_fma(a, dt == TTV_BF16, s);
   if (e != hipSuccess) return TTV_E_LAUNCH;
@@ -158,7 +185,7 @@ ttv_status launch_attn(const AttnPlan& p, ttv_dtype dt, int B, int N, int Hq, in
   return TTV_OK;
 }
 
-}  // namespace
+}  // namespace ttv
 
 extern "C" {
 
@@ -210,18 +237,11 @@ ttv_status ttv_tree_attn_tuned(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, i
                                uint64_t* anc_out, int32_t* depth_out, int32_t* dev_status,
                                void* workspace, size_t workspace_bytes, int32_t rows_per_block,
                                int32_t chunk_keys, void* stream) {
-  if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
-  if (!q || !k_cache || !v_cache || !cache_len || !parents || !out || (!k_tree != !v_tree))
-    return TTV_E_NULL;
-  const bool tree_in_cache = !k_tree;  // both NULL: node i at cache row L_b + i
-  if (Lcap < 0 || Lmax > Lcap || !std::isfinite(scale) || !(scale > 0.f)) return TTV_E_SHAPE;
-  if (tree_in_cache && (long)Lmax + N > Lcap) return TTV_E_SHAPE;
   AttnPlan p;
-  const ttv_status st = attn_plan(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys, &p);
+  const ttv_status st = attn_prepare(dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap,
+                                     cache_len, Lmax, k_tree, v_tree, parents, out,
+                                     rows_per_block, chunk_keys, &p);
   if (st != TTV_OK) return st;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      (!tree_in_cache && (!aligned16(k_tree) || !aligned16(v_tree))) || !aligned16(out))
-    return TTV_E_ALIGN;
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return TTV_E_WORKSPACE;
   if (p.ws_bytes > 0 && !aligned16(workspace)) return TTV_E_ALIGN;
   return launch_attn(p, dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap, cache_len, Lmax,

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ttv.h"
+
 namespace ttv {
 
 // ------------------------------------------------------------- attention --
@@ -35,8 +37,8 @@ struct AttnArgs {
   float* lse;
   int32_t* dev_status;
   float* ws_acc;   // [B*Hkv][chunks][R][D] partial outputs: fp32 sums (fp32 output), or
-                   // the normalised output as bf16 at the same index (bf16 output)
-  float* ws_ml;    // [B*Hkv][chunks][R][2]  running max (log2 units) and sum
+                   // the normalised output in bf16 (bf16 output; 2 bytes per element)
+  float* ws_ml;    // [B*Hkv][chunks][R][2]  running max (log2 units) and sum, right after
   int32_t* ws_nchunks;  // [B] balanced split: chunks request b got
   int B, N, Hq, Hkv, G, D, Lcap, Lmax, R;
   int rows_per_block, chunk_keys, chunks;
@@ -49,6 +51,21 @@ struct AttnArgs {
 // and at least this many 64-key tiles per chunk.
 constexpr int kBalancedMaxB = 64;
 constexpr int kBalancedMinTiles = 2;
+
+// Host validation of one ttv_tree_attn call (everything but the workspace)
+// and its launch plan.
+ttv_status attn_prepare(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, float scale,
+                        const void* q, const void* k_cache, const void* v_cache, int Lcap,
+                        const int32_t* cache_len, int Lmax, const void* k_tree,
+                        const void* v_tree, const int32_t* parents, const void* out,
+                        int rows_per_block, int chunk_keys, AttnPlan* p);
+// The launches of a validated call; ws = p.ws_bytes of device scratch.
+ttv_status launch_attn(const AttnPlan& p, ttv_dtype dt, int B, int N, int Hq, int Hkv, int D,
+                       float scale, const void* q, const void* k_cache, const void* v_cache,
+                       int Lcap, const int32_t* cache_len, int Lmax, const void* k_tree,
+                       const void* v_tree, const int32_t* parents, void* out, float* lse,
+                       uint64_t* anc_out, int32_t* depth_out, int32_t* dev_status, void* ws,
+                       hipStream_t s);
 
 hipError_t launch_attn_fma(const AttnArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
