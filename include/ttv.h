@@ -29,8 +29,9 @@
  *  - Node 0 of every tree is its root; a tree is valid iff parents[0] == -1 and
  *    0 <= parents[i] < i for i >= 1 (any topological numbering; depth-first is
  *    one valid numbering but is not assumed).
- *  - The library holds no global state; calls on different streams are
- *    independent as long as their output buffers do not overlap.
+ *  - The library holds no global state (except the static scratch of
+ *    ttv_tree_attn_noalloc); calls on different streams are independent as
+ *    long as their output buffers do not overlap.
  */
 #ifndef TTV_H
 #define TTV_H
@@ -52,7 +53,9 @@ enum {
   TTV_E_WORKSPACE = 5,   /* workspace NULL or smaller than *_workspace_size    */
   TTV_E_LAUNCH = 6,      /* a kernel launch failed (hipGetLastError)           */
   TTV_E_TREE = 7,        /* device: malformed parents[] of one request         */
-  TTV_E_ALIGN = 8        /* a tensor pointer is not 16-byte aligned            */
+  TTV_E_ALIGN = 8,       /* a tensor pointer is not 16-byte aligned            */
+  TTV_E_SCRATCH = 9      /* needs more than the no-allocation entry point's
+                            static scratch (TTV_NOALLOC_SCRATCH_BYTES)         */
 };
 
 typedef int32_t ttv_dtype;
@@ -185,6 +188,40 @@ size_t ttv_tree_attn_tuned_workspace_size(ttv_dtype dt, int32_t B, int32_t N,
                                           int32_t Hq, int32_t Hkv, int32_t D,
                                           int32_t Lmax, int32_t rows_per_block,
                                           int32_t chunk_keys);
+
+/* Bytes of the device array ttv_tree_attn_noalloc keeps its partials in. */
+#define TTV_NOALLOC_SCRATCH_BYTES (48u << 20)
+
+/*
+ * ttv_tree_attn_noalloc -- ttv_tree_attn_tuned without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, results and errors are those of ttv_tree_attn_tuned (0, 0 for
+ * rows_per_block, chunk_keys: the automatic shape of ttv_tree_attn), and so
+ * are the kernels.  The split-KV partials go to a static device array of
+ * TTV_NOALLOC_SCRATCH_BYTES (48 MiB) that each GPU the library runs on holds
+ * until the process ends; a call whose ttv_tree_attn_tuned_workspace_size
+ * exceeds it returns TTV_E_SCRATCH before anything is enqueued.  (The
+ * automatic shape needs at most about 35 MB of partials, e.g. 33 MiB for 4
+ * requests x 8 kv heads x 1024 query rows x 32768 keys; small forced chunks
+ * can need more.)  The
+ * array's address on the current device is looked up on the first call made
+ * on that device (a failure there gives TTV_E_LAUNCH).  Nothing is allocated
+ * or freed.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller; the array needs no initialisation.
+ */
+ttv_status ttv_tree_attn_noalloc(ttv_dtype dt, int32_t B, int32_t N,
+                                 int32_t Hq, int32_t Hkv, int32_t D,
+                                 float scale, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 int32_t Lcap, const int32_t* cache_len,
+                                 int32_t Lmax, const void* k_tree,
+                                 const void* v_tree, const int32_t* parents,
+                                 void* out, float* lse, uint64_t* anc_out,
+                                 int32_t* depth_out, int32_t* dev_status,
+                                 int32_t rows_per_block, int32_t chunk_keys,
+                                 void* stream);
 
 /*
  * ttv_tree_verify -- verify every request's token tree against the LLM's

@@ -53,7 +53,7 @@ def test_library_links_no_torch():
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(10):
         assert ttv.status_string(s) != "unknown status"
     assert ttv.status_string(99) == "unknown status"
 
@@ -272,3 +272,35 @@ def test_tree_verify_commit_takes_every_commit_shape():
     assert verify_commit(clo=A, ws=None) == ttv.E_WORKSPACE
     assert verify_commit(dt=0, D=128, N=128, Lcap=1000, ws=None) == ttv.E_WORKSPACE
 
+
+def noalloc(**kw):
+    args = dict(dt=1, B=1, N=8, Hq=4, Hkv=2, D=64, scale=0.125, q=A, kc=A, vc=A, Lcap=128,
+                cl=A, Lmax=100, kt=A, vt=A, par=A, out=A, lse=None, anc=None, depth=None,
+                st=None, rpb=0, ck=0)
+    args.update(kw)
+    return ttv.lib().ttv_tree_attn_noalloc(*args.values(), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), ttv.E_DTYPE), (dict(q=None), ttv.E_NULL), (dict(kt=None), ttv.E_NULL),
+    (dict(B=0), ttv.E_SHAPE), (dict(Lmax=129), ttv.E_SHAPE), (dict(scale=0.0), ttv.E_SHAPE),
+    (dict(N=129), ttv.E_UNSUPPORTED), (dict(D=96), ttv.E_UNSUPPORTED), (dict(q=MIS), ttv.E_ALIGN),
+    (dict(rpb=96), ttv.E_UNSUPPORTED), (dict(ck=100), ttv.E_UNSUPPORTED),
+    # 4 requests x 8 kv heads x 1024 rows x 32768 keys in 128-key chunks: 4.3 GB of partials
+    (dict(B=4, N=128, Hq=64, Hkv=8, D=128, Lcap=32768 + 128, Lmax=32768, ck=128),
+     ttv.E_SCRATCH),
+])
+def test_tree_attn_noalloc_host_validation(kw, status):
+    """The no-allocation entry point validates like ttv_tree_attn and refuses
+    a call whose partials exceed its static scratch before any HIP call."""
+    assert noalloc(**kw) == status
+
+
+def test_noalloc_scratch_limit_is_the_stated_one():
+    f = ttv.lib().ttv_tree_attn_tuned_workspace_size
+    assert f(1, 4, 128, 64, 8, 128, 32768, 0, 128) > ttv.NOALLOC_SCRATCH_BYTES
+    # the automatic shape of the long-context workload fits
+    assert 0 < f(1, 4, 128, 64, 8, 128, 32768, 0, 0) <= ttv.NOALLOC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert "#define TTV_NOALLOC_SCRATCH_BYTES (48u << 20)" in text
+    assert ttv.NOALLOC_SCRATCH_BYTES == 48 << 20

@@ -25,13 +25,16 @@ import torch
 
 __all__ = ["tree_topology", "tree_attn", "tree_verify", "tree_verify_uniforms", "kv_commit",
            "tree_verify_commit", "tree_expand", "tree_merge", "probs_from_logits",
-           "kv_commit_inplace", "tree_attn_workspace_size", "tree_verify_workspace_size",
+           "kv_commit_inplace", "tree_attn_noalloc", "tree_attn_workspace_size",
+           "tree_verify_workspace_size",
            "status_string",
            "TTVError", "LibraryNotBuilt", "lib", "LIB_PATH", "GREEDY", "STOCHASTIC"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttv.so")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH, E_TREE, E_ALIGN = range(9)
+(OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH, E_TREE, E_ALIGN,
+ E_SCRATCH) = range(10)
+NOALLOC_SCRATCH_BYTES = 48 << 20
 F32, BF16 = 0, 1
 GREEDY, STOCHASTIC = 0, 1
 MAX_NODES = 128
@@ -68,6 +71,8 @@ def lib():
                                     _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.ttv_tree_attn_tuned.argtypes = [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P, _I, _P,
                                           _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _P]
+        L.ttv_tree_attn_noalloc.argtypes = [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P, _I,
+                                            _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P]
         L.ttv_tree_attn_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I]
         L.ttv_tree_attn_workspace_size.restype = _SZ
         L.ttv_tree_attn_tuned_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I]
@@ -89,7 +94,8 @@ def lib():
                                              _U64, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
                                              _P, _SZ, _P]
         for f in ("ttv_tree_verify_commit", "ttv_kv_commit_inplace", "ttv_tree_topology",
-                  "ttv_tree_attn", "ttv_tree_attn_tuned", "ttv_tree_verify",
+                  "ttv_tree_attn", "ttv_tree_attn_tuned", "ttv_tree_attn_noalloc",
+                  "ttv_tree_verify",
                   "ttv_tree_verify_uniforms", "ttv_kv_commit", "ttv_tree_expand",
                   "ttv_tree_merge", "ttv_probs_from_logits"):
             getattr(L, f).restype = _I
@@ -212,6 +218,48 @@ def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int
                                                                 chunk_keys, _stream(dev)))
     else:
         _check("ttv_tree_attn", lib().ttv_tree_attn(*args, _stream(dev)))
+    return out, lse, dev_status
+
+
+def tree_attn_noalloc(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int,
+                      scale: Optional[float] = None, out=None, lse=None, dev_status=None,
+                      anc_out=None, depth_out=None, rows_per_block: int = 0,
+                      chunk_keys: int = 0):
+    """tree_attn without a workspace: the library keeps the split partials in
+    its own static device array (ttv_tree_attn_noalloc), so the call itself
+    allocates nothing when out, lse and dev_status are given (None: allocated
+    here by torch).  Calls on one GPU must not overlap in time."""
+    B, N, Hq, D = q.shape
+    Hkv, Lcap = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    dt = q.dtype
+    _need(q, "q", dt, (B, N, Hq, D), dev)
+    _need(k_cache, "k_cache", dt, (B, Hkv, Lcap, D), dev)
+    _need(v_cache, "v_cache", dt, (B, Hkv, Lcap, D), dev)
+    if k_tree is not None or v_tree is not None:
+        _need(k_tree, "k_tree", dt, (B, Hkv, N, D), dev)
+        _need(v_tree, "v_tree", dt, (B, Hkv, N, D), dev)
+    _need(cache_len, "cache_len", torch.int32, (B,), dev)
+    _need(parents, "parents", torch.int32, (B, N), dev)
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, N, Hq, D), dtype=dt, device=dev)
+    _need(out, "out", dt, (B, N, Hq, D), dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, N, Hq), dev)
+    if anc_out is not None:
+        _need(anc_out, "anc_out", torch.int64, (B, N, (N + 63) // 64), dev)
+    if depth_out is not None:
+        _need(depth_out, "depth_out", torch.int32, (B, N), dev)
+    if dev_status is None:
+        dev_status = torch.empty(B, dtype=torch.int32, device=dev)
+    st = lib().ttv_tree_attn_noalloc(_dt(dt), B, N, Hq, Hkv, D, float(scale), _ptr(q),
+                                     _ptr(k_cache), _ptr(v_cache), Lcap, _ptr(cache_len),
+                                     int(Lmax), _ptr(k_tree), _ptr(v_tree), _ptr(parents),
+                                     _ptr(out), _ptr(lse), _ptr(anc_out), _ptr(depth_out),
+                                     _ptr(dev_status), rows_per_block, chunk_keys, _stream(dev))
+    _check("ttv_tree_attn_noalloc", st)
     return out, lse, dev_status
 
 

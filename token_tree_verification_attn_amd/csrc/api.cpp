@@ -200,6 +200,7 @@ const char* ttv_status_string(ttv_status s) {
     case TTV_E_LAUNCH: return "kernel launch failed";
     case TTV_E_TREE: return "malformed token tree";
     case TTV_E_ALIGN: return "pointer not 16-byte aligned";
+    case TTV_E_SCRATCH: return "needs more than the no-allocation entry point's static scratch";
     default: return "unknown status";
   }
 }
