@@ -48,11 +48,11 @@ def build(force: bool = False) -> str:
 def _bind(lib):
     P = ctypes.c_void_p
     I = ctypes.c_int
-    lib.orc_topology.argtypes = [I, I, P, P, P, P]
+    lib.orc_topology.argtypes = [I, I, P, P, P, P, P]
     lib.orc_tree_attn_rows.argtypes = [I, I, I, I, I, ctypes.c_double, P, P, P, I,
-                                       P, P, P, P, I, P, P, P, P]
-    lib.orc_verify_greedy.argtypes = [I, I, I, P, P, P, P, P, P, P]
-    lib.orc_verify_mss.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P]
+                                       P, P, P, P, P, I, P, P, P, P]
+    lib.orc_verify_greedy.argtypes = [I, I, I, P, P, P, P, P, P, P, P]
+    lib.orc_verify_mss.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P, P, P]
     lib.orc_kv_commit.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
     lib.orc_tree_expand.argtypes = [I, I, I, I, P, P, P, I, P, P, P, P, P]
     lib.orc_tree_merge.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P]
@@ -60,7 +60,7 @@ def _bind(lib):
     lib.orc_kv_commit_inplace.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]
     U64 = ctypes.c_uint64
     lib.orc_philox4x64_10.argtypes = [P, P, P]
-    lib.orc_verify_mss_seeded.argtypes = [I, I, I, P, P, P, P, U64, U64, P, P, P, P]
+    lib.orc_verify_mss_seeded.argtypes = [I, I, I, P, P, P, P, P, U64, U64, P, P, P, P]
     lib.orc_set_threads.argtypes = [I]
     lib.orc_max_threads.restype = I
     for f in (lib.orc_kv_commit_inplace, lib.orc_topology, lib.orc_tree_attn_rows, lib.orc_verify_greedy,
@@ -97,30 +97,44 @@ def _c(a, dtype):
     return a, a.ctypes.data_as(ctypes.c_void_p)
 
 
-def topology(parents):
+def _nodes(n_nodes, B):
+    """Per-request node counts int32 [B] (a batch of trees of different
+    sizes, each in the first n_nodes[b] entries of its rows), or None: every
+    request has N nodes."""
+    if n_nodes is None:
+        return None, None
+    a, p = _c(n_nodes, np.int32)
+    assert a.shape == (B,)
+    return a, p
+
+
+def topology(parents, n_nodes=None):
     """[SI] §4 "Tree Attention": depth and root->node ancestor bitsets.
 
-    parents int32 [B,N] -> (depth int32 [B,N], anc uint64 [B,N,W], status [B]).
+    parents int32 [B,N], n_nodes int32 [B] or None -> (depth int32 [B,N],
+    anc uint64 [B,N,W], status [B]); padding nodes get depth -1, no bits.
     """
     par, pp = _c(parents, np.int32)
     B, N = par.shape
+    nn, nnp = _nodes(n_nodes, B)
     W = (N + 63) // 64
     depth = np.empty((B, N), np.int32)
     anc = np.empty((B, N, W), np.uint64)
     status = np.empty(B, np.int32)
-    _load().orc_topology(B, N, pp, depth.ctypes.data_as(ctypes.c_void_p),
+    _load().orc_topology(B, N, pp, nnp, depth.ctypes.data_as(ctypes.c_void_p),
                          anc.ctypes.data_as(ctypes.c_void_p),
                          status.ctypes.data_as(ctypes.c_void_p))
     return depth, anc, status
 
 
 def tree_attn_rows(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, scale,
-                   rows):
+                   rows, n_nodes=None):
     """[SI] §4 "Tree Attention"/"Tree-Based Parallel Decoding", [SSD] §3.
 
     Attention of the listed rows (b, i, hq) over prefix ++ path(root -> i), in
     fp64.  q [B,N,Hq,D], k/v_cache [B,Hkv,Lcap,D], k/v_tree [B,Hkv,N,D] (any
-    float type; widened to float32 exactly), rows int [R,3].
+    float type; widened to float32 exactly), rows int [R,3], n_nodes int32
+    [B] or None (rows of padding nodes i >= n_nodes[b] are zero).
     Returns (out float64 [R,D], lse float64 [R], status int32 [R]).
     """
     q, qp = _c(q, np.float32)
@@ -139,11 +153,12 @@ def tree_attn_rows(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, scal
     assert rows.size == 0 or (rows[:, 0].min() >= 0 and rows[:, 0].max() < B
                               and rows[:, 2].min() >= 0 and rows[:, 2].max() < Hq)
     R = rows.shape[0]
+    nn, nnp = _nodes(n_nodes, B)
     out = np.zeros((R, D), np.float64)
     lse = np.zeros(R, np.float64)
     status = np.zeros(R, np.int32)
     _load().orc_tree_attn_rows(B, N, Hq, Hkv, D, float(scale), qp, kcp, vcp, Lcap, clp,
-                               ktp, vtp, pp, R, rp,
+                               ktp, vtp, pp, nnp, R, rp,
                                out.ctypes.data_as(ctypes.c_void_p),
                                lse.ctypes.data_as(ctypes.c_void_p),
                                status.ctypes.data_as(ctypes.c_void_p))
@@ -156,19 +171,19 @@ def all_rows(B, N, Hq):
     return np.stack([b.ravel(), i.ravel(), h.ravel()], axis=1).astype(np.int32)
 
 
-def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, scale):
+def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, scale, n_nodes=None):
     """Full output [B,N,Hq,D] (fp64), lse [B,N,Hq], per-row status."""
     B, N, Hq, D = np.shape(q)
     out, lse, st = tree_attn_rows(q, k_cache, v_cache, cache_len, k_tree, v_tree,
-                                  parents, scale, all_rows(B, N, Hq))
+                                  parents, scale, all_rows(B, N, Hq), n_nodes)
     return out.reshape(B, N, Hq, D), lse.reshape(B, N, Hq), st.reshape(B, N, Hq)
 
 
-def verify_greedy(parents, tokens, llm):
+def verify_greedy(parents, tokens, llm, n_nodes=None):
     """[SI] §4 "Token Tree Verification", §6: greedy acceptance of the tree.
 
-    parents/tokens int32 [B,N], llm float32 [B,N,V] logits.
-    Returns (path [B,N], path_len [B], out_tokens [B,N], status [B]).
+    parents/tokens int32 [B,N], llm float32 [B,N,V] logits, n_nodes int32 [B]
+    or None.  Returns (path [B,N], path_len [B], out_tokens [B,N], status [B]).
     """
     par, pp = _c(parents, np.int32)
     tok, tp = _c(tokens, np.int32)
@@ -176,18 +191,19 @@ def verify_greedy(parents, tokens, llm):
     B, N = par.shape
     V = lg.shape[2]
     assert lg.shape == (B, N, V) and tok.shape == (B, N)
+    nn, nnp = _nodes(n_nodes, B)
     path = np.empty((B, N), np.int32)
     plen = np.empty(B, np.int32)
     outt = np.empty((B, N), np.int32)
     st = np.empty(B, np.int32)
-    _load().orc_verify_greedy(B, N, V, pp, tp, lp, path.ctypes.data_as(ctypes.c_void_p),
+    _load().orc_verify_greedy(B, N, V, pp, tp, nnp, lp, path.ctypes.data_as(ctypes.c_void_p),
                               plen.ctypes.data_as(ctypes.c_void_p),
                               outt.ctypes.data_as(ctypes.c_void_p),
                               st.ctypes.data_as(ctypes.c_void_p))
     return path, plen, outt, st
 
 
-def verify_mss(parents, tokens, llm, ssm, u_accept, u_bonus):
+def verify_mss(parents, tokens, llm, ssm, u_accept, u_bonus, n_nodes=None):
     """[SI] §4 "Token Verification": multi-step speculative sampling.
 
     llm/ssm float32 [B,N,V] probabilities, u_accept float32 [B,N], u_bonus
@@ -203,11 +219,12 @@ def verify_mss(parents, tokens, llm, ssm, u_accept, u_bonus):
     V = p.shape[2]
     assert p.shape == (B, N, V) and q.shape == p.shape
     assert ua.shape == (B, N) and ub.shape == (B,) and tok.shape == (B, N)
+    nn, nnp = _nodes(n_nodes, B)
     path = np.empty((B, N), np.int32)
     plen = np.empty(B, np.int32)
     outt = np.empty((B, N), np.int32)
     st = np.empty(B, np.int32)
-    _load().orc_verify_mss(B, N, V, pp, tp, ppr, qpr, uap, ubp,
+    _load().orc_verify_mss(B, N, V, pp, tp, nnp, ppr, qpr, uap, ubp,
                            path.ctypes.data_as(ctypes.c_void_p),
                            plen.ctypes.data_as(ctypes.c_void_p),
                            outt.ctypes.data_as(ctypes.c_void_p),
@@ -227,7 +244,7 @@ def philox4x64_10(counter, key):
     return out
 
 
-def verify_mss_seeded(parents, tokens, llm, ssm, seed, step):
+def verify_mss_seeded(parents, tokens, llm, ssm, seed, step, n_nodes=None):
     """[SI] §4 "Token Verification": multi-step speculative sampling with the
     uniforms drawn from Philox4x64-10, key (seed, 0): the ratio test of the
     j-th child (ascending node index) of node u in request b takes counter
@@ -241,12 +258,13 @@ def verify_mss_seeded(parents, tokens, llm, ssm, seed, step):
     B, N = par.shape
     V = p.shape[2]
     assert p.shape == (B, N, V) and q.shape == p.shape and tok.shape == (B, N)
+    nn, nnp = _nodes(n_nodes, B)
     path = np.empty((B, N), np.int32)
     plen = np.empty(B, np.int32)
     outt = np.empty((B, N), np.int32)
     st = np.empty(B, np.int32)
     P = ctypes.c_void_p
-    _load().orc_verify_mss_seeded(B, N, V, pp, tp, ppr, qpr, int(seed) & (2**64 - 1),
+    _load().orc_verify_mss_seeded(B, N, V, pp, tp, nnp, ppr, qpr, int(seed) & (2**64 - 1),
                                   int(step) & (2**64 - 1), path.ctypes.data_as(P),
                                   plen.ctypes.data_as(P), outt.ctypes.data_as(P),
                                   st.ctypes.data_as(P))

@@ -41,22 +41,36 @@ static int tree_is_valid(int N, const int32_t* par) {
   return 1;
 }
 
+/* Nodes of request b: n_nodes[b] when given (a batch of trees of different
+ * sizes stored in rows of N entries; entries at or past n_nodes[b] are
+ * padding and never read), else N.  [SI] §5 "Scheduling": requests of a
+ * continuous batch are verified together whatever their tree sizes. */
+static int nodes_of(const int32_t* n_nodes, int b, int N) {
+  return n_nodes ? n_nodes[b] : N;
+}
+
 /* depth[b,i] = edges from the root; anc[b,i,w] = bitset of the nodes on the
- * path root -> i (i included), found by walking the parent pointers. */
-void orc_topology(int B, int N, const int32_t* parents, int32_t* depth,
-                  uint64_t* anc, int32_t* status) {
+ * path root -> i (i included), found by walking the parent pointers.  Padding
+ * nodes (i >= n) get depth -1 and no bits; n outside [1, N] is ORC_E_SHAPE. */
+void orc_topology(int B, int N, const int32_t* parents, const int32_t* n_nodes,
+                  int32_t* depth, uint64_t* anc, int32_t* status) {
   const int W = (N + 63) / 64;
   for (int b = 0; b < B; ++b) {
     const int32_t* par = parents + (size_t)b * N;
     int32_t* dep = depth + (size_t)b * N;
     uint64_t* an = anc + (size_t)b * N * W;
+    const int n = nodes_of(n_nodes, b, N);
     memset(an, 0, sizeof(uint64_t) * (size_t)N * W);
-    if (!tree_is_valid(N, par)) {
-      for (int i = 0; i < N; ++i) dep[i] = -1;
+    for (int i = 0; i < N; ++i) dep[i] = -1;
+    if (n < 1 || n > N) {
+      status[b] = ORC_E_SHAPE;
+      continue;
+    }
+    if (!tree_is_valid(n, par)) {
       status[b] = ORC_E_TREE;
       continue;
     }
-    for (int i = 0; i < N; ++i) {
+    for (int i = 0; i < n; ++i) {
       int d = -1;
       for (int j = i; j != -1; j = par[j]) {
         an[(size_t)i * W + j / 64] |= (uint64_t)1 << (j % 64);
@@ -81,15 +95,16 @@ void orc_topology(int B, int N, const int32_t* parents, int32_t* depth,
 /* Only the listed rows (b, i, hq) are computed, so a large problem can be     */
 /* checked on a sample.  Inputs are float arrays holding the exact values      */
 /* (bf16 widens to float exactly).  status[r]: 0, ORC_E_TREE, ORC_E_SHAPE;     */
-/* a rejected row gets o = 0 and lse = 0.                                      */
+/* a rejected row gets o = 0 and lse = 0.  With n_nodes, rows of padding       */
+/* nodes (i >= n_nodes[b]) are 0 with the request's status.                    */
 /* ------------------------------------------------------------------------ */
 void orc_tree_attn_rows(int B, int N, int Hq, int Hkv, int D, double scale,
                         const float* q, const float* k_cache,
                         const float* v_cache, int Lcap,
                         const int32_t* cache_len, const float* k_tree,
                         const float* v_tree, const int32_t* parents,
-                        int nrows, const int32_t* rows, double* out,
-                        double* lse, int32_t* status) {
+                        const int32_t* n_nodes, int nrows, const int32_t* rows,
+                        double* out, double* lse, int32_t* status) {
   const int G = Hq / Hkv;
   (void)B;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -101,8 +116,11 @@ void orc_tree_attn_rows(int B, int N, int Hq, int Hkv, int D, double scale,
     double* o = out + (size_t)r * D;
     for (int d = 0; d < D; ++d) o[d] = 0.0;
     lse[r] = 0.0;
-    if (!tree_is_valid(N, par)) { status[r] = ORC_E_TREE; continue; }
+    const int n = nodes_of(n_nodes, b, N);
+    if (n < 1 || n > N) { status[r] = ORC_E_SHAPE; continue; }
+    if (!tree_is_valid(n, par)) { status[r] = ORC_E_TREE; continue; }
     if (L < 0 || L > Lcap || i < 0 || i >= N) { status[r] = ORC_E_SHAPE; continue; }
+    if (i >= n) { status[r] = ORC_OK; continue; } /* a padding node: zero output */
 
     /* the key/value rows of the sequence node i represents */
     int* path = (int*)malloc(sizeof(int) * (size_t)N);
@@ -171,9 +189,9 @@ static int write_path(int N, const int32_t* par, int end, int32_t* path) {
 /*   path = root -> d; out_tokens = tokens of path[1..], then amax[d].        */
 /* ------------------------------------------------------------------------ */
 void orc_verify_greedy(int B, int N, int V, const int32_t* parents,
-                       const int32_t* tokens, const float* llm, int32_t* path,
-                       int32_t* path_len, int32_t* out_tokens,
-                       int32_t* status) {
+                       const int32_t* tokens, const int32_t* n_nodes,
+                       const float* llm, int32_t* path, int32_t* path_len,
+                       int32_t* out_tokens, int32_t* status) {
   int32_t* amax = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
   int32_t* dep = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
   char* acc = (char*)malloc((size_t)N);
@@ -182,13 +200,19 @@ void orc_verify_greedy(int B, int N, int V, const int32_t* parents,
     const int32_t* tok = tokens + (size_t)b * N;
     int32_t* pb = path + (size_t)b * N;
     int32_t* ob = out_tokens + (size_t)b * N;
+    const int n = nodes_of(n_nodes, b, N);
     for (int k = 0; k < N; ++k) { pb[k] = -1; ob[k] = -1; }
-    if (!tree_is_valid(N, par)) {
+    if (n < 1 || n > N) {
+      path_len[b] = 0;
+      status[b] = ORC_E_SHAPE;
+      continue;
+    }
+    if (!tree_is_valid(n, par)) {
       path_len[b] = 0;
       status[b] = ORC_E_TREE;
       continue;
     }
-    for (int u = 0; u < N; ++u) {
+    for (int u = 0; u < n; ++u) {
       const float* row = llm + ((size_t)b * N + u) * V;
       int best = 0;
       for (int v = 1; v < V; ++v)
@@ -197,12 +221,12 @@ void orc_verify_greedy(int B, int N, int V, const int32_t* parents,
     }
     acc[0] = 1;
     dep[0] = 0;
-    for (int c = 1; c < N; ++c) {
+    for (int c = 1; c < n; ++c) {
       dep[c] = dep[par[c]] + 1;
       acc[c] = acc[par[c]] && tok[c] == amax[par[c]];
     }
     int end = 0;
-    for (int c = 1; c < N; ++c)
+    for (int c = 1; c < n; ++c)
       if (acc[c] && dep[c] > dep[end]) end = c;
     int len = write_path(N, par, end, pb);
     for (int k = 0; k + 1 < len; ++k) ob[k] = tok[pb[k + 1]];
@@ -302,18 +326,23 @@ static int sample_from(const float* w, int V, uint64_t R) {
 
 /* One request's walk; the uniforms come from u_accept/u_bonus when they are
  * given (seeded == 0), else from Philox (seed, step). */
-static void mss_request(int b, int N, int V, const int32_t* par, const int32_t* tok,
+static void mss_request(int b, int N, int n, int V, const int32_t* par, const int32_t* tok,
                         const float* llm, const float* ssm, const float* u_accept,
                         const float* u_bonus, int seeded, uint64_t seed, uint64_t step,
                         int32_t* pb, int32_t* ob, int32_t* path_len, int32_t* status) {
   for (int k = 0; k < N; ++k) { pb[k] = -1; ob[k] = -1; }
-  if (!tree_is_valid(N, par)) {
+  if (n < 1 || n > N) {
+    path_len[b] = 0;
+    status[b] = ORC_E_SHAPE;
+    return;
+  }
+  if (!tree_is_valid(n, par)) {
     path_len[b] = 0;
     status[b] = ORC_E_TREE;
     return;
   }
   int tokens_ok = 1; /* every drafted token must index the vocabulary */
-  for (int c = 1; c < N; ++c)
+  for (int c = 1; c < n; ++c)
     if (tok[c] < 0 || tok[c] >= V) tokens_ok = 0;
   if (!tokens_ok) {
     path_len[b] = 0;
@@ -328,7 +357,7 @@ static void mss_request(int b, int N, int V, const int32_t* par, const int32_t* 
     float s = 1.0f;
     int next = -1;
     uint64_t j = 0; /* attempt ordinal at u */
-    for (int c = u + 1; c < N; ++c) { /* children of u, ascending index */
+    for (int c = u + 1; c < n; ++c) { /* children of u, ascending index */
       if (par[c] != u) continue;
       const float* qc = ssm + ((size_t)b * N + c) * V;
       const int x = tok[c];
@@ -363,23 +392,24 @@ static void mss_request(int b, int N, int V, const int32_t* par, const int32_t* 
 }
 
 void orc_verify_mss(int B, int N, int V, const int32_t* parents,
-                    const int32_t* tokens, const float* llm, const float* ssm,
-                    const float* u_accept, const float* u_bonus, int32_t* path,
-                    int32_t* path_len, int32_t* out_tokens, int32_t* status) {
+                    const int32_t* tokens, const int32_t* n_nodes, const float* llm,
+                    const float* ssm, const float* u_accept, const float* u_bonus,
+                    int32_t* path, int32_t* path_len, int32_t* out_tokens,
+                    int32_t* status) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int b = 0; b < B; ++b)
-    mss_request(b, N, V, parents + (size_t)b * N, tokens + (size_t)b * N, llm, ssm, u_accept,
+    mss_request(b, N, nodes_of(n_nodes, b, N), V, parents + (size_t)b * N, tokens + (size_t)b * N, llm, ssm, u_accept,
                 u_bonus, 0, 0, 0, path + (size_t)b * N, out_tokens + (size_t)b * N, path_len,
                 status);
 }
 
 void orc_verify_mss_seeded(int B, int N, int V, const int32_t* parents,
-                           const int32_t* tokens, const float* llm, const float* ssm,
-                           uint64_t seed, uint64_t step, int32_t* path, int32_t* path_len,
-                           int32_t* out_tokens, int32_t* status) {
+                           const int32_t* tokens, const int32_t* n_nodes, const float* llm,
+                           const float* ssm, uint64_t seed, uint64_t step, int32_t* path,
+                           int32_t* path_len, int32_t* out_tokens, int32_t* status) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int b = 0; b < B; ++b)
-    mss_request(b, N, V, parents + (size_t)b * N, tokens + (size_t)b * N, llm, ssm, NULL, NULL,
+    mss_request(b, N, nodes_of(n_nodes, b, N), V, parents + (size_t)b * N, tokens + (size_t)b * N, llm, ssm, NULL, NULL,
                 1, seed, step, path + (size_t)b * N, out_tokens + (size_t)b * N, path_len,
                 status);
 }

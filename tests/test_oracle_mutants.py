@@ -19,6 +19,7 @@ import test_oracle_greedy as G
 import test_oracle_mss as M
 import test_oracle_philox as PH
 import test_oracle_topology as T
+import test_oracle_varlen as VL
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -75,6 +76,22 @@ MUTANTS = [
     ("mss_bonus_counter", "#define ORC_BONUS_ORDINAL 0x8000000000000000ull",
      "#define ORC_BONUS_ORDINAL 0x4000000000000000ull",
      lambda: PH.test_seeded_walk_uses_documented_counters(1005, 0, {})),
+    ("varlen_attn_validity_over_padding", "if (!tree_is_valid(n, par)) { status[r] = ORC_E_TREE; continue; }",
+     "if (!tree_is_valid(N, par)) { status[r] = ORC_E_TREE; continue; }",
+     lambda: VL.test_attention_per_request(0)),
+    ("varlen_attn_padding_rows_flagged", "if (i >= n) { status[r] = ORC_OK; continue; }",
+     "if (i >= n) { status[r] = ORC_E_SHAPE; continue; }",
+     lambda: VL.test_attention_per_request(0)),
+    ("varlen_topology_padding_walked", "for (int i = 0; i < n; ++i) {\n      int d = -1;",
+     "for (int i = 0; i < N && tree_is_valid(N, par); ++i) {\n      int d = -1;",
+     lambda: [VL.test_topology_per_request(s) for s in range(4)]),
+    ("varlen_greedy_ignores_node_count",
+     "int32_t* ob = out_tokens + (size_t)b * N;\n    const int n = nodes_of(n_nodes, b, N);",
+     "int32_t* ob = out_tokens + (size_t)b * N;\n    const int n = N;",
+     lambda: [VL.test_greedy_per_request(s) for s in range(6)]),
+    ("varlen_mss_padding_children", "for (int c = u + 1; c < n; ++c) {",
+     "for (int c = u + 1; c < N; ++c) {",
+     lambda: [VL.test_stochastic_per_request(s) for s in range(6)]),
     ("expand_ties_to_highest", "(best < 0 || row[v] > row[best])", "(best < 0 || row[v] >= row[best])",
      lambda: [E.test_topk_matches_stable_argsort_with_ties(s) for s in range(5)]),
     ("expand_token_reused", "taken[best] = 1;", "taken[best] = 0;",
