@@ -20,10 +20,12 @@ copy of them (enough copies to exceed twice the 256 MB last-level cache), so
 the prefix KV and logits come from HBM, not from cache.
 
 Exactly --steps steps are timed, each between two HIP events on the launch
-stream (each step one HIP-graph replay; a short spin kernel ahead of them
-lets the host enqueue every step before the first one runs, so the steps run
-back to back).  ms_per_step is the median step time, ms_per_step_mean the
-mean over the same steps.
+stream; a short spin kernel ahead of them lets the host enqueue every step
+before the first one runs, so the steps run back to back.  A step's kernels
+are launched directly (measured on MI355X: a HIP-graph replay per step,
+--graph, adds ~7 us of launch gap per replay: c5 109.5 vs 103.6 us per step,
+the commit kernel alone 13.9 vs 6.4 us).  ms_per_step is the median step
+time, ms_per_step_mean the mean over the same steps.
 
 Prints one JSON line: value = verified tree-node queries per second (B*N per
 step at the median step time); roofline = tree_attn's algorithmic work per
@@ -171,8 +173,8 @@ def capture(fn, dev):
             fn()
         torch.cuda.synchronize()
         return g
-    except Exception as e:  # pragma: no cover - reported, then eager timing
-        log("graph capture failed (%s); timing eager launches" % e)
+    except Exception as e:  # pragma: no cover - reported, then direct launches
+        log("graph capture failed (%s); timing direct launches" % e)
         return None
 
 
@@ -306,8 +308,9 @@ def main():
     ap.add_argument("--workload", default="c4", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=16.0,
                     help="seconds of CPU oracle work for the baseline (0 = skip)")
-    ap.add_argument("--eager", action="store_true",
-                    help="time eager launches instead of HIP-graph replays")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step (and stage) from a HIP graph instead of launching "
+                         "its kernels directly")
     ap.add_argument("--warm", action="store_true",
                     help="reuse one input copy (cache-resident) instead of rotating copies")
     ap.add_argument("--unfused", action="store_true",
@@ -332,11 +335,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def launches(fn):
-        """One callable per input copy: a graph replay of fn on that copy
-        (eager launches with --eager or when capture fails)."""
+        """One callable per input copy: fn on that copy, or with --graph a
+        replay of its HIP graph (direct launches when capture fails)."""
         out = []
         for c in copies:
-            g = None if args.eager else capture(lambda c=c: fn(c), dev)
+            g = capture(lambda c=c: fn(c), dev) if args.graph else None
             out.append(g.replay if g is not None else (lambda c=c: fn(c)))
         return out
 
@@ -352,7 +355,7 @@ def main():
         one_step(copies[i % ncopies])
     torch.cuda.synchronize()
     step_fns = launches(one_step)
-    graphed = not args.eager and all(getattr(f, "__self__", None) is not None for f in step_fns)
+    graphed = args.graph and all(getattr(f, "__self__", None) is not None for f in step_fns)
     t_step = summary(timed_steps(step_fns, args.steps, stream))
     # per-entry-point times over the same rotation, launched the same way
     stage = lambda fn: summary(timed_steps(launches(fn), args.steps, stream))
@@ -401,7 +404,7 @@ def main():
                    "verify": d["mode"],
                    "verify_commit": "one pass" if step.fused else "two calls",
                    "input_copies": ncopies,
-                   "launch": "hip graph replay per step" if graphed else "eager",
+                   "launch": "hip graph replay per step" if graphed else "direct kernel launches",
                    "inputs": "rotated, HBM-resident" if ncopies > 1 else
                              ("one copy (warm)" if args.warm else
                               "one copy larger than twice the last-level cache, HBM-resident")},

@@ -10,7 +10,7 @@ Workload: B requests, each expanding F frontier nodes by the k most probable
 tokens of their speculator rows of V fp32 probabilities (softmax of N(0,2)
 logits at temperature 0.8, the stochastic workload's recipe).  Inputs are
 resident in HBM and rotated over enough copies to exceed twice the 256 MB
-MALL; exactly --steps calls are timed, each a HIP-graph replay between two
+MALL; exactly --steps calls are timed, each launched directly between two
 HIP events on the launch stream.  One JSON line: value = frontier rows
 expanded per second at the median call time; roofline = the rows' bytes
 (B*F*V*4, each read once) per call over the call's average duration, against
@@ -67,18 +67,13 @@ def cpu_baseline(probs, k, budget_s):
                       % (rows, rows // F, F, V, k, el)}
 
 
-def time_calls(call, ncopies, steps, dev, stream, eager=False):
+def time_calls(call, ncopies, steps, dev, stream):
     """Exactly `steps` calls call(i), i = 0..steps-1 (input copy i % ncopies),
-    each a HIP-graph replay of its copy's call (eager with eager=True or when
-    capture fails), timed one by one with HIP events on the launch stream
-    (bench.timed_steps).  Returns (median ms, mean ms, launch kind)."""
-    fns = []
-    for i in range(ncopies):
-        g = None if eager else bench.capture(lambda i=i: call(i), dev)
-        fns.append(g.replay if g is not None else (lambda i=i: call(i)))
-    graphed = all(getattr(f, "__self__", None) is not None for f in fns)
+    launched directly and timed one by one with HIP events on the launch
+    stream (bench.timed_steps).  Returns (median ms, mean ms, launch kind)."""
+    fns = [lambda i=i: call(i) for i in range(ncopies)]
     t = bench.summary(bench.timed_steps(fns, steps, stream))
-    return t["median"], t["mean"], "hip graph replay per call" if graphed else "eager"
+    return t["median"], t["mean"], "direct kernel launches"
 
 
 def bench_merge(args):

@@ -6,11 +6,11 @@ Runs, each as its own child process under rocprofv3 (the program follows
 `--` directly; this script itself never touches the GPU):
   1. --kernel-trace --stats of `bench.py --workload W --steps S` -> per-kernel
      average durations (the tree_attn entry point = its kernels' sum);
-  2. --pmc FETCH_SIZE, then --pmc WRITE_SIZE of the same bench in eager mode,
+  2. --pmc FETCH_SIZE, then --pmc WRITE_SIZE of the same bench (direct launches),
      one counter group per run -> KiB per dispatch of every tree_attn kernel;
   3. the same two counters on a plain device copy of known size (`--copy-ref`
      mode of this script), whose ratio to the true bytes calibrates them;
-  4. one --pmc run of SQ counters plus GRBM_GUI_ACTIVE on the eager bench ->
+  4. one --pmc run of SQ counters plus GRBM_GUI_ACTIVE on the same bench ->
      matrix-core busy fraction and instruction mix of the attention kernels.
 Writes tree_attn_W_kernels.md (durations, with the command),
 tree_attn_W_traffic.json + .md (HBM bytes per tree_attn launch = calibrated
@@ -114,10 +114,9 @@ def main():
                     sum(r[2] for r in attn)))
 
     # 2./3. HBM traffic
-    eager = bench_cmd + ["--eager"]
     tr = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
-        f, c = rocprof(os.path.join(out, ctr.lower()), ["--pmc", ctr], eager, 120)
+        f, c = rocprof(os.path.join(out, ctr.lower()), ["--pmc", ctr], bench_cmd, 120)
         tr[ctr] = (counter_kib(f, ctr, ["attn_mfma2", "attn_fma", "attn_combine"]), c)
         f, c = rocprof(os.path.join(out, "copy_" + ctr.lower()), ["--pmc", ctr],
                        [sys.executable, os.path.abspath(__file__), "--copy-ref"], 120)
@@ -158,7 +157,7 @@ def main():
             fh.write("    %s\n" % c)
     # 4. matrix-core busy fraction and instruction mix
     ctrs = SQ_COUNTERS + ["GRBM_GUI_ACTIVE"]
-    f, c_sq = rocprof(os.path.join(out, "sq"), ["--pmc"] + ctrs, eager, 120)
+    f, c_sq = rocprof(os.path.join(out, "sq"), ["--pmc"] + ctrs, bench_cmd, 120)
     per = {k: counter_kib(f, k, ["attn_mfma2", "attn_fma"]) for k in ctrs}
     with open(os.path.join(dest, "tree_attn_%s_counters.md" % w), "w") as fh:
         fh.write("# SQ counters of the attention kernel, workload %s\n\n" % w)

@@ -43,6 +43,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility: these declarations are its
+ * only exported symbols. */
+#pragma GCC visibility push(default)
+
 typedef int32_t ttv_status;
 enum {
   TTV_OK = 0,
@@ -189,6 +193,41 @@ size_t ttv_tree_attn_tuned_workspace_size(ttv_dtype dt, int32_t B, int32_t N,
                                           int32_t Lmax, int32_t rows_per_block,
                                           int32_t chunk_keys);
 
+/*
+ * Batches of trees of different sizes ([SI] §5 "Scheduling": iteration-level
+ * continuous batching verifies the requests of a batch together, whatever
+ * the size of each one's token tree).  The _varlen entry points take, after
+ * `parents`/`tokens`, a device array
+ *   n_nodes   int32 [B]: request b's tree is nodes 0..n_nodes[b]-1; every
+ *             [B,N,...] tensor keeps N entries per request and the entries
+ *             of nodes >= n_nodes[b] are padding: never read for the result
+ *             (they may hold anything, NaN included) and, for outputs,
+ *             written as stated below.
+ * and otherwise mean exactly what the entry point without the suffix means;
+ * each request's results equal that entry point's on the request alone with
+ * its rows cut to n_nodes[b] (the stochastic draws keep their counters
+ * (j, u, b, step), b the request's index in the batch).  A count outside
+ * [1, N] rejects the request with dev_status TTV_E_SHAPE (attention: zero
+ * output; verification: path_len 0, nothing committed).  NULL n_nodes is
+ * TTV_E_NULL.
+ *
+ * ttv_tree_attn_varlen: rows of padding nodes get zero output and lse 0;
+ *   anc_out/depth_out give padding nodes 0 words and depth -1.  The launch
+ *   still covers N nodes per request (the split of the prefix follows each
+ *   request's node count).
+ */
+ttv_status ttv_tree_attn_varlen(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq,
+                                int32_t Hkv, int32_t D, float scale,
+                                const void* q, const void* k_cache,
+                                const void* v_cache, int32_t Lcap,
+                                const int32_t* cache_len, int32_t Lmax,
+                                const void* k_tree, const void* v_tree,
+                                const int32_t* parents, const int32_t* n_nodes,
+                                void* out, float* lse, uint64_t* anc_out,
+                                int32_t* depth_out, int32_t* dev_status,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Bytes of the device array ttv_tree_attn_noalloc keeps its partials in. */
 #define TTV_NOALLOC_SCRATCH_BYTES (48u << 20)
 
@@ -286,6 +325,18 @@ ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N,
 size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B,
                                       int32_t N, int32_t V);
 
+/* ttv_tree_verify for a batch of trees of different sizes (n_nodes as for
+ * ttv_tree_attn_varlen): paths and tokens only ever name nodes < n_nodes[b];
+ * the logits rows of padding nodes are not read. */
+ttv_status ttv_tree_verify_varlen(ttv_verify_mode mode, int32_t B, int32_t N,
+                                  int32_t V, const int32_t* parents,
+                                  const int32_t* tokens, const int32_t* n_nodes,
+                                  const float* llm, const float* ssm,
+                                  uint64_t seed, uint64_t step, int32_t* path,
+                                  int32_t* path_len, int32_t* out_tokens,
+                                  int32_t* dev_status, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /*
  * ttv_tree_verify_uniforms -- stochastic ttv_tree_verify with the uniforms
  * given by the caller instead of drawn from (seed, step): the test of child c
@@ -367,6 +418,19 @@ ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt,
                                   int32_t* out_tokens, int32_t* committed_src,
                                   int32_t* dev_status, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* ttv_tree_verify_commit for a batch of trees of different sizes (n_nodes
+ * as for ttv_tree_attn_varlen). */
+ttv_status ttv_tree_verify_commit_varlen(
+    ttv_verify_mode mode, ttv_dtype dt, int32_t B, int32_t N, int32_t V,
+    int32_t Hkv, int32_t D, int32_t Lcap, const int32_t* parents,
+    const int32_t* tokens, const int32_t* n_nodes, const float* llm,
+    const float* ssm, uint64_t seed, uint64_t step, const void* k_tree,
+    const void* v_tree, void* k_cache, void* v_cache,
+    const int32_t* cache_len_in, int32_t* cache_len_out, int32_t Lmax,
+    int32_t* path, int32_t* path_len, int32_t* out_tokens,
+    int32_t* committed_src, int32_t* dev_status, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 /*
  * ttv_tree_expand -- one level of expansion-based token-tree construction
@@ -497,6 +561,8 @@ ttv_status ttv_kv_commit_inplace(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv
                                  const int32_t* path, const int32_t* path_len,
                                  int32_t* committed_src, int32_t* dev_status,
                                  void* stream);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -41,10 +41,10 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ttv.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (ttv_\w+)$", out, flags=re.M))
+    exported = set(re.findall(r"\bT (\S+)$", out, flags=re.M))
     assert set(declared_functions()) <= exported
     # the C ABI is the only exported interface of the library
-    assert all(n.startswith("ttv_") for n in exported)
+    assert all(n.startswith("ttv_") for n in exported), sorted(exported)
 
 
 def test_library_links_no_torch():
@@ -304,3 +304,24 @@ def test_noalloc_scratch_limit_is_the_stated_one():
     text = open(HEADER).read()
     assert "#define TTV_NOALLOC_SCRATCH_BYTES (48u << 20)" in text
     assert ttv.NOALLOC_SCRATCH_BYTES == 48 << 20
+
+
+def test_varlen_entry_points_need_node_counts():
+    """The _varlen entry points validate like their fixed-size forms and
+    refuse a NULL node-count array."""
+    L = ttv.lib()
+    attn_args = [1, 1, 8, 4, 2, 64, 0.125, A, A, A, 128, A, 100, A, A, A]
+    tail = [A, None, None, None, None, A, 1 << 30, None]
+    assert L.ttv_tree_attn_varlen(*attn_args, None, *tail) == ttv.E_NULL
+    assert L.ttv_tree_attn_varlen(*attn_args, A, *tail[:0], MIS, *tail[1:]) == ttv.E_ALIGN
+    assert L.ttv_tree_attn_varlen(1, 1, 129, 4, 2, 64, 0.125, A, A, A, 1280, A, 100, A, A, A, A,
+                                  *tail) == ttv.E_UNSUPPORTED
+    ver = lambda n, **kw: L.ttv_tree_verify_varlen(
+        kw.get("mode", 0), 2, 8, 100, A, A, n, A, kw.get("ssm"), 1, 2, A, A, A, None, A, 1 << 30,
+        None)
+    assert ver(None) == ttv.E_NULL
+    assert ver(A, mode=1) == ttv.E_NULL and ver(A, mode=3) == ttv.E_DTYPE
+    vc = lambda n, **kw: L.ttv_tree_verify_commit_varlen(
+        0, 1, 2, 8, 64, 2, 64, 100, A, A, n, A, None, 7, 0, A, A, A, A, A, A + 0x100,
+        kw.get("Lmax", 50), A, A, A, None, None, A, 1 << 20, None)
+    assert vc(None) == ttv.E_NULL and vc(A, Lmax=93) == ttv.E_SHAPE

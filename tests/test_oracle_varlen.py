@@ -17,20 +17,26 @@ import synth
 INVALID_N = 2  # status of a request whose node count is outside [1, N]
 
 
-def varlen_batch(seed, mode="greedy", B=6, N=24, V=40, Hq=4, Hkv=2, D=64, L=(3, 60)):
+def varlen_batch(seed, mode="greedy", B=6, N=24, V=40, Hq=4, Hkv=2, D=64, L=(3, 60),
+                 dtype="f32", n=None, dmax=8):
+    """A batch of B trees of N-entry rows with node counts n (random in
+    [1, N] with the first request full and the last a lone root, unless
+    given), padded as the module docstring says."""
     rng = np.random.default_rng(seed)
-    s = synth.Spec("vl", B, N, Hq, Hkv, D, L, "f32", V, mode, "random", 900 + seed, dmax=8,
+    s = synth.Spec("vl", B, N, Hq, Hkv, D, L, dtype, V, mode, "random", 900 + seed, dmax=dmax,
                    max_children=4, plant=0.8, prob_sigma=0.5)
     d = synth.make(s)
-    n = rng.integers(1, N + 1, size=B).astype(np.int32)
-    n[0], n[-1] = N, 1
+    if n is None:
+        n = rng.integers(1, N + 1, size=B).astype(np.int32)
+        n[0], n[-1] = N, 1
+    n = np.asarray(n, np.int32)
     par = d["parents"].copy()
     tok = d["tokens"].copy()
     llm = d["llm"].copy()
     for b in range(B):
         for i in range(n[b], N):
             if b % 2 == 0:   # a valid, acceptable extension
-                par[b, i] = rng.integers(0, i)
+                par[b, i] = rng.integers(0, i) if i > 0 else -1
                 if mode == "greedy":
                     tok[b, i] = int(np.argmax(llm[b, par[b, i]]))
                 else:

@@ -71,6 +71,13 @@ def lib():
                                     _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.ttv_tree_attn_tuned.argtypes = [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P, _I, _P,
                                           _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _P]
+        L.ttv_tree_attn_varlen.argtypes = [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P, _I, _P,
+                                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.ttv_tree_verify_varlen.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _U64, _U64, _P,
+                                             _P, _P, _P, _P, _SZ, _P]
+        L.ttv_tree_verify_commit_varlen.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
+                                                    _P, _P, _U64, _U64, _P, _P, _P, _P, _P, _P,
+                                                    _I, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.ttv_tree_attn_noalloc.argtypes = [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _I, _P, _I,
                                             _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P]
         L.ttv_tree_attn_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I]
@@ -95,7 +102,8 @@ def lib():
                                              _P, _SZ, _P]
         for f in ("ttv_tree_verify_commit", "ttv_kv_commit_inplace", "ttv_tree_topology",
                   "ttv_tree_attn", "ttv_tree_attn_tuned", "ttv_tree_attn_noalloc",
-                  "ttv_tree_verify",
+                  "ttv_tree_attn_varlen", "ttv_tree_verify_varlen",
+                  "ttv_tree_verify_commit_varlen", "ttv_tree_verify",
                   "ttv_tree_verify_uniforms", "ttv_kv_commit", "ttv_tree_expand",
                   "ttv_tree_merge", "ttv_probs_from_logits"):
             getattr(L, f).restype = _I
@@ -172,13 +180,14 @@ def tree_attn_workspace_size(dtype, B, N, Hq, Hkv, D, Lmax, rows_per_block=0, ch
 def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int,
               scale: Optional[float] = None, out=None, lse=None, want_lse: bool = True,
               dev_status=None, workspace=None, anc_out=None, depth_out=None,
-              rows_per_block: int = 0, chunk_keys: int = 0):
+              rows_per_block: int = 0, chunk_keys: int = 0, n_nodes=None):
     """Tree attention for every node; returns (out [B,N,Hq,D], lse [B,N,Hq] or None,
     dev_status [B]).  k_tree = v_tree = None reads node i's K/V from cache row
     L_b + i.  anc_out (int64 [B,N,W] holding the uint64 words) and depth_out
     (int32 [B,N]), when given, receive the tree mask and the node depths.
     rows_per_block / chunk_keys other than 0 fix the launch shape
-    (ttv_tree_attn_tuned)."""
+    (ttv_tree_attn_tuned).  n_nodes (int32 [B]) gives each request's node
+    count in a batch of trees of different sizes (ttv_tree_attn_varlen)."""
     B, N, Hq, D = q.shape
     Hkv, Lcap = k_cache.shape[1], k_cache.shape[2]
     dev = q.device
@@ -204,6 +213,10 @@ def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int
         _need(anc_out, "anc_out", torch.int64, (B, N, (N + 63) // 64), dev)
     if depth_out is not None:
         _need(depth_out, "depth_out", torch.int32, (B, N), dev)
+    if n_nodes is not None:
+        _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+        if rows_per_block or chunk_keys:
+            raise ValueError("n_nodes takes the automatic launch shape")
     if dev_status is None:
         dev_status = torch.empty(B, dtype=torch.int32, device=dev)
     nbytes = tree_attn_workspace_size(dt, B, N, Hq, Hkv, D, Lmax, rows_per_block, chunk_keys)
@@ -213,7 +226,10 @@ def tree_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, parents, Lmax: int
     args = (_dt(dt), B, N, Hq, Hkv, D, float(scale), _ptr(q), _ptr(k_cache), _ptr(v_cache), Lcap,
             _ptr(cache_len), int(Lmax), _ptr(k_tree), _ptr(v_tree), _ptr(parents), _ptr(out),
             _ptr(lse), _ptr(anc_out), _ptr(depth_out), _ptr(dev_status), _ptr(workspace), wsb)
-    if rows_per_block or chunk_keys:
+    if n_nodes is not None:
+        args = args[:16] + (_ptr(n_nodes),) + args[16:]
+        _check("ttv_tree_attn_varlen", lib().ttv_tree_attn_varlen(*args, _stream(dev)))
+    elif rows_per_block or chunk_keys:
         _check("ttv_tree_attn_tuned", lib().ttv_tree_attn_tuned(*args, rows_per_block,
                                                                 chunk_keys, _stream(dev)))
     else:
@@ -271,10 +287,12 @@ def tree_verify_workspace_size(mode, B, N, V):
 
 
 def tree_verify(mode: int, parents, tokens, llm, ssm=None, seed: int = 0, step: int = 0,
-                path=None, path_len=None, out_tokens=None, dev_status=None, workspace=None):
+                path=None, path_len=None, out_tokens=None, dev_status=None, workspace=None,
+                n_nodes=None):
     """Greedy (mode GREEDY, llm = logits) or multi-step speculative sampling
     (mode STOCHASTIC, llm/ssm = probabilities, uniforms drawn on the device
     from Philox4x64-10 with key (seed, 0) and counter word 3 = step).
+    n_nodes (int32 [B]): each request's node count (ttv_tree_verify_varlen).
     Returns (path [B,N], path_len [B], out_tokens [B,N], dev_status [B])."""
     B, N = parents.shape
     V = llm.shape[2]
@@ -284,16 +302,21 @@ def tree_verify(mode: int, parents, tokens, llm, ssm=None, seed: int = 0, step: 
     _need(llm, "llm", torch.float32, (B, N, V), dev)
     if mode == STOCHASTIC:
         _need(ssm, "ssm", torch.float32, (B, N, V), dev)
+    if n_nodes is not None:
+        _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
     path, path_len, out_tokens, dev_status = _verify_outputs(B, N, dev, path, path_len,
                                                              out_tokens, dev_status)
     nbytes = tree_verify_workspace_size(mode, B, N, V)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().ttv_tree_verify(mode, B, N, V, _ptr(parents), _ptr(tokens), _ptr(llm), _ptr(ssm),
-                               _u64(seed), _u64(step), _ptr(path), _ptr(path_len),
-                               _ptr(out_tokens), _ptr(dev_status), _ptr(workspace), wsb,
-                               _stream(dev))
+    tail = (_ptr(llm), _ptr(ssm), _u64(seed), _u64(step), _ptr(path), _ptr(path_len),
+            _ptr(out_tokens), _ptr(dev_status), _ptr(workspace), wsb, _stream(dev))
+    if n_nodes is not None:
+        st = lib().ttv_tree_verify_varlen(mode, B, N, V, _ptr(parents), _ptr(tokens),
+                                          _ptr(n_nodes), *tail)
+    else:
+        st = lib().ttv_tree_verify(mode, B, N, V, _ptr(parents), _ptr(tokens), *tail)
     _check("ttv_tree_verify", st)
     return path, path_len, out_tokens, dev_status
 
@@ -379,11 +402,12 @@ def tree_verify_commit(mode: int, parents, tokens, llm, k_tree, v_tree, k_cache,
                        cache_len_in, Lmax: int, ssm=None, seed: int = 0, step: int = 0,
                        cache_len_out=None, path=None, path_len=None, out_tokens=None,
                        committed_src=None, want_src: bool = True, dev_status=None,
-                       workspace=None):
+                       workspace=None, n_nodes=None):
     """Verification (mode GREEDY or STOCHASTIC with (seed, step), as in
     tree_verify) and the KV
     commit of its path in one pass: the same results as tree_verify(...) then
-    kv_commit(...); cache_len_out may be cache_len_in.  Returns (path,
+    kv_commit(...); cache_len_out may be cache_len_in; n_nodes (int32 [B]) as
+    in tree_verify.  Returns (path,
     path_len, out_tokens, cache_len_out, committed_src or None, dev_status)."""
     B, N = parents.shape
     V = llm.shape[2]
@@ -418,12 +442,18 @@ def tree_verify_commit(mode: int, parents, tokens, llm, k_tree, v_tree, k_cache,
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().ttv_tree_verify_commit(
-        mode, _dt(dt), B, N, V, Hkv, D, Lcap, _ptr(parents), _ptr(tokens), _ptr(llm), _ptr(ssm),
-        _u64(seed), _u64(step), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache),
-        _ptr(cache_len_in), _ptr(cache_len_out), int(Lmax), _ptr(path), _ptr(path_len),
-        _ptr(out_tokens), _ptr(committed_src), _ptr(dev_status), _ptr(workspace), wsb,
-        _stream(dev))
+    tail = (_ptr(llm), _ptr(ssm), _u64(seed), _u64(step), _ptr(k_tree), _ptr(v_tree),
+            _ptr(k_cache), _ptr(v_cache), _ptr(cache_len_in), _ptr(cache_len_out), int(Lmax),
+            _ptr(path), _ptr(path_len), _ptr(out_tokens), _ptr(committed_src), _ptr(dev_status),
+            _ptr(workspace), wsb, _stream(dev))
+    if n_nodes is not None:
+        _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+        st = lib().ttv_tree_verify_commit_varlen(mode, _dt(dt), B, N, V, Hkv, D, Lcap,
+                                                 _ptr(parents), _ptr(tokens), _ptr(n_nodes),
+                                                 *tail)
+    else:
+        st = lib().ttv_tree_verify_commit(mode, _dt(dt), B, N, V, Hkv, D, Lcap, _ptr(parents),
+                                          _ptr(tokens), *tail)
     _check("ttv_tree_verify_commit", st)
     return path, path_len, out_tokens, cache_len_out, committed_src, dev_status
 

@@ -8,6 +8,8 @@ compile (-packed-fp32-ops); the host pass warns that it does not know that
 feature, which is harmless.  Matrix-core results are kept in ordinary VGPRs
 (-amdgpu-mfma-vgpr-form): the attention scores feed vector ALU work right
 after their MFMAs, and accumulator registers would cost a copy each way.
+Symbols are hidden by default: the declarations of include/ttv.h are the
+library's only exported interface.
 """
 from __future__ import annotations
 
@@ -25,6 +27,7 @@ ARCH = "gfx950"
 
 FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xarch_host", "-fvisibility=hidden",
     "-Wall", "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form",

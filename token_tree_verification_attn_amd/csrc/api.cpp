@@ -136,11 +136,11 @@ ttv_status attn_prepare(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, floa
 ttv_status launch_attn(const AttnPlan& p, ttv_dtype dt, int B, int N, int Hq, int Hkv, int D,
                        float scale, const void* q, const void* k_cache, const void* v_cache,
                        int Lcap, const int32_t* cache_len, int Lmax, const void* k_tree,
-                       const void* v_tree, const int32_t* parents, void* out, float* lse,
-                       uint64_t* anc_out, int32_t* depth_out, int32_t* dev_status, void* ws,
-                       hipStream_t s) {
+                       const void* v_tree, const int32_t* parents, const int32_t* n_nodes,
+                       void* out, float* lse, uint64_t* anc_out, int32_t* depth_out,
+                       int32_t* dev_status, void* ws, hipStream_t s) {
   if (anc_out || depth_out) {
-    if (launch_topology(B, N, parents, anc_out, depth_out, nullptr, s) != hipSuccess)
+    if (launch_topology(B, N, parents, n_nodes, anc_out, depth_out, nullptr, s) != hipSuccess)
       return TTV_E_LAUNCH;
   }
   AttnArgs a;
@@ -153,6 +153,7 @@ ttv_status launch_attn(const AttnPlan& p, ttv_dtype dt, int B, int N, int Hq, in
   a.tree_in_cache = k_tree ? 0 : 1;
   a.cache_len = cache_len;
   a.parents = parents;
+  a.n_nodes = n_nodes;
   a.out = out;
   a.lse = lse;
   a.dev_status = dev_status;
@@ -212,7 +213,7 @@ ttv_status ttv_tree_topology(int32_t B, int32_t N, const int32_t* parents, uint6
   if (!parents) return TTV_E_NULL;
   if (B < 1 || N < 1) return TTV_E_SHAPE;
   if (N > TTV_MAX_NODES) return TTV_E_UNSUPPORTED;
-  return launch_status(launch_topology(B, N, parents, anc_out, depth_out, dev_status,
+  return launch_status(launch_topology(B, N, parents, nullptr, anc_out, depth_out, dev_status,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -230,14 +231,20 @@ size_t ttv_tree_attn_workspace_size(ttv_dtype dt, int32_t B, int32_t N, int32_t 
   return ttv_tree_attn_tuned_workspace_size(dt, B, N, Hq, Hkv, D, Lmax, 0, 0);
 }
 
-ttv_status ttv_tree_attn_tuned(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
-                               int32_t D, float scale, const void* q, const void* k_cache,
-                               const void* v_cache, int32_t Lcap, const int32_t* cache_len,
-                               int32_t Lmax, const void* k_tree, const void* v_tree,
-                               const int32_t* parents, void* out, float* lse,
-                               uint64_t* anc_out, int32_t* depth_out, int32_t* dev_status,
-                               void* workspace, size_t workspace_bytes, int32_t rows_per_block,
-                               int32_t chunk_keys, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ttv_tree_attn with per-request node counts (nullptr: N each) and a launch
+// shape (0, 0: automatic).
+ttv_status tree_attn_call(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                          float scale, const void* q, const void* k_cache, const void* v_cache,
+                          int32_t Lcap, const int32_t* cache_len, int32_t Lmax,
+                          const void* k_tree, const void* v_tree, const int32_t* parents,
+                          const int32_t* n_nodes, void* out, float* lse, uint64_t* anc_out,
+                          int32_t* depth_out, int32_t* dev_status, void* workspace,
+                          size_t workspace_bytes, int32_t rows_per_block, int32_t chunk_keys,
+                          void* stream) {
   AttnPlan p;
   const ttv_status st = attn_prepare(dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap,
                                      cache_len, Lmax, k_tree, v_tree, parents, out,
@@ -246,8 +253,26 @@ ttv_status ttv_tree_attn_tuned(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, i
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return TTV_E_WORKSPACE;
   if (p.ws_bytes > 0 && !aligned16(workspace)) return TTV_E_ALIGN;
   return launch_attn(p, dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap, cache_len, Lmax,
-                     k_tree, v_tree, parents, out, lse, anc_out, depth_out, dev_status,
+                     k_tree, v_tree, parents, n_nodes, out, lse, anc_out, depth_out, dev_status,
                      workspace, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+ttv_status ttv_tree_attn_tuned(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                               int32_t D, float scale, const void* q, const void* k_cache,
+                               const void* v_cache, int32_t Lcap, const int32_t* cache_len,
+                               int32_t Lmax, const void* k_tree, const void* v_tree,
+                               const int32_t* parents, void* out, float* lse,
+                               uint64_t* anc_out, int32_t* depth_out, int32_t* dev_status,
+                               void* workspace, size_t workspace_bytes, int32_t rows_per_block,
+                               int32_t chunk_keys, void* stream) {
+  return tree_attn_call(dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap, cache_len, Lmax,
+                        k_tree, v_tree, parents, nullptr, out, lse, anc_out, depth_out,
+                        dev_status, workspace, workspace_bytes, rows_per_block, chunk_keys,
+                        stream);
 }
 
 ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
@@ -257,9 +282,23 @@ ttv_status ttv_tree_attn(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t
                          const int32_t* parents, void* out, float* lse, uint64_t* anc_out,
                          int32_t* depth_out, int32_t* dev_status, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  return ttv_tree_attn_tuned(dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap, cache_len,
-                             Lmax, k_tree, v_tree, parents, out, lse, anc_out, depth_out,
-                             dev_status, workspace, workspace_bytes, 0, 0, stream);
+  return tree_attn_call(dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap, cache_len, Lmax,
+                        k_tree, v_tree, parents, nullptr, out, lse, anc_out, depth_out,
+                        dev_status, workspace, workspace_bytes, 0, 0, stream);
+}
+
+ttv_status ttv_tree_attn_varlen(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                int32_t D, float scale, const void* q, const void* k_cache,
+                                const void* v_cache, int32_t Lcap, const int32_t* cache_len,
+                                int32_t Lmax, const void* k_tree, const void* v_tree,
+                                const int32_t* parents, const int32_t* n_nodes, void* out,
+                                float* lse, uint64_t* anc_out, int32_t* depth_out,
+                                int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!n_nodes) return TTV_E_NULL;
+  return tree_attn_call(dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap, cache_len, Lmax,
+                        k_tree, v_tree, parents, n_nodes, out, lse, anc_out, depth_out,
+                        dev_status, workspace, workspace_bytes, 0, 0, stream);
 }
 
 size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V) {
@@ -270,11 +309,13 @@ size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B, int32_t N
   return greedy_plan(B, N, V).ws_bytes;
 }
 
-ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V,
-                           const int32_t* parents, const int32_t* tokens, const float* llm,
-                           const float* ssm, uint64_t seed, uint64_t step, int32_t* path,
-                           int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+// ttv_tree_verify with per-request node counts (nullptr: N each).
+static ttv_status tree_verify_call(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V,
+                                   const int32_t* parents, const int32_t* tokens,
+                                   const int32_t* n_nodes, const float* llm, const float* ssm,
+                                   uint64_t seed, uint64_t step, int32_t* path,
+                                   int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
   if (mode != TTV_GREEDY && mode != TTV_STOCHASTIC) return TTV_E_DTYPE;
   if (!parents || !tokens || !llm || !path || !path_len || !out_tokens) return TTV_E_NULL;
   if (mode == TTV_STOCHASTIC && !ssm) return TTV_E_NULL;
@@ -285,7 +326,7 @@ ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V
   if (mode == TTV_STOCHASTIC) {
     if (V > kMssMaxVocab) return TTV_E_UNSUPPORTED;
     if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
-    return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm,
+    return launch_status(launch_verify_mss(B, N, V, parents, tokens, n_nodes, llm, ssm,
                                            MssDraws{nullptr, nullptr, seed, step}, path,
                                            path_len, out_tokens, dev_status, CommitArgs{}, s));
   }
@@ -294,8 +335,28 @@ ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V
   if (!aligned16(llm)) return TTV_E_ALIGN;
   if (!workspace || workspace_bytes < p.ws_bytes) return TTV_E_WORKSPACE;
   if (!aligned16(workspace)) return TTV_E_ALIGN;
-  return launch_status(launch_verify_greedy(B, N, V, parents, tokens, llm, path, path_len,
-                                            out_tokens, dev_status, workspace, p, s));
+  return launch_status(launch_verify_greedy(B, N, V, parents, tokens, n_nodes, llm, path,
+                                            path_len, out_tokens, dev_status, workspace, p, s));
+}
+
+ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V,
+                           const int32_t* parents, const int32_t* tokens, const float* llm,
+                           const float* ssm, uint64_t seed, uint64_t step, int32_t* path,
+                           int32_t* path_len, int32_t* out_tokens, int32_t* dev_status,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return tree_verify_call(mode, B, N, V, parents, tokens, nullptr, llm, ssm, seed, step, path,
+                          path_len, out_tokens, dev_status, workspace, workspace_bytes, stream);
+}
+
+ttv_status ttv_tree_verify_varlen(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V,
+                                  const int32_t* parents, const int32_t* tokens,
+                                  const int32_t* n_nodes, const float* llm, const float* ssm,
+                                  uint64_t seed, uint64_t step, int32_t* path, int32_t* path_len,
+                                  int32_t* out_tokens, int32_t* dev_status, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!n_nodes) return TTV_E_NULL;
+  return tree_verify_call(mode, B, N, V, parents, tokens, n_nodes, llm, ssm, seed, step, path,
+                          path_len, out_tokens, dev_status, workspace, workspace_bytes, stream);
 }
 
 ttv_status ttv_tree_verify_uniforms(int32_t B, int32_t N, int32_t V, const int32_t* parents,
@@ -310,7 +371,7 @@ ttv_status ttv_tree_verify_uniforms(int32_t B, int32_t N, int32_t V, const int32
   if (N > TTV_MAX_NODES || V > kMssMaxVocab) return TTV_E_UNSUPPORTED;
   if ((long)B * N > 0x7fffffffL) return TTV_E_UNSUPPORTED;
   if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
-  return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm,
+  return launch_status(launch_verify_mss(B, N, V, parents, tokens, nullptr, llm, ssm,
                                          MssDraws{u_accept, u_bonus, 0, 0}, path, path_len,
                                          out_tokens, dev_status, CommitArgs{},
                                          static_cast<hipStream_t>(stream)));
@@ -337,16 +398,15 @@ ttv_status ttv_kv_commit(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv, int32_
                                         static_cast<hipStream_t>(stream)));
 }
 
-ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt, int32_t B, int32_t N,
-                                  int32_t V, int32_t Hkv, int32_t D, int32_t Lcap,
-                                  const int32_t* parents, const int32_t* tokens, const float* llm,
-                                  const float* ssm, uint64_t seed, uint64_t step,
-                                  const void* k_tree, const void* v_tree, void* k_cache,
-                                  void* v_cache, const int32_t* cache_len_in,
-                                  int32_t* cache_len_out, int32_t Lmax, int32_t* path,
-                                  int32_t* path_len, int32_t* out_tokens, int32_t* committed_src,
-                                  int32_t* dev_status, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+// ttv_tree_verify_commit with per-request node counts (nullptr: N each).
+static ttv_status tree_verify_commit_call(
+    ttv_verify_mode mode, ttv_dtype dt, int32_t B, int32_t N, int32_t V, int32_t Hkv, int32_t D,
+    int32_t Lcap, const int32_t* parents, const int32_t* tokens, const int32_t* n_nodes,
+    const float* llm, const float* ssm, uint64_t seed, uint64_t step, const void* k_tree,
+    const void* v_tree, void* k_cache, void* v_cache, const int32_t* cache_len_in,
+    int32_t* cache_len_out, int32_t Lmax, int32_t* path, int32_t* path_len, int32_t* out_tokens,
+    int32_t* committed_src, int32_t* dev_status, void* workspace, size_t workspace_bytes,
+    void* stream) {
   if (mode != TTV_GREEDY && mode != TTV_STOCHASTIC) return TTV_E_DTYPE;
   if (dt != TTV_F32 && dt != TTV_BF16) return TTV_E_DTYPE;
   if (!parents || !tokens || !llm || !k_tree || !v_tree || !k_cache || !v_cache ||
@@ -367,7 +427,7 @@ ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt, int32_t B,
     if (!aligned16(ssm)) return TTV_E_ALIGN;
     CommitArgs cm{D * elt / 16, Hkv, Lcap, Lmax, k_tree, v_tree, k_cache, v_cache,
                   cache_len_in, cache_len_out, committed_src};
-    return launch_status(launch_verify_mss(B, N, V, parents, tokens, llm, ssm,
+    return launch_status(launch_verify_mss(B, N, V, parents, tokens, n_nodes, llm, ssm,
                                            MssDraws{nullptr, nullptr, seed, step}, path,
                                            path_len, out_tokens, dev_status, cm, s));
   }
@@ -376,9 +436,40 @@ ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt, int32_t B,
   if (!workspace || workspace_bytes < p.ws_bytes) return TTV_E_WORKSPACE;
   if (!aligned16(workspace)) return TTV_E_ALIGN;
   return launch_status(launch_verify_greedy_commit(
-      B, N, V, parents, tokens, llm, path, path_len, out_tokens, dev_status, workspace, p, elt, Hkv,
-      D, Lcap, Lmax, k_tree, v_tree, k_cache, v_cache, cache_len_in, cache_len_out, committed_src,
-      s));
+      B, N, V, parents, tokens, n_nodes, llm, path, path_len, out_tokens, dev_status, workspace, p,
+      elt, Hkv, D, Lcap, Lmax, k_tree, v_tree, k_cache, v_cache, cache_len_in, cache_len_out,
+      committed_src, s));
+}
+
+ttv_status ttv_tree_verify_commit(ttv_verify_mode mode, ttv_dtype dt, int32_t B, int32_t N,
+                                  int32_t V, int32_t Hkv, int32_t D, int32_t Lcap,
+                                  const int32_t* parents, const int32_t* tokens, const float* llm,
+                                  const float* ssm, uint64_t seed, uint64_t step,
+                                  const void* k_tree, const void* v_tree, void* k_cache,
+                                  void* v_cache, const int32_t* cache_len_in,
+                                  int32_t* cache_len_out, int32_t Lmax, int32_t* path,
+                                  int32_t* path_len, int32_t* out_tokens, int32_t* committed_src,
+                                  int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return tree_verify_commit_call(mode, dt, B, N, V, Hkv, D, Lcap, parents, tokens, nullptr, llm,
+                                 ssm, seed, step, k_tree, v_tree, k_cache, v_cache, cache_len_in,
+                                 cache_len_out, Lmax, path, path_len, out_tokens, committed_src,
+                                 dev_status, workspace, workspace_bytes, stream);
+}
+
+ttv_status ttv_tree_verify_commit_varlen(
+    ttv_verify_mode mode, ttv_dtype dt, int32_t B, int32_t N, int32_t V, int32_t Hkv, int32_t D,
+    int32_t Lcap, const int32_t* parents, const int32_t* tokens, const int32_t* n_nodes,
+    const float* llm, const float* ssm, uint64_t seed, uint64_t step, const void* k_tree,
+    const void* v_tree, void* k_cache, void* v_cache, const int32_t* cache_len_in,
+    int32_t* cache_len_out, int32_t Lmax, int32_t* path, int32_t* path_len, int32_t* out_tokens,
+    int32_t* committed_src, int32_t* dev_status, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (!n_nodes) return TTV_E_NULL;
+  return tree_verify_commit_call(mode, dt, B, N, V, Hkv, D, Lcap, parents, tokens, n_nodes, llm,
+                                 ssm, seed, step, k_tree, v_tree, k_cache, v_cache, cache_len_in,
+                                 cache_len_out, Lmax, path, path_len, out_tokens, committed_src,
+                                 dev_status, workspace, workspace_bytes, stream);
 }
 
 ttv_status ttv_tree_expand(int32_t B, int32_t F, int32_t V, int32_t k, const float* probs,

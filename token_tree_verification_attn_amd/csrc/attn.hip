@@ -31,8 +31,10 @@ namespace ttv {
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kKeysPerTile = 64;
 
-// Status of request b as every kernel of the call sees it.
-__device__ __forceinline__ int request_status(bool tree_ok, int L, int Lmax) {
+// Status of request b as every kernel of the call sees it (n_raw its node
+// count as given).
+__device__ __forceinline__ int request_status(bool tree_ok, int L, int Lmax, int n_raw, int N) {
+  if (!nodes_ok(n_raw, N)) return TTV_E_SHAPE;
   if (!tree_ok) return TTV_E_TREE;
   if (L < 0 || L > Lmax) return TTV_E_SHAPE;
   return TTV_OK;
@@ -77,10 +79,13 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int N = a.N, G = a.G, R = a.R;
   const int L = a.cache_len[b];
+  const int n_raw = nodes_raw(a.n_nodes, b, N);
+  const int nU = nodes_used(n_raw, N);
+  const int Rn = nU * G;  // rows of real nodes; rows Rn..R-1 are padding
   if (wave == 0) {
-    const bool tree_ok = wave_build_tree(a.parents + (size_t)b * N, N, s_anc, s_depth);
+    const bool tree_ok = wave_build_tree(a.parents + (size_t)b * N, nU, s_anc, s_depth);
     if (lane == 0) {
-      s_status = request_status(tree_ok, L, a.Lmax);
+      s_status = request_status(tree_ok, L, a.Lmax, n_raw, N);
       if (a.dev_status && c == 0 && rb == 0 && h == 0) a.dev_status[b] = s_status;
     }
   }
@@ -103,7 +108,7 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
     return;
   }
   const int nP = (k_begin < k_end) ? (k_end - k_begin + KT - 1) / KT : 0;
-  const int nT = (c == 0) ? (N + KT - 1) / KT : 0;
+  const int nT = (c == 0) ? (nU + KT - 1) / KT : 0;
   if (nP + nT == 0) return;  // empty chunk: the combine skips it
 
   // queries of this block's rows, widened to fp32
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
   for (int t = threadIdx.x; t < RPB * D; t += blockDim.x) {
     const int rr = t / D, d = t % D, r = row0 + rr;
     float v = 0.f;
-    if (r < R) {
+    if (r < Rn) {
       const int i = r / G, hq = h * G + (r - i * G);
       v = load_elt<T>(q + (((size_t)b * N + i) * a.Hq + hq) * D + d);
     }
@@ -127,9 +132,9 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[k][e] = 0.f;
     const int r = row0 + wave * RPW + k;
-    const int i = r < R ? r / G : 0;
-    anc_w[k][0] = r < R ? s_anc[2 * i] : 0ull;
-    anc_w[k][1] = r < R ? s_anc[2 * i + 1] : 0ull;
+    const int i = r < Rn ? r / G : 0;
+    anc_w[k][0] = r < Rn ? s_anc[2 * i] : 0ull;
+    anc_w[k][1] = r < Rn ? s_anc[2 * i + 1] : 0ull;
   }
 
   const T* kc = static_cast<const T*>(a.k_cache) + ((size_t)bh * a.Lcap) * D;
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
   for (int tile = 0; tile < nP + nT; ++tile) {
     const bool is_tree = tile >= nP;
     const int key0 = is_tree ? (tile - nP) * KT : k_begin + tile * KT;
-    const int nvalid = is_tree ? min(KT, N - key0) : min(KT, k_end - key0);
+    const int nvalid = is_tree ? min(KT, nU - key0) : min(KT, k_end - key0);
     const T* ks = is_tree ? kt : kc;
     const T* vs = is_tree ? vt : vc;
     __syncthreads();  // previous tile fully consumed
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
       const int rr = wave * RPW + k;
-      if (row0 + rr >= R) continue;  // wave-uniform
+      if (row0 + rr >= Rn) continue;  // wave-uniform (padding rows stay empty)
       float dot = 0.f;
 #pragma unroll 8
       for (int d = 0; d < D; ++d) dot = fmaf(s_q[rr * D + d], s_k[lane * DP + d], dot);
@@ -194,11 +199,13 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
     if (r >= R) continue;
     const int i = r / G, hq = h * G + (r - i * G);
     if (a.chunks == 1) {
-      const float inv = 1.f / l[k];
+      const bool real = r < Rn;  // a padding node's row gets zeros
+      const float inv = real ? 1.f / l[k] : 0.f;
       T* o = static_cast<T*>(a.out) + (((size_t)b * N + i) * a.Hq + hq) * D;
 #pragma unroll
-      for (int e = 0; e < E; ++e) store_elt<T>(o + lane + 64 * e, acc[k][e] * inv);
-      if (lane == 0 && a.lse) a.lse[((size_t)b * N + i) * a.Hq + hq] = (m[k] + __log2f(l[k])) * kLn2;
+      for (int e = 0; e < E; ++e) store_elt<T>(o + lane + 64 * e, real ? acc[k][e] * inv : 0.f);
+      if (lane == 0 && a.lse)
+        a.lse[((size_t)b * N + i) * a.Hq + hq] = real ? (m[k] + __log2f(l[k])) * kLn2 : 0.f;
     } else {
       const size_t pr = ((size_t)bh * a.chunks + c) * R + r;
       if constexpr (sizeof(T) == 2) {
@@ -236,12 +243,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int r = blockIdx.x * 4 + wave;
   const int N = a.N, G = a.G, R = a.R;
   const int L = a.cache_len[b];
-  const bool tree_ok = wave_tree_valid(a.parents + (size_t)b * N, N);
+  const int n_raw = nodes_raw(a.n_nodes, b, N);
+  const int nU = nodes_used(n_raw, N);
+  const bool tree_ok = wave_tree_valid(a.parents + (size_t)b * N, nU);
   if (r >= R) return;
   const int i = r / G, hq = h * G + (r - i * G);
   T* o = static_cast<T*>(a.out) + (((size_t)b * N + i) * a.Hq + hq) * D;
   float* lse = a.lse ? a.lse + ((size_t)b * N + i) * a.Hq + hq : nullptr;
-  if (request_status(tree_ok, L, a.Lmax) != TTV_OK) {
+  // a rejected request or a padding node's row: zeros
+  if (request_status(tree_ok, L, a.Lmax, n_raw, N) != TTV_OK || i >= nU) {
 #pragma unroll
     for (int e = 0; e < E; ++e) store_elt<T>(o + lane + 64 * e, 0.f);
     if (lane == 0 && lse) *lse = 0.f;

@@ -282,6 +282,11 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   // lanes and rows past the end read index 0 / row 0 and are masked below.
   const int L = *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
       reinterpret_cast<uintptr_t>(a.cache_len + b));
+  // the request's node count (rows of padding nodes get zero output)
+  const int n_raw = a.n_nodes ? *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+                                    reinterpret_cast<uintptr_t>(a.n_nodes + b))
+                              : N;
+  const int nU = nodes_used(__builtin_amdgcn_readfirstlane(n_raw), N);
   const int32_t* par = a.parents + (size_t)b * N;
   int p0 = gload4_async(par + min(lane, N - 1));
   int p1 = gload4_async(par + min(lane + 64, N - 1));
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     sc.k_begin = c * a.chunk_keys;
     sc.k_end = min(Lc, sc.k_begin + a.chunk_keys);
     sc.nP = (sc.k_begin < sc.k_end) ? (sc.k_end - sc.k_begin + KT - 1) / KT : 0;
-    sc.nT = (c == 0) ? (N + KT - 1) / KT : 0;
+    sc.nT = (c == 0) ? (nU + KT - 1) / KT : 0;
     sc.tree0 = 0;
   }
   const int ntiles = sc.nP + sc.nT;
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     constexpr int S = decltype(stage_tag)::value;
     const bool tree = sc.tree(tile);
     const int key0 = sc.key0(tile);
-    const int nvalid = tree ? min(KT, N - key0) : min(KT, sc.k_end - key0);
+    const int nvalid = tree ? min(KT, nU - key0) : min(KT, sc.k_end - key0);
     const char* ks = (tree ? ktr : kc) + (size_t)key0 * (D * 2);
     const char* vs = (tree ? vtr : vc) + (size_t)key0 * (D * 2);
     TTV_LDS unsigned char* kst = (TTV_LDS unsigned char*)(s_dyn + S * C::TILE_BYTES);
@@ -401,8 +406,11 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   // case to merge, and it merges by copying the registers before the wait.
   if (ntiles < kPre) wait_vmcnt<0>();
   wait_pin<kPre * 2 * C::LOADS>(qraw, p0, p1);
-  p0 = lane < N ? p0 : -1;
-  p1 = lane + 64 < N ? p1 : -1;
+  p0 = lane < nU ? p0 : -1;
+  p1 = lane + 64 < nU ? p1 : -1;
+  // rows of padding nodes work on zero queries and are written as zeros
+#pragma unroll
+  for (int qt = 0; qt < C::QT; ++qt) qnode[qt] = qnode[qt] < nU ? qnode[qt] : -1;
   bf16x8 qB[C::QT][C::KS];
 #pragma unroll
   for (int qt = 0; qt < C::QT; ++qt)
@@ -418,7 +426,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   bool tree_ok = true, tree_built = false;
   auto build_tree = [&]() {
     uint64_t a0lo, a1lo, a1hi;
-    tree_ok = wave_tree_bits(p0, p1, N, a0lo, a1lo, a1hi);
+    tree_ok = wave_tree_bits(p0, p1, nU, a0lo, a1lo, a1hi);
 #pragma unroll
     for (int qt = 0; qt < C::QT; ++qt) {
       const int i = qnode[qt] >= 0 ? qnode[qt] : 0;
@@ -538,7 +546,7 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   auto softmax = [&](int tile, SAcc& s, PFrag& pB, float (&alpha)[C::QT]) -> bool {
     const bool tree = sc.tree(tile);
     const int key0 = sc.key0(tile);
-    const int nvalid = tree ? min(KT, N - key0) : min(KT, sc.k_end - key0);
+    const int nvalid = tree ? min(KT, nU - key0) : min(KT, sc.k_end - key0);
     const bool masked = tree || nvalid < KT;
     bool any_rescale = false;
 #pragma unroll
@@ -662,7 +670,8 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   // kernel, its chunk count).
   const bool writer = c == 0 && rb == 0 && h == 0;
   if (!tree_built && (n_chunks == 1 || writer)) build_tree();
-  const int status = !tree_ok ? TTV_E_TREE : (L < 0 || L > a.Lmax ? TTV_E_SHAPE : TTV_OK);
+  const int status = !nodes_ok(n_raw, N) ? TTV_E_SHAPE
+                     : !tree_ok ? TTV_E_TREE : (L < 0 || L > a.Lmax ? TTV_E_SHAPE : TTV_OK);
   if (writer && wave == 0 && lane == 0) {
     if (a.dev_status) a.dev_status[b] = status;
     if (a.ws_nchunks) a.ws_nchunks[b] = n_chunks;
@@ -679,14 +688,15 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
       if (r >= R) continue;
       const int i = r / G, hq = h * G + (r - i * G);
       uint16_t* o = out + (((size_t)b * N + i) * a.Hq + hq) * D;
-      const float inv = has_work ? 1.f / lt : 0.f;  // a rejected request gets zeros
+      const bool real = has_work && i < nU;  // a rejected request or a padding node gets zeros
+      const float inv = real ? 1.f / lt : 0.f;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
         const f32x4 v = oacc[qt][dt] * inv;
         *reinterpret_cast<u32x2*>(o + dt * 16 + g16 * 4) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
       }
       if (g16 == 0 && a.lse)
-        a.lse[((size_t)b * N + i) * a.Hq + hq] = has_work ? (m_run[qt] + __log2f(lt)) * kLn2f : 0.f;
+        a.lse[((size_t)b * N + i) * a.Hq + hq] = real ? (m_run[qt] + __log2f(lt)) * kLn2f : 0.f;
     }
     return;
   }

@@ -2,8 +2,9 @@
 // from the actual prefix lengths (internal; included by the kernels that need
 // it).
 //
-// Every (request b, kv head, row block) owns n_b = ceil(N/64) + ceil(L_b/64)
-// key tiles: the in-tree tiles first, then the prefix tiles.  The launched
+// Every (request b, kv head, row block) owns n_b = ceil(N_b/64) + ceil(L_b/64)
+// key tiles (N_b the nodes of its tree): the prefix tiles, then the in-tree
+// tiles.  The launched
 // workgroups are shared out so that the longest chunk is as short as it can
 // be: with s tiles per chunk a unit takes C_b = min(chunks, ceil(n_b / s))
 // chunks, and s is the smallest value (at least kBalancedMinTiles) for which
@@ -24,7 +25,7 @@ struct PlanItem {
   int b, h, rb, c;  // request, kv head, row block, chunk
   int C;            // chunks of this request's units
   int t0, t1;       // the chunk's tiles
-  int nT;           // in-tree tiles of a unit (tiles [0, nT) are in-tree)
+  int nT;           // in-tree tiles of a unit (the last nT of its tiles)
   int L;            // the request's prefix length, clamped to [0, Lmax]
 };
 
@@ -39,11 +40,11 @@ __device__ __forceinline__ int plan_wave_sum(int v) {
 // used.  Requires B <= kBalancedMaxB.
 __device__ inline bool attn_plan_item(const AttnArgs& a, int item, PlanItem& it) {
   const int lane = threadIdx.x & 63;
-  const int nT = (a.N + 63) / 64;
   const int U = a.Hkv * a.row_blocks;  // units per request
-  int L = 0, n = 0;
+  int L = 0, n = 0, nT = 0;
   if (lane < a.B) {
     L = min(max(a.cache_len[lane], 0), a.Lmax);
+    nT = (nodes_used(nodes_raw(a.n_nodes, lane, a.N), a.N) + 63) / 64;
     n = nT + (L + 63) / 64;
   }
   const long T = (long)U * plan_wave_sum(n);
@@ -90,7 +91,7 @@ __device__ inline bool attn_plan_item(const AttnArgs& a, int item, PlanItem& it)
   it.h = j / (a.row_blocks * it.C);
   it.t0 = (int)((long)it.c * nb / it.C);
   it.t1 = (int)((long)(it.c + 1) * nb / it.C);
-  it.nT = nT;
+  it.nT = __builtin_amdgcn_readfirstlane(__shfl(nT, b));
   return true;
 }
 

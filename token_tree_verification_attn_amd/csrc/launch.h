@@ -33,6 +33,7 @@ struct AttnArgs {
   const void* v_tree;
   const int32_t* cache_len;
   const int32_t* parents;
+  const int32_t* n_nodes;  // [B] nodes of each request's tree, or nullptr: N each
   void* out;
   float* lse;
   int32_t* dev_status;
@@ -63,17 +64,18 @@ ttv_status attn_prepare(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, floa
 ttv_status launch_attn(const AttnPlan& p, ttv_dtype dt, int B, int N, int Hq, int Hkv, int D,
                        float scale, const void* q, const void* k_cache, const void* v_cache,
                        int Lcap, const int32_t* cache_len, int Lmax, const void* k_tree,
-                       const void* v_tree, const int32_t* parents, void* out, float* lse,
-                       uint64_t* anc_out, int32_t* depth_out, int32_t* dev_status, void* ws,
-                       hipStream_t s);
+                       const void* v_tree, const int32_t* parents, const int32_t* n_nodes,
+                       void* out, float* lse, uint64_t* anc_out, int32_t* depth_out,
+                       int32_t* dev_status, void* ws, hipStream_t s);
 
 hipError_t launch_attn_fma(const AttnArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, bool bf16, hipStream_t s);
 
 // -------------------------------------------------------------- topology --
-hipError_t launch_topology(int B, int N, const int32_t* parents, uint64_t* anc_out,
-                           int32_t* depth_out, int32_t* dev_status, hipStream_t s);
+hipError_t launch_topology(int B, int N, const int32_t* parents, const int32_t* n_nodes,
+                           uint64_t* anc_out, int32_t* depth_out, int32_t* dev_status,
+                           hipStream_t s);
 
 // ---------------------------------------------------------- verification --
 struct GreedyPlan {
@@ -84,7 +86,7 @@ struct GreedyPlan {
 GreedyPlan greedy_plan(int B, int N, int V);
 
 hipError_t launch_verify_greedy(int B, int N, int V, const int32_t* parents,
-                                const int32_t* tokens, const float* llm,
+                                const int32_t* tokens, const int32_t* n_nodes, const float* llm,
                                 int32_t* path, int32_t* path_len, int32_t* out_tokens,
                                 int32_t* dev_status, void* ws, const GreedyPlan& p,
                                 hipStream_t s);
@@ -92,7 +94,8 @@ hipError_t launch_verify_greedy(int B, int N, int V, const int32_t* parents,
 // Greedy verification and the KV commit in one pass: argmax partials, then
 // one launch that scans each tree and copies the path's rows.
 hipError_t launch_verify_greedy_commit(int B, int N, int V, const int32_t* parents,
-                                       const int32_t* tokens, const float* llm, int32_t* path,
+                                       const int32_t* tokens, const int32_t* n_nodes,
+                                       const float* llm, int32_t* path,
                                        int32_t* path_len, int32_t* out_tokens,
                                        int32_t* dev_status, void* ws, const GreedyPlan& p,
                                        int elt, int Hkv, int D, int Lcap, int Lmax,
@@ -125,7 +128,8 @@ struct MssDraws {
 // Largest vocabulary the stochastic verifier holds in LDS.
 constexpr int kMssMaxVocab = 36864;
 hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
-                             const int32_t* tokens, const float* llm, const float* ssm,
+                             const int32_t* tokens, const int32_t* n_nodes, const float* llm,
+                             const float* ssm,
                              const MssDraws& dr, int32_t* path, int32_t* path_len,
                              int32_t* out_tokens, int32_t* dev_status, const CommitArgs& cm,
                              hipStream_t s);

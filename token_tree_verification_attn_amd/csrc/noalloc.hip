@@ -67,6 +67,6 @@ extern "C" ttv_status ttv_tree_attn_noalloc(ttv_dtype dt, int32_t B, int32_t N, 
   // the partials need no initialisation: every one a combine reads was written
   // by this call's attention kernel
   return launch_attn(p, dt, B, N, Hq, Hkv, D, scale, q, k_cache, v_cache, Lcap, cache_len, Lmax,
-                     k_tree, v_tree, parents, out, lse, anc_out, depth_out, dev_status, ws,
+                     k_tree, v_tree, parents, nullptr, out, lse, anc_out, depth_out, dev_status, ws,
                      static_cast<hipStream_t>(stream));
 }

@@ -164,6 +164,17 @@ __device__ inline bool wave_build_tree(const int32_t* __restrict__ par, int N,
   return true;
 }
 
+// Nodes of request b in a batch of trees of different sizes: n_nodes[b]
+// when given (rows hold N entries; entries at or past n_nodes[b] are padding
+// and never used), else N.  A count outside [1, N] rejects the request; the
+// kernels then work on the count clamped to [1, N] so that every access stays
+// inside the rows.
+__device__ __forceinline__ int nodes_raw(const int32_t* n_nodes, int b, int N) {
+  return n_nodes ? n_nodes[b] : N;
+}
+__device__ __forceinline__ bool nodes_ok(int n, int N) { return n >= 1 && n <= N; }
+__device__ __forceinline__ int nodes_used(int n, int N) { return min(max(n, 1), N); }
+
 // Tree validity only (one wave): parents[0] == -1 and 0 <= parents[i] < i.
 __device__ inline bool wave_tree_valid(const int32_t* __restrict__ par, int N) {
   bool bad = false;

@@ -29,12 +29,15 @@ __device__ __forceinline__ void amax_merge(float& bv, int& bi, float v, int i) {
 // once with 16-byte loads.  grid = (B*N, splits).
 template <bool VEC>
 __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* __restrict__ llm, int V,
-                                                             int slice, int splits,
+                                                             int slice, int splits, int N,
+                                                             const int32_t* __restrict__ n_nodes,
                                                              float* __restrict__ ws_val,
                                                              int* __restrict__ ws_idx) {
   __shared__ float s_v[4];
   __shared__ int s_i[4];
   const int row = blockIdx.x, sp = blockIdx.y;
+  // rows of padding nodes (past the request's node count) are never used
+  if (n_nodes && row % N >= nodes_used(n_nodes[row / N], N)) return;
   const int v0 = sp * slice, v1 = min(V, v0 + slice);
   const float* x = llm + (size_t)row * V;
   float bv = -INFINITY;
@@ -92,27 +95,31 @@ constexpr int kVerifyCommitThreads = 1024;
 // The scan of request b by one wavefront (lanes 0..63 of the caller).  Fills
 // s_path[0..n-1] with the path's nodes by depth; writes path / out_tokens /
 // path_len / dev_status when `write`.  Returns n (0 for a
-// malformed tree).  LDS is only written and read by this wavefront, whose LDS
+// malformed tree, -1 for a node count outside [1, N]).  LDS is only written and read by this wavefront, whose LDS
 // operations complete in order.
 __device__ int greedy_scan_wave(int b, int N, int splits, const int32_t* __restrict__ parents,
                                 const int32_t* __restrict__ tokens,
+                                const int32_t* __restrict__ n_nodes,
                                 const float* __restrict__ ws_val, const int* __restrict__ ws_idx,
                                 int32_t* __restrict__ path, int32_t* __restrict__ path_len,
                                 int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status,
                                 bool write, int32_t* s_path) {
   const int lane = threadIdx.x & 63;
   const int i0 = lane, i1 = lane + 64;
-  const bool v0 = i0 < N, v1 = i1 < N;
   const int32_t* par = parents + (size_t)b * N;
   const int32_t* tok = tokens + (size_t)b * N;
-  const int p0 = v0 ? par[i0] : -1, p1 = v1 ? par[i1] : -1;
-  const int t0 = v0 ? tok[i0] : -1, t1 = v1 ? tok[i1] : -1;
+  // every entry of the rows is requested at once with the node count; the
+  // entries of padding nodes are dropped afterwards
+  const int n_raw = nodes_raw(n_nodes, b, N);
+  const bool l0 = i0 < N, l1 = i1 < N;
+  int p0 = l0 ? par[i0] : -1, p1 = l1 ? par[i1] : -1;
+  const int t0 = l0 ? tok[i0] : -1, t1 = l1 ? tok[i1] : -1;
   float bv0[kMaxSplits], bv1[kMaxSplits];
   int bi0[kMaxSplits], bi1[kMaxSplits];
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp) {
     const size_t r0 = ((size_t)b * N + i0) * splits + sp, r1 = ((size_t)b * N + i1) * splits + sp;
-    const bool u0 = v0 && sp < splits, u1 = v1 && sp < splits;
+    const bool u0 = l0 && sp < splits, u1 = l1 && sp < splits;
     bv0[sp] = u0 ? ws_val[r0] : -INFINITY;
     bi0[sp] = u0 ? ws_idx[r0] : INT_MAX;
     bv1[sp] = u1 ? ws_val[r1] : -INFINITY;
@@ -125,8 +132,13 @@ __device__ int greedy_scan_wave(int b, int N, int splits, const int32_t* __restr
     amax_merge(m0, am0, bv0[sp], bi0[sp]);
     amax_merge(m1, am1, bv1[sp], bi1[sp]);
   }
+  const int nU = nodes_used(n_raw, N);
+  const bool n_ok = nodes_ok(n_raw, N);  // the same in every lane
+  const bool v0 = i0 < nU, v1 = i1 < nU;
+  p0 = v0 ? p0 : -1;
+  p1 = v1 ? p1 : -1;
   uint64_t a0lo, a1lo, a1hi;
-  if (!wave_tree_bits(p0, p1, N, a0lo, a1lo, a1hi)) {
+  if (!n_ok || !wave_tree_bits(p0, p1, nU, a0lo, a1lo, a1hi)) {
     if (write) {
       for (int k = lane; k < N; k += kWave) {
         path[(size_t)b * N + k] = -1;
@@ -134,10 +146,10 @@ __device__ int greedy_scan_wave(int b, int N, int splits, const int32_t* __restr
       }
       if (lane == 0) {
         path_len[b] = 0;
-        if (dev_status) dev_status[b] = TTV_E_TREE;
+        if (dev_status) dev_status[b] = n_ok ? TTV_E_TREE : TTV_E_SHAPE;
       }
     }
-    return 0;
+    return n_ok ? 0 : -1;
   }
   // node x lives in lane x & 63, slot x >> 6: both slots are shuffled by
   // every lane, then each picks its own
@@ -195,6 +207,7 @@ __device__ int greedy_scan_wave(int b, int N, int splits, const int32_t* __restr
 __global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
                                                          const int32_t* __restrict__ parents,
                                                          const int32_t* __restrict__ tokens,
+                                                         const int32_t* __restrict__ n_nodes,
                                                          const float* __restrict__ ws_val,
                                                          const int* __restrict__ ws_idx,
                                                          int32_t* __restrict__ path,
@@ -202,8 +215,8 @@ __global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
                                                          int32_t* __restrict__ out_tokens,
                                                          int32_t* __restrict__ dev_status) {
   __shared__ int32_t s_path[kMaxNodes];
-  greedy_scan_wave(blockIdx.x, N, splits, parents, tokens, ws_val, ws_idx, path, path_len,
-                   out_tokens, dev_status, true, s_path);
+  greedy_scan_wave(blockIdx.x, N, splits, parents, tokens, n_nodes, ws_val, ws_idx, path,
+                   path_len, out_tokens, dev_status, true, s_path);
 }
 
 // Kernel B and the KV commit in one launch.  Wave 0 scans request b's tree
@@ -222,7 +235,8 @@ __global__ __launch_bounds__(64) void greedy_scan_kernel(int N, int splits,
 // Statuses: the verifier's if it rejects the tree, else the commit's.
 __global__ __launch_bounds__(kVerifyCommitThreads) void greedy_scan_commit_kernel(
     int N, int splits, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
-    const float* __restrict__ ws_val, const int* __restrict__ ws_idx, int32_t* __restrict__ path,
+    const int32_t* __restrict__ n_nodes, const float* __restrict__ ws_val,
+    const int* __restrict__ ws_idx, int32_t* __restrict__ path,
     int32_t* __restrict__ path_len, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ dev_status, int row_vecs, int Hkv, int Lcap, int Lmax,
     const u32x4* __restrict__ k_tree, const u32x4* __restrict__ v_tree,
@@ -236,15 +250,15 @@ __global__ __launch_bounds__(kVerifyCommitThreads) void greedy_scan_commit_kerne
   const bool first = blockIdx.y == 0;  // writes the request's verifier outputs and lengths
   if (tid < kWave) {
     const int Lr = tid == 0 ? cache_len_in[b] : 0;  // requested with the scan's loads
-    const int n = greedy_scan_wave(b, N, splits, parents, tokens, ws_val, ws_idx, path, path_len,
-                                   out_tokens, nullptr, first, s_path);
+    const int n = greedy_scan_wave(b, N, splits, parents, tokens, n_nodes, ws_val, ws_idx, path,
+                                   path_len, out_tokens, nullptr, first, s_path);
     if (tid == 0) {
       s_n = n;
       s_len = Lr;
     }
   }
   __syncthreads();
-  const int n = s_n;  // 0: malformed tree
+  const int n = s_n;  // 0: malformed tree, -1: bad node count
   const int L = s_len;
   const bool shape_ok = L >= 0 && L <= Lmax && (long)L + n <= Lcap;
   const bool ok = n > 0 && shape_ok;
@@ -268,13 +282,15 @@ __global__ __launch_bounds__(kVerifyCommitThreads) void greedy_scan_commit_kerne
         committed_src[(size_t)b * N + j] = (ok && j < n) ? s_path[j] : -1;
     if (tid == 0) {
       cache_len_out[b] = ok ? L + n : L;
-      if (dev_status) dev_status[b] = n == 0 ? TTV_E_TREE : (shape_ok ? TTV_OK : TTV_E_SHAPE);
+      if (dev_status)
+        dev_status[b] = n == 0 ? TTV_E_TREE : (n > 0 && shape_ok ? TTV_OK : TTV_E_SHAPE);
     }
   }
 }
 
 hipError_t launch_verify_greedy_commit(int B, int N, int V, const int32_t* parents,
-                                       const int32_t* tokens, const float* llm, int32_t* path,
+                                       const int32_t* tokens, const int32_t* n_nodes,
+                                       const float* llm, int32_t* path,
                                        int32_t* path_len, int32_t* out_tokens,
                                        int32_t* dev_status, void* ws, const GreedyPlan& p,
                                        int elt, int Hkv, int D, int Lcap, int Lmax,
@@ -286,14 +302,18 @@ hipError_t launch_verify_greedy_commit(int B, int N, int V, const int32_t* paren
   int* ws_idx = reinterpret_cast<int*>(ws_val + (size_t)B * N * p.splits);
   const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(llm) & 15) == 0);
   const dim3 grid(B * N, p.splits);
-  if (vec) hipLaunchKernelGGL(argmax_partial_kernel<true>, grid, dim3(256), 0, s, llm, V, p.slice, p.splits, ws_val, ws_idx);
-  else hipLaunchKernelGGL(argmax_partial_kernel<false>, grid, dim3(256), 0, s, llm, V, p.slice, p.splits, ws_val, ws_idx);
+  if (vec)
+    hipLaunchKernelGGL(argmax_partial_kernel<true>, grid, dim3(256), 0, s, llm, V, p.slice,
+                       p.splits, N, n_nodes, ws_val, ws_idx);
+  else
+    hipLaunchKernelGGL(argmax_partial_kernel<false>, grid, dim3(256), 0, s, llm, V, p.slice,
+                       p.splits, N, n_nodes, ws_val, ws_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool per_head = cache_len_out != cache_len_in && Hkv > 1 && Hkv <= 65535;
   const dim3 grid2(B, per_head ? Hkv : 1), block2(per_head ? 256 : kVerifyCommitThreads);
   hipLaunchKernelGGL(greedy_scan_commit_kernel, grid2, block2, 0, s, N, p.splits, parents, tokens,
-                     ws_val, ws_idx, path, path_len, out_tokens, dev_status, D * elt / 16, Hkv,
+                     n_nodes, ws_val, ws_idx, path, path_len, out_tokens, dev_status, D * elt / 16, Hkv,
                      Lcap, Lmax, static_cast<const u32x4*>(k_tree),
                      static_cast<const u32x4*>(v_tree), static_cast<u32x4*>(k_cache),
                      static_cast<u32x4*>(v_cache), cache_len_in, cache_len_out, committed_src);
@@ -321,7 +341,7 @@ GreedyPlan greedy_plan(int B, int N, int V) {
 }
 
 hipError_t launch_verify_greedy(int B, int N, int V, const int32_t* parents,
-                                const int32_t* tokens, const float* llm,
+                                const int32_t* tokens, const int32_t* n_nodes, const float* llm,
                                 int32_t* path, int32_t* path_len, int32_t* out_tokens,
                                 int32_t* dev_status, void* ws, const GreedyPlan& p,
                                 hipStream_t s) {
@@ -329,12 +349,16 @@ hipError_t launch_verify_greedy(int B, int N, int V, const int32_t* parents,
   int* ws_idx = reinterpret_cast<int*>(ws_val + (size_t)B * N * p.splits);
   const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(llm) & 15) == 0);
   const dim3 grid(B * N, p.splits);
-  if (vec) hipLaunchKernelGGL(argmax_partial_kernel<true>, grid, dim3(256), 0, s, llm, V, p.slice, p.splits, ws_val, ws_idx);
-  else hipLaunchKernelGGL(argmax_partial_kernel<false>, grid, dim3(256), 0, s, llm, V, p.slice, p.splits, ws_val, ws_idx);
+  if (vec)
+    hipLaunchKernelGGL(argmax_partial_kernel<true>, grid, dim3(256), 0, s, llm, V, p.slice,
+                       p.splits, N, n_nodes, ws_val, ws_idx);
+  else
+    hipLaunchKernelGGL(argmax_partial_kernel<false>, grid, dim3(256), 0, s, llm, V, p.slice,
+                       p.splits, N, n_nodes, ws_val, ws_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(greedy_scan_kernel, dim3(B), dim3(kWave), 0, s, N, p.splits, parents, tokens,
-                     ws_val, ws_idx, path, path_len, out_tokens, dev_status);
+                     n_nodes, ws_val, ws_idx, path, path_len, out_tokens, dev_status);
   return hipGetLastError();
 }
 
@@ -567,7 +591,8 @@ __device__ __forceinline__ double mss_residual_regs(const f32x4 (&r)[kMssPfChunk
 template <bool VEC, bool PF>
 __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     int N, int V, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
-    const float* __restrict__ llm, const float* __restrict__ ssm, MssDraws dr,
+    const int32_t* __restrict__ n_nodes, const float* __restrict__ llm,
+    const float* __restrict__ ssm, MssDraws dr,
     int32_t* __restrict__ path, int32_t* __restrict__ path_len,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status, CommitArgs cm) {
   extern __shared__ __attribute__((aligned(16))) float s_w[];  // residual w, widx() layout
@@ -579,7 +604,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   __shared__ unsigned long long s_kids[kMaxNodes][2];
   __shared__ uint64_t s_first_ok[2];
   __shared__ double s_redd[kMssThreads / 64];
-  __shared__ int s_status, s_pick, s_len;
+  __shared__ int s_status, s_pick, s_len, s_nodes;
 
   const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
   const size_t rowN = (size_t)b * N;
@@ -599,12 +624,16 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   if (t == 0) {
     s_status = 0;
     s_len = commit ? cm.cache_len_in[b] : 0;
+    s_nodes = nodes_raw(n_nodes, b, N);
   }
   __syncthreads();
   const int L = s_len;
+  // the request's nodes (entries past them are padding, never used)
+  const int n_raw = s_nodes;
+  const int nU = nodes_used(n_raw, N);
   if (wave < 2) {  // nodes 0..127: tree validity and token range
     bool bad_tree = false, bad_tok = false;
-    if (t < N) {
+    if (t < nU) {
       const int p = s_par[t];
       bad_tree = (t == 0) ? (p != -1) : (p < 0 || p >= t);
       bad_tok = t > 0 && (s_tok[t] < 0 || s_tok[t] >= V);
@@ -612,7 +641,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     const uint64_t bt = __ballot(bad_tree), bk = __ballot(bad_tok);
     if ((t & 63) == 0) {
       if (bt) atomicOr(&s_status, 1);
-      if (bk) atomicOr(&s_status, 2);
+      if (bk || !nodes_ok(n_raw, N)) atomicOr(&s_status, 2);
     }
   }
   __syncthreads();
@@ -627,7 +656,9 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     __syncthreads();  // every thread has read cache_len_in[b]
     if (t == 0) {
       path_len[b] = 0;
-      if (dev_status) dev_status[b] = (st & 1) ? TTV_E_TREE : TTV_E_SHAPE;
+      // a bad node count or token is TTV_E_SHAPE, a malformed tree TTV_E_TREE
+      if (dev_status)
+        dev_status[b] = !nodes_ok(n_raw, N) ? TTV_E_SHAPE : (st & 1) ? TTV_E_TREE : TTV_E_SHAPE;
       if (commit) cm.cache_len_out[b] = L;
     }
     return;
@@ -637,7 +668,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   // The gathers go out first; the final-draw integer of every node (the walk
   // may end anywhere) is computed by waves 2-3 meanwhile.
   float qx = 0.f, px = 0.f, ua = 0.f;
-  if (t >= 1 && t < N) {
+  if (t >= 1 && t < nU) {
     const int p = s_par[t], x = s_tok[t];
     atomicOr(&s_kids[p][t >> 6], 1ull << (t & 63));
     qx = ssm[(rowN + t) * V + x];
@@ -651,7 +682,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   }
   __syncthreads();  // the children bitsets are complete
   bool first_ok = false;
-  if (t >= 1 && t < N) {
+  if (t >= 1 && t < nU) {
     const int p = s_par[t];
     float r = ua;
     if (seeded) {  // t is the j-th child of p, j = its lower siblings
@@ -913,8 +944,8 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
 }
 
 hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
-                             const int32_t* tokens, const float* llm, const float* ssm,
-                             const MssDraws& dr, int32_t* path, int32_t* path_len,
+                             const int32_t* tokens, const int32_t* n_nodes, const float* llm,
+                             const float* ssm, const MssDraws& dr, int32_t* path, int32_t* path_len,
                              int32_t* out_tokens, int32_t* dev_status, const CommitArgs& cm,
                              hipStream_t s) {
   const size_t lds = (size_t)(V + 4 * (V >> 7) + 4) * sizeof(float);  // widx(V - 1) + 1, 16-byte padded
@@ -925,8 +956,8 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(B), dim3(kMssThreads), lds, s, N, V, parents, tokens, llm, ssm,
-                     dr, path, path_len, out_tokens, dev_status, cm);
+  hipLaunchKernelGGL(kern, dim3(B), dim3(kMssThreads), lds, s, N, V, parents, tokens, n_nodes, llm,
+                     ssm, dr, path, path_len, out_tokens, dev_status, cm);
   return hipGetLastError();
 }
 
