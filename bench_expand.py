@@ -4,7 +4,7 @@ construction (ttv_tree_merge, --op merge).
 
     python bench_expand.py [--steps K] [--warmup W] [--B 16] [--F 16] [--V 32000] [--k 4]
     python bench_expand.py --op merge [--B 4] [--S 4] [--Ls 16]
-    python bench_expand.py --op probs [--B 16] [--F 64] [--V 32000] [--k 0] [--T 0.8]
+    python bench_expand.py --op probs [--B 16] [--F 64] [--V 32000] [--k 0] [--T 0.8] [--top-p 1]
 
 Workload: B requests, each expanding F frontier nodes by the k most probable
 tokens of their speculator rows of V fp32 probabilities (softmax of N(0,2)
@@ -117,7 +117,8 @@ def bench_merge(args):
 
 def bench_probs(args):
     """Probabilities from logits for B*F rows of V logits (N(0,2), the
-    stochastic workload's recipe) at temperature T, top-k k (0: all tokens);
+    stochastic workload's recipe) at temperature T, top-k k (0: all tokens),
+    top-p (1: off);
     each row read once and written once: 8V bytes per row."""
     B, F, V = args.B, args.F, args.V
     dev = torch.device("cuda:0")
@@ -130,7 +131,8 @@ def bench_probs(args):
     outs = [torch.empty_like(z) for _ in range(ncopies)]
 
     def call(i):
-        ttv.probs_from_logits(ins[i % ncopies], args.T, args.k, out=outs[i % ncopies])
+        ttv.probs_from_logits(ins[i % ncopies], args.T, args.k, out=outs[i % ncopies],
+                              top_p=args.top_p)
 
     stream = torch.cuda.current_stream(dev)
     for i in range(args.warmup):
@@ -146,6 +148,7 @@ def bench_probs(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "probs", "rows": B * F, "V": V, "T": args.T, "topk": args.k,
+                   "top_p": args.top_p,
                    "input_copies": ncopies, "launch": launch,
                    "inputs": "rotated, HBM-resident"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -167,6 +170,7 @@ def main():
                     help="frontier rows per request (expand: 16) or rows per request (probs: 64)")
     ap.add_argument("--V", type=int, default=32000)
     ap.add_argument("--k", type=int, default=4)
+    ap.add_argument("--top-p", type=float, default=1.0)
     ap.add_argument("--cpu-budget", type=float, default=3.0)
     args = ap.parse_args()
     if args.F is None:

@@ -507,28 +507,68 @@ ttv_status ttv_tree_merge(int32_t B, int32_t S, int32_t Ls, const int32_t* seqs,
 
 /*
  * ttv_probs_from_logits -- next-token probabilities from logits at a
- * temperature, optionally over the top-k logits only ([SI] §4 "Token
- * Verification": the stochastic verifier takes the LLM's and the
- * speculators' next-token distributions; [SSD] §4 samples with top-k, k = 50,
- * at T = 1).  For each of the R rows of V logits z:
- *   kept = every token, or with 0 < topk < V the topk highest logits (equal
- *          logits: the lower token id first);
- *   probs[r,v] = exp((z_v - m)/T) / sum over kept u of exp((z_u - m)/T) for
- *          kept v, 0 otherwise; m = the row maximum.
- * fp32 arithmetic (exp as 2^(x log2 e)); each row is read once from HBM and
- * written once.
+ * temperature, over the top-k logits and/or the top-p share of the mass
+ * ([SI] §4 "Token Verification": the stochastic verifier takes the LLM's and
+ * the speculators' next-token distributions; §7 "Multi-sample decoding":
+ * top-k or top-p sampling; [SSD] §4 samples with top-k, k = 50, at T = 1).
+ * For each of the R rows of V logits z, in the order (higher logit, then
+ * lower token id):
+ *   top-k  with 0 < topk < V the first topk tokens are kept (else all);
+ *   top-p  with top_p < 1, of those the shortest prefix whose mass reaches
+ *          ceil(P * S / 2^24), P = floor(top_p * 2^24), S their mass;
+ *   probs[r,v] = 2^t_v * (float)(2^40 / S') for kept v, 0 otherwise, with
+ *          t_v = (z_v - m) * (float)(log2(e) / T) (m = the row maximum),
+ *          S' the mass of the kept tokens.
+ * The arithmetic is fixed to the bit: 2^t = 2^n * P(t - n), n = t rounded to
+ * the nearest integer (ties to even), P the degree-7 Taylor polynomial of
+ * 2^f = exp(f ln 2) in Horner form with fused multiply-adds (coefficients
+ * ln(2)^k / k! formed in double, rounded to float), 0 for n < -125; the mass
+ * of a token is floor(2^t * 2^40) as an exact integer.  Each row is read
+ * once from HBM and written once.
  *
  *   R            rows (e.g. B*N for [B,N,V] logits).
  *   logits       float32 [R,V] device, finite.
  *   probs        float32 [R,V] device (may not alias logits).
- *   temperature  finite, > 0 (TTV_E_SHAPE otherwise).
+ *   temperature  finite, > 0, with log2(e)/T finite in float (TTV_E_SHAPE
+ *                otherwise).
  *   topk         0 (or >= V): every token; 1..512: the topk highest;
  *                larger values below V give TTV_E_UNSUPPORTED.
+ *   top_p        in (0, 1]; 1 keeps every token top-k kept (TTV_E_SHAPE
+ *                outside).
  * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_UNSUPPORTED, TTV_E_LAUNCH.
  */
 ttv_status ttv_probs_from_logits(int32_t R, int32_t V, float temperature,
-                                 int32_t topk, const float* logits, float* probs,
-                                 void* stream);
+                                 int32_t topk, float top_p, const float* logits,
+                                 float* probs, void* stream);
+
+/*
+ * ttv_tree_verify_logits -- stochastic ttv_tree_verify(_varlen) fed with
+ * logits: llm_logits [B,N,V] and ssm_logits [B,N,V] (float32, finite) stand
+ * for the distributions ttv_probs_from_logits(temperature, topk, top_p)
+ * gives for them, bit for bit, without those probabilities being written:
+ * one pass per tensor computes each row's maximum, normaliser and last kept
+ * token into the workspace, and the walk computes every probability it
+ * reads from the logits.  Results equal ttv_tree_verify_varlen(STOCHASTIC,
+ * ..., seed, step) on those probabilities; n_nodes is nullable (every
+ * request has N nodes).  Needs V % 4 == 0 and V <= 32768 (TTV_E_UNSUPPORTED
+ * otherwise) and 16-byte aligned logits.
+ *   workspace >= ttv_tree_verify_logits_workspace_size(B, N) bytes (2*B*N
+ *   row statistics of 16 bytes; no initialisation).
+ * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_UNSUPPORTED, TTV_E_ALIGN,
+ *         TTV_E_WORKSPACE, TTV_E_LAUNCH.
+ */
+ttv_status ttv_tree_verify_logits(int32_t B, int32_t N, int32_t V,
+                                  const int32_t* parents, const int32_t* tokens,
+                                  const int32_t* n_nodes,
+                                  const float* llm_logits,
+                                  const float* ssm_logits, float temperature,
+                                  int32_t topk, float top_p, uint64_t seed,
+                                  uint64_t step, int32_t* path,
+                                  int32_t* path_len, int32_t* out_tokens,
+                                  int32_t* dev_status, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+size_t ttv_tree_verify_logits_workspace_size(int32_t B, int32_t N);
 
 /*
  * ttv_kv_commit_inplace -- ttv_kv_commit for a tree stored inside the cache

@@ -56,7 +56,8 @@ def _bind(lib):
     lib.orc_kv_commit.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
     lib.orc_tree_expand.argtypes = [I, I, I, I, P, P, P, I, P, P, P, P, P]
     lib.orc_tree_merge.argtypes = [I, I, I, P, P, P, I, P, P, P, P, P]
-    lib.orc_probs_from_logits.argtypes = [I, I, ctypes.c_double, I, P, P]
+    lib.orc_probs_from_logits.argtypes = [I, I, ctypes.c_float, I, ctypes.c_float, P, P]
+    lib.orc_exp2_taylor.argtypes = [I, P, P]
     lib.orc_kv_commit_inplace.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P]
     U64 = ctypes.c_uint64
     lib.orc_philox4x64_10.argtypes = [P, P, P]
@@ -66,6 +67,7 @@ def _bind(lib):
     for f in (lib.orc_kv_commit_inplace, lib.orc_topology, lib.orc_tree_attn_rows, lib.orc_verify_greedy,
               lib.orc_verify_mss, lib.orc_kv_commit, lib.orc_tree_expand, lib.orc_tree_merge,
               lib.orc_probs_from_logits, lib.orc_philox4x64_10, lib.orc_verify_mss_seeded,
+              lib.orc_exp2_taylor,
               lib.orc_set_threads):
         f.restype = None
     return lib
@@ -361,17 +363,40 @@ def tree_merge(seqs, seq_len, root_tok, Ncap):
     return par, tok, src, n_out, status
 
 
-def probs_from_logits(logits, T=1.0, topk=0):
-    """Next-token probabilities from logits [..., V] at temperature T,
-    restricted to the topk highest logits when topk > 0 (equal logits: the
-    lower token id first); fp64 arithmetic, fp32 result."""
+def probs_from_logits(logits, T=1.0, topk=0, top_p=1.0):
+    """[SI] §4 "Token Verification", §7 (top-k / top-p sampling); [SSD] §4:
+    next-token probabilities from logits [..., V] at temperature T, over the
+    topk highest logits when topk > 0 (equal logits: the lower token id
+    first), then over the shortest prefix of those holding the share top_p
+    of their mass when 0 < top_p < 1.  fp32 arithmetic fixed exactly (see
+    oracle.c): 2^x by a degree-7 Taylor polynomial after range reduction,
+    masses as integers in 2^-40 units."""
     z, zp = _c(logits, np.float32)
     V = z.shape[-1]
     R = z.size // V
     out = np.empty_like(z)
-    _load().orc_probs_from_logits(R, V, float(T), int(topk), zp,
+    _load().orc_probs_from_logits(R, V, float(T), int(topk), float(top_p), zp,
                                   out.ctypes.data_as(ctypes.c_void_p))
     return out
+
+
+def exp2_taylor(t):
+    """2^t (fp32, t <= 0) exactly as the probabilities compute it."""
+    t, tp = _c(t, np.float32)
+    out = np.empty_like(t)
+    _load().orc_exp2_taylor(t.size, tp, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def verify_mss_logits(parents, tokens, llm_logits, ssm_logits, T, topk, top_p, seed, step,
+                      n_nodes=None):
+    """[SI] §4 "Token Verification" from raw logits: multi-step speculative
+    sampling (seeded draws) over the distributions probs_from_logits gives
+    for the LLM's and the speculator's logits at temperature T (top-k, top-p
+    as there)."""
+    p = probs_from_logits(llm_logits, T, topk, top_p)
+    q = probs_from_logits(ssm_logits, T, topk, top_p)
+    return verify_mss_seeded(parents, tokens, p, q, seed, step, n_nodes)
 
 
 def kv_commit_inplace(k_cache, v_cache, cache_len_in, path, path_len, Lmax, N):

@@ -595,38 +595,104 @@ void orc_tree_merge(int B, int S, int Ls, const int32_t* seqs, const int32_t* se
 
 /* ------------------------------------------------------------------------ */
 /* Probabilities from logits.  [SI] §4 "Token Verification" takes the LLM's  */
-/* and the speculators' next-token distributions for stochastic decoding;    */
-/* [SSD] §4 samples with top-k (k = 50) at temperature T = 1.  Row r:        */
-/* kept = all tokens, or with topk > 0 the topk highest logits (equal logits: */
-/* the lower token id first); probs[r,v] = exp((z_v - m)/T) / sum over kept   */
-/* of exp((z_u - m)/T) for kept v, 0 otherwise, m = the largest kept logit;   */
-/* in fp64, stored as fp32.                                                   */
+/* and the speculators' next-token distributions for stochastic decoding     */
+/* (§7 "Multi-sample decoding": top-k or top-p sampling); [SSD] §4 samples    */
+/* with top-k (k = 50) at temperature T = 1.  Row r of logits z:             */
+/*   order  tokens by logit, higher first, equal logits by lower token id;   */
+/*   top-k  with 0 < topk < V, keep the first topk in that order;            */
+/*   top-p  with 0 < top_p < 1, keep the shortest prefix (of what top-k      */
+/*          kept, in the same order) holding at least the share top_p of its */
+/*          probability mass;                                                */
+/*   p_v    proportional to exp((z_v - m) / T) over the kept tokens, 0 off   */
+/*          them, m = the largest logit.                                     */
+/* The arithmetic is fixed exactly (the GPU computes the same bits): with    */
+/* c = (float)(log2(e) / T) the exponent is t_v = (z_v - m) * c in fp32 and   */
+/* e_v = 2^t_v by range reduction to the nearest integer n and the Taylor    */
+/* polynomial of 2^f = exp(f ln 2), |f| <= 1/2, to degree 7 in Horner form    */
+/* with fused multiply-adds (truncation error below 1e-8 relative), 0 when   */
+/* n < -125; masses are M_v = floor(e_v * 2^40) as exact integers; top-p      */
+/* keeps the prefix up to the token where the running mass first reaches     */
+/* ceil(P * S / 2^24), P = floor(top_p * 2^24), S the kept mass before top-p; */
+/* p_v = e_v * (float)(2^40 / S') in fp32, S' the kept mass.                   */
 /* ------------------------------------------------------------------------ */
-void orc_probs_from_logits(int R, int V, double T, int topk, const float* logits, float* probs) {
-  unsigned char* kept = (unsigned char*)malloc((size_t)V);
+#define ORC_LOG2E 1.4426950408889634
+#define ORC_LN2 0.6931471805599453
+
+/* Taylor coefficients ln(2)^k / k!, each from the previous one by one       */
+/* multiplication and one division in double, then rounded to float.         */
+static void exp2_coefficients(float* cf) {
+  double a = 1.0;
+  cf[0] = 1.0f;
+  for (int k = 1; k <= 7; ++k) {
+    a = (a * ORC_LN2) / (double)k;
+    cf[k] = (float)a;
+  }
+}
+
+static float exp2_taylor(float t, const float* cf) {
+  const float n = rintf(t); /* nearest integer, ties to even */
+  if (n < -125.0f) return 0.0f;
+  const float f = t - n; /* exact, |f| <= 1/2 */
+  float p = cf[7];
+  for (int k = 6; k >= 0; --k) p = fmaf(p, f, cf[k]);
+  return ldexpf(p, (int)n);
+}
+
+static uint64_t mass40(float e) { return (uint64_t)((double)e * 1099511627776.0); }
+
+/* exact 2^t of the probabilities' definition, for the pins */
+void orc_exp2_taylor(int n, const float* t, float* out) {
+  float cf[8];
+  exp2_coefficients(cf);
+  for (int i = 0; i < n; ++i) out[i] = exp2_taylor(t[i], cf);
+}
+
+static const float* g_sort_z; /* the row being ordered (qsort has no context) */
+static int by_logit_then_id(const void* a, const void* b) {
+  const int i = *(const int*)a, j = *(const int*)b;
+  if (g_sort_z[i] > g_sort_z[j]) return -1;
+  if (g_sort_z[i] < g_sort_z[j]) return 1;
+  return i < j ? -1 : (i > j ? 1 : 0);
+}
+
+void orc_probs_from_logits(int R, int V, float T, int topk, float top_p, const float* logits,
+                           float* probs) {
+  float cf[8];
+  exp2_coefficients(cf);
+  const float c = (float)(ORC_LOG2E / (double)T);
+  int* order = (int*)malloc(sizeof(int) * (size_t)V);
+  float* e = (float*)malloc(sizeof(float) * (size_t)V);
   for (int r = 0; r < R; ++r) {
     const float* z = logits + (size_t)r * V;
     float* p = probs + (size_t)r * V;
-    if (topk > 0 && topk < V) {
-      memset(kept, 0, (size_t)V);
-      for (int j = 0; j < topk; ++j) {
-        int best = -1;
-        for (int v = 0; v < V; ++v)
-          if (!kept[v] && (best < 0 || z[v] > z[best])) best = v;
-        kept[best] = 1;
+    for (int v = 0; v < V; ++v) order[v] = v;
+    g_sort_z = z;
+    qsort(order, (size_t)V, sizeof(int), by_logit_then_id);
+    const float m = z[order[0]];
+    for (int v = 0; v < V; ++v) e[v] = exp2_taylor((z[v] - m) * c, cf);
+    int kept = (topk > 0 && topk < V) ? topk : V; /* the first `kept` of the order */
+    if (top_p > 0.0f && top_p < 1.0f) {
+      uint64_t S = 0;
+      for (int j = 0; j < kept; ++j) S += mass40(e[order[j]]);
+      const uint64_t P = (uint64_t)(top_p * 16777216.0f); /* exact: scaling by 2^24 */
+      const uint64_t need = (uint64_t)(((unsigned __int128)P * S + 16777215u) >> 24);
+      uint64_t run = 0;
+      int j = 0;
+      while (j < kept) {
+        run += mass40(e[order[j]]);
+        ++j;
+        if (run >= need) break;
       }
-    } else {
-      memset(kept, 1, (size_t)V);
+      kept = j;
     }
-    double m = -INFINITY;
-    for (int v = 0; v < V; ++v)
-      if (kept[v] && (double)z[v] > m) m = (double)z[v];
-    double s = 0.0;
-    for (int v = 0; v < V; ++v)
-      if (kept[v]) s += exp(((double)z[v] - m) / T);
-    for (int v = 0; v < V; ++v) p[v] = kept[v] ? (float)(exp(((double)z[v] - m) / T) / s) : 0.0f;
+    uint64_t S = 0;
+    for (int j = 0; j < kept; ++j) S += mass40(e[order[j]]);
+    const float inv = (float)(1099511627776.0 / (double)S);
+    for (int v = 0; v < V; ++v) p[v] = 0.0f;
+    for (int j = 0; j < kept; ++j) p[order[j]] = e[order[j]] * inv;
   }
-  free(kept);
+  free(order);
+  free(e);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -223,10 +223,12 @@ def test_tree_merge_host_validation(kw, status):
     (dict(z=None), ttv.E_NULL), (dict(p=None), ttv.E_NULL), (dict(R=0), ttv.E_SHAPE),
     (dict(V=0), ttv.E_SHAPE), (dict(T=0.0), ttv.E_SHAPE), (dict(T=float("inf")), ttv.E_SHAPE),
     (dict(T=float("nan")), ttv.E_SHAPE), (dict(k=-1), ttv.E_SHAPE),
-    (dict(k=513), ttv.E_UNSUPPORTED),
+    (dict(k=513), ttv.E_UNSUPPORTED), (dict(top_p=0.0), ttv.E_SHAPE),
+    (dict(top_p=1.5), ttv.E_SHAPE), (dict(top_p=float("nan")), ttv.E_SHAPE),
+    (dict(T=1e-39), ttv.E_SHAPE),
 ])
 def test_probs_from_logits_host_validation(kw, status):
-    args = dict(R=4, V=1000, T=0.8, k=50, z=A, p=A)
+    args = dict(R=4, V=1000, T=0.8, k=50, top_p=1.0, z=A, p=A)
     args.update(kw)
     assert ttv.lib().ttv_probs_from_logits(*args.values(), None) == status
 
@@ -325,3 +327,19 @@ def test_varlen_entry_points_need_node_counts():
         0, 1, 2, 8, 64, 2, 64, 100, A, A, n, A, None, 7, 0, A, A, A, A, A, A + 0x100,
         kw.get("Lmax", 50), A, A, A, None, None, A, 1 << 20, None)
     assert vc(None) == ttv.E_NULL and vc(A, Lmax=93) == ttv.E_SHAPE
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(par=None), ttv.E_NULL), (dict(zl=None), ttv.E_NULL), (dict(zs=None), ttv.E_NULL),
+    (dict(B=0), ttv.E_SHAPE), (dict(T=0.0), ttv.E_SHAPE), (dict(top_p=0.0), ttv.E_SHAPE),
+    (dict(V=1002), ttv.E_UNSUPPORTED), (dict(V=32772), ttv.E_UNSUPPORTED),
+    (dict(N=129), ttv.E_UNSUPPORTED), (dict(k=600), ttv.E_UNSUPPORTED),
+    (dict(zl=MIS), ttv.E_ALIGN), (dict(ws=None), ttv.E_WORKSPACE),
+    (dict(wsb=2 * 2 * 8 * 16 - 1), ttv.E_WORKSPACE),
+])
+def test_tree_verify_logits_host_validation(kw, status):
+    args = dict(B=2, N=8, V=1000, par=A, tok=A, nn=None, zl=A, zs=A, T=0.8, k=0, top_p=0.9,
+                seed=1, step=0, path=A, plen=A, outt=A, st=None, ws=A, wsb=1 << 20)
+    args.update(kw)
+    assert ttv.lib().ttv_tree_verify_logits(*args.values(), None) == status
+    assert ttv.lib().ttv_tree_verify_logits_workspace_size(2, 8) == 2 * 2 * 8 * 16

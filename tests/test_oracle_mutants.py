@@ -70,7 +70,7 @@ MUTANTS = [
     ("mss_counter_words_swapped", "const uint64_t ctr[4] = {j, (uint64_t)u, (uint64_t)b, step};",
      "const uint64_t ctr[4] = {(uint64_t)u, j, (uint64_t)b, step};",
      lambda: PH.test_seeded_walk_uses_documented_counters(1005, 0, {})),
-    ("mss_attempt_ordinal_not_advanced", "      ++j;\n", "\n",
+    ("mss_attempt_ordinal_not_advanced", "      ++j;\n      const float lhs", "\n      const float lhs",
      lambda: PH.test_seeded_walk_uses_documented_counters(3, 2, dict(
          B=64, N=9, tree="star", V=8, prob_sigma=3.0))),
     ("mss_bonus_counter", "#define ORC_BONUS_ORDINAL 0x8000000000000000ull",
@@ -107,11 +107,21 @@ MUTANTS = [
      lambda: [MG.test_brute_force_prefix_sets(s) for s in range(8)]),
     ("merge_parent_same_depth", "pb[next] = node_of[(size_t)s * (Ls + 1) + d - 1];",
      "pb[next] = node_of[(size_t)s * (Ls + 1) + (d > 1 ? d - 2 : 0)];", MG.test_hand_example),
-    ("probs_temperature_dropped", "if (kept[v]) s += exp(((double)z[v] - m) / T);",
-     "if (kept[v]) s += exp(((double)z[v] - m));", lambda: PR.test_matches_scipy_softmax(0.8)),
-    ("probs_topk_ties_to_highest", "if (!kept[v] && (best < 0 || z[v] > z[best])) best = v;",
-     "if (!kept[v] && (best < 0 || z[v] >= z[best])) best = v;",
+    ("probs_temperature_dropped", "const float c = (float)(ORC_LOG2E / (double)T);",
+     "const float c = (float)ORC_LOG2E;", lambda: PR.test_matches_scipy_softmax(0.8)),
+    ("probs_ties_to_highest_id", "return i < j ? -1 : (i > j ? 1 : 0);",
+     "return i > j ? -1 : (i < j ? 1 : 0);",
      lambda: PR.test_topk_keeps_the_stable_argsort_prefix(5)),
+    ("probs_taylor_degree_6", "float p = cf[7];\n  for (int k = 6; k >= 0; --k)",
+     "float p = cf[6];\n  for (int k = 5; k >= 0; --k)", PR.test_exp2_against_numpy),
+    ("probs_range_reduction_floor", "const float n = rintf(t);", "const float n = floorf(t);",
+     PR.test_exp2_against_numpy),
+    ("probs_topp_crossing_token_dropped", "        run += mass40(e[order[j]]);\n        ++j;\n        if (run >= need) break;",
+     "        if (run + mass40(e[order[j]]) >= need) break;\n        run += mass40(e[order[j]]);\n        ++j;",
+     lambda: PR.test_topp_keeps_the_shortest_prefix_reaching_p(0.8, 0, 0.9)),
+    ("probs_topp_before_topk", "int kept = (topk > 0 && topk < V) ? topk : V;",
+     "int kept = V;",
+     lambda: PR.test_topp_keeps_the_shortest_prefix_reaching_p(0.8, 50, 0.95)),
     ("commit_inplace_source_without_length",
      "memcpy(tk + (size_t)j * row, (const char*)k_cache + (base + L + pb[j]) * row, row);",
      "memcpy(tk + (size_t)j * row, (const char*)k_cache + (base + pb[j]) * row, row);",

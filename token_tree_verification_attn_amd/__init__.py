@@ -24,7 +24,8 @@ from typing import Optional
 import torch
 
 __all__ = ["tree_topology", "tree_attn", "tree_verify", "tree_verify_uniforms", "kv_commit",
-           "tree_verify_commit", "tree_expand", "tree_merge", "probs_from_logits",
+           "tree_verify_commit", "tree_verify_logits", "tree_expand", "tree_merge",
+           "probs_from_logits",
            "kv_commit_inplace", "tree_attn_noalloc", "tree_attn_workspace_size",
            "tree_verify_workspace_size",
            "status_string",
@@ -94,7 +95,11 @@ def lib():
                                     _P, _P, _P]
         L.ttv_tree_expand.argtypes = [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
         L.ttv_tree_merge.argtypes = [_I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P]
-        L.ttv_probs_from_logits.argtypes = [_I, _I, _F, _I, _P, _P, _P]
+        L.ttv_probs_from_logits.argtypes = [_I, _I, _F, _I, _F, _P, _P, _P]
+        L.ttv_tree_verify_logits.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _F, _I, _F, _U64,
+                                             _U64, _P, _P, _P, _P, _P, _SZ, _P]
+        L.ttv_tree_verify_logits_workspace_size.argtypes = [_I, _I]
+        L.ttv_tree_verify_logits_workspace_size.restype = _SZ
         L.ttv_kv_commit_inplace.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P,
                                             _P, _P, _P]
         L.ttv_tree_verify_commit.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _U64,
@@ -105,7 +110,7 @@ def lib():
                   "ttv_tree_attn_varlen", "ttv_tree_verify_varlen",
                   "ttv_tree_verify_commit_varlen", "ttv_tree_verify",
                   "ttv_tree_verify_uniforms", "ttv_kv_commit", "ttv_tree_expand",
-                  "ttv_tree_merge", "ttv_probs_from_logits"):
+                  "ttv_tree_merge", "ttv_probs_from_logits", "ttv_tree_verify_logits"):
             getattr(L, f).restype = _I
         _lib = L
     return _lib
@@ -458,6 +463,40 @@ def tree_verify_commit(mode: int, parents, tokens, llm, k_tree, v_tree, k_cache,
     return path, path_len, out_tokens, cache_len_out, committed_src, dev_status
 
 
+def tree_verify_logits(parents, tokens, llm_logits, ssm_logits, temperature: float,
+                       topk: int = 0, top_p: float = 1.0, seed: int = 0, step: int = 0,
+                       n_nodes=None, path=None, path_len=None, out_tokens=None,
+                       dev_status=None, workspace=None):
+    """Multi-step speculative sampling fed with logits [B,N,V]: the
+    distributions probs_from_logits(temperature, topk, top_p) gives for
+    them, computed by the verifier as it reads them.  Returns (path,
+    path_len, out_tokens, dev_status)."""
+    B, N = parents.shape
+    V = llm_logits.shape[2]
+    dev = parents.device
+    _need(parents, "parents", torch.int32, (B, N), dev)
+    _need(tokens, "tokens", torch.int32, (B, N), dev)
+    _need(llm_logits, "llm_logits", torch.float32, (B, N, V), dev)
+    _need(ssm_logits, "ssm_logits", torch.float32, (B, N, V), dev)
+    if n_nodes is not None:
+        _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    path, path_len, out_tokens, dev_status = _verify_outputs(B, N, dev, path, path_len,
+                                                             out_tokens, dev_status)
+    nbytes = lib().ttv_tree_verify_logits_workspace_size(B, N)
+    if nbytes == ctypes.c_size_t(-1).value:
+        raise ValueError("unsupported tree_verify_logits sizes")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib().ttv_tree_verify_logits(B, N, V, _ptr(parents), _ptr(tokens), _ptr(n_nodes),
+                                      _ptr(llm_logits), _ptr(ssm_logits), float(temperature),
+                                      int(topk), float(top_p), _u64(seed), _u64(step),
+                                      _ptr(path), _ptr(path_len), _ptr(out_tokens),
+                                      _ptr(dev_status), _ptr(workspace), wsb, _stream(dev))
+    _check("ttv_tree_verify_logits", st)
+    return path, path_len, out_tokens, dev_status
+
+
 def tree_expand(probs, frontier, n_in, k: int, parents, tokens, src_row=None, n_out=None,
                 dev_status=None):
     """One level of expansion-based tree construction, appended in place to
@@ -515,9 +554,12 @@ def tree_merge(seqs, seq_len, root_tok, Ncap: int = 128, parents=None, tokens=No
     return out[0], out[1], out[2], n_out, dev_status
 
 
-def probs_from_logits(logits, temperature: float = 1.0, topk: int = 0, out=None):
+def probs_from_logits(logits, temperature: float = 1.0, topk: int = 0, out=None,
+                      top_p: float = 1.0):
     """Probabilities over the last axis of fp32 logits [..., V] at a
-    temperature, restricted to the topk highest logits when topk > 0."""
+    temperature, restricted to the topk highest logits when topk > 0 and to
+    the shortest prefix holding the share top_p of their mass when
+    top_p < 1."""
     V = logits.shape[-1]
     R = logits.numel() // V
     dev = logits.device
@@ -525,8 +567,8 @@ def probs_from_logits(logits, temperature: float = 1.0, topk: int = 0, out=None)
     if out is None:
         out = torch.empty_like(logits)
     _need(out, "out", torch.float32, tuple(logits.shape), dev)
-    st = lib().ttv_probs_from_logits(R, V, float(temperature), int(topk), _ptr(logits),
-                                     _ptr(out), _stream(dev))
+    st = lib().ttv_probs_from_logits(R, V, float(temperature), int(topk), float(top_p),
+                                     _ptr(logits), _ptr(out), _stream(dev))
     _check("ttv_probs_from_logits", st)
     return out
 

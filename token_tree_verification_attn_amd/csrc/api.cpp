@@ -8,6 +8,7 @@
 #include <cmath>
 
 #include "launch.h"
+#include "softmax_exact.h"
 #include "ttv.h"
 
 using namespace ttv;
@@ -327,7 +328,7 @@ static ttv_status tree_verify_call(ttv_verify_mode mode, int32_t B, int32_t N, i
     if (V > kMssMaxVocab) return TTV_E_UNSUPPORTED;
     if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
     return launch_status(launch_verify_mss(B, N, V, parents, tokens, n_nodes, llm, ssm,
-                                           MssDraws{nullptr, nullptr, seed, step}, path,
+                                           MssDraws{nullptr, nullptr, seed, step}, LogitRows{}, path,
                                            path_len, out_tokens, dev_status, CommitArgs{}, s));
   }
   const GreedyPlan p = greedy_plan(B, N, V);
@@ -372,7 +373,7 @@ ttv_status ttv_tree_verify_uniforms(int32_t B, int32_t N, int32_t V, const int32
   if ((long)B * N > 0x7fffffffL) return TTV_E_UNSUPPORTED;
   if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
   return launch_status(launch_verify_mss(B, N, V, parents, tokens, nullptr, llm, ssm,
-                                         MssDraws{u_accept, u_bonus, 0, 0}, path, path_len,
+                                         MssDraws{u_accept, u_bonus, 0, 0}, LogitRows{}, path, path_len,
                                          out_tokens, dev_status, CommitArgs{},
                                          static_cast<hipStream_t>(stream)));
 }
@@ -428,7 +429,7 @@ static ttv_status tree_verify_commit_call(
     CommitArgs cm{D * elt / 16, Hkv, Lcap, Lmax, k_tree, v_tree, k_cache, v_cache,
                   cache_len_in, cache_len_out, committed_src};
     return launch_status(launch_verify_mss(B, N, V, parents, tokens, n_nodes, llm, ssm,
-                                           MssDraws{nullptr, nullptr, seed, step}, path,
+                                           MssDraws{nullptr, nullptr, seed, step}, LogitRows{}, path,
                                            path_len, out_tokens, dev_status, cm, s));
   }
   const GreedyPlan p = greedy_plan(B, N, V);
@@ -500,15 +501,70 @@ ttv_status ttv_tree_merge(int32_t B, int32_t S, int32_t Ls, const int32_t* seqs,
                                          static_cast<hipStream_t>(stream)));
 }
 
-ttv_status ttv_probs_from_logits(int32_t R, int32_t V, float temperature, int32_t topk,
-                                 const float* logits, float* probs, void* stream) {
-  if (!logits || !probs) return TTV_E_NULL;
-  if (R < 1 || V < 1 || topk < 0 || !std::isfinite(temperature) || !(temperature > 0.f))
+}  // extern "C"
+
+namespace {
+
+// Host checks of the logits processing arguments shared by the entry points.
+ttv_status probs_args_ok(int32_t V, float temperature, int32_t topk, float top_p) {
+  if (V < 1 || topk < 0 || !std::isfinite(temperature) || !(temperature > 0.f) ||
+      !std::isfinite(probs_scale(temperature)) || !(top_p > 0.f && top_p <= 1.f))
     return TTV_E_SHAPE;
   if (topk > kProbsMaxTopk && topk < V) return TTV_E_UNSUPPORTED;
+  return TTV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttv_status ttv_probs_from_logits(int32_t R, int32_t V, float temperature, int32_t topk,
+                                 float top_p, const float* logits, float* probs, void* stream) {
+  if (!logits || !probs) return TTV_E_NULL;
+  if (R < 1) return TTV_E_SHAPE;
+  const ttv_status st = probs_args_ok(V, temperature, topk, top_p);
+  if (st != TTV_OK) return st;
   const bool vec = V % 4 == 0 && aligned16(logits) && aligned16(probs);
-  return launch_status(launch_probs(R, V, temperature, topk, logits, probs, vec,
+  return launch_status(launch_probs(R, V, temperature, topk, top_p, logits, probs, nullptr, vec,
                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t ttv_tree_verify_logits_workspace_size(int32_t B, int32_t N) {
+  if (B < 1 || N < 1 || N > TTV_MAX_NODES) return (size_t)-1;
+  return (size_t)2 * B * N * sizeof(RowStats);
+}
+
+ttv_status ttv_tree_verify_logits(int32_t B, int32_t N, int32_t V, const int32_t* parents,
+                                  const int32_t* tokens, const int32_t* n_nodes,
+                                  const float* llm_logits, const float* ssm_logits,
+                                  float temperature, int32_t topk, float top_p, uint64_t seed,
+                                  uint64_t step, int32_t* path, int32_t* path_len,
+                                  int32_t* out_tokens, int32_t* dev_status, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!parents || !tokens || !llm_logits || !ssm_logits || !path || !path_len || !out_tokens)
+    return TTV_E_NULL;
+  if (B < 1 || N < 1) return TTV_E_SHAPE;
+  const ttv_status st = probs_args_ok(V, temperature, topk, top_p);
+  if (st != TTV_OK) return st;
+  if (N > TTV_MAX_NODES || (long)B * N > 0x7fffffffL) return TTV_E_UNSUPPORTED;
+  if (V % 4 != 0 || V > kMssLogitsMaxVocab) return TTV_E_UNSUPPORTED;
+  if (!aligned16(llm_logits) || !aligned16(ssm_logits)) return TTV_E_ALIGN;
+  const size_t need = (size_t)2 * B * N * sizeof(RowStats);
+  if (!workspace || workspace_bytes < need) return TTV_E_WORKSPACE;
+  if (!aligned16(workspace)) return TTV_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RowStats* st_llm = static_cast<RowStats*>(workspace);
+  RowStats* st_ssm = st_llm + (size_t)B * N;
+  // each row's statistics, then the walk computes the probabilities it reads
+  if (launch_probs(B * N, V, temperature, topk, top_p, llm_logits, nullptr, st_llm, true, s) !=
+          hipSuccess ||
+      launch_probs(B * N, V, temperature, topk, top_p, ssm_logits, nullptr, st_ssm, true, s) !=
+          hipSuccess)
+    return TTV_E_LAUNCH;
+  return launch_status(launch_verify_mss(
+      B, N, V, parents, tokens, n_nodes, llm_logits, ssm_logits,
+      MssDraws{nullptr, nullptr, seed, step}, LogitRows{st_llm, st_ssm, probs_scale(temperature)},
+      path, path_len, out_tokens, dev_status, CommitArgs{}, s));
 }
 
 ttv_status ttv_kv_commit_inplace(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv, int32_t D,

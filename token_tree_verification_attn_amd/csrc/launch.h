@@ -125,14 +125,25 @@ struct MssDraws {
   uint64_t seed, step;
 };
 
-// Largest vocabulary the stochastic verifier holds in LDS.
+// Rows of llm / ssm given as logits: their statistics (from launch_probs in
+// statistics mode) and c = (float)(log2(e) / T); st_llm == nullptr means the
+// rows are probabilities.
+struct RowStats;
+struct LogitRows {
+  const RowStats* st_llm;
+  const RowStats* st_ssm;
+  float c;
+};
+
+// Largest vocabulary the stochastic verifier holds in LDS; rows given as
+// logits need 16-byte rows of at most kMssLogitsMaxVocab entries.
 constexpr int kMssMaxVocab = 36864;
+constexpr int kMssLogitsMaxVocab = 32768;
 hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                              const int32_t* tokens, const int32_t* n_nodes, const float* llm,
-                             const float* ssm,
-                             const MssDraws& dr, int32_t* path, int32_t* path_len,
-                             int32_t* out_tokens, int32_t* dev_status, const CommitArgs& cm,
-                             hipStream_t s);
+                             const float* ssm, const MssDraws& dr, const LogitRows& lr,
+                             int32_t* path, int32_t* path_len, int32_t* out_tokens,
+                             int32_t* dev_status, const CommitArgs& cm, hipStream_t s);
 
 // ----------------------------------------------------------------- commit --
 hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,
@@ -159,8 +170,10 @@ hipError_t launch_tree_merge(int B, int S, int Ls, const int32_t* seqs, const in
 
 // --------------------------------------------------------- probabilities --
 constexpr int kProbsMaxTopk = 512;  // the top-k bound takes ceil(k/16) <= 64 maxima per wave
-hipError_t launch_probs(int R, int V, float T, int topk, const float* logits, float* probs,
-                        bool vec, hipStream_t s);
+// probabilities (probs != nullptr) or each row's statistics (stats)
+hipError_t launch_probs(int R, int V, float T, int topk, float top_p, const float* logits,
+                        float* probs, RowStats* stats, bool vec, hipStream_t s);
+float probs_scale(float T);  // (float)(log2(e) / T)
 
 hipError_t launch_kv_commit_inplace(int elt, int B, int N, int Hkv, int D, int Lcap, void* k_cache,
                                     void* v_cache, const int32_t* cache_len_in,

@@ -1,25 +1,35 @@
-// probs.hip -- next-token probabilities from logits at a temperature,
-// optionally over the top-k logits only ([SI] §4 "Token Verification": the
-// stochastic verifier takes the LLM's and the speculators' distributions;
-// [SSD] §4 samples with top-k, k = 50, at T = 1).
+// probs.hip -- next-token probabilities from logits at a temperature, over
+// the top-k logits and/or the top-p share of the mass ([SI] §4 "Token
+// Verification": the stochastic verifier takes the LLM's and the
+// speculators' distributions; §7 "Multi-sample decoding": top-k or top-p
+// sampling; [SSD] §4 samples with top-k, k = 50, at T = 1).  The arithmetic
+// is fixed to the bit (softmax_exact.h).
 //
 // One 1024-thread workgroup per row.  A row of up to 32768 logits is requested
-// whole (8 16-byte loads per thread) and kept in registers; a longer one is
-// streamed, once per pass.  With top-k, the k-th entry of the row in the
-// order (higher logit, then lower token id) is found much as in tree
-// expansion: the smallest over the 16 waves of each wave's ceil(k/16)-th
-// largest per-thread maximum bounds it from below, the entries at or above
-// that bound are gathered in LDS, and the one that exactly k-1
-// gathered entries rank before is it (each thread counts for its own
-// candidates; a row whose ties overflow the buffer takes k rounds of a
-// block arg-max over the whole row instead); an entry is kept iff it ranks at
-// or before it.  Then m = the row maximum (always
-// kept), s = the sum over kept entries of 2^((z - m) * log2(e) / T), and
-// probs = 2^((z - m) * log2(e) / T) / s for kept entries, 0 for the others.
-// The row is read once from HBM and written once.
+// whole (8 16-byte loads per thread) and kept in registers with its 2^t
+// values; a longer one is streamed, once per pass.
+//  * top-k: the k-th entry in the order (higher logit, then lower token id)
+//    is found as in tree expansion: the smallest over the 16 waves of each
+//    wave's ceil(k/16)-th largest per-thread maximum bounds it from below,
+//    the entries at or above that bound are gathered in LDS, and the one that
+//    exactly k-1 gathered entries rank before is it (a row whose ties
+//    overflow the buffer takes k rounds of a block arg-max instead).
+//  * top-p: with S the exact mass kept by top-k and P = floor(top_p * 2^24),
+//    the last kept token is the one where the running mass in that order
+//    first reaches ceil(P * S / 2^24).  It is found by histograms of the
+//    masses over 2048 equal bins of the logit range (LDS 64-bit atomics;
+//    exact integer sums, so any order gives the same bins): the bin where the
+//    running mass crosses becomes the next range until it holds at most
+//    1024 tokens, which are gathered and ranked in LDS; a range of equal
+//    logits (equal masses) is settled by counting token ids.
+// Then S' = the kept mass, p = 2^t * (float)(2^40 / S') for kept tokens, 0
+// for the others.  The row is read once from HBM and written once; with
+// `stats` the kernel writes the row's (max, normaliser, last kept token)
+// instead, for a consumer that computes probabilities from the logits itself.
 #include <limits.h>
 
 #include "launch.h"
+#include "softmax_exact.h"
 #include "ttv_common.h"
 
 namespace ttv {
@@ -30,6 +40,8 @@ constexpr int kProbThreads = 1024;  // 512 measured 3.5% slower with top-50
 constexpr int kProbWaves = kProbThreads / 64;
 constexpr int kProbRegQuads = 8;
 constexpr int kProbCandidates = 2048;
+constexpr int kPBins = 2048;        // top-p histogram bins
+constexpr int kPGather = 1024;      // top-p: tokens ranked in LDS at once
 
 __device__ __forceinline__ bool p_ranks_before(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
@@ -47,27 +59,44 @@ __device__ __forceinline__ void p_wave_argmax(float& bv, int& bi) {
   }
 }
 
+// An unsigned key of a logit that orders like the logit (-0 taken as +0, so
+// that equal logits have equal keys).
+__device__ __forceinline__ uint32_t p_order_key(float z) {
+  const uint32_t u = __float_as_uint(z + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t p_wave_sum_u64(uint64_t x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += shfl_xor_u64(x, m);
+  return x;
+}
+
 }  // namespace
 
 template <bool VEC>
 __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int topk,
+                                                             uint32_t top_p24,
                                                              const float* __restrict__ logits,
-                                                             float* __restrict__ probs) {
+                                                             float* __restrict__ probs,
+                                                             RowStats* __restrict__ stats) {
   __shared__ float s_red[kProbWaves];
+  __shared__ uint64_t s_red64[kProbWaves];
   __shared__ float s_cv[kProbCandidates];
   __shared__ int s_ci[kProbCandidates];
+  __shared__ uint64_t s_hist[kPBins];
   __shared__ float s_wv[kProbWaves];
   __shared__ int s_wi[kProbWaves];
-  __shared__ int s_cnt;
-  __shared__ float s_thr;
+  __shared__ int s_cnt, s_bin, s_done;
+  __shared__ float s_thr, s_zt;
+  __shared__ int s_it;
+  __shared__ uint64_t s_above;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* row = logits + (size_t)blockIdx.x * V;
-  float* out = probs + (size_t)blockIdx.x * V;
   const f32x4* r4 = reinterpret_cast<const f32x4*>(row);
-  f32x4* o4 = reinterpret_cast<f32x4*>(out);
   const int n4 = V / 4;
   const bool in_regs = VEC && n4 <= kProbRegQuads * kProbThreads;
-  f32x4 rq[kProbRegQuads];
+  f32x4 rq[kProbRegQuads], re[kProbRegQuads];
   if (in_regs) {
 #pragma unroll
     for (int u = 0; u < kProbRegQuads; ++u) {
@@ -107,14 +136,14 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
     __syncthreads();
     return r;
   };
-  auto block_sum = [&](float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-    if (lane == 0) s_red[wave] = x;
+  auto block_min = [&](float x) { return -block_max(-x); };
+  auto block_sum_u64 = [&](uint64_t x) {
+    x = p_wave_sum_u64(x);
+    if (lane == 0) s_red64[wave] = x;
     __syncthreads();
-    float r = s_red[0];
+    uint64_t r = 0;
 #pragma unroll
-    for (int w = 1; w < kProbWaves; ++w) r += s_red[w];
+    for (int w = 0; w < kProbWaves; ++w) r += s_red64[w];
     __syncthreads();
     return r;
   };
@@ -123,6 +152,27 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
   float tmax = -INFINITY;
   visit_row([&](float z, int) { tmax = fmaxf(tmax, z); });
   const float m = block_max(tmax);
+  // 2^t of every entry, kept in registers with the row
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < kProbRegQuads; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) re[u][e] = exp2_taylor((rq[u][e] - m) * c);
+  }
+  auto visit_ze = [&](auto visit) {
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < kProbRegQuads; ++u) {
+        const int x = tid + u * kProbThreads;
+        if (x < n4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) visit(rq[u][e], re[u][e], 4 * x + e);
+        }
+      }
+    } else {
+      visit_row([&](float z, int i) { visit(z, exp2_taylor((z - m) * c), i); });
+    }
+  };
 
   // ---- top-k: the k-th entry (kv, ki); every entry is kept without top-k
   float kv = -INFINITY;
@@ -215,41 +265,206 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
       kv = pv;
       ki = pi;
     }
+    __syncthreads();  // s_wv / s_cnt are reused below
   }
-  auto kept = [&](float z, int i) { return z > kv || (z == kv && i <= ki); };
+  auto kept_k = [&](float z, int i) { return z > kv || (z == kv && i <= ki); };
+  float zthr = kv;
+  int ithr = ki;
 
-  // ---- normaliser and probabilities
-  float part = 0.f;
-  visit_row([&](float z, int i) {
-    if (kept(z, i)) part += __builtin_amdgcn_exp2f((z - m) * c);
+  // ---- top-p: the token where the running mass reaches ceil(P*S/2^24)
+  if (top_p24 > 0u && top_p24 < (1u << 24)) {
+    double part = 0.0;  // at most 8*4 masses below 2^40 each: exact
+    float zmin = INFINITY;
+    visit_ze([&](float z, float e, int i) {
+      if (kept_k(z, i)) {
+        part += mass40(e);
+        zmin = fminf(zmin, z);
+      }
+    });
+    const uint64_t S = block_sum_u64((uint64_t)part);
+    const float lo0 = block_min(zmin);
+    // need = ceil(P * S / 2^24) with S = hi*2^24 + lo split (no overflow)
+    const uint64_t need = (uint64_t)top_p24 * (S >> 24) +
+                          (((uint64_t)top_p24 * (S & 0xffffffull) + 0xffffffull) >> 24);
+    float lo = lo0, hi = m;  // the candidate range of logits (all kept_k tokens in it)
+    uint64_t above = 0;      // the mass of the tokens ranking before the range
+    if (tid == 0) s_done = 0;
+    __syncthreads();
+    for (int it = 0; it < 64; ++it) {
+      if (lo == hi) {
+        // every candidate has the logit lo, hence the same mass mu: the
+        // crossing is the c-th lowest token id among them, c = ceil((need -
+        // above) / mu); binary search on the id
+        const uint64_t mu = (uint64_t)mass40(exp2_taylor((lo - m) * c));
+        const uint64_t cneed = mu > 0 ? (need - above + mu - 1) / mu : 1;
+        int a = 0, b = V - 1;  // the smallest id x with count(id <= x) >= cneed
+        while (a < b) {
+          const int mid = a + (b - a) / 2;
+          double n = 0.0;
+          visit_row([&](float z, int i) { n += (z == lo && kept_k(z, i) && i <= mid) ? 1.0 : 0.0; });
+          const uint64_t cnt = block_sum_u64((uint64_t)n);
+          if (cnt >= cneed) b = mid;
+          else a = mid + 1;
+        }
+        zthr = lo;
+        ithr = a;
+        break;
+      }
+      // histogram of the candidates' masses over 2048 bins, higher logits
+      // first: bins of equal width in logit value (or, for a range too
+      // narrow for that in fp32, in the logits' order keys); any monotone
+      // map keeps each bin a range of logits
+      const float scv = (float)kPBins / (hi - lo);
+      const bool linear = (hi - lo) >= 1e-30f && scv <= 3.0e38f;
+      const uint32_t khi = p_order_key(hi);
+      const float sck = (float)kPBins / ((float)(khi - p_order_key(lo)) + 1.0f);
+      auto bin_of = [&](float z) {
+        const float x = linear ? (hi - z) * scv : (float)(khi - p_order_key(z)) * sck;
+        return min(kPBins - 1, (int)x);
+      };
+      for (int b = tid; b < kPBins; b += kProbThreads) s_hist[b] = 0ull;
+      __syncthreads();
+      visit_ze([&](float z, float e, int i) {
+        if (z >= lo && z <= hi && kept_k(z, i))
+          atomicAdd(reinterpret_cast<unsigned long long*>(&s_hist[bin_of(z)]),
+                    (unsigned long long)mass40(e));
+      });
+      __syncthreads();
+      if (wave == 0) {  // lane l scans bins 32l .. 32l+31
+        uint64_t loc = 0;
+        for (int k = 0; k < kPBins / 64; ++k) loc += s_hist[lane * (kPBins / 64) + k];
+        uint64_t incl = loc;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const uint64_t o = ((uint64_t)(uint32_t)__shfl_up((int)(incl >> 32), d) << 32) |
+                             (uint32_t)__shfl_up((int)(uint32_t)incl, d);
+          if (lane >= d) incl += o;
+        }
+        const uint64_t excl = incl - loc;
+        const uint64_t first = __ballot(above + incl >= need);
+        const int L = first ? __ffsll((unsigned long long)first) - 1 : 63;
+        if (lane == L) {
+          uint64_t run = above + excl;
+          int b = lane * (kPBins / 64);
+          for (int k = 0; k < kPBins / 64; ++k) {
+            const uint64_t h = s_hist[lane * (kPBins / 64) + k];
+            if (run + h >= need || k == kPBins / 64 - 1) {
+              b = lane * (kPBins / 64) + k;
+              break;
+            }
+            run += h;
+          }
+          s_bin = b;
+          s_above = run;
+        }
+      }
+      __syncthreads();
+      const int bsel = s_bin;
+      above = s_above;
+      // the crossing bin's tokens: count and logit range
+      double n = 0.0;
+      float bmin = INFINITY, bmax = -INFINITY;
+      visit_row([&](float z, int i) {
+        if (z >= lo && z <= hi && kept_k(z, i) && bin_of(z) == bsel) {
+          n += 1.0;
+          bmin = fminf(bmin, z);
+          bmax = fmaxf(bmax, z);
+        }
+      });
+      const uint64_t cnt = block_sum_u64((uint64_t)n);
+      const float nlo = block_min(bmin), nhi = block_max(bmax);
+      if (cnt <= (uint64_t)kPGather) {
+        // gather them and rank them in LDS: the crossing token is the one
+        // whose running mass (above + the tokens ranking before it, itself
+        // included) first reaches need
+        if (tid == 0) s_cnt = 0;
+        __syncthreads();
+        visit_ze([&](float z, float e, int i) {
+          if (z >= lo && z <= hi && kept_k(z, i) && bin_of(z) == bsel) {
+            const int slot = atomicAdd(&s_cnt, 1);
+            s_cv[slot] = z;
+            s_ci[slot] = i;
+            s_hist[slot] = (uint64_t)mass40(e);
+          }
+        });
+        __syncthreads();
+        const int nc = s_cnt;
+        for (int q = tid; q < nc; q += kProbThreads) {
+          const float z = s_cv[q];
+          const int i = s_ci[q];
+          uint64_t before = 0;
+          for (int u = 0; u < nc; ++u)
+            if (p_ranks_before(s_cv[u], s_ci[u], z, i)) before += s_hist[u];
+          if (above + before < need && above + before + s_hist[q] >= need) {
+            s_zt = z;
+            s_it = i;
+          }
+        }
+        __syncthreads();
+        zthr = s_zt;
+        ithr = s_it;
+        break;
+      }
+      lo = nlo;  // the next range: the crossing bin (its members are exactly
+      hi = nhi;  // the kept tokens with logits in [nlo, nhi])
+    }
+  }
+
+  // ---- normaliser and probabilities (or the row's statistics)
+  auto kept = [&](float z, int i) { return z > zthr || (z == zthr && i <= ithr); };
+  double part = 0.0;
+  visit_ze([&](float z, float e, int i) {
+    if (kept(z, i)) part += mass40(e);
   });
-  const float inv = 1.f / block_sum(part);
-  auto prob = [&](float z, int i) { return kept(z, i) ? __builtin_amdgcn_exp2f((z - m) * c) * inv : 0.f; };
+  const uint64_t S = block_sum_u64((uint64_t)part);
+  const float inv = (float)(1099511627776.0 / (double)S);
+  if (stats) {
+    if (tid == 0) stats[blockIdx.x] = RowStats{m, inv, zthr, ithr};
+    return;
+  }
+  float* out = probs + (size_t)blockIdx.x * V;
+  f32x4* o4 = reinterpret_cast<f32x4*>(out);
   if (in_regs) {
 #pragma unroll
     for (int u = 0; u < kProbRegQuads; ++u) {
       const int x = tid + u * kProbThreads;
-      if (x < n4)
-        o4[x] = f32x4{prob(rq[u][0], 4 * x), prob(rq[u][1], 4 * x + 1), prob(rq[u][2], 4 * x + 2),
-                      prob(rq[u][3], 4 * x + 3)};
-    }
-  } else if (VEC) {
-    for (int x = tid; x < n4; x += kProbThreads) {
-      const f32x4 q = r4[x];
-      o4[x] = f32x4{prob(q[0], 4 * x), prob(q[1], 4 * x + 1), prob(q[2], 4 * x + 2), prob(q[3], 4 * x + 3)};
+      if (x < n4) {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = kept(rq[u][e], 4 * x + e) ? re[u][e] * inv : 0.f;
+        o4[x] = o;
+      }
     }
   } else {
-    for (int v = tid; v < V; v += kProbThreads) out[v] = prob(row[v], v);
+    const RowStats rs{m, inv, zthr, ithr};
+    if (VEC) {
+      for (int x = tid; x < n4; x += kProbThreads) {
+        const f32x4 q = r4[x];
+        o4[x] = f32x4{row_prob(rs, c, q[0], 4 * x), row_prob(rs, c, q[1], 4 * x + 1),
+                      row_prob(rs, c, q[2], 4 * x + 2), row_prob(rs, c, q[3], 4 * x + 3)};
+      }
+    } else {
+      for (int v = tid; v < V; v += kProbThreads) out[v] = row_prob(rs, c, row[v], v);
+    }
   }
 }
 
-hipError_t launch_probs(int R, int V, float T, int topk, const float* logits, float* probs,
-                        bool vec, hipStream_t s) {
-  const float c = 1.4426950408889634f / T;  // log2(e) / T
+float probs_scale(float T) { return (float)(kLog2Ed / (double)T); }
+
+uint32_t probs_top_p24(float top_p) {
+  return top_p > 0.f && top_p < 1.f ? (uint32_t)(top_p * 16777216.0f) : 0u;
+}
+
+hipError_t launch_probs(int R, int V, float T, int topk, float top_p, const float* logits,
+                        float* probs, RowStats* stats, bool vec, hipStream_t s) {
+  const float c = probs_scale(T);
+  const uint32_t p24 = probs_top_p24(top_p);
   if (vec)
-    hipLaunchKernelGGL(probs_kernel<true>, dim3(R), dim3(kProbThreads), 0, s, V, c, topk, logits, probs);
+    hipLaunchKernelGGL(probs_kernel<true>, dim3(R), dim3(kProbThreads), 0, s, V, c, topk, p24,
+                       logits, probs, stats);
   else
-    hipLaunchKernelGGL(probs_kernel<false>, dim3(R), dim3(kProbThreads), 0, s, V, c, topk, logits, probs);
+    hipLaunchKernelGGL(probs_kernel<false>, dim3(R), dim3(kProbThreads), 0, s, V, c, topk, p24,
+                       logits, probs, stats);
   return hipGetLastError();
 }
 

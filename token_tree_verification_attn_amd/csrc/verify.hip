@@ -9,6 +9,7 @@
 
 #include "launch.h"
 #include "philox.h"
+#include "softmax_exact.h"
 #include "ttv_common.h"
 
 namespace ttv {
@@ -534,6 +535,7 @@ __device__ __forceinline__ double mss_residual(const float* __restrict__ q, int 
 // the next child's row can be in flight while the current one is used.
 constexpr int kMssPfChunks = 8;
 constexpr int kMssPfMaxVocab = 4 * kMssThreads * kMssPfChunks;
+static_assert(kMssLogitsMaxVocab == kMssPfMaxVocab, "logits rows take the double-buffered walk");
 
 // Buffer loads with one resource per chunk (base = the chunk's first entry,
 // range = the bytes of the row from there): entries past the row read as
@@ -557,19 +559,35 @@ __device__ __forceinline__ void mss_issue_row(const float* __restrict__ row, int
   }
 }
 
-// s_w[widx(v)] = r
-__device__ __forceinline__ void mss_regs_to_lds(const f32x4 (&r)[kMssPfChunks], int V, float* s_w) {
+// Rows given as logits: entry v of the row becomes its probability, computed
+// from the row's statistics exactly as the probabilities kernel does.
+template <bool LG>
+__device__ __forceinline__ f32x4 mss_entry4(f32x4 x, int v, const RowStats& st, float c) {
+  if constexpr (LG) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = row_prob(st, c, x[e], v + e);
+  }
+  return x;
+}
+
+// s_w[widx(v)] = r (probabilities, or logits made probabilities with `st`)
+template <bool LG>
+__device__ __forceinline__ void mss_regs_to_lds(const f32x4 (&r)[kMssPfChunks], int V, float* s_w,
+                                                const RowStats& st, float c) {
   const int t = threadIdx.x;
   f32x4* wp = reinterpret_cast<f32x4*>(s_w + 4 * t + 4 * (t >> 5));
 #pragma unroll
-  for (int j = 0; j < kMssPfChunks; ++j)
-    if (4 * (t + kMssThreads * j) < V) wp[(kMssChunkStride / 4) * j] = r[j];
+  for (int j = 0; j < kMssPfChunks; ++j) {
+    const int v = 4 * (t + kMssThreads * j);
+    if (v < V) wp[(kMssChunkStride / 4) * j] = mss_entry4<LG>(r[j], v, st, c);
+  }
 }
 
 // w = max(w - s*q, +0) in place with q in registers; returns this thread's
 // sum of fx40(w) (as an integer-valued double)
+template <bool LG>
 __device__ __forceinline__ double mss_residual_regs(const f32x4 (&r)[kMssPfChunks], int V, float s,
-                                                    float* s_w) {
+                                                    float* s_w, const RowStats& st, float c) {
   const int t = threadIdx.x;
   double part = 0.0;
   f32x4* wp = reinterpret_cast<f32x4*>(s_w + 4 * t + 4 * (t >> 5));
@@ -577,9 +595,10 @@ __device__ __forceinline__ double mss_residual_regs(const f32x4 (&r)[kMssPfChunk
   for (int j = 0; j < kMssPfChunks; ++j)
     if (4 * (t + kMssThreads * j) < V) {
       f32x4 w = wp[(kMssChunkStride / 4) * j];
+      const f32x4 q = mss_entry4<LG>(r[j], 4 * (t + kMssThreads * j), st, c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float d = fmaf(-s, r[j][e], w[e]);
+        const float d = fmaf(-s, q[e], w[e]);
         w[e] = d > 0.0f ? d : 0.0f;
         part += fx40d(w[e]);
       }
@@ -588,11 +607,13 @@ __device__ __forceinline__ double mss_residual_regs(const f32x4 (&r)[kMssPfChunk
   return part;
 }
 
-template <bool VEC, bool PF>
+// LG: llm and ssm hold logits; st_llm / st_ssm [B*N] their rows' statistics
+// (ttv_tree_verify_logits), c = (float)(log2(e) / T).
+template <bool VEC, bool PF, bool LG>
 __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     int N, int V, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ n_nodes, const float* __restrict__ llm,
-    const float* __restrict__ ssm, MssDraws dr,
+    const float* __restrict__ ssm, MssDraws dr, LogitRows lr,
     int32_t* __restrict__ path, int32_t* __restrict__ path_len,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status, CommitArgs cm) {
   extern __shared__ __attribute__((aligned(16))) float s_w[];  // residual w, widx() layout
@@ -610,6 +631,10 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   const size_t rowN = (size_t)b * N;
   // uniforms: drawn here from Philox (seed, step), or given by the caller
   const bool seeded = dr.u_accept == nullptr;
+  // statistics of row u of llm / row c of ssm when they hold logits (read
+  // when a row is turned into probabilities; wave-uniform scalar loads)
+  auto p_stats = [&](int u) { return LG ? lr.st_llm[rowN + u] : RowStats{}; };
+  auto q_stats = [&](int c) { return LG ? lr.st_ssm[rowN + c] : RowStats{}; };
   // with the commit: thread 0 alone reads the prefix length (the others take
   // it from LDS); its write of the new one, which may alias it, depends on
   // that read, and only this workgroup touches entry b
@@ -673,6 +698,10 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     atomicOr(&s_kids[p][t >> 6], 1ull << (t & 63));
     qx = ssm[(rowN + t) * V + x];
     px = llm[(rowN + p) * V + x];
+    if constexpr (LG) {
+      qx = row_prob(lr.st_ssm[rowN + t], lr.c, qx, x);
+      px = row_prob(lr.st_llm[rowN + p], lr.c, px, x);
+    }
     if (!seeded) ua = dr.u_accept[rowN + t];
   }
   static_assert(kMssThreads >= 128 + kMaxNodes, "waves 2-3 compute the final draws");
@@ -722,7 +751,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
         f32x4 ra[kMssPfChunks];
         mss_issue_row(llm + (rowN + u) * V, V, ra);
         __syncthreads();
-        mss_regs_to_lds(ra, V, s_w);
+        mss_regs_to_lds<LG>(ra, V, s_w, p_stats(u), lr.c);
         __syncthreads();
       } else {
         load_p_row(u);
@@ -747,7 +776,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       if (k0) k0 &= k0 - 1;
       else k1 &= k1 - 1;
       __syncthreads();  // every thread has read the old residual
-      mss_regs_to_lds(ra, V, s_w);
+      mss_regs_to_lds<LG>(ra, V, s_w, p_stats(u), lr.c);
       __syncthreads();
       float s = 1.0f;
       int next = -1, ccur = c0;
@@ -765,14 +794,15 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
           k1 &= k1 - 1;
         }
         mss_issue_row(ssm + (rowN + (cn >= 0 ? cn : ccur)) * V, V, nxt);
+        const int crow = ccur;  // the child whose q row is in cur
         ccur = cn;
-        const double part = mss_residual_regs(cur, V, s, s_w);
+        const double part = mss_residual_regs<LG>(cur, V, s, s_w, q_stats(crow), lr.c);
         const double S = block_sum_f64(part, s_redd);  // its barriers publish s_w
         s = (float)(S * 0x1p-40);
         if (s == 0.0f) {  // empty residual: stop testing, sample from p_u
           mss_issue_row(llm + (rowN + u) * V, V, cur);  // cur is consumed
           __syncthreads();
-          mss_regs_to_lds(cur, V, s_w);
+          mss_regs_to_lds<LG>(cur, V, s_w, p_stats(u), lr.c);
           __syncthreads();
           return true;
         }
@@ -945,19 +975,22 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
 
 hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                              const int32_t* tokens, const int32_t* n_nodes, const float* llm,
-                             const float* ssm, const MssDraws& dr, int32_t* path, int32_t* path_len,
-                             int32_t* out_tokens, int32_t* dev_status, const CommitArgs& cm,
-                             hipStream_t s) {
+                             const float* ssm, const MssDraws& dr, const LogitRows& lr,
+                             int32_t* path, int32_t* path_len, int32_t* out_tokens,
+                             int32_t* dev_status, const CommitArgs& cm, hipStream_t s) {
   const size_t lds = (size_t)(V + 4 * (V >> 7) + 4) * sizeof(float);  // widx(V - 1) + 1, 16-byte padded
   const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(llm) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(ssm) & 15) == 0;
-  auto kern = !vec ? mss_kernel<false, false>
-                   : (V <= kMssPfMaxVocab ? mss_kernel<true, true> : mss_kernel<true, false>);
+  const bool lg = lr.st_llm != nullptr;
+  auto kern = lg ? mss_kernel<true, true, true>
+                 : (!vec ? mss_kernel<false, false, false>
+                         : (V <= kMssPfMaxVocab ? mss_kernel<true, true, false>
+                                                : mss_kernel<true, false, false>));
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(B), dim3(kMssThreads), lds, s, N, V, parents, tokens, n_nodes, llm,
-                     ssm, dr, path, path_len, out_tokens, dev_status, cm);
+                     ssm, dr, lr, path, path_len, out_tokens, dev_status, cm);
   return hipGetLastError();
 }
 
