@@ -29,9 +29,10 @@
  *  - Node 0 of every tree is its root; a tree is valid iff parents[0] == -1 and
  *    0 <= parents[i] < i for i >= 1 (any topological numbering; depth-first is
  *    one valid numbering but is not assumed).
- *  - The library holds no global state (except the static scratch of
- *    ttv_tree_attn_noalloc); calls on different streams are independent as
- *    long as their output buffers do not overlap.
+ *  - The library holds no global state besides the static scratch of
+ *    ttv_tree_attn_noalloc and a record of the kernel attributes it has set
+ *    per device; calls on different streams are independent as long as
+ *    their output buffers do not overlap.
  */
 #ifndef TTV_H
 #define TTV_H

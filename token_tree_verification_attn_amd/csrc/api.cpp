@@ -6,6 +6,9 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "launch.h"
 #include "softmax_exact.h"
@@ -110,6 +113,20 @@ ttv_status launch_status(hipError_t e) { return e == hipSuccess ? TTV_OK : TTV_E
 }  // namespace
 
 namespace ttv {
+
+hipError_t lds_limit_once(const void* kern, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> done;  // (kernel, device) pairs already set
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& d : done)
+    if (d.first == kern && d.second == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.emplace_back(kern, dev);
+  return e;
+}
 
 ttv_status attn_prepare(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, float scale,
                         const void* q, const void* k_cache, const void* v_cache, int Lcap,

@@ -737,8 +737,7 @@ static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
   const long items = a.balanced ? (long)a.items : (long)a.B * a.Hkv * nrb * a.chunks;
   const long blocks = (items + kXcds - 1) / kXcds * kXcds;
   auto kern = attn_mfma2_kernel<D, QW, NW, NST>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  hipError_t e = lds_limit_once(reinterpret_cast<const void*>(kern), C::LDS_BYTES);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::kThreads), C::LDS_BYTES, s, a, (int)items);
   return hipGetLastError();

@@ -188,8 +188,9 @@ hipError_t launch_kv_commit_inplace(int elt, int B, int N, int Hkv, int D, int L
   const bool per_head = cache_len_out != cache_len_in && Hkv > 1 && Hkv <= 65535;
   const size_t lds = (size_t)2 * N * D * elt;  // K and V rows of one head: at most 128 KB
   const dim3 grid(B, per_head ? Hkv : 1);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kv_commit_inplace_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // the most any launch takes: 128 rows of 128 fp32 values, K and V
+  hipError_t e = lds_limit_once(reinterpret_cast<const void*>(kv_commit_inplace_kernel),
+                                2 * TTV_MAX_NODES * 128 * 4);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kv_commit_inplace_kernel, grid, dim3(kCommitHeadThreads), lds, s, D * elt, N,
                      Hkv, Lcap, Lmax, static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache),

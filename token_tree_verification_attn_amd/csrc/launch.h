@@ -9,6 +9,10 @@
 
 namespace ttv {
 
+// Raises kernel `kern`'s dynamic-LDS limit to `bytes` (the most any launch of
+// it requests) once per device and kernel, instead of on every launch.
+hipError_t lds_limit_once(const void* kern, int bytes);
+
 // ------------------------------------------------------------- attention --
 // Launch plan of ttv_tree_attn, a pure function of the call's sizes (the
 // size query and the call compute the same plan).

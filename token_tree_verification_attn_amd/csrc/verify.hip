@@ -986,8 +986,8 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                  : (!vec ? mss_kernel<false, false, false>
                          : (V <= kMssPfMaxVocab ? mss_kernel<true, true, false>
                                                 : mss_kernel<true, false, false>));
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  constexpr int kMaxLds = (kMssMaxVocab + 4 * (kMssMaxVocab >> 7) + 4) * (int)sizeof(float);
+  hipError_t e = lds_limit_once(reinterpret_cast<const void*>(kern), kMaxLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(B), dim3(kMssThreads), lds, s, N, V, parents, tokens, n_nodes, llm,
                      ssm, dr, lr, path, path_len, out_tokens, dev_status, cm);
