@@ -81,7 +81,10 @@ def counter_kib(files, counter, match):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--steps", type=int, default=20)
+    # bench.py's own defaults, so that the traced average covers the same
+    # number of launches as the live measurement it is compared with
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copy-ref", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.copy_ref:
@@ -94,7 +97,7 @@ def main():
     dest = os.path.join(out, "summary")
     os.makedirs(dest, exist_ok=True)
     bench_cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", w, "--steps",
-                 str(args.steps), "--warmup", "3", "--cpu-budget", "0"]
+                 str(args.steps), "--warmup", str(args.warmup), "--cpu-budget", "0"]
 
     # 1. kernel durations
     files, cmd_trace = rocprof(os.path.join(out, "trace"), ["--kernel-trace", "--stats"],
