@@ -1,10 +1,13 @@
 """Throughput of token-tree construction on one GPU: one level of
 expansion-based construction (ttv_tree_expand, the default), or merge-based
-construction (ttv_tree_merge, --op merge).
+construction (ttv_tree_merge, --op merge), probabilities from logits
+(ttv_probs_from_logits, --op probs), or stochastic verification fed with
+logits (ttv_tree_verify_logits, --op verify_logits).
 
     python bench_expand.py [--steps K] [--warmup W] [--B 16] [--F 16] [--V 32000] [--k 4]
     python bench_expand.py --op merge [--B 4] [--S 4] [--Ls 16]
     python bench_expand.py --op probs [--B 16] [--F 64] [--V 32000] [--k 0] [--T 0.8] [--top-p 1]
+    python bench_expand.py --op verify_logits [--k 0] [--T 0.8] [--top-p 1]
 
 Workload: B requests, each expanding F frontier nodes by the k most probable
 tokens of their speculator rows of V fp32 probabilities (softmax of N(0,2)
@@ -111,7 +114,7 @@ def bench_merge(args):
         "ms_per_step_mean": ms_mean, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": "merge", "B": B, "S": S, "Ls": Ls,
-                   "nodes": n_out.cpu().tolist(), "launch": "hip graph replay"},
+                   "nodes": n_out.cpu().tolist(), "launch": launch},
         "roofline": None}), flush=True)
 
 
@@ -157,9 +160,94 @@ def bench_probs(args):
           flush=True)
 
 
+def bench_verify_logits(args):
+    """Multi-step speculative sampling from raw logits on the stochastic
+    workload's trees (16 requests x 64 nodes, V = 32000; LLM and speculator
+    logits N(0,2), temperature T; each node's token drawn from its
+    speculator distribution): ttv_tree_verify_logits (one statistics pass
+    per tensor, then the walk) against the unfused route, probabilities of
+    both tensors written by ttv_probs_from_logits and then ttv_tree_verify.
+    Both routes give the same paths (checked)."""
+    import synth
+    spec = synth.WORKLOADS["c5"]
+    B, N, V = spec.B, spec.N, spec.V
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tree = synth.make(spec, with_kv=False, with_verify=False)
+    rng = np.random.default_rng(np.random.SeedSequence([spec.seed, 14]))
+    z_llm = rng.normal(0.0, 2.0, (B, N, V)).astype(np.float32)
+    z_ssm = rng.normal(0.0, 2.0, (B, N, V)).astype(np.float32)
+    q = np.exp((z_ssm - z_ssm.max(-1, keepdims=True)).astype(np.float64) / args.T)
+    cdf = np.cumsum(q, -1)
+    u = rng.random((B, N, 1)) * cdf[..., -1:]
+    tokens = np.minimum((cdf < u).sum(-1), V - 1).astype(np.int32)
+    tokens[:, 0] = 0
+    parents = torch.from_numpy(tree["parents"]).to(dev)
+    tok = torch.from_numpy(tokens).to(dev)
+    per_copy = 2 * z_llm.nbytes
+    ncopies = max(1, min(64, -(-2 * bench.MALL_BYTES // per_copy)))
+    zl = [torch.from_numpy(z_llm).to(dev)]
+    zs = [torch.from_numpy(z_ssm).to(dev)]
+    for _ in range(ncopies - 1):
+        zl.append(zl[0].clone())
+        zs.append(zs[0].clone())
+    pl = [torch.empty_like(zl[0]) for _ in range(ncopies)]
+    ps = [torch.empty_like(zs[0]) for _ in range(ncopies)]
+    outs = [ttv._verify_outputs(B, N, dev, None, None, None, None) for _ in range(2)]
+    ws = torch.empty(ttv.lib().ttv_tree_verify_logits_workspace_size(B, N), dtype=torch.uint8,
+                     device=dev)
+    nv = ttv.tree_verify_workspace_size(ttv.STOCHASTIC, B, N, V)
+    wsv = torch.empty(nv, dtype=torch.uint8, device=dev) if nv else None
+    seed = spec.seed
+
+    def fused(i):
+        c = i % ncopies
+        path, plen, otok, st = outs[0]
+        ttv.tree_verify_logits(parents, tok, zl[c], zs[c], args.T, args.k, args.top_p, seed, 0,
+                               path=path, path_len=plen, out_tokens=otok, dev_status=st,
+                               workspace=ws)
+
+    def two_pass(i):
+        c = i % ncopies
+        ttv.probs_from_logits(zl[c], args.T, args.k, out=pl[c], top_p=args.top_p)
+        ttv.probs_from_logits(zs[c], args.T, args.k, out=ps[c], top_p=args.top_p)
+        path, plen, otok, st = outs[1]
+        ttv.tree_verify(ttv.STOCHASTIC, parents, tok, pl[c], ps[c], seed, 0, path=path,
+                        path_len=plen, out_tokens=otok, dev_status=st, workspace=wsv)
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        fused(i)
+        two_pass(i)
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b), "the fused and the two-pass routes disagree"
+    assert int(outs[0][3].abs().sum()) == 0
+    ms_f, mean_f, launch = time_calls(fused, ncopies, args.steps, dev, stream)
+    ms_t, mean_t, _ = time_calls(two_pass, ncopies, args.steps, dev, stream)
+    nbytes = 2 * B * N * V * 4  # both logit tensors read once
+    gbs = nbytes / (mean_f * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "tree_verify_logits trees/s", "value": B / (ms_f * 1e-3), "unit": "trees/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_f,
+        "ms_per_step_mean": mean_f, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "verify_logits", "B": B, "N": N, "V": V, "T": args.T,
+                   "topk": args.k, "top_p": args.top_p, "input_copies": ncopies,
+                   "launch": launch, "inputs": "rotated, HBM-resident",
+                   "path_len_mean": float(outs[0][1].float().mean())},
+        "two_pass_ms_per_step": ms_t, "two_pass_ms_per_step_mean": mean_t,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "ttv_tree_verify_logits (statistics passes + walk)",
+                     "per_launch_algorithmic": nbytes, "avg_launch_us": mean_f * 1e3}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--op", choices=["expand", "merge", "probs"], default="expand")
+    ap.add_argument("--op", choices=["expand", "merge", "probs", "verify_logits"],
+                    default="expand")
     ap.add_argument("--T", type=float, default=0.8)
     ap.add_argument("--S", type=int, default=4)
     ap.add_argument("--Ls", type=int, default=16)
@@ -179,6 +267,10 @@ def main():
         return bench_merge(args)
     if args.op == "probs":
         return bench_probs(args)
+    if args.op == "verify_logits":
+        if args.k == 4 and "--k" not in sys.argv:
+            args.k = 0
+        return bench_verify_logits(args)
     B, F, V, k = args.B, args.F, args.V, args.k
     assert F + F * k <= 128, "the expanded tree must fit 128 nodes"
     dev = torch.device("cuda:0")

@@ -9,7 +9,9 @@
 //   S^T[key][query] = K Q^T     v_mfma_f32_16x16x32_bf16, A = K (LDS,
 //                               ds_read_b128), B = the wave's queries (VGPRs)
 //   online softmax on S^T       a query's KT scores sit in 4 lanes x KT/16
-//                               registers; its max needs two lane swaps
+//                               registers; p = 2^(s*c - m) against the running
+//                               max m, whose update (two lane swaps) is only
+//                               needed when a tile would overflow a bound
 //   O^T[d][query] += V^T P^T    A = V^T read from the row-major V tile with
 //                               ds_read_b64_tr_b16, B = P^T straight from the
 //                               S^T registers (bf16 by v_cvt_pk_bf16_f32)
@@ -443,8 +445,12 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
     anc_lo[qt] = 0ull;
     anc_hi[qt] = 0ull;
   }
+  // m_run: the running max in log2 units (-inf until the query has seen a
+  // key); m_set: every query of the wave has one (wave-uniform), which
+  // enables the fast softmax.
   f32x4 oacc[C::QT][C::DT];
   float m_run[C::QT], l_run[C::QT];
+  bool m_set = false;
 #pragma unroll
   for (int qt = 0; qt < C::QT; ++qt) {
     m_run[qt] = -INFINITY;
@@ -481,13 +487,17 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
   // Masking: bit k of tmask[qt] says whether key key0 + k is visible to this
   // lane's query (the valid-key prefix for a tail tile, the ancestor bits for
   // an in-tree tile); full prefix tiles skip it.
-  // Softmax: scores stay raw until the exponent, exp2(s*c - m) with
-  // c = scale*log2(e) > 0, so masked scores are -inf and the max is taken on
-  // raw scores.  The running max m only moves when a tile's max exceeds it by
-  // more than kLazy (log2 units); the probabilities are then at most 2^kLazy,
-  // which is exact after the final normalisation and far from fp32 overflow,
-  // and the rescale of O is skipped when no query of the wave needs it.
+  // Softmax: scores stay raw until the exponent, p = 2^(s*c - m) with
+  // c = scale*log2(e) > 0, so masked scores are -inf.  Fast path (every query
+  // of the wave has a running max m): p against the current m without
+  // looking for the tile's max; the tile stands if every lane's sum of its p
+  // is at most kBound (so no p exceeds it: far from fp32 and bf16 overflow,
+  // and exact after the final normalisation).  Otherwise -- the first keys a
+  // query sees, or a tile that overshoots -- the slow path takes the tile's
+  // max and moves m when it exceeds m by more than kLazy (log2 units),
+  // rescaling O; the moved queries' largest p is then 1.
   constexpr float kLazy = 8.0f;
+  constexpr float kBound = 65536.0f;  // 2^16
   const float cs = a.scale_log2;
   using KFrag = u32x4[C::KB][C::KS];
   using SAcc = f32x4[C::KB][C::QT];
@@ -540,21 +550,18 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
       vhi[k2][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TTV_LDS i16x4*)(uintptr_t)(pa + 16 * (D * 2)));
     }
   };
-  // online softmax of tile `tile` in place of its scores; lane holds keys
-  // kb*16 + g16*4 + e of query c16.  Returns whether any query of the lane
-  // moved its running max (O must then be rescaled by alpha).
-  auto softmax = [&](int tile, SAcc& s, PFrag& pB, float (&alpha)[C::QT]) -> bool {
+  // Softmax of tile `tile`, in place of its scores; lane holds keys
+  // kb*16 + g16*4 + e of query c16.
+  auto mask_tile = [&](int tile, SAcc& s) {
     const bool tree = sc.tree(tile);
     const int key0 = sc.key0(tile);
     const int nvalid = tree ? min(KT, nU - key0) : min(KT, sc.k_end - key0);
-    const bool masked = tree || nvalid < KT;
-    bool any_rescale = false;
+    if (tree || nvalid < KT) {
+      // the empty asm keeps this a branch taken only by tree and tail tiles
+      // (if-converted, its selects would run on every tile)
+      asm volatile("");
 #pragma unroll
-    for (int qt = 0; qt < C::QT; ++qt) {
-      if (masked) {
-        // the empty asm keeps this a branch taken only by tree and tail tiles
-        // (if-converted, its selects would run on every tile)
-        asm volatile("");
+      for (int qt = 0; qt < C::QT; ++qt) {
         const uint64_t w = key0 < 64 ? anc_lo[qt] : anc_hi[qt];
         const uint64_t vmask = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1ull);
         const uint64_t tm = ((tree ? w : ~0ull) & vmask) >> (g16 * 4);  // lane keys: kb*16 + g16*4 + e
@@ -564,6 +571,54 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
           for (int e = 0; e < 4; ++e)
             if (!((tm >> (kb * 16 + e)) & 1ull)) s[kb][qt][e] = -INFINITY;
       }
+    }
+  };
+  auto pack_p = [&](const SAcc& s, PFrag& pB) {
+    // P^T operands: slots 0-3 = keys 32*k2 + g16*4 + e, 4-7 = +16
+#pragma unroll
+    for (int qt = 0; qt < C::QT; ++qt)
+#pragma unroll
+      for (int k2 = 0; k2 < C::PK; ++k2) {
+        const u32x4 pk = {pack2(s[2 * k2][qt][0], s[2 * k2][qt][1]),
+                          pack2(s[2 * k2][qt][2], s[2 * k2][qt][3]),
+                          pack2(s[2 * k2 + 1][qt][0], s[2 * k2 + 1][qt][1]),
+                          pack2(s[2 * k2 + 1][qt][2], s[2 * k2 + 1][qt][3])};
+        pB[qt][k2] = __builtin_bit_cast(bf16x8, pk);
+      }
+  };
+  // Fast path: p against the current max; false (and the scores lost) when
+  // some lane's sum of its p exceeds the bound, after which the caller forms
+  // the scores again.
+  auto softmax_fast = [&](SAcc& s, PFrag& pB) -> bool {
+    float psum[C::QT];
+    bool over = false;
+#pragma unroll
+    for (int qt = 0; qt < C::QT; ++qt) {
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qt][e], cs, -m_run[qt]));
+          s[kb][qt][e] = p;
+          ps += p;
+        }
+      psum[qt] = ps;
+      over |= !(ps <= kBound);
+    }
+    if (__builtin_amdgcn_ballot_w64(over) != 0ull) return false;
+#pragma unroll
+    for (int qt = 0; qt < C::QT; ++qt) l_run[qt] += psum[qt];
+    pack_p(s, pB);
+    return true;
+  };
+  // Slow path: the tile's max; m moves when it exceeds m by more than kLazy.
+  // Returns whether any query of the lane moved (O must then be rescaled by
+  // alpha).
+  auto softmax_slow = [&](SAcc& s, PFrag& pB, float (&alpha)[C::QT]) -> bool {
+    bool any_rescale = false, unset = false;
+#pragma unroll
+    for (int qt = 0; qt < C::QT; ++qt) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
@@ -576,29 +631,23 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
       alpha[qt] = move ? __builtin_amdgcn_exp2f(m_run[qt] - m_new) : 1.f;
       any_rescale |= move;
       m_run[qt] = m_new;
+      unset |= m_new == -INFINITY;
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      float psum = 0.f;
+      float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qt][e], cs, -m_use));
           s[kb][qt][e] = p;
-          psum += p;
+          ps += p;
         }
       // fp32 row sum of the unrounded probabilities (an MFMA sum of the
       // bf16-rounded P would save these adds but costs the lse ~2^-9)
-      l_run[qt] = l_run[qt] * alpha[qt] + psum;
-      // P^T operands: slots 0-3 = keys 32*k2 + g16*4 + e, 4-7 = +16
-#pragma unroll
-      for (int k2 = 0; k2 < C::PK; ++k2) {
-        const u32x4 pk = {pack2(s[2 * k2][qt][0], s[2 * k2][qt][1]),
-                          pack2(s[2 * k2][qt][2], s[2 * k2][qt][3]),
-                          pack2(s[2 * k2 + 1][qt][0], s[2 * k2 + 1][qt][1]),
-                          pack2(s[2 * k2 + 1][qt][2], s[2 * k2 + 1][qt][3])};
-        pB[qt][k2] = __builtin_bit_cast(bf16x8, pk);
-      }
+      l_run[qt] = l_run[qt] * alpha[qt] + ps;
     }
+    pack_p(s, pB);
+    m_set = __builtin_amdgcn_ballot_w64(unset) == 0ull;
     return any_rescale;
   };
   auto rescale = [&](const float (&alpha)[C::QT], bool any) {
@@ -653,8 +702,15 @@ __global__ __launch_bounds__(64 * NW, (MfmaCfg<D, QW, NW, NST>::MIN_BLOCKS)) voi
 #pragma unroll
       for (int k2 = 0; k2 < C::PK; ++k2) read_v(stage_tag, k2, vlo, vhi);
     }
-    const bool any = softmax(tile, s, pB, alpha);
-    rescale(alpha, any);
+    mask_tile(tile, s);
+    if (!(m_set && softmax_fast(s, pB))) {
+      if (m_set) {  // the tile overshot: its scores again (the stage is intact until the next barrier)
+        read_k(stage_tag, kf);
+        qk(kf, s);
+        mask_tile(tile, s);
+      }
+      rescale(alpha, softmax_slow(s, pB, alpha));
+    }
     pv(stage_tag, vlo, vhi, pB);
   };
   for (int tile = 0; tile < ntiles; tile += NST) {
