@@ -368,29 +368,22 @@ hipError_t launch_verify_greedy(int B, int N, int V, const int32_t* parents,
 // ====================================================================== //
 constexpr int kMssThreads = 1024;
 
-// floor(x * 2^40) for finite x in [0, 2^24), from the float's fields: a
-// normal x is m * 2^(e-150) with a 24-bit m, so x * 2^40 = m * 2^(e-110).
-__device__ __forceinline__ uint64_t fx40(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const int e = (u >> 23) & 0xff;
-  if (e == 0) return 0ull;  // zero or subnormal: below 2^-126
-  const uint64_t m = (u & 0x7fffffu) | 0x800000u;
-  const int sh = e - 110;
-  if (sh >= 0) return m << sh;
-  if (sh <= -24) return 0ull;
-  return m >> (-sh);
-}
-// LDS index of vocabulary entry v: four pad words after every 128 keep the
-// 16-byte accesses of the row passes aligned and both the 16-byte
-// (v = 4*(t + 1024*j)) and the 4-byte (v = t + 1024*k) walks conflict-free.
+// LDS index of vocabulary entry v: four pad words after every 128 entries
+// (16-byte groups stay aligned, and consecutive lanes reading consecutive
+// 16-byte groups or words stay conflict-free).
 __device__ __forceinline__ int widx(int v) { return v + 4 * (v >> 7); }
 
-// floor(x * 2^40) as a double, for x in [0, 1]: the scaling by 2^40 and the
-// floor are exact in fp32 (a power-of-two scale of a float, no overflow; a
-// result of 2^23 or more is already an integer), the widening is exact, and
-// so is any sum of such terms below 2^53 in any order -- the same integers
-// fx40() gives.
+// floor(x * 2^40) -- the fixed-point mass of a probability -- as a double,
+// for x in [0, 1]: the scaling by 2^40 and the floor are exact in fp32 (a
+// power-of-two scale of a float, no overflow; a result of 2^23 or more is
+// already an integer), the widening is exact, and so is any sum of such
+// terms below 2^53 in any order.
 __device__ __forceinline__ double fx40d(float x) { return (double)floorf(x * 0x1p40f); }
+
+// max(d, +0) for finite d in one integer max of the bits: a positive float
+// is a positive integer, a negative one (or -0) a negative integer, which
+// becomes 0, i.e. +0.
+__device__ __forceinline__ float clamp_pos(float d) { return __int_as_float(max(__float_as_int(d), 0)); }
 
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
@@ -441,13 +434,31 @@ __device__ __forceinline__ double block_excl_scan_f64(double v, double* s_redd, 
   return before + incl - v;
 }
 
-// Row passes.  With 16-byte-aligned rows (VEC) a row moves whole: thread t
-// requests entries v = 4*(t + kMssThreads*j) .. +3, j < kMssRowChunks, all
-// at once (one memory round trip per pass), and their LDS slots are the 16
-// bytes at widx(v) = 4t + 4*(t/32) + 4224*j.  Otherwise entries
-// v = t + kMssThreads*k are streamed, 8 loads in flight per thread.
-constexpr int kMssRowChunks = (kMssMaxVocab + 4 * kMssThreads - 1) / (4 * kMssThreads);
-constexpr int kMssChunkStride = 4 * kMssThreads + 4 * ((4 * kMssThreads) >> 7);  // widx step of j
+// Row passes.  Every wavefront owns a contiguous range of the vocabulary,
+// wave w the entries [w*WS, (w+1)*WS), so the per-wave sums of a pass's
+// block reduction are the masses of those ranges (the final draw uses them).
+// Inside its range a wave's lanes interleave: with 16-byte-aligned rows
+// (VEC) lane l takes the 16-byte chunks at w*WS + 4*(64*k + l), k < CH
+// (WS = 256*CH), so each wave instruction moves 1 KB of consecutive entries;
+// a row moves whole, every chunk requested at once (one memory round trip
+// per pass).  Otherwise lane l takes the words w*WS + 64*k + l (WS = 64*CH),
+// streamed 8 loads at a time.
+constexpr int kMssWaves = kMssThreads / 64;
+constexpr int kMssRowChunks = (kMssMaxVocab + 4 * kMssThreads - 1) / (4 * kMssThreads);  // 16-byte chunks per lane
+constexpr int kMssSpan = 256 * kMssRowChunks;                 // WS of the single-buffered walks
+constexpr int kMssWordChunks = kMssSpan / 64;                 // words per lane, unaligned rows
+static_assert(kMssWaves * kMssSpan >= kMssMaxVocab, "the waves' ranges cover the vocabulary");
+// first entry of lane-chunk k of thread t, 16-byte chunks, wave span 256*CH
+template <int CH>
+__device__ __forceinline__ int mss_chunk_v(int t, int k) {
+  return 256 * CH * (t >> 6) + 4 * (64 * k + (t & 63));
+}
+// its LDS slot: widx(mss_chunk_v) = mss_slot0 + 66*4*k (each 256 entries of
+// a wave's range take 264 LDS words)
+template <int CH>
+__device__ __forceinline__ int mss_slot0(int t) {
+  return 264 * CH * (t >> 6) + 4 * (t & 63) + 4 * ((t & 63) >> 5);
+}
 
 // s_w[widx(v)] = row[v]
 template <bool VEC>
@@ -457,32 +468,33 @@ __device__ __forceinline__ void mss_row_to_lds(const float* __restrict__ row, in
     f32x4 r[kMssRowChunks];
 #pragma unroll
     for (int j = 0; j < kMssRowChunks; ++j) {
-      const int v = 4 * (t + kMssThreads * j);
+      const int v = mss_chunk_v<kMssRowChunks>(t, j);
       r[j] = v < V ? *reinterpret_cast<const f32x4*>(row + v) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    f32x4* wp = reinterpret_cast<f32x4*>(s_w + 4 * t + 4 * (t >> 5));
+    f32x4* wp = reinterpret_cast<f32x4*>(s_w + mss_slot0<kMssRowChunks>(t));
 #pragma unroll
     for (int j = 0; j < kMssRowChunks; ++j)
-      if (4 * (t + kMssThreads * j) < V) wp[(kMssChunkStride / 4) * j] = r[j];
+      if (mss_chunk_v<kMssRowChunks>(t, j) < V) wp[66 * j] = r[j];
   } else {
-    for (int v0 = t; v0 < V; v0 += 8 * kMssThreads) {
+    const int v00 = kMssSpan * (t >> 6) + (t & 63);
+#pragma unroll 1  // rolled: unrolled, every address and bound would be hoisted into registers
+    for (int k0 = 0; k0 < kMssWordChunks; k0 += 8) {
       float x[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int v = v0 + k * kMssThreads;
-        x[k] = v < V ? row[v] : 0.f;
+        const int v = v00 + 64 * (k0 + k);
+        x[k] = k0 + k < kMssWordChunks && v < V ? row[v] : 0.f;
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int v = v0 + k * kMssThreads;
-        if (v < V) s_w[widx(v)] = x[k];
+        const int v = v00 + 64 * (k0 + k);
+        if (k0 + k < kMssWordChunks && v < V) s_w[widx(v)] = x[k];
       }
     }
   }
 }
 
-// w = max(w - s*q, +0) in place; returns this thread's sum of fx40(w) (as
-// an integer-valued double)
+// w = max(w - s*q, +0) in place; returns this thread's sum of fx40d(w)
 template <bool VEC>
 __device__ __forceinline__ double mss_residual(const float* __restrict__ q, int V, float s, float* s_w) {
   const int t = threadIdx.x;
@@ -491,36 +503,38 @@ __device__ __forceinline__ double mss_residual(const float* __restrict__ q, int 
     f32x4 r[kMssRowChunks];
 #pragma unroll
     for (int j = 0; j < kMssRowChunks; ++j) {
-      const int v = 4 * (t + kMssThreads * j);
+      const int v = mss_chunk_v<kMssRowChunks>(t, j);
       r[j] = v < V ? *reinterpret_cast<const f32x4*>(q + v) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    f32x4* wp = reinterpret_cast<f32x4*>(s_w + 4 * t + 4 * (t >> 5));
+    f32x4* wp = reinterpret_cast<f32x4*>(s_w + mss_slot0<kMssRowChunks>(t));
 #pragma unroll
     for (int j = 0; j < kMssRowChunks; ++j)
-      if (4 * (t + kMssThreads * j) < V) {
-        f32x4 w = wp[(kMssChunkStride / 4) * j];
+      if (mss_chunk_v<kMssRowChunks>(t, j) < V) {
+        f32x4 w = wp[66 * j];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float d = fmaf(-s, r[j][e], w[e]);
-          w[e] = d > 0.0f ? d : 0.0f;
+          w[e] = clamp_pos(d);
           part += fx40d(w[e]);
         }
-        wp[(kMssChunkStride / 4) * j] = w;
+        wp[66 * j] = w;
       }
   } else {
-    for (int v0 = t; v0 < V; v0 += 8 * kMssThreads) {
+    const int v00 = kMssSpan * (t >> 6) + (t & 63);
+#pragma unroll 1  // rolled: unrolled, every address and bound would be hoisted into registers
+    for (int k0 = 0; k0 < kMssWordChunks; k0 += 8) {
       float qv[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int v = v0 + k * kMssThreads;
-        qv[k] = v < V ? q[v] : 0.f;
+        const int v = v00 + 64 * (k0 + k);
+        qv[k] = k0 + k < kMssWordChunks && v < V ? q[v] : 0.f;
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int v = v0 + k * kMssThreads;
-        if (v < V) {
+        const int v = v00 + 64 * (k0 + k);
+        if (k0 + k < kMssWordChunks && v < V) {
           const float d = fmaf(-s, qv[k], s_w[widx(v)]);
-          const float w = d > 0.0f ? d : 0.0f;
+          const float w = clamp_pos(d);
           s_w[widx(v)] = w;
           part += fx40d(w);
         }
@@ -533,6 +547,7 @@ __device__ __forceinline__ double mss_residual(const float* __restrict__ q, int 
 // Double-buffered row passes (16-byte rows, V <= 4 * kMssThreads * kMssPfChunks):
 // a row is requested into registers by mss_issue_row and consumed later, so
 // the next child's row can be in flight while the current one is used.
+// Wave span 256 * kMssPfChunks.
 constexpr int kMssPfChunks = 8;
 constexpr int kMssPfMaxVocab = 4 * kMssThreads * kMssPfChunks;
 static_assert(kMssLogitsMaxVocab == kMssPfMaxVocab, "logits rows take the double-buffered walk");
@@ -547,10 +562,11 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access (gfx9 fami
 
 __device__ __forceinline__ void mss_issue_row(const float* __restrict__ row, int V,
                                               f32x4 (&r)[kMssPfChunks]) {
-  const int off = 16 * (int)threadIdx.x;
+  const int off = 16 * (int)(threadIdx.x & 63);
+  const int wbase = 256 * kMssPfChunks * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int j = 0; j < kMssPfChunks; ++j) {
-    const int first = 4 * kMssThreads * j;
+    const int first = wbase + 256 * j;  // the wave's chunk j (uniform)
     const int bytes = V > first ? 4 * (V - first) : 0;
     const float* base = V > first ? row + first : row;
     const __amdgpu_buffer_rsrc_t rs =
@@ -570,39 +586,47 @@ __device__ __forceinline__ f32x4 mss_entry4(f32x4 x, int v, const RowStats& st, 
   return x;
 }
 
-// s_w[widx(v)] = r (probabilities, or logits made probabilities with `st`)
+// s_w[widx(v)] = r (probabilities, or logits made probabilities with `st`);
+// returns this thread's sum of fx40d of them (computed only where used)
 template <bool LG>
-__device__ __forceinline__ void mss_regs_to_lds(const f32x4 (&r)[kMssPfChunks], int V, float* s_w,
-                                                const RowStats& st, float c) {
+__device__ __forceinline__ double mss_regs_to_lds(const f32x4 (&r)[kMssPfChunks], int V, float* s_w,
+                                                  const RowStats& st, float c) {
   const int t = threadIdx.x;
-  f32x4* wp = reinterpret_cast<f32x4*>(s_w + 4 * t + 4 * (t >> 5));
+  double part = 0.0;
+  f32x4* wp = reinterpret_cast<f32x4*>(s_w + mss_slot0<kMssPfChunks>(t));
 #pragma unroll
   for (int j = 0; j < kMssPfChunks; ++j) {
-    const int v = 4 * (t + kMssThreads * j);
-    if (v < V) wp[(kMssChunkStride / 4) * j] = mss_entry4<LG>(r[j], v, st, c);
+    const int v = mss_chunk_v<kMssPfChunks>(t, j);
+    if (v < V) {
+      const f32x4 p = mss_entry4<LG>(r[j], v, st, c);
+      wp[66 * j] = p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part += fx40d(p[e]);
+    }
   }
+  return part;
 }
 
 // w = max(w - s*q, +0) in place with q in registers; returns this thread's
-// sum of fx40(w) (as an integer-valued double)
+// sum of fx40d(w)
 template <bool LG>
 __device__ __forceinline__ double mss_residual_regs(const f32x4 (&r)[kMssPfChunks], int V, float s,
                                                     float* s_w, const RowStats& st, float c) {
   const int t = threadIdx.x;
   double part = 0.0;
-  f32x4* wp = reinterpret_cast<f32x4*>(s_w + 4 * t + 4 * (t >> 5));
+  f32x4* wp = reinterpret_cast<f32x4*>(s_w + mss_slot0<kMssPfChunks>(t));
 #pragma unroll
   for (int j = 0; j < kMssPfChunks; ++j)
-    if (4 * (t + kMssThreads * j) < V) {
-      f32x4 w = wp[(kMssChunkStride / 4) * j];
-      const f32x4 q = mss_entry4<LG>(r[j], 4 * (t + kMssThreads * j), st, c);
+    if (mss_chunk_v<kMssPfChunks>(t, j) < V) {
+      f32x4 w = wp[66 * j];
+      const f32x4 q = mss_entry4<LG>(r[j], mss_chunk_v<kMssPfChunks>(t, j), st, c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float d = fmaf(-s, q[e], w[e]);
-        w[e] = d > 0.0f ? d : 0.0f;
+        w[e] = clamp_pos(d);
         part += fx40d(w[e]);
       }
-      wp[(kMssChunkStride / 4) * j] = w;
+      wp[66 * j] = w;
     }
   return part;
 }
@@ -650,6 +674,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     s_status = 0;
     s_len = commit ? cm.cache_len_in[b] : 0;
     s_nodes = nodes_raw(n_nodes, b, N);
+    s_path[0] = 0;
   }
   __syncthreads();
   const int L = s_len;
@@ -740,8 +765,18 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
 
   // ---- the walk: control flow is uniform, decisions are recomputed by every
   // thread from the same LDS values.  Every row is requested whole: one
-  // memory round trip per pass.
-  int u = 0;
+  // memory round trip per pass.  s_path[d] gets the node at depth d as the
+  // walk descends (it never backtracks; each entry is written before one of
+  // the walk's barriers).  `totals`: s_redd holds the masses of the waves'
+  // ranges of what s_w holds for the final draw (the last residual pass, or
+  // the copy of p_u the draw comes from, left them there).
+  int u = 0, depth = 0;
+  bool totals = false;
+  auto descend = [&](int c) {
+    u = c;
+    ++depth;
+    if (t == 0) s_path[depth] = c;
+  };
   for (;;) {
     // the same in every lane: scalar registers (children, nodes and row
     // addresses derived from them stay scalar)
@@ -751,8 +786,10 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
         f32x4 ra[kMssPfChunks];
         mss_issue_row(llm + (rowN + u) * V, V, ra);
         __syncthreads();
-        mss_regs_to_lds<LG>(ra, V, s_w, p_stats(u), lr.c);
-        __syncthreads();
+        // the masses of the waves' ranges come with the copy; the
+        // reduction's barriers publish s_w
+        block_sum_f64(mss_regs_to_lds<LG>(ra, V, s_w, p_stats(u), lr.c), s_redd);
+        totals = true;
       } else {
         load_p_row(u);
       }
@@ -761,7 +798,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     const int c0 = k0 ? __ffsll((unsigned long long)k0) - 1 : 64 + __ffsll((unsigned long long)k1) - 1;
     const bool ok0 = (c0 < 64 ? (s_first_ok[0] >> c0) : (s_first_ok[1] >> (c0 - 64))) & 1ull;
     if (ok0) {
-      u = c0;
+      descend(c0);
       continue;
     }
     // first child rejected: sequential residual tests at u
@@ -802,11 +839,14 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
         if (s == 0.0f) {  // empty residual: stop testing, sample from p_u
           mss_issue_row(llm + (rowN + u) * V, V, cur);  // cur is consumed
           __syncthreads();
-          mss_regs_to_lds<LG>(cur, V, s_w, p_stats(u), lr.c);
-          __syncthreads();
+          block_sum_f64(mss_regs_to_lds<LG>(cur, V, s_w, p_stats(u), lr.c), s_redd);
+          totals = true;
           return true;
         }
-        if (cn < 0) return true;  // every child rejected: bonus from the residual
+        if (cn < 0) {  // every child rejected: bonus from the residual
+          totals = true;
+          return true;
+        }
         const bool accept = s_rq[cn] * s < s_w[widx(s_tok[cn])];
         __syncthreads();  // every thread has read w[x] before it is updated
         if (accept) {
@@ -820,13 +860,13 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
         if (pass(ra, rb)) break;
       }
       if (next < 0) break;  // bonus from the residual in s_w (or p_u)
-      u = next;
+      descend(next);
       continue;
     }
     load_p_row(u);
     float s = 1.0f;
     int next = -1;
-    bool first = true;
+    bool first = true, emptied = false;
     while (k0 | k1) {
       // lowest remaining child (written out: a helper taking both words by
       // reference made the compiler keep them in private memory)
@@ -853,72 +893,139 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       s = (float)(S * 0x1p-40);
       if (s == 0.0f) {  // empty residual: stop testing, sample from p_u
         load_p_row(u);
+        emptied = true;
         break;
       }
     }
-    if (next < 0) break;  // bonus from the residual in s_w
-    u = next;
+    if (next < 0) {  // bonus from the residual in s_w (or p_u)
+      totals = !emptied;
+      break;
+    }
+    descend(next);
+  }
+  const int len = depth + 1;
+
+  // ---- the commit's first rows (one 16-byte vector of K and of V per
+  // thread) are requested before the final draw, which works in LDS only, so
+  // their round trip overlaps it
+  const bool cok = commit && L >= 0 && L <= cm.Lmax && (long)L + len <= cm.Lcap;
+  const int rv = cm.row_vecs, cper = len * rv, ncopy = cok ? cm.Hkv * cper : 0;
+  const u32x4* ktr = static_cast<const u32x4*>(cm.k_tree);
+  const u32x4* vtr = static_cast<const u32x4*>(cm.v_tree);
+  u32x4* kca = static_cast<u32x4*>(cm.k_cache);
+  u32x4* vca = static_cast<u32x4*>(cm.v_cache);
+  auto copy_src = [&](int x, size_t& dst) {
+    const int h = x / cper, r = x - h * cper;
+    const int j = r / rv, e = r - j * rv;
+    const size_t bh = (size_t)b * cm.Hkv + h;
+    dst = (bh * cm.Lcap + (size_t)(L + j)) * rv + e;
+    return (bh * N + s_path[j]) * rv + e;
+  };
+  u32x4 kx0 = {0u, 0u, 0u, 0u}, vx0 = {0u, 0u, 0u, 0u};
+  size_t dst0 = 0;
+  if (t < ncopy) {
+    const size_t src = copy_src(t, dst0);
+    kx0 = ktr[src];
+    vx0 = vtr[src];
   }
 
-  // ---- bonus: inverse CDF over the exact integer prefix sums of fx40(w).
-  // Thread t owns the entries [per*t, per*t + per), per a multiple of 4, so
-  // each 4-entry group is 16 aligned bytes of s_w (a 128-entry block never
-  // splits one); masses are exact integers carried in doubles.
-  const int per = 4 * ((V + 4 * kMssThreads - 1) / (4 * kMssThreads));
-  constexpr int kGroups = (kMssMaxVocab + 4 * kMssThreads - 1) / (4 * kMssThreads);
-  const int v_lo = min(V, t * per), v_hi = min(V, v_lo + per);
-  double mine = 0.0, gsum[kGroups];  // gsum[i]: mass of the group at v_lo + 4i
+  // ---- bonus: inverse CDF over the exact integer prefix sums of fx40d(w).
+  // The masses of the waves' ranges (left by the walk, else summed here,
+  // each wave over its own range in the row passes' order)
+  // locate the wave whose range holds the target; that wave alone finds the
+  // entry: lane l takes P consecutive entries of the range (P a multiple of
+  // 4: each 4-entry group is 16 aligned bytes of s_w), an exclusive scan over
+  // the lanes gives each run's start, and the lane whose run crosses the
+  // target walks its groups.  Masses are exact integers carried in doubles.
+  constexpr int kSpan = PF ? 256 * kMssPfChunks : kMssSpan;
+  if (!totals) {
+    double part = 0.0;
 #pragma unroll
-  for (int i = 0; i < kGroups; ++i) {
-    const int v = v_lo + 4 * i;
-    double g = 0.0;
-    if (v < v_hi) {
-      const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
+    for (int k = 0; k < kSpan / 256; ++k) {
+      const int v = kSpan * wave + 4 * (64 * k + (t & 63));
+      if (v < V) {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) g += v + e < v_hi ? fx40d(w4[e]) : 0.0;
-    }
-    gsum[i] = g;
-    mine += g;
-  }
-  double Sd;
-  const double excl = block_excl_scan_f64(mine, s_redd, Sd);
-  if (t == 0) s_pick = -1;
-  __syncthreads();
-  if (Sd > 0.0) {
-    const uint64_t S = (uint64_t)Sd, lo = (uint64_t)excl, hi = (uint64_t)(excl + mine);
-    const uint64_t R = s_bonus[u];
-    const uint64_t T = R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24);  // floor(R*S/2^24)
-    if (lo <= T && T < hi) {
-      // the group that crosses T from the register sums, then its entries
-      // (unrolled with constant indices: gsum stays in registers; a group
-      // with no entries has mass 0 and never crosses)
-      uint64_t cum = lo;
-      int gi = kGroups - 1;
-      bool found = false;
-#pragma unroll
-      for (int i = 0; i < kGroups; ++i) {
-        const uint64_t g = (uint64_t)gsum[i];
-        if (!found && cum + g > T) {
-          gi = i;
-          found = true;
-        } else if (!found) {
-          cum += g;
-        }
+        for (int e = 0; e < 4; ++e) part += v + e < V ? fx40d(w4[e]) : 0.0;
       }
-      const int v = v_lo + 4 * gi;
-      const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
-      int pick = v_hi - 1;
+    }
+    block_sum_f64(part, s_redd);  // s_redd[w] = mass of wave w's range
+  }
+  // masses below 2^53: exact in doubles, compared as doubles
+  double Sd = 0.0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (v + e < v_hi) {
-          cum += fx40(w4[e]);
-          if (cum > T) {
-            pick = v + e;
-            break;
+  for (int w = 0; w < kMssWaves; ++w) Sd += s_redd[w];
+  if (Sd > 0.0) {
+    const uint64_t S = (uint64_t)Sd, R = s_bonus[u];
+    const double T = (double)(R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24));  // floor(R*S/2^24)
+    double before = 0.0;
+    int ws = kMssWaves - 1;
+    bool found = false;
+#pragma unroll
+    for (int w = 0; w < kMssWaves; ++w) {
+      const double g = s_redd[w];
+      if (!found && before + g > T) {
+        ws = w;
+        found = true;
+      } else if (!found) {
+        before += g;
+      }
+    }
+    if (wave == ws) {
+      constexpr int P = kSpan / 64, kG = P / 4;
+      const int lane = t & 63;
+      const int v_lo = min(V, ws * kSpan + lane * P), v_hi = min(V, v_lo + P);
+      double mine = 0.0, gsum[kG];  // gsum[i]: mass of the group at v_lo + 4i
+#pragma unroll
+      for (int i = 0; i < kG; ++i) {
+        const int v = v_lo + 4 * i;
+        double g = 0.0;
+        if (v < v_hi) {
+          const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) g += v + e < v_hi ? fx40d(w4[e]) : 0.0;
+        }
+        gsum[i] = g;
+        mine += g;
+      }
+      double incl = mine;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const double o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      const double lo = before + (incl - mine), hi = before + incl;
+      if (lo <= T && T < hi) {
+        // the group that crosses T from the register sums, then its entries
+        // (unrolled with constant indices: gsum stays in registers; a group
+        // with no entries has mass 0 and never crosses)
+        double cum = lo;
+        int gi = kG - 1;
+        bool gfound = false;
+#pragma unroll
+        for (int i = 0; i < kG; ++i) {
+          if (!gfound && cum + gsum[i] > T) {
+            gi = i;
+            gfound = true;
+          } else if (!gfound) {
+            cum += gsum[i];
           }
         }
+        const int v = v_lo + 4 * gi;
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
+        int pick = v_hi - 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (v + e < v_hi) {
+            cum += fx40d(w4[e]);
+            if (cum > T) {
+              pick = v + e;
+              break;
+            }
+          }
+        }
+        s_pick = pick;
       }
-      s_pick = pick;
     }
   } else if (t == 0) {  // nothing representable left: the largest entry
     int bi = 0;
@@ -930,46 +1037,30 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   const int bonus = s_pick;
 
   // ---- path root -> u and the emitted tokens
-  if (t == 0) {
-    int d = 0;
-    for (int j = u; j != -1; j = s_par[j]) ++d;
-    int k = d - 1;
-    for (int j = u; j != -1; j = s_par[j]) s_path[k--] = j;
-    s_pick = d;
-  }
-  __syncthreads();
-  const int len = s_pick;
   for (int k = t; k < N; k += kMssThreads) {
     path[rowN + k] = k < len ? s_path[k] : -1;
     out_tokens[rowN + k] = k + 1 < len ? s_tok[s_path[k + 1]] : (k + 1 == len ? bonus : -1);
   }
   // ---- the commit: row L + j of every kv head takes tree node s_path[j]
-  bool ok = true;
   if (commit) {
-    ok = L >= 0 && L <= cm.Lmax && (long)L + len <= cm.Lcap;
-    const int rv = cm.row_vecs, per = len * rv;
-    if (ok) {
-      const u32x4* kt = static_cast<const u32x4*>(cm.k_tree);
-      const u32x4* vt = static_cast<const u32x4*>(cm.v_tree);
-      u32x4* kc = static_cast<u32x4*>(cm.k_cache);
-      u32x4* vc = static_cast<u32x4*>(cm.v_cache);
-      for (int x = t; x < cm.Hkv * per; x += kMssThreads) {
-        const int h = x / per, r = x - (x / per) * per;
-        const int j = r / rv, e = r - (r / rv) * rv;
-        const size_t bh = (size_t)b * cm.Hkv + h;
-        const u32x4 kx = kt[(bh * N + s_path[j]) * rv + e];
-        const u32x4 vx = vt[(bh * N + s_path[j]) * rv + e];
-        kc[(bh * cm.Lcap + (size_t)(L + j)) * rv + e] = kx;
-        vc[(bh * cm.Lcap + (size_t)(L + j)) * rv + e] = vx;
-      }
+    if (t < ncopy) {
+      kca[dst0] = kx0;
+      vca[dst0] = vx0;
+    }
+    for (int x = t + kMssThreads; x < ncopy; x += kMssThreads) {
+      size_t dst;
+      const size_t src = copy_src(x, dst);
+      const u32x4 kx = ktr[src], vx = vtr[src];
+      kca[dst] = kx;
+      vca[dst] = vx;
     }
     if (cm.committed_src)
-      for (int k = t; k < N; k += kMssThreads) cm.committed_src[rowN + k] = (ok && k < len) ? s_path[k] : -1;
-    if (t == 0) cm.cache_len_out[b] = ok ? L + len : L;
+      for (int k = t; k < N; k += kMssThreads) cm.committed_src[rowN + k] = (cok && k < len) ? s_path[k] : -1;
+    if (t == 0) cm.cache_len_out[b] = cok ? L + len : L;
   }
   if (t == 0) {
     path_len[b] = len;
-    if (dev_status) dev_status[b] = ok ? TTV_OK : TTV_E_SHAPE;
+    if (dev_status) dev_status[b] = (!commit || cok) ? TTV_OK : TTV_E_SHAPE;
   }
 }
 
