@@ -29,11 +29,7 @@ struct PlanItem {
   int L;            // the request's prefix length, clamped to [0, Lmax]
 };
 
-__device__ __forceinline__ int plan_wave_sum(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
+__device__ __forceinline__ int plan_wave_sum(int v) { return wave_allsum_i32(v); }
 
 // Work item `item` of the balanced split, computed by one wavefront (every
 // wave of a workgroup computes the same values); false when the item is not

@@ -72,6 +72,57 @@ __device__ __forceinline__ int wave_max_i32(int v) {
   return v;
 }
 
+// -------------------------------------------- register-only wave sums ----
+// Sums over the 64 lanes that stay in the VALU (a __shfl_xor step is an LDS
+// round trip, ds_bpermute): two quad permutations and two row rotations
+// (DPP) sum each 16-lane row, then v_permlane16_swap and v_permlane32_swap
+// add the other rows.  Every lane gets the total; all 64 lanes must be
+// active.  For doubles each DPP move carries both halves, so the sum is
+// exact where the terms are (integer-valued doubles below 2^53).
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;  // row_ror:4
+constexpr int kDppRowRor8 = 0x128;  // row_ror:8
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ int wave_allsum_i32(int v) {
+  v += (int)dpp_u32<kDppQuadXor1>((uint32_t)v);
+  v += (int)dpp_u32<kDppQuadXor2>((uint32_t)v);
+  v += (int)dpp_u32<kDppRowRor4>((uint32_t)v);
+  v += (int)dpp_u32<kDppRowRor8>((uint32_t)v);
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = (int)(r[0] + r[1]);
+  r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return (int)(r[0] + r[1]);
+}
+__device__ __forceinline__ double wave_allsum_f64(double v) {
+  v += dpp_f64<kDppQuadXor1>(v);
+  v += dpp_f64<kDppQuadXor2>(v);
+  v += dpp_f64<kDppRowRor4>(v);
+  v += dpp_f64<kDppRowRor8>(v);
+  // each swap returns the lane's own and its partner's words, the low and the
+  // high halves in the same order
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  v = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])) +
+      __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+  u = (uint64_t)__double_as_longlong(v);
+  lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+  hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  return __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])) +
+         __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+}
+
 // --------------------------------------------------------- tree topology --
 // Ancestor bitsets of one request's token tree, built by ONE wavefront.
 // [SI] §4 "Tree Attention": node i stands for the sequence root -> i, so the

@@ -391,16 +391,11 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
 
 // Sum over the block of integer-valued doubles (exact below 2^53).
 __device__ __forceinline__ double block_sum_f64(double v, double* s_redd) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  v = wave_sum_f64(v);
+  v = wave_allsum_f64(v);
   __syncthreads();  // s_redd free from its previous use
   if (lane == 0) s_redd[wave] = v;
   __syncthreads();
@@ -410,29 +405,6 @@ __device__ __forceinline__ double block_sum_f64(double v, double* s_redd) {
   return t;
 }
 
-// Exclusive prefix sum over the threads of the block (thread order) of
-// integer-valued doubles (exact below 2^53); `total` gets the block's sum.
-__device__ __forceinline__ double block_excl_scan_f64(double v, double* s_redd, double& total) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  double incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
-  }
-  __syncthreads();  // s_redd free from its previous use
-  if (lane == 63) s_redd[wave] = incl;
-  __syncthreads();
-  double before = 0.0, tot = 0.0;
-#pragma unroll
-  for (int w = 0; w < kMssThreads / 64; ++w) {
-    const double x = s_redd[w];
-    tot += x;
-    before += w < wave ? x : 0.0;
-  }
-  total = tot;
-  return before + incl - v;
-}
 
 // Row passes.  Every wavefront owns a contiguous range of the vocabulary,
 // wave w the entries [w*WS, (w+1)*WS), so the per-wave sums of a pass's
