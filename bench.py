@@ -37,6 +37,9 @@ launch (flops for c4, KV bytes otherwise) over its average launch time (HIP
 events on the launch stream); cpu_baseline = the CPU oracle timed on a
 bounded sample of the same workload on all host cores and on one (the
 oracle is test infrastructure; it is imported only here, for that leg).
+sub_workloads (--also, default c3,c5): the same measurement of the
+HBM-bound workloads after the main one, compact (value, step and stage
+medians, roofline), without a CPU leg.
 """
 from __future__ import annotations
 
@@ -364,6 +367,9 @@ def main():
                     help="reuse one input copy (cache-resident) instead of rotating copies")
     ap.add_argument("--unfused", action="store_true",
                     help="verification and commit as two calls instead of one pass")
+    ap.add_argument("--also", default="c3,c5",
+                    help="comma-separated workloads measured after the main one and reported "
+                         "in compact form under sub_workloads ('' = none; no CPU leg)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -372,14 +378,41 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
+    also = [w for w in args.also.split(",") if w and w != args.workload]
+    for w in also:
+        if w not in synth.WORKLOADS:
+            print("--also: unknown workload %s" % w, file=sys.stderr)
+            sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    d = synth.make(args.workload)
+    res, d = measure(args.workload, args, dev)
+    if also:
+        res["sub_workloads"] = {}
+        for w in also:
+            torch.cuda.empty_cache()
+            sub, _ = measure(w, args, dev)
+            r = sub["roofline"]
+            res["sub_workloads"][w] = {
+                "value": sub["value"], "unit": sub["unit"], "ms_per_step": sub["ms_per_step"],
+                "steps": sub["steps"], "config": sub["config"],
+                "stage_us_median": {k: (v["median"] if v else None)
+                                    for k, v in sub["stage_us"].items()},
+                "roofline": {k: r[k] for k in ("bound", "achieved", "peak", "unit", "frac",
+                                               "traffic", "avg_launch_us")}}
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+def measure(workload, args, dev):
+    """One workload: its timed steps and per-entry-point stages, as the JSON
+    record (without the CPU leg); returns (record, the workload's arrays)."""
+    d = synth.make(workload)
     first = Inputs(d, dev)
     per_copy = first.nbytes()
     ncopies = 1 if args.warm else max(1, min(64, -(-2 * MALL_BYTES // per_copy)))
     copies = [first] + [Inputs(d, dev) for _ in range(ncopies - 1)]
-    log("workload %s: %d input copies of %.1f MB" % (args.workload, ncopies, per_copy / 1e6))
+    log("workload %s: %d input copies of %.1f MB" % (workload, ncopies, per_copy / 1e6))
     step = Step(d, copies, dev, fuse=not args.unfused)
     stream = torch.cuda.current_stream(dev)
 
@@ -419,7 +452,7 @@ def main():
     kv_bytes, flops = attn_work(d)
     ms_attn = t_attn["mean"]  # the roofline takes the average launch
     kv_gbs = kv_bytes / (ms_attn * 1e-3) / 1e9
-    mfma_bound = args.workload == "c4"
+    mfma_bound = workload == "c4"
     if mfma_bound:
         ach = flops / (ms_attn * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -427,7 +460,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": kv_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": kv_gbs / HBM_PEAK_GBS}
-    roof["traffic"] = stored_traffic(args.workload)
+    roof["traffic"] = stored_traffic(workload)
     roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
     roof["kernel"] = "ttv_tree_attn (all kernels of one call)"
     roof["per_launch_algorithmic"] = flops if mfma_bound else kv_bytes
@@ -448,8 +481,8 @@ def main():
         "ms_per_step_mean": t_step["mean"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": d["dtype"], "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "N": N, "Hq": d["Hq"], "Hkv": d["Hkv"],
-                   "D": d["D"], "prefix": synth.WORKLOADS[args.workload].L, "V": d["V"],
+        "config": {"workload": workload, "B": B, "N": N, "Hq": d["Hq"], "Hkv": d["Hkv"],
+                   "D": d["D"], "prefix": synth.WORKLOADS[workload].L, "V": d["V"],
                    "verify": d["mode"],
                    "verify_commit": "one pass" if step.fused else "two calls",
                    "input_copies": ncopies,
@@ -464,9 +497,7 @@ def main():
         "step_us": us(t_step),
         "roofline": roof,
     }
-    if args.cpu_budget > 0:
-        res["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
-    print(json.dumps(res), flush=True)
+    return res, d
 
 
 if __name__ == "__main__":

@@ -97,7 +97,7 @@ def main():
     dest = os.path.join(out, "summary")
     os.makedirs(dest, exist_ok=True)
     bench_cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", w, "--steps",
-                 str(args.steps), "--warmup", str(args.warmup), "--cpu-budget", "0"]
+                 str(args.steps), "--warmup", str(args.warmup), "--cpu-budget", "0", "--also", ""]
 
     # 1. kernel durations
     files, cmd_trace = rocprof(os.path.join(out, "trace"), ["--kernel-trace", "--stats"],

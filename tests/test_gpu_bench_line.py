@@ -46,6 +46,7 @@ def run_bench(*args):
     return d
 
 
+@pytest.mark.timeout(280)  # three workloads' inputs are built and measured
 def test_default_bench_line():
     """The default line: the long-context workload, exactly the steps asked
     for, its roofline against the bf16 matrix-core peak with the KV GB/s
@@ -57,10 +58,20 @@ def test_default_bench_line():
     r = d["roofline"]
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
     assert r["per_launch_algorithmic_unit"] == "flop" and 0 < r["kv_frac_of_hbm_peak"] < 1
+    # the HBM-bound workloads ride along in compact form
+    assert sorted(d["sub_workloads"]) == ["c3", "c5"]
+    for w, sub in d["sub_workloads"].items():
+        assert sub["config"]["workload"] == w and sub["steps"] == 4
+        c = sub["config"]
+        assert sub["value"] == pytest.approx(c["B"] * c["N"] / (sub["ms_per_step"] * 1e-3), rel=1e-6)
+        rs = sub["roofline"]
+        assert rs["bound"] == "hbm" and 0 < rs["frac"] < 1 and rs["peak"] == 8000.0
 
 
 def test_stochastic_bench_line():
-    d = run_bench("--workload", "c5", "--steps", "3", "--warmup", "1", "--cpu-budget", "0.5")
+    d = run_bench("--workload", "c5", "--steps", "3", "--warmup", "1", "--cpu-budget", "0.5",
+                  "--also", "")
+    assert "sub_workloads" not in d
     assert d["steps"] == 3 and d["config"]["workload"] == "c5"
     assert d["config"]["verify"] == "stochastic"
     r = d["roofline"]
