@@ -66,16 +66,15 @@ __device__ __forceinline__ uint32_t p_order_key(float z) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t p_wave_sum_u64(uint64_t x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += shfl_xor_u64(x, m);
-  return x;
-}
 
 }  // namespace
 
-template <bool VEC>
-__global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int topk,
+// SEL: top-k and/or top-p.  Without them a thread's row needs one register
+// set (the logits become their exponentials), and two workgroups share a
+// CU, so one's loads are in flight while the other reduces.
+template <bool VEC, bool SEL>
+__global__ __launch_bounds__(kProbThreads) __attribute__((amdgpu_waves_per_eu(SEL ? 4 : 8)))
+void probs_kernel(int V, float c, int topk,
                                                              uint32_t top_p24,
                                                              const float* __restrict__ logits,
                                                              float* __restrict__ probs,
@@ -96,7 +95,13 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
   const f32x4* r4 = reinterpret_cast<const f32x4*>(row);
   const int n4 = V / 4;
   const bool in_regs = VEC && n4 <= kProbRegQuads * kProbThreads;
-  f32x4 rq[kProbRegQuads], re[kProbRegQuads];
+  // the row's logits and their exponentials; without selection the
+  // exponentials overwrite the logits (which are not needed again)
+  f32x4 rq[kProbRegQuads], re_sel[SEL ? kProbRegQuads : 1];
+  auto RE = [&](int u) -> f32x4& {
+    if constexpr (SEL) return re_sel[u];
+    else return rq[u];
+  };
   if (in_regs) {
 #pragma unroll
     for (int u = 0; u < kProbRegQuads; ++u) {
@@ -126,8 +131,7 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
     }
   };
   auto block_max = [&](float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    x = wave_allmax_f32(x);
     if (lane == 0) s_red[wave] = x;
     __syncthreads();
     float r = s_red[0];
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
   };
   auto block_min = [&](float x) { return -block_max(-x); };
   auto block_sum_u64 = [&](uint64_t x) {
-    x = p_wave_sum_u64(x);
+    x = wave_allsum_u64(x);
     if (lane == 0) s_red64[wave] = x;
     __syncthreads();
     uint64_t r = 0;
@@ -152,12 +156,13 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
   float tmax = -INFINITY;
   visit_row([&](float z, int) { tmax = fmaxf(tmax, z); });
   const float m = block_max(tmax);
-  // 2^t of every entry, kept in registers with the row
+  // 2^t of every entry, kept in registers with the row (without selection
+  // the logits are not needed again, and the compiler reuses their registers)
   if (in_regs) {
 #pragma unroll
     for (int u = 0; u < kProbRegQuads; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) re[u][e] = exp2_taylor((rq[u][e] - m) * c);
+      for (int e = 0; e < 4; ++e) RE(u)[e] = exp2_taylor((rq[u][e] - m) * c);
   }
   auto visit_ze = [&](auto visit) {
     if (in_regs) {
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
         const int x = tid + u * kProbThreads;
         if (x < n4) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) visit(rq[u][e], re[u][e], 4 * x + e);
+          for (int e = 0; e < 4; ++e) visit(rq[u][e], RE(u)[e], 4 * x + e);
         }
       }
     } else {
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
   // ---- top-k: the k-th entry (kv, ki); every entry is kept without top-k
   float kv = -INFINITY;
   int ki = INT_MAX;
-  if (topk > 0 && topk < V) {
+  if (SEL && topk > 0 && topk < V) {
     // a lower bound of the k-th entry: every wave takes the ceil(k/16)-th
     // largest of its 64 per-thread maxima, and the smallest of those has at
     // least 16*ceil(k/16) >= k entries of the row at or above it
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
   int ithr = ki;
 
   // ---- top-p: the token where the running mass reaches ceil(P*S/2^24)
-  if (top_p24 > 0u && top_p24 < (1u << 24)) {
+  if (SEL && top_p24 > 0u && top_p24 < (1u << 24)) {
     double part = 0.0;  // at most 8*4 masses below 2^40 each: exact
     float zmin = INFINITY;
     visit_ze([&](float z, float e, int i) {
@@ -411,7 +416,7 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
   }
 
   // ---- normaliser and probabilities (or the row's statistics)
-  auto kept = [&](float z, int i) { return z > zthr || (z == zthr && i <= ithr); };
+  auto kept = [&](float z, int i) { return !SEL || z > zthr || (z == zthr && i <= ithr); };
   double part = 0.0;
   visit_ze([&](float z, float e, int i) {
     if (kept(z, i)) part += mass40(e);
@@ -431,7 +436,7 @@ __global__ __launch_bounds__(kProbThreads) void probs_kernel(int V, float c, int
       if (x < n4) {
         f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = kept(rq[u][e], 4 * x + e) ? re[u][e] * inv : 0.f;
+        for (int e = 0; e < 4; ++e) o[e] = !SEL || kept(rq[u][e], 4 * x + e) ? RE(u)[e] * inv : 0.f;
         o4[x] = o;
       }
     }
@@ -459,12 +464,10 @@ hipError_t launch_probs(int R, int V, float T, int topk, float top_p, const floa
                         float* probs, RowStats* stats, bool vec, hipStream_t s) {
   const float c = probs_scale(T);
   const uint32_t p24 = probs_top_p24(top_p);
-  if (vec)
-    hipLaunchKernelGGL(probs_kernel<true>, dim3(R), dim3(kProbThreads), 0, s, V, c, topk, p24,
-                       logits, probs, stats);
-  else
-    hipLaunchKernelGGL(probs_kernel<false>, dim3(R), dim3(kProbThreads), 0, s, V, c, topk, p24,
-                       logits, probs, stats);
+  const bool sel = (topk > 0 && topk < V) || p24 != 0u;
+  auto kern = vec ? (sel ? probs_kernel<true, true> : probs_kernel<true, false>)
+                  : (sel ? probs_kernel<false, true> : probs_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3(R), dim3(kProbThreads), 0, s, V, c, topk, p24, logits, probs, stats);
   return hipGetLastError();
 }
 

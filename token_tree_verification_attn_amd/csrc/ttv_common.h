@@ -104,23 +104,52 @@ __device__ __forceinline__ int wave_allsum_i32(int v) {
   r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
   return (int)(r[0] + r[1]);
 }
+// the two 64-bit words a permlane swap hands a lane (its own and its
+// partner's; the low and the high halves come in the same order)
+template <bool S32>
+__device__ __forceinline__ void swap_pair_u64(uint64_t u, uint64_t& a, uint64_t& b) {
+  const uint32_t l = (uint32_t)u, h = (uint32_t)(u >> 32);
+  const auto lo = S32 ? __builtin_amdgcn_permlane32_swap(l, l, false, false)
+                      : __builtin_amdgcn_permlane16_swap(l, l, false, false);
+  const auto hi = S32 ? __builtin_amdgcn_permlane32_swap(h, h, false, false)
+                      : __builtin_amdgcn_permlane16_swap(h, h, false, false);
+  a = ((uint64_t)hi[0] << 32) | lo[0];
+  b = ((uint64_t)hi[1] << 32) | lo[1];
+}
 __device__ __forceinline__ double wave_allsum_f64(double v) {
   v += dpp_f64<kDppQuadXor1>(v);
   v += dpp_f64<kDppQuadXor2>(v);
   v += dpp_f64<kDppRowRor4>(v);
   v += dpp_f64<kDppRowRor8>(v);
-  // each swap returns the lane's own and its partner's words, the low and the
-  // high halves in the same order
-  uint64_t u = (uint64_t)__double_as_longlong(v);
-  auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
-  auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
-  v = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])) +
-      __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
-  u = (uint64_t)__double_as_longlong(v);
-  lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
-  hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
-  return __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])) +
-         __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+  uint64_t a, b;
+  swap_pair_u64<false>((uint64_t)__double_as_longlong(v), a, b);
+  v = __longlong_as_double((long long)a) + __longlong_as_double((long long)b);
+  swap_pair_u64<true>((uint64_t)__double_as_longlong(v), a, b);
+  return __longlong_as_double((long long)a) + __longlong_as_double((long long)b);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(x >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)x);
+}
+__device__ __forceinline__ uint64_t wave_allsum_u64(uint64_t v) {
+  v += dpp_u64<kDppQuadXor1>(v);
+  v += dpp_u64<kDppQuadXor2>(v);
+  v += dpp_u64<kDppRowRor4>(v);
+  v += dpp_u64<kDppRowRor8>(v);
+  uint64_t a, b;
+  swap_pair_u64<false>(v, a, b);
+  swap_pair_u64<true>(a + b, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float wave_allmax_f32(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuadXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuadXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppRowRor4>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppRowRor8>(__float_as_uint(v))));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // --------------------------------------------------------- tree topology --
