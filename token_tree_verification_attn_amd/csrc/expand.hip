@@ -41,17 +41,7 @@ __device__ __forceinline__ bool ranks_before(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(bv, m);
-    const int oi = __shfl_xor(bi, m);
-    if (ranks_before(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-}
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) { wave_allargmax(bv, bi); }
 
 }  // namespace
 
@@ -173,9 +163,7 @@ __global__ __launch_bounds__(kExpandThreads) void tree_expand_kernel(
       float lm = a[0];
 #pragma unroll
       for (int j = 1; j < PER; ++j) lm = fmaxf(lm, a[j]);
-      float wm = lm;
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) wm = fmaxf(wm, __shfl_xor(wm, m));
+      const float wm = wave_allmax_f32(lm);
       const uint64_t has = __ballot(lm == wm);
       if (lane == __ffsll((unsigned long long)has) - 1) {
         bool done = false;

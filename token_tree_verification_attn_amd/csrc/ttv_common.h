@@ -152,6 +152,37 @@ __device__ __forceinline__ float wave_allmax_f32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// The (value, index) pair ranking first over the wave -- the larger value,
+// the lower index on equal values -- in every lane, register-only as the
+// sums above (the ranking is a total order, so any pairing order gives the
+// same winner).
+__device__ __forceinline__ void argmax_take(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp_step(float& v, int& i) {
+  argmax_take(v, i, __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v))), (int)dpp_u32<CTRL>((uint32_t)i));
+}
+__device__ __forceinline__ void wave_allargmax(float& v, int& i) {
+  argmax_dpp_step<kDppQuadXor1>(v, i);
+  argmax_dpp_step<kDppQuadXor2>(v, i);
+  argmax_dpp_step<kDppRowRor4>(v, i);
+  argmax_dpp_step<kDppRowRor8>(v, i);
+  auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  auto ri = __builtin_amdgcn_permlane16_swap((uint32_t)i, (uint32_t)i, false, false);
+  v = __uint_as_float(rv[0]);
+  i = (int)ri[0];
+  argmax_take(v, i, __uint_as_float(rv[1]), (int)ri[1]);
+  rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  ri = __builtin_amdgcn_permlane32_swap((uint32_t)i, (uint32_t)i, false, false);
+  v = __uint_as_float(rv[0]);
+  i = (int)ri[0];
+  argmax_take(v, i, __uint_as_float(rv[1]), (int)ri[1]);
+}
+
 // --------------------------------------------------------- tree topology --
 // Ancestor bitsets of one request's token tree, built by ONE wavefront.
 // [SI] §4 "Tree Attention": node i stands for the sequence root -> i, so the
