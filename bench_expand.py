@@ -1,13 +1,16 @@
 """Throughput of token-tree construction on one GPU: one level of
 expansion-based construction (ttv_tree_expand, the default), or merge-based
 construction (ttv_tree_merge, --op merge), probabilities from logits
-(ttv_probs_from_logits, --op probs), or stochastic verification fed with
-logits (ttv_tree_verify_logits, --op verify_logits).
+(ttv_probs_from_logits, --op probs), stochastic verification fed with
+logits (ttv_tree_verify_logits, --op verify_logits), or stochastic
+verification of stored probabilities at any vocabulary size
+(ttv_tree_verify, --op verify).
 
     python bench_expand.py [--steps K] [--warmup W] [--B 16] [--F 16] [--V 32000] [--k 4]
     python bench_expand.py --op merge [--B 4] [--S 4] [--Ls 16]
     python bench_expand.py --op probs [--B 16] [--F 64] [--V 32000] [--k 0] [--T 0.8] [--top-p 1]
     python bench_expand.py --op verify_logits [--k 0] [--T 0.8] [--top-p 1]
+    python bench_expand.py --op verify [--V 32000]
 
 Workload: B requests, each expanding F frontier nodes by the k most probable
 tokens of their speculator rows of V fp32 probabilities (softmax of N(0,2)
@@ -244,9 +247,62 @@ def bench_verify_logits(args):
           flush=True)
 
 
+def bench_verify(args):
+    """Multi-step speculative sampling (ttv_tree_verify, stochastic) on the
+    stochastic workload's trees and probability rows (16 requests x 64 nodes,
+    softmax of N(0,2) logits at temperature 0.8, each node's token drawn from
+    its speculator row) at vocabulary size --V; past 36864 entries the
+    residual lives in the workspace.  Checked against the oracle on the first
+    request."""
+    import dataclasses
+    import oracle
+    import synth
+    spec = dataclasses.replace(synth.WORKLOADS["c5"], V=args.V)
+    B, N, V = spec.B, spec.N, spec.V
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = synth.make(spec, with_kv=False)
+    per_copy = 2 * d["llm"].nbytes
+    ncopies = max(1, min(16, -(-2 * bench.MALL_BYTES // per_copy)))
+    parents = torch.from_numpy(d["parents"]).to(dev)
+    tok = torch.from_numpy(d["tokens"]).to(dev)
+    pl = [torch.from_numpy(d["llm"]).to(dev)]
+    ps = [torch.from_numpy(d["ssm"]).to(dev)]
+    for _ in range(ncopies - 1):
+        pl.append(pl[0].clone())
+        ps.append(ps[0].clone())
+    path, plen, otok, st = ttv._verify_outputs(B, N, dev, None, None, None, None)
+    nv = ttv.tree_verify_workspace_size(ttv.STOCHASTIC, B, N, V)
+    ws = torch.empty(nv, dtype=torch.uint8, device=dev) if nv else None
+
+    def call(i):
+        c = i % ncopies
+        ttv.tree_verify(ttv.STOCHASTIC, parents, tok, pl[c], ps[c], d["seed"], 0, path=path,
+                        path_len=plen, out_tokens=otok, dev_status=st, workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ref = oracle.verify_mss_seeded(d["parents"][:1], d["tokens"][:1], d["llm"][:1],
+                                   d["ssm"][:1], d["seed"], 0)
+    for g, r in zip((path, plen, otok, st), ref):
+        assert np.array_equal(g[:1].cpu().numpy(), r), "differs from the oracle"
+    ms, mean, launch = time_calls(call, ncopies, args.steps, dev, stream)
+    print(json.dumps({
+        "metric": "tree_verify stochastic trees/s", "value": B / (ms * 1e-3), "unit": "trees/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_mean": mean, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "verify", "B": B, "N": N, "V": V, "input_copies": ncopies,
+                   "launch": launch, "inputs": "rotated, HBM-resident",
+                   "residual": "workspace" if nv else "LDS",
+                   "path_len_mean": float(plen.float().mean())}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--op", choices=["expand", "merge", "probs", "verify_logits"],
+    ap.add_argument("--op", choices=["expand", "merge", "probs", "verify_logits", "verify"],
                     default="expand")
     ap.add_argument("--T", type=float, default=0.8)
     ap.add_argument("--S", type=int, default=4)
@@ -267,6 +323,8 @@ def main():
         return bench_merge(args)
     if args.op == "probs":
         return bench_probs(args)
+    if args.op == "verify":
+        return bench_verify(args)
     if args.op == "verify_logits":
         if args.k == 4 and "--k" not in sys.argv:
             args.k = 0

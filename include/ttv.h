@@ -307,10 +307,12 @@ ttv_status ttv_tree_attn_noalloc(ttv_dtype dt, int32_t B, int32_t N,
  *            after (path_len entries in all).
  *   A malformed tree gives path_len 0 and -1 everywhere, dev_status TTV_E_TREE;
  *   in stochastic mode a non-root token outside [0,V) does the same with
- *   TTV_E_SHAPE.  Stochastic mode needs V <= 36864 (the residual lives in
- *   on-chip memory), else TTV_E_UNSUPPORTED.
- *   workspace >= ttv_tree_verify_workspace_size(...) bytes (contents need no
- *            initialisation).
+ *   TTV_E_SHAPE.  Stochastic mode keeps the walk's residual distribution on
+ *   chip up to V = 36864; from there up to V = 262144 (V % 4 == 0, else
+ *   TTV_E_UNSUPPORTED) it keeps it in the workspace, B*V floats.
+ *   workspace >= ttv_tree_verify_workspace_size(...) bytes, 16-byte aligned
+ *            (contents need no initialisation); greedy: argmax partials;
+ *            stochastic: none up to V = 36864, else the residual.
  * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_DTYPE (mode), TTV_E_UNSUPPORTED,
  *         TTV_E_ALIGN, TTV_E_WORKSPACE, TTV_E_LAUNCH.
  */
@@ -323,6 +325,8 @@ ttv_status ttv_tree_verify(ttv_verify_mode mode, int32_t B, int32_t N,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Bytes of workspace ttv_tree_verify(_varlen) and ttv_tree_verify_commit(_varlen)
+ * need; (size_t)-1 for sizes they do not take. */
 size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B,
                                       int32_t N, int32_t V);
 

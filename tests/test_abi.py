@@ -122,7 +122,11 @@ def verify(**kw):
     (dict(mode=1), ttv.E_NULL),
     (dict(B=0), ttv.E_SHAPE), (dict(V=0), ttv.E_SHAPE),
     (dict(N=200), ttv.E_UNSUPPORTED),
-    (dict(mode=1, ssm=A, V=40000), ttv.E_UNSUPPORTED),
+    (dict(mode=1, ssm=A, V=40001), ttv.E_UNSUPPORTED),   # residual in memory: V % 4 == 0
+    (dict(mode=1, ssm=A, V=(1 << 18) + 4), ttv.E_UNSUPPORTED),
+    (dict(mode=1, ssm=A, V=40000, ws=None), ttv.E_WORKSPACE),
+    (dict(mode=1, ssm=A, V=40000, wsb=2 * 40000 * 4 - 4), ttv.E_WORKSPACE),
+    (dict(mode=1, ssm=A, V=40000, ws=MIS), ttv.E_ALIGN),
     (dict(llm=MIS), ttv.E_ALIGN), (dict(mode=1, ssm=MIS), ttv.E_ALIGN),
     (dict(ws=None), ttv.E_WORKSPACE), (dict(wsb=8), ttv.E_WORKSPACE),
 ])
@@ -146,8 +150,12 @@ def test_tree_verify_uniforms_host_validation(kw, status):
 
 def test_tree_verify_workspace_size():
     f = ttv.lib().ttv_tree_verify_workspace_size
-    assert f(1, 4, 64, 32000) == 0           # stochastic needs none
-    assert f(1, 4, 64, 40000) == SZ_ERR      # vocabulary too large for on-chip residual
+    assert f(1, 4, 64, 32000) == 0           # stochastic: the residual on chip
+    assert f(1, 4, 64, 36864) == 0
+    assert f(1, 4, 64, 40000) == 4 * 40000 * 4          # beyond it: B*V floats
+    assert f(1, 3, 64, 1 << 18) == 3 * (1 << 18) * 4
+    assert f(1, 4, 64, 40001) == SZ_ERR      # V % 4 != 0
+    assert f(1, 4, 64, (1 << 18) + 4) == SZ_ERR
     assert f(0, 1, 64, 32000) > 0
     assert f(0, 1, 200, 32000) == SZ_ERR
     assert f(5, 1, 8, 32) == SZ_ERR
@@ -262,7 +270,9 @@ def verify_commit(**kw):
     (dict(llm=MIS), ttv.E_ALIGN), (dict(kt=MIS), ttv.E_ALIGN), (dict(ws=None), ttv.E_WORKSPACE),
     (dict(wsb=64), ttv.E_WORKSPACE), (dict(ws=MIS), ttv.E_ALIGN), (dict(mode=2), ttv.E_DTYPE),
     (dict(mode=1), ttv.E_NULL),                                  # stochastic without ssm
-    (dict(mode=1, ssm=A, V=40000), ttv.E_UNSUPPORTED),  # residual past on-chip memory
+    (dict(mode=1, ssm=A, V=40002), ttv.E_UNSUPPORTED),  # residual in memory: V % 4 == 0
+    (dict(mode=1, ssm=A, V=40000, ws=None), ttv.E_WORKSPACE),
+    (dict(mode=1, ssm=A, V=40000, wsb=64), ttv.E_WORKSPACE),
     (dict(mode=1, ssm=MIS), ttv.E_ALIGN),
 ])
 def test_tree_verify_commit_host_validation(kw, status):

@@ -131,6 +131,13 @@ def test_stochastic(seed):
     assert ref[1].max() >= 2
 
 
+def test_stochastic_large_vocabulary():
+    announce("verify varlen stochastic V=40000")
+    d = varlen_batch(33, mode="stochastic", B=6, N=30, V=40000, dmax=12, n=[30, 1, 0, 17, 2, 29])
+    ref = verify_both(d, ttv.STOCHASTIC)
+    assert ref[3].tolist() == [0, 0, ttv.E_SHAPE, 0, 0, 0]
+
+
 def test_verify_rejected_counts():
     announce("verify varlen bad counts")
     for mode, kw in ((ttv.GREEDY, {}), (ttv.STOCHASTIC, dict(mode="stochastic"))):

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 import token_tree_verification_attn_amd as ttv
 from gpu_case import announce, check_verify, to_dev
@@ -91,6 +92,57 @@ def test_stochastic_edge_cases(kw):
     d = synth.make(mss_spec(**kw), with_kv=False)
     check_verify(d)
     check_verify(d, uniforms=True)
+
+
+# Past 36864 entries the residual lives in the workspace (B*V floats) rather
+# than on chip: the first size past that, common vocabularies, the largest
+# supported, one-node trees (the bonus from the root's own row), stars whose
+# root tests many children, near-uniform rows and a ragged batch.
+@pytest.mark.parametrize("kw", [
+    dict(V=36868, B=2, N=8, seed=31), dict(V=50272, B=3, N=16, seed=32),
+    dict(V=65536, B=2, N=12, seed=33, prob_sigma=0.3), dict(V=131072, B=2, N=8, seed=34),
+    dict(V=1 << 18, B=1, N=6, seed=35), dict(N=1, V=40000, B=4, seed=36),
+    dict(N=65, tree="star", V=40000, B=2, seed=37), dict(V=152064, B=5, N=10, seed=38),
+    dict(N=128, dmax=127, max_children=3, V=40960, B=1, seed=39),
+])
+def test_stochastic_large_vocabulary(kw):
+    announce("verify stochastic large vocabulary %s" % kw)
+    d = synth.make(mss_spec(**kw), with_kv=False)
+    check_verify(d)
+
+
+def test_stochastic_large_vocabulary_accept_and_empty_residual():
+    """At V = 65536: a chain with p == q is accepted whole; a star whose root's
+    p is half its first child's q leaves an empty residual on rejection."""
+    announce("verify stochastic large vocabulary p == q / emptied residual")
+    d = synth.make(mss_spec(B=2, N=24, tree="chain", V=65536, seed=41), with_kv=False)
+    d["ssm"] = d["ssm"].copy()
+    d["ssm"][:, 1:] = d["llm"][:, :-1]
+    _, plen, _, _ = check_verify(d)
+    assert torch.all(plen == 24)
+    d = synth.make(mss_spec(B=16, N=6, V=65536, tree="star", seed=42), with_kv=False)
+    d["llm"] = d["llm"].copy()
+    d["llm"][:, 0] = 0.5 * d["ssm"][:, 1]
+    _, plen, _, _ = check_verify(d)
+    assert 0 < int((plen == 1).sum()) < 16
+
+
+def test_stochastic_large_vocabulary_repeated():
+    """The workspace keeps the previous launch's residuals: successive launches
+    (and steps) on it still match the oracle."""
+    d = synth.make(mss_spec(V=50272, B=3, N=16, seed=43), with_kv=False)
+    t = to_dev(d)
+    ws = torch.empty(ttv.tree_verify_workspace_size(ttv.STOCHASTIC, 3, 16, 50272),
+                     dtype=torch.uint8, device="cuda")
+    for step in range(4):
+        announce("verify stochastic large vocabulary step %d" % step)
+        got = ttv.tree_verify(ttv.STOCHASTIC, t["parents"], t["tokens"], t["llm"], t["ssm"],
+                              seed=d["seed"], step=step, workspace=ws)
+        ref = oracle.verify_mss_seeded(d["parents"], d["tokens"], d["llm"], d["ssm"], d["seed"],
+                                       step)
+        torch.cuda.synchronize()
+        for name, g, r in zip(("path", "path_len", "out_tokens", "status"), got, ref):
+            assert np.array_equal(g.cpu().numpy(), r), name
 
 
 @pytest.mark.parametrize("seed,step", [(0, 0), (2**64 - 1, 2**64 - 1), (1005, 2**63 + 1),

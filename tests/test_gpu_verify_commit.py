@@ -97,6 +97,8 @@ SHAPES = {
     # empty prefixes (L = Lmax = 0): the path lands at cache rows 0..
     "empty_prefix": dict(L=0, N=20, Hkv=4, Hq=8),
     "mss_empty_prefix": dict(mode="stochastic", L=0, N=20, Hkv=4, Hq=8, V=64),
+    # the residual in the workspace (V past 36864)
+    "mss_large_vocab": dict(mode="stochastic", B=3, N=24, Hkv=2, Hq=8, V=50272, L=(0, 200)),
 }
 
 

@@ -319,10 +319,42 @@ ttv_status ttv_tree_attn_varlen(ttv_dtype dt, int32_t B, int32_t N, int32_t Hq, 
                         dev_status, workspace, workspace_bytes, 0, 0, stream);
 }
 
+// Stochastic verification: no workspace while the residual fits the LDS; for
+// larger vocabularies (V % 4 == 0) the residual, B*V floats.
+static size_t mss_workspace_bytes(int32_t B, int32_t V) {
+  if (V <= kMssMaxVocab) return 0;
+  if (V > kMssGmMaxVocab || V % 4 != 0) return (size_t)-1;
+  return (size_t)B * (size_t)V * sizeof(float);
+}
+
+// The stochastic launch with the host checks of its residual: a vocabulary
+// beyond the LDS needs V % 4 == 0 and a 16-byte-aligned workspace of
+// mss_workspace_bytes.
+static ttv_status launch_mss_checked(int32_t B, int32_t N, int32_t V, const int32_t* parents,
+                                     const int32_t* tokens, const int32_t* n_nodes,
+                                     const float* llm, const float* ssm, const MssDraws& dr,
+                                     int32_t* path, int32_t* path_len, int32_t* out_tokens,
+                                     int32_t* dev_status, void* workspace,
+                                     size_t workspace_bytes, const CommitArgs& cm,
+                                     hipStream_t s) {
+  const size_t need = mss_workspace_bytes(B, V);
+  if (need == (size_t)-1) return TTV_E_UNSUPPORTED;
+  if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
+  float* gm_w = nullptr;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return TTV_E_WORKSPACE;
+    if (!aligned16(workspace)) return TTV_E_ALIGN;
+    gm_w = static_cast<float*>(workspace);
+  }
+  return launch_status(launch_verify_mss(B, N, V, parents, tokens, n_nodes, llm, ssm, dr,
+                                         LogitRows{}, path, path_len, out_tokens, dev_status,
+                                         gm_w, cm, s));
+}
+
 size_t ttv_tree_verify_workspace_size(ttv_verify_mode mode, int32_t B, int32_t N, int32_t V) {
   if (mode != TTV_GREEDY && mode != TTV_STOCHASTIC) return (size_t)-1;
   if (B < 1 || N < 1 || V < 1 || N > TTV_MAX_NODES) return (size_t)-1;
-  if (mode == TTV_STOCHASTIC) return V > kMssMaxVocab ? (size_t)-1 : 0;
+  if (mode == TTV_STOCHASTIC) return mss_workspace_bytes(B, V);
   if ((long)B * N > 0x7fffffffL) return (size_t)-1;
   return greedy_plan(B, N, V).ws_bytes;
 }
@@ -341,13 +373,10 @@ static ttv_status tree_verify_call(ttv_verify_mode mode, int32_t B, int32_t N, i
   if (N > TTV_MAX_NODES) return TTV_E_UNSUPPORTED;
   if ((long)B * N > 0x7fffffffL) return TTV_E_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (mode == TTV_STOCHASTIC) {
-    if (V > kMssMaxVocab) return TTV_E_UNSUPPORTED;
-    if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
-    return launch_status(launch_verify_mss(B, N, V, parents, tokens, n_nodes, llm, ssm,
-                                           MssDraws{nullptr, nullptr, seed, step}, LogitRows{}, path,
-                                           path_len, out_tokens, dev_status, CommitArgs{}, s));
-  }
+  if (mode == TTV_STOCHASTIC)
+    return launch_mss_checked(B, N, V, parents, tokens, n_nodes, llm, ssm,
+                              MssDraws{nullptr, nullptr, seed, step}, path, path_len, out_tokens,
+                              dev_status, workspace, workspace_bytes, CommitArgs{}, s);
   const GreedyPlan p = greedy_plan(B, N, V);
   if (p.splits > kMaxGridYZ) return TTV_E_UNSUPPORTED;
   if (!aligned16(llm)) return TTV_E_ALIGN;
@@ -391,7 +420,7 @@ ttv_status ttv_tree_verify_uniforms(int32_t B, int32_t N, int32_t V, const int32
   if (!aligned16(llm) || !aligned16(ssm)) return TTV_E_ALIGN;
   return launch_status(launch_verify_mss(B, N, V, parents, tokens, nullptr, llm, ssm,
                                          MssDraws{u_accept, u_bonus, 0, 0}, LogitRows{}, path, path_len,
-                                         out_tokens, dev_status, CommitArgs{},
+                                         out_tokens, dev_status, nullptr, CommitArgs{},
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -441,13 +470,11 @@ static ttv_status tree_verify_commit_call(
   const int elt = dt == TTV_BF16 ? 2 : 4;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (mode == TTV_STOCHASTIC) {
-    if (V > kMssMaxVocab) return TTV_E_UNSUPPORTED;
-    if (!aligned16(ssm)) return TTV_E_ALIGN;
     CommitArgs cm{D * elt / 16, Hkv, Lcap, Lmax, k_tree, v_tree, k_cache, v_cache,
                   cache_len_in, cache_len_out, committed_src};
-    return launch_status(launch_verify_mss(B, N, V, parents, tokens, n_nodes, llm, ssm,
-                                           MssDraws{nullptr, nullptr, seed, step}, LogitRows{}, path,
-                                           path_len, out_tokens, dev_status, cm, s));
+    return launch_mss_checked(B, N, V, parents, tokens, n_nodes, llm, ssm,
+                              MssDraws{nullptr, nullptr, seed, step}, path, path_len, out_tokens,
+                              dev_status, workspace, workspace_bytes, cm, s);
   }
   const GreedyPlan p = greedy_plan(B, N, V);
   if (p.splits > kMaxGridYZ) return TTV_E_UNSUPPORTED;
@@ -581,7 +608,7 @@ ttv_status ttv_tree_verify_logits(int32_t B, int32_t N, int32_t V, const int32_t
   return launch_status(launch_verify_mss(
       B, N, V, parents, tokens, n_nodes, llm_logits, ssm_logits,
       MssDraws{nullptr, nullptr, seed, step}, LogitRows{st_llm, st_ssm, probs_scale(temperature)},
-      path, path_len, out_tokens, dev_status, CommitArgs{}, s));
+      path, path_len, out_tokens, dev_status, nullptr, CommitArgs{}, s));
 }
 
 ttv_status ttv_kv_commit_inplace(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv, int32_t D,

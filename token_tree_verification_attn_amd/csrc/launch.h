@@ -140,14 +140,18 @@ struct LogitRows {
 };
 
 // Largest vocabulary the stochastic verifier holds in LDS; rows given as
-// logits need 16-byte rows of at most kMssLogitsMaxVocab entries.
+// logits need 16-byte rows of at most kMssLogitsMaxVocab entries.  Larger
+// vocabularies (V % 4 == 0, at most kMssGmMaxVocab) keep the residual in
+// global memory: gm_w, B*V floats of workspace, 16-byte aligned.
 constexpr int kMssMaxVocab = 36864;
 constexpr int kMssLogitsMaxVocab = 32768;
+constexpr int kMssGmMaxVocab = 1 << 18;
 hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                              const int32_t* tokens, const int32_t* n_nodes, const float* llm,
                              const float* ssm, const MssDraws& dr, const LogitRows& lr,
                              int32_t* path, int32_t* path_len, int32_t* out_tokens,
-                             int32_t* dev_status, const CommitArgs& cm, hipStream_t s);
+                             int32_t* dev_status, float* gm_w, const CommitArgs& cm,
+                             hipStream_t s);
 
 // ----------------------------------------------------------------- commit --
 hipError_t launch_kv_commit(int elt, int B, int N, int Hkv, int D, int Lcap,

@@ -516,6 +516,76 @@ __device__ __forceinline__ double mss_residual(const float* __restrict__ q, int 
   return part;
 }
 
+// Residual in global memory, for vocabularies beyond the LDS (16-byte rows,
+// V % 4 == 0, V <= kMssGmMaxVocab): request b's residual is w[v], v < V, in
+// the caller's workspace.  The waves keep contiguous ranges, wave w the
+// entries [w*S, (w+1)*S) with S = 256*CH and CH = ceil(V / (4*kMssThreads))
+// 16-byte chunks per lane (lane l: w*S + 4*(64*k + l)), so the per-wave sums
+// of a pass are again the masses of the ranges; a pass goes through
+// kMssGmBatch chunks at a time (loads of a batch issued together).
+constexpr int kMssGmBatch = 8;
+static_assert(kMssGmMaxVocab <= 4 * kMssThreads * 64,
+              "the final draw's lanes take one group each of a lane run (at most 64)");
+__device__ __forceinline__ int mss_gm_chunks(int V) {
+  return (V + 4 * kMssThreads - 1) / (4 * kMssThreads);
+}
+// w = row; returns this thread's sum of fx40d of the entries copied
+__device__ __forceinline__ double mss_gm_row_to_w(const float* __restrict__ row, int V, float* w,
+                                                  int CH) {
+  const int t = threadIdx.x, base = 256 * CH * (t >> 6) + 4 * (t & 63);
+  double part = 0.0;
+#pragma unroll 1
+  for (int k0 = 0; k0 < CH; k0 += kMssGmBatch) {
+    f32x4 r[kMssGmBatch];
+#pragma unroll
+    for (int j = 0; j < kMssGmBatch; ++j) {
+      const int v = base + 256 * (k0 + j);
+      r[j] = k0 + j < CH && v < V ? *reinterpret_cast<const f32x4*>(row + v) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kMssGmBatch; ++j) {
+      const int v = base + 256 * (k0 + j);
+      if (k0 + j < CH && v < V) {
+        *reinterpret_cast<f32x4*>(w + v) = r[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part += fx40d(r[j][e]);
+      }
+    }
+  }
+  return part;
+}
+// w = max(w - s*q, +0); returns this thread's sum of fx40d(w)
+__device__ __forceinline__ double mss_gm_residual(const float* __restrict__ q, int V, float s,
+                                                  float* w, int CH) {
+  const int t = threadIdx.x, base = 256 * CH * (t >> 6) + 4 * (t & 63);
+  double part = 0.0;
+#pragma unroll 1
+  for (int k0 = 0; k0 < CH; k0 += kMssGmBatch) {
+    f32x4 r[kMssGmBatch], x[kMssGmBatch];
+#pragma unroll
+    for (int j = 0; j < kMssGmBatch; ++j) {
+      const int v = base + 256 * (k0 + j);
+      const bool in = k0 + j < CH && v < V;
+      r[j] = in ? *reinterpret_cast<const f32x4*>(q + v) : f32x4{0.f, 0.f, 0.f, 0.f};
+      x[j] = in ? *reinterpret_cast<const f32x4*>(w + v) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kMssGmBatch; ++j) {
+      const int v = base + 256 * (k0 + j);
+      if (k0 + j < CH && v < V) {
+        f32x4 y = x[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[e] = clamp_pos(fmaf(-s, r[j][e], y[e]));
+          part += fx40d(y[e]);
+        }
+        *reinterpret_cast<f32x4*>(w + v) = y;
+      }
+    }
+  }
+  return part;
+}
+
 // Double-buffered row passes (16-byte rows, V <= 4 * kMssThreads * kMssPfChunks):
 // a row is requested into registers by mss_issue_row and consumed later, so
 // the next child's row can be in flight while the current one is used.
@@ -605,13 +675,17 @@ __device__ __forceinline__ double mss_residual_regs(const f32x4 (&r)[kMssPfChunk
 
 // LG: llm and ssm hold logits; st_llm / st_ssm [B*N] their rows' statistics
 // (ttv_tree_verify_logits), c = (float)(log2(e) / T).
-template <bool VEC, bool PF, bool LG>
+// GM: the residual lives in global memory (gm_w [B][V], see above), for
+// vocabularies beyond the LDS; single-buffered 16-byte rows only.
+template <bool VEC, bool PF, bool LG, bool GM>
 __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     int N, int V, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ n_nodes, const float* __restrict__ llm,
     const float* __restrict__ ssm, MssDraws dr, LogitRows lr,
     int32_t* __restrict__ path, int32_t* __restrict__ path_len,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status, CommitArgs cm) {
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status, float* __restrict__ gm_w,
+    CommitArgs cm) {
+  static_assert(!GM || (VEC && !PF && !LG), "the global residual takes single-buffered 16-byte rows");
   extern __shared__ __attribute__((aligned(16))) float s_w[];  // residual w, widx() layout
   __shared__ int32_t s_par[kMaxNodes];
   __shared__ int32_t s_tok[kMaxNodes];
@@ -622,9 +696,18 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   __shared__ uint64_t s_first_ok[2];
   __shared__ double s_redd[kMssThreads / 64];
   __shared__ int s_status, s_pick, s_len, s_nodes;
+  __shared__ float s_av[GM ? kMssWaves : 1];  // the all-zero fallback of the global residual
+  __shared__ int s_ai[GM ? kMssWaves : 1];
 
   const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
   const size_t rowN = (size_t)b * N;
+  // the residual: this request's slice of gm_w, or LDS
+  float* const wg = GM ? gm_w + (size_t)b * V : nullptr;
+  const int gmCH = GM ? mss_gm_chunks(V) : 0;
+  auto wref = [&](int v) -> float& {
+    if constexpr (GM) return wg[v];
+    else return s_w[widx(v)];
+  };
   // uniforms: drawn here from Philox (seed, step), or given by the caller
   const bool seeded = dr.u_accept == nullptr;
   // statistics of row u of llm / row c of ssm when they hold logits (read
@@ -729,10 +812,16 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
 
   // s_w = p_u.  The first barrier lets every thread finish reading the old
   // residual (the test that led here reads it), the second publishes p_u.
+  // (GM: with the masses of the waves' ranges in s_redd, left by the
+  // reduction whose barriers publish w)
   auto load_p_row = [&](int u) {
     __syncthreads();
-    mss_row_to_lds<VEC>(llm + (rowN + u) * V, V, s_w);
-    __syncthreads();
+    if constexpr (GM) {
+      block_sum_f64(mss_gm_row_to_w(llm + (rowN + u) * V, V, wg, gmCH), s_redd);
+    } else {
+      mss_row_to_lds<VEC>(llm + (rowN + u) * V, V, s_w);
+      __syncthreads();
+    }
   };
 
   // ---- the walk: control flow is uniform, decisions are recomputed by every
@@ -764,6 +853,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
         totals = true;
       } else {
         load_p_row(u);
+        totals = GM;
       }
       break;
     }
@@ -851,7 +941,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
         k1 &= k1 - 1;
       }
       if (!first) {  // c's test against w, mass s
-        const bool accept = s_rq[c] * s < s_w[widx(s_tok[c])];
+        const bool accept = s_rq[c] * s < wref(s_tok[c]);
         __syncthreads();  // every thread has read w[x] before it is updated below
         if (accept) {
           next = c;
@@ -860,7 +950,9 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       }
       first = false;
       // rejected: w = max(w - s*q_c, +0), s = its mass in 2^-40 units
-      const double part = mss_residual<VEC>(ssm + (rowN + c) * V, V, s, s_w);
+      double part;
+      if constexpr (GM) part = mss_gm_residual(ssm + (rowN + c) * V, V, s, wg, gmCH);
+      else part = mss_residual<VEC>(ssm + (rowN + c) * V, V, s, s_w);
       const double S = block_sum_f64(part, s_redd);  // its barriers publish s_w
       s = (float)(S * 0x1p-40);
       if (s == 0.0f) {  // empty residual: stop testing, sample from p_u
@@ -870,7 +962,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       }
     }
     if (next < 0) {  // bonus from the residual in s_w (or p_u)
-      totals = !emptied;
+      totals = GM || !emptied;
       break;
     }
     descend(next);
@@ -909,101 +1001,206 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   // 4: each 4-entry group is 16 aligned bytes of s_w), an exclusive scan over
   // the lanes gives each run's start, and the lane whose run crosses the
   // target walks its groups.  Masses are exact integers carried in doubles.
-  constexpr int kSpan = PF ? 256 * kMssPfChunks : kMssSpan;
-  if (!totals) {
-    double part = 0.0;
+  if constexpr (GM) {
+    // the same search over the wave ranges in global memory (span 256*CH,
+    // lane runs of 4*CH entries); the masses of the ranges are in s_redd
+    // (every exit of the walk leaves them there)
+    const int span = 256 * gmCH, P = 4 * gmCH;
+    double Sd = 0.0;
 #pragma unroll
-    for (int k = 0; k < kSpan / 256; ++k) {
-      const int v = kSpan * wave + 4 * (64 * k + (t & 63));
-      if (v < V) {
-        const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
+    for (int w = 0; w < kMssWaves; ++w) Sd += s_redd[w];
+    if (Sd > 0.0) {
+      const uint64_t S = (uint64_t)Sd, R = s_bonus[u];
+      const double T = (double)(R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24));  // floor(R*S/2^24)
+      double before = 0.0;
+      int ws = kMssWaves - 1;
+      bool found = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part += v + e < V ? fx40d(w4[e]) : 0.0;
-      }
-    }
-    block_sum_f64(part, s_redd);  // s_redd[w] = mass of wave w's range
-  }
-  // masses below 2^53: exact in doubles, compared as doubles
-  double Sd = 0.0;
-#pragma unroll
-  for (int w = 0; w < kMssWaves; ++w) Sd += s_redd[w];
-  if (Sd > 0.0) {
-    const uint64_t S = (uint64_t)Sd, R = s_bonus[u];
-    const double T = (double)(R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24));  // floor(R*S/2^24)
-    double before = 0.0;
-    int ws = kMssWaves - 1;
-    bool found = false;
-#pragma unroll
-    for (int w = 0; w < kMssWaves; ++w) {
-      const double g = s_redd[w];
-      if (!found && before + g > T) {
-        ws = w;
-        found = true;
-      } else if (!found) {
-        before += g;
-      }
-    }
-    if (wave == ws) {
-      constexpr int P = kSpan / 64, kG = P / 4;
-      const int lane = t & 63;
-      const int v_lo = min(V, ws * kSpan + lane * P), v_hi = min(V, v_lo + P);
-      double mine = 0.0, gsum[kG];  // gsum[i]: mass of the group at v_lo + 4i
-#pragma unroll
-      for (int i = 0; i < kG; ++i) {
-        const int v = v_lo + 4 * i;
-        double g = 0.0;
-        if (v < v_hi) {
-          const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) g += v + e < v_hi ? fx40d(w4[e]) : 0.0;
+      for (int w = 0; w < kMssWaves; ++w) {
+        const double g = s_redd[w];
+        if (!found && before + g > T) {
+          ws = w;
+          found = true;
+        } else if (!found) {
+          before += g;
         }
-        gsum[i] = g;
-        mine += g;
       }
-      double incl = mine;
+      if (wave == ws) {
+        const int lane = t & 63;
+        const int v_lo = min(V, ws * span + lane * P), v_hi = min(V, v_lo + P);
+        double mine = 0.0;
+#pragma unroll 4
+        for (int i = 0; i < gmCH; ++i) {
+          const int v = v_lo + 4 * i;
+          if (v < v_hi) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(wg + v);
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const double o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-      }
-      const double lo = before + (incl - mine), hi = before + incl;
-      if (lo <= T && T < hi) {
-        // the group that crosses T from the register sums, then its entries
-        // (unrolled with constant indices: gsum stays in registers; a group
-        // with no entries has mass 0 and never crosses)
-        double cum = lo;
-        int gi = kG - 1;
-        bool gfound = false;
-#pragma unroll
-        for (int i = 0; i < kG; ++i) {
-          if (!gfound && cum + gsum[i] > T) {
-            gi = i;
-            gfound = true;
-          } else if (!gfound) {
-            cum += gsum[i];
+            for (int e = 0; e < 4; ++e) mine += v + e < v_hi ? fx40d(w4[e]) : 0.0;
           }
         }
-        const int v = v_lo + 4 * gi;
-        const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
-        int pick = v_hi - 1;
+        double incl = mine;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (v + e < v_hi) {
-            cum += fx40d(w4[e]);
-            if (cum > T) {
-              pick = v + e;
-              break;
+        for (int d = 1; d < 64; d <<= 1) {
+          const double o = __shfl_up(incl, d);
+          if (lane >= d) incl += o;
+        }
+        const double lo = before + (incl - mine);
+        const uint64_t crossing = __ballot(lo <= T && T < before + incl);
+        if (crossing != 0ull) {
+          // the lanes take the groups of the crossing lane's run, one each
+          // (a run has CH <= 64 groups), and scan them
+          const int Lc = __ffsll((unsigned long long)crossing) - 1;
+          const double loL = __shfl(lo, Lc);
+          const int vloL = __shfl(v_lo, Lc), vhiL = __shfl(v_hi, Lc);
+          const int v = vloL + 4 * lane;
+          f32x4 w4 = {0.f, 0.f, 0.f, 0.f};
+          double g = 0.0;
+          if (lane < gmCH && v < vhiL) {
+            w4 = *reinterpret_cast<const f32x4*>(wg + v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g += v + e < vhiL ? fx40d(w4[e]) : 0.0;
+          }
+          double gin = g;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {
+            const double o = __shfl_up(gin, d);
+            if (lane >= d) gin += o;
+          }
+          double cum = loL + (gin - g);
+          if (cum <= T && T < loL + gin) {
+            int pick = vhiL - 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (v + e < vhiL) {
+                cum += fx40d(w4[e]);
+                if (cum > T) {
+                  pick = v + e;
+                  break;
+                }
+              }
+            }
+            s_pick = pick;
+          }
+        }
+      }
+    } else {  // nothing representable left: the largest entry (lowest index on ties)
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+      for (int v = t; v < V; v += kMssThreads)
+        if (wg[v] > bv) {
+          bv = wg[v];
+          bi = v;
+        }
+      wave_allargmax(bv, bi);
+      if ((t & 63) == 0) {
+        s_av[wave] = bv;
+        s_ai[wave] = bi;
+      }
+      __syncthreads();
+      if (t == 0) {
+        float v0 = s_av[0];
+        int i0 = s_ai[0];
+        for (int w = 1; w < kMssWaves; ++w) argmax_take(v0, i0, s_av[w], s_ai[w]);
+        s_pick = i0;
+      }
+    }
+  } else {
+    constexpr int kSpan = PF ? 256 * kMssPfChunks : kMssSpan;
+    if (!totals) {
+      double part = 0.0;
+  #pragma unroll
+      for (int k = 0; k < kSpan / 256; ++k) {
+        const int v = kSpan * wave + 4 * (64 * k + (t & 63));
+        if (v < V) {
+          const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) part += v + e < V ? fx40d(w4[e]) : 0.0;
+        }
+      }
+      block_sum_f64(part, s_redd);  // s_redd[w] = mass of wave w's range
+    }
+    // masses below 2^53: exact in doubles, compared as doubles
+    double Sd = 0.0;
+  #pragma unroll
+    for (int w = 0; w < kMssWaves; ++w) Sd += s_redd[w];
+    if (Sd > 0.0) {
+      const uint64_t S = (uint64_t)Sd, R = s_bonus[u];
+      const double T = (double)(R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24));  // floor(R*S/2^24)
+      double before = 0.0;
+      int ws = kMssWaves - 1;
+      bool found = false;
+  #pragma unroll
+      for (int w = 0; w < kMssWaves; ++w) {
+        const double g = s_redd[w];
+        if (!found && before + g > T) {
+          ws = w;
+          found = true;
+        } else if (!found) {
+          before += g;
+        }
+      }
+      if (wave == ws) {
+        constexpr int P = kSpan / 64, kG = P / 4;
+        const int lane = t & 63;
+        const int v_lo = min(V, ws * kSpan + lane * P), v_hi = min(V, v_lo + P);
+        double mine = 0.0, gsum[kG];  // gsum[i]: mass of the group at v_lo + 4i
+  #pragma unroll
+        for (int i = 0; i < kG; ++i) {
+          const int v = v_lo + 4 * i;
+          double g = 0.0;
+          if (v < v_hi) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) g += v + e < v_hi ? fx40d(w4[e]) : 0.0;
+          }
+          gsum[i] = g;
+          mine += g;
+        }
+        double incl = mine;
+  #pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const double o = __shfl_up(incl, d);
+          if (lane >= d) incl += o;
+        }
+        const double lo = before + (incl - mine), hi = before + incl;
+        if (lo <= T && T < hi) {
+          // the group that crosses T from the register sums, then its entries
+          // (unrolled with constant indices: gsum stays in registers; a group
+          // with no entries has mass 0 and never crosses)
+          double cum = lo;
+          int gi = kG - 1;
+          bool gfound = false;
+  #pragma unroll
+          for (int i = 0; i < kG; ++i) {
+            if (!gfound && cum + gsum[i] > T) {
+              gi = i;
+              gfound = true;
+            } else if (!gfound) {
+              cum += gsum[i];
             }
           }
+          const int v = v_lo + 4 * gi;
+          const f32x4 w4 = *reinterpret_cast<const f32x4*>(s_w + widx(v));
+          int pick = v_hi - 1;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (v + e < v_hi) {
+              cum += fx40d(w4[e]);
+              if (cum > T) {
+                pick = v + e;
+                break;
+              }
+            }
+          }
+          s_pick = pick;
         }
-        s_pick = pick;
       }
+    } else if (t == 0) {  // nothing representable left: the largest entry
+      int bi = 0;
+      for (int v = 1; v < V; ++v)
+        if (s_w[widx(v)] > s_w[widx(bi)]) bi = v;
+      s_pick = bi;
     }
-  } else if (t == 0) {  // nothing representable left: the largest entry
-    int bi = 0;
-    for (int v = 1; v < V; ++v)
-      if (s_w[widx(v)] > s_w[widx(bi)]) bi = v;
-    s_pick = bi;
   }
   __syncthreads();
   const int bonus = s_pick;
@@ -1040,20 +1237,27 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                              const int32_t* tokens, const int32_t* n_nodes, const float* llm,
                              const float* ssm, const MssDraws& dr, const LogitRows& lr,
                              int32_t* path, int32_t* path_len, int32_t* out_tokens,
-                             int32_t* dev_status, const CommitArgs& cm, hipStream_t s) {
+                             int32_t* dev_status, float* gm_w, const CommitArgs& cm,
+                             hipStream_t s) {
+  if (V > kMssMaxVocab) {  // the residual in global memory (host checks: V % 4 == 0, gm_w)
+    hipLaunchKernelGGL((mss_kernel<true, false, false, true>), dim3(B), dim3(kMssThreads), 0, s, N,
+                       V, parents, tokens, n_nodes, llm, ssm, dr, lr, path, path_len, out_tokens,
+                       dev_status, gm_w, cm);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)(V + 4 * (V >> 7) + 4) * sizeof(float);  // widx(V - 1) + 1, 16-byte padded
   const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(llm) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(ssm) & 15) == 0;
   const bool lg = lr.st_llm != nullptr;
-  auto kern = lg ? mss_kernel<true, true, true>
-                 : (!vec ? mss_kernel<false, false, false>
-                         : (V <= kMssPfMaxVocab ? mss_kernel<true, true, false>
-                                                : mss_kernel<true, false, false>));
+  auto kern = lg ? mss_kernel<true, true, true, false>
+                 : (!vec ? mss_kernel<false, false, false, false>
+                         : (V <= kMssPfMaxVocab ? mss_kernel<true, true, false, false>
+                                                : mss_kernel<true, false, false, false>));
   constexpr int kMaxLds = (kMssMaxVocab + 4 * (kMssMaxVocab >> 7) + 4) * (int)sizeof(float);
   hipError_t e = lds_limit_once(reinterpret_cast<const void*>(kern), kMaxLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(B), dim3(kMssThreads), lds, s, N, V, parents, tokens, n_nodes, llm,
-                     ssm, dr, lr, path, path_len, out_tokens, dev_status, cm);
+                     ssm, dr, lr, path, path_len, out_tokens, dev_status, nullptr, cm);
   return hipGetLastError();
 }
 
