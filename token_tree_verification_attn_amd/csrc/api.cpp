@@ -39,7 +39,7 @@ ttv_status attn_plan(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, int Lma
   const long pairs = (long)B * Hkv;
   if (pairs > kMaxGridYZ) return TTV_E_UNSUPPORTED;
   // Workgroups that fit on the chip at once: one matrix-core workgroup per CU
-  // (its copy ring takes 128 KB of LDS), two FMA workgroups; 256 CUs.
+  // (up to 256 VGPRs per lane), two FMA workgroups; 256 CUs.
   long slots = 512;
   if (p->mfma) {
     if (rpb_hint) {

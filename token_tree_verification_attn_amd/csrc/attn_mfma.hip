@@ -177,7 +177,7 @@ struct MfmaCfg {
   // immediate (no address arithmetic in the tile loop)
   static constexpr int LDS_BYTES = NST * 2 * TILE_BYTES;
   static constexpr int V_REGION = NST * TILE_BYTES;
-  // one workgroup per CU: the 4-deep ring takes 128 KB of LDS
+  // one workgroup per CU (the matrix-core shapes take up to 256 VGPRs per lane)
   static constexpr int MIN_BLOCKS = 1;
   static_assert(LOADS >= 1 && TILE_BYTES % (16 * kThreads) == 0, "tile / loads");
   static_assert(NST >= 2 && NST <= 4, "ring depth");
@@ -800,7 +800,12 @@ static hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
 }
 
 // rows per workgroup -> shape: 64 rows = 4 waves x 16 queries, 128 = 8 x 16
-// and 256 = 8 x 32; each one workgroup per CU with a 4-deep 128 KB ring.
+// and 256 = 8 x 32; each one workgroup per CU.  Head dimension 128 takes a
+// 3-stage ring (96 KB, two tiles in flight during a tile's math): on MI355X a
+// fourth stage made every workload slower (long-context 1024 rows x 32768
+// keys per kv head: 545 vs 523 us; 8 requests of 1024..4096 keys: 38-41 vs
+// 35-36 us; 64 rows x 512 keys: 17.4 vs 15.7 us), and two stages ran as fast
+// as three.
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.D == 64) {
     switch (a.rows_per_block) {
@@ -810,9 +815,9 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
     }
   }
   switch (a.rows_per_block) {
-    case 64: return launch_cfg<128, 16, 4, 4>(a, s);
-    case 128: return launch_cfg<128, 16, 8, 4>(a, s);
-    default: return launch_cfg<128, 32, 8, 4>(a, s);
+    case 64: return launch_cfg<128, 16, 4, 3>(a, s);
+    case 128: return launch_cfg<128, 16, 8, 3>(a, s);
+    default: return launch_cfg<128, 32, 8, 3>(a, s);
   }
 }
 
