@@ -231,30 +231,46 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
 // Split-KV combine: o = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),
 // M = max_c m_c, over the chunks that hold keys of request b (chunk 0 always
 // does: it owns the tree keys, and every node sees at least itself; with the
-// balanced split every chunk of the request holds keys).
-// One wavefront per query row; lanes cover D.
+// balanced split every chunk of the request holds keys).  A lane takes 16
+// bytes of a row's partial (LPR lanes per row, 64/LPR rows per wavefront);
+// the partials of kCombineBatch chunks are requested together and merged
+// with a running max, so a row costs about two memory round trips for the
+// usual few chunks.  (bf16 partials are each chunk's normalised output,
+// weighted by l_c 2^(m_c - M); fp32 partials are the unnormalised sums.)
 // =========================================================================
+constexpr int kCombineBatch = 4;
+constexpr int kCombineWaves = 4;
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  constexpr int E = D / 64;
+struct CombineShape {
+  static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane
+  static constexpr int LPR = D / EPL;               // lanes per row
+  static constexpr int RPW = 64 / LPR;              // rows per wavefront
+  static constexpr int RPB = kCombineWaves * RPW;   // rows per workgroup
+  static_assert(D % EPL == 0 && 64 % LPR == 0, "combine lanes");
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kCombineWaves) void attn_combine_kernel(AttnArgs a) {
+  using Sh = CombineShape<T, D>;
+  constexpr int EPL = Sh::EPL;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bh = blockIdx.y;
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
-  const int r = blockIdx.x * 4 + wave;
+  const int col = (lane % Sh::LPR) * EPL;
+  const int r = (blockIdx.x * kCombineWaves + wave) * Sh::RPW + lane / Sh::LPR;
   const int N = a.N, G = a.G, R = a.R;
   const int L = a.cache_len[b];
   const int n_raw = nodes_raw(a.n_nodes, b, N);
   const int nU = nodes_used(n_raw, N);
-  const bool tree_ok = wave_tree_valid(a.parents + (size_t)b * N, nU);
+  const bool tree_ok = wave_tree_valid(a.parents + (size_t)b * N, nU);  // every lane takes part
   if (r >= R) return;
   const int i = r / G, hq = h * G + (r - i * G);
-  T* o = static_cast<T*>(a.out) + (((size_t)b * N + i) * a.Hq + hq) * D;
-  float* lse = a.lse ? a.lse + ((size_t)b * N + i) * a.Hq + hq : nullptr;
+  T* o = static_cast<T*>(a.out) + (((size_t)b * N + i) * a.Hq + hq) * D + col;
+  float* lse = a.lse && col == 0 ? a.lse + ((size_t)b * N + i) * a.Hq + hq : nullptr;
   // a rejected request or a padding node's row: zeros
   if (request_status(tree_ok, L, a.Lmax, n_raw, N) != TTV_OK || i >= nU) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) store_elt<T>(o + lane + 64 * e, 0.f);
-    if (lane == 0 && lse) *lse = 0.f;
+    *reinterpret_cast<u32x4*>(o) = u32x4{0u, 0u, 0u, 0u};
+    if (lse) *lse = 0.f;
     return;
   }
   int used = 1;
@@ -265,31 +281,61 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     while (used < a.chunks && used * a.chunk_keys < L) ++used;
   }
   const size_t base = (size_t)bh * a.chunks * R + r;
-  float M = -INFINITY;
-  for (int c = 0; c < used; ++c) M = fmaxf(M, a.ws_ml[(base + (size_t)c * R) * 2]);
-  float lsum = 0.f, acc[E];
+  const T* part = reinterpret_cast<const T*>(a.ws_acc);
+  float M = -INFINITY, lsum = 0.f, acc[EPL];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int c = 0; c < used; ++c) {
-    const size_t pr = base + (size_t)c * R;
-    const float w = __builtin_amdgcn_exp2f(a.ws_ml[pr * 2] - M);
-    if constexpr (sizeof(T) == 2) {
-      // bf16 partials hold the chunk's normalised output: weight l * w
-      const uint16_t* wsb = reinterpret_cast<const uint16_t*>(a.ws_acc);
-      const float lw = a.ws_ml[pr * 2 + 1] * w;
-      lsum += lw;
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int c0 = 0; c0 < used; c0 += kCombineBatch) {
+    // chunks past the last re-read the last one (from cache) with weight 0
+    float2 ml[kCombineBatch];
+    u32x4 pv[kCombineBatch];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(bf16_to_f32(wsb[pr * D + lane + 64 * e]), lw, acc[e]);
-    } else {
-      lsum = fmaf(a.ws_ml[pr * 2 + 1], w, lsum);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(a.ws_acc[pr * D + lane + 64 * e], w, acc[e]);
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const size_t pr = base + (size_t)min(c0 + k, used - 1) * R;
+      ml[k] = *reinterpret_cast<const float2*>(a.ws_ml + pr * 2);
+      pv[k] = *reinterpret_cast<const u32x4*>(part + pr * D + col);
     }
+    // chunk 0 (in the first batch) has a finite max, so M is finite after it
+    float mb = M;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k)
+      if (c0 + k < used) mb = fmaxf(mb, ml[k].x);
+    const float sc = __builtin_amdgcn_exp2f(M - mb);  // 0 for the first batch
+    lsum *= sc;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      if (c0 + k >= used) continue;
+      const float w = __builtin_amdgcn_exp2f(ml[k].x - mb);
+      if constexpr (sizeof(T) == 2) {
+        const float lw = ml[k].y * w;
+        lsum += lw;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 2) {
+          const uint32_t x = pv[k][e / 2];
+          acc[e] = fmaf(bf16_to_f32((uint16_t)(x & 0xffffu)), lw, acc[e]);
+          acc[e + 1] = fmaf(bf16_to_f32((uint16_t)(x >> 16)), lw, acc[e + 1]);
+        }
+      } else {
+        lsum = fmaf(ml[k].y, w, lsum);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(__uint_as_float(pv[k][e]), w, acc[e]);
+      }
+    }
+    M = mb;
   }
   const float inv = 1.f / lsum;
+  u32x4 ov;
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) store_elt<T>(o + lane + 64 * e, acc[e] * inv);
-  if (lane == 0 && lse) *lse = (M + __log2f(lsum)) * kLn2;
+    for (int e = 0; e < EPL; e += 2) ov[e / 2] = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ov[e] = __float_as_uint(acc[e] * inv);
+  }
+  *reinterpret_cast<u32x4*>(o) = ov;
+  if (lse) *lse = (M + __log2f(lsum)) * kLn2;
 }
 
 // ------------------------------------------------------------- launchers --
@@ -309,14 +355,20 @@ hipError_t launch_attn_fma(const AttnArgs& a, bool bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int D>
+static void combine_launch(const AttnArgs& a, hipStream_t s) {
+  constexpr int RPB = CombineShape<T, D>::RPB;
+  const dim3 grid((a.R + RPB - 1) / RPB, a.B * a.Hkv);
+  hipLaunchKernelGGL((attn_combine_kernel<T, D>), grid, dim3(64 * kCombineWaves), 0, s, a);
+}
+
 hipError_t launch_attn_combine(const AttnArgs& a, bool bf16, hipStream_t s) {
-  const dim3 grid((a.R + 3) / 4, a.B * a.Hkv);
   if (bf16) {
-    if (a.D == 64) hipLaunchKernelGGL((attn_combine_kernel<uint16_t, 64>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_combine_kernel<uint16_t, 128>), grid, dim3(256), 0, s, a);
+    if (a.D == 64) combine_launch<uint16_t, 64>(a, s);
+    else combine_launch<uint16_t, 128>(a, s);
   } else {
-    if (a.D == 64) hipLaunchKernelGGL((attn_combine_kernel<float, 64>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_combine_kernel<float, 128>), grid, dim3(256), 0, s, a);
+    if (a.D == 64) combine_launch<float, 64>(a, s);
+    else combine_launch<float, 128>(a, s);
   }
   return hipGetLastError();
 }
