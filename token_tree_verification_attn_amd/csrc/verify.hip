@@ -634,8 +634,21 @@ template <bool LG>
 __device__ __forceinline__ double mss_regs_to_lds(const f32x4 (&r)[kMssPfChunks], int V, float* s_w,
                                                   const RowStats& st, float c) {
   const int t = threadIdx.x;
-  double part = 0.0;
   f32x4* wp = reinterpret_cast<f32x4*>(s_w + mss_slot0<kMssPfChunks>(t));
+  if constexpr (!LG) {
+    // probabilities: every chunk of the span is written (the row's loads
+    // read zeros past V, and the LDS holds the whole span), so w = 0 there
+    // and no chunk needs a branch
+    double part[2] = {0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < kMssPfChunks; ++j) {
+      wp[66 * j] = r[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[e >> 1] += fx40d(r[j][e]);
+    }
+    return part[0] + part[1];
+  }
+  double part = 0.0;
 #pragma unroll
   for (int j = 0; j < kMssPfChunks; ++j) {
     const int v = mss_chunk_v<kMssPfChunks>(t, j);
@@ -655,8 +668,27 @@ template <bool LG>
 __device__ __forceinline__ double mss_residual_regs(const f32x4 (&r)[kMssPfChunks], int V, float s,
                                                     float* s_w, const RowStats& st, float c) {
   const int t = threadIdx.x;
-  double part = 0.0;
   f32x4* wp = reinterpret_cast<f32x4*>(s_w + mss_slot0<kMssPfChunks>(t));
+  if constexpr (!LG) {
+    // the whole span, without branches: past V both w and q are 0 (see
+    // mss_regs_to_lds), so those entries stay 0.  The LDS reads go out
+    // together, and the exact integer masses go to two sums.
+    f32x4 w[kMssPfChunks];
+#pragma unroll
+    for (int j = 0; j < kMssPfChunks; ++j) w[j] = wp[66 * j];
+    double part[2] = {0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < kMssPfChunks; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[j][e] = clamp_pos(fmaf(-s, r[j][e], w[j][e]));
+        part[e >> 1] += fx40d(w[j][e]);
+      }
+      wp[66 * j] = w[j];
+    }
+    return part[0] + part[1];
+  }
+  double part = 0.0;
 #pragma unroll
   for (int j = 0; j < kMssPfChunks; ++j)
     if (mss_chunk_v<kMssPfChunks>(t, j) < V) {
@@ -1245,10 +1277,13 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                        dev_status, gm_w, cm);
     return hipGetLastError();
   }
-  const size_t lds = (size_t)(V + 4 * (V >> 7) + 4) * sizeof(float);  // widx(V - 1) + 1, 16-byte padded
   const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(llm) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(ssm) & 15) == 0;
   const bool lg = lr.st_llm != nullptr;
+  // widx(V - 1) + 1, 16-byte padded; the double-buffered walk over
+  // probabilities keeps its whole span (kMssPfMaxVocab entries) in LDS
+  const int Vl = (vec && !lg && V <= kMssPfMaxVocab) ? kMssPfMaxVocab : V;
+  const size_t lds = (size_t)(Vl + 4 * (Vl >> 7) + 4) * sizeof(float);
   auto kern = lg ? mss_kernel<true, true, true, false>
                  : (!vec ? mss_kernel<false, false, false, false>
                          : (V <= kMssPfMaxVocab ? mss_kernel<true, true, false, false>
