@@ -5,12 +5,13 @@
 // sampling; [SSD] §4 samples with top-k, k = 50, at T = 1).  The arithmetic
 // is fixed to the bit (softmax_exact.h).
 //
-// One 1024-thread workgroup per row.  A row of up to 32768 logits is requested
-// whole (8 16-byte loads per thread) and kept in registers with its 2^t
-// values; a longer one is streamed, once per pass.
+// One workgroup per row (1024 threads, or 512 with top-k/top-p).  A row of
+// up to 32768 logits is requested whole (8 or 16 16-byte loads per thread)
+// and kept in registers with its 2^t values; a longer one is streamed, once
+// per pass.
 //  * top-k: the k-th entry in the order (higher logit, then lower token id)
-//    is found as in tree expansion: the smallest over the 16 waves of each
-//    wave's ceil(k/16)-th largest per-thread maximum bounds it from below,
+//    is found as in tree expansion: the smallest over the W waves of each
+//    wave's ceil(k/W)-th largest per-thread maximum bounds it from below,
 //    the entries at or above that bound are gathered in LDS, and the one that
 //    exactly k-1 gathered entries rank before is it (a row whose ties
 //    overflow the buffer takes k rounds of a block arg-max instead).
@@ -36,9 +37,17 @@ namespace ttv {
 
 namespace {
 
-constexpr int kProbThreads = 1024;  // 512 measured 3.5% slower with top-50
-constexpr int kProbWaves = kProbThreads / 64;
-constexpr int kProbRegQuads = 8;
+// Threads per row: 1024 without selection (8 16-byte loads each); with
+// top-k/top-p, 512 (16 loads each), whose 256 VGPRs per lane hold the row's
+// logits and exponentials (1024 threads leave 128, and that kernel spilled
+// to scratch memory).
+template <bool SEL>
+struct ProbShape {
+  static constexpr int kThreads = SEL ? 512 : 1024;
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kRegQuads = 32768 / 4 / kThreads;  // rows up to 32768 stay in registers
+};
+constexpr int kProbMaxWaves = 16;
 constexpr int kProbCandidates = 2048;
 constexpr int kPBins = 2048;        // top-p histogram bins
 constexpr int kPGather = 1024;      // top-p: tokens ranked in LDS at once
@@ -73,19 +82,22 @@ __device__ __forceinline__ uint32_t p_order_key(float z) {
 // set (the logits become their exponentials), and two workgroups share a
 // CU, so one's loads are in flight while the other reduces.
 template <bool VEC, bool SEL>
-__global__ __launch_bounds__(kProbThreads) __attribute__((amdgpu_waves_per_eu(SEL ? 4 : 8)))
+__global__ __launch_bounds__(ProbShape<SEL>::kThreads) __attribute__((amdgpu_waves_per_eu(SEL ? 2 : 8)))
 void probs_kernel(int V, float c, int topk,
                                                              uint32_t top_p24,
                                                              const float* __restrict__ logits,
                                                              float* __restrict__ probs,
                                                              RowStats* __restrict__ stats) {
-  __shared__ float s_red[kProbWaves];
-  __shared__ uint64_t s_red64[kProbWaves];
+  constexpr int kProbThreads = ProbShape<SEL>::kThreads;
+  constexpr int kProbWaves = ProbShape<SEL>::kWaves;
+  constexpr int kProbRegQuads = ProbShape<SEL>::kRegQuads;
+  __shared__ float s_red[kProbMaxWaves];
+  __shared__ uint64_t s_red64[kProbMaxWaves];
   __shared__ float s_cv[kProbCandidates];
   __shared__ int s_ci[kProbCandidates];
   __shared__ uint64_t s_hist[kPBins];
-  __shared__ float s_wv[kProbWaves];
-  __shared__ int s_wi[kProbWaves];
+  __shared__ float s_wv[kProbMaxWaves];
+  __shared__ int s_wi[kProbMaxWaves];
   __shared__ int s_cnt, s_bin, s_done;
   __shared__ float s_thr, s_zt;
   __shared__ int s_it;
@@ -164,6 +176,18 @@ void probs_kernel(int V, float c, int topk,
 #pragma unroll
       for (int e = 0; e < 4; ++e) RE(u)[e] = exp2_taylor((rq[u][e] - m) * c);
   }
+  // Per-entry values that a loop over passes would otherwise hoist out of
+  // it (order keys, 64-bit masses: three registers per entry, which spilled)
+  // are kept inside by declaring the row's registers rewritten (no code).
+  auto pin_row = [&]() {
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < kProbRegQuads; ++u) {
+        asm volatile("" : "+v"(rq[u]));
+        if constexpr (SEL) asm volatile("" : "+v"(RE(u)));
+      }
+    }
+  };
   auto visit_ze = [&](auto visit) {
     if (in_regs) {
 #pragma unroll
@@ -183,9 +207,9 @@ void probs_kernel(int V, float c, int topk,
   float kv = -INFINITY;
   int ki = INT_MAX;
   if (SEL && topk > 0 && topk < V) {
-    // a lower bound of the k-th entry: every wave takes the ceil(k/16)-th
-    // largest of its 64 per-thread maxima, and the smallest of those has at
-    // least 16*ceil(k/16) >= k entries of the row at or above it
+    // a lower bound of the k-th entry: every wave takes the ceil(k/W)-th
+    // largest of its 64 per-thread maxima (W waves), and the smallest of
+    // those has at least W*ceil(k/W) >= k entries of the row at or above it
     if (tid == 0) s_cnt = 0;
     {
       const int kw = (topk + kProbWaves - 1) / kProbWaves;
@@ -296,6 +320,7 @@ void probs_kernel(int V, float c, int topk,
     if (tid == 0) s_done = 0;
     __syncthreads();
     for (int it = 0; it < 64; ++it) {
+      pin_row();
       if (lo == hi) {
         // every candidate has the logit lo, hence the same mass mu: the
         // crossing is the c-th lowest token id among them, c = ceil((need -
@@ -467,7 +492,8 @@ hipError_t launch_probs(int R, int V, float T, int topk, float top_p, const floa
   const bool sel = (topk > 0 && topk < V) || p24 != 0u;
   auto kern = vec ? (sel ? probs_kernel<true, true> : probs_kernel<true, false>)
                   : (sel ? probs_kernel<false, true> : probs_kernel<false, false>);
-  hipLaunchKernelGGL(kern, dim3(R), dim3(kProbThreads), 0, s, V, c, topk, p24, logits, probs, stats);
+  const int threads = sel ? ProbShape<true>::kThreads : ProbShape<false>::kThreads;
+  hipLaunchKernelGGL(kern, dim3(R), dim3(threads), 0, s, V, c, topk, p24, logits, probs, stats);
   return hipGetLastError();
 }
 
