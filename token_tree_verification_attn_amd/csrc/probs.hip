@@ -56,17 +56,7 @@ __device__ __forceinline__ bool p_ranks_before(float v, int i, float bv, int bi)
   return v > bv || (v == bv && i < bi);
 }
 
-__device__ __forceinline__ void p_wave_argmax(float& bv, int& bi) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(bv, m);
-    const int oi = __shfl_xor(bi, m);
-    if (p_ranks_before(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-}
+__device__ __forceinline__ void p_wave_argmax(float& bv, int& bi) { wave_allargmax(bv, bi); }
 
 // An unsigned key of a logit that orders like the logit (-0 taken as +0, so
 // that equal logits have equal keys).
@@ -215,9 +205,7 @@ void probs_kernel(int V, float c, int topk,
       const int kw = (topk + kProbWaves - 1) / kProbWaves;
       float a = tmax, wm = -INFINITY;
       for (int r = 0; r < kw; ++r) {  // remove one copy of the wave's largest per round
-        wm = a;
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) wm = fmaxf(wm, __shfl_xor(wm, s));
+        wm = wave_allmax_f32(a);
         const uint64_t has = __ballot(a == wm);
         if (lane == __ffsll((unsigned long long)has) - 1) a = -INFINITY;
       }
@@ -246,12 +234,15 @@ void probs_kernel(int V, float c, int topk,
     if (cnt <= kProbCandidates) {
       // the gathered pairs are distinct (distinct ids), so their ranks are
       // 0..cnt-1 and exactly one candidate has rank topk-1 (cnt >= topk)
-      for (int q = tid; q < cnt; q += kProbThreads) {
+      // (wave w ranks candidates w, w + W, ...; its lanes compare one with
+      // every 64th of the others, and a register-only wave sum counts)
+      for (int q = wave; q < cnt; q += kProbWaves) {
         const float z = s_cv[q];
         const int i = s_ci[q];
         int rank = 0;
-        for (int u = 0; u < cnt; ++u) rank += p_ranks_before(s_cv[u], s_ci[u], z, i) ? 1 : 0;
-        if (rank == topk - 1) {
+        for (int u = lane; u < cnt; u += 64) rank += p_ranks_before(s_cv[u], s_ci[u], z, i) ? 1 : 0;
+        rank = wave_allsum_i32(rank);
+        if (rank == topk - 1 && lane == 0) {
           s_wv[0] = z;
           s_wi[0] = i;
         }
