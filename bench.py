@@ -37,9 +37,12 @@ launch (flops for c4, KV bytes otherwise) over its average launch time (HIP
 events on the launch stream); cpu_baseline = the CPU oracle timed on a
 bounded sample of the same workload on all host cores and on one (the
 oracle is test infrastructure; it is imported only here, for that leg).
+warm_us: the medians of tree_attn and of the whole step on one input copy
+run back to back (whatever of it fits stays in L2/MALL); the metric is the
+rotated, cold measurement.
 sub_workloads (--also, default c3,c5): the same measurement of the
 HBM-bound workloads after the main one, compact (value, step and stage
-medians, roofline), without a CPU leg.
+medians, warm medians, roofline), without a CPU leg.
 """
 from __future__ import annotations
 
@@ -397,6 +400,7 @@ def main():
                 "steps": sub["steps"], "config": sub["config"],
                 "stage_us_median": {k: (v["median"] if v else None)
                                     for k, v in sub["stage_us"].items()},
+                "warm_us": sub["warm_us"],
                 "roofline": {k: r[k] for k in ("bound", "achieved", "peak", "unit", "frac",
                                                "traffic", "avg_launch_us")}}
     if args.cpu_budget > 0:
@@ -445,6 +449,9 @@ def measure(workload, args, dev):
     t_verify = stage(step.verify)
     t_commit = stage(step.commit)
     t_fused = stage(step.verify_commit) if step.fused else None
+    # warm: one input copy back to back (what of it fits stays in the caches)
+    t_warm_attn = summary(timed_steps([lambda: step.attn(copies[0])], args.steps, stream))
+    t_warm_step = summary(timed_steps([lambda: one_step(copies[0])], args.steps, stream))
     st = torch.stack([c.st for c in copies]).cpu()
     assert int(st.abs().sum()) == 0, "a request was rejected: %s" % st
 
@@ -495,6 +502,9 @@ def measure(workload, args, dev):
         "stage_us": {"tree_attn": us(t_attn), "tree_verify": us(t_verify),
                      "kv_commit": us(t_commit), "tree_verify_commit": us(t_fused)},
         "step_us": us(t_step),
+        "warm_us": {"tree_attn_median": t_warm_attn["median"] * 1e3,
+                    "step_median": t_warm_step["median"] * 1e3,
+                    "inputs": "one copy, back to back (the metric is the rotated, cold one)"},
         "roofline": roof,
     }
     return res, d

@@ -58,6 +58,8 @@ def test_default_bench_line():
     r = d["roofline"]
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
     assert r["per_launch_algorithmic_unit"] == "flop" and 0 < r["kv_frac_of_hbm_peak"] < 1
+    # warm medians beside the cold metric
+    assert d["warm_us"]["tree_attn_median"] > 0 and d["warm_us"]["step_median"] > 0
     # the HBM-bound workloads ride along in compact form
     assert sorted(d["sub_workloads"]) == ["c3", "c5"]
     for w, sub in d["sub_workloads"].items():
@@ -66,6 +68,7 @@ def test_default_bench_line():
         assert sub["value"] == pytest.approx(c["B"] * c["N"] / (sub["ms_per_step"] * 1e-3), rel=1e-6)
         rs = sub["roofline"]
         assert rs["bound"] == "hbm" and 0 < rs["frac"] < 1 and rs["peak"] == 8000.0
+        assert sub["warm_us"]["tree_attn_median"] > 0
 
 
 def test_stochastic_bench_line():

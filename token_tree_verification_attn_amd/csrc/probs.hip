@@ -88,7 +88,7 @@ void probs_kernel(int V, float c, int topk,
   __shared__ uint64_t s_hist[kPBins];
   __shared__ float s_wv[kProbMaxWaves];
   __shared__ int s_wi[kProbMaxWaves];
-  __shared__ int s_cnt, s_bin, s_done;
+  __shared__ int s_cnt, s_bin;
   __shared__ float s_thr, s_zt;
   __shared__ int s_it;
   __shared__ uint64_t s_above;
@@ -308,8 +308,6 @@ void probs_kernel(int V, float c, int topk,
                           (((uint64_t)top_p24 * (S & 0xffffffull) + 0xffffffull) >> 24);
     float lo = lo0, hi = m;  // the candidate range of logits (all kept_k tokens in it)
     uint64_t above = 0;      // the mass of the tokens ranking before the range
-    if (tid == 0) s_done = 0;
-    __syncthreads();
     for (int it = 0; it < 64; ++it) {
       pin_row();
       if (lo == hi) {
