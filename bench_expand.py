@@ -197,7 +197,7 @@ def bench_verify_logits(args):
     pl = [torch.empty_like(zl[0]) for _ in range(ncopies)]
     ps = [torch.empty_like(zs[0]) for _ in range(ncopies)]
     outs = [ttv._verify_outputs(B, N, dev, None, None, None, None) for _ in range(2)]
-    ws = torch.empty(ttv.lib().ttv_tree_verify_logits_workspace_size(B, N), dtype=torch.uint8,
+    ws = torch.empty(ttv.lib().ttv_tree_verify_logits_workspace_size(B, N, V), dtype=torch.uint8,
                      device=dev)
     nv = ttv.tree_verify_workspace_size(ttv.STOCHASTIC, B, N, V)
     wsv = torch.empty(nv, dtype=torch.uint8, device=dev) if nv else None

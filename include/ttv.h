@@ -555,10 +555,12 @@ ttv_status ttv_probs_from_logits(int32_t R, int32_t V, float temperature,
  * token into the workspace, and the walk computes every probability it
  * reads from the logits.  Results equal ttv_tree_verify_varlen(STOCHASTIC,
  * ..., seed, step) on those probabilities; n_nodes is nullable (every
- * request has N nodes).  Needs V % 4 == 0 and V <= 32768 (TTV_E_UNSUPPORTED
+ * request has N nodes).  Needs V % 4 == 0 and V <= 262144 (TTV_E_UNSUPPORTED
  * otherwise) and 16-byte aligned logits.
- *   workspace >= ttv_tree_verify_logits_workspace_size(B, N) bytes (2*B*N
- *   row statistics of 16 bytes; no initialisation).
+ *   workspace >= ttv_tree_verify_logits_workspace_size(B, N, V) bytes: 2*B*N
+ *   row statistics of 16 bytes, then for V > 32768 the walk's residual
+ *   distribution, B*V floats (the rows no longer fit its registers); no
+ *   initialisation, 16-byte aligned.
  * Errors: TTV_E_NULL, TTV_E_SHAPE, TTV_E_UNSUPPORTED, TTV_E_ALIGN,
  *         TTV_E_WORKSPACE, TTV_E_LAUNCH.
  */
@@ -573,7 +575,9 @@ ttv_status ttv_tree_verify_logits(int32_t B, int32_t N, int32_t V,
                                   int32_t* dev_status, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
-size_t ttv_tree_verify_logits_workspace_size(int32_t B, int32_t N);
+/* Bytes of workspace ttv_tree_verify_logits needs; (size_t)-1 for sizes it
+ * does not take. */
+size_t ttv_tree_verify_logits_workspace_size(int32_t B, int32_t N, int32_t V);
 
 /*
  * ttv_kv_commit_inplace -- ttv_kv_commit for a tree stored inside the cache

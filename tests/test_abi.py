@@ -342,14 +342,22 @@ def test_varlen_entry_points_need_node_counts():
 @pytest.mark.parametrize("kw,status", [
     (dict(par=None), ttv.E_NULL), (dict(zl=None), ttv.E_NULL), (dict(zs=None), ttv.E_NULL),
     (dict(B=0), ttv.E_SHAPE), (dict(T=0.0), ttv.E_SHAPE), (dict(top_p=0.0), ttv.E_SHAPE),
-    (dict(V=1002), ttv.E_UNSUPPORTED), (dict(V=32772), ttv.E_UNSUPPORTED),
+    (dict(V=1002), ttv.E_UNSUPPORTED), (dict(V=(1 << 18) + 4), ttv.E_UNSUPPORTED),
     (dict(N=129), ttv.E_UNSUPPORTED), (dict(k=600), ttv.E_UNSUPPORTED),
     (dict(zl=MIS), ttv.E_ALIGN), (dict(ws=None), ttv.E_WORKSPACE),
     (dict(wsb=2 * 2 * 8 * 16 - 1), ttv.E_WORKSPACE),
+    # past 32768 entries the residual joins the workspace (B*V floats)
+    (dict(V=32772, wsb=2 * 2 * 8 * 16 + 2 * 32772 * 4 - 4), ttv.E_WORKSPACE),
+    (dict(V=32772, ws=MIS), ttv.E_ALIGN),
 ])
 def test_tree_verify_logits_host_validation(kw, status):
     args = dict(B=2, N=8, V=1000, par=A, tok=A, nn=None, zl=A, zs=A, T=0.8, k=0, top_p=0.9,
                 seed=1, step=0, path=A, plen=A, outt=A, st=None, ws=A, wsb=1 << 20)
     args.update(kw)
     assert ttv.lib().ttv_tree_verify_logits(*args.values(), None) == status
-    assert ttv.lib().ttv_tree_verify_logits_workspace_size(2, 8) == 2 * 2 * 8 * 16
+    f = ttv.lib().ttv_tree_verify_logits_workspace_size
+    assert f(2, 8, 1000) == 2 * 2 * 8 * 16
+    assert f(2, 8, 32768) == 2 * 2 * 8 * 16
+    assert f(2, 8, 32772) == 2 * 2 * 8 * 16 + 2 * 32772 * 4
+    assert f(2, 8, 1 << 18) == 2 * 2 * 8 * 16 + 2 * (1 << 18) * 4
+    assert f(2, 8, 1002) == SZ_ERR and f(2, 8, (1 << 18) + 4) == SZ_ERR and f(2, 129, 1000) == SZ_ERR

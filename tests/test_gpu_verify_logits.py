@@ -64,6 +64,23 @@ def test_against_oracle(V, T, k, p):
     run(d, T, min(k, V), p)
 
 
+# Past 32768 entries the rows no longer fit the walk's registers and its
+# residual goes to the workspace (B*V floats): the first size past that, a
+# common vocabulary with top-k and with top-p, a large one, and a ragged batch.
+@pytest.mark.parametrize("V,T,k,p", [(32772, 0.8, 0, 1.0), (50272, 1.0, 50, 1.0),
+                                     (50272, 0.8, 0, 0.9), (131072, 0.8, 20, 0.95)])
+def test_large_vocabulary(V, T, k, p):
+    announce("verify logits large vocabulary V=%d T=%g topk=%d top_p=%g" % (V, T, k, p))
+    d = logits_case(3, 24, V, seed=V + 7)
+    run(d, T, k, p)
+
+
+def test_large_vocabulary_node_counts():
+    announce("verify logits V=40000 with node counts")
+    d = logits_case(4, 20, 40000, seed=77)
+    run(d, 0.8, 0, 1.0, n_nodes=[20, 1, 13, 2])
+
+
 def test_stochastic_workload_shape():
     """16 requests x 64 nodes x 32000 tokens, T = 0.8 (the stochastic
     workload's shape, its LLM and speculator rows given as logits)."""

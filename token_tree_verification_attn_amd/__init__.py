@@ -98,7 +98,7 @@ def lib():
         L.ttv_probs_from_logits.argtypes = [_I, _I, _F, _I, _F, _P, _P, _P]
         L.ttv_tree_verify_logits.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _F, _I, _F, _U64,
                                              _U64, _P, _P, _P, _P, _P, _SZ, _P]
-        L.ttv_tree_verify_logits_workspace_size.argtypes = [_I, _I]
+        L.ttv_tree_verify_logits_workspace_size.argtypes = [_I, _I, _I]
         L.ttv_tree_verify_logits_workspace_size.restype = _SZ
         L.ttv_kv_commit_inplace.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P,
                                             _P, _P, _P]
@@ -482,7 +482,7 @@ def tree_verify_logits(parents, tokens, llm_logits, ssm_logits, temperature: flo
         _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
     path, path_len, out_tokens, dev_status = _verify_outputs(B, N, dev, path, path_len,
                                                              out_tokens, dev_status)
-    nbytes = lib().ttv_tree_verify_logits_workspace_size(B, N)
+    nbytes = lib().ttv_tree_verify_logits_workspace_size(B, N, V)
     if nbytes == ctypes.c_size_t(-1).value:
         raise ValueError("unsupported tree_verify_logits sizes")
     if workspace is None:

@@ -573,9 +573,18 @@ ttv_status ttv_probs_from_logits(int32_t R, int32_t V, float temperature, int32_
                                     static_cast<hipStream_t>(stream)));
 }
 
-size_t ttv_tree_verify_logits_workspace_size(int32_t B, int32_t N) {
-  if (B < 1 || N < 1 || N > TTV_MAX_NODES) return (size_t)-1;
-  return (size_t)2 * B * N * sizeof(RowStats);
+// Row statistics of both tensors (2*B*N RowStats), then, for logits rows
+// past the walk's registers, the residual (B*V floats); -1 for V the
+// verifier does not take.
+static size_t logits_workspace_bytes(int32_t B, int32_t N, int32_t V) {
+  if (B < 1 || N < 1 || N > TTV_MAX_NODES || V < 1) return (size_t)-1;
+  if (V % 4 != 0 || V > kMssGmMaxVocab) return (size_t)-1;
+  const size_t stats = (size_t)2 * B * N * sizeof(RowStats);
+  return V > kMssLogitsMaxVocab ? stats + (size_t)B * V * sizeof(float) : stats;
+}
+
+size_t ttv_tree_verify_logits_workspace_size(int32_t B, int32_t N, int32_t V) {
+  return logits_workspace_bytes(B, N, V);
 }
 
 ttv_status ttv_tree_verify_logits(int32_t B, int32_t N, int32_t V, const int32_t* parents,
@@ -591,14 +600,17 @@ ttv_status ttv_tree_verify_logits(int32_t B, int32_t N, int32_t V, const int32_t
   const ttv_status st = probs_args_ok(V, temperature, topk, top_p);
   if (st != TTV_OK) return st;
   if (N > TTV_MAX_NODES || (long)B * N > 0x7fffffffL) return TTV_E_UNSUPPORTED;
-  if (V % 4 != 0 || V > kMssLogitsMaxVocab) return TTV_E_UNSUPPORTED;
+  const size_t need = logits_workspace_bytes(B, N, V);
+  if (need == (size_t)-1) return TTV_E_UNSUPPORTED;
   if (!aligned16(llm_logits) || !aligned16(ssm_logits)) return TTV_E_ALIGN;
-  const size_t need = (size_t)2 * B * N * sizeof(RowStats);
   if (!workspace || workspace_bytes < need) return TTV_E_WORKSPACE;
   if (!aligned16(workspace)) return TTV_E_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   RowStats* st_llm = static_cast<RowStats*>(workspace);
   RowStats* st_ssm = st_llm + (size_t)B * N;
+  // the residual, for rows past the walk's registers (16-byte aligned: the
+  // statistics are 16-byte records)
+  float* gm_w = V > kMssLogitsMaxVocab ? reinterpret_cast<float*>(st_ssm + (size_t)B * N) : nullptr;
   // each row's statistics, then the walk computes the probabilities it reads
   if (launch_probs(B * N, V, temperature, topk, top_p, llm_logits, nullptr, st_llm, true, s) !=
           hipSuccess ||
@@ -608,7 +620,7 @@ ttv_status ttv_tree_verify_logits(int32_t B, int32_t N, int32_t V, const int32_t
   return launch_status(launch_verify_mss(
       B, N, V, parents, tokens, n_nodes, llm_logits, ssm_logits,
       MssDraws{nullptr, nullptr, seed, step}, LogitRows{st_llm, st_ssm, probs_scale(temperature)},
-      path, path_len, out_tokens, dev_status, nullptr, CommitArgs{}, s));
+      path, path_len, out_tokens, dev_status, gm_w, CommitArgs{}, s));
 }
 
 ttv_status ttv_kv_commit_inplace(ttv_dtype dt, int32_t B, int32_t N, int32_t Hkv, int32_t D,

@@ -139,10 +139,10 @@ struct LogitRows {
   float c;
 };
 
-// Largest vocabulary the stochastic verifier holds in LDS; rows given as
-// logits need 16-byte rows of at most kMssLogitsMaxVocab entries.  Larger
-// vocabularies (V % 4 == 0, at most kMssGmMaxVocab) keep the residual in
-// global memory: gm_w, B*V floats of workspace, 16-byte aligned.
+// Largest vocabulary the stochastic verifier holds in LDS (rows given as
+// logits: kMssLogitsMaxVocab, 16-byte rows).  Larger vocabularies (V % 4 ==
+// 0, at most kMssGmMaxVocab) keep the residual in global memory: gm_w, B*V
+// floats of workspace, 16-byte aligned.
 constexpr int kMssMaxVocab = 36864;
 constexpr int kMssLogitsMaxVocab = 32768;
 constexpr int kMssGmMaxVocab = 1 << 18;

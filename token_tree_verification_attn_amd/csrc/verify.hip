@@ -516,9 +516,21 @@ __device__ __forceinline__ double mss_residual(const float* __restrict__ q, int 
   return part;
 }
 
+// Rows given as logits: entry v of the row becomes its probability, computed
+// from the row's statistics exactly as the probabilities kernel does.
+template <bool LG>
+__device__ __forceinline__ f32x4 mss_entry4(f32x4 x, int v, const RowStats& st, float c) {
+  if constexpr (LG) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = row_prob(st, c, x[e], v + e);
+  }
+  return x;
+}
+
 // Residual in global memory, for vocabularies beyond the LDS (16-byte rows,
-// V % 4 == 0, V <= kMssGmMaxVocab): request b's residual is w[v], v < V, in
-// the caller's workspace.  The waves keep contiguous ranges, wave w the
+// V % 4 == 0, V <= kMssGmMaxVocab; rows of probabilities, or of logits made
+// probabilities with their row's statistics): request b's residual is w[v],
+// v < V, in the caller's workspace.  The waves keep contiguous ranges, wave w the
 // entries [w*S, (w+1)*S) with S = 256*CH and CH = ceil(V / (4*kMssThreads))
 // 16-byte chunks per lane (lane l: w*S + 4*(64*k + l)), so the per-wave sums
 // of a pass are again the masses of the ranges; a pass goes through
@@ -530,8 +542,9 @@ __device__ __forceinline__ int mss_gm_chunks(int V) {
   return (V + 4 * kMssThreads - 1) / (4 * kMssThreads);
 }
 // w = row; returns this thread's sum of fx40d of the entries copied
+template <bool LG>
 __device__ __forceinline__ double mss_gm_row_to_w(const float* __restrict__ row, int V, float* w,
-                                                  int CH) {
+                                                  int CH, const RowStats& st, float c) {
   const int t = threadIdx.x, base = 256 * CH * (t >> 6) + 4 * (t & 63);
   double part = 0.0;
 #pragma unroll 1
@@ -546,17 +559,19 @@ __device__ __forceinline__ double mss_gm_row_to_w(const float* __restrict__ row,
     for (int j = 0; j < kMssGmBatch; ++j) {
       const int v = base + 256 * (k0 + j);
       if (k0 + j < CH && v < V) {
-        *reinterpret_cast<f32x4*>(w + v) = r[j];
+        const f32x4 p = mss_entry4<LG>(r[j], v, st, c);
+        *reinterpret_cast<f32x4*>(w + v) = p;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part += fx40d(r[j][e]);
+        for (int e = 0; e < 4; ++e) part += fx40d(p[e]);
       }
     }
   }
   return part;
 }
 // w = max(w - s*q, +0); returns this thread's sum of fx40d(w)
+template <bool LG>
 __device__ __forceinline__ double mss_gm_residual(const float* __restrict__ q, int V, float s,
-                                                  float* w, int CH) {
+                                                  float* w, int CH, const RowStats& st, float c) {
   const int t = threadIdx.x, base = 256 * CH * (t >> 6) + 4 * (t & 63);
   double part = 0.0;
 #pragma unroll 1
@@ -574,9 +589,10 @@ __device__ __forceinline__ double mss_gm_residual(const float* __restrict__ q, i
       const int v = base + 256 * (k0 + j);
       if (k0 + j < CH && v < V) {
         f32x4 y = x[j];
+        const f32x4 qv = mss_entry4<LG>(r[j], v, st, c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          y[e] = clamp_pos(fmaf(-s, r[j][e], y[e]));
+          y[e] = clamp_pos(fmaf(-s, qv[e], y[e]));
           part += fx40d(y[e]);
         }
         *reinterpret_cast<f32x4*>(w + v) = y;
@@ -615,17 +631,6 @@ __device__ __forceinline__ void mss_issue_row(const float* __restrict__ row, int
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, kBufferWord3);
     r[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
   }
-}
-
-// Rows given as logits: entry v of the row becomes its probability, computed
-// from the row's statistics exactly as the probabilities kernel does.
-template <bool LG>
-__device__ __forceinline__ f32x4 mss_entry4(f32x4 x, int v, const RowStats& st, float c) {
-  if constexpr (LG) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = row_prob(st, c, x[e], v + e);
-  }
-  return x;
 }
 
 // s_w[widx(v)] = r (probabilities, or logits made probabilities with `st`);
@@ -717,7 +722,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     int32_t* __restrict__ path, int32_t* __restrict__ path_len,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ dev_status, float* __restrict__ gm_w,
     CommitArgs cm) {
-  static_assert(!GM || (VEC && !PF && !LG), "the global residual takes single-buffered 16-byte rows");
+  static_assert(!GM || (VEC && !PF), "the global residual takes single-buffered 16-byte rows");
   extern __shared__ __attribute__((aligned(16))) float s_w[];  // residual w, widx() layout
   __shared__ int32_t s_par[kMaxNodes];
   __shared__ int32_t s_tok[kMaxNodes];
@@ -849,7 +854,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   auto load_p_row = [&](int u) {
     __syncthreads();
     if constexpr (GM) {
-      block_sum_f64(mss_gm_row_to_w(llm + (rowN + u) * V, V, wg, gmCH), s_redd);
+      block_sum_f64(mss_gm_row_to_w<LG>(llm + (rowN + u) * V, V, wg, gmCH, p_stats(u), lr.c), s_redd);
     } else {
       mss_row_to_lds<VEC>(llm + (rowN + u) * V, V, s_w);
       __syncthreads();
@@ -983,7 +988,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       first = false;
       // rejected: w = max(w - s*q_c, +0), s = its mass in 2^-40 units
       double part;
-      if constexpr (GM) part = mss_gm_residual(ssm + (rowN + c) * V, V, s, wg, gmCH);
+      if constexpr (GM) part = mss_gm_residual<LG>(ssm + (rowN + c) * V, V, s, wg, gmCH, q_stats(c), lr.c);
       else part = mss_residual<VEC>(ssm + (rowN + c) * V, V, s, s_w);
       const double S = block_sum_f64(part, s_redd);  // its barriers publish s_w
       s = (float)(S * 0x1p-40);
@@ -1271,15 +1276,18 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
                              int32_t* path, int32_t* path_len, int32_t* out_tokens,
                              int32_t* dev_status, float* gm_w, const CommitArgs& cm,
                              hipStream_t s) {
-  if (V > kMssMaxVocab) {  // the residual in global memory (host checks: V % 4 == 0, gm_w)
-    hipLaunchKernelGGL((mss_kernel<true, false, false, true>), dim3(B), dim3(kMssThreads), 0, s, N,
-                       V, parents, tokens, n_nodes, llm, ssm, dr, lr, path, path_len, out_tokens,
-                       dev_status, gm_w, cm);
+  const bool lg = lr.st_llm != nullptr;
+  // the residual in global memory (host checks: V % 4 == 0, 16-byte rows,
+  // gm_w): vocabularies beyond the LDS, and logits rows beyond the
+  // double-buffered walk's registers
+  if (V > kMssMaxVocab || (lg && V > kMssPfMaxVocab)) {
+    auto kern = lg ? mss_kernel<true, false, true, true> : mss_kernel<true, false, false, true>;
+    hipLaunchKernelGGL(kern, dim3(B), dim3(kMssThreads), 0, s, N, V, parents, tokens, n_nodes,
+                       llm, ssm, dr, lr, path, path_len, out_tokens, dev_status, gm_w, cm);
     return hipGetLastError();
   }
   const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(llm) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(ssm) & 15) == 0;
-  const bool lg = lr.st_llm != nullptr;
   // widx(V - 1) + 1, 16-byte padded; the double-buffered walk over
   // probabilities keeps its whole span (kMssPfMaxVocab entries) in LDS
   const int Vl = (vec && !lg && V <= kMssPfMaxVocab) ? kMssPfMaxVocab : V;
