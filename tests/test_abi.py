@@ -102,10 +102,13 @@ def test_tree_attn_workspace_size_matches_plan():
     assert f(9, 1, 8, 4, 2, 64, 64, 0, 0) == SZ_ERR
     # the binding allocates exactly that much
     assert ttv.tree_attn_workspace_size(torch.bfloat16, 1, 8, 4, 2, 64, 100, 0, 64) == 8704
-    # the automatic shape: no split up to 512 keys, one shape for both entry points
+    # the automatic shape: no split up to 256 keys, one shape for both entry points
     g = ttv.lib().ttv_tree_attn_workspace_size
     assert g(1, 1, 8, 4, 2, 64, 100) == 0 == f(1, 1, 8, 4, 2, 64, 100, 0, 0)
     assert g(1, 4, 128, 64, 8, 128, 32768) == f(1, 4, 128, 64, 8, 128, 32768, 0, 0) > 0
+    # one request of 32 kv heads x 64 rows x 512 keys: four 128-key chunks
+    assert g(1, 1, 64, 32, 32, 128, 512) == 32 * 4 * 64 * (128 * 2 + 8)
+    assert g(1, 1, 64, 32, 32, 128, 256) == 0
     assert g(1, 1, 129, 4, 2, 64, 64) == SZ_ERR
 
 

@@ -69,14 +69,15 @@ ttv_status attn_plan(ttv_dtype dt, int B, int N, int Hq, int Hkv, int D, int Lma
     chunk = chunk_hint;
   } else {
     // split the prefix only as far as needed to occupy the free slots, in
-    // chunks of at least 256 keys (fp32 partials cost ~2*rows/chunk of the KV),
-    // and not at all up to 512 keys: there a split saves at most a few tiles
-    // per workgroup, about what the combine launch costs (measured on MI355X:
-    // 32 heads x 64 rows x 512 keys, unsplit 4% faster than two chunks)
+    // chunks of at least 128 keys (partials cost ~rows/chunk of the KV in
+    // bf16, twice that in fp32), and not at all up to 256 keys, where a split
+    // saves at most a few tiles per workgroup (measured on MI355X: 32 heads x
+    // 64 rows x 512 keys, 32 workgroups streaming 9 tiles each: 128-key
+    // chunks 14.1 us, 64-key 15.4, 256-key 15.3, unsplit 15.7)
     const long want = (slots + units - 1) / units;
-    long c = want > 1 && Lmax > 512 ? (Lmax + want - 1) / want : Lmax;
+    long c = want > 1 && Lmax > 256 ? (Lmax + want - 1) / want : Lmax;
     c = (c + 63) / 64 * 64;
-    if (c < 256) c = 256;
+    if (c < 128) c = 128;
     chunk = (int)c;
   }
   p->chunk_keys = chunk;

@@ -58,7 +58,9 @@ __device__ __forceinline__ void store_elt<uint16_t>(uint16_t* p, float v) { *p =
 // FMA path: fp32 inputs, or bf16 with fewer than 16 query rows per kv head.
 // Each wavefront owns up to 4 query rows; per 64-key tile a lane scores one
 // key (dot product over D from LDS), the wave does the online-softmax update
-// with shuffles, then each lane accumulates D/64 output columns.
+// with register-only wave reductions (DPP and lane swaps), then each lane
+// accumulates D/64 output columns, reading each key's probability from its
+// lane with v_readlane.
 // =========================================================================
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
@@ -164,10 +166,15 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
     }
     __syncthreads();
     bool key_ok = lane < nvalid;
+    // the scores and the online-softmax update of the wave's rows (padding
+    // rows get p = 0 and stay empty), then one pass over the tile's keys
+    // that reads each V row once for all of them
+    float p[RPW];
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
       const int rr = wave * RPW + k;
-      if (row0 + rr >= Rn) continue;  // wave-uniform (padding rows stay empty)
+      p[k] = 0.f;
+      if (row0 + rr >= Rn) continue;  // wave-uniform
       float dot = 0.f;
 #pragma unroll 8
       for (int d = 0; d < D; ++d) dot = fmaf(s_q[rr * D + d], s_k[lane * DP + d], dot);
@@ -177,18 +184,26 @@ __global__ __launch_bounds__(256) void attn_fma_kernel(AttnArgs a) {
         ok = ok && ((anc_w[k][j >> 6] >> (j & 63)) & 1ull);
       }
       const float t = ok ? dot * a.scale_log2 : -INFINITY;
-      const float m_new = fmaxf(m[k], wave_max(t));
+      const float m_new = fmaxf(m[k], wave_allmax_f32(t));
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float p = __builtin_amdgcn_exp2f(t - m_use);
+      p[k] = __builtin_amdgcn_exp2f(t - m_use);
       const float alpha = __builtin_amdgcn_exp2f(m[k] - m_use);
-      l[k] = l[k] * alpha + wave_sum(p);
+      l[k] = l[k] * alpha + wave_allsum_f32(p[k]);
       m[k] = m_new;
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[k][e] *= alpha;
-      for (int j = 0; j < KT; ++j) {
-        const float pj = __shfl(p, j);
+    }
+#pragma unroll 8
+    for (int j = 0; j < KT; ++j) {
+      float vj[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[k][e] = fmaf(pj, s_v[j * DP + lane + 64 * e], acc[k][e]);
+      for (int e = 0; e < E; ++e) vj[e] = s_v[j * DP + lane + 64 * e];
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) {
+        // key j's probability from lane j (a register read, no LDS round trip)
+        const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[k]), j));
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[k][e] = fmaf(pj, vj[e], acc[k][e]);
       }
     }
   }

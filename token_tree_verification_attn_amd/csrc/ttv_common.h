@@ -46,32 +46,6 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   uint32_t hi = __shfl(static_cast<uint32_t>(v >> 32), src);
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
-  uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_u64(v, m);
-  return v;
-}
-__device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m));
-  return v;
-}
-
 // -------------------------------------------- register-only wave sums ----
 // Sums over the 64 lanes that stay in the VALU (a __shfl_xor step is an LDS
 // round trip, ds_bpermute): two quad permutations and two row rotations
@@ -140,6 +114,26 @@ __device__ __forceinline__ uint64_t wave_allsum_u64(uint64_t v) {
   swap_pair_u64<false>(v, a, b);
   swap_pair_u64<true>(a + b, a, b);
   return a + b;
+}
+__device__ __forceinline__ float wave_allsum_f32(float v) {
+  v += __uint_as_float(dpp_u32<kDppQuadXor1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppQuadXor2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppRowRor4>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppRowRor8>(__float_as_uint(v)));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ int wave_allmax_i32(int v) {
+  v = max(v, (int)dpp_u32<kDppQuadXor1>((uint32_t)v));
+  v = max(v, (int)dpp_u32<kDppQuadXor2>((uint32_t)v));
+  v = max(v, (int)dpp_u32<kDppRowRor4>((uint32_t)v));
+  v = max(v, (int)dpp_u32<kDppRowRor8>((uint32_t)v));
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = max((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return max((int)r[0], (int)r[1]);
 }
 __device__ __forceinline__ float wave_allmax_f32(float v) {
   v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuadXor1>(__float_as_uint(v))));

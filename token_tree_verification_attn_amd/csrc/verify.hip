@@ -167,7 +167,7 @@ __device__ int greedy_scan_wave(int b, int N, int splits, const int32_t* __restr
   int key = -1;  // (depth, -index) of the deepest accepted node
   if (v0 && (a0lo & ~E0) == 0ull) key = max(key, (d0 << 8) | (255 - i0));
   if (v1 && (a1lo & ~E0) == 0ull && (a1hi & ~E1) == 0ull) key = max(key, (d1 << 8) | (255 - i1));
-  key = wave_max_i32(key);  // the root is always accepted: key >= 0
+  key = wave_allmax_i32(key);  // the root is always accepted: key >= 0
   const int end = 255 - (key & 255), dend = key >> 8;
   const uint64_t x_lo0 = shfl_u64(a0lo, end & 63), x_lo1 = shfl_u64(a1lo, end & 63);
   const uint64_t x_hi1 = shfl_u64(a1hi, end & 63);
