@@ -341,6 +341,7 @@ void probs_kernel(int V, float c, int topk,
         const float x = linear ? (hi - z) * scv : (float)(khi - p_order_key(z)) * sck;
         return min(kPBins - 1, (int)x);
       };
+      if (tid == 0) s_cnt = 0;  // the gather's counter (last read before a barrier)
       for (int b = tid; b < kPBins; b += kProbThreads) s_hist[b] = 0ull;
       __syncthreads();
       visit_ze([&](float z, float e, int i) {
@@ -380,34 +381,23 @@ void probs_kernel(int V, float c, int topk,
       __syncthreads();
       const int bsel = s_bin;
       above = s_above;
-      // the crossing bin's tokens: count and logit range
-      double n = 0.0;
-      float bmin = INFINITY, bmax = -INFINITY;
-      visit_row([&](float z, int i) {
+      // gather the crossing bin's tokens into LDS (at most kPGather of them;
+      // the counter counts them all) and rank them there: the crossing token
+      // is the one whose running mass (above + the tokens ranking before it,
+      // itself included) first reaches need
+      visit_ze([&](float z, float e, int i) {
         if (z >= lo && z <= hi && kept_k(z, i) && bin_of(z) == bsel) {
-          n += 1.0;
-          bmin = fminf(bmin, z);
-          bmax = fmaxf(bmax, z);
-        }
-      });
-      const uint64_t cnt = block_sum_u64((uint64_t)n);
-      const float nlo = block_min(bmin), nhi = block_max(bmax);
-      if (cnt <= (uint64_t)kPGather) {
-        // gather them and rank them in LDS: the crossing token is the one
-        // whose running mass (above + the tokens ranking before it, itself
-        // included) first reaches need
-        if (tid == 0) s_cnt = 0;
-        __syncthreads();
-        visit_ze([&](float z, float e, int i) {
-          if (z >= lo && z <= hi && kept_k(z, i) && bin_of(z) == bsel) {
-            const int slot = atomicAdd(&s_cnt, 1);
+          const int slot = atomicAdd(&s_cnt, 1);
+          if (slot < kPGather) {
             s_cv[slot] = z;
             s_ci[slot] = i;
             s_hist[slot] = (uint64_t)mass40(e);
           }
-        });
-        __syncthreads();
-        const int nc = s_cnt;
+        }
+      });
+      __syncthreads();
+      const int nc = s_cnt;
+      if (nc <= kPGather) {
         for (int q = tid; q < nc; q += kProbThreads) {
           const float z = s_cv[q];
           const int i = s_ci[q];
@@ -424,8 +414,18 @@ void probs_kernel(int V, float c, int topk,
         ithr = s_it;
         break;
       }
-      lo = nlo;  // the next range: the crossing bin (its members are exactly
-      hi = nhi;  // the kept tokens with logits in [nlo, nhi])
+      // too many: the next range is the crossing bin (its members are
+      // exactly the kept tokens with logits in [nlo, nhi])
+      float bmin = INFINITY, bmax = -INFINITY;
+      visit_row([&](float z, int i) {
+        if (z >= lo && z <= hi && kept_k(z, i) && bin_of(z) == bsel) {
+          bmin = fminf(bmin, z);
+          bmax = fmaxf(bmax, z);
+        }
+      });
+      const float nlo = block_min(bmin), nhi = block_max(bmax);
+      lo = nlo;
+      hi = nhi;
     }
   }
 
