@@ -91,7 +91,7 @@ void probs_kernel(int V, float c, int topk,
   __shared__ int s_cnt, s_bin;
   __shared__ float s_thr, s_zt;
   __shared__ int s_it;
-  __shared__ uint64_t s_above;
+  __shared__ uint64_t s_above, s_need, s_kept;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* row = logits + (size_t)blockIdx.x * V;
   const f32x4* r4 = reinterpret_cast<const f32x4*>(row);
@@ -154,10 +154,16 @@ void probs_kernel(int V, float c, int topk,
     return r;
   };
 
-  // ---- the row maximum, from the per-thread maxima
-  float tmax = -INFINITY;
-  visit_row([&](float z, int) { tmax = fmaxf(tmax, z); });
+  // ---- the row maximum, from the per-thread maxima (and the per-thread
+  // minima, which top-p without top-k starts its range from)
+  float tmax = -INFINITY, tmin = INFINITY;
+  visit_row([&](float z, int) {
+    tmax = fmaxf(tmax, z);
+    tmin = fminf(tmin, z);
+  });
   const float m = block_max(tmax);
+  const bool use_topk = SEL && topk > 0 && topk < V;
+  const bool use_topp = SEL && top_p24 > 0u && top_p24 < (1u << 24);
   // 2^t of every entry, kept in registers with the row (without selection
   // the logits are not needed again, and the compiler reuses their registers)
   if (in_regs) {
@@ -196,7 +202,7 @@ void probs_kernel(int V, float c, int topk,
   // ---- top-k: the k-th entry (kv, ki); every entry is kept without top-k
   float kv = -INFINITY;
   int ki = INT_MAX;
-  if (SEL && topk > 0 && topk < V) {
+  if (use_topk) {
     // a lower bound of the k-th entry: every wave takes the ceil(k/W)-th
     // largest of its 64 per-thread maxima (W waves), and the smallest of
     // those has at least W*ceil(k/W) >= k entries of the row at or above it
@@ -291,26 +297,22 @@ void probs_kernel(int V, float c, int topk,
   float zthr = kv;
   int ithr = ki;
 
-  // ---- top-p: the token where the running mass reaches ceil(P*S/2^24)
-  if (SEL && top_p24 > 0u && top_p24 < (1u << 24)) {
-    double part = 0.0;  // at most 8*4 masses below 2^40 each: exact
-    float zmin = INFINITY;
-    visit_ze([&](float z, float e, int i) {
-      if (kept_k(z, i)) {
-        part += mass40(e);
-        zmin = fminf(zmin, z);
-      }
-    });
-    const uint64_t S = block_sum_u64((uint64_t)part);
-    const float lo0 = block_min(zmin);
-    // need = ceil(P * S / 2^24) with S = hi*2^24 + lo split (no overflow)
-    const uint64_t need = (uint64_t)top_p24 * (S >> 24) +
-                          (((uint64_t)top_p24 * (S & 0xffffffull) + 0xffffffull) >> 24);
-    float lo = lo0, hi = m;  // the candidate range of logits (all kept_k tokens in it)
-    uint64_t above = 0;      // the mass of the tokens ranking before the range
+  // ---- top-p: the token where the running mass reaches ceil(P*S/2^24),
+  // S the kept mass (taken from the first histogram, which holds every kept
+  // token); the running mass there is the kept mass S' the probabilities
+  // are normalised by
+  bool have_kept = false;
+  uint64_t kept_mass = 0;
+  const float row_min = use_topp && !use_topk ? block_min(tmin) : 0.f;
+  if (use_topp) {
+    // the candidate range of logits (all kept_k tokens in it): from the
+    // smallest kept logit (the k-th with top-k) to the maximum
+    float lo = use_topk ? kv : row_min, hi = m;
+    uint64_t above = 0;  // the mass of the tokens ranking before the range
+    uint64_t need = 0;   // ceil(P * S / 2^24), known after the first histogram
     for (int it = 0; it < 64; ++it) {
       pin_row();
-      if (lo == hi) {
+      if (it > 0 && lo == hi) {
         // every candidate has the logit lo, hence the same mass mu: the
         // crossing is the c-th lowest token id among them, c = ceil((need -
         // above) / mu); binary search on the id
@@ -327,6 +329,8 @@ void probs_kernel(int V, float c, int topk,
         }
         zthr = lo;
         ithr = a;
+        kept_mass = above + cneed * mu;  // the range's first cneed tokens, mass mu each
+        have_kept = true;
         break;
       }
       // histogram of the candidates' masses over 2048 bins, higher logits
@@ -361,6 +365,14 @@ void probs_kernel(int V, float c, int topk,
           if (lane >= d) incl += o;
         }
         const uint64_t excl = incl - loc;
+        if (it == 0) {  // every kept token is in this histogram: S is its total
+          const uint64_t S = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(incl >> 32), 63) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, 63);
+          // need = ceil(P * S / 2^24) with S = hi*2^24 + lo split (no overflow)
+          need = (uint64_t)top_p24 * (S >> 24) +
+                 (((uint64_t)top_p24 * (S & 0xffffffull) + 0xffffffull) >> 24);
+          if (lane == 0) s_need = need;
+        }
         const uint64_t first = __ballot(above + incl >= need);
         const int L = first ? __ffsll((unsigned long long)first) - 1 : 63;
         if (lane == L) {
@@ -381,6 +393,7 @@ void probs_kernel(int V, float c, int topk,
       __syncthreads();
       const int bsel = s_bin;
       above = s_above;
+      need = s_need;
       // gather the crossing bin's tokens into LDS (at most kPGather of them;
       // the counter counts them all) and rank them there: the crossing token
       // is the one whose running mass (above + the tokens ranking before it,
@@ -407,11 +420,14 @@ void probs_kernel(int V, float c, int topk,
           if (above + before < need && above + before + s_hist[q] >= need) {
             s_zt = z;
             s_it = i;
+            s_kept = above + before + s_hist[q];
           }
         }
         __syncthreads();
         zthr = s_zt;
         ithr = s_it;
+        kept_mass = s_kept;
+        have_kept = true;
         break;
       }
       // too many: the next range is the crossing bin (its members are
@@ -431,11 +447,14 @@ void probs_kernel(int V, float c, int topk,
 
   // ---- normaliser and probabilities (or the row's statistics)
   auto kept = [&](float z, int i) { return !SEL || z > zthr || (z == zthr && i <= ithr); };
-  double part = 0.0;
-  visit_ze([&](float z, float e, int i) {
-    if (kept(z, i)) part += mass40(e);
-  });
-  const uint64_t S = block_sum_u64((uint64_t)part);
+  uint64_t S = kept_mass;
+  if (!have_kept) {
+    double part = 0.0;  // at most 64 masses below 2^40 each per thread: exact
+    visit_ze([&](float z, float e, int i) {
+      if (kept(z, i)) part += mass40(e);
+    });
+    S = block_sum_u64((uint64_t)part);
+  }
   const float inv = (float)(1099511627776.0 / (double)S);
   if (stats) {
     if (tid == 0) stats[blockIdx.x] = RowStats{m, inv, zthr, ithr};
