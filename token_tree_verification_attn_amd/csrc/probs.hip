@@ -199,6 +199,10 @@ void probs_kernel(int V, float c, int topk,
     }
   };
 
+  // the kept mass S', when a selection step has it (else summed at the end)
+  bool have_kept = false;
+  uint64_t kept_mass = 0;
+
   // ---- top-k: the k-th entry (kv, ki); every entry is kept without top-k
   float kv = -INFINITY;
   int ki = INT_MAX;
@@ -226,15 +230,31 @@ void probs_kernel(int V, float c, int topk,
       __syncthreads();
     }
     const float thr = s_thr;
-    visit_row([&](float z, int i) {
-      if (z >= thr) {
-        const int slot = atomicAdd(&s_cnt, 1);
-        if (slot < kProbCandidates) {
-          s_cv[slot] = z;
-          s_ci[slot] = i;
+    // (without top-p the kept mass is summed from the candidates' masses;
+    // top-p finds its own)
+    const bool sum_kept = !use_topp;
+    if (sum_kept) {
+      visit_ze([&](float z, float e, int i) {
+        if (z >= thr) {
+          const int slot = atomicAdd(&s_cnt, 1);
+          if (slot < kProbCandidates) {
+            s_cv[slot] = z;
+            s_ci[slot] = i;
+            s_hist[slot] = (uint64_t)mass40(e);
+          }
         }
-      }
-    });
+      });
+    } else {
+      visit_row([&](float z, int i) {
+        if (z >= thr) {
+          const int slot = atomicAdd(&s_cnt, 1);
+          if (slot < kProbCandidates) {
+            s_cv[slot] = z;
+            s_ci[slot] = i;
+          }
+        }
+      });
+    }
     __syncthreads();
     const int cnt = s_cnt;
     if (cnt <= kProbCandidates) {
@@ -242,6 +262,9 @@ void probs_kernel(int V, float c, int topk,
       // 0..cnt-1 and exactly one candidate has rank topk-1 (cnt >= topk)
       // (wave w ranks candidates w, w + W, ...; its lanes compare one with
       // every 64th of the others, and a register-only wave sum counts)
+      // The kept tokens are exactly the candidates of rank < topk: their
+      // masses, summed per wave and then over the waves, are the kept mass.
+      uint64_t kmass = 0;
       for (int q = wave; q < cnt; q += kProbWaves) {
         const float z = s_cv[q];
         const int i = s_ci[q];
@@ -252,8 +275,16 @@ void probs_kernel(int V, float c, int topk,
           s_wv[0] = z;
           s_wi[0] = i;
         }
+        if (sum_kept && rank < topk) kmass += s_hist[q];
       }
+      if (lane == 0) s_red64[wave] = kmass;
       __syncthreads();
+      if (sum_kept) {
+        kept_mass = 0;
+#pragma unroll
+        for (int w = 0; w < kProbWaves; ++w) kept_mass += s_red64[w];
+        have_kept = true;
+      }
       kv = s_wv[0];
       ki = s_wi[0];
     } else {
@@ -301,8 +332,6 @@ void probs_kernel(int V, float c, int topk,
   // S the kept mass (taken from the first histogram, which holds every kept
   // token); the running mass there is the kept mass S' the probabilities
   // are normalised by
-  bool have_kept = false;
-  uint64_t kept_mass = 0;
   const float row_min = use_topp && !use_topk ? block_min(tmin) : 0.f;
   if (use_topp) {
     // the candidate range of logits (all kept_k tokens in it): from the
