@@ -5,10 +5,11 @@
 // sampling; [SSD] §4 samples with top-k, k = 50, at T = 1).  The arithmetic
 // is fixed to the bit (softmax_exact.h).
 //
-// One workgroup per row (1024 threads, or 512 with top-k/top-p).  A row of
-// up to 32768 logits is requested whole (8 or 16 16-byte loads per thread)
-// and kept in registers with its 2^t values; a longer one is streamed, once
-// per pass.
+// One workgroup per row (1024 threads, or 512 with top-k/top-p), two per CU.
+// A row of up to 32768 logits is requested whole (8 or 16 16-byte loads per
+// thread) and kept in registers (without selection its 2^t values replace
+// it; with selection they are formed again where a pass needs them); a
+// longer one is streamed, once per pass.
 //  * top-k: the k-th entry in the order (higher logit, then lower token id)
 //    is found as in tree expansion: the smallest over the W waves of each
 //    wave's ceil(k/W)-th largest per-thread maximum bounds it from below,
@@ -38,9 +39,11 @@ namespace ttv {
 namespace {
 
 // Threads per row: 1024 without selection (8 16-byte loads each); with
-// top-k/top-p, 512 (16 loads each), whose 256 VGPRs per lane hold the row's
-// logits and exponentials (1024 threads leave 128, and that kernel spilled
-// to scratch memory).
+// top-k/top-p, 512 (16 loads each) holding the row's logits in 128 VGPRs per
+// lane, so that two workgroups share a CU and one's loads and stores overlap
+// the other's passes.  (Keeping the exponentials in registers too took 256
+// VGPRs and one workgroup per CU: top-50 116 vs 87 us, top-p 0.9 167 vs 129
+// us on 1024 x 32000 logits; at 1024 threads it spilled to scratch.)
 template <bool SEL>
 struct ProbShape {
   static constexpr int kThreads = SEL ? 512 : 1024;
@@ -68,11 +71,10 @@ __device__ __forceinline__ uint32_t p_order_key(float z) {
 
 }  // namespace
 
-// SEL: top-k and/or top-p.  Without them a thread's row needs one register
-// set (the logits become their exponentials), and two workgroups share a
-// CU, so one's loads are in flight while the other reduces.
+// SEL: top-k and/or top-p.  Either way two workgroups share a CU, so one's
+// loads are in flight while the other computes.
 template <bool VEC, bool SEL>
-__global__ __launch_bounds__(ProbShape<SEL>::kThreads) __attribute__((amdgpu_waves_per_eu(SEL ? 2 : 8)))
+__global__ __launch_bounds__(ProbShape<SEL>::kThreads) __attribute__((amdgpu_waves_per_eu(SEL ? 4 : 8)))
 void probs_kernel(int V, float c, int topk,
                                                              uint32_t top_p24,
                                                              const float* __restrict__ logits,
@@ -97,13 +99,9 @@ void probs_kernel(int V, float c, int topk,
   const f32x4* r4 = reinterpret_cast<const f32x4*>(row);
   const int n4 = V / 4;
   const bool in_regs = VEC && n4 <= kProbRegQuads * kProbThreads;
-  // the row's logits and their exponentials; without selection the
-  // exponentials overwrite the logits (which are not needed again)
-  f32x4 rq[kProbRegQuads], re_sel[SEL ? kProbRegQuads : 1];
-  auto RE = [&](int u) -> f32x4& {
-    if constexpr (SEL) return re_sel[u];
-    else return rq[u];
-  };
+  // the row's logits; without selection their exponentials overwrite them
+  // (the logits are not needed again)
+  f32x4 rq[kProbRegQuads];
   if (in_regs) {
 #pragma unroll
     for (int u = 0; u < kProbRegQuads; ++u) {
@@ -164,26 +162,25 @@ void probs_kernel(int V, float c, int topk,
   const float m = block_max(tmax);
   const bool use_topk = SEL && topk > 0 && topk < V;
   const bool use_topp = SEL && top_p24 > 0u && top_p24 < (1u << 24);
-  // 2^t of every entry, kept in registers with the row (without selection
-  // the logits are not needed again, and the compiler reuses their registers)
+  // without selection: 2^t of every entry, in place of its logit
   if (in_regs) {
 #pragma unroll
     for (int u = 0; u < kProbRegQuads; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) RE(u)[e] = exp2_taylor((rq[u][e] - m) * c);
+      for (int e = 0; e < 4; ++e) if constexpr (!SEL) rq[u][e] = exp2_taylor((rq[u][e] - m) * c);
   }
   // Per-entry values that a loop over passes would otherwise hoist out of
-  // it (order keys, 64-bit masses: three registers per entry, which spilled)
+  // it (order keys, exponentials, 64-bit masses: registers per entry, which
+  // spilled)
   // are kept inside by declaring the row's registers rewritten (no code).
   auto pin_row = [&]() {
     if (in_regs) {
 #pragma unroll
-      for (int u = 0; u < kProbRegQuads; ++u) {
-        asm volatile("" : "+v"(rq[u]));
-        if constexpr (SEL) asm volatile("" : "+v"(RE(u)));
-      }
+      for (int u = 0; u < kProbRegQuads; ++u) asm volatile("" : "+v"(rq[u]));
     }
   };
+  // visit(z, 2^t, i) for this thread's entries (with selection 2^t is
+  // formed here, from the logit and the row maximum)
   auto visit_ze = [&](auto visit) {
     if (in_regs) {
 #pragma unroll
@@ -191,7 +188,10 @@ void probs_kernel(int V, float c, int topk,
         const int x = tid + u * kProbThreads;
         if (x < n4) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) visit(rq[u][e], RE(u)[e], 4 * x + e);
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (SEL) visit(rq[u][e], exp2_taylor((rq[u][e] - m) * c), 4 * x + e);
+            else visit(rq[u][e], rq[u][e], 4 * x + e);
+          }
         }
       }
     } else {
@@ -498,7 +498,10 @@ void probs_kernel(int V, float c, int topk,
       if (x < n4) {
         f32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = !SEL || kept(rq[u][e], 4 * x + e) ? RE(u)[e] * inv : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (SEL) o[e] = kept(rq[u][e], 4 * x + e) ? exp2_taylor((rq[u][e] - m) * c) * inv : 0.f;
+          else o[e] = rq[u][e] * inv;
+        }
         o4[x] = o;
       }
     }
