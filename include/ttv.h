@@ -299,7 +299,8 @@ ttv_status ttv_tree_attn_noalloc(ttv_dtype dt, int32_t B, int32_t N,
  *   B,N,V    requests, nodes per request (<= 128), vocabulary (>= 1).
  *   parents  int32 [B,N]; tokens int32 [B,N] (tokens[b,0] = root's token,
  *            unused); llm float [B,N,V]; ssm float [B,N,V] (stochastic only,
- *            else NULL); seed, step: the draws' key and counter word 3
+ *            else NULL; in stochastic mode both hold probabilities, every
+ *            entry in [0, 1]); seed, step: the draws' key and counter word 3
  *            (stochastic only, else ignored).
  *   path     int32 [B,N]: path[b,k] = node at depth k on the accepted path,
  *            -1 after the end.   path_len int32 [B]: accepted nodes + 1 (>= 1).

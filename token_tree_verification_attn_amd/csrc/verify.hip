@@ -380,6 +380,26 @@ __device__ __forceinline__ int widx(int v) { return v + 4 * (v >> 7); }
 // terms below 2^53 in any order.
 __device__ __forceinline__ double fx40d(float x) { return (double)floorf(x * 0x1p40f); }
 
+// The same sums with one f64 FMA per entry.  A double in [2^52, 2^53) has
+// unit spacing, so with double-precision rounding toward -infinity
+// (MODE.FP_ROUND[3:2] = 2) an accumulator biased by 2^52 takes acc + x*2^40
+// to exactly acc + floor(x*2^40), for x in [0, 1] while the unbiased total
+// stays below 2^52.  The mode is set and restored around an accumulation,
+// and the FMAs are inline assembly, so that the compiler neither moves them
+// out of that window nor folds them (it assumes round-to-nearest for the
+// arithmetic it sees); the widening to double is exact in either mode.
+constexpr double kFxBias = 0x1p52;
+__device__ __forceinline__ void f64_round_down() {
+  asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 2, 2), 2\n\ts_nop 1");
+}
+__device__ __forceinline__ void f64_round_nearest() {
+  asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 2, 2), 0\n\ts_nop 1");
+}
+__device__ __forceinline__ void fx40_acc(double& acc, float x) {
+  const double d = (double)x;
+  asm volatile("v_fma_f64 %0, %1, %2, %0" : "+v"(acc) : "v"(d), "s"(0x1p40));
+}
+
 // max(d, +0) for finite d in one integer max of the bits: a positive float
 // is a positive integer, a negative one (or -0) a negative integer, which
 // becomes 0, i.e. +0.
@@ -602,35 +622,40 @@ __device__ __forceinline__ double mss_gm_residual(const float* __restrict__ q, i
   return part;
 }
 
-// Double-buffered row passes (16-byte rows, V <= 4 * kMssThreads * kMssPfChunks):
-// a row is requested into registers by mss_issue_row and consumed later, so
-// the next child's row can be in flight while the current one is used.
-// Wave span 256 * kMssPfChunks.
+// Prefetching row passes (16-byte rows, V <= 4 * kMssThreads * kMssPfChunks):
+// rows are requested into registers and consumed later, so the next child's
+// row is in flight while the current one is used.  Wave span
+// 256 * kMssPfChunks.
 constexpr int kMssPfChunks = 8;
 constexpr int kMssPfMaxVocab = 4 * kMssThreads * kMssPfChunks;
-static_assert(kMssLogitsMaxVocab == kMssPfMaxVocab, "logits rows take the double-buffered walk");
+static_assert(kMssLogitsMaxVocab == kMssPfMaxVocab, "logits rows take the prefetching walk");
 
-// Buffer loads with one resource per chunk (base = the chunk's first entry,
-// range = the bytes of the row from there): entries past the row read as
-// zero without a branch or a clamped address, so one offset register serves
-// every chunk (loads under a branch would also make the compiler wait for
-// all outstanding loads at their first use, draining the prefetch).  The
-// row pointer must be uniform: a resource lives in scalar registers.
+// Buffer loads: one resource per row and wave (base = the wave's first
+// entry, range = the row's bytes from there), chunk j at byte 1024*j + 16*lane
+// of it.  Entries past the row read as zero without a branch or a clamped
+// address (loads under a branch would also make the compiler wait for all
+// outstanding loads at their first use, draining the prefetch), and a chunk
+// costs no scalar arithmetic.  The row pointer must be uniform: a resource
+// lives in scalar registers.
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mss_row_rsrc(const float* __restrict__ row, int V) {
+  const int first = 256 * kMssPfChunks * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int bytes = V > first ? 4 * (V - first) : 0;
+  const float* base = V > first ? row + first : row;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ f32x4 mss_rsrc_chunk(__amdgpu_buffer_rsrc_t rs, int j) {
+  return __builtin_bit_cast(
+      f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (int)(threadIdx.x & 63), 1024 * j, 0));
+}
 
 __device__ __forceinline__ void mss_issue_row(const float* __restrict__ row, int V,
                                               f32x4 (&r)[kMssPfChunks]) {
-  const int off = 16 * (int)(threadIdx.x & 63);
-  const int wbase = 256 * kMssPfChunks * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rs = mss_row_rsrc(row, V);
 #pragma unroll
-  for (int j = 0; j < kMssPfChunks; ++j) {
-    const int first = wbase + 256 * j;  // the wave's chunk j (uniform)
-    const int bytes = V > first ? 4 * (V - first) : 0;
-    const float* base = V > first ? row + first : row;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, kBufferWord3);
-    r[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-  }
+  for (int j = 0; j < kMssPfChunks; ++j) r[j] = mss_rsrc_chunk(rs, j);
 }
 
 // s_w[widx(v)] = r (probabilities, or logits made probabilities with `st`);
@@ -667,47 +692,90 @@ __device__ __forceinline__ double mss_regs_to_lds(const f32x4 (&r)[kMssPfChunks]
   return part;
 }
 
-// w = max(w - s*q, +0) in place with q in registers; returns this thread's
-// sum of fx40d(w)
+// The residual of the prefetching walk lives in registers: thread t
+// holds w of its chunks (entries mss_chunk_v<kMssPfChunks>(t, j)) in wr[j],
+// and the speculator's rows stream through one register buffer qr, chunk j
+// of the next row requested as soon as chunk j of the current one is used
+// (one row in flight during a pass, no LDS traffic).  LDS receives w only for
+// the final draw.
+
+// wr = the row loaded into it, as probabilities (LG: logits made
+// probabilities with `st`, 0 past V; rows of probabilities read 0 there)
 template <bool LG>
-__device__ __forceinline__ double mss_residual_regs(const f32x4 (&r)[kMssPfChunks], int V, float s,
-                                                    float* s_w, const RowStats& st, float c) {
-  const int t = threadIdx.x;
-  f32x4* wp = reinterpret_cast<f32x4*>(s_w + mss_slot0<kMssPfChunks>(t));
-  if constexpr (!LG) {
-    // the whole span, without branches: past V both w and q are 0 (see
-    // mss_regs_to_lds), so those entries stay 0.  The LDS reads go out
-    // together, and the exact integer masses go to two sums.
-    f32x4 w[kMssPfChunks];
-#pragma unroll
-    for (int j = 0; j < kMssPfChunks; ++j) w[j] = wp[66 * j];
-    double part[2] = {0.0, 0.0};
+__device__ __forceinline__ void mss_row_regs(f32x4 (&wr)[kMssPfChunks], int V, const RowStats& st, float c) {
+  if constexpr (LG) {
 #pragma unroll
     for (int j = 0; j < kMssPfChunks; ++j) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w[j][e] = clamp_pos(fmaf(-s, r[j][e], w[j][e]));
-        part[e >> 1] += fx40d(w[j][e]);
-      }
-      wp[66 * j] = w[j];
+      const int v = mss_chunk_v<kMssPfChunks>(threadIdx.x, j);
+      wr[j] = v < V ? mss_entry4<LG>(wr[j], v, st, c) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    return part[0] + part[1];
   }
-  double part = 0.0;
+}
+
+// w = max(w - s*q, +0) with q in qr, whose chunk j then receives chunk j of
+// `next`; returns this thread's sum of fx40d(w)
+template <bool LG>
+__device__ __forceinline__ double mss_residual_roll(f32x4 (&wr)[kMssPfChunks], f32x4 (&qr)[kMssPfChunks],
+                                                    const float* __restrict__ next, int V, float s,
+                                                    const RowStats& st, float c) {
+  const __amdgpu_buffer_rsrc_t rs = mss_row_rsrc(next, V);
+  double part[4] = {kFxBias, kFxBias, kFxBias, kFxBias};
+  f64_round_down();
+#pragma unroll
+  for (int j = 0; j < kMssPfChunks; ++j) {
+    f32x4 q = qr[j];
+    if constexpr (LG) {
+      const int v = mss_chunk_v<kMssPfChunks>(threadIdx.x, j);
+      q = v < V ? mss_entry4<LG>(q, v, st, c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // max(w - s*q, +0) as the FMA's clamp to [0, 1] (w <= 1 already; the
+    // clamp gives +0 or -0 for a negative result, which every later use --
+    // the masses, the tests, the draw -- takes as 0)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wr[j][e] = __builtin_amdgcn_fmed3f(fmaf(-s, q[e], wr[j][e]), 0.f, 1.f);
+      fx40_acc(part[e], wr[j][e]);
+    }
+    // chunk j of q is used up; the request for its successor is ordered
+    // after that use (the empty asm ties its resource to the last w), so the
+    // new chunk can take the old one's registers: a copy at the end of the
+    // pass would wait for every request in flight
+    __amdgpu_buffer_rsrc_t rj = rs;
+    asm volatile("" : "+s"(rj) : "v"(wr[j][3]));
+    qr[j] = mss_rsrc_chunk(rj, j);
+    // and no work of a later chunk is scheduled ahead of this one (it would
+    // wait for that chunk's request, issued late in the previous pass)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  f64_round_nearest();
+  return ((part[0] - kFxBias) + (part[1] - kFxBias)) + ((part[2] - kFxBias) + (part[3] - kFxBias));
+}
+
+// s_w[widx(v)] = w for the final draw (LG: the chunks below V; otherwise the
+// LDS holds the whole span)
+template <bool LG>
+__device__ __forceinline__ void mss_regs_store(const f32x4 (&wr)[kMssPfChunks], int V, float* s_w) {
+  const int t = threadIdx.x;
+  f32x4* wp = reinterpret_cast<f32x4*>(s_w + mss_slot0<kMssPfChunks>(t));
 #pragma unroll
   for (int j = 0; j < kMssPfChunks; ++j)
-    if (mss_chunk_v<kMssPfChunks>(t, j) < V) {
-      f32x4 w = wp[66 * j];
-      const f32x4 q = mss_entry4<LG>(r[j], mss_chunk_v<kMssPfChunks>(t, j), st, c);
+    if (!LG || mss_chunk_v<kMssPfChunks>(t, j) < V) wp[66 * j] = wr[j];
+}
+
+// w[x] from the registers of the thread that holds it (x = 2048*wave +
+// 256*j + 4*lane + e), stored to *dst by that thread
+__device__ __forceinline__ void mss_regs_entry(const f32x4 (&wr)[kMssPfChunks], int x, float* dst) {
+  static_assert(256 * kMssPfChunks == 2048, "wave span");
+  if ((int)threadIdx.x == ((x >> 11) << 6) + ((x & 255) >> 2)) {
+    const int jx = (x >> 8) & (kMssPfChunks - 1), ex = x & 3;
+    float val = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float d = fmaf(-s, q[e], w[e]);
-        w[e] = clamp_pos(d);
-        part += fx40d(w[e]);
-      }
-      wp[66 * j] = w;
-    }
-  return part;
+    for (int j = 0; j < kMssPfChunks; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j == jx && e == ex) val = wr[j][e];
+    *dst = val;
+  }
 }
 
 // LG: llm and ssm hold logits; st_llm / st_ssm [B*N] their rows' statistics
@@ -728,6 +796,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   __shared__ int32_t s_tok[kMaxNodes];
   __shared__ int32_t s_path[kMaxNodes];
   __shared__ float s_rq[kMaxNodes];  // r_c * q_c[token c]: the left side of c's test at s = 1
+  __shared__ float s_wx[2];  // w[token] of the next child tested (alternating slots)
   __shared__ uint32_t s_bonus[kMaxNodes];  // the final draw's 24-bit integer if the walk ends at u
   __shared__ unsigned long long s_kids[kMaxNodes][2];
   __shared__ uint64_t s_first_ok[2];
@@ -828,15 +897,27 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   }
   __syncthreads();  // the children bitsets are complete
   bool first_ok = false;
+  float r = ua;
+  if (seeded && t >= 1 && t < nU) {  // t is the j-th child of p, j = its lower siblings
+    const int p = s_par[t];
+    const uint64_t lo = s_kids[p][0], hi = s_kids[p][1];
+    const int j = t < 64 ? __popcll(lo & ((1ull << t) - 1ull))
+                         : __popcll(lo) + __popcll(hi & ((1ull << (t - 64)) - 1ull));
+    r = (float)mss_draw24(dr.seed, dr.step, (uint64_t)j, p, b) * 0x1p-24f;
+  }
+  // the root's row and that of its first child, node 1 (whose parent can
+  // only be the root), are requested now and stream in while the first tests
+  // are made; the walk starts from them when that child's test fails.  (The
+  // requests go out unconditionally -- a root without children reads its own
+  // row twice -- so that the waits for the loads above stay exact.)
+  f32x4 wr[kMssPfChunks], qr[kMssPfChunks];
+  const bool pre = PF && nU >= 2;
+  if constexpr (PF) {
+    mss_issue_row(llm + rowN * V, V, wr);
+    mss_issue_row(pre ? ssm + (rowN + 1) * V : ssm + rowN * V, V, qr);
+  }
   if (t >= 1 && t < nU) {
     const int p = s_par[t];
-    float r = ua;
-    if (seeded) {  // t is the j-th child of p, j = its lower siblings
-      const uint64_t lo = s_kids[p][0], hi = s_kids[p][1];
-      const int j = t < 64 ? __popcll(lo & ((1ull << t) - 1ull))
-                           : __popcll(lo) + __popcll(hi & ((1ull << (t - 64)) - 1ull));
-      r = (float)mss_draw24(dr.seed, dr.step, (uint64_t)j, p, b) * 0x1p-24f;
-    }
     const float rq = r * qx;
     s_rq[t] = rq;
     first_ok = rq * 1.0f < px;
@@ -868,14 +949,69 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   // the walk's barriers).  `totals`: s_redd holds the masses of the waves'
   // ranges of what s_w holds for the final draw (the last residual pass, or
   // the copy of p_u the draw comes from, left them there).
-  int u = 0, depth = 0;
+  int u = 0, depth = 0, wx_slot = 0;
   bool totals = false;
   auto descend = [&](int c) {
     u = c;
     ++depth;
     if (t == 0) s_path[depth] = c;
   };
-  for (;;) {
+  // PF: the residual tests at node u once its first child c0 has failed its
+  // test, with p_u in wr and q of c0 in qr (requested by the caller; k0/k1
+  // the other children).  The residual stays in registers, and while child
+  // c's residual pass runs, the next child's row streams into qr chunk by
+  // chunk (after the last child, c's row again, from cache, so the request
+  // is never under a branch).  w[x] of the child tested next goes through
+  // LDS from the thread that holds it, published by the pass's reduction;
+  // its slots alternate, so no barrier is needed before the next pass writes
+  // one.  Returns the accepted child, or -1 when the walk ends at u (the
+  // draw's row then in s_w, the masses of its waves' ranges in s_redd).
+  auto pf_node = [&](int u, uint64_t k0, uint64_t k1, int c0, f32x4 (&wr)[kMssPfChunks],
+                     f32x4 (&qr)[kMssPfChunks]) -> int {
+    mss_row_regs<LG>(wr, V, p_stats(u), lr.c);
+    float s = 1.0f;
+    int ccur = c0;
+    for (;;) {
+      int cn = -1;
+      if (k0) {
+        cn = __ffsll((unsigned long long)k0) - 1;
+        k0 &= k0 - 1;
+      } else if (k1) {
+        cn = 64 + __ffsll((unsigned long long)k1) - 1;
+        k1 &= k1 - 1;
+      }
+      const int crow = ccur;  // the child whose q row is in qr
+      ccur = cn;
+      const double part = mss_residual_roll<LG>(wr, qr, ssm + (rowN + (cn >= 0 ? cn : crow)) * V, V, s,
+                                                q_stats(crow), lr.c);
+      if (cn >= 0) mss_regs_entry(wr, s_tok[cn], &s_wx[wx_slot]);
+      else mss_regs_store<LG>(wr, V, s_w);  // every child rejected: the draw reads w
+      const double S = block_sum_f64(part, s_redd);  // its barriers publish s_wx / s_w
+      s = (float)(S * 0x1p-40);
+      if (s == 0.0f) {  // empty residual: stop testing, sample from p_u
+        mss_issue_row(llm + (rowN + u) * V, V, qr);
+        __syncthreads();
+        block_sum_f64(mss_regs_to_lds<LG>(qr, V, s_w, p_stats(u), lr.c), s_redd);
+        return -1;
+      }
+      if (cn < 0) return -1;  // every child rejected: bonus from the residual
+      const bool accept = s_rq[cn] * s < s_wx[wx_slot];
+      wx_slot ^= 1;
+      if (accept) return cn;
+    }
+  };
+  bool ended = false;
+  if constexpr (PF) {
+    // the root, with the rows requested during the set-up, if its first
+    // child (node 1) failed its test
+    if (pre && !(s_first_ok[0] & 2ull)) {
+      const int nx = pf_node(0, uniform_u64(s_kids[0][0]) & ~2ull, uniform_u64(s_kids[0][1]), 1, wr, qr);
+      totals = true;
+      if (nx < 0) ended = true;
+      else descend(nx);
+    }
+  }
+  while (!ended) {
     // the same in every lane: scalar registers (children, nodes and row
     // addresses derived from them stay scalar)
     uint64_t k0 = uniform_u64(s_kids[u][0]), k1 = uniform_u64(s_kids[u][1]);
@@ -902,64 +1038,16 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     }
     // first child rejected: sequential residual tests at u
     if constexpr (PF) {
-      // p_u and q of the first child are requested together; while child c's
-      // residual pass runs, the next child's row is already in flight (the
-      // buffers alternate by unrolling: copying a register row would wait
-      // for its loads)
+      // p_u and q of the first child, requested together
       f32x4 ra[kMssPfChunks], rb[kMssPfChunks];
       mss_issue_row(llm + (rowN + u) * V, V, ra);
       mss_issue_row(ssm + (rowN + c0) * V, V, rb);
       if (k0) k0 &= k0 - 1;
       else k1 &= k1 - 1;
-      __syncthreads();  // every thread has read the old residual
-      mss_regs_to_lds<LG>(ra, V, s_w, p_stats(u), lr.c);
-      __syncthreads();
-      float s = 1.0f;
-      int next = -1, ccur = c0;
-      // one rejected child ccur whose row is in cur: prefetch the next child
-      // into nxt (after the last child, ccur's row again, from cache, so the
-      // request is never under a branch), w = max(w - s*q, +0), then test
-      // the next child; true = done
-      auto pass = [&](f32x4 (&cur)[kMssPfChunks], f32x4 (&nxt)[kMssPfChunks]) -> bool {
-        int cn = -1;
-        if (k0) {
-          cn = __ffsll((unsigned long long)k0) - 1;
-          k0 &= k0 - 1;
-        } else if (k1) {
-          cn = 64 + __ffsll((unsigned long long)k1) - 1;
-          k1 &= k1 - 1;
-        }
-        mss_issue_row(ssm + (rowN + (cn >= 0 ? cn : ccur)) * V, V, nxt);
-        const int crow = ccur;  // the child whose q row is in cur
-        ccur = cn;
-        const double part = mss_residual_regs<LG>(cur, V, s, s_w, q_stats(crow), lr.c);
-        const double S = block_sum_f64(part, s_redd);  // its barriers publish s_w
-        s = (float)(S * 0x1p-40);
-        if (s == 0.0f) {  // empty residual: stop testing, sample from p_u
-          mss_issue_row(llm + (rowN + u) * V, V, cur);  // cur is consumed
-          __syncthreads();
-          block_sum_f64(mss_regs_to_lds<LG>(cur, V, s_w, p_stats(u), lr.c), s_redd);
-          totals = true;
-          return true;
-        }
-        if (cn < 0) {  // every child rejected: bonus from the residual
-          totals = true;
-          return true;
-        }
-        const bool accept = s_rq[cn] * s < s_w[widx(s_tok[cn])];
-        __syncthreads();  // every thread has read w[x] before it is updated
-        if (accept) {
-          next = cn;
-          return true;
-        }
-        return false;
-      };
-      for (;;) {
-        if (pass(rb, ra)) break;
-        if (pass(ra, rb)) break;
-      }
-      if (next < 0) break;  // bonus from the residual in s_w (or p_u)
-      descend(next);
+      const int nx = pf_node(u, k0, k1, c0, ra, rb);
+      totals = true;
+      if (nx < 0) break;  // bonus from the residual in s_w (or p_u)
+      descend(nx);
       continue;
     }
     load_p_row(u);
@@ -1279,7 +1367,7 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
   const bool lg = lr.st_llm != nullptr;
   // the residual in global memory (host checks: V % 4 == 0, 16-byte rows,
   // gm_w): vocabularies beyond the LDS, and logits rows beyond the
-  // double-buffered walk's registers
+  // prefetching walk's registers
   if (V > kMssMaxVocab || (lg && V > kMssPfMaxVocab)) {
     auto kern = lg ? mss_kernel<true, false, true, true> : mss_kernel<true, false, false, true>;
     hipLaunchKernelGGL(kern, dim3(B), dim3(kMssThreads), 0, s, N, V, parents, tokens, n_nodes,
@@ -1288,7 +1376,7 @@ hipError_t launch_verify_mss(int B, int N, int V, const int32_t* parents,
   }
   const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(llm) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(ssm) & 15) == 0;
-  // widx(V - 1) + 1, 16-byte padded; the double-buffered walk over
+  // widx(V - 1) + 1, 16-byte padded; the prefetching walk over
   // probabilities keeps its whole span (kMssPfMaxVocab entries) in LDS
   const int Vl = (vec && !lg && V <= kMssPfMaxVocab) ? kMssPfMaxVocab : V;
   const size_t lds = (size_t)(Vl + 4 * (Vl >> 7) + 4) * sizeof(float);
