@@ -14,6 +14,36 @@
 
 namespace ttv {
 
+// Inclusive prefix sum over the 64 lanes in lane order, all in the VALU (all
+// lanes active): within each 16-lane row lane i adds the row's lanes i-1,
+// i-2..i-3, i-4..i-7, i-8..i-15 (row_shr by 1, 2, 4 and 8; a lane shifted in
+// from outside the row reads 0); then row_bcast:15 adds the last lane of rows
+// 0 and 2 to every lane of rows 1 and 3, and row_bcast:31 the last lane of
+// row 1 to rows 2 and 3 (rows a move does not write keep 0).  Exact for
+// integer-valued doubles below 2^53.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64_rows(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xF, true);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_inclusive_sum_f64(double v) {
+  v += dpp_f64_rows<kDppRowShr1, 0xF>(v);
+  v += dpp_f64_rows<kDppRowShr2, 0xF>(v);
+  v += dpp_f64_rows<kDppRowShr4, 0xF>(v);
+  v += dpp_f64_rows<kDppRowShr8, 0xF>(v);
+  v += dpp_f64_rows<kDppRowBcast15, 0xA>(v);
+  v += dpp_f64_rows<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
 // ====================================================================== //
 // Greedy                                                                   //
 // ====================================================================== //
@@ -713,12 +743,13 @@ __device__ __forceinline__ void mss_row_regs(f32x4 (&wr)[kMssPfChunks], int V, c
 }
 
 // w = max(w - s*q, +0) with q in qr, whose chunk j then receives chunk j of
-// `next`; returns this thread's sum of fx40d(w)
+// `next` (nV of its entries; nV = 0 reads zeros without touching memory);
+// returns this thread's sum of fx40d(w)
 template <bool LG>
 __device__ __forceinline__ double mss_residual_roll(f32x4 (&wr)[kMssPfChunks], f32x4 (&qr)[kMssPfChunks],
-                                                    const float* __restrict__ next, int V, float s,
-                                                    const RowStats& st, float c) {
-  const __amdgpu_buffer_rsrc_t rs = mss_row_rsrc(next, V);
+                                                    const float* __restrict__ next, int nV, int V,
+                                                    float s, const RowStats& st, float c) {
+  const __amdgpu_buffer_rsrc_t rs = mss_row_rsrc(next, nV);
   double part[4] = {kFxBias, kFxBias, kFxBias, kFxBias};
   f64_round_down();
 #pragma unroll
@@ -960,8 +991,8 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   // test, with p_u in wr and q of c0 in qr (requested by the caller; k0/k1
   // the other children).  The residual stays in registers, and while child
   // c's residual pass runs, the next child's row streams into qr chunk by
-  // chunk (after the last child, c's row again, from cache, so the request
-  // is never under a branch).  w[x] of the child tested next goes through
+  // chunk (after the last child, requests of an empty range, which return
+  // zeros without a memory access, so that no request is under a branch).  w[x] of the child tested next goes through
   // LDS from the thread that holds it, published by the pass's reduction;
   // its slots alternate, so no barrier is needed before the next pass writes
   // one.  Returns the accepted child, or -1 when the walk ends at u (the
@@ -982,8 +1013,8 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       }
       const int crow = ccur;  // the child whose q row is in qr
       ccur = cn;
-      const double part = mss_residual_roll<LG>(wr, qr, ssm + (rowN + (cn >= 0 ? cn : crow)) * V, V, s,
-                                                q_stats(crow), lr.c);
+      const double part = mss_residual_roll<LG>(wr, qr, ssm + (rowN + (cn >= 0 ? cn : crow)) * V,
+                                                cn >= 0 ? V : 0, V, s, q_stats(crow), lr.c);
       if (cn >= 0) mss_regs_entry(wr, s_tok[cn], &s_wx[wx_slot]);
       else mss_regs_store<LG>(wr, V, s_w);  // every child rejected: the draw reads w
       const double S = block_sum_f64(part, s_redd);  // its barriers publish s_wx / s_w
@@ -1163,12 +1194,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
             for (int e = 0; e < 4; ++e) mine += v + e < v_hi ? fx40d(w4[e]) : 0.0;
           }
         }
-        double incl = mine;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const double o = __shfl_up(incl, d);
-          if (lane >= d) incl += o;
-        }
+        const double incl = wave_inclusive_sum_f64(mine);
         const double lo = before + (incl - mine);
         const uint64_t crossing = __ballot(lo <= T && T < before + incl);
         if (crossing != 0ull) {
@@ -1185,12 +1211,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) g += v + e < vhiL ? fx40d(w4[e]) : 0.0;
           }
-          double gin = g;
-#pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            const double o = __shfl_up(gin, d);
-            if (lane >= d) gin += o;
-          }
+          const double gin = wave_inclusive_sum_f64(g);
           double cum = loL + (gin - g);
           if (cum <= T && T < loL + gin) {
             int pick = vhiL - 1;
@@ -1281,12 +1302,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
           gsum[i] = g;
           mine += g;
         }
-        double incl = mine;
-  #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const double o = __shfl_up(incl, d);
-          if (lane >= d) incl += o;
-        }
+        const double incl = wave_inclusive_sum_f64(mine);
         const double lo = before + (incl - mine), hi = before + incl;
         if (lo <= T && T < hi) {
           // the group that crosses T from the register sums, then its entries
