@@ -455,6 +455,19 @@ __device__ __forceinline__ double block_sum_f64(double v, double* s_redd) {
   return t;
 }
 
+// The same with one barrier, for reductions that alternate between two slot
+// arrays (a late reader of the previous reduction's slots is never
+// overwritten: the next write to them follows a barrier it has passed); lane
+// w of every wave reads wave w's sum, and a wave sum adds them (exact, so in
+// any order).
+__device__ __forceinline__ double block_sum_f64_alt(double v, double* slots) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  v = wave_allsum_f64(v);
+  if (lane == 0) slots[wave] = v;
+  __syncthreads();
+  return wave_allsum_f64(lane < kMssThreads / 64 ? slots[lane] : 0.0);
+}
+
 
 // Row passes.  Every wavefront owns a contiguous range of the vocabulary,
 // wave w the entries [w*WS, (w+1)*WS), so the per-wave sums of a pass's
@@ -831,7 +844,8 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   __shared__ uint32_t s_bonus[kMaxNodes];  // the final draw's 24-bit integer if the walk ends at u
   __shared__ unsigned long long s_kids[kMaxNodes][2];
   __shared__ uint64_t s_first_ok[2];
-  __shared__ double s_redd[kMssThreads / 64];
+  __shared__ double s_red3[3][kMssThreads / 64];  // [0]: two-barrier sums, [1], [2]: alternating
+  double* const s_redd = s_red3[0];
   __shared__ int s_status, s_pick, s_len, s_nodes;
   __shared__ float s_av[GM ? kMssWaves : 1];  // the all-zero fallback of the global residual
   __shared__ int s_ai[GM ? kMssWaves : 1];
@@ -980,8 +994,9 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   // the walk's barriers).  `totals`: s_redd holds the masses of the waves'
   // ranges of what s_w holds for the final draw (the last residual pass, or
   // the copy of p_u the draw comes from, left them there).
-  int u = 0, depth = 0, wx_slot = 0;
+  int u = 0, depth = 0, wx_slot = 0, red_alt = 0;
   bool totals = false;
+  const double* s_tot = s_redd;  // the slots holding the masses of the waves' ranges (totals)
   auto descend = [&](int c) {
     u = c;
     ++depth;
@@ -1017,12 +1032,23 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
                                                 cn >= 0 ? V : 0, V, s, q_stats(crow), lr.c);
       if (cn >= 0) mss_regs_entry(wr, s_tok[cn], &s_wx[wx_slot]);
       else mss_regs_store<LG>(wr, V, s_w);  // every child rejected: the draw reads w
-      const double S = block_sum_f64(part, s_redd);  // its barriers publish s_wx / s_w
+      // its barriers publish s_wx / s_w (the walk over logits, short of
+      // registers, keeps the two-barrier form)
+      double S;
+      if constexpr (LG) {
+        S = block_sum_f64(part, s_redd);
+      } else {
+        double* const sl = s_red3[1 + red_alt];
+        red_alt ^= 1;
+        S = block_sum_f64_alt(part, sl);
+        s_tot = sl;
+      }
       s = (float)(S * 0x1p-40);
       if (s == 0.0f) {  // empty residual: stop testing, sample from p_u
         mss_issue_row(llm + (rowN + u) * V, V, qr);
         __syncthreads();
         block_sum_f64(mss_regs_to_lds<LG>(qr, V, s_w, p_stats(u), lr.c), s_redd);
+        s_tot = s_redd;
         return -1;
       }
       if (cn < 0) return -1;  // every child rejected: bonus from the residual
@@ -1054,6 +1080,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
         // the masses of the waves' ranges come with the copy; the
         // reduction's barriers publish s_w
         block_sum_f64(mss_regs_to_lds<LG>(ra, V, s_w, p_stats(u), lr.c), s_redd);
+        s_tot = s_redd;
         totals = true;
       } else {
         load_p_row(u);
@@ -1164,7 +1191,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     const int span = 256 * gmCH, P = 4 * gmCH;
     double Sd = 0.0;
 #pragma unroll
-    for (int w = 0; w < kMssWaves; ++w) Sd += s_redd[w];
+    for (int w = 0; w < kMssWaves; ++w) Sd += s_tot[w];
     if (Sd > 0.0) {
       const uint64_t S = (uint64_t)Sd, R = s_bonus[u];
       const double T = (double)(R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24));  // floor(R*S/2^24)
@@ -1173,7 +1200,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       bool found = false;
 #pragma unroll
       for (int w = 0; w < kMssWaves; ++w) {
-        const double g = s_redd[w];
+        const double g = s_tot[w];
         if (!found && before + g > T) {
           ws = w;
           found = true;
@@ -1264,11 +1291,12 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
         }
       }
       block_sum_f64(part, s_redd);  // s_redd[w] = mass of wave w's range
+      s_tot = s_redd;
     }
     // masses below 2^53: exact in doubles, compared as doubles
     double Sd = 0.0;
   #pragma unroll
-    for (int w = 0; w < kMssWaves; ++w) Sd += s_redd[w];
+    for (int w = 0; w < kMssWaves; ++w) Sd += s_tot[w];
     if (Sd > 0.0) {
       const uint64_t S = (uint64_t)Sd, R = s_bonus[u];
       const double T = (double)(R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24));  // floor(R*S/2^24)
@@ -1277,7 +1305,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       bool found = false;
   #pragma unroll
       for (int w = 0; w < kMssWaves; ++w) {
-        const double g = s_redd[w];
+        const double g = s_tot[w];
         if (!found && before + g > T) {
           ws = w;
           found = true;
