@@ -34,6 +34,12 @@ __device__ __forceinline__ double dpp_f64_rows(double x) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xF, true);
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 __device__ __forceinline__ double wave_inclusive_sum_f64(double v) {
   v += dpp_f64_rows<kDppRowShr1, 0xF>(v);
   v += dpp_f64_rows<kDppRowShr2, 0xF>(v);
@@ -1293,26 +1299,19 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       block_sum_f64(part, s_redd);  // s_redd[w] = mass of wave w's range
       s_tot = s_redd;
     }
-    // masses below 2^53: exact in doubles, compared as doubles
-    double Sd = 0.0;
-  #pragma unroll
-    for (int w = 0; w < kMssWaves; ++w) Sd += s_tot[w];
+    // masses below 2^53: exact in doubles, compared as doubles.  Lane w of
+    // every wave takes wave w's mass; their prefix sums give the total, the
+    // first wave whose cumulative mass exceeds the target (a ballot) and the
+    // mass before it.
+    const int lw = t & 63;
+    const double cw = wave_inclusive_sum_f64(lw < kMssWaves ? s_tot[lw] : 0.0);
+    const double Sd = readlane_f64(cw, kMssWaves - 1);
     if (Sd > 0.0) {
       const uint64_t S = (uint64_t)Sd, R = s_bonus[u];
       const double T = (double)(R * (S >> 24) + ((R * (S & 0xffffffull)) >> 24));  // floor(R*S/2^24)
-      double before = 0.0;
-      int ws = kMssWaves - 1;
-      bool found = false;
-  #pragma unroll
-      for (int w = 0; w < kMssWaves; ++w) {
-        const double g = s_tot[w];
-        if (!found && before + g > T) {
-          ws = w;
-          found = true;
-        } else if (!found) {
-          before += g;
-        }
-      }
+      const uint64_t past = __ballot(lw < kMssWaves && cw > T);  // T < S: wave kMssWaves-1 is set
+      const int ws = past ? __ffsll((unsigned long long)past) - 1 : kMssWaves - 1;
+      const double before = ws > 0 ? readlane_f64(cw, ws - 1) : 0.0;
       if (wave == ws) {
         constexpr int P = kSpan / 64, kG = P / 4;
         const int lane = t & 63;
