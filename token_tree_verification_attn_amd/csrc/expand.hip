@@ -3,15 +3,15 @@
 // speculative model at a node become that node's children).
 //
 // One 512-thread workgroup per (request b, frontier entry f), in three steps:
-//   1. read the row once for each thread's maximum; the k-th largest of
-//      those 512 maxima, T, is a lower bound of the row's k-th largest
-//      probability.  A row of up to 32768 entries is requested whole at the
+//   1. read the row once for each thread's maximum; T, a lower bound of the
+//      row's k-th largest probability, is the k-th largest of the 8 wave
+//      maxima (k <= 8) or of the 512 thread maxima.  A row of up to 32768 entries is requested whole at the
 //      start (16 16-byte loads per thread, right after the frontier's, so
 //      the frontier check does not wait for them) and stays in registers;
 //      a longer one is streamed (8 loads in flight per thread);
 //   2. gather the entries >= T into an LDS buffer (usually only a little
-//      more than k of them), from the registers or by reading the row again
-//      (then from L2);
+//      more than k of them), from the registers (a ballot per entry, in the
+//      waves that hold any) or by reading the row again (then from L2);
 //   3. wave 0 takes the k best of the buffer by k rounds of a wave arg-max,
 //      each over the entries that rank after the previous winner (higher
 //      probability first, then the lower token id), so the order is exact
@@ -55,6 +55,7 @@ __global__ __launch_bounds__(kExpandThreads) void tree_expand_kernel(
   __shared__ float s_cv[kExpandCandidates];
   __shared__ int s_ci[kExpandCandidates];
   __shared__ float s_wv[kExpandWaves];
+  __shared__ float s_wm[kExpandWaves];
   __shared__ int s_wi[kExpandWaves];
   __shared__ int s_cnt;
   __shared__ float s_thr;
@@ -150,47 +151,102 @@ __global__ __launch_bounds__(kExpandThreads) void tree_expand_kernel(
   // let the compiler move the row's loads behind the frontier check.
   const bool active = st == TTV_OK && fr >= 0;
 
+  // ---- T.  k <= 8: the k-th largest of the 8 wave maxima (k distinct
+  // entries of the row are >= it, so the row's k best are too), found by
+  // every thread after one barrier.  Larger k: the k-th largest of the 512
+  // thread maxima, found by wave 0 (k rounds, each removing one copy of the
+  // largest) and handed over through LDS.
+  const float wmax = wave_allmax_f32(tmax);
+  if (lane == 0) s_wm[wave] = wmax;
   s_max[tid] = tmax;
   if (tid == 0) s_cnt = 0;
   __syncthreads();
-  if (wave == 0) {
-    constexpr int PER = kExpandThreads / 64;
-    float a[PER];
+  float thr = -INFINITY;
+  if (k <= kExpandWaves) {
+    float a[kExpandWaves];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) a[j] = s_max[j * 64 + lane];
-    float thr = -INFINITY;
-    for (int r = 0; r < k; ++r) {  // remove one copy of the largest per round
-      float lm = a[0];
+    for (int w = 0; w < kExpandWaves; ++w) a[w] = s_wm[w];
+    for (int r = 0; r < k; ++r) {
+      float m = a[0];
 #pragma unroll
-      for (int j = 1; j < PER; ++j) lm = fmaxf(lm, a[j]);
-      const float wm = wave_allmax_f32(lm);
-      const uint64_t has = __ballot(lm == wm);
-      if (lane == __ffsll((unsigned long long)has) - 1) {
-        bool done = false;
+      for (int w = 1; w < kExpandWaves; ++w) m = fmaxf(m, a[w]);
+      bool done = false;
 #pragma unroll
-        for (int j = 0; j < PER; ++j)
-          if (!done && a[j] == wm) {
-            a[j] = -INFINITY;
-            done = true;
-          }
-      }
-      thr = wm;
+      for (int w = 0; w < kExpandWaves; ++w)
+        if (!done && a[w] == m) {
+          a[w] = -INFINITY;
+          done = true;
+        }
+      thr = m;
     }
-    if (lane == 0) s_thr = thr;
+  } else {
+    if (wave == 0) {
+      constexpr int PER = kExpandThreads / 64;
+      float a[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) a[j] = s_max[j * 64 + lane];
+      float t = -INFINITY;
+      for (int r = 0; r < k; ++r) {
+        float lm = a[0];
+#pragma unroll
+        for (int j = 1; j < PER; ++j) lm = fmaxf(lm, a[j]);
+        const float wm = wave_allmax_f32(lm);
+        const uint64_t has = __ballot(lm == wm);
+        if (lane == __ffsll((unsigned long long)has) - 1) {
+          bool done = false;
+#pragma unroll
+          for (int j = 0; j < PER; ++j)
+            if (!done && a[j] == wm) {
+              a[j] = -INFINITY;
+              done = true;
+            }
+        }
+        t = wm;
+      }
+      if (lane == 0) s_thr = t;
+    }
+    __syncthreads();
+    thr = s_thr;
   }
-  __syncthreads();
 
-  // ---- 2. the entries >= T
-  const float thr = s_thr;
-  visit_row([&](float v, int i) {
-    if (v >= thr) {
-      const int slot = atomicAdd(&s_cnt, 1);
-      if (slot < kExpandCandidates) {
-        s_cv[slot] = v;
-        s_ci[slot] = i;
+  // ---- 2. the entries >= T.  From the registers, a wave whose threads'
+  // maxima are all below T has none; the others test their entries with a
+  // ballot each, and the wave takes the slots of an entry's hits with one
+  // LDS atomic (entries >= T are few: usually a little more than k).
+  if (in_regs) {
+    if (__ballot(tmax >= thr) != 0ull) {
+      const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int u = 0; u < kExpandRegQuads; ++u) {
+        const int x = tid + u * kExpandThreads;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool hit = x < n4 && rq[u][e] >= thr;
+          const uint64_t m = __ballot(hit);
+          if (m != 0ull) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&s_cnt, __popcll(m));
+            base = __builtin_amdgcn_readfirstlane(base);
+            const int slot = base + __popcll(m & below);
+            if (hit && slot < kExpandCandidates) {
+              s_cv[slot] = rq[u][e];
+              s_ci[slot] = 4 * x + e;
+            }
+          }
+        }
       }
     }
-  });
+  } else {
+    stream([&](float v, int i) {
+      if (v >= thr) {
+        const int slot = atomicAdd(&s_cnt, 1);
+        if (slot < kExpandCandidates) {
+          s_cv[slot] = v;
+          s_ci[slot] = i;
+        }
+      }
+    });
+  }
   __syncthreads();
   const int cnt = s_cnt;
 
@@ -200,10 +256,17 @@ __global__ __launch_bounds__(kExpandThreads) void tree_expand_kernel(
   int pi = -1;
   if (cnt <= kExpandCandidates) {
     if (wave != 0) return;
+    // the first 64 candidates stay in registers across the rounds
+    const float cv0 = lane < cnt ? s_cv[lane] : -INFINITY;
+    const int ci0 = lane < cnt ? s_ci[lane] : INT_MAX;
     for (int j = 0; j < k; ++j) {
       float bv = -INFINITY;
       int bi = INT_MAX;
-      for (int c = lane; c < cnt; c += 64) {
+      if (lane < cnt && ranks_before(pv, pi, cv0, ci0)) {
+        bv = cv0;
+        bi = ci0;
+      }
+      for (int c = lane + 64; c < cnt; c += 64) {
         const float v = s_cv[c];
         const int i = s_ci[c];
         if (ranks_before(pv, pi, v, i) && ranks_before(v, i, bv, bi)) {
