@@ -707,6 +707,17 @@ __device__ __forceinline__ void mss_issue_row(const float* __restrict__ row, int
   for (int j = 0; j < kMssPfChunks; ++j) r[j] = mss_rsrc_chunk(rs, j);
 }
 
+// Two rows, their chunks requested in turn.
+__device__ __forceinline__ void mss_issue_rows2(const float* __restrict__ a, const float* __restrict__ b,
+                                                int V, f32x4 (&ra)[kMssPfChunks], f32x4 (&rb)[kMssPfChunks]) {
+  const __amdgpu_buffer_rsrc_t sa = mss_row_rsrc(a, V), sb = mss_row_rsrc(b, V);
+#pragma unroll
+  for (int j = 0; j < kMssPfChunks; ++j) {
+    ra[j] = mss_rsrc_chunk(sa, j);
+    rb[j] = mss_rsrc_chunk(sb, j);
+  }
+}
+
 // s_w[widx(v)] = r (probabilities, or logits made probabilities with `st`);
 // returns this thread's sum of fx40d of them (computed only where used)
 template <bool LG>
@@ -872,41 +883,121 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   auto p_stats = [&](int u) { return LG ? lr.st_llm[rowN + u] : RowStats{}; };
   auto q_stats = [&](int c) { return LG ? lr.st_ssm[rowN + c] : RowStats{}; };
   // with the commit: thread 0 alone reads the prefix length (the others take
-  // it from LDS); its write of the new one, which may alias it, depends on
-  // that read, and only this workgroup touches entry b
+  // it from LDS after the set-up's barrier); its write of the new one, which
+  // may alias it, depends on that read, and only this workgroup touches
+  // entry b
   const bool commit = cm.k_tree != nullptr;
-  // ---- tree, tokens and the children of every node
-  if (t < N) {
-    s_par[t] = parents[rowN + t];
-    s_tok[t] = tokens[rowN + t];
-    s_kids[t][0] = 0ull;
-    s_kids[t][1] = 0ull;
+  // ---- the set-up, with one barrier.  Wave 0 alone (lane l holds nodes l
+  // and l + 64, so its LDS accesses need no barrier) reads the tree, checks
+  // it, builds the children bitsets and makes the first-attempt test of
+  // every non-root node (r*q[x] against p[x] of its parent, mass 1; only
+  // first children use it), the gathers going out first.  Wave 1 draws the
+  // final-draw integer of every node (the walk may end anywhere).  With the
+  // prefetching walk, the root's row and that of node 1 (the root's first
+  // child in every tree of two or more nodes) are requested by every wave --
+  // at once by the others, after their work by waves 0 and 1 -- so that they
+  // stream in during the set-up; the walk starts from them when node 1's
+  // test fails.  (A one-node tree reads the root's q row instead: unused.)
+  f32x4 wr[kMssPfChunks], qr[kMssPfChunks];
+  const float* const p0row = llm + rowN * V;
+  const float* const q1row = ssm + (rowN + (N >= 2 ? 1 : 0)) * V;
+  if constexpr (PF) {
+    if (wave >= 2) mss_issue_rows2(p0row, q1row, V, wr, qr);
   }
-  if (t == 0) {
-    s_status = 0;
-    s_len = commit ? cm.cache_len_in[b] : 0;
-    s_nodes = nodes_raw(n_nodes, b, N);
-    s_path[0] = 0;
+  if (wave == 0) {
+    const int lane = t;
+    const int n_raw0 = nodes_raw(n_nodes, b, N);
+    const int nU0 = nodes_used(n_raw0, N);
+    int par[2], tok[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = lane + 64 * h;
+      par[h] = i < N ? parents[rowN + i] : -1;
+      tok[h] = i < N ? tokens[rowN + i] : 0;
+      if (i < N) {
+        s_par[i] = par[h];
+        s_tok[i] = tok[h];
+        s_kids[i][0] = 0ull;
+        s_kids[i][1] = 0ull;
+      }
+    }
+    if (lane == 0) {
+      s_len = commit ? cm.cache_len_in[b] : 0;
+      s_nodes = n_raw0;
+      s_path[0] = 0;
+    }
+    bool bad_tree = false, bad_tok = false;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = lane + 64 * h;
+      if (i < nU0) {
+        bad_tree |= (i == 0) ? (par[h] != -1) : (par[h] < 0 || par[h] >= i);
+        bad_tok |= i > 0 && (tok[h] < 0 || tok[h] >= V);
+      }
+    }
+    const int st0 = (__ballot(bad_tree) ? 1 : 0) | ((__ballot(bad_tok) || !nodes_ok(n_raw0, N)) ? 2 : 0);
+    if (lane == 0) s_status = st0;
+    if (st0 == 0) {
+      float qx[2] = {0.f, 0.f}, px[2] = {0.f, 0.f}, ua[2] = {0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = lane + 64 * h;
+        if (i >= 1 && i < nU0) {
+          atomicOr(&s_kids[par[h]][i >> 6], 1ull << (i & 63));
+          qx[h] = ssm[(rowN + i) * V + tok[h]];
+          px[h] = llm[(rowN + par[h]) * V + tok[h]];
+          if constexpr (LG) {
+            qx[h] = row_prob(lr.st_ssm[rowN + i], lr.c, qx[h], tok[h]);
+            px[h] = row_prob(lr.st_llm[rowN + par[h]], lr.c, px[h], tok[h]);
+          }
+          if (!seeded) ua[h] = dr.u_accept[rowN + i];
+        }
+      }
+      // the bitsets are complete: this wave's LDS operations run in order
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      bool first_ok[2] = {false, false};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = lane + 64 * h;
+        if (i >= 1 && i < nU0) {
+          float r = ua[h];
+          if (seeded) {  // i is the j-th child of its parent, j = its lower siblings
+            const uint64_t lo = s_kids[par[h]][0], hi = s_kids[par[h]][1];
+            const int j = i < 64 ? __popcll(lo & ((1ull << i) - 1ull))
+                                 : __popcll(lo) + __popcll(hi & ((1ull << (i - 64)) - 1ull));
+            r = (float)mss_draw24(dr.seed, dr.step, (uint64_t)j, par[h], b) * 0x1p-24f;
+          }
+          const float rq = r * qx[h];
+          s_rq[i] = rq;
+          first_ok[h] = rq * 1.0f < px[h];
+        }
+      }
+      const uint64_t ok0 = __ballot(first_ok[0]), ok1 = __ballot(first_ok[1]);
+      if (lane == 0) {
+        s_first_ok[0] = ok0;
+        s_first_ok[1] = ok1;
+      }
+    }
+  } else if (wave == 1) {
+    static_assert(kMaxNodes <= 128, "two nodes per lane");
+    const float ub = seeded ? 0.f : dr.u_bonus[b];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = (t - 64) + 64 * h;
+      if (i < N)
+        s_bonus[i] = seeded ? mss_draw24(dr.seed, dr.step, kBonusOrdinal, i, b)
+                            : (uint32_t)(ub * 16777216.0f);  // exact: scaling by 2^24
+    }
+  }
+  if constexpr (PF) {
+    if (wave < 2) mss_issue_rows2(p0row, q1row, V, wr, qr);
   }
   __syncthreads();
   const int L = s_len;
   // the request's nodes (entries past them are padding, never used)
   const int n_raw = s_nodes;
   const int nU = nodes_used(n_raw, N);
-  if (wave < 2) {  // nodes 0..127: tree validity and token range
-    bool bad_tree = false, bad_tok = false;
-    if (t < nU) {
-      const int p = s_par[t];
-      bad_tree = (t == 0) ? (p != -1) : (p < 0 || p >= t);
-      bad_tok = t > 0 && (s_tok[t] < 0 || s_tok[t] >= V);
-    }
-    const uint64_t bt = __ballot(bad_tree), bk = __ballot(bad_tok);
-    if ((t & 63) == 0) {
-      if (bt) atomicOr(&s_status, 1);
-      if (bk || !nodes_ok(n_raw, N)) atomicOr(&s_status, 2);
-    }
-  }
-  __syncthreads();
+  const bool pre = PF && nU >= 2;
   const int st = s_status;
   if (st != 0) {
     for (int k = t; k < N; k += kMssThreads) {
@@ -915,7 +1006,6 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     }
     if (commit && cm.committed_src)
       for (int k = t; k < N; k += kMssThreads) cm.committed_src[rowN + k] = -1;
-    __syncthreads();  // every thread has read cache_len_in[b]
     if (t == 0) {
       path_len[b] = 0;
       // a bad node count or token is TTV_E_SHAPE, a malformed tree TTV_E_TREE
@@ -925,59 +1015,6 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     }
     return;
   }
-  // children bitsets, r*q[x] of every non-root node, and its first-attempt
-  // test with w = p of its parent and mass 1 (only first children use it).
-  // The gathers go out first; the final-draw integer of every node (the walk
-  // may end anywhere) is computed by waves 2-3 meanwhile.
-  float qx = 0.f, px = 0.f, ua = 0.f;
-  if (t >= 1 && t < nU) {
-    const int p = s_par[t], x = s_tok[t];
-    atomicOr(&s_kids[p][t >> 6], 1ull << (t & 63));
-    qx = ssm[(rowN + t) * V + x];
-    px = llm[(rowN + p) * V + x];
-    if constexpr (LG) {
-      qx = row_prob(lr.st_ssm[rowN + t], lr.c, qx, x);
-      px = row_prob(lr.st_llm[rowN + p], lr.c, px, x);
-    }
-    if (!seeded) ua = dr.u_accept[rowN + t];
-  }
-  static_assert(kMssThreads >= 128 + kMaxNodes, "waves 2-3 compute the final draws");
-  if (t >= 128 && t - 128 < N) {
-    s_bonus[t - 128] = seeded ? mss_draw24(dr.seed, dr.step, kBonusOrdinal, t - 128, b)
-                              : (uint32_t)(dr.u_bonus[b] * 16777216.0f);  // exact: scaling by 2^24
-  }
-  __syncthreads();  // the children bitsets are complete
-  bool first_ok = false;
-  float r = ua;
-  if (seeded && t >= 1 && t < nU) {  // t is the j-th child of p, j = its lower siblings
-    const int p = s_par[t];
-    const uint64_t lo = s_kids[p][0], hi = s_kids[p][1];
-    const int j = t < 64 ? __popcll(lo & ((1ull << t) - 1ull))
-                         : __popcll(lo) + __popcll(hi & ((1ull << (t - 64)) - 1ull));
-    r = (float)mss_draw24(dr.seed, dr.step, (uint64_t)j, p, b) * 0x1p-24f;
-  }
-  // the root's row and that of its first child, node 1 (whose parent can
-  // only be the root), are requested now and stream in while the first tests
-  // are made; the walk starts from them when that child's test fails.  (The
-  // requests go out unconditionally -- a root without children reads its own
-  // row twice -- so that the waits for the loads above stay exact.)
-  f32x4 wr[kMssPfChunks], qr[kMssPfChunks];
-  const bool pre = PF && nU >= 2;
-  if constexpr (PF) {
-    mss_issue_row(llm + rowN * V, V, wr);
-    mss_issue_row(pre ? ssm + (rowN + 1) * V : ssm + rowN * V, V, qr);
-  }
-  if (t >= 1 && t < nU) {
-    const int p = s_par[t];
-    const float rq = r * qx;
-    s_rq[t] = rq;
-    first_ok = rq * 1.0f < px;
-  }
-  if (wave < 2) {
-    const uint64_t bal = __ballot(first_ok);
-    if ((t & 63) == 0) s_first_ok[wave] = bal;
-  }
-  __syncthreads();
 
   // s_w = p_u.  The first barrier lets every thread finish reading the old
   // residual (the test that led here reads it), the second publishes p_u.
