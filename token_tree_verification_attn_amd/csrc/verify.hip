@@ -897,7 +897,8 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   // child in every tree of two or more nodes) are requested by every wave --
   // at once by the others, after their work by waves 0 and 1 -- so that they
   // stream in during the set-up; the walk starts from them when node 1's
-  // test fails.  (A one-node tree reads the root's q row instead: unused.)
+  // test fails.  (With N = 1 there is no row of node 1: the root's q row is
+  // read instead, and not used.)
   f32x4 wr[kMssPfChunks], qr[kMssPfChunks];
   const float* const p0row = llm + rowN * V;
   const float* const q1row = ssm + (rowN + (N >= 2 ? 1 : 0)) * V;
