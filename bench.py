@@ -50,6 +50,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import platform
 import subprocess
@@ -173,12 +174,16 @@ def hip_check(rc, what):
         raise RuntimeError("%s failed with HIP error %d" % (what, rc))
 
 
-def timed_steps(fns, n, stream):
+def timed_steps(fns, n, stream, preroll=0):
     """Run fns[i % len(fns)]() for i = 0..n-1 on `stream`, each between two
     HIP events recorded on that stream; returns the n durations in ms.  A
     spin kernel enqueued first keeps the GPU busy while the host enqueues
     every step, so the steps run back to back as they would in a serving
-    loop, not paced by the host."""
+    loop, not paced by the host.  `preroll` untimed calls of the same
+    functions run between the spin and the first event: the spin leaves the
+    GPU nearly idle, and its clocks take tens of milliseconds of real work to
+    come back to their working level (measured on MI355X: c4 attention 600 us
+    per call over 20-step batches, 520 us over 100-step ones, without them)."""
     h = hip_runtime()
     hs = ctypes.c_void_p(stream.cuda_stream)
     ev = []
@@ -191,6 +196,8 @@ def timed_steps(fns, n, stream):
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             torch.cuda._sleep(int(2e7))  # ~10 ms of clock cycles: the queue fills meanwhile
+        for i in range(preroll):
+            fns[i % len(fns)]()
         hip_check(h.hipEventRecord(ev[0], hs), "hipEventRecord")
         for i in range(n):
             fns[i % len(fns)]()
@@ -440,18 +447,24 @@ def measure(workload, args, dev):
     for i in range(args.warmup):
         one_step(copies[i % ncopies])
     torch.cuda.synchronize()
+    # untimed calls ahead of every timed batch: ~40 ms of GPU work, from one
+    # step timed here (4..128 calls)
+    t0 = time.perf_counter()
+    one_step(copies[0])
+    torch.cuda.synchronize()
+    preroll = int(min(128, max(4, math.ceil(0.040 / max(time.perf_counter() - t0, 1e-6)))))
     step_fns = launches(one_step)
     graphed = args.graph and all(getattr(f, "__self__", None) is not None for f in step_fns)
-    t_step = summary(timed_steps(step_fns, args.steps, stream))
+    t_step = summary(timed_steps(step_fns, args.steps, stream, preroll))
     # per-entry-point times over the same rotation, launched the same way
-    stage = lambda fn: summary(timed_steps(launches(fn), args.steps, stream))
+    stage = lambda fn: summary(timed_steps(launches(fn), args.steps, stream, preroll))
     t_attn = stage(step.attn)
     t_verify = stage(step.verify)
     t_commit = stage(step.commit)
     t_fused = stage(step.verify_commit) if step.fused else None
     # warm: one input copy back to back (what of it fits stays in the caches)
-    t_warm_attn = summary(timed_steps([lambda: step.attn(copies[0])], args.steps, stream))
-    t_warm_step = summary(timed_steps([lambda: one_step(copies[0])], args.steps, stream))
+    t_warm_attn = summary(timed_steps([lambda: step.attn(copies[0])], args.steps, stream, preroll))
+    t_warm_step = summary(timed_steps([lambda: one_step(copies[0])], args.steps, stream, preroll))
     st = torch.stack([c.st for c in copies]).cpu()
     assert int(st.abs().sum()) == 0, "a request was rejected: %s" % st
 
@@ -493,6 +506,7 @@ def measure(workload, args, dev):
                    "verify": d["mode"],
                    "verify_commit": "one pass" if step.fused else "two calls",
                    "input_copies": ncopies,
+                   "untimed_calls_before_each_timed_batch": preroll,
                    "launch": "hip graph replay per step" if graphed else "direct kernel launches",
                    "inputs": "rotated, HBM-resident" if ncopies > 1 else
                              ("one copy (warm)" if args.warm else
