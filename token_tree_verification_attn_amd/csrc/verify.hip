@@ -839,6 +839,64 @@ __device__ __forceinline__ void mss_regs_entry(const f32x4 (&wr)[kMssPfChunks], 
   }
 }
 
+// The final draw from a residual held in registers in the prefetching
+// walk's layout (thread t: entries 2048*wave + 256*j + 4*lane + e, zero past
+// V), with the masses of the waves' ranges in s_tot (total > 0): the wave
+// whose range holds the target is found as in the LDS draw; inside it the
+// masses of its eight 256-entry chunks, in order, locate the chunk, and a
+// lane scan over the chunk's 4-entry groups the entry, which the crossing
+// lane writes to *pick.  The same masses in the same order as the LDS draw.
+__device__ __forceinline__ void mss_draw_regs(const f32x4 (&w)[kMssPfChunks], const double* s_tot,
+                                              uint32_t R, int* pick) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const double cw = wave_inclusive_sum_f64(lane < kMssWaves ? s_tot[lane] : 0.0);
+  const uint64_t S = (uint64_t)readlane_f64(cw, kMssWaves - 1);
+  const double T = (double)((uint64_t)R * (S >> 24) + (((uint64_t)R * (S & 0xffffffull)) >> 24));
+  const uint64_t past = __ballot(lane < kMssWaves && cw > T);
+  const int ws = past ? __ffsll((unsigned long long)past) - 1 : kMssWaves - 1;
+  if (wave != ws) return;
+  auto group = [](const f32x4& g4) {
+    return (fx40d(g4[0]) + fx40d(g4[1])) + (fx40d(g4[2]) + fx40d(g4[3]));
+  };
+  double before = ws > 0 ? readlane_f64(cw, ws - 1) : 0.0;
+  int jx = kMssPfChunks - 1;
+  bool found = false;
+#pragma unroll
+  for (int j = 0; j < kMssPfChunks; ++j) {
+    const double c = wave_allsum_f64(group(w[j]));
+    if (!found) {
+      if (before + c > T) {
+        jx = j;
+        found = true;
+      } else {
+        before += c;
+      }
+    }
+  }
+  f32x4 wx = w[0];
+#pragma unroll
+  for (int j = 1; j < kMssPfChunks; ++j)
+    if (j == jx) wx = w[j];
+  const double gx = group(wx);
+  const double incl = wave_inclusive_sum_f64(gx);
+  const double lo = before + (incl - gx);
+  if (lo <= T && T < before + incl) {
+    const int v0 = 2048 * ws + 256 * jx + 4 * lane;
+    double cum = lo;
+    int p = v0 + 3;
+    bool hit = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cum += fx40d(wx[e]);
+      if (!hit && cum > T) {
+        p = v0 + e;
+        hit = true;
+      }
+    }
+    *pick = p;
+  }
+}
+
 // LG: llm and ssm hold logits; st_llm / st_ssm [B*N] their rows' statistics
 // (ttv_tree_verify_logits), c = (float)(log2(e) / T).
 // GM: the residual lives in global memory (gm_w [B][V], see above), for
@@ -1046,6 +1104,41 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     ++depth;
     if (t == 0) s_path[depth] = c;
   };
+
+  // ---- the commit's first rows (one 16-byte vector of K and of V per
+  // thread), requested once the walk has ended: before the final draw in
+  // LDS, so their round trip overlaps it (the draw from registers at the end
+  // of the walk returns at once in every wave but the one that holds the
+  // target, which requests them after it)
+  const int rv = cm.row_vecs;
+  int cper = 0, ncopy = 0;
+  bool cok = false;  // the commit fits the cache
+  const u32x4* ktr = static_cast<const u32x4*>(cm.k_tree);
+  const u32x4* vtr = static_cast<const u32x4*>(cm.v_tree);
+  u32x4* kca = static_cast<u32x4*>(cm.k_cache);
+  u32x4* vca = static_cast<u32x4*>(cm.v_cache);
+  auto copy_src = [&](int x, size_t& dst) {
+    const int h = x / cper, r = x - h * cper;
+    const int j = r / rv, e = r - j * rv;
+    const size_t bh = (size_t)b * cm.Hkv + h;
+    dst = (bh * cm.Lcap + (size_t)(L + j)) * rv + e;
+    return (bh * N + s_path[j]) * rv + e;
+  };
+  u32x4 kx0 = {0u, 0u, 0u, 0u}, vx0 = {0u, 0u, 0u, 0u};
+  size_t dst0 = 0;
+  auto issue_commit = [&](int len_) {
+    cok = commit && L >= 0 && L <= cm.Lmax && (long)L + len_ <= cm.Lcap;
+    cper = len_ * rv;
+    ncopy = cok ? cm.Hkv * cper : 0;
+    if (t < ncopy) {
+      const size_t src = copy_src(t, dst0);
+      kx0 = ktr[src];
+      vx0 = vtr[src];
+    }
+  };
+  // the walk that ends in the residual of the prefetching tests draws the
+  // bonus from its registers (s_pick)
+  bool drawn = false;
   // PF: the residual tests at node u once its first child c0 has failed its
   // test, with p_u in wr and q of c0 in qr (requested by the caller; k0/k1
   // the other children).  The residual stays in registers, and while child
@@ -1075,9 +1168,8 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
       const double part = mss_residual_roll<LG>(wr, qr, ssm + (rowN + (cn >= 0 ? cn : crow)) * V,
                                                 cn >= 0 ? V : 0, V, s, q_stats(crow), lr.c);
       if (cn >= 0) mss_regs_entry(wr, s_tok[cn], &s_wx[wx_slot]);
-      else mss_regs_store<LG>(wr, V, s_w);  // every child rejected: the draw reads w
-      // its barriers publish s_wx / s_w (the walk over logits, short of
-      // registers, keeps the two-barrier form)
+      // its barriers publish s_wx (the walk over logits, short of registers,
+      // keeps the two-barrier form)
       double S;
       if constexpr (LG) {
         S = block_sum_f64(part, s_redd);
@@ -1095,7 +1187,11 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
         s_tot = s_redd;
         return -1;
       }
-      if (cn < 0) return -1;  // every child rejected: bonus from the residual
+      if (cn < 0) {  // every child rejected: the bonus from the residual in wr
+        mss_draw_regs(wr, s_tot, s_bonus[u], &s_pick);
+        drawn = true;
+        return -1;
+      }
       const bool accept = s_rq[cn] * s < s_wx[wx_slot];
       wx_slot ^= 1;
       if (accept) return cn;
@@ -1195,30 +1291,7 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
     descend(next);
   }
   const int len = depth + 1;
-
-  // ---- the commit's first rows (one 16-byte vector of K and of V per
-  // thread) are requested before the final draw, which works in LDS only, so
-  // their round trip overlaps it
-  const bool cok = commit && L >= 0 && L <= cm.Lmax && (long)L + len <= cm.Lcap;
-  const int rv = cm.row_vecs, cper = len * rv, ncopy = cok ? cm.Hkv * cper : 0;
-  const u32x4* ktr = static_cast<const u32x4*>(cm.k_tree);
-  const u32x4* vtr = static_cast<const u32x4*>(cm.v_tree);
-  u32x4* kca = static_cast<u32x4*>(cm.k_cache);
-  u32x4* vca = static_cast<u32x4*>(cm.v_cache);
-  auto copy_src = [&](int x, size_t& dst) {
-    const int h = x / cper, r = x - h * cper;
-    const int j = r / rv, e = r - j * rv;
-    const size_t bh = (size_t)b * cm.Hkv + h;
-    dst = (bh * cm.Lcap + (size_t)(L + j)) * rv + e;
-    return (bh * N + s_path[j]) * rv + e;
-  };
-  u32x4 kx0 = {0u, 0u, 0u, 0u}, vx0 = {0u, 0u, 0u, 0u};
-  size_t dst0 = 0;
-  if (t < ncopy) {
-    const size_t src = copy_src(t, dst0);
-    kx0 = ktr[src];
-    vx0 = vtr[src];
-  }
+  issue_commit(len);
 
   // ---- bonus: inverse CDF over the exact integer prefix sums of fx40d(w).
   // The masses of the waves' ranges (left by the walk, else summed here,
@@ -1228,7 +1301,8 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   // 4: each 4-entry group is 16 aligned bytes of s_w), an exclusive scan over
   // the lanes gives each run's start, and the lane whose run crosses the
   // target walks its groups.  Masses are exact integers carried in doubles.
-  if constexpr (GM) {
+  if (drawn) {  // drawn from the registers at the end of the walk
+  } else if constexpr (GM) {
     // the same search over the wave ranges in global memory (span 256*CH,
     // lane runs of 4*CH entries); the masses of the ranges are in s_redd
     // (every exit of the walk leaves them there)
