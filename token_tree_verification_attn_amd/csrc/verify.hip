@@ -756,8 +756,8 @@ __device__ __forceinline__ double mss_regs_to_lds(const f32x4 (&r)[kMssPfChunks]
 // holds w of its chunks (entries mss_chunk_v<kMssPfChunks>(t, j)) in wr[j],
 // and the speculator's rows stream through one register buffer qr, chunk j
 // of the next row requested as soon as chunk j of the current one is used
-// (one row in flight during a pass, no LDS traffic).  LDS receives w only for
-// the final draw.
+// (one row in flight during a pass, no LDS traffic); the final draw from
+// that residual reads the registers too.
 
 // wr = the row loaded into it, as probabilities (LG: logits made
 // probabilities with `st`, 0 past V; rows of probabilities read 0 there)
@@ -810,17 +810,6 @@ __device__ __forceinline__ double mss_residual_roll(f32x4 (&wr)[kMssPfChunks], f
   }
   f64_round_nearest();
   return ((part[0] - kFxBias) + (part[1] - kFxBias)) + ((part[2] - kFxBias) + (part[3] - kFxBias));
-}
-
-// s_w[widx(v)] = w for the final draw (LG: the chunks below V; otherwise the
-// LDS holds the whole span)
-template <bool LG>
-__device__ __forceinline__ void mss_regs_store(const f32x4 (&wr)[kMssPfChunks], int V, float* s_w) {
-  const int t = threadIdx.x;
-  f32x4* wp = reinterpret_cast<f32x4*>(s_w + mss_slot0<kMssPfChunks>(t));
-#pragma unroll
-  for (int j = 0; j < kMssPfChunks; ++j)
-    if (!LG || mss_chunk_v<kMssPfChunks>(t, j) < V) wp[66 * j] = wr[j];
 }
 
 // w[x] from the registers of the thread that holds it (x = 2048*wave +
@@ -1147,8 +1136,9 @@ __global__ __launch_bounds__(kMssThreads) void mss_kernel(
   // zeros without a memory access, so that no request is under a branch).  w[x] of the child tested next goes through
   // LDS from the thread that holds it, published by the pass's reduction;
   // its slots alternate, so no barrier is needed before the next pass writes
-  // one.  Returns the accepted child, or -1 when the walk ends at u (the
-  // draw's row then in s_w, the masses of its waves' ranges in s_redd).
+  // one.  Returns the accepted child, or -1 when the walk ends at u: every
+  // child rejected, with the bonus drawn from the registers (s_pick), or the
+  // residual emptied, with p_u in s_w and its waves' masses in s_redd.
   auto pf_node = [&](int u, uint64_t k0, uint64_t k1, int c0, f32x4 (&wr)[kMssPfChunks],
                      f32x4 (&qr)[kMssPfChunks]) -> int {
     mss_row_regs<LG>(wr, V, p_stats(u), lr.c);
